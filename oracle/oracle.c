@@ -1,0 +1,434 @@
+/*
+ * CPU oracle for one tensor-parallel rank's share of a decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file: only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg do. It shares no code, header, helper or
+ * table with the HIP library; the two meet only through the byte arrays of
+ * the seeded input generator.
+ *
+ * Plain C99, slow and obvious by design. Floating point:
+ *   - bf16 inputs are widened exactly to double (a bf16 is the top half of an
+ *     IEEE binary32, so the widening is a shift);
+ *   - every product of two bf16 values is exact in double (8-bit significands
+ *     give a 16-bit product), and the products are summed in double in
+ *     ascending k; the double result is rounded once to float;
+ *   - the ring-ordered reduction is done in float, one IEEE addition at a
+ *     time, in the rank order fixed below. Build with -ffp-contract=off and
+ *     without -ffast-math so the compiler neither fuses nor reassociates.
+ *
+ * Sources (the pages this follows):
+ *   [P1] "Interconnects e clusters", llmdeepdive.com lesson 9.9,
+ *        section "01 · Conceito".
+ *   [P2] "Hosting Qwen on Blackwell", Perplexity blog (Bengali and Greek
+ *        editions), sections "All-Reduce", "MoE Dispatch-Combine",
+ *        "Expert Parallel".
+ *
+ * Parity pins (checked by the CPU tests) are listed per function. The MoE
+ * routing step has no printed example on the pages; its pins are the
+ * invariants named at oracle_moe_route.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+/* Exact widening: a bf16 bit pattern is the upper 16 bits of a binary32. */
+static float bf16_bits_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 to bf16, nearest-even; NaN stays a (quiet) NaN. */
+static uint16_t float_to_bf16_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lower = u & 0xffffu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u; /* carries into the exponent correctly, up to Inf */
+    return (uint16_t)upper;
+}
+
+float oracle_bf16_to_f32(uint16_t h) { return bf16_bits_to_float(h); }
+uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16_bits(f); }
+
+int oracle_abi_version(void) { return 1; }
+
+/* ------------------------------------------------------ thread helper -- */
+
+typedef void (*col_fn)(void* ctx, int64_t n_begin, int64_t n_end);
+
+typedef struct {
+    col_fn fn;
+    void* ctx;
+    int64_t n_begin, n_end;
+} col_job;
+
+static void* col_job_run(void* p)
+{
+    col_job* j = (col_job*)p;
+    j->fn(j->ctx, j->n_begin, j->n_end);
+    return NULL;
+}
+
+/* Split the output columns [0, n) into nthreads contiguous ranges. Each
+ * output element is computed by exactly one thread, so the result does not
+ * depend on the thread count. */
+static void for_columns(col_fn fn, void* ctx, int64_t n, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = n > 0 ? (int)n : 1;
+    if (nthreads == 1) {
+        fn(ctx, 0, n);
+        return;
+    }
+    pthread_t th[256];
+    col_job jobs[256];
+    int started[256];
+    int64_t per = (n + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].n_begin = (int64_t)t * per < n ? (int64_t)t * per : n;
+        jobs[t].n_end = (int64_t)(t + 1) * per < n ? (int64_t)(t + 1) * per : n;
+        started[t] = pthread_create(&th[t], NULL, col_job_run, &jobs[t]) == 0;
+        if (!started[t]) col_job_run(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t]) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------- row-parallel projection -- */
+
+typedef struct {
+    const uint16_t* x; /* [batch][ldx] bf16, columns [0, k) used */
+    int64_t ldx;
+    const uint16_t* w; /* [k][hidden] bf16, row-major */
+    int64_t batch, k, hidden;
+    double* y64;       /* [batch][hidden] or NULL */
+    float* y32;        /* [batch][hidden] or NULL */
+} partial_ctx;
+
+static void partial_cols(void* p, int64_t n0, int64_t n1)
+{
+    partial_ctx* c = (partial_ctx*)p;
+    int64_t width = n1 - n0;
+    if (width <= 0) return;
+    double* acc = (double*)malloc((size_t)width * sizeof(double));
+    for (int64_t b = 0; b < c->batch; ++b) {
+        for (int64_t n = 0; n < width; ++n) acc[n] = 0.0;
+        /* y[b,n] = sum over k of x[b,k] * W[k,n]; for every n the terms are
+         * added in ascending k, one rounding per addition, in double. */
+        for (int64_t kk = 0; kk < c->k; ++kk) {
+            double xv = (double)bf16_bits_to_float(c->x[b * c->ldx + kk]);
+            const uint16_t* wrow = c->w + kk * c->hidden + n0;
+            for (int64_t n = 0; n < width; ++n)
+                acc[n] += xv * (double)bf16_bits_to_float(wrow[n]);
+        }
+        for (int64_t n = 0; n < width; ++n) {
+            if (c->y64) c->y64[b * c->hidden + n0 + n] = acc[n];
+            if (c->y32) c->y32[b * c->hidden + n0 + n] = (float)acc[n];
+        }
+    }
+    free(acc);
+}
+
+/*
+ * Row-parallel partial projection [P1, Conceito]: under tensor parallelism a
+ * projection's weight matrix W[K, H] is split by rows over the ranks; rank r
+ * holds rows K_r and computes p_r = x[:, K_r] . W[K_r, :], a partial result
+ * that still has to be summed over ranks. With the whole of K this is the
+ * unsharded projection y = x . W.
+ *
+ *   x   bf16 [batch][ldx], the first k columns are the rank's slice
+ *   w   bf16 [k][hidden] row-major (the rank's rows of W)
+ *   y64 double [batch][hidden] (optional), y32 float [batch][hidden]
+ *       (optional, the double value rounded once, nearest-even)
+ *
+ * Pins: exact big-integer brute force on tiny shapes (y32 is the correctly
+ * rounded exact sum up to the stated double error bound); the shard
+ * partials sum to the unsharded product; one rank (N=1) is the full GEMV.
+ */
+void oracle_partial(const uint16_t* x, int64_t ldx, const uint16_t* w,
+                    int64_t batch, int64_t k, int64_t hidden,
+                    double* y64, float* y32, int nthreads)
+{
+    partial_ctx c = {x, ldx, w, batch, k, hidden, y64, y32};
+    for_columns(partial_cols, &c, hidden, nthreads);
+}
+
+/* -------------------------------------------------- ring reduction -- */
+
+/*
+ * Ring all-reduce sum plus residual [P1, Conceito; P2, All-Reduce].
+ *
+ * The payload of one reduction is the flattened row-major [batch x hidden]
+ * vector of `len` elements, split into n_ranks equal contiguous chunks of
+ * C = len / n_ranks elements. In the reduce-scatter phase chunk c starts on
+ * rank c and travels once round the ring, each rank adding its own partial
+ * to the running sum it received, so chunk c is summed in the rank order
+ * c, c+1, ..., c+N-1 (mod N). That takes N-1 steps; the all-gather phase
+ * then copies the finished chunks round the ring in N-1 more steps and adds
+ * nothing. The residual is added once, after the full sum:
+ *
+ *     s = p_c[i];  for j = 1..N-1: s = s + p_{(c+j) mod N}[i];
+ *     out[i] = s + residual[i]                          (all in binary32)
+ *
+ * partials: float [n_ranks][len], rank-major. residual may alias out.
+ * out_bf16 (optional) receives out rounded to bf16, nearest-even.
+ * Returns 0, or -1 if n_ranks < 1 or n_ranks does not divide len.
+ *
+ * Pins: the IEEE vector p = (2^24, 1, -2^24, 1) at N=4 gives (1, 2, 2, 0)
+ * per chunk under this start convention, which no other rank order gives;
+ * N=1 is the identity plus residual; N=2 is p0 + p1 + residual; for small
+ * integer partials every order is exact and the output is the exact sum.
+ */
+int oracle_ring_reduce(const float* partials, int32_t n_ranks, int64_t len,
+                       const float* residual, float* out, uint16_t* out_bf16)
+{
+    if (n_ranks < 1 || len < 0 || len % n_ranks != 0) return -1;
+    int64_t chunk = len / n_ranks;
+    for (int64_t i = 0; i < len; ++i) {
+        int32_t c = (int32_t)(i / chunk);
+        volatile float s = partials[(int64_t)c * len + i];
+        for (int32_t j = 1; j < n_ranks; ++j) {
+            int32_t r = (c + j) % n_ranks;
+            s = s + partials[(int64_t)r * len + i];
+        }
+        volatile float o = s + residual[i];
+        out[i] = o;
+        if (out_bf16) out_bf16[i] = float_to_bf16_bits(o);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ wire bytes -- */
+
+/*
+ * Bytes a ring all-reduce puts on each rank's wire [P1, Conceito]:
+ * 2(N-1)/N times the payload, i.e. N-1 reduce-scatter sends plus N-1
+ * all-gather sends of one chunk of payload/N elements each.
+ * Returns -1 if the payload does not split into N equal chunks.
+ */
+int64_t oracle_ring_wire_bytes_per_rank(int32_t n_ranks, int64_t payload_elems,
+                                        int32_t elem_bytes)
+{
+    if (n_ranks < 1 || payload_elems % n_ranks != 0) return -1;
+    int64_t chunk = payload_elems / n_ranks;
+    return 2 * (int64_t)(n_ranks - 1) * chunk * elem_bytes;
+}
+
+/*
+ * Total over all ranks [P2, All-Reduce]: every peer reduces one 1/N slice,
+ * reading (N-1) * B/N bytes from the others, then broadcasts it, for
+ * (N-1) * B * 2 reads and writes in all. The naive scheme, where one peer
+ * reads everything from every other, moves N * (N-1) * B.
+ */
+int64_t oracle_split_allreduce_total_bytes(int32_t n_ranks, int64_t payload_bytes)
+{
+    if (n_ranks < 1) return -1;
+    return (int64_t)(n_ranks - 1) * payload_bytes * 2;
+}
+
+int64_t oracle_naive_allreduce_total_bytes(int32_t n_ranks, int64_t payload_bytes)
+{
+    if (n_ranks < 1) return -1;
+    return (int64_t)n_ranks * (n_ranks - 1) * payload_bytes;
+}
+
+/* ------------------------------------------------- layer stack -- */
+
+/*
+ * One rank's share of a decode step over a stack of layers [P1, Conceito]:
+ * every layer has two reconciliation points, after the sequence-mixer's
+ * output projection and after the FFN down projection, and at each the
+ * rank's partial is all-reduced and the result added to the residual
+ * stream before it goes on. The operations between the points are not
+ * part of this path; each point's activation slice is an input.
+ *
+ *   x_attn  bf16 [L][batch][ka_r]      w_o    bf16 [L][ka_r][hidden]
+ *   x_ffn   bf16 [L][batch][ki_r]      w_down bf16 [L][ki_r][hidden]
+ *   slots   float [L][2][n_ranks][batch][hidden]: the other ranks' partials
+ *           are inputs; this rank's entry is written (rounded once from
+ *           double) and then reduced with them.
+ *   hidden_state float [batch][hidden], in/out: h <- ring(slots) + h at each
+ *           of the 2L points in order.
+ * Returns 0, or -1 on bad sizes.
+ */
+int oracle_decode_layers(int32_t n_layers, int32_t n_ranks, int32_t rank,
+                         int64_t batch, int64_t hidden, int64_t ka_r, int64_t ki_r,
+                         const uint16_t* x_attn, const uint16_t* w_o,
+                         const uint16_t* x_ffn, const uint16_t* w_down,
+                         float* slots, float* hidden_state, int nthreads)
+{
+    if (n_layers < 0 || n_ranks < 1 || rank < 0 || rank >= n_ranks) return -1;
+    int64_t len = batch * hidden;
+    if (len % n_ranks != 0) return -1;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        for (int point = 0; point < 2; ++point) {
+            int64_t kr = point == 0 ? ka_r : ki_r;
+            const uint16_t* x = point == 0 ? x_attn + (int64_t)l * batch * ka_r
+                                           : x_ffn + (int64_t)l * batch * ki_r;
+            const uint16_t* w = point == 0 ? w_o + (int64_t)l * ka_r * hidden
+                                           : w_down + (int64_t)l * ki_r * hidden;
+            float* slot = slots + ((int64_t)l * 2 + point) * n_ranks * len;
+            oracle_partial(x, kr, w, batch, kr, hidden, NULL,
+                           slot + (int64_t)rank * len, nthreads);
+            if (oracle_ring_reduce(slot, n_ranks, len, hidden_state,
+                                   hidden_state, NULL) != 0)
+                return -1;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------- MoE -- */
+
+/*
+ * Top-k routing of decode tokens to experts [P2, Prefillers: each token is
+ * sent to 8 of 128 experts]. The pages give only the top-8-of-128 choice
+ * and a weighted combine; the reading taken here is the usual one:
+ *   - probabilities = softmax over all experts of the token's logits
+ *     (in double, shifted by the maximum);
+ *   - the top_k experts by probability are selected (softmax is monotone,
+ *     so this is the top_k by logit), ties going to the lower expert index;
+ *   - with renorm != 0 the selected probabilities are divided by their sum,
+ *     otherwise they are the plain softmax values;
+ *   - per token the selection is listed in ascending expert index.
+ *
+ *   logits [tokens][experts] float; sel_expert [tokens][top_k] int32;
+ *   sel_weight [tokens][top_k] double.
+ * Pins: the selected logits dominate the unselected ones; ties resolve to
+ * the lower index; renormalised weights sum to 1; top_k = experts gives the
+ * full softmax.
+ */
+int oracle_moe_route(const float* logits, int32_t tokens, int32_t experts,
+                     int32_t top_k, int32_t renorm, int32_t* sel_expert,
+                     double* sel_weight)
+{
+    if (tokens < 0 || experts < 1 || top_k < 1 || top_k > experts) return -1;
+    double* prob = (double*)malloc((size_t)experts * sizeof(double));
+    unsigned char* taken = (unsigned char*)malloc((size_t)experts);
+    for (int32_t t = 0; t < tokens; ++t) {
+        const float* z = logits + (int64_t)t * experts;
+        double zmax = z[0];
+        for (int32_t e = 1; e < experts; ++e)
+            if (z[e] > zmax) zmax = z[e];
+        double denom = 0.0;
+        for (int32_t e = 0; e < experts; ++e) {
+            prob[e] = exp((double)z[e] - zmax);
+            denom += prob[e];
+        }
+        for (int32_t e = 0; e < experts; ++e) {
+            prob[e] /= denom;
+            taken[e] = 0;
+        }
+        /* repeated arg-max: the first maximum found is the lowest index */
+        for (int32_t s = 0; s < top_k; ++s) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < experts; ++e)
+                if (!taken[e] && (best < 0 || z[e] > z[best])) best = e;
+            taken[best] = 1;
+        }
+        double sel_sum = 0.0;
+        for (int32_t e = 0; e < experts; ++e)
+            if (taken[e]) sel_sum += prob[e];
+        int32_t s = 0;
+        for (int32_t e = 0; e < experts; ++e) {
+            if (!taken[e]) continue;
+            sel_expert[(int64_t)t * top_k + s] = e;
+            sel_weight[(int64_t)t * top_k + s] = renorm ? prob[e] / sel_sum : prob[e];
+            ++s;
+        }
+    }
+    free(taken);
+    free(prob);
+    return 0;
+}
+
+typedef struct {
+    int32_t tokens, top_k, e_begin, e_end;
+    const int32_t* sel_expert;
+    const double* sel_weight;
+    const uint16_t* u;   /* [tokens][top_k][moe_inter] bf16 */
+    const uint16_t* w;   /* [e_end - e_begin][moe_inter][hidden] bf16 */
+    int64_t moe_inter, hidden;
+    double* part64;
+    float* part32;
+} moe_ctx;
+
+static void moe_cols(void* p, int64_t n0, int64_t n1)
+{
+    moe_ctx* c = (moe_ctx*)p;
+    int64_t width = n1 - n0;
+    if (width <= 0) return;
+    double* acc = (double*)malloc((size_t)width * sizeof(double));
+    double* y = (double*)malloc((size_t)width * sizeof(double));
+    for (int32_t t = 0; t < c->tokens; ++t) {
+        for (int64_t n = 0; n < width; ++n) acc[n] = 0.0;
+        /* the token's selection is in ascending expert order */
+        for (int32_t s = 0; s < c->top_k; ++s) {
+            int32_t e = c->sel_expert[(int64_t)t * c->top_k + s];
+            if (e < c->e_begin || e >= c->e_end) continue;
+            double g = c->sel_weight[(int64_t)t * c->top_k + s];
+            const uint16_t* uv = c->u + ((int64_t)t * c->top_k + s) * c->moe_inter;
+            const uint16_t* we = c->w + (int64_t)(e - c->e_begin) * c->moe_inter * c->hidden;
+            for (int64_t n = 0; n < width; ++n) y[n] = 0.0;
+            for (int64_t kk = 0; kk < c->moe_inter; ++kk) {
+                double xv = (double)bf16_bits_to_float(uv[kk]);
+                const uint16_t* wrow = we + kk * c->hidden + n0;
+                for (int64_t n = 0; n < width; ++n)
+                    y[n] += xv * (double)bf16_bits_to_float(wrow[n]);
+            }
+            for (int64_t n = 0; n < width; ++n) acc[n] += g * y[n];
+        }
+        for (int64_t n = 0; n < width; ++n) {
+            if (c->part64) c->part64[(int64_t)t * c->hidden + n0 + n] = acc[n];
+            if (c->part32) c->part32[(int64_t)t * c->hidden + n0 + n] = (float)acc[n];
+        }
+    }
+    free(y);
+    free(acc);
+}
+
+/*
+ * Expert-parallel down projection and local combine [P2, MoE Dispatch-
+ * Combine; Expert Parallel]: the rank holds experts [e_begin, e_end); for
+ * each token it accumulates, over its selected experts that live on this
+ * rank (ascending expert index), the routing weight times that expert's
+ * down projection of the token's activation. The result is this rank's
+ * partial, which the all-reduce over ranks then sums.
+ *
+ *   part[t, :] = sum_{s: e_begin <= sel_expert[t,s] < e_end}
+ *                    sel_weight[t,s] * (u[t,s,:] . W_e)        (double)
+ *
+ *   u        bf16 [tokens][top_k][moe_inter]: one activation per selection
+ *   w_local  bf16 [e_end-e_begin][moe_inter][hidden]
+ *   part64 / part32 [tokens][hidden] (either may be NULL)
+ * Pins: with all experts local the partial is the full combine; the
+ * partials of all ranks sum to it; a single selection with weight 1 is the
+ * dense projection of oracle_partial.
+ */
+int oracle_moe_partial(int32_t tokens, int32_t top_k, const int32_t* sel_expert,
+                       const double* sel_weight, int32_t e_begin, int32_t e_end,
+                       const uint16_t* u, const uint16_t* w_local,
+                       int64_t moe_inter, int64_t hidden,
+                       double* part64, float* part32, int nthreads)
+{
+    if (tokens < 0 || top_k < 1 || e_end < e_begin) return -1;
+    moe_ctx c = {tokens, top_k, e_begin, e_end, sel_expert, sel_weight,
+                 u, w_local, moe_inter, hidden, part64, part32};
+    for_columns(moe_cols, &c, hidden, nthreads);
+    return 0;
+}

@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-types the oracle's own formula: they use exact
+big-number arithmetic, closed forms printed on the pages, IEEE special-case
+vectors derived by hand (tests/golden), invariants and library routines for
+special cases. Each is chosen so that a plausible slip in the oracle (a
+dropped term, a transposed operand, a wrong slice offset, a wrong ring start,
+a misplaced residual) fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from row_gemv_reduction_amd import synth
+
+U64 = 2.0 ** -53
+
+
+# ------------------------------------------------------------ helpers --
+
+def bf16_to_fraction(bits):
+    return Fraction(float(synth.bf16_bits_to_f32(np.array([bits], np.uint16))[0]))
+
+
+def rne_f32(fr: Fraction) -> np.float32:
+    """Exact round-to-nearest-even of a rational to binary32."""
+    if fr == 0:
+        return np.float32(0.0)
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+
+    def key(c):
+        return (abs(Fraction(float(c)) - fr), int(np.array(c, np.float32).view(np.uint32)) & 1)
+    return min(cands, key=key)
+
+
+def wide_range_bf16(shape, seed):
+    """bf16 values spread over ~40 binades, to stress the accumulation."""
+    g = np.random.default_rng(seed)
+    v = g.standard_normal(shape) * np.exp2(g.integers(-20, 21, size=shape))
+    return synth.f32_to_bf16_bits(v.astype(np.float32))
+
+
+def exact_product(x_bits, w_bits):
+    b, k = x_bits.shape
+    _, h = w_bits.shape
+    xf = [[bf16_to_fraction(x_bits[i, j]) for j in range(k)] for i in range(b)]
+    wf = [[bf16_to_fraction(w_bits[i, j]) for j in range(h)] for i in range(k)]
+    exact = [[sum((xf[i][kk] * wf[kk][n] for kk in range(k)), Fraction(0)) for n in range(h)]
+             for i in range(b)]
+    absum = [[sum((abs(xf[i][kk] * wf[kk][n]) for kk in range(k)), Fraction(0)) for n in range(h)]
+             for i in range(b)]
+    return exact, absum
+
+
+# ------------------------------------------------------ bf16 rounding --
+
+def test_bf16_conversion_matches_torch_and_special_cases():
+    g = np.random.default_rng(1)
+    v = np.concatenate([
+        g.standard_normal(4096).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-40, 3.4e38, -3.4e38,
+                  1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9], np.float32),
+    ])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got_np = synth.f32_to_bf16_bits(v)
+    got_or = np.array([oracle.f32_to_bf16(x) for x in v], np.uint16)
+    assert np.array_equal(got_np, want)
+    assert np.array_equal(got_or, want)
+    # halfway cases: 1 + 2^-8 is exactly between 1 and 1 + 2^-7 -> even (1.0)
+    assert oracle.f32_to_bf16(1.0 + 2.0 ** -8) == 0x3F80
+    assert oracle.f32_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    # NaN stays NaN
+    assert math.isnan(oracle.bf16_to_f32(oracle.f32_to_bf16(float("nan"))))
+    # widening is exact for every bit pattern's finite values
+    allbits = np.arange(0, 65536, 97, dtype=np.uint16)
+    wide = np.array([oracle.bf16_to_f32(int(b)) for b in allbits], np.float32)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(wide[fin], ref[fin])
+
+
+# --------------------------------------------- row-parallel projection --
+
+@pytest.mark.parametrize("b,k,h,seed", [(1, 1, 1, 0), (1, 7, 5, 1), (2, 33, 12, 2),
+                                        (3, 24, 40, 3), (1, 64, 64, 4)])
+def test_partial_equals_exact_bruteforce(b, k, h, seed):
+    x = wide_range_bf16((b, k), seed)
+    w = wide_range_bf16((k, h), seed + 100)
+    y64, y32 = oracle.partial(x, w)
+    exact, absum = exact_product(x, w)
+    gamma = Fraction(k * U64) / (1 - Fraction(k * U64))
+    for i in range(b):
+        for n in range(h):
+            bound = gamma * absum[i][n]
+            assert abs(Fraction(float(y64[i, n])) - exact[i][n]) <= bound
+            want = rne_f32(exact[i][n])
+            got = np.float32(y32[i, n])
+            if got != want:
+                # only allowed where the double result straddles a rounding
+                # boundary of binary32 within its own error bound
+                mid = (Fraction(float(got)) + Fraction(float(want))) / 2
+                assert abs(mid - exact[i][n]) <= bound
+                assert abs(int(np.array(got).view(np.uint32)) - int(np.array(want).view(np.uint32))) == 1
+
+
+def test_partial_closed_form_column_sums():
+    """x = 1, W[k, n] = (k + 1) * (n + 1): y[n] = (n + 1) * K (K + 1) / 2, exact."""
+    k, h = 48, 7
+    x = synth.f32_to_bf16_bits(np.ones((1, k), np.float32))
+    w = synth.f32_to_bf16_bits(np.outer(np.arange(1, k + 1), np.arange(1, h + 1)).astype(np.float32))
+    y64, y32 = oracle.partial(x, w)
+    want = np.arange(1, h + 1) * k * (k + 1) / 2
+    assert np.array_equal(y64[0], want)
+    assert np.array_equal(y32[0], want.astype(np.float32))
+
+
+def test_partial_not_transposed_on_rectangular_shape():
+    """A one-hot x picks out one row of W (not a column)."""
+    k, h = 5, 9
+    w = wide_range_bf16((k, h), 7)
+    for row in range(k):
+        x = np.zeros((1, k), np.float32)
+        x[0, row] = 1.0
+        _, y32 = oracle.partial(synth.f32_to_bf16_bits(x), w)
+        assert np.array_equal(y32[0], synth.bf16_bits_to_f32(w[row]))
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 4, 8])
+def test_shard_partials_sum_to_unsharded(n_ranks):
+    """Row-parallel split [lesson 9.9, Conceito]: sum over ranks of
+    x[:, K_r] W[K_r, :] equals x W, to the double rounding bound."""
+    b, k, h = 3, 24 * 8, 40
+    x = synth.normal_bf16((b, k), 1.0, seed=0, tensor="x")
+    w = synth.normal_bf16((k, h), synth.WEIGHT_STD, seed=0, tensor="w")
+    y64, _ = oracle.partial(x, w)
+    kr = k // n_ranks
+    total = np.zeros((b, h))
+    for r in range(n_ranks):
+        p64, _ = oracle.partial(x[:, r * kr:(r + 1) * kr], w[r * kr:(r + 1) * kr])
+        total += p64
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(w).astype(np.float64)
+    bound = 2 * (k + n_ranks) * U64 * (np.abs(xf) @ np.abs(wf))
+    assert np.all(np.abs(total - y64) <= bound)
+    if n_ranks == 1:
+        p64, p32 = oracle.partial(x[:, :k], w[:k])
+        assert np.array_equal(p64, y64)
+    # a planted slip (rank 1 given rank 0's rows) must break the invariant
+    if n_ranks >= 2:
+        wrong = total - oracle.partial(x[:, kr:2 * kr], w[kr:2 * kr])[0] \
+            + oracle.partial(x[:, kr:2 * kr], w[0:kr])[0]
+        assert not np.all(np.abs(wrong - y64) <= bound)
+
+
+def test_partial_thread_count_does_not_change_bits():
+    x = synth.normal_bf16((2, 300), 1.0, seed=3, tensor="x")
+    w = synth.normal_bf16((300, 257), synth.WEIGHT_STD, seed=3, tensor="w")
+    a64, a32 = oracle.partial(x, w, nthreads=1)
+    b64, b32 = oracle.partial(x, w, nthreads=7)
+    assert np.array_equal(a64, b64) and np.array_equal(a32, b32)
+
+
+# --------------------------------------------------- ring reduction --
+
+def _ring_cases(golden_dir):
+    with open(os.path.join(golden_dir, "ring_order_vectors.json")) as f:
+        return json.load(f)["cases"]
+
+
+def test_ring_order_ieee_vectors(golden_dir):
+    for case in _ring_cases(golden_dir):
+        n, L = case["n"], case["batch"] * case["hidden"]
+        parts = np.array([[v] * L for v in case["rank_values"]], np.float32)
+        res = np.full(L, case["residual"], np.float32)
+        out = oracle.ring_reduce(parts, res)
+        assert out.tolist() == case["expected"], case["name"]
+
+
+def test_ring_rank_zero_first_order_is_rejected_by_the_vector(golden_dir):
+    """The n4 vector separates the ring order from a naive rank-0-first sum."""
+    case = _ring_cases(golden_dir)[0]
+    v = [np.float32(x) for x in case["rank_values"]]
+    s = v[0]
+    for x in v[1:]:
+        s = np.float32(s + x)
+    assert [float(s)] * 4 != case["expected"]
+
+
+@pytest.mark.parametrize("n_ranks", [1, 2, 3, 4, 5, 8])
+def test_ring_small_integers_is_exact_sum(n_ranks):
+    """Small integer partials make every addition exact, so any order must
+    give the exact sum of all ranks plus the residual."""
+    g = np.random.default_rng(n_ranks)
+    b, h = 3, 40
+    parts = g.integers(-1000, 1000, size=(n_ranks, b, h)).astype(np.float32)
+    res = g.integers(-1000, 1000, size=(b, h)).astype(np.float32)
+    out = oracle.ring_reduce(parts, res)
+    assert np.array_equal(out, parts.astype(np.int64).sum(0) + res.astype(np.int64))
+
+
+def test_ring_special_cases_n1_n2():
+    g = np.random.default_rng(5)
+    res = g.standard_normal((2, 16)).astype(np.float32)
+    p1 = g.standard_normal((1, 2, 16)).astype(np.float32)
+    assert np.array_equal(oracle.ring_reduce(p1, res), p1[0] + res)
+    p2 = g.standard_normal((2, 2, 16)).astype(np.float32)
+    assert np.array_equal(oracle.ring_reduce(p2, res), (p2[0] + p2[1]) + res)
+
+
+def test_ring_bf16_output_and_errors():
+    g = np.random.default_rng(6)
+    parts = g.standard_normal((4, 1, 64)).astype(np.float32)
+    res = g.standard_normal((1, 64)).astype(np.float32)
+    out, ob = oracle.ring_reduce(parts, res, want_bf16=True)
+    want = torch.from_numpy(out).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ob, want)
+    with pytest.raises(ValueError):
+        oracle.ring_reduce(np.zeros((3, 1, 4), np.float32), np.zeros((1, 4), np.float32))
+
+
+# ------------------------------------------------------- wire bytes --
+
+def test_wire_bytes_reproduce_the_pages_worked_example(golden_dir):
+    with open(os.path.join(golden_dir, "ring_wire_bytes.json")) as f:
+        g = json.load(f)
+    mib = 1 << 20
+    for n, want_mib in g["per_token_wire_mib"].items():
+        per_red = oracle.ring_wire_bytes_per_rank(int(n), g["hidden"], g["elem_bytes"])
+        assert per_red * g["reductions_per_token"] == want_mib * mib
+    per_s = oracle.ring_wire_bytes_per_rank(4, g["hidden"], g["elem_bytes"]) \
+        * g["reductions_per_token"] * g["rate_tokens_per_s"]
+    assert per_s / mib == 93.75 and per_s / mib < g["rate_bound_mib_per_s"]
+    for fab in ("fast", "slow"):
+        ms = g["reductions_per_token"] * g["latency_us"][fab] / 1000.0
+        assert math.isclose(ms, g["latency_per_token_ms"][fab])
+    assert oracle.ring_wire_bytes_per_rank(3, 10, 2) == -1
+
+
+def test_wire_bytes_agree_with_split_reduce_broadcast_totals(golden_dir):
+    with open(os.path.join(golden_dir, "allreduce_traffic.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        n, B = c["n"], c["payload_bytes"]
+        assert oracle.split_allreduce_total_bytes(n, B) == c["split"]
+        assert oracle.naive_allreduce_total_bytes(n, B) == c["naive"]
+        # the ring's per-rank bytes over all N ranks give the same total
+        assert n * oracle.ring_wire_bytes_per_rank(n, B // 2, 2) == c["split"]
+
+
+# ------------------------------------------------------- layer stack --
+
+def _stack(L, n, b, h, ka, ki, seed):
+    kw = dict(seed=seed)
+    xa = synth.normal_bf16((L, b, ka // n), 1.0, tensor="x_attn", **kw)
+    wo = synth.normal_bf16((L, ka // n, h), synth.WEIGHT_STD, tensor="w_o", **kw)
+    xf = synth.normal_bf16((L, b, ki // n), 1.0, tensor="x_ffn", **kw)
+    wd = synth.normal_bf16((L, ki // n, h), synth.WEIGHT_STD, tensor="w_down", **kw)
+    slots = synth.normal_f32((L, 2, n, b, h), 0.1, tensor="slots", **kw)
+    h0 = synth.normal_f32((b, h), 1.0, tensor="residual", **kw)
+    return xa, wo, xf, wd, slots, h0
+
+
+def test_decode_layers_writes_each_points_partial_in_its_slot():
+    L, n, b, h, ka, ki, rank = 3, 4, 2, 24, 32, 64, 2
+    xa, wo, xf, wd, slots, h0 = _stack(L, n, b, h, ka, ki, 11)
+    s_out, _ = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
+    for l in range(L):
+        assert np.array_equal(s_out[l, 0, rank], oracle.partial(xa[l], wo[l])[1])
+        assert np.array_equal(s_out[l, 1, rank], oracle.partial(xf[l], wd[l])[1])
+        for r in range(n):
+            if r != rank:
+                assert np.array_equal(s_out[l, :, r], slots[l, :, r])
+
+
+def test_decode_layers_chains_the_residual_exactly_on_integers():
+    """With zero weights this rank's partials are 0, and small integer
+    partials on the other ranks make every sum exact: the final hidden
+    state is the initial one plus all 2L reductions."""
+    L, n, b, h, ka, ki, rank = 4, 3, 1, 12, 6, 9, 0
+    g = np.random.default_rng(9)
+    xa = synth.normal_bf16((L, b, ka // n), 1.0, seed=1, tensor="x_attn")
+    xf = synth.normal_bf16((L, b, ki // n), 1.0, seed=1, tensor="x_ffn")
+    wo = np.zeros((L, ka // n, h), np.uint16)
+    wd = np.zeros((L, ki // n, h), np.uint16)
+    slots = g.integers(-50, 50, size=(L, 2, n, b, h)).astype(np.float32)
+    h0 = g.integers(-50, 50, size=(b, h)).astype(np.float32)
+    _, h1 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
+    others = slots.astype(np.int64)
+    others[:, :, rank] = 0
+    assert np.array_equal(h1, h0 + others.sum(axis=(0, 1, 2)))
+
+
+def test_decode_layers_one_layer_is_partial_then_ring():
+    L, n, b, h, ka, ki, rank = 1, 2, 1, 16, 8, 20, 1
+    xa, wo, xf, wd, slots, h0 = _stack(L, n, b, h, ka, ki, 12)
+    _, h1 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
+    s = slots[0].copy()
+    s[0, rank] = oracle.partial(xa[0], wo[0])[1]
+    s[1, rank] = oracle.partial(xf[0], wd[0])[1]
+    want = oracle.ring_reduce(s[1], oracle.ring_reduce(s[0], h0))
+    assert np.array_equal(h1, want)
+
+
+# --------------------------------------------------------------- MoE --
+
+def test_moe_route_invariants():
+    t, e, k = 64, 128, 8
+    z = synth.normal_f32((t, e), 1.0, seed=0, tensor="logits")
+    se, sw = oracle.moe_route(z, k)
+    for i in range(t):
+        sel = set(se[i].tolist())
+        assert len(sel) == k and list(se[i]) == sorted(se[i])
+        assert min(z[i, list(sel)]) >= max(z[i, [j for j in range(e) if j not in sel]])
+        assert math.isclose(sw[i].sum(), 1.0, rel_tol=0, abs_tol=1e-15)
+        # weights ordered like the logits of the selected experts
+        order = np.argsort(z[i, se[i]], kind="stable")
+        assert np.all(np.diff(sw[i][order]) >= 0)
+
+
+def test_moe_route_ties_go_to_the_lower_index():
+    z = np.zeros((1, 16), np.float32)
+    z[0, [3, 9, 12]] = 1.0
+    se, sw = oracle.moe_route(z, 5)
+    assert se[0].tolist() == [0, 1, 3, 9, 12]
+    assert sw[0, 2] == sw[0, 3] == sw[0, 4] and sw[0, 0] == sw[0, 1]
+
+
+def test_moe_route_full_selection_is_the_softmax():
+    z = synth.normal_f32((5, 12), 1.0, seed=2, tensor="logits")
+    se, sw = oracle.moe_route(z, 12, renorm=False)
+    ref = torch.softmax(torch.from_numpy(z).double(), dim=1).numpy()
+    assert np.array_equal(se, np.tile(np.arange(12), (5, 1)))
+    assert np.allclose(sw, ref, rtol=1e-15, atol=1e-16)
+
+
+def _moe_inputs(t, e, k, mi, h, seed):
+    z = synth.normal_f32((t, e), 1.0, seed=seed, tensor="logits")
+    se, sw = oracle.moe_route(z, k)
+    u = synth.normal_bf16((t, k, mi), 1.0, seed=seed, tensor="u")
+    w = synth.normal_bf16((e, mi, h), synth.WEIGHT_STD, seed=seed, tensor="w_expert")
+    return se, sw, u, w
+
+
+def test_moe_rank_partials_sum_to_the_full_combine():
+    t, e, k, mi, h, ep = 6, 16, 4, 24, 10, 4
+    se, sw, u, w = _moe_inputs(t, e, k, mi, h, 4)
+    full64, _ = oracle.moe_partial(se, sw, 0, u, w)
+    le = e // ep
+    tot = sum(oracle.moe_partial(se, sw, r * le, u, w[r * le:(r + 1) * le])[0] for r in range(ep))
+    xf = synth.bf16_bits_to_f32(u).astype(np.float64)
+    scale = np.abs(xf).sum() * np.abs(synth.bf16_bits_to_f32(w)).max()
+    assert np.all(np.abs(tot - full64) <= 64 * U64 * scale)
+
+
+def test_moe_single_selection_is_the_dense_projection():
+    t, mi, h = 3, 40, 12
+    u = synth.normal_bf16((t, 1, mi), 1.0, seed=5, tensor="u")
+    w = synth.normal_bf16((1, mi, h), synth.WEIGHT_STD, seed=5, tensor="w_expert")
+    se = np.zeros((t, 1), np.int32)
+    p64, p32 = oracle.moe_partial(se, np.ones((t, 1)), 0, u, w)
+    d64, d32 = oracle.partial(u[:, 0, :], w[0])
+    assert np.array_equal(p64, d64) and np.array_equal(p32, d32)
+    # a power-of-two routing weight scales exactly
+    q64, _ = oracle.moe_partial(se, np.full((t, 1), 0.25), 0, u, w)
+    assert np.array_equal(q64, d64 * 0.25)
+    # experts outside this rank's range contribute nothing
+    z64, _ = oracle.moe_partial(se, np.ones((t, 1)), 1, u, w)
+    assert np.array_equal(z64, np.zeros_like(z64))
+
+
+def test_moe_partial_exact_bruteforce_tiny():
+    t, e, k, mi, h = 2, 4, 2, 6, 3
+    se, sw, u, w = _moe_inputs(t, e, k, mi, h, 6)
+    p64, p32 = oracle.moe_partial(se, sw, 0, u, w)
+    for ti in range(t):
+        for n in range(h):
+            ex = Fraction(0)
+            for s in range(k):
+                ee = int(se[ti, s])
+                dot = sum(bf16_to_fraction(u[ti, s, kk]) * bf16_to_fraction(w[ee, kk, n])
+                          for kk in range(mi))
+                ex += Fraction(float(sw[ti, s])) * dot
+            assert abs(Fraction(float(p64[ti, n])) - ex) <= Fraction(1, 2 ** 40) * (1 + abs(ex))
