@@ -1,0 +1,269 @@
+/*
+ * tp_decode.h — one tensor-parallel rank's share of an LLM decode step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Under tensor parallelism every weight matrix W[K, H] of a row-parallel
+ * projection is split by rows over N ranks; rank r holds rows K_r and
+ * computes a partial p_r = x[:, K_r] . W[K_r, :], and the N partials are
+ * summed (an all-reduce) before the residual stream continues. Each layer
+ * has two such reconciliation points: after the sequence mixer's output
+ * projection and after the FFN down projection ("Interconnects e clusters",
+ * llmdeepdive.com lesson 9.9, section 01 · Conceito). The all-reduce is a
+ * ring: reduce-scatter then all-gather, 2(N-1)/N of the payload on each
+ * rank's wire (same section).
+ *
+ * On one GPU the N ranks are emulated as N fp32 partial buffers in device
+ * memory; the reduction sums them in the fixed order a ring would, so the
+ * result is bit-for-bit what a ring all-reduce with the same chunk
+ * convention produces.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named x, w, u, partials, residual, out, slots, hidden,
+ *    workspace are DEVICE pointers owned by the caller. The library keeps
+ *    none of them after the call returns and allocates no device memory.
+ *  - bf16 arrays are passed as `const void*` (IEEE bfloat16, 2 bytes each).
+ *  - Every device pointer must be 16-byte aligned (TP_ERR_ALIGNMENT).
+ *  - `stream` is a hipStream_t (NULL means the default stream). All device
+ *    work is enqueued on it asynchronously; results are valid once the
+ *    stream has been synchronised.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is enqueued. A failed launch returns TP_ERR_DEVICE.
+ *  - No C++ exception crosses this interface.
+ *  - A plan is a host object. After its setters have run it is read-only
+ *    and may be shared by threads and streams. Calls that share one
+ *    workspace must not overlap in time (they would race on it).
+ */
+#ifndef TP_DECODE_H
+#define TP_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_INVALID_ARG = 1, /* null pointer, bad size, N not dividing K or b*H */
+    TP_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle */
+    TP_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned */
+    TP_ERR_DEVICE = 4,      /* a HIP launch or runtime call failed */
+    TP_ERR_OOM = 5          /* host allocation of the plan failed */
+} tp_status;
+
+/* The two reconciliation points of a layer (lesson 9.9, Conceito). */
+typedef enum {
+    TP_POINT_ATTN_OUT = 0, /* sequence-mixer output projection, K = k_attn */
+    TP_POINT_FFN_DOWN = 1  /* FFN down projection, K = inter */
+} tp_point;
+
+/* Kernel family a point runs on. */
+typedef enum {
+    TP_PATH_VALU = 0, /* batch < 16: vector-ALU GEMV, 128-bit weight streaming */
+    TP_PATH_MFMA = 1  /* batch >= 16: bf16 matrix-core skinny GEMM */
+} tp_path;
+
+typedef struct tp_plan_s* tp_plan_t;
+
+typedef struct {
+    int64_t hidden;          /* H */
+    int64_t inter;           /* FFN intermediate size I */
+    int64_t k_attn;          /* K of the mixer output projection (default H) */
+    int32_t n_ranks;         /* N */
+    int32_t batch;           /* b, decode tokens per step */
+    int64_t k_rank[2];       /* K_r = K / N per point (index: tp_point) */
+    int32_t path[2];         /* tp_path per point */
+    int32_t splits[2];       /* split-K factor the projection kernels use */
+    int64_t chunk_elems;     /* C = b*H / N: ring chunk length */
+    int64_t wire_bytes_bf16; /* per rank per reduction, bf16 payload: 2(N-1)*C*2 */
+    int64_t wire_bytes_fp32; /* the same with the fp32 payload emulated here */
+    int64_t workspace_bytes; /* device workspace every entry point may use */
+    /* MoE share (zero unless tp_plan_set_moe was called) */
+    int32_t n_experts, top_k, ep, local_experts;
+    int64_t moe_inter;
+    int32_t max_tokens;
+} tp_plan_info;
+
+/*
+ * Create a plan for hidden size H, FFN intermediate size I, N ranks and a
+ * decode batch of b tokens. Host-only: touches no device.
+ * Errors: TP_ERR_INVALID_ARG if any size < 1, N does not divide I or H
+ * (the default k_attn), or N does not divide b*H (the ring needs N equal
+ * chunks; a model is never split along a boundary its dimensions do not
+ * divide, lesson 9.9, Conceito); TP_ERR_UNSUPPORTED if H is not a multiple
+ * of 8 (rows are streamed in 16-byte vectors) or b > 64;
+ * TP_ERR_OOM if the host allocation fails.
+ */
+tp_status tp_plan(int64_t hidden, int64_t inter, int32_t n_ranks, int32_t batch,
+                  tp_plan_t* out);
+
+/* Override K of the mixer output projection (e.g. 8192 -> 4096). Must be
+ * called before the plan is first used. TP_ERR_INVALID_ARG if k_attn < 1
+ * or N does not divide it. */
+tp_status tp_plan_set_attn_dim(tp_plan_t plan, int64_t k_attn);
+
+/* Enable the expert-parallel MoE share: n_experts experts of intermediate
+ * size moe_inter, top_k per token, spread over ep ranks (rank r owns the
+ * contiguous experts [r*E/ep, (r+1)*E/ep)), for up to max_tokens tokens
+ * ("Hosting Qwen on Blackwell", sections Prefillers, MoE Dispatch-Combine
+ * and Expert Parallel). Must be called before first use.
+ * TP_ERR_INVALID_ARG on sizes < 1, top_k > n_experts or ep not dividing
+ * n_experts; TP_ERR_UNSUPPORTED if top_k > 32 or max_tokens > 4096. */
+tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int32_t ep,
+                          int64_t moe_inter, int32_t max_tokens);
+
+/* Tuning knobs (advanced; the defaults are tuned for MI355X). Known keys:
+ * "splits_attn", "splits_ffn" (split-K factor, 0 = automatic),
+ * "valu_cols" (columns per VALU workgroup: 128, 256 or 512),
+ * "decode_mode" (0 = automatic, 1 = one launch per point,
+ *                2 = one persistent launch per step),
+ * "strip_variant" (0 = automatic, 1..3: kernel variant of the strip-packed
+ *                step: 7+1 waves x 10 vectors, 3+1 x 24, 7+1 x 20).
+ * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
+tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
+
+tp_status tp_plan_info_get(tp_plan_t plan, tp_plan_info* out);
+void tp_plan_destroy(tp_plan_t plan);
+const char* tp_status_str(tp_status status);
+
+/*
+ * Prepare a workspace of at least info.workspace_bytes device bytes for use
+ * with this plan (clears the completion counters the kernels use). Call it
+ * once after allocating the workspace; every later call leaves it ready for
+ * the next. The fill is a kernel, not a memset, so it may be captured into
+ * a HIP graph.
+ */
+tp_status tp_workspace_init(tp_plan_t plan, void* workspace, void* stream);
+
+/*
+ * Read the workspace's error word (synchronous: waits for the device).
+ * *flags = 0 after successful calls. Bit 0 is set if a decode step's
+ * bounded wait for the previous reconciliation point timed out (the step
+ * then drains without completing and its outputs are not valid).
+ * tp_workspace_init clears it.
+ */
+tp_status tp_workspace_status(tp_plan_t plan, const void* workspace, int32_t* flags);
+
+/*
+ * Row-parallel partial projection for one point (lesson 9.9, Conceito):
+ *     p[b, n] = sum_{k < K_r} x[b, k] * w[k, n]
+ * bf16 products accumulated in fp32 (split-K, fixed summation order, so
+ * repeated calls give identical bits).
+ *   x  bf16 [batch][K_r] row-major — the rank's slice of the activation
+ *   w  bf16 [K_r][hidden] row-major — the rank's rows of W
+ *   p  fp32 [batch][hidden] (output)
+ *   workspace: info.workspace_bytes, prepared by tp_workspace_init.
+ * Errors: TP_ERR_INVALID_ARG (null pointer, point not 0/1),
+ * TP_ERR_ALIGNMENT, TP_ERR_DEVICE.
+ */
+tp_status tp_rowparallel_partial(tp_plan_t plan, int32_t point, const void* x, const void* w,
+                                 float* p, void* workspace, void* stream);
+
+/*
+ * Ring-ordered all-reduce sum of the N partials plus the residual
+ * (lesson 9.9, Conceito; "Hosting Qwen on Blackwell", All-Reduce). The
+ * payload is the flattened [batch x hidden] vector cut into N chunks of
+ * C = b*H/N elements; chunk c is summed in rank order c, c+1, ..., c+N-1
+ * (mod N) — the order of a ring reduce-scatter started by rank c — one
+ * binary32 addition at a time, then the residual is added:
+ *     out[i] = (((p_c[i] + p_{c+1}[i]) + ...) + p_{c+N-1}[i]) + residual[i]
+ * Bit-exact: no fused or reassociated arithmetic, denormals kept.
+ *   partials fp32 [N][batch][hidden] rank-major
+ *   residual fp32 [batch][hidden]; out fp32 [batch][hidden] (may alias residual)
+ *   out_bf16 bf16 [batch][hidden] or NULL: out rounded to nearest-even bf16
+ */
+tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* residual,
+                         float* out, void* out_bf16, void* stream);
+
+/*
+ * One rank's share of a decode step over n_layers layers: for each layer,
+ * for the mixer output point and then the FFN down point, compute this
+ * rank's partial into its slot and set hidden <- ring_sum(slot) + hidden
+ * (lesson 9.9, Conceito: two reconciliation points per layer, each an
+ * all-reduce of one hidden vector per decoded token). Each point's
+ * activation slice is an input (the operations between the points are
+ * not part of this path), and each point's work starts only after the
+ * previous point's hidden state is complete.
+ *   x_attn bf16 [L][batch][k_attn/N]   w_o    bf16 [L][k_attn/N][hidden]
+ *   x_ffn  bf16 [L][batch][inter/N]    w_down bf16 [L][inter/N][hidden]
+ *   slots  fp32 [L][2][N][batch][hidden]: the other N-1 ranks' partials are
+ *          inputs; entry [l][point][rank] is overwritten with this rank's
+ *   hidden fp32 [batch][hidden], in/out (the residual stream)
+ * Results equal tp_rowparallel_partial followed by tp_ring_reduce at each
+ * point, bit for bit. For batch < 16 the whole step is one cooperative
+ * (persistent) launch; the workspace's error word (tp_workspace_status)
+ * reports a wait that timed out.
+ */
+tp_status tp_decode_layers(tp_plan_t plan, int32_t n_layers, int32_t rank,
+                           const void* x_attn, const void* w_o,
+                           const void* x_ffn, const void* w_down,
+                           float* slots, float* hidden, void* workspace, void* stream);
+
+/*
+ * Strip-packed weights for the decode step. A rank's weight slice
+ * W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is stored as
+ *     P[s][k][c] = W_r[k][8s + c],   s < H/8, k < K_r, c < 8
+ * i.e. H/8 strips of 8 columns, each strip's K_r rows of 16 bytes stored
+ * contiguously. Same bytes as the row-major slice, laid out so a
+ * workgroup streams a whole strip (all of K) in contiguous loads and needs
+ * no split of K over workgroups. Packing is done once, when the weights
+ * are loaded; it is not part of the decode step.
+ *
+ * tp_pack_weights: w bf16 [n_layers][K_r][hidden] -> w_packed bf16
+ * [n_layers][hidden/8][K_r][8] for `point`. w and w_packed must not overlap.
+ */
+tp_status tp_pack_weights(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w,
+                          void* w_packed, void* stream);
+
+/*
+ * The decode step of tp_decode_layers on strip-packed weights (same
+ * arguments and results, within the projections' fp tolerance; the ring
+ * stage is the same binary32 additions in the same order). One cooperative
+ * (persistent) launch: per point, each workgroup reduces whole strips over
+ * K in registers/LDS, forms the ring-order sum plus residual for them and
+ * signals; point j reads its activation only after point j-1's hidden
+ * state is complete. TP_ERR_UNSUPPORTED unless batch <= 8, n_ranks <= 8,
+ * K_r % 8 == 0 for both points and max(K_r) * batch * 2 <= 48 KiB.
+ */
+tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank,
+                                  const void* x_attn, const void* w_o_packed,
+                                  const void* x_ffn, const void* w_down_packed,
+                                  float* slots, float* hidden, void* workspace, void* stream);
+
+/*
+ * Top-k routing of decode tokens ("Hosting Qwen on Blackwell", Prefillers:
+ * each token goes to top_k of the experts). Per token: softmax over the
+ * experts' logits, the top_k experts by probability (ties to the lower
+ * index), their probabilities renormalised to sum to 1 (renorm != 0) or
+ * left as they are; listed in ascending expert order.
+ *   logits fp32 [tokens][n_experts]
+ *   sel_expert int32 [tokens][top_k], sel_weight fp32 [tokens][top_k] (outputs)
+ * tokens <= max_tokens of tp_plan_set_moe. The expert choice compares the
+ * fp32 logits directly, so it is exact.
+ */
+tp_status tp_moe_route(tp_plan_t plan, const float* logits, int32_t tokens, int32_t renorm,
+                       int32_t* sel_expert, float* sel_weight, void* stream);
+
+/*
+ * Expert-parallel down projection and local weighted combine for rank
+ * `rank` ("Hosting Qwen on Blackwell", MoE Dispatch-Combine and Expert
+ * Parallel: the combine first accumulates, per token, the contributions of
+ * the experts on this rank, weighted by the routing weights; the all-reduce
+ * over ranks follows):
+ *     part[t, :] = sum over s with sel_expert[t,s] on this rank, in
+ *                  ascending expert order, of sel_weight[t,s] * (u[t,s,:] . W_e)
+ *   sel_expert int32 [tokens][top_k], sel_weight fp32 [tokens][top_k]
+ *   u       bf16 [tokens][top_k][moe_inter]: one activation per selection
+ *   w_local bf16 [E/ep][moe_inter][hidden]: this rank's experts, in order
+ *   part    fp32 [tokens][hidden] (output)
+ * Experts that no token selected are not read.
+ */
+tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
+                         const float* sel_weight, int32_t tokens, const void* u,
+                         const void* w_local, float* part, void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_DECODE_H */

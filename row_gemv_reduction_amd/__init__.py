@@ -1,2 +1,12 @@
-"""MI355X-native row-parallel decode projections and ring-ordered reduction."""
+"""MI355X-native row-parallel decode projections and ring-ordered reduction.
+
+The compute path is libtpdecode.so (HIP, gfx950); this package holds its
+build script, a thin ctypes binding with the C interface's names, the seeded
+input generators and the workload shapes. Nothing here computes on the CPU.
+"""
 from . import synth, workloads  # noqa: F401
+from .binding import (  # noqa: F401
+    TP_PATH_MFMA, TP_PATH_VALU, TP_POINT_ATTN_OUT, TP_POINT_FFN_DOWN, Plan, TPError,
+    tp_decode_layers, tp_decode_layers_packed, tp_moe_partial, tp_pack_weights, tp_moe_route, tp_plan, tp_ring_reduce,
+    tp_rowparallel_partial, tp_workspace_init, tp_workspace_status,
+)

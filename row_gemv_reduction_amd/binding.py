@@ -1,0 +1,285 @@
+"""ctypes binding of libtpdecode.so (the C interface in include/tp_decode.h).
+
+Argument marshalling only: every function checks dtype, shape, contiguity
+and device of the torch tensors it is given, then passes raw device
+pointers and the current HIP stream to the library. All arithmetic runs in
+the library's HIP kernels. Loading fails loudly if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtpdecode.so")
+
+TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_ALIGNMENT, TP_ERR_DEVICE, TP_ERR_OOM = range(6)
+TP_POINT_ATTN_OUT, TP_POINT_FFN_DOWN = 0, 1
+TP_PATH_VALU, TP_PATH_MFMA = 0, 1
+
+
+class TPError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib().tp_status_str(status).decode() if _LIB is not None else str(status)
+        super().__init__("%s failed: %s (status %d)" % (where, msg, status))
+
+
+class tp_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64), ("k_attn", ctypes.c_int64),
+        ("n_ranks", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("k_rank", ctypes.c_int64 * 2), ("path", ctypes.c_int32 * 2),
+        ("splits", ctypes.c_int32 * 2),
+        ("chunk_elems", ctypes.c_int64), ("wire_bytes_bf16", ctypes.c_int64),
+        ("wire_bytes_fp32", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+        ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("ep", ctypes.c_int32),
+        ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
+        ("max_tokens", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "tp_plan": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.POINTER(ctypes.c_void_p)]),
+    "tp_plan_set_attn_dim": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "tp_plan_set_moe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
+    "tp_plan_tune": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int64]),
+    "tp_plan_info_get": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(tp_plan_info)]),
+    "tp_plan_destroy": (None, [ctypes.c_void_p]),
+    "tp_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "tp_workspace_init": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tp_workspace_status": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_int32)]),
+    "tp_rowparallel_partial": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "tp_ring_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tp_decode_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                         + [ctypes.c_void_p] * 8),
+    "tp_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tp_decode_layers_packed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                                + [ctypes.c_void_p] * 8),
+    "tp_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]),
+    "tp_moe_partial": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+}
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libtpdecode.so is not built (%s); run `python -m row_gemv_reduction_amd.build` "
+                "or __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status, where):
+    if status != TP_OK:
+        raise TPError(status, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """Owns a tp_plan_t. Sizes follow tp_plan(); optional k_attn, MoE share
+    and tuning knobs are applied before first use."""
+
+    def __init__(self, hidden, inter, n_ranks, batch, k_attn=None, moe=None, tune=None):
+        h = ctypes.c_void_p()
+        _check(_lib().tp_plan(hidden, inter, n_ranks, batch, ctypes.byref(h)), "tp_plan")
+        self._h = h
+        try:
+            if k_attn is not None:
+                _check(_lib().tp_plan_set_attn_dim(h, k_attn), "tp_plan_set_attn_dim")
+            if moe is not None:
+                _check(_lib().tp_plan_set_moe(h, moe["n_experts"], moe["top_k"], moe["ep"],
+                                              moe["moe_inter"], moe["max_tokens"]),
+                       "tp_plan_set_moe")
+            for k, v in (tune or {}).items():
+                _check(_lib().tp_plan_tune(h, k.encode(), int(v)), "tp_plan_tune(%s)" % k)
+        except Exception:
+            self.close()
+            raise
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan is closed")
+        return self._h
+
+    def info(self) -> dict:
+        i = tp_plan_info()
+        _check(_lib().tp_plan_info_get(self.handle, ctypes.byref(i)), "tp_plan_info_get")
+        d = {}
+        for name, _ in tp_plan_info._fields_:
+            v = getattr(i, name)
+            d[name] = list(v) if hasattr(v, "__len__") else v
+        return d
+
+    def new_workspace(self, device="cuda"):
+        """Allocate (torch) and prepare a workspace for this plan."""
+        nbytes = max(self.info()["workspace_bytes"], 256)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        tp_workspace_init(self, ws)
+        return ws
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and _LIB is not None:
+            _LIB.tp_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tp_plan(hidden, inter, n_ranks, batch, **kw) -> Plan:
+    return Plan(hidden, inter, n_ranks, batch, **kw)
+
+
+def tp_workspace_init(plan: Plan, workspace):
+    _check(_lib().tp_workspace_init(plan.handle, _dev(workspace, "workspace", torch.uint8),
+                                    _stream()), "tp_workspace_init")
+
+
+def tp_workspace_status(plan: Plan, workspace) -> int:
+    flags = ctypes.c_int32(0)
+    _check(_lib().tp_workspace_status(plan.handle, _dev(workspace, "workspace", torch.uint8),
+                                      ctypes.byref(flags)), "tp_workspace_status")
+    return flags.value
+
+
+def tp_rowparallel_partial(plan: Plan, point, x, w, p, workspace):
+    i = plan.info()
+    b, H, kr = i["batch"], i["hidden"], i["k_rank"][point] if point in (0, 1) else -1
+    if point not in (0, 1):
+        raise ValueError("point must be 0 (attention out) or 1 (FFN down)")
+    args = (_dev(x, "x", torch.bfloat16, (b, kr)), _dev(w, "w", torch.bfloat16, (kr, H)),
+            _dev(p, "p", torch.float32, (b, H)), _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_rowparallel_partial(plan.handle, point, *args, _stream()),
+           "tp_rowparallel_partial")
+
+
+def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):
+    i = plan.info()
+    n, b, H = i["n_ranks"], i["batch"], i["hidden"]
+    ob = None if out_bf16 is None else _dev(out_bf16, "out_bf16", torch.bfloat16, (b, H))
+    _check(_lib().tp_ring_reduce(plan.handle, _dev(partials, "partials", torch.float32, (n, b, H)),
+                                 _dev(residual, "residual", torch.float32, (b, H)),
+                                 _dev(out, "out", torch.float32, (b, H)), ob, _stream()),
+           "tp_ring_reduce")
+
+
+def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slots, hidden,
+                     workspace):
+    i = plan.info()
+    n, b, H = i["n_ranks"], i["batch"], i["hidden"]
+    ka, ki = i["k_rank"]
+    L = n_layers
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
+            _dev(w_o, "w_o", torch.bfloat16, (L, ka, H)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
+            _dev(w_down, "w_down", torch.bfloat16, (L, ki, H)),
+            _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
+            _dev(hidden, "hidden", torch.float32, (b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_decode_layers(plan.handle, L, rank, *args, _stream()), "tp_decode_layers")
+
+
+def tp_pack_weights(plan: Plan, point, w, w_packed):
+    """Strip-pack a stack of row-major weight slices [L, K_r, H] -> [L, H/8, K_r, 8]."""
+    i = plan.info()
+    kr, H = i["k_rank"][point] if point in (0, 1) else -1, i["hidden"]
+    if point not in (0, 1):
+        raise ValueError("point must be 0 or 1")
+    L = w.shape[0]
+    _check(_lib().tp_pack_weights(plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, kr, H)),
+                                  _dev(w_packed, "w_packed", torch.bfloat16, (L, H // 8, kr, 8)),
+                                  _stream()), "tp_pack_weights")
+
+
+def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
+                            slots, hidden, workspace):
+    i = plan.info()
+    n, b, H = i["n_ranks"], i["batch"], i["hidden"]
+    ka, ki = i["k_rank"]
+    L = n_layers
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
+            _dev(w_o_packed, "w_o_packed", torch.bfloat16, (L, H // 8, ka, 8)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
+            _dev(w_down_packed, "w_down_packed", torch.bfloat16, (L, H // 8, ki, 8)),
+            _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
+            _dev(hidden, "hidden", torch.float32, (b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_decode_layers_packed(plan.handle, L, rank, *args, _stream()),
+           "tp_decode_layers_packed")
+
+
+def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):
+    i = plan.info()
+    t = logits.shape[0]
+    k, e = i["top_k"], i["n_experts"]
+    _check(_lib().tp_moe_route(plan.handle, _dev(logits, "logits", torch.float32, (t, e)), t,
+                               1 if renorm else 0,
+                               _dev(sel_expert, "sel_expert", torch.int32, (t, k)),
+                               _dev(sel_weight, "sel_weight", torch.float32, (t, k)), _stream()),
+           "tp_moe_route")
+
+
+def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_local, part, workspace):
+    i = plan.info()
+    t = sel_expert.shape[0]
+    k, le, mi, H = i["top_k"], i["local_experts"], i["moe_inter"], i["hidden"]
+    args = (_dev(sel_expert, "sel_expert", torch.int32, (t, k)),
+            _dev(sel_weight, "sel_weight", torch.float32, (t, k)))
+    rest = (_dev(u, "u", torch.bfloat16, (t, k, mi)),
+            _dev(w_local, "w_local", torch.bfloat16, (le, mi, H)),
+            _dev(part, "part", torch.float32, (t, H)), _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_moe_partial(plan.handle, rank, *args, t, *rest, _stream()), "tp_moe_partial")

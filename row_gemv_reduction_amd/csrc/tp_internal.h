@@ -1,0 +1,93 @@
+// Internal plan representation shared by the host plan code and the HIP
+// launchers. Not part of the public interface.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/tp_decode.h"
+
+// Target device: MI355X, 256 compute units in 8 XCDs of 32.
+constexpr int kTargetCUs = 256;
+constexpr int kXCDs = 8;
+
+// Workspace layout: [column-tile counters | step sync words][split-K partials][MoE scratch]
+constexpr int64_t kCounterBytes = 128 * 1024;
+constexpr int kCounterStride = 16;            // one counter per 64-byte line
+constexpr int kMaxCounters = 1024;            // column-tile arrival counters (64 KiB)
+constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, error
+constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
+// Tree barrier of the strip step (word offsets in the sync area; every
+// counter and release word on its own 256-byte line)
+constexpr int kTreeGroups = 32;
+constexpr int kTreeLine = 64;                         // words per line
+constexpr int kTreeTop = 64;
+constexpr int kTreeGroupBase = 128;                   // + q * kTreeLine
+constexpr int kTreeReleaseBase = kTreeGroupBase + kTreeGroups * kTreeLine;  // + q * kTreeLine
+
+// VALU GEMV geometry limits
+constexpr int kValuWaves = 4;        // waves per workgroup
+constexpr int kValuMaxRows = 512;    // rows of x staged in LDS per workgroup
+constexpr int kValuXsFloats = 4096;  // LDS floats for the staged x slice
+constexpr int kValuMaxBatch = 15;
+constexpr int kValuLoadsPerLane = 24;  // a tile's weights are loaded into registers at once
+
+// Rows of one VALU split: every lane holds all of its rows' 16-byte weight
+// vectors in registers (kValuLoadsPerLane), and x[rows][B] fits the LDS
+// staging buffer.
+constexpr int valu_rows_max(int batch, int cols) {
+    int r = kValuLoadsPerLane * kValuWaves * (64 / (cols / 8));
+    int x = kValuXsFloats / batch;
+    r = r > x ? x : r;
+    r = r > kValuMaxRows ? kValuMaxRows : r;
+    return r - r % 16;
+}
+constexpr int kMfmaMinBatch = 16;
+constexpr int kMfmaMaxBatch = 64;
+constexpr int kMfmaCols = 128;       // columns per MFMA workgroup
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaKStep = 32;       // k rows per MFMA step
+constexpr int kMfmaMaxRows = 1024;   // rows per MFMA split (multiple of 128)
+
+// Strip-packed decode step
+constexpr int kStripComputeWaves = 8;       // compute waves per workgroup (+1 control wave)
+constexpr int kStripMaxBatch = 8;
+constexpr int kStripMaxPerWg = 4;           // strips (of 8 columns) per workgroup
+constexpr int64_t kStripMaxXsBytes = 48 * 1024;  // LDS for one point's x: K * B * 2
+
+// MoE
+constexpr int kMoeMaxTopK = 32;
+constexpr int kMoeMaxTokens = 4096;
+
+struct tp_plan_s {
+    int64_t hidden = 0, inter = 0, k_attn = 0;
+    int32_t n_ranks = 0, batch = 0;
+    // tuning (0 = automatic)
+    int32_t splits_user[2] = {0, 0};
+    int32_t valu_cols = 0;
+    int32_t decode_mode = 0;
+    int32_t target_wgs = 0;
+    int32_t strip_variant = 0;  // 0 = automatic, else 1-based index of the strip kernel variant
+    // MoE
+    int32_t n_experts = 0, top_k = 0, ep = 0;
+    int64_t moe_inter = 0;
+    int32_t max_tokens = 0;
+};
+
+// Geometry of one point's projection launch, derived from the plan.
+struct PointGeom {
+    int64_t k_r;        // rows of the rank's slice
+    int32_t path;       // tp_path
+    int32_t cols;       // columns per workgroup tile
+    int32_t col_tiles;  // ceil(H / cols)
+    int32_t splits;     // split-K factor S
+    int32_t rows;       // rows per split (last split may be shorter)
+    int32_t grid;       // col_tiles * splits
+};
+
+PointGeom tp_point_geom(const tp_plan_s* p, int point);
+PointGeom tp_geom_for(const tp_plan_s* p, int64_t k_r, int32_t batch, int32_t splits_user);
+int64_t tp_workspace_bytes(const tp_plan_s* p);
+int64_t tp_ws_partials_offset();
+int64_t tp_ws_moe_offset(const tp_plan_s* p);
+int tp_decode_mode(const tp_plan_s* p);
+int tp_strip_loads(const tp_plan_s* p);  // nonzero if the strip-packed step can run the plan

@@ -1,0 +1,702 @@
+// HIP kernels for gfx950 (MI355X) and the entry points that launch them.
+//
+// Path ("Interconnects e clusters", llmdeepdive.com lesson 9.9, section
+// 01 · Conceito): at each of a layer's two reconciliation points the rank
+// computes its row-parallel partial p_r = x[:, K_r] . W[K_r, :] and the
+// partials of all ranks are summed, ring-style, before the residual stream
+// continues. Decode projections are bound by streaming the weights from HBM
+// ("Hosting Qwen on Blackwell", section Decoders), so the kernels are built
+// around moving each weight byte once, in 16-byte coalesced nontemporal
+// loads, with enough loads in flight to cover HBM latency on 256 CUs.
+//
+// Kernels:
+//   valu_gemv       batch 1..15, one projection. A workgroup owns a tile of
+//                   COLS columns x `rows` rows (split-K). Each lane loads
+//                   all of its rows' 16-byte weight vectors (8 columns each)
+//                   into registers at once, then multiplies them by x
+//                   staged as fp32 in LDS, accumulating in fp32.
+//   decode_step     batch 1..15, the whole decode step in one cooperative
+//                   (persistent) launch: workgroups walk the step's tiles in
+//                   point order. A workgroup issues the weight loads of its
+//                   next tile before it waits for the previous point's
+//                   hidden state to complete, so the weight stream of point
+//                   j+1 overlaps the reduction of point j; the launch gap
+//                   between points disappears.
+//   mfma_gemm       batch 16..64: the tile streamed as 8 rows x 16 bytes per
+//                   lane, transposed in registers with v_perm into k-major
+//                   bf16x8 operands, multiplied on the bf16 matrix cores
+//                   (v_mfma_f32_16x16x32_bf16).
+//   ring_reduce     the stand-alone ring-order sum + residual.
+//
+// Split-K fixup: every workgroup publishes its fp32 partial tile; the last
+// workgroup of a column tile (arrival counter) sums the splits in split
+// order, so the result does not depend on scheduling. With the ring
+// epilogue (decode) it then sums the N ranks' partials in ring order and
+// adds the residual.
+//
+// Cross-workgroup visibility inside a launch: see tp_device.h.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tp_device.h"
+#include "tp_internal.h"
+
+namespace {
+
+using namespace tpdev;
+
+// ------------------------------------------------------------ epilogue --
+
+struct Epilogue {
+    float* p;                 // final partial [B][H] (the rank's slot when fused)
+    float* ws_part;           // split partials [S][B][H]
+    uint32_t* counters;       // one per column tile, stride kCounterStride
+    int32_t splits;
+    // ring epilogue (decode); ring_slots == nullptr disables it
+    const float* ring_slots;  // this point's [N][B][H]
+    float* hidden;            // [B][H] residual stream, updated in place
+    int32_t n_ranks, rank;
+    int64_t chunk;            // B*H / N
+};
+
+// Publish this split's partial tile [batch][COLS] (LDS) and find out whether
+// this workgroup arrived last for its column tile. Returns true for the
+// last arrival (and always when there is a single split).
+template <int COLS, int NT>
+__device__ bool publish_split(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
+                              int sp, int tid, int* s_flag) {
+    if (e.splits == 1) return true;
+    const int64_t n0 = (int64_t)ct * COLS;
+    for (int idx = tid; idx < batch * COLS; idx += NT) {
+        int bb = idx / COLS, c = idx - bb * COLS;
+        int64_t n = n0 + c;
+        if (n < H) st_dev(e.ws_part + ((int64_t)sp * batch + bb) * H + n, tile[idx]);
+    }
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t prev = add_dev_u32(&e.counters[ct * kCounterStride], 1u);
+        *s_flag = prev == (uint32_t)(e.splits - 1);
+    }
+    __syncthreads();
+    compiler_barrier();
+    return *s_flag != 0;
+}
+
+// Last arrival: sum the splits in split order, write the partial and, with
+// the ring epilogue, the ring-order sum + residual into the hidden state.
+template <int COLS, int NT>
+__device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
+                           int tid) {
+    const int64_t n0 = (int64_t)ct * COLS;
+    const int64_t len = (int64_t)batch * H;
+    for (int idx = tid; idx < batch * COLS; idx += NT) {
+        int bb = idx / COLS, c = idx - bb * COLS;
+        int64_t n = n0 + c;
+        if (n >= H) continue;
+        const int64_t i = (int64_t)bb * H + n;
+        // the residual load goes out with the split loads (one round trip)
+        const float res = e.ring_slots ? ld_dev(e.hidden + i) : 0.f;
+        const float v = e.splits > 1 ? sum_splits(e.ws_part + i, e.splits, len) : tile[idx];
+        e.p[i] = v;
+        if (e.ring_slots)
+            st_dev(e.hidden + i, ring_element(e.ring_slots, len, i, e.chunk, e.n_ranks, e.rank, v, res));
+    }
+    if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
+    wait_mem();
+}
+
+// ------------------------------------------------------------ VALU tile --
+
+template <int B>
+__device__ __forceinline__ void fma_row(float (&acc)[B][8], const u32x4_t& wv, const float* xr) {
+    float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                   bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+        float xv = xr[bb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[bb][j] = __builtin_fmaf(xv, wf[j], acc[bb][j]);
+    }
+}
+
+template <int B, int COLS>
+struct ValuShared {
+    static constexpr int XS = valu_rows_max(B, COLS) * B;
+    float xs[XS];
+    float red[kValuWaves * COLS];
+    float tile[B * COLS];
+    int flag;
+};
+
+// One VALU tile: columns [ct*COLS, +COLS) x rows [k0, k0+nr) of W[K][H],
+// x [B][K]. `before_compute` runs after the weight loads are issued and
+// before x is read (the decode step waits there for the previous point).
+// Leaves the workgroup's partial in sh.tile. Returns false if
+// before_compute asked to abandon the tile.
+template <int B, int COLS, typename Hook>
+__device__ bool valu_tile(ValuShared<B, COLS>& sh, const uint16_t* x, const uint16_t* w,
+                          int64_t K, int64_t H, int64_t k0, int nr, int ct, Hook before_compute) {
+    constexpr int NT = kValuWaves * 64;
+    constexpr int LPR = COLS / 8;   // lanes per row segment
+    constexpr int RPW = 64 / LPR;   // row groups per wave
+    constexpr int RSTEP = kValuWaves * RPW;
+    constexpr int NI = kValuLoadsPerLane;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = (int64_t)ct * COLS + (lane % LPR) * 8;
+    const bool col_ok = n < H;
+    const int r0 = wave * RPW + lane / LPR;
+
+    // every weight vector of this lane's rows, in flight at once
+    u32x4_t wv[NI];
+    const uint16_t* wp = w + (k0 + r0) * H + n;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if (col_ok && r0 + i * RSTEP < nr) wv[i] = load_stream16(wp + (int64_t)i * RSTEP * H);
+        else wv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    if (!before_compute()) return false;
+
+    for (int i = tid; i < nr * B; i += NT) {
+        int bb = i / nr, r = i - bb * nr;
+        sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
+    }
+    __syncthreads();
+
+    float acc[B][8];
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[bb][j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        int r = r0 + i * RSTEP;
+        if (r < nr) fma_row<B>(acc, wv[i], &sh.xs[r * B]);
+    }
+
+    // Sum the wave's row groups (lanes that share columns); an xor pair
+    // adds the same two values, so both lanes hold identical bits.
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[bb][j] += __shfl_xor(acc[bb][j], m);
+
+    // Sum the waves in wave order, one batch row at a time.
+    for (int bb = 0; bb < B; ++bb) {
+        if (lane < LPR) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sh.red[wave * COLS + lane * 8 + j] = acc[bb][j];
+        }
+        __syncthreads();
+        for (int c = tid; c < COLS; c += NT) {
+            float s = sh.red[c];
+#pragma unroll
+            for (int wq = 1; wq < kValuWaves; ++wq) s += sh.red[wq * COLS + c];
+            sh.tile[bb * COLS + c] = s;
+        }
+        __syncthreads();
+    }
+    return true;
+}
+
+struct GemvArgs {
+    const uint16_t* x;  // [B][K]
+    const uint16_t* w;  // [K][H]
+    int64_t K, H;
+    int32_t rows;       // rows per split
+    int32_t col_tiles;
+    Epilogue epi;
+};
+
+template <int B, int COLS>
+__global__ __launch_bounds__(kValuWaves * 64) void valu_gemv(GemvArgs a) {
+    constexpr int NT = kValuWaves * 64;
+    __shared__ ValuShared<B, COLS> sh;
+    const int ct = blockIdx.x % a.col_tiles;
+    const int sp = blockIdx.x / a.col_tiles;
+    const int64_t k0 = (int64_t)sp * a.rows;
+    const int nr = (int)(a.K - k0 < a.rows ? a.K - k0 : a.rows);
+    valu_tile<B, COLS>(sh, a.x, a.w, a.K, a.H, k0, nr, ct, [] { return true; });
+    if (publish_split<COLS, NT>(a.epi, sh.tile, B, a.H, ct, sp, threadIdx.x, &sh.flag))
+        fixup_tile<COLS, NT>(a.epi, sh.tile, B, a.H, ct, threadIdx.x);
+}
+
+// ------------------------------------------------------- decode step --
+
+struct StepArgs {
+    const uint16_t* x[2];   // x_attn [L][B][K0], x_ffn [L][B][K1]
+    const uint16_t* w[2];   // w_o [L][K0][H], w_down [L][K1][H]
+    float* slots;           // [L][2][N][B][H]
+    float* hidden;          // [B][H]
+    float* ws_part;
+    uint32_t* counters;     // column-tile arrival counters
+    uint32_t* sync;         // done / exit / error words
+    int64_t H, K[2];
+    int32_t rows[2], splits[2], tiles[2];
+    int32_t col_tiles, layers, n_ranks, rank;
+    int64_t chunk;
+    uint32_t spin_limit;
+};
+
+template <int B, int COLS>
+__global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
+    constexpr int NT = kValuWaves * 64;
+    __shared__ ValuShared<B, COLS> sh;
+    const int tid = threadIdx.x;
+    uint32_t* done = a.sync + kSyncDone;
+    uint32_t* err = a.sync + kSyncErr;
+    const int64_t len = (int64_t)B * a.H;
+    const int per_layer = a.tiles[0] + a.tiles[1];
+    const int64_t total = (int64_t)a.layers * per_layer;
+
+    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const int l = (int)(q / per_layer);
+        const int rem = (int)(q - (int64_t)l * per_layer);
+        const int pt = rem >= a.tiles[0];
+        const int t = pt ? rem - a.tiles[0] : rem;
+        const int ct = t % a.col_tiles, sp = t / a.col_tiles;
+        const int j = 2 * l + pt;  // point index in the step
+        const int64_t K = a.K[pt];
+        const int64_t k0 = (int64_t)sp * a.rows[pt];
+        const int nr = (int)(K - k0 < a.rows[pt] ? K - k0 : a.rows[pt]);
+        const uint16_t* x = a.x[pt] + (int64_t)l * B * K;
+        const uint16_t* w = a.w[pt] + (int64_t)l * K * a.H;
+
+        __syncthreads();  // LDS of the previous tile is no longer read
+        // Point j reads its activation only once point j-1's hidden state is
+        // complete (all column tiles of j-1 reduced).
+        auto wait_prev = [&]() -> bool {
+            if (tid == 0) sh.flag = wait_at_least(done, (uint32_t)j * a.col_tiles, err, a.spin_limit);
+            __syncthreads();
+            compiler_barrier();
+            return sh.flag != 0;
+        };
+        if (!valu_tile<B, COLS>(sh, x, w, K, a.H, k0, nr, ct, wait_prev)) continue;
+
+        float* slot = a.slots + (int64_t)j * a.n_ranks * len;
+        Epilogue e;
+        e.p = slot + (int64_t)a.rank * len;
+        e.ws_part = a.ws_part;
+        e.counters = a.counters;
+        e.splits = a.splits[pt];
+        e.ring_slots = slot;
+        e.hidden = a.hidden;
+        e.n_ranks = a.n_ranks;
+        e.rank = a.rank;
+        e.chunk = a.chunk;
+        if (publish_split<COLS, NT>(e, sh.tile, B, a.H, ct, sp, tid, &sh.flag)) {
+            fixup_tile<COLS, NT>(e, sh.tile, B, a.H, ct, tid);
+            __syncthreads();
+            if (tid == 0) add_dev_u32(done, 1u);
+        }
+    }
+    // The last workgroup to leave resets the step's sync words for the next
+    // launch (no workgroup waits on them any more).
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t prev = add_dev_u32(a.sync + kSyncExit, 1u);
+        if (prev == gridDim.x - 1) {
+            st_dev_u32(done, 0u);
+            st_dev_u32(a.sync + kSyncExit, 0u);
+        }
+    }
+}
+
+// ------------------------------------------------------------ MFMA GEMM --
+
+// Select the low (even column) or high (odd column) bf16 of two row words
+// into one k-major pair: result = {row0 half, row1 half}.
+__device__ __forceinline__ uint32_t pair_rows(uint32_t row0, uint32_t row1, bool high) {
+    return __builtin_amdgcn_perm(row1, row0, high ? 0x07060302u : 0x05040100u);
+}
+
+template <int BT>  // batch tiles of 16 rows
+__global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int batch) {
+    constexpr int NT = kMfmaWaves * 64;
+    constexpr int COLS = kMfmaCols;
+    __shared__ float red[kMfmaWaves * 16 * COLS];  // 32 KB
+    __shared__ float tile[BT * 16 * COLS];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ct = blockIdx.x % a.col_tiles;
+    const int sp = blockIdx.x / a.col_tiles;
+    const int64_t k0 = (int64_t)sp * a.rows;
+    const int rows = (int)(a.K - k0 < a.rows ? a.K - k0 : a.rows);
+    const int g = lane >> 4;   // k group: rows 8g .. 8g+7 of a 32-row step
+    const int i = lane & 15;   // column group: columns 8i .. 8i+7 of the tile
+    const int64_t n = (int64_t)ct * COLS + i * 8;
+    const bool col_ok = n < a.H;
+    const bool x_vec = (a.K & 7) == 0;
+
+    floatx4_t acc[BT][8];
+#pragma unroll
+    for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[bt][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int step = wave * 32; step < rows; step += kMfmaWaves * 32) {
+        const int64_t kr = k0 + step + 8 * g;  // first of this lane's 8 rows
+        u32x4_t wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bool ok = col_ok && (step + 8 * g + j) < rows;
+            wv[j] = ok ? load_stream16(a.w + (kr + j) * a.H + n) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        // A operands: x[bt*16 + i][kr .. kr+7]
+        bf16x8_t xa[BT];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt) {
+            int brow = bt * 16 + i;
+            u32x4_t xv = u32x4_t{0u, 0u, 0u, 0u};
+            if (brow < batch) {
+                const uint16_t* xp = a.x + (int64_t)brow * a.K + kr;
+                int left = rows - (step + 8 * g);
+                if (x_vec && left >= 8) {
+                    xv = *reinterpret_cast<const u32x4_t*>(xp);
+                } else {
+                    uint16_t t[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t[j] = j < left ? xp[j] : (uint16_t)0;
+                    xv.x = t[0] | ((uint32_t)t[1] << 16);
+                    xv.y = t[2] | ((uint32_t)t[3] << 16);
+                    xv.z = t[4] | ((uint32_t)t[5] << 16);
+                    xv.w = t[6] | ((uint32_t)t[7] << 16);
+                }
+            }
+            xa[bt] = __builtin_bit_cast(bf16x8_t, xv);
+        }
+        // B operands: for each of the lane's 8 columns c, its 8 rows as k-major bf16x8
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const bool hi = c & 1;
+            uint32_t w0[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w0[j] = wv[j][c >> 1];
+            u32x4_t bw;
+            bw.x = pair_rows(w0[0], w0[1], hi);
+            bw.y = pair_rows(w0[2], w0[3], hi);
+            bw.z = pair_rows(w0[4], w0[5], hi);
+            bw.w = pair_rows(w0[6], w0[7], hi);
+            bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt)
+                acc[bt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[bt], bop, acc[bt][c], 0, 0, 0);
+        }
+    }
+
+    // D layout of a 16x16 fp32 MFMA tile: lane holds rows 4*(lane/16)+q,
+    // column lane%16. Here rows are batch rows and MFMA column i' is
+    // tile column 8*i' + c.
+    for (int bt = 0; bt < BT; ++bt) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                red[(wave * 16 + 4 * g + q) * COLS + i * 8 + c] = acc[bt][c][q];
+        __syncthreads();
+        for (int idx = tid; idx < 16 * COLS; idx += NT) {
+            float s = red[idx];
+#pragma unroll
+            for (int wq = 1; wq < kMfmaWaves; ++wq) s += red[wq * 16 * COLS + idx];
+            tile[bt * 16 * COLS + idx] = s;
+        }
+        __syncthreads();
+    }
+    if (publish_split<COLS, NT>(a.epi, tile, batch, a.H, ct, sp, tid, &s_flag))
+        fixup_tile<COLS, NT>(a.epi, tile, batch, a.H, ct, tid);
+}
+
+// ----------------------------------------------------------- ring reduce --
+
+__global__ void ring_reduce_kernel(const float* partials, const float* residual, float* out,
+                                   uint16_t* out_bf16, int64_t len, int64_t chunk, int n_ranks) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= len) return;
+    float o = ring_element(partials, len, i, chunk, n_ranks, -1, 0.f, residual[i]);
+    out[i] = o;
+    if (out_bf16) out_bf16[i] = f32_to_bf16_rne(o);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------- dispatch --
+
+typedef void (*valu_fn)(GemvArgs);
+typedef void (*step_fn)(StepArgs);
+
+template <int COLS>
+valu_fn valu_kernel_for(int b) {
+    switch (b) {
+        case 1: return valu_gemv<1, COLS>;   case 2: return valu_gemv<2, COLS>;
+        case 3: return valu_gemv<3, COLS>;   case 4: return valu_gemv<4, COLS>;
+        case 5: return valu_gemv<5, COLS>;   case 6: return valu_gemv<6, COLS>;
+        case 7: return valu_gemv<7, COLS>;   case 8: return valu_gemv<8, COLS>;
+        case 9: return valu_gemv<9, COLS>;   case 10: return valu_gemv<10, COLS>;
+        case 11: return valu_gemv<11, COLS>; case 12: return valu_gemv<12, COLS>;
+        case 13: return valu_gemv<13, COLS>; case 14: return valu_gemv<14, COLS>;
+        case 15: return valu_gemv<15, COLS>;
+    }
+    return nullptr;
+}
+
+template <int COLS>
+step_fn step_kernel_for(int b) {
+    switch (b) {
+        case 1: return decode_step<1, COLS>;   case 2: return decode_step<2, COLS>;
+        case 3: return decode_step<3, COLS>;   case 4: return decode_step<4, COLS>;
+        case 5: return decode_step<5, COLS>;   case 6: return decode_step<6, COLS>;
+        case 7: return decode_step<7, COLS>;   case 8: return decode_step<8, COLS>;
+        case 9: return decode_step<9, COLS>;   case 10: return decode_step<10, COLS>;
+        case 11: return decode_step<11, COLS>; case 12: return decode_step<12, COLS>;
+        case 13: return decode_step<13, COLS>; case 14: return decode_step<14, COLS>;
+        case 15: return decode_step<15, COLS>;
+    }
+    return nullptr;
+}
+
+valu_fn valu_kernel(int b, int cols) {
+    switch (cols) {
+        case 128: return valu_kernel_for<128>(b);
+        case 256: return valu_kernel_for<256>(b);
+        case 512: return valu_kernel_for<512>(b);
+    }
+    return nullptr;
+}
+
+step_fn step_kernel(int b, int cols) {
+    switch (cols) {
+        case 128: return step_kernel_for<128>(b);
+        case 256: return step_kernel_for<256>(b);
+        case 512: return step_kernel_for<512>(b);
+    }
+    return nullptr;
+}
+
+typedef void (*mfma_fn)(GemvArgs, int);
+mfma_fn mfma_kernel(int b) {
+    switch ((b + 15) / 16) {
+        case 1: return mfma_gemm<1>;
+        case 2: return mfma_gemm<2>;
+        case 3: return mfma_gemm<3>;
+        case 4: return mfma_gemm<4>;
+    }
+    return nullptr;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+uint32_t* ws_counters(void* ws) { return reinterpret_cast<uint32_t*>(ws); }
+uint32_t* ws_sync(void* ws) {
+    return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + kSyncOffset);
+}
+float* ws_partials(void* ws) {
+    return reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + tp_ws_partials_offset());
+}
+
+// Launch one projection (and its optional ring epilogue).
+tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, const void* x,
+                            const void* w, const Epilogue& epi, hipStream_t st) {
+    GemvArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.w = static_cast<const uint16_t*>(w);
+    a.K = g.k_r;
+    a.H = p->hidden;
+    a.rows = g.rows;
+    a.col_tiles = g.col_tiles;
+    a.epi = epi;
+    // host-side checks of what the kernels assume
+    if (g.splits < 1 || g.col_tiles < 1 || (int64_t)g.rows * g.splits < g.k_r) return TP_ERR_INVALID_ARG;
+    if (g.col_tiles > kMaxCounters) return TP_ERR_UNSUPPORTED;
+    if (g.path == TP_PATH_VALU) {
+        if (batch < 1 || batch > kValuMaxBatch || g.rows > valu_rows_max(batch, g.cols))
+            return TP_ERR_UNSUPPORTED;
+        valu_fn k = valu_kernel(batch, g.cols);
+        if (!k) return TP_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k, dim3(g.grid), dim3(kValuWaves * 64), 0, st, a);
+    } else {
+        if (batch < kMfmaMinBatch || batch > kMfmaMaxBatch || g.cols != kMfmaCols) return TP_ERR_UNSUPPORTED;
+        mfma_fn k = mfma_kernel(batch);
+        if (!k) return TP_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k, dim3(g.grid), dim3(kMfmaWaves * 64), 0, st, a, batch);
+    }
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+// Resident workgroups of a kernel on the current device (cooperative grid).
+int resident_grid(const void* kernel, int block) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+    return per_cu * cus;
+}
+
+tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
+                            const void* w_o, const void* x_ffn, const void* w_down, float* slots,
+                            float* hidden, void* ws, hipStream_t st) {
+    const int b = p->batch;
+    PointGeom geo[2] = {tp_point_geom(p, 0), tp_point_geom(p, 1)};
+    if (geo[0].cols != geo[1].cols || geo[0].col_tiles != geo[1].col_tiles) return TP_ERR_UNSUPPORTED;
+    if (geo[0].col_tiles > kMaxCounters) return TP_ERR_UNSUPPORTED;
+    for (int pt = 0; pt < 2; ++pt)
+        if (geo[pt].path != TP_PATH_VALU || geo[pt].rows > valu_rows_max(b, geo[pt].cols) ||
+            (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
+            return TP_ERR_UNSUPPORTED;
+    if ((int64_t)n_layers * 2 * geo[0].col_tiles >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
+    step_fn k = step_kernel(b, geo[0].cols);
+    if (!k) return TP_ERR_UNSUPPORTED;
+    StepArgs a;
+    a.x[0] = static_cast<const uint16_t*>(x_attn);
+    a.x[1] = static_cast<const uint16_t*>(x_ffn);
+    a.w[0] = static_cast<const uint16_t*>(w_o);
+    a.w[1] = static_cast<const uint16_t*>(w_down);
+    a.slots = slots;
+    a.hidden = hidden;
+    a.ws_part = ws_partials(ws);
+    a.counters = ws_counters(ws);
+    a.sync = ws_sync(ws);
+    a.H = p->hidden;
+    for (int pt = 0; pt < 2; ++pt) {
+        a.K[pt] = geo[pt].k_r;
+        a.rows[pt] = geo[pt].rows;
+        a.splits[pt] = geo[pt].splits;
+        a.tiles[pt] = geo[pt].grid;
+    }
+    a.col_tiles = geo[0].col_tiles;
+    a.layers = n_layers;
+    a.n_ranks = p->n_ranks;
+    a.rank = rank;
+    a.chunk = (int64_t)b * p->hidden / p->n_ranks;
+    a.spin_limit = 1u << 21;
+    if (n_layers == 0) return TP_OK;
+    int cap = resident_grid(reinterpret_cast<const void*>(k), kValuWaves * 64);
+    if (cap < 1) return TP_ERR_DEVICE;
+    int want = geo[0].grid > geo[1].grid ? geo[0].grid : geo[1].grid;
+    int grid = want < cap ? want : cap;
+    void* args[] = {&a};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid),
+                                   dim3(kValuWaves * 64), args, 0, st) != hipSuccess)
+        return TP_ERR_DEVICE;
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_workspace_init(tp_plan_t p, void* ws, void* stream) {
+    if (!p || !ws) return TP_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return TP_ERR_ALIGNMENT;
+    int64_t n = kCounterBytes / 4;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, ws_counters(ws), n, 0u);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_workspace_status(tp_plan_t p, const void* ws, int32_t* flags) {
+    if (!p || !ws || !flags) return TP_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return TP_ERR_ALIGNMENT;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, static_cast<const char*>(ws) + kSyncOffset + 4 * kSyncErr, 4,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+        return TP_ERR_DEVICE;
+    *flags = (int32_t)v;
+    return TP_OK;
+}
+
+tp_status tp_rowparallel_partial(tp_plan_t p, int32_t point, const void* x, const void* w,
+                                 float* out, void* ws, void* stream) {
+    if (!p || !x || !w || !out || !ws) return TP_ERR_INVALID_ARG;
+    if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(ws)) return TP_ERR_ALIGNMENT;
+    PointGeom g = tp_point_geom(p, point);
+    Epilogue e{};
+    e.p = out;
+    e.ws_part = ws_partials(ws);
+    e.counters = ws_counters(ws);
+    e.splits = g.splits;
+    return launch_projection(p, g, p->batch, x, w, e, (hipStream_t)stream);
+}
+
+tp_status tp_ring_reduce(tp_plan_t p, const float* partials, const float* residual, float* out,
+                         void* out_bf16, void* stream) {
+    if (!p || !partials || !residual || !out) return TP_ERR_INVALID_ARG;
+    if (!aligned16(partials) || !aligned16(residual) || !aligned16(out) ||
+        (out_bf16 && !aligned16(out_bf16)))
+        return TP_ERR_ALIGNMENT;
+    int64_t len = (int64_t)p->batch * p->hidden;
+    int64_t chunk = len / p->n_ranks;
+    hipLaunchKernelGGL(ring_reduce_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, partials, residual, out,
+                       static_cast<uint16_t*>(out_bf16), len, chunk, (int)p->n_ranks);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_decode_layers(tp_plan_t p, int32_t n_layers, int32_t rank, const void* x_attn,
+                           const void* w_o, const void* x_ffn, const void* w_down, float* slots,
+                           float* hidden, void* ws, void* stream) {
+    if (!p || !x_attn || !w_o || !x_ffn || !w_down || !slots || !hidden || !ws)
+        return TP_ERR_INVALID_ARG;
+    if (n_layers < 0 || rank < 0 || rank >= p->n_ranks) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x_attn) || !aligned16(w_o) || !aligned16(x_ffn) || !aligned16(w_down) ||
+        !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    const int64_t b = p->batch, H = p->hidden, N = p->n_ranks;
+    const int64_t len = b * H;
+    PointGeom geo[2] = {tp_point_geom(p, 0), tp_point_geom(p, 1)};
+    // every slice of the stacked inputs must stay 16-byte aligned
+    for (int pt = 0; pt < 2; ++pt)
+        if ((b * geo[pt].k_r) % 8) return TP_ERR_ALIGNMENT;
+    hipStream_t st = (hipStream_t)stream;
+    if (tp_decode_mode(p) == 2)
+        return decode_persistent(p, n_layers, rank, x_attn, w_o, x_ffn, w_down, slots, hidden, ws, st);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        for (int pt = 0; pt < 2; ++pt) {
+            const PointGeom& g = geo[pt];
+            const uint16_t* xb = static_cast<const uint16_t*>(pt == 0 ? x_attn : x_ffn);
+            const uint16_t* wb = static_cast<const uint16_t*>(pt == 0 ? w_o : w_down);
+            float* slot = slots + ((int64_t)l * 2 + pt) * N * len;
+            Epilogue e{};
+            e.p = slot + rank * len;
+            e.ws_part = ws_partials(ws);
+            e.counters = ws_counters(ws);
+            e.splits = g.splits;
+            e.ring_slots = slot;
+            e.hidden = hidden;
+            e.n_ranks = (int32_t)N;
+            e.rank = rank;
+            e.chunk = len / N;
+            tp_status s = launch_projection(p, g, (int)b, xb + (int64_t)l * b * g.k_r,
+                                            wb + (int64_t)l * g.k_r * H, e, st);
+            if (s != TP_OK) return s;
+        }
+    }
+    return TP_OK;
+}
+
+tp_status tp_moe_route(tp_plan_t p, const float* logits, int32_t tokens, int32_t renorm,
+                       int32_t* sel_expert, float* sel_weight, void* stream) {
+    (void)p; (void)logits; (void)tokens; (void)renorm; (void)sel_expert; (void)sel_weight;
+    (void)stream;
+    return TP_ERR_UNSUPPORTED;
+}
+
+tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
+                         const float* sel_weight, int32_t tokens, const void* u,
+                         const void* w_local, float* part, void* ws, void* stream) {
+    (void)p; (void)rank; (void)sel_expert; (void)sel_weight; (void)tokens; (void)u;
+    (void)w_local; (void)part; (void)ws; (void)stream;
+    return TP_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Host-side plan: sizes, validation, kernel geometry and workspace layout.
+// Touches no device, so it runs (and is tested) without a GPU.
+#include <new>
+#include <string.h>
+
+#include "tp_internal.h"
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int default_valu_cols(int32_t batch) {
+    // Narrower column tiles keep the split-K partial traffic small; 256
+    // columns = 32 lanes x 16 bytes, two full 256-byte row segments per
+    // wave instruction.
+    (void)batch;
+    return 256;
+}
+
+}  // namespace
+
+PointGeom tp_geom_for(const tp_plan_s* p, int64_t k_r, int32_t batch, int32_t splits_user) {
+    PointGeom g{};
+    g.k_r = k_r;
+    g.path = batch >= kMfmaMinBatch ? TP_PATH_MFMA : TP_PATH_VALU;
+    int64_t gran, max_rows;
+    if (g.path == TP_PATH_VALU) {
+        g.cols = p->valu_cols ? p->valu_cols : default_valu_cols(batch);
+        int lanes_per_row = g.cols / 8;
+        gran = (int64_t)kValuWaves * (64 / lanes_per_row);
+        max_rows = valu_rows_max(batch, g.cols);
+    } else {
+        g.cols = kMfmaCols;
+        gran = kMfmaKStep;
+        max_rows = kMfmaMaxRows;
+    }
+    g.col_tiles = (int32_t)ceil_div(p->hidden, g.cols);
+    int64_t target = p->target_wgs ? p->target_wgs : 2 * kTargetCUs;
+    int64_t s = splits_user > 0 ? splits_user
+                                : (target + g.col_tiles / 2) / g.col_tiles;
+    if (s < 1) s = 1;
+    int64_t s_max = ceil_div(k_r, gran);
+    if (s > s_max) s = s_max;
+    int64_t rows = round_up(ceil_div(k_r, s), gran);
+    if (rows > max_rows) rows = max_rows;
+    s = ceil_div(k_r, rows);
+    if (s > kMaxCounters) s = kMaxCounters;  // unreachable for supported sizes
+    g.rows = (int32_t)rows;
+    g.splits = (int32_t)s;
+    g.grid = g.col_tiles * g.splits;
+    return g;
+}
+
+PointGeom tp_point_geom(const tp_plan_s* p, int point) {
+    int64_t k = point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter;
+    return tp_geom_for(p, k / p->n_ranks, p->batch, p->splits_user[point]);
+}
+
+int64_t tp_ws_partials_offset() { return kCounterBytes; }
+
+static int64_t partial_bytes(const tp_plan_s* p) {
+    int64_t m = 0;
+    for (int pt = 0; pt < 2; ++pt) {
+        PointGeom g = tp_point_geom(p, pt);
+        int64_t b = g.splits > 1 ? (int64_t)g.splits * p->batch * p->hidden * 4 : 0;
+        if (b > m) m = b;
+    }
+    return round_up(m, 256);
+}
+
+int64_t tp_ws_moe_offset(const tp_plan_s* p) {
+    return tp_ws_partials_offset() + partial_bytes(p);
+}
+
+static int64_t moe_bytes(const tp_plan_s* p) {
+    if (!p->n_experts) return 0;
+    int64_t pairs = (int64_t)p->max_tokens * p->top_k;
+    int64_t le = p->n_experts / p->ep;
+    // per-expert pair lists (offsets, token, selection index), then the
+    // per-selection fp32 projections Y[pair][H] and their split-K partials
+    int64_t lists = round_up((le + 1) * 4 + pairs * 8 + 256, 256);
+    PointGeom g = tp_geom_for(p, p->moe_inter, kMfmaMinBatch, 0);
+    int64_t y = round_up(pairs * p->hidden * 4, 256);
+    int64_t parts = round_up((int64_t)g.splits * 16 * p->hidden * 4 * le, 256);
+    return lists + y + parts;
+}
+
+int64_t tp_workspace_bytes(const tp_plan_s* p) {
+    return tp_ws_moe_offset(p) + moe_bytes(p);
+}
+
+int tp_decode_mode(const tp_plan_s* p) {
+    if (p->decode_mode) return p->decode_mode;
+    return p->batch < kMfmaMinBatch ? 2 : 1;  // persistent step for the VALU path
+}
+
+extern "C" {
+
+tp_status tp_plan(int64_t hidden, int64_t inter, int32_t n_ranks, int32_t batch,
+                  tp_plan_t* out) {
+    if (!out) return TP_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (hidden < 1 || inter < 1 || n_ranks < 1 || batch < 1) return TP_ERR_INVALID_ARG;
+    if (inter % n_ranks || hidden % n_ranks) return TP_ERR_INVALID_ARG;
+    if (((int64_t)batch * hidden) % n_ranks) return TP_ERR_INVALID_ARG;
+    if (hidden % 8) return TP_ERR_UNSUPPORTED;
+    if (batch > kMfmaMaxBatch) return TP_ERR_UNSUPPORTED;
+    if (hidden > (int64_t)1 << 24 || inter > (int64_t)1 << 24) return TP_ERR_UNSUPPORTED;
+    tp_plan_s* p = new (std::nothrow) tp_plan_s();
+    if (!p) return TP_ERR_OOM;
+    p->hidden = hidden;
+    p->inter = inter;
+    p->k_attn = hidden;
+    p->n_ranks = n_ranks;
+    p->batch = batch;
+    *out = p;
+    return TP_OK;
+}
+
+tp_status tp_plan_set_attn_dim(tp_plan_t p, int64_t k_attn) {
+    if (!p || k_attn < 1 || k_attn % p->n_ranks) return TP_ERR_INVALID_ARG;
+    if (k_attn > (int64_t)1 << 24) return TP_ERR_UNSUPPORTED;
+    p->k_attn = k_attn;
+    return TP_OK;
+}
+
+tp_status tp_plan_set_moe(tp_plan_t p, int32_t n_experts, int32_t top_k, int32_t ep,
+                          int64_t moe_inter, int32_t max_tokens) {
+    if (!p || n_experts < 1 || top_k < 1 || ep < 1 || moe_inter < 1 || max_tokens < 1)
+        return TP_ERR_INVALID_ARG;
+    if (top_k > n_experts || n_experts % ep) return TP_ERR_INVALID_ARG;
+    if (top_k > kMoeMaxTopK || max_tokens > kMoeMaxTokens) return TP_ERR_UNSUPPORTED;
+    if (moe_inter > (int64_t)1 << 20 || n_experts > 1 << 16) return TP_ERR_UNSUPPORTED;
+    p->n_experts = n_experts;
+    p->top_k = top_k;
+    p->ep = ep;
+    p->moe_inter = moe_inter;
+    p->max_tokens = max_tokens;
+    return TP_OK;
+}
+
+tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
+    if (!p || !key) return TP_ERR_INVALID_ARG;
+    if (!strcmp(key, "splits_attn") || !strcmp(key, "splits_ffn")) {
+        if (value < 0 || value > 4096) return TP_ERR_INVALID_ARG;
+        p->splits_user[key[7] == 'a' ? 0 : 1] = (int32_t)value;
+    } else if (!strcmp(key, "valu_cols")) {
+        if (value != 0 && value != 128 && value != 256 && value != 512) return TP_ERR_INVALID_ARG;
+        p->valu_cols = (int32_t)value;
+    } else if (!strcmp(key, "decode_mode")) {
+        if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
+        p->decode_mode = (int32_t)value;
+    } else if (!strcmp(key, "strip_variant")) {
+        if (value < 0 || value > 3) return TP_ERR_INVALID_ARG;
+        p->strip_variant = (int32_t)value;
+    } else if (!strcmp(key, "target_wgs")) {
+        if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
+        p->target_wgs = (int32_t)value;
+    } else {
+        return TP_ERR_INVALID_ARG;
+    }
+    return TP_OK;
+}
+
+tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
+    if (!p || !o) return TP_ERR_INVALID_ARG;
+    memset(o, 0, sizeof *o);
+    o->hidden = p->hidden;
+    o->inter = p->inter;
+    o->k_attn = p->k_attn;
+    o->n_ranks = p->n_ranks;
+    o->batch = p->batch;
+    for (int pt = 0; pt < 2; ++pt) {
+        PointGeom g = tp_point_geom(p, pt);
+        o->k_rank[pt] = g.k_r;
+        o->path[pt] = g.path;
+        o->splits[pt] = g.splits;
+    }
+    o->chunk_elems = (int64_t)p->batch * p->hidden / p->n_ranks;
+    o->wire_bytes_bf16 = 2 * (int64_t)(p->n_ranks - 1) * o->chunk_elems * 2;
+    o->wire_bytes_fp32 = 2 * (int64_t)(p->n_ranks - 1) * o->chunk_elems * 4;
+    o->workspace_bytes = tp_workspace_bytes(p);
+    o->n_experts = p->n_experts;
+    o->top_k = p->top_k;
+    o->ep = p->ep;
+    o->local_experts = p->ep ? p->n_experts / p->ep : 0;
+    o->moe_inter = p->moe_inter;
+    o->max_tokens = p->max_tokens;
+    return TP_OK;
+}
+
+void tp_plan_destroy(tp_plan_t p) { delete p; }
+
+const char* tp_status_str(tp_status s) {
+    switch (s) {
+        case TP_OK: return "ok";
+        case TP_ERR_INVALID_ARG: return "invalid argument";
+        case TP_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TP_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+        case TP_ERR_DEVICE: return "HIP device error";
+        case TP_ERR_OOM: return "out of host memory";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

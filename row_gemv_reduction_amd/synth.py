@@ -33,7 +33,7 @@ TENSOR_IDS = {
 }
 
 
-def _key_ints(seed, workload, layer, tensor, rank):
+def _key_ints(seed=0, workload=0, layer=0, tensor="x", rank=0):
     if isinstance(workload, str):
         workload = int.from_bytes(hashlib.sha256(workload.encode()).digest()[:4], "little")
     return [int(seed), int(workload), int(layer), TENSOR_IDS[tensor], int(rank)]

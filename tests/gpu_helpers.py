@@ -1,0 +1,60 @@
+"""Shared helpers of the GPU parity tests: host<->device copies of bf16 bit
+patterns and the parity tolerances.
+
+Tolerances (the acceptance bar of this path):
+  * fp32 partial projections: max|got - ref| <= 1e-5 * rms(ref), with ref
+    the oracle's double-accumulated value (normwise; a per-element relative
+    error is undefined near zero).
+  * ring-order reduction: bit-exact, given identical partials.
+  * bf16 outputs: |got - ref| <= max(1e-2 * rms(ref), one bf16 ulp of ref)
+    per element (correct rounding of the exact value already moves an
+    element by up to half an ulp, which at |y| ~ 4-5 rms is ~1-2 % of rms).
+"""
+import sys
+
+import numpy as np
+import torch
+
+PARTIAL_RTOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bf16_bits_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def assert_partial_close(got, ref64, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref64 ** 2)))
+    err = float(np.abs(got - ref64).max()) if got.size else 0.0
+    assert err <= PARTIAL_RTOL * rms, "%s: max|d|=%.3e > %.0e*rms=%.3e" % (
+        what, err, PARTIAL_RTOL, PARTIAL_RTOL * rms)
+    return err / rms if rms else 0.0
+
+
+def assert_bits_equal(got, want, what=""):
+    got = np.ascontiguousarray(got)
+    want = np.ascontiguousarray(want)
+    assert got.shape == want.shape, what
+    gb = got.view(np.uint32 if got.dtype == np.float32 else np.uint16)
+    wb = want.view(np.uint32 if want.dtype == np.float32 else np.uint16)
+    bad = np.flatnonzero(gb.ravel() != wb.ravel())
+    assert bad.size == 0, "%s: %d elements differ, first at %d: %r vs %r" % (
+        what, bad.size, bad[0], got.ravel()[bad[0]], want.ravel()[bad[0]])
