@@ -136,8 +136,8 @@ def main():
         layout = "packed" if w.batch <= 8 else "rowmajor"
     if layout == "packed":
         # load-time layout change, outside the timed region
-        po = torch.empty((w.layers, w.hidden // 8, w.ka_r, 8), dtype=torch.bfloat16, device="cuda")
-        pd = torch.empty((w.layers, w.hidden // 8, w.ki_r, 8), dtype=torch.bfloat16, device="cuda")
+        po = torch.empty(tp.packed_shape(plan, 0, w.layers), dtype=torch.bfloat16, device="cuda")
+        pd = torch.empty(tp.packed_shape(plan, 1, w.layers), dtype=torch.bfloat16, device="cuda")
         tp.tp_pack_weights(plan, 0, wo, po)
         tp.tp_pack_weights(plan, 1, wd, pd)
         torch.cuda.synchronize()

@@ -117,8 +117,12 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "valu_cols" (columns per VALU workgroup: 128, 256 or 512),
  * "decode_mode" (0 = automatic, 1 = one launch per point,
  *                2 = one persistent launch per step),
- * "strip_variant" (0 = automatic, 1..3: kernel variant of the strip-packed
- *                step: 7+1 waves x 10 vectors, 3+1 x 24, 7+1 x 20).
+ * "segment_loads" (0 or 4: 4, or 8: 16-byte loads per lane in each of the
+ *                two register banks of tp_decode_layers_packed; 8 only
+ *                takes effect for batch <= 4),
+ * "serial_points" (tp_decode_layers_packed: 0 = each hidden-state element
+ *                follows its own chain, 1 = point j+1 also waits for all of
+ *                point j, see there).
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
@@ -200,30 +204,48 @@ tp_status tp_decode_layers(tp_plan_t plan, int32_t n_layers, int32_t rank,
                            float* slots, float* hidden, void* workspace, void* stream);
 
 /*
- * Strip-packed weights for the decode step. A rank's weight slice
- * W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is stored as
- *     P[s][k][c] = W_r[k][8s + c],   s < H/8, k < K_r, c < 8
- * i.e. H/8 strips of 8 columns, each strip's K_r rows of 16 bytes stored
- * contiguously. Same bytes as the row-major slice, laid out so a
- * workgroup streams a whole strip (all of K) in contiguous loads and needs
- * no split of K over workgroups. Packing is done once, when the weights
- * are loaded; it is not part of the decode step.
+ * Pair-strip packed weights for the streamed decode step. A rank's weight
+ * slice W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is
+ * stored as
+ *     P[s][kp][c][q] = W_r[2kp + q][4s + c]
+ *     s < H/4, kp < ceil(K_r/2), c < 4, q < 2   (rows past K_r are zero)
+ * i.e. H/4 strips of 4 columns; each 16-byte vector holds rows 2kp and
+ * 2kp+1 of its strip as one bf16 pair per column, and a strip's rows are
+ * contiguous. Same bytes as the row-major slice (plus one zero row when
+ * K_r is odd). Packing is done once, when the weights are loaded; it is not
+ * part of the decode step.
  *
  * tp_pack_weights: w bf16 [n_layers][K_r][hidden] -> w_packed bf16
- * [n_layers][hidden/8][K_r][8] for `point`. w and w_packed must not overlap.
+ * [n_layers][hidden/4][ceil(K_r/2)][8] for `point`. w and w_packed must not
+ * overlap. TP_ERR_UNSUPPORTED if hidden is not a multiple of 4.
  */
 tp_status tp_pack_weights(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w,
                           void* w_packed, void* stream);
 
 /*
- * The decode step of tp_decode_layers on strip-packed weights (same
- * arguments and results, within the projections' fp tolerance; the ring
- * stage is the same binary32 additions in the same order). One cooperative
- * (persistent) launch: per point, each workgroup reduces whole strips over
- * K in registers/LDS, forms the ring-order sum plus residual for them and
- * signals; point j reads its activation only after point j-1's hidden
- * state is complete. TP_ERR_UNSUPPORTED unless batch <= 8, n_ranks <= 8,
- * K_r % 8 == 0 for both points and max(K_r) * batch * 2 <= 48 KiB.
+ * The decode step of tp_decode_layers on pair-strip packed weights: same
+ * arguments and results (the projections within their fp tolerance, the
+ * ring stage the same binary32 additions in the same order). One launch
+ * per step: each workgroup owns a set of 4-column strips for every point,
+ * streams their weights over all of K_r, and keeps its columns of the
+ * hidden state on chip between points; per point it writes the rank's
+ * partial into its slot and sets hidden <- ring_sum(slot) + hidden for its
+ * columns (lesson 9.9, Conceito).
+ *
+ * Point order. Every element of the hidden state is updated point after
+ * point, each update reading the previous one; since each point's
+ * activation slice is an input, no point has to wait for other columns.
+ * With the plan knob "serial_points" = 1 the step also emulates a model in
+ * which a point's activation depends on the whole previous hidden state:
+ * point j+1's activation is read only after every column of point j is
+ * complete (a grid-wide wait per point; cooperative launch). Both orders
+ * give the same bits. In the serial order the workspace's error word
+ * (tp_workspace_status) reports a wait that timed out.
+ *
+ * TP_ERR_UNSUPPORTED unless batch <= 8, n_ranks <= 8, K_r is even for both
+ * points, batch * K_r is a multiple of 8, the activation slices of a point
+ * fit the on-chip buffers (2 * batch * K_r bytes per point kind, about
+ * 150 KiB in all) and 16 * batch * ceil(hidden / 1024) <= 192.
  */
 tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank,
                                   const void* x_attn, const void* w_o_packed,

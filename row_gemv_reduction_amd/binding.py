@@ -138,6 +138,10 @@ class Plan:
             self.close()
             raise
 
+    def tune(self, key, value):
+        """Set a tuning knob (tp_plan_tune)."""
+        _check(_lib().tp_plan_tune(self.handle, key.encode(), int(value)), "tp_plan_tune(%s)" % key)
+
     @property
     def handle(self):
         if self._h is None:
@@ -229,15 +233,21 @@ def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slo
     _check(_lib().tp_decode_layers(plan.handle, L, rank, *args, _stream()), "tp_decode_layers")
 
 
-def tp_pack_weights(plan: Plan, point, w, w_packed):
-    """Strip-pack a stack of row-major weight slices [L, K_r, H] -> [L, H/8, K_r, 8]."""
-    i = plan.info()
-    kr, H = i["k_rank"][point] if point in (0, 1) else -1, i["hidden"]
+def packed_shape(plan: Plan, point, n_layers):
+    """Shape of a pair-strip packed weight stack: [L, H/4, ceil(K_r/2), 8]."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
-    L = w.shape[0]
+    i = plan.info()
+    kr, H = i["k_rank"][point], i["hidden"]
+    return (n_layers, H // 4, (kr + 1) // 2, 8)
+
+
+def tp_pack_weights(plan: Plan, point, w, w_packed):
+    """Pair-strip pack a stack of row-major weight slices [L, K_r, H] -> packed_shape()."""
+    shape = packed_shape(plan, point, w.shape[0])
+    L, kr, H = shape[0], plan.info()["k_rank"][point], plan.info()["hidden"]
     _check(_lib().tp_pack_weights(plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, kr, H)),
-                                  _dev(w_packed, "w_packed", torch.bfloat16, (L, H // 8, kr, 8)),
+                                  _dev(w_packed, "w_packed", torch.bfloat16, shape),
                                   _stream()), "tp_pack_weights")
 
 
@@ -248,9 +258,9 @@ def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ff
     ka, ki = i["k_rank"]
     L = n_layers
     args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
-            _dev(w_o_packed, "w_o_packed", torch.bfloat16, (L, H // 8, ka, 8)),
+            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
             _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
-            _dev(w_down_packed, "w_down_packed", torch.bfloat16, (L, H // 8, ki, 8)),
+            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
             _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
             _dev(hidden, "hidden", torch.float32, (b, H)),
             _dev(workspace, "workspace", torch.uint8))

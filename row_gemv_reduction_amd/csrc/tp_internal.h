@@ -16,14 +16,6 @@ constexpr int kCounterStride = 16;            // one counter per 64-byte line
 constexpr int kMaxCounters = 1024;            // column-tile arrival counters (64 KiB)
 constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, error
 constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
-// Tree barrier of the strip step (word offsets in the sync area; every
-// counter and release word on its own 256-byte line)
-constexpr int kTreeGroups = 32;
-constexpr int kTreeLine = 64;                         // words per line
-constexpr int kTreeTop = 64;
-constexpr int kTreeGroupBase = 128;                   // + q * kTreeLine
-constexpr int kTreeReleaseBase = kTreeGroupBase + kTreeGroups * kTreeLine;  // + q * kTreeLine
-
 // VALU GEMV geometry limits
 constexpr int kValuWaves = 4;        // waves per workgroup
 constexpr int kValuMaxRows = 512;    // rows of x staged in LDS per workgroup
@@ -48,11 +40,11 @@ constexpr int kMfmaWaves = 4;
 constexpr int kMfmaKStep = 32;       // k rows per MFMA step
 constexpr int kMfmaMaxRows = 1024;   // rows per MFMA split (multiple of 128)
 
-// Strip-packed decode step
-constexpr int kStripComputeWaves = 8;       // compute waves per workgroup (+1 control wave)
+// Streamed decode step on pair-strip packed weights
 constexpr int kStripMaxBatch = 8;
-constexpr int kStripMaxPerWg = 4;           // strips (of 8 columns) per workgroup
-constexpr int64_t kStripMaxXsBytes = 48 * 1024;  // LDS for one point's x: K * B * 2
+constexpr int kStreamMaxLdsBytes = 150 * 1024;  // x buffers (dynamic LDS)
+// completion words of the serial point order (byte offset in the workspace)
+constexpr int64_t kStreamFlagOffset = kSyncOffset + 16 * 1024;
 
 // MoE
 constexpr int kMoeMaxTopK = 32;
@@ -66,7 +58,8 @@ struct tp_plan_s {
     int32_t valu_cols = 0;
     int32_t decode_mode = 0;
     int32_t target_wgs = 0;
-    int32_t strip_variant = 0;  // 0 = automatic, else 1-based index of the strip kernel variant
+    int32_t segment_loads = 0;  // 16-byte loads per lane per bank of the streamed step (0 = 4)
+    int32_t serial_points = 0;  // streamed step: point j+1 waits for all of point j
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -90,4 +83,14 @@ int64_t tp_workspace_bytes(const tp_plan_s* p);
 int64_t tp_ws_partials_offset();
 int64_t tp_ws_moe_offset(const tp_plan_s* p);
 int tp_decode_mode(const tp_plan_s* p);
-int tp_strip_loads(const tp_plan_s* p);  // nonzero if the strip-packed step can run the plan
+
+// Geometry of the streamed decode step (tp_packed.hip).
+struct StreamGeom {
+    int32_t grid, block;  // workgroups (strip owners) and threads per workgroup
+    int32_t ns, wps, sl;  // strips per workgroup, waves per strip, loads per bank
+    int32_t kh0, kh1;     // row pairs per point kind
+    int32_t bpw0, bpw1;   // 1 KB row blocks per compute wave per point kind
+    int32_t xoff1, xdwords, lds_bytes;
+};
+bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
+int tp_strip_loads(const tp_plan_s* p);  // nonzero if the streamed step can run the plan

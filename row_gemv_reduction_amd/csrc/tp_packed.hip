@@ -1,32 +1,52 @@
-// Column-strip weight layout and the decode step that streams it.
+// Pair-strip weight layout and the decode step that streams it.
 //
-// The decode projections are weight-streaming bound ("Hosting Qwen on
-// Blackwell", section Decoders); the reconciliation after each one is a
-// short serial dependency (lesson 9.9 "Interconnects e clusters", section
-// 01 · Conceito: every point is a blocking round trip). Row-major W[K][H]
-// forces a split of K over workgroups, and the split partials then have to
-// meet in memory (publish, count arrivals, gather) on that serial path. The
-// strip layout removes that exchange: the rank's slice W_r[K][H] is stored
-// once, at load time, as
+// The decode projections are bound by streaming the weights from HBM
+// ("Hosting Qwen on Blackwell", section Decoders: the decode matmuls depend
+// on the cost of loading the weights); each reconciliation point is followed
+// by the sum of the ranks' partials before the residual stream continues
+// (lesson 9.9 "Interconnects e clusters", section 01 · Conceito).
 //
-//     P[s][k][c] = W_r[k][8s + c]      s < H/8, k < K, c < 8
+// Layout. A rank's slice W_r[K][H] is stored once, at load time, as
 //
-// (same bytes, 16 contiguous bytes per row of a strip), so one workgroup
-// streams a whole strip of 8 columns over all K rows as contiguous 1 KB
-// wave loads and reduces over K inside the workgroup: lanes by a shuffle
-// butterfly, waves through LDS. No partial leaves the workgroup.
+//     P[s][kp][c][q] = W_r[2kp + q][4s + c]   s < H/4, kp < ceil(K/2), c < 4, q < 2
 //
-// decode_strips: one cooperative (persistent) launch per decode step. Each
-// workgroup owns strips g, g+G, ... for every point of the step and runs
-//   - NW compute waves: hold the weights of the current task in registers,
-//     multiply them by x (staged in LDS), reduce, and issue the loads of
-//     their next task right away, so those are in flight while the current
-//     point is reduced and the next point is waited for;
-//   - one control wave: waits for the previous point, stages x, forms the
-//     ring-order sum of the N ranks' values plus the residual for its strip
-//     (the strip's hidden state stays in LDS between points), stores it
-//     device-coherently and signals completion. Its memory counter never
-//     waits behind the bulk weight loads.
+// (rows past K read as zero). Same bytes as the row-major slice. A 16-byte
+// vector holds two consecutive rows of a 4-column strip, column by column,
+// so each of its dwords is a (row 2kp, row 2kp+1) bf16 pair that one
+// v_dot2c_f32_bf16 multiplies by the matching pair of x. A strip's K rows
+// are K*8 contiguous bytes: a wave streams 128 rows of a strip per 1 KB
+// load, and one workgroup reduces whole strips over K, so no partial leaves
+// the workgroup.
+//
+// decode_stream: one launch per decode step. Workgroup g of G owns strips
+// g, g+G, g+2G, ... (NS of them: H/4 strips spread evenly, one workgroup
+// per CU at the page-1 shapes) for every point of the step, and keeps the
+// hidden state of its columns in registers for the whole step. It runs
+//   - NS*WPS compute waves: WPS waves share a strip, interleaving its
+//     1 KB row blocks. Each wave streams its blocks of every point through
+//     two banks of SL 16-byte loads per lane: while one bank is multiplied,
+//     the other is in flight, and a consumed bank is refilled at once with
+//     the blocks two segments ahead, across point boundaries. The bank
+//     loads are never conditional: blocks past a strip (or past the step)
+//     go through a buffer descriptor whose range makes them read zero
+//     without touching memory, so the wait counts stay exact and no point
+//     boundary drains the pipeline.
+//   - one control wave: stages each point's x into LDS with direct
+//     global->LDS loads (x of the next point of the same kind is staged
+//     while the current one is multiplied), and at the end of each point
+//     sums the compute waves' partials, writes the rank's partial to its
+//     slot, forms the ring-order sum of the N ranks' values plus the
+//     residual, and keeps the result as the next residual.
+//
+// Point order. The hidden state is chained element by element (a point's
+// residual is the previous point's output at the same element), which the
+// ownership of columns by one workgroup preserves without any grid-wide
+// synchronisation. With `serial` set, the step also emulates a model in
+// which each point's activation is a function of the whole previous hidden
+// state: after point j every workgroup publishes its completion, and point
+// j+1's x is staged only once all workgroups have completed point j (a
+// flag barrier; needs a cooperative launch). The results are the same bits
+// in both orders.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -38,396 +58,416 @@ namespace {
 
 using namespace tpdev;
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // ------------------------------------------------------------- packing --
 
-// P[l][s][k][0..8) = W[l][k][8s .. 8s+8): one 16-byte vector per thread.
-__global__ void pack_strips_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
-                                   int64_t layers, int64_t K, int64_t H) {
-    const int64_t strips = H / 8;
-    const int64_t per_layer = K * strips;
+// P[l][s][kp][c][q] = W[l][2kp+q][4s+c]: one 16-byte output vector per thread.
+__global__ void pack_pairs_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
+                                  int64_t layers, int64_t K, int64_t H) {
+    const int64_t strips = H / 4;
+    const int64_t kh = (K + 1) / 2;
+    const int64_t per_layer = strips * kh;
     const int64_t total = layers * per_layer;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
          v += (int64_t)gridDim.x * blockDim.x) {
         const int64_t l = v / per_layer;
         const int64_t rem = v - l * per_layer;
-        const int64_t k = rem / strips;
-        const int64_t s = rem - k * strips;
-        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(w + (l * K + k) * H + s * 8);
-        *reinterpret_cast<u32x4_t*>(p + ((l * strips + s) * K + k) * 8) = val;
+        const int64_t s = rem / kh;
+        const int64_t kp = rem - s * kh;
+        const uint16_t* r0 = w + (l * K + 2 * kp) * H + 4 * s;
+        uint16_t a[4], b[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a[c] = r0[c];
+            b[c] = 2 * kp + 1 < K ? r0[H + c] : (uint16_t)0;
+        }
+        u32x4_t out;
+        out.x = a[0] | ((uint32_t)b[0] << 16);
+        out.y = a[1] | ((uint32_t)b[1] << 16);
+        out.z = a[2] | ((uint32_t)b[2] << 16);
+        out.w = a[3] | ((uint32_t)b[3] << 16);
+        *reinterpret_cast<u32x4_t*>(p + v * 8) = out;
     }
 }
 
 // ------------------------------------------------------- decode step --
 
-// Per-point fields are separate scalars (not arrays indexed by the point),
-// so the compiler keeps them, and the buffer descriptors built from them,
-// in scalar registers.
-struct StripArgs {
+constexpr int kStreamMaxWaves = 16;   // 1 control + up to 15 compute waves
+constexpr int kStreamMaxNS = 15;      // strips per workgroup
+constexpr int kBlockBytes = 1024;     // one wave load: 64 lanes x 16 bytes = 128 rows of a strip
+
+struct StreamArgs {
     const uint16_t* x0;     // x_attn [L][B][K0]
     const uint16_t* x1;     // x_ffn  [L][B][K1]
-    const uint16_t* w0;     // strip-packed w_o    [L][H/8][K0][8]
-    const uint16_t* w1;     // strip-packed w_down [L][H/8][K1][8]
+    const uint16_t* w0;     // packed w_o    [L][S][Kh0][8]
+    const uint16_t* w1;     // packed w_down [L][S][Kh1][8]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
-    uint32_t* sync;         // done / exit / error words
-    int32_t H, K0, K1;
-    int32_t strips, layers, n_ranks, rank;
-    int32_t chunk;
+    uint32_t* flags;        // serial order: G completion words, then the exit counter
+    uint32_t* err;          // error word (bit 0: a bounded wait timed out)
+    int32_t H, S, NS, WPS;
+    int32_t K0, K1, Kh0, Kh1;
+    int32_t bpw0, bpw1;     // row blocks per compute wave per point (same for every wave)
+    int32_t layers, n_ranks, rank, chunk;
+    int32_t xoff1;          // dword offset of the second x buffer in LDS
+    int32_t xdwords;        // total LDS dwords of the two x buffers
     uint32_t spin_limit;
-    int32_t xs_bytes;       // dynamic LDS for x: rows padded to NW * 64, * B * 2
 };
 
-// An opaque 0 that the compiler can only produce after every accumulator
-// value is final (inline asm consuming them, 8 at a time). Loads whose
-// offsets take it cannot be hoisted above the multiplies.
-template <int B>
-__device__ __forceinline__ int after_all(const float (&acc)[B][8]) {
-    int z = 0;
-#pragma unroll
-    for (int bb = 0; bb < B; ++bb)
-        asm volatile("; wait for %1..%8\n\tv_mov_b32 %0, 0"
-                     : "=v"(z)
-                     : "v"(acc[bb][0]), "v"(acc[bb][1]), "v"(acc[bb][2]), "v"(acc[bb][3]),
-                       "v"(acc[bb][4]), "v"(acc[bb][5]), "v"(acc[bb][6]), "v"(acc[bb][7]), "0"(z));
-    return z;
+// Flag words (serial order): [0, G) completion of each workgroup, then the
+// exit counter on a line of its own.
+constexpr int kFlagExit = 1024;
+
+// Hidden-state elements of a workgroup (NS * 4 * B) held per control lane:
+// at most 3, so the control wave's registers stay few (the host keeps NS
+// small enough).
+constexpr int stream_elems_per_lane(int b) {
+    return (kStreamMaxNS * 4 * b + 63) / 64 < 3 ? (kStreamMaxNS * 4 * b + 63) / 64 : 3;
 }
 
-// Grid-wide "point complete" signal as a two-level tree. A single counter
-// that every workgroup increments and polls serialises hundreds of atomics
-// and loads on one address (microseconds per point). Here workgroup g
-// arrives on group counter g % M; the last arrival of a group arrives on the
-// top counter; the last group's arrival writes every group's release word;
-// workgroups wait on their own group's release word. Counters only grow
-// during a launch (point j is complete when a counter reaches (j+1) x its
-// arrivals per point); the last workgroup to leave resets them.
-struct TreeBarrier {
-    uint32_t* sync;
-    int groups;  // active groups: min(kTreeGroups, grid)
-    __device__ uint32_t* group_ctr(int q) const { return sync + kTreeGroupBase + q * kTreeLine; }
-    __device__ uint32_t* release(int q) const { return sync + kTreeReleaseBase + q * kTreeLine; }
-    __device__ uint32_t* top() const { return sync + kTreeTop; }
+// Wave-uniform cursor over a compute wave's stream of segments: segment
+// (j, m0) is row blocks m0 .. m0+SL-1 of this wave's blocks of point j.
+struct Cursor {
+    int j, m0;
 };
 
-// Control wave of workgroup g: point j's strips of this workgroup are done.
-__device__ __forceinline__ void tree_arrive(const TreeBarrier& tb, int g, int G, int j, int lane) {
-    const int q = g % tb.groups;
-    const uint32_t members = (uint32_t)((G - 1 - q) / tb.groups + 1);
-    int last = 0;
-    if (lane == 0) {
-        const uint32_t old = add_dev_u32(tb.group_ctr(q), 1u);
-        if (old + 1 == members * (uint32_t)(j + 1)) {
-            const uint32_t t = add_dev_u32(tb.top(), 1u);
-            last = t + 1 == (uint32_t)tb.groups * (uint32_t)(j + 1);
-        }
-    }
-    if (__builtin_amdgcn_readfirstlane(last)) {
-        for (int r = lane; r < tb.groups; r += 64) st_dev_u32(tb.release(r), (uint32_t)(j + 1));
-    }
-}
+template <int B, int SL, bool SERIAL>
+__global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs a) {
+    extern __shared__ __align__(16) uint32_t xs[];             // two x buffers, bf16 pairs
+    __shared__ float red[2][kStreamMaxWaves - 1][B * 4];        // per point parity
 
-// Lane 0: wait until point j-1 is complete (release word of my group >= j).
-__device__ __forceinline__ bool tree_wait(const TreeBarrier& tb, int g, int j, uint32_t* err,
-                                          uint32_t limit) {
-    return wait_at_least(tb.release(g % tb.groups), (uint32_t)j, err, limit);
-}
-
-template <int B, int NW, int NI>
-__global__ __launch_bounds__((NW + 1) * 64) void decode_strips(StripArgs a) {
-    extern __shared__ __align__(16) uint16_t xs[];    // x of the current point, [rows][B] bf16
-    __shared__ float red[NW * B * 8];
-    __shared__ float h_strip[kStripMaxPerWg * B * 8]; // this workgroup's strips of the hidden state
-    __shared__ int flag;
-
-    // The wave index and everything derived from the task index are
-    // wave-uniform; readfirstlane tells the compiler, which then keeps them
-    // in scalar registers.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t* err = a.sync + kSyncErr;
+    const int g = blockIdx.x, G = gridDim.x;
+    const int n_points = 2 * a.layers;
     const int len = B * a.H;
-    const int G = gridDim.x;
-    TreeBarrier tb;
-    tb.sync = a.sync;
-    tb.groups = G < kTreeGroups ? G : kTreeGroups;
-    const int my_strips = (a.strips - (int)blockIdx.x + G - 1) / G;
-    // task t of this workgroup: point j = t / my_strips, strip s = g + (t % my_strips) * G
-    // (all task, row and element indices fit in 32 bits; the host checks)
-    const int n_tasks = a.layers * 2 * my_strips;
-    auto task_point = [&](int t) { return t / my_strips; };
-    auto task_strip = [&](int t) { return (int)blockIdx.x + (t % my_strips) * G; };
-    auto task_k = [&](int t) { return (task_point(t) & 1) ? a.K1 : a.K0; };
 
-    // Per task: barrier A (x of the point staged, or the wait failed), then
-    // barrier B (the compute waves' sums are in LDS). The two roles run
-    // separate loops with the same barriers, so neither role's registers
-    // are live in the other's code.
+    // zero both x buffers: rows past a point's K are multiplied by zero
+    // weights and must hold finite values
+    for (int i = tid; i < a.xdwords; i += blockDim.x) xs[i] = 0u;
+    __syncthreads();
+
     if (wave == 0) {
         // ---------------------------------------------------- control wave
-        // Its few memory operations (wait, x, signal) are the serial path of
-        // the step: give them issue priority over the compute waves' bulk
-        // weight loads in this CU.
         __builtin_amdgcn_s_setprio(3);
-        for (int e = lane; e < my_strips * B * 8; e += 64) {
-            const int k = e / (B * 8), bb = (e / 8) % B, c = e % 8;
-            const int64_t s = blockIdx.x + (int64_t)k * G;
-            h_strip[e] = a.hidden[(int64_t)bb * a.H + s * 8 + c];
-        }
-        // the other ranks' values of the task, loaded ahead, in ring order
-        float others[8];
-        auto fetch_others = [&](int t) {
-            if (lane >= B * 8) return;
-            const int j = task_point(t), s = task_strip(t);
-            const int i = (lane / 8) * a.H + s * 8 + (lane % 8);
-            const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
-            const int c = i / a.chunk;
+        constexpr int EQ_MAX = stream_elems_per_lane(B);
+        const int n_el = a.NS * 4 * B;
+        // element e = (b * NS + si) * 4 + c -> hidden index b*H + 4*(g + si*G) + c
+        int idx[EQ_MAX];
+        bool valid[EQ_MAX];
+        float h[EQ_MAX];
+        float oth[EQ_MAX][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                int r = c + u;
-                if (r >= a.n_ranks) r -= a.n_ranks;
-                others[u] = (u < a.n_ranks && r != a.rank) ? slot[(int64_t)r * len + i] : 0.f;
-            }
-        };
-        if (n_tasks > 0) fetch_others(0);
-        for (int t = 0; t < n_tasks; ++t) {
-            const int j = task_point(t), s = task_strip(t), K = task_k(t);
-            // point j reads its activation only after point j-1 is complete
-            int ok = 1;
-            if (lane == 0 && t % my_strips == 0) ok = tree_wait(tb, blockIdx.x, j, err, a.spin_limit);
-            ok = __builtin_amdgcn_readfirstlane(ok);
-            if (ok) {
-                // stage x_j as [rows][B] bf16; rows past K (up to the padded
-                // row count the compute lanes walk) are zero, so the multiply
-                // loop needs no per-row test (the weights there read as zero)
-                const uint16_t* x = ((j & 1) ? a.x1 : a.x0) + (int64_t)(j >> 1) * B * K;
-                const int rows = (K + NW * 64 - 1) / (NW * 64) * (NW * 64);
-                if (B == 1) {
-                    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x);
-                    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs);
-                    for (int v = lane; v < rows / 8; v += 64)
-                        dst[v] = v < K / 8 ? src[v] : u32x4_t{0u, 0u, 0u, 0u};
-                } else {
-                    for (int e = lane; e < K * B; e += 64) {
-                        const int bb = e / K, r = e - bb * K;
-                        xs[r * B + bb] = x[e];
-                    }
-                    for (int e = K * B + lane; e < rows * B; e += 64) xs[e] = 0;
+        for (int q = 0; q < EQ_MAX; ++q) {
+            const int e = lane + 64 * q;
+            const int c = e & 3, si = (e >> 2) % a.NS, b = (e >> 2) / a.NS;
+            const int s = g + si * G;
+            valid[q] = e < n_el && s < a.S;
+            idx[q] = valid[q] ? b * a.H + 4 * s + c : 0;
+            h[q] = valid[q] ? a.hidden[idx[q]] : 0.f;
+        }
+        auto fetch_others = [&](int j) {
+            const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
+#pragma unroll
+            for (int q = 0; q < EQ_MAX; ++q) {
+                const int cidx = idx[q] / a.chunk;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    int r = cidx + u;
+                    if (r >= a.n_ranks) r -= a.n_ranks;
+                    oth[q][u] = (valid[q] && u < a.n_ranks && r != a.rank)
+                                    ? slot[(int64_t)r * len + idx[q]] : 0.f;
                 }
             }
-            if (lane == 0) flag = ok;
-            __syncthreads();  // A
-            if (!ok) break;
-            __syncthreads();  // B
-            if (lane < B * 8) {
-#pragma clang fp contract(off)
-                float v = red[lane];
+        };
+        // x of point j -> its buffer (j & 1), as 1 KB direct-to-LDS copies;
+        // lanes past the end re-read the last vector into the buffer's pad
+        auto stage_x = [&](int j) {
+            const int t = j & 1, l = j >> 1;
+            const int K = t ? a.K1 : a.K0;
+            const uint16_t* src = (t ? a.x1 : a.x0) + (int64_t)l * B * K;
+            const int n16 = B * K / 8;
+            uint32_t* dst = xs + (t ? a.xoff1 : 0);
+            for (int v0 = 0; v0 < n16; v0 += 64) {
+                int v = v0 + lane;
+                v = v < n16 ? v : n16 - 1;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)v * 8),
+                                                 (lds_void_t*)(dst + v0 * 4), 16, 0, 0);
+            }
+        };
+        uint32_t* err = a.err;
+        int ok = 1;
+        // serial order: wait until every workgroup has completed point j
+        auto grid_wait = [&](int j) {
+            if (!ok) return;
+            const uint32_t target = (uint32_t)(j + 1);
+            for (uint32_t n = 0;; ++n) {
+                uint32_t mn = 0xffffffffu;
+                for (int w0 = lane; w0 < G; w0 += 64) {
+                    const uint32_t f = ld_dev_u32(a.flags + w0);
+                    mn = f < mn ? f : mn;
+                }
+                const bool done = __builtin_amdgcn_ballot_w64(mn < target) == 0;
+                if (done) return;
+                if ((n & 15) == 15 && __builtin_amdgcn_readfirstlane(ld_dev_u32(err))) { ok = 0; return; }
+                if (n >= a.spin_limit) {
+                    if (lane == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = 0;
+                    return;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        };
+
+        stage_x(0);
+        if (!SERIAL && n_points > 1) stage_x(1);
+        fetch_others(0);
+        wait_mem();
+        __syncthreads();  // start: x of the first point(s) is in LDS
+
+        for (int j = 0; j < n_points; ++j) {
+            __syncthreads();  // P_j: the compute waves' sums of point j are in red[j & 1]
+            float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
 #pragma unroll
-                for (int w = 1; w < NW; ++w) v += red[w * B * 8 + lane];
-                const int i = (lane / 8) * a.H + s * 8 + (lane % 8);
-                float* slot = a.slots + (int64_t)j * a.n_ranks * len;
-                slot[(int64_t)a.rank * len + i] = v;
+            for (int q = 0; q < EQ_MAX; ++q) {
+#pragma clang fp contract(off)
+                if (!valid[q]) continue;
+                const int e = lane + 64 * q;
+                const int c = e & 3, si = (e >> 2) % a.NS, b = (e >> 2) / a.NS;
+                float v = red[j & 1][si * a.WPS][b * 4 + c];
+                for (int wi = 1; wi < a.WPS; ++wi) v += red[j & 1][si * a.WPS + wi][b * 4 + c];
+                slot[idx[q]] = v;
                 // ring order: chunk c starts at rank c, then c+1, ... (mod N)
-                const int c = i / a.chunk;
+                const int cidx = idx[q] / a.chunk;
                 float sum = 0.f;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     if (u < a.n_ranks) {
-                        int r = c + u;
+                        int r = cidx + u;
                         if (r >= a.n_ranks) r -= a.n_ranks;
-                        const float val = r == a.rank ? v : others[u];
+                        const float val = r == a.rank ? v : oth[q][u];
                         sum = u == 0 ? val : sum + val;
                     }
                 }
-                float* hs = h_strip + (t % my_strips) * B * 8 + lane;
-                const float h = sum + *hs;
-                *hs = h;
-                // The strip's hidden state lives in this workgroup's LDS for
-                // the whole step (no other workgroup reads it), so the store
-                // is for the caller only and the strip can count as done now.
-                a.hidden[i] = h;
+                h[q] = sum + h[q];
             }
-            // this workgroup's strips of point j are done after its last one
-            if (t % my_strips == my_strips - 1) tree_arrive(tb, blockIdx.x, G, j, lane);
-            if (t + 1 < n_tasks) fetch_others(t + 1);
+            if (j + 1 < n_points) fetch_others(j + 1);
+            if (SERIAL) {
+                if (j + 1 < n_points) {
+                    wait_mem();
+                    if (lane == 0) st_dev_u32(a.flags + g, (uint32_t)(j + 1));
+                    grid_wait(j);
+                    stage_x(j + 1);
+                    wait_mem();
+                    __syncthreads();  // A_{j+1}: x of point j+1 is in LDS
+                }
+            } else {
+                if (j + 2 < n_points) stage_x(j + 2);
+                wait_mem();  // x staged before P_{j+1}; needed from P_{j+1} on
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EQ_MAX; ++q)
+            if (valid[q]) a.hidden[idx[q]] = h[q];
+        if (SERIAL) {
+            // the last workgroup to leave clears the flags for the next launch
+            wait_mem();
+            int last = 0;
+            if (lane == 0) last = add_dev_u32(a.flags + kFlagExit, 1u) == (uint32_t)G - 1;
+            if (__builtin_amdgcn_readfirstlane(last)) {
+                for (int w0 = lane; w0 < G; w0 += 64) st_dev_u32(a.flags + w0, 0u);
+                if (lane == 0) st_dev_u32(a.flags + kFlagExit, 0u);
+            }
         }
     } else {
         // --------------------------------------------------- compute waves
         const int cw = wave - 1;
-        // Weight loads go through a buffer descriptor per task: one lane
-        // offset VGPR, a uniform scalar offset per load, and the hardware
-        // range check returns zeros past the strip's K rows.
-        u32x4_t wv[NI];
-        const int lane_off = (cw * 64 + lane) * 16;
-        auto issue = [&](int t, int dep) {
-            const int j = task_point(t), s = task_strip(t), K = task_k(t);
-            const uint16_t* base = ((j & 1) ? a.w1 : a.w0) + ((int64_t)(j >> 1) * a.strips + s) * K * 8;
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(base), (short)0, K * 16, kBufferRsrcWord3);
-            const int ni_used = (K + NW * 64 - 1) / (NW * 64);  // wave-uniform
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-                if (i < ni_used)
-                    wv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                            rs, lane_off + dep, i * NW * 1024, kCachePolicyNT));
+        const int si = cw / a.WPS, wi = cw - si * a.WPS;
+        const bool active = si < a.NS && g + si * G < a.S;
+        const int s = g + si * G;
+        const int voff = lane * 16 + wi * kBlockBytes;  // + block offset: all in the VGPR
+                                                        // offset, which the range check covers
+        const int stride = a.WPS * kBlockBytes;
+
+        auto bpw = [&](int j) { return (j & 1) ? a.bpw1 : a.bpw0; };
+        auto advance = [&](Cursor& cu) {
+            cu.m0 += SL;
+            if (cu.m0 >= bpw(cu.j)) { cu.j += 1; cu.m0 = 0; }
         };
-        if (n_tasks > 0) issue(0, 0);
-        for (int t = 0; t < n_tasks; ++t) {
-            const int K = task_k(t);
-            __syncthreads();  // A
-            if (!__builtin_amdgcn_readfirstlane(flag)) break;
-            float acc[B][8];
+        // SL loads, always issued; a segment past the strip or the step has
+        // an empty range and reads zeros without a memory access
+        auto issue = [&](u32x4_t (&bank)[SL], const Cursor& cu) {
+            const int t = cu.j & 1, l = cu.j >> 1;
+            const int kh = t ? a.Kh1 : a.Kh0;
+            const bool live = active && cu.j < n_points;
+            const uint16_t* base = (t ? a.w1 : a.w0) + ((int64_t)l * a.S + s) * kh * 8;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(live ? base : a.w0), (short)0, live ? kh * 16 : 0,
+                kBufferRsrcWord3);
 #pragma unroll
-            for (int bb = 0; bb < B; ++bb)
+            for (int i = 0; i < SL; ++i)
+                bank[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rs, voff + (cu.m0 + i) * stride, 0, kCachePolicyNT));
+        };
+        float acc[B][4];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[bb][c] = 0.f;
-            const uint16_t* xr = xs + (cw * 64 + lane) * B;
-            const int ni_used = (K + NW * 64 - 1) / (NW * 64);  // wave-uniform
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                if (i < ni_used) {
-                    const u32x4_t wq = wv[i];
-                    const float wf[8] = {bf16_lo(wq.x), bf16_hi(wq.x), bf16_lo(wq.y), bf16_hi(wq.y),
-                                         bf16_lo(wq.z), bf16_hi(wq.z), bf16_lo(wq.w), bf16_hi(wq.w)};
+            for (int c = 0; c < 4; ++c) acc[b][c] = 0.f;
+        auto consume = [&](const u32x4_t (&bank)[SL], const Cursor& cu) {
+            const int t = cu.j & 1;
+            const int kh = t ? a.Kh1 : a.Kh0;
+            const uint32_t* xb = xs + (t ? a.xoff1 : 0);
 #pragma unroll
-                    for (int bb = 0; bb < B; ++bb) {
-                        const float xv = bf16_to_f32(xr[i * NW * 64 * B + bb]);
+            for (int i = 0; i < SL; ++i) {
+                const int kp = (wi + (cu.m0 + i) * a.WPS) * 64 + lane;
+                const u32x4_t wq = bank[i];
+                const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) acc[bb][c] = __builtin_fmaf(xv, wf[c], acc[bb][c]);
-                    }
+                for (int b = 0; b < B; ++b) {
+                    const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xb[b * kh + kp]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[b][c] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2_t, wd[c]), xv, acc[b][c], false);
                 }
             }
-            // loads that take this opaque zero cannot move above the multiplies
-            const int dep = after_all(acc);
-            // sum over the wave's 64 rows
+        };
+        auto point_end = [&](int j) {
 #pragma unroll
-            for (int bb = 0; bb < B; ++bb)
+            for (int b = 0; b < B; ++b)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[bb][c] = wave_sum(acc[bb][c]);
-            if (lane < B * 8) {
-                float v = 0.f;
-#pragma unroll
-                for (int bb = 0; bb < B; ++bb)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        if (lane == bb * 8 + c) v = acc[bb][c];
-                red[cw * B * 8 + lane] = v;
+                for (int c = 0; c < 4; ++c) {
+                    const float v = wave_sum(acc[b][c]);
+                    if (lane == 0) red[j & 1][cw][b * 4 + c] = v;
+                    acc[b][c] = 0.f;
+                }
+            __syncthreads();                                   // P_j
+            if (SERIAL && j + 1 < n_points) __syncthreads();   // A_{j+1}
+        };
+
+        u32x4_t bank0[SL], bank1[SL];
+        Cursor ci{0, 0}, cc{0, 0};
+        issue(bank0, ci);
+        advance(ci);
+        issue(bank1, ci);
+        advance(ci);
+        __syncthreads();  // start
+        while (cc.j < n_points) {
+            {
+                consume(bank0, cc);
+                const int j = cc.j;
+                const bool last = cc.m0 + SL >= bpw(j);
+                advance(cc);
+                issue(bank0, ci);
+                advance(ci);
+                if (last) point_end(j);
             }
-            __syncthreads();  // B
-            // the registers are free: start the next task's weights
-            if (t + 1 < n_tasks) issue(t + 1, dep);
-        }
-    }
-    // The last workgroup to leave resets the step's sync words for the next
-    // launch (no workgroup reads them any more).
-    __syncthreads();
-    if (wave == 0) {
-        int last = 0;
-        if (lane == 0) last = add_dev_u32(a.sync + kSyncExit, 1u) == gridDim.x - 1;
-        if (__builtin_amdgcn_readfirstlane(last)) {
-            for (int r = lane; r < kTreeGroups; r += 64) {
-                st_dev_u32(tb.group_ctr(r), 0u);
-                st_dev_u32(tb.release(r), 0u);
-            }
-            if (lane == 0) {
-                st_dev_u32(tb.top(), 0u);
-                st_dev_u32(a.sync + kSyncExit, 0u);
+            {
+                const bool live = cc.j < n_points;
+                int j = cc.j;
+                bool last = false;
+                if (live) {
+                    consume(bank1, cc);
+                    last = cc.m0 + SL >= bpw(j);
+                    advance(cc);
+                }
+                issue(bank1, ci);
+                advance(ci);
+                if (last) point_end(j);
             }
         }
     }
 }
 
-typedef void (*strip_fn)(StripArgs);
+typedef void (*stream_fn)(StreamArgs);
 
-template <int NW, int NI>
-strip_fn strip_kernel_for(int b) {
+template <int SL, bool SERIAL>
+stream_fn stream_kernel_for(int b) {
+    static_assert(SL == 4, "8-load banks: stream_kernel_sl8");
     switch (b) {
-        case 1: return decode_strips<1, NW, NI>;
-        case 2: return decode_strips<2, NW, NI>;
-        case 3: return decode_strips<3, NW, NI>;
-        case 4: return decode_strips<4, NW, NI>;
-        case 5: return decode_strips<5, NW, NI>;
-        case 6: return decode_strips<6, NW, NI>;
-        case 7: return decode_strips<7, NW, NI>;
-        case 8: return decode_strips<8, NW, NI>;
+        case 1: return decode_stream<1, SL, SERIAL>;
+        case 2: return decode_stream<2, SL, SERIAL>;
+        case 3: return decode_stream<3, SL, SERIAL>;
+        case 4: return decode_stream<4, SL, SERIAL>;
+        case 5: return decode_stream<5, SL, SERIAL>;
+        case 6: return decode_stream<6, SL, SERIAL>;
+        case 7: return decode_stream<7, SL, SERIAL>;
+        case 8: return decode_stream<8, SL, SERIAL>;
     }
+    return nullptr;
+}
+
+// 8-load banks only for batch <= 4 (beyond, the registers would spill).
+template <bool SERIAL>
+stream_fn stream_kernel_sl8(int b) {
+    switch (b) {
+        case 1: return decode_stream<1, 8, SERIAL>;
+        case 2: return decode_stream<2, 8, SERIAL>;
+        case 3: return decode_stream<3, 8, SERIAL>;
+        case 4: return decode_stream<4, 8, SERIAL>;
+    }
+    return nullptr;
+}
+
+stream_fn stream_kernel(int b, int sl, bool serial) {
+    if (sl == 4) return serial ? stream_kernel_for<4, true>(b) : stream_kernel_for<4, false>(b);
+    if (sl == 8) return serial ? stream_kernel_sl8<true>(b) : stream_kernel_sl8<false>(b);
     return nullptr;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Kernel variants: compute waves per workgroup x 16-byte weight vectors per
-// compute lane. A task (one strip of one point) must fit: K <= NI * NW * 64.
-// Workgroups are 4 or 8 waves (control + NW): a workgroup's waves are spread
-// round-robin over the CU's four SIMDs, so only multiples of 4 let the
-// residency that the occupancy query reports actually be reached (the
-// cooperative grid relies on it).
-struct StripVariant {
-    int nw, ni;
-    strip_fn (*get)(int);
-};
-const StripVariant kStripVariants[] = {
-    {7, 10, strip_kernel_for<7, 10>},
-    {3, 24, strip_kernel_for<3, 24>},
-    {7, 20, strip_kernel_for<7, 20>},
-};
-
 }  // namespace
 
-// Can the strip step run this plan? (batch, ranks, K alignment, LDS for x)
-int tp_strip_loads(const tp_plan_s* p) {
-    if (p->batch > kStripMaxBatch || p->n_ranks > 8) return 0;
+// Geometry of the streamed step for a plan (host side; see tp_internal.h).
+bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
+    if (p->batch < 1 || p->batch > kStripMaxBatch || p->n_ranks > 8) return false;
+    if (p->hidden % 4) return false;
     const int64_t k0 = p->k_attn / p->n_ranks, k1 = p->inter / p->n_ranks;
-    const int64_t kmax = k0 > k1 ? k0 : k1;
-    if (k0 % 8 || k1 % 8) return 0;
-    if (kmax * p->batch * 2 > kStripMaxXsBytes) return 0;
-    for (const StripVariant& v : kStripVariants)
-        if (kmax <= (int64_t)v.ni * v.nw * 64) return v.ni;
-    return 0;
+    if (k0 < 2 || k1 < 2 || (k0 & 1) || (k1 & 1)) return false;
+    if ((k0 * p->batch) % 8 || (k1 * p->batch) % 8) return false;
+    const int64_t S = p->hidden / 4;
+    int64_t ns = (S + kTargetCUs - 1) / kTargetCUs;
+    if (ns > kStreamMaxNS) ns = kStreamMaxNS;
+    const int64_t G = (S + ns - 1) / ns;
+    if (ns * 4 * p->batch > 64 * stream_elems_per_lane(p->batch)) return false;
+    const int wps = (int)((kStreamMaxWaves - 1) / ns);
+    const int sl = p->segment_loads == 8 && p->batch <= 4 ? 8 : 4;
+    const int64_t kh0 = k0 / 2, kh1 = k1 / 2;
+    const int64_t nb0 = (kh0 + 63) / 64, nb1 = (kh1 + 63) / 64;
+    const int64_t bpw0 = (nb0 + wps - 1) / wps, bpw1 = (nb1 + wps - 1) / wps;
+    // x buffer t: B*Kh_t dwords staged in 1 KB pieces, and every pair index a
+    // compute lane reads (up to the last block of its last segment)
+    auto xbuf = [&](int64_t kh, int64_t bpw) {
+        const int64_t n16 = p->batch * kh * 4 / 16;
+        const int64_t staged = (n16 + 63) / 64 * 256;
+        const int64_t segs = (bpw + sl - 1) / sl;
+        const int64_t read = (p->batch - 1) * kh + ((wps - 1) + (segs * sl - 1) * wps) * 64 + 64;
+        const int64_t d = staged > read ? staged : read;
+        return (d + 255) / 256 * 256;
+    };
+    g->xoff1 = xbuf(kh0, bpw0);
+    g->xdwords = g->xoff1 + xbuf(kh1, bpw1);
+    g->grid = (int32_t)G;
+    g->ns = (int32_t)ns;
+    g->wps = wps;
+    g->sl = sl;
+    g->block = (int32_t)(1 + ns * wps) * 64;
+    g->kh0 = (int32_t)kh0;
+    g->kh1 = (int32_t)kh1;
+    g->bpw0 = (int32_t)bpw0;
+    g->bpw1 = (int32_t)bpw1;
+    g->lds_bytes = g->xdwords * 4;
+    return g->lds_bytes <= kStreamMaxLdsBytes;
 }
 
-namespace {
-
-// Pick the variant whose resident grid covers the most strips per wave
-// (ideally every strip has its own workgroup). Returns false if none fits.
-bool pick_strip_variant(const tp_plan_s* p, int64_t kmax, strip_fn* fn, int* block, int* grid,
-                        int* xs_out) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return false;
-    const int64_t strips = p->hidden / 8;
-    int64_t best_per_wg = -1;
-    int idx = 0;
-    for (const StripVariant& v : kStripVariants) {
-        ++idx;
-        if (p->strip_variant && idx != p->strip_variant) continue;
-        if (kmax > (int64_t)v.ni * v.nw * 64) continue;
-        strip_fn k = v.get(p->batch);
-        if (!k) continue;
-        const int blk = (v.nw + 1) * 64;
-        const int64_t rows = (kmax + v.nw * 64 - 1) / (v.nw * 64) * (v.nw * 64);
-        const int xs_bytes = (int)(rows * p->batch * 2);
-        if (xs_bytes > kStripMaxXsBytes) continue;
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k),
-                                                         blk, xs_bytes) != hipSuccess)
-            continue;
-        const int64_t cap = (int64_t)per_cu * cus;
-        if (cap < 1) continue;
-        const int64_t g = strips < cap ? strips : cap;
-        const int64_t per_wg = (strips + g - 1) / g;
-        if (per_wg > kStripMaxPerWg) continue;
-        if (best_per_wg < 0 || per_wg < best_per_wg) {
-            best_per_wg = per_wg;
-            *fn = k;
-            *block = blk;
-            *grid = (int)g;
-            *xs_out = xs_bytes;
-        }
-    }
-    return best_per_wg > 0;
+int tp_strip_loads(const tp_plan_s* p) {
+    StreamGeom g;
+    return tp_stream_geometry(p, &g) ? 1 : 0;
 }
-
-}  // namespace
 
 extern "C" {
 
@@ -437,11 +477,12 @@ tp_status tp_pack_weights(tp_plan_t p, int32_t point, int32_t n_layers, const vo
     if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
     if (w == w_packed) return TP_ERR_INVALID_ARG;
+    if (p->hidden % 4) return TP_ERR_UNSUPPORTED;
     const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
-    const int64_t total = (int64_t)n_layers * K * (p->hidden / 8);
+    const int64_t total = (int64_t)n_layers * ((K + 1) / 2) * (p->hidden / 4);
     if (total == 0) return TP_OK;
     const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
-    hipLaunchKernelGGL(pack_strips_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(pack_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint16_t*>(w), static_cast<uint16_t*>(w_packed),
                        (int64_t)n_layers, K, p->hidden);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
@@ -457,38 +498,57 @@ tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, c
     if (!aligned16(x_attn) || !aligned16(w_o_packed) || !aligned16(x_ffn) ||
         !aligned16(w_down_packed) || !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
         return TP_ERR_ALIGNMENT;
-    if (!tp_strip_loads(p)) return TP_ERR_UNSUPPORTED;
-    const int64_t strips = p->hidden / 8;
-    if ((int64_t)n_layers * 2 * strips >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
+    StreamGeom geo;
+    if (!tp_stream_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
+    if ((int64_t)n_layers * 2 >= ((int64_t)1 << 30)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)p->batch * p->hidden >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
+    if ((int64_t)n_layers * geo.grid * (int64_t)(geo.kh0 > geo.kh1 ? geo.kh0 : geo.kh1) * 8 >=
+        ((int64_t)1 << 62))
+        return TP_ERR_UNSUPPORTED;
+    if (geo.grid > 1024) return TP_ERR_UNSUPPORTED;  // completion words of the serial order
     if (n_layers == 0) return TP_OK;
-    StripArgs a;
+    const bool serial = p->serial_points != 0;
+    stream_fn k = stream_kernel(p->batch, geo.sl, serial);
+    if (!k) return TP_ERR_UNSUPPORTED;
+    StreamArgs a;
     a.x0 = static_cast<const uint16_t*>(x_attn);
     a.x1 = static_cast<const uint16_t*>(x_ffn);
     a.w0 = static_cast<const uint16_t*>(w_o_packed);
     a.w1 = static_cast<const uint16_t*>(w_down_packed);
     a.slots = slots;
     a.hidden = hidden;
-    a.sync = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSyncOffset);
+    a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kStreamFlagOffset);
+    a.err = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSyncOffset) + kSyncErr;
     a.H = (int32_t)p->hidden;
+    a.S = (int32_t)(p->hidden / 4);
+    a.NS = geo.ns;
+    a.WPS = geo.wps;
     a.K0 = (int32_t)(p->k_attn / p->n_ranks);
     a.K1 = (int32_t)(p->inter / p->n_ranks);
-    a.strips = (int32_t)strips;
+    a.Kh0 = geo.kh0;
+    a.Kh1 = geo.kh1;
+    a.bpw0 = geo.bpw0;
+    a.bpw1 = geo.bpw1;
     a.layers = n_layers;
     a.n_ranks = p->n_ranks;
     a.rank = rank;
     a.chunk = (int32_t)((int64_t)p->batch * p->hidden / p->n_ranks);
-    a.spin_limit = 1u << 21;
-    const int64_t kmax = a.K0 > a.K1 ? a.K0 : a.K1;
-    strip_fn k = nullptr;
-    int block = 0, grid = 0, xs_bytes = 0;
-    if (!pick_strip_variant(p, kmax, &k, &block, &grid, &xs_bytes)) return TP_ERR_UNSUPPORTED;
-    a.xs_bytes = xs_bytes;
-    void* args[] = {&a};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                   dim3((unsigned)block), args, (unsigned)a.xs_bytes,
-                                   (hipStream_t)stream) != hipSuccess)
+    a.xoff1 = geo.xoff1;
+    a.xdwords = geo.xdwords;
+    a.spin_limit = 1u << 20;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, geo.lds_bytes) != hipSuccess)
         return TP_ERR_DEVICE;
+    if (serial) {
+        void* args[] = {&a};
+        if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3((unsigned)geo.grid),
+                                       dim3((unsigned)geo.block), args, (unsigned)geo.lds_bytes,
+                                       (hipStream_t)stream) != hipSuccess)
+            return TP_ERR_DEVICE;
+    } else {
+        hipLaunchKernelGGL(k, dim3((unsigned)geo.grid), dim3((unsigned)geo.block),
+                           (unsigned)geo.lds_bytes, (hipStream_t)stream, a);
+    }
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 

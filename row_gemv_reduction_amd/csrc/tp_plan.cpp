@@ -151,9 +151,12 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "decode_mode")) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->decode_mode = (int32_t)value;
-    } else if (!strcmp(key, "strip_variant")) {
-        if (value < 0 || value > 3) return TP_ERR_INVALID_ARG;
-        p->strip_variant = (int32_t)value;
+    } else if (!strcmp(key, "segment_loads")) {
+        if (value != 0 && value != 4 && value != 8) return TP_ERR_INVALID_ARG;
+        p->segment_loads = (int32_t)value;
+    } else if (!strcmp(key, "serial_points")) {
+        if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
+        p->serial_points = (int32_t)value;
     } else if (!strcmp(key, "target_wgs")) {
         if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
         p->target_wgs = (int32_t)value;

@@ -387,25 +387,41 @@ def test_persistent_step_repeated_runs_are_identical():
 
 def pack_dev(plan, point, w_bits_host_or_dev):
     w = w_bits_host_or_dev if isinstance(w_bits_host_or_dev, torch.Tensor) else to_dev_bf16(w_bits_host_or_dev)
-    L, K, H = w.shape
-    p = torch.empty((L, H // 8, K, 8), dtype=torch.bfloat16, device="cuda")
+    p = torch.empty(tp.packed_shape(plan, point, w.shape[0]), dtype=torch.bfloat16, device="cuda")
     tp.tp_pack_weights(plan, point, w, p)
     return p
 
 
-def test_pack_weights_is_the_strip_transpose():
-    L, n, H, ka, ki = 3, 2, 1032, 640, 2000
+def test_pack_weights_is_the_pair_strip_layout():
+    # P[l][s][kp][c][q] = W[l][2kp+q][4s+c], rows past K zero (k = 321 is odd)
+    L, n, H, ka, ki = 3, 2, 1032, 642, 2000
     plan = tp.Plan(H, ki, n, 1, k_attn=ka)
     say("pack layout")
     for point, k in ((0, ka // n), (1, ki // n)):
         w = synth.normal_bf16((L, k, H), synth.WEIGHT_STD, seed=4, tensor="w", layer=point)
         p = pack_dev(plan, point, w)
         torch.cuda.synchronize()
-        want = w.reshape(L, k, H // 8, 8).transpose(0, 2, 1, 3)
-        assert_bits_equal(bf16_bits_host(p), np.ascontiguousarray(want), "packed point %d" % point)
+        kh = (k + 1) // 2
+        wz = np.zeros((L, 2 * kh, H), np.uint16)
+        wz[:, :k] = w
+        want = wz.reshape(L, kh, 2, H // 4, 4).transpose(0, 3, 1, 4, 2)
+        assert_bits_equal(bf16_bits_host(p), np.ascontiguousarray(want).reshape(L, H // 4, kh, 8),
+                          "packed point %d" % point)
 
 
 def run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
+    """Both point orders on the same inputs; they must give the same bits."""
+    outs = []
+    for serial in (0, 1):
+        plan.tune("serial_points", serial)
+        outs.append(_run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps))
+    plan.tune("serial_points", 0)
+    assert_bits_equal(outs[0][0], outs[1][0], "slots, dataflow vs serial order")
+    assert_bits_equal(outs[0][1], outs[1][1], "hidden, dataflow vs serial order")
+    return outs[0]
+
+
+def _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
     ws = plan.new_workspace()
     S = to_dev_f32(slots)
     Hd = to_dev_f32(h0)
