@@ -255,34 +255,52 @@ tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank
 /*
  * Top-k routing of decode tokens ("Hosting Qwen on Blackwell", Prefillers:
  * each token goes to top_k of the experts). Per token: softmax over the
- * experts' logits, the top_k experts by probability (ties to the lower
- * index), their probabilities renormalised to sum to 1 (renorm != 0) or
- * left as they are; listed in ascending expert order.
- *   logits fp32 [tokens][n_experts]
+ * experts' logits (computed in double), the top_k experts by probability
+ * (ties to the lower index), their probabilities renormalised to sum to 1
+ * (renorm != 0) or left as they are; listed in ascending expert order.
+ *   logits fp32 [tokens][n_experts] (finite or -inf; NaN is not allowed)
  *   sel_expert int32 [tokens][top_k], sel_weight fp32 [tokens][top_k] (outputs)
- * tokens <= max_tokens of tp_plan_set_moe. The expert choice compares the
- * fp32 logits directly, so it is exact.
+ * The expert choice compares the fp32 logits directly (softmax is
+ * monotone), so it is exact. TP_ERR_INVALID_ARG if the plan has no MoE
+ * share or tokens > max_tokens; TP_ERR_UNSUPPORTED if n_experts > 2048.
  */
 tp_status tp_moe_route(tp_plan_t plan, const float* logits, int32_t tokens, int32_t renorm,
                        int32_t* sel_expert, float* sel_weight, void* stream);
+
+/*
+ * Pack one rank's experts for tp_moe_partial, once, at load time:
+ *     w_local  bf16 [E/ep][moe_inter][hidden] (row-major, as trained)
+ *     w_packed bf16 [E/ep][ceil(moe_inter/2)][hidden/4][8], with
+ *     w_packed[e][kp][g][2c + q] = w_local[e][2kp + q][4g + c]
+ * (rows past moe_inter are zero): each 16-byte vector is a pair of rows of
+ * 4 columns, one bf16 pair per column, and a row pair of an expert is
+ * contiguous across all columns. Same bytes as the row-major experts.
+ */
+tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packed, void* stream);
 
 /*
  * Expert-parallel down projection and local weighted combine for rank
  * `rank` ("Hosting Qwen on Blackwell", MoE Dispatch-Combine and Expert
  * Parallel: the combine first accumulates, per token, the contributions of
  * the experts on this rank, weighted by the routing weights; the all-reduce
- * over ranks follows):
+ * over ranks follows, e.g. tp_ring_reduce over the ep ranks' parts):
  *     part[t, :] = sum over s with sel_expert[t,s] on this rank, in
  *                  ascending expert order, of sel_weight[t,s] * (u[t,s,:] . W_e)
  *   sel_expert int32 [tokens][top_k], sel_weight fp32 [tokens][top_k]
- *   u       bf16 [tokens][top_k][moe_inter]: one activation per selection
- *   w_local bf16 [E/ep][moe_inter][hidden]: this rank's experts, in order
- *   part    fp32 [tokens][hidden] (output)
- * Experts that no token selected are not read.
+ *   u        bf16 [tokens][top_k][moe_inter]: one activation per selection
+ *   w_packed this rank's experts packed by tp_moe_pack_experts
+ *   part     fp32 [tokens][hidden] (output; rows of tokens with no local
+ *            expert are zero)
+ * Each projection accumulates in fp32 (fixed order); the combine adds the
+ * local experts' weighted rows in ascending expert order. Experts that no
+ * token selected are not read. Expert ids outside this rank's range are
+ * skipped. Uses the workspace (pair table and per-selection rows).
+ * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8 or larger than
+ * 4096, or E/ep > 8192.
  */
 tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                          const float* sel_weight, int32_t tokens, const void* u,
-                         const void* w_local, float* part, void* workspace, void* stream);
+                         const void* w_packed, float* part, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

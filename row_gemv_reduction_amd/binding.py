@@ -71,6 +71,8 @@ EXPORTS = {
     "tp_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]),
+    "tp_moe_pack_experts": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
     "tp_moe_partial": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -281,14 +283,28 @@ def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):
            "tp_moe_route")
 
 
-def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_local, part, workspace):
+def moe_packed_shape(plan: Plan):
+    """Shape of a rank's packed experts: [E/ep, ceil(moe_inter/2), H/4, 8]."""
+    i = plan.info()
+    return (i["local_experts"], (i["moe_inter"] + 1) // 2, i["hidden"] // 4, 8)
+
+
+def tp_moe_pack_experts(plan: Plan, w_local, w_packed):
+    i = plan.info()
+    le, mi, H = i["local_experts"], i["moe_inter"], i["hidden"]
+    _check(_lib().tp_moe_pack_experts(plan.handle, _dev(w_local, "w_local", torch.bfloat16, (le, mi, H)),
+                                      _dev(w_packed, "w_packed", torch.bfloat16, moe_packed_shape(plan)),
+                                      _stream()), "tp_moe_pack_experts")
+
+
+def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, part, workspace):
     i = plan.info()
     t = sel_expert.shape[0]
-    k, le, mi, H = i["top_k"], i["local_experts"], i["moe_inter"], i["hidden"]
+    k, mi, H = i["top_k"], i["moe_inter"], i["hidden"]
     args = (_dev(sel_expert, "sel_expert", torch.int32, (t, k)),
             _dev(sel_weight, "sel_weight", torch.float32, (t, k)))
     rest = (_dev(u, "u", torch.bfloat16, (t, k, mi)),
-            _dev(w_local, "w_local", torch.bfloat16, (le, mi, H)),
+            _dev(w_packed, "w_packed", torch.bfloat16, moe_packed_shape(plan)),
             _dev(part, "part", torch.float32, (t, H)), _dev(workspace, "workspace", torch.uint8))
     if workspace.numel() < i["workspace_bytes"]:
         raise ValueError("workspace too small")

@@ -94,3 +94,4 @@ struct StreamGeom {
 };
 bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
 int tp_strip_loads(const tp_plan_s* p);  // nonzero if the streamed step can run the plan
+int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections

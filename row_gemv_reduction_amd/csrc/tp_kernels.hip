@@ -684,19 +684,4 @@ tp_status tp_decode_layers(tp_plan_t p, int32_t n_layers, int32_t rank, const vo
     return TP_OK;
 }
 
-tp_status tp_moe_route(tp_plan_t p, const float* logits, int32_t tokens, int32_t renorm,
-                       int32_t* sel_expert, float* sel_weight, void* stream) {
-    (void)p; (void)logits; (void)tokens; (void)renorm; (void)sel_expert; (void)sel_weight;
-    (void)stream;
-    return TP_ERR_UNSUPPORTED;
-}
-
-tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
-                         const float* sel_weight, int32_t tokens, const void* u,
-                         const void* w_local, float* part, void* ws, void* stream) {
-    (void)p; (void)rank; (void)sel_expert; (void)sel_weight; (void)tokens; (void)u;
-    (void)w_local; (void)part; (void)ws; (void)stream;
-    return TP_ERR_UNSUPPORTED;
-}
-
 }  // extern "C"

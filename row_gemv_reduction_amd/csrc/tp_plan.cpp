@@ -73,21 +73,8 @@ int64_t tp_ws_moe_offset(const tp_plan_s* p) {
     return tp_ws_partials_offset() + partial_bytes(p);
 }
 
-static int64_t moe_bytes(const tp_plan_s* p) {
-    if (!p->n_experts) return 0;
-    int64_t pairs = (int64_t)p->max_tokens * p->top_k;
-    int64_t le = p->n_experts / p->ep;
-    // per-expert pair lists (offsets, token, selection index), then the
-    // per-selection fp32 projections Y[pair][H] and their split-K partials
-    int64_t lists = round_up((le + 1) * 4 + pairs * 8 + 256, 256);
-    PointGeom g = tp_geom_for(p, p->moe_inter, kMfmaMinBatch, 0);
-    int64_t y = round_up(pairs * p->hidden * 4, 256);
-    int64_t parts = round_up((int64_t)g.splits * 16 * p->hidden * 4 * le, 256);
-    return lists + y + parts;
-}
-
 int64_t tp_workspace_bytes(const tp_plan_s* p) {
-    return tp_ws_moe_offset(p) + moe_bytes(p);
+    return tp_ws_moe_offset(p) + round_up(tp_moe_workspace_bytes(p), 256);
 }
 
 int tp_decode_mode(const tp_plan_s* p) {
