@@ -13,6 +13,12 @@ partials are inputs already in HBM.
 Prints one JSON line: decode tokens/s per rank-shard, plus the achieved HBM
 bandwidth of the dominant kernel against the MI355X peak (8 TB/s) and the
 CPU oracle timed on the host cores.
+
+Other workloads (--workload NAME, see row_gemv_reduction_amd/workloads.py)
+print the same line for that shape; the MoE decode share times one layer's
+share (the 8192->4096 attention output slice at 64 tokens, its ring sum,
+routing, the rank's experts and their ring sum) and rotates weight copies
+so that the weights stream from HBM rather than from the 256 MB cache.
 """
 from __future__ import annotations
 
@@ -91,38 +97,67 @@ def cpu_baseline(w, rank, xa, wo, xf, wd, slots, h0, budget_s):
                       % (reps, nl, w.layers, rank, total, w.layers)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=None, help="workload name (default: page-1 stack, N=4, b=1)")
-    ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
-    ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
-                    help="weight layout: strip-packed (packed once at load, untimed) or row-major")
-    args = ap.parse_args()
+def measured_traffic(w, layout):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), when it covers this
+    workload and the kernel source is the one the counters were taken on;
+    otherwise None."""
+    import hashlib
+    import re
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the N virtual ranks are emulated on a single "
-              "MI355X, so --gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+    from row_gemv_reduction_amd import workloads
+    if w.name != workloads.PAGE1.name or layout != "packed":
+        return None
+    try:
+        text = open(os.path.join(ROOT, "profiles", "decode_stream_page1_n4_b1.md")).read()
+        src = open(os.path.join(ROOT, "row_gemv_reduction_amd", "csrc", "tp_packed.hip"), "rb").read()
+    except OSError:
+        return None
+    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    m_sha = re.search(r"sha256 prefix ([0-9a-f]+)", text)
+    if not (m_bytes and m_sha) or not hashlib.sha256(src).hexdigest().startswith(m_sha.group(1)):
+        return None
+    return int(m_bytes.group(1))
 
+
+def time_steps(step, steps, warmup, stream):
+    """W untimed steps, then K timed steps between two HIP events recorded
+    on the stream the library launches on. Returns ms per step."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    log("timed %d steps: %.4f ms/step (events), wall %.4f ms/step" % (steps, ms, wall * 1e3 / steps))
+    return ms
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size (outside any timed region): its
+    FETCH_SIZE / WRITE_SIZE counters calibrate the decode kernel's."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: %d x %d bytes read and written" % (reps, nbytes))
+
+
+def dense_run(args, w, tune):
     import torch
 
     import row_gemv_reduction_amd as tp
-    from row_gemv_reduction_amd import workloads
-
-    w = workloads.ALL[args.workload] if args.workload else workloads.PAGE1
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    torch.cuda.set_device(0)
-    tune = {}
-    for kv in args.tune:
-        k, v = kv.split("=")
-        tune[k] = int(v)
     plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn, tune=tune)
     info = plan.info()
     log("workload %s: K_r = %s, splits %s, path %s" % (w.name, info["k_rank"], info["splits"],
@@ -133,7 +168,8 @@ def main():
     stream = torch.cuda.current_stream()
     layout = args.layout
     if layout == "auto":
-        layout = "packed" if w.batch <= 8 else "rowmajor"
+        layout = "packed" if info["packed_step"] else "rowmajor"
+    extra = {}
     if layout == "packed":
         # load-time layout change, outside the timed region
         po = torch.empty(tp.packed_shape(plan, 0, w.layers), dtype=torch.bfloat16, device="cuda")
@@ -144,56 +180,250 @@ def main():
 
         def step():
             tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
+        kernel = "decode_stream (one launch per step, %d reconciliation points)" % (2 * w.layers)
     else:
         def step():
             tp.tp_decode_layers(plan, w.layers, args.rank, xa, wo, xf, wd, slots, hidden, ws)
+        kernel = "decode step on row-major weights (%s)" % (
+            "MFMA skinny GEMM + ring epilogue, one launch per point" if w.batch >= 16
+            else "persistent VALU step")
     log("weight layout: %s" % layout)
+    ms = time_steps(step, args.steps, args.warmup, stream)
+    if layout == "packed" and not args.no_serial:
+        # the same step with the grid-wide wait per point (serial point order)
+        plan.tune("serial_points", 1)
+        ms_serial = time_steps(step, args.steps, args.warmup, stream)
+        plan.tune("serial_points", 0)
+        b_serial = w.algorithmic_bytes_per_step() / (ms_serial * 1e-3) / 1e9
+        extra["serial_point_order"] = {
+            "ms_per_step": round(ms_serial, 5), "tokens_per_s": round(w.batch / (ms_serial * 1e-3), 3),
+            "achieved_gbs": round(b_serial, 2), "frac": round(b_serial / HBM_PEAK_GBS, 4),
+            "note": "point j+1 reads its activation only after every column of point j is complete"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.rank, xa, wo, xf, wd, slots, h0, args.cpu_seconds)
+    config = {"workload": w.name, "hidden": w.hidden, "inter": w.inter, "k_attn": w.k_attn,
+              "layers": w.layers, "n_ranks": w.n_ranks, "rank": args.rank, "batch": w.batch,
+              "reductions_per_token": 2 * w.layers, "weight_layout": layout,
+              "weight_bytes_per_step": w.weight_bytes_per_step()}
+    extra["traffic"] = measured_traffic(w, layout)
+    return ms, w.batch, w.algorithmic_bytes_per_step(), kernel, config, cpu, extra
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log("warmup done (%d steps)" % args.warmup)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+def moe_build(w, rank, copies, seed=0):
+    """Inputs of the MoE decode share, `copies` independent layer copies."""
+    import torch
+
+    from row_gemv_reduction_amd import synth
+    T, H, E, k, I, ep = w.batch, w.hidden, w.n_experts, w.top_k, w.moe_inter, w.ep
+    el = E // ep
+    layers = []
+    for c in range(copies):
+        kw = dict(seed=seed, workload=w.name, rank=rank, layer=c)
+        layers.append(dict(
+            xa=synth.device_normal((T, w.ka_r), 1.0, torch.bfloat16, tensor="x_attn", **kw),
+            wo=synth.device_normal((w.ka_r, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_o", **kw),
+            logits=synth.device_normal((T, E), 1.0, torch.float32, tensor="logits", seed=seed,
+                                       workload=w.name, layer=c),
+            u=synth.device_normal((T, k, I), 1.0, torch.bfloat16, tensor="u", **kw),
+            we=synth.device_normal((el, I, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_expert",
+                                   **kw)))
+    slots = synth.device_normal((copies, 2, w.n_ranks, T, H), synth.WEIGHT_STD * 40, torch.float32,
+                                tensor="slots", seed=seed, workload=w.name)
+    h0 = synth.device_normal((T, H), 1.0, torch.float32, tensor="residual", seed=seed, workload=w.name)
     torch.cuda.synchronize()
+    return layers, slots, h0
+
+
+def moe_run(args, w, tune):
+    import torch
+
+    import row_gemv_reduction_amd as tp
+    T, H, E, k, I, ep = w.batch, w.hidden, w.n_experts, w.top_k, w.moe_inter, w.ep
+    rank = args.rank
+    plan = tp.Plan(H, w.k_attn, w.n_ranks, T, k_attn=w.k_attn, tune=tune,
+                   moe=dict(n_experts=E, top_k=k, ep=ep, moe_inter=I, max_tokens=T))
+    copies = 3  # 3 x ~400 MB of distinct weights per rotation: more than the 256 MB cache
+    layers, slots, h0 = moe_build(w, rank, copies)
+    for L in layers:  # load-time expert packing (untimed)
+        L["wp"] = torch.empty(tp.moe_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
+        tp.tp_moe_pack_experts(plan, L["we"], L["wp"])
+        del L["we"]
+    torch.cuda.synchronize()
+    ws = plan.new_workspace()
+    hidden = h0.clone()
+    se = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    sw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def step():
+        c = it[0] % copies
+        it[0] += 1
+        L = layers[c]
+        tp.tp_rowparallel_partial(plan, 0, L["xa"], L["wo"], slots[c, 0, rank], ws)
+        tp.tp_ring_reduce(plan, slots[c, 0], hidden, hidden)
+        tp.tp_moe_route(plan, L["logits"], se, sw)
+        tp.tp_moe_partial(plan, rank, se, sw, L["u"], L["wp"], slots[c, 1, rank], ws)
+        tp.tp_ring_reduce(plan, slots[c, 1], hidden, hidden)
+
+    ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream())
+    # algorithmic bytes of one layer share (averaged over the rotated copies)
+    el = E // ep
+    step_bytes = 0
+    active_total = 0
+    for c in range(copies):
+        tp.tp_moe_route(plan, layers[c]["logits"], se, sw)
+        sel = se.cpu().numpy()
+        local = sel[(sel >= rank * el) & (sel < (rank + 1) * el)]
+        active = len(set(local.tolist()))
+        active_total += active
+        pairs = local.size
+        b = (w.ka_r * H * 2 + T * w.ka_r * 2 + T * H * 4                  # attention slice
+             + T * E * 4 + T * k * 8                                         # routing
+             + active * I * H * 2 + pairs * I * 2 + pairs * H * 8 + T * H * 4  # experts, combine
+             + 2 * (w.n_ranks + 2) * T * H * 4)                              # two ring sums
+        step_bytes += b
+    step_bytes //= copies
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = moe_cpu_baseline(w, rank, layers[0], slots, h0, plan, args.cpu_seconds)
+    config = {"workload": w.name, "hidden": H, "k_attn": w.k_attn, "n_ranks": w.n_ranks,
+              "rank": rank, "tokens": T, "n_experts": E, "top_k": k, "ep": ep, "moe_inter": I,
+              "layers": 1, "active_local_experts_mean": active_total / copies,
+              "weight_layout": "row-major attention slice, pair-row packed experts",
+              "weight_copies_rotated": copies}
+    kernel = "MoE layer share (attention slice MFMA, ring sums, routing, expert GEMV, combine)"
+    return ms, T, step_bytes, kernel, config, cpu, {}
+
+
+def moe_cpu_baseline(w, rank, L, slots, h0, plan, budget_s):
+    """The oracle on the same MoE layer share: attention partial, ring sum
+    and routing in full; the expert projections + combine on a sample of
+    columns sized to the time budget, scaled to all columns (every column
+    costs the same)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    H, E, k, ep = w.hidden, w.n_experts, w.top_k, w.ep
+    el = E // ep
+    xa, wo, u = bits(L["xa"]), bits(L["wo"]), bits(L["u"])
+    logits = L["logits"].cpu().numpy()
+    s = slots[0].cpu().numpy()
+    h = h0.cpu().numpy()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log("timed %d steps: %.4f ms/step (events), wall %.4f ms/step" % (args.steps, ms,
-                                                                       wall * 1e3 / args.steps))
+    _, p32 = oracle.partial(xa, wo, nthreads=cores)
+    s[0, rank] = p32
+    oracle.ring_reduce(s[0], h)
+    se, sw = oracle.moe_route(logits, k, True)
+    t_fixed = time.perf_counter() - t0
 
-    tok_s = w.batch / (ms * 1e-3)
-    step_bytes = w.algorithmic_bytes_per_step()
+    def expert_cols(ncols):
+        we = bits(synth_cols(w, rank, ncols))
+        t1 = time.perf_counter()
+        oracle.moe_partial(se, sw, rank * el, u, we, nthreads=cores)
+        return time.perf_counter() - t1
+
+    ncols = 64
+    t_cols = expert_cols(ncols)
+    want = int(min(H, max(ncols, ncols * max(budget_s - t_fixed, 0.0) / max(t_cols, 1e-6))))
+    if want > ncols:
+        ncols = want
+        t_cols = expert_cols(ncols)
+    per_share = t_fixed + t_cols * H / ncols
+    # repeat whole shares until the budget is spent, for a stable figure
+    reps, spent = 1, t_fixed + t_cols
+    while spent < budget_s and ncols == H:
+        t0 = time.perf_counter()
+        _, p32 = oracle.partial(xa, wo, nthreads=cores)
+        oracle.ring_reduce(s[0], h)
+        oracle.moe_route(logits, k, True)
+        dt = time.perf_counter() - t0 + expert_cols(ncols)
+        spent += dt
+        reps += 1
+        per_share = spent / reps
+    return {"value": w.batch / per_share, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d run(s) of one layer share: attention partial, ring sum and routing in "
+                      "full; expert projections + combine on %d of %d columns, scaled to all "
+                      "columns; %.1f s in all" % (reps, ncols, H, spent)}
+
+
+def synth_cols(w, rank, ncols):
+    """The first ncols columns of copy 0's local experts (same seeded draw)."""
+    import torch
+
+    from row_gemv_reduction_amd import synth
+    el = w.n_experts // w.ep
+    full = synth.device_normal((el, w.moe_inter, w.hidden), synth.WEIGHT_STD, torch.bfloat16,
+                               tensor="w_expert", seed=0, workload=w.name, rank=rank, layer=0)
+    return full[:, :, :ncols].contiguous()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name (default: page-1 stack, N=4, b=1)")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-serial", action="store_true", help="skip the serial-point-order timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
+    ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
+                    help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the N virtual ranks are emulated on a single "
+              "MI355X, so --gpus %d is not supported (use --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from row_gemv_reduction_amd import workloads
+
+    w = workloads.ALL[args.workload] if args.workload else workloads.PAGE1
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    tune = {}
+    for kv in args.tune:
+        k, v = kv.split("=")
+        tune[k] = int(v)
+    run = moe_run if w.n_experts else dense_run
+    ms, tokens, step_bytes, kernel, config, cpu, extra = run(args, w, tune)
+    if args.copy_calibration:
+        copy_calibration()
+
+    tok_s = tokens / (ms * 1e-3)
     achieved = step_bytes / (ms * 1e-3) / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "kernel": "decode step, %s weights (%d reconciliation points, one launch)" % (layout, 2 * w.layers),
-        "algorithmic_bytes_per_launch": step_bytes,
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": extra.pop("traffic", None),
+        "kernel": kernel, "algorithmic_bytes_per_launch": step_bytes,
     }
     out = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
-        "config": {"workload": w.name, "hidden": w.hidden, "inter": w.inter, "k_attn": w.k_attn,
-                   "layers": w.layers, "n_ranks": w.n_ranks, "rank": args.rank,
-                   "batch": w.batch, "reductions_per_token": 2 * w.layers, "weight_layout": layout,
-                   "weight_bytes_per_step": w.weight_bytes_per_step()},
+        "config": config,
         "roofline": roofline,
         "context": {"pages_collective_latency_us": {"fast": 10, "slow": 50},
                     "pages_comm_ms_per_token": {"fast": 1.28, "slow": 6.4},
                     "pages_peer_bandwidth_gbs_gb200": 1800},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.rank, xa, wo, xf, wd, slots, h0,
-                                           args.cpu_seconds)
+    out.update(extra)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -82,6 +82,7 @@ typedef struct {
     int32_t n_experts, top_k, ep, local_experts;
     int64_t moe_inter;
     int32_t max_tokens;
+    int32_t packed_step;     /* 1 if tp_decode_layers_packed can run this plan */
 } tp_plan_info;
 
 /*
@@ -117,9 +118,10 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "valu_cols" (columns per VALU workgroup: 128, 256 or 512),
  * "decode_mode" (0 = automatic, 1 = one launch per point,
  *                2 = one persistent launch per step),
- * "segment_loads" (0 or 4: 4, or 8: 16-byte loads per lane in each of the
- *                two register banks of tp_decode_layers_packed; 8 only
- *                takes effect for batch <= 4),
+ * "segment_loads" (16-byte loads per lane in each of the two register
+ *                banks of tp_decode_layers_packed: 4 or 8; 0 = automatic,
+ *                8 for batch <= 4, else 4; 8 only takes effect for
+ *                batch <= 4),
  * "serial_points" (tp_decode_layers_packed: 0 = each hidden-state element
  *                follows its own chain, 1 = point j+1 also waits for all of
  *                point j, see there).

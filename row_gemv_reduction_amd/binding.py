@@ -37,7 +37,7 @@ class tp_plan_info(ctypes.Structure):
         ("wire_bytes_fp32", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("ep", ctypes.c_int32),
         ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
-        ("max_tokens", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32), ("packed_step", ctypes.c_int32),
     ]
 
 

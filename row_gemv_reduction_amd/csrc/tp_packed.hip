@@ -435,7 +435,8 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
     const int64_t G = (S + ns - 1) / ns;
     if (ns * 4 * p->batch > 64 * stream_elems_per_lane(p->batch)) return false;
     const int wps = (int)((kStreamMaxWaves - 1) / ns);
-    const int sl = p->segment_loads == 8 && p->batch <= 4 ? 8 : 4;
+    // 8-load banks (more bytes in flight) where the registers allow it
+    const int sl = p->segment_loads == 4 || p->batch > 4 ? 4 : 8;
     const int64_t kh0 = k0 / 2, kh1 = k1 / 2;
     const int64_t nb0 = (kh0 + 63) / 64, nb1 = (kh1 + 63) / 64;
     const int64_t bpw0 = (nb0 + wps - 1) / wps, bpw1 = (nb1 + wps - 1) / wps;

@@ -177,6 +177,7 @@ tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
     o->local_experts = p->ep ? p->n_experts / p->ep : 0;
     o->moe_inter = p->moe_inter;
     o->max_tokens = p->max_tokens;
+    o->packed_step = tp_strip_loads(p);
     return TP_OK;
 }
 
