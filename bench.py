@@ -168,7 +168,7 @@ def dense_run(args, w, tune):
     stream = torch.cuda.current_stream()
     layout = args.layout
     if layout == "auto":
-        layout = "packed" if info["packed_step"] else "rowmajor"
+        layout = "packed" if info["packed_kind"] else "rowmajor"
     extra = {}
     if layout == "packed":
         # load-time layout change, outside the timed region
@@ -180,7 +180,8 @@ def dense_run(args, w, tune):
 
         def step():
             tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
-        kernel = "decode_stream (one launch per step, %d reconciliation points)" % (2 * w.layers)
+        kernel = "%s (one launch per step, %d reconciliation points)" % (
+            "decode_stream" if info["packed_kind"] == 1 else "decode_stream_mfma", 2 * w.layers)
     else:
         def step():
             tp.tp_decode_layers(plan, w.layers, args.rank, xa, wo, xf, wd, slots, hidden, ws)
@@ -189,7 +190,7 @@ def dense_run(args, w, tune):
             else "persistent VALU step")
     log("weight layout: %s" % layout)
     ms = time_steps(step, args.steps, args.warmup, stream)
-    if layout == "packed" and not args.no_serial:
+    if layout == "packed" and not args.no_serial and info["packed_kind"] == 1:
         # the same step with the grid-wide wait per point (serial point order)
         plan.tune("serial_points", 1)
         ms_serial = time_steps(step, args.steps, args.warmup, stream)

@@ -82,7 +82,9 @@ typedef struct {
     int32_t n_experts, top_k, ep, local_experts;
     int64_t moe_inter;
     int32_t max_tokens;
-    int32_t packed_step;     /* 1 if tp_decode_layers_packed can run this plan */
+    int32_t packed_kind;     /* layout of tp_pack_weights / kernel of tp_decode_layers_packed:
+                                0 = the plan is not supported, 1 = pair strips (vector ALU),
+                                2 = MFMA tiles (matrix cores) */
 } tp_plan_info;
 
 /*

@@ -37,7 +37,7 @@ class tp_plan_info(ctypes.Structure):
         ("wire_bytes_fp32", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("ep", ctypes.c_int32),
         ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
-        ("max_tokens", ctypes.c_int32), ("packed_step", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32), ("packed_kind", ctypes.c_int32),
     ]
 
 
@@ -236,12 +236,17 @@ def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slo
 
 
 def packed_shape(plan: Plan, point, n_layers):
-    """Shape of a pair-strip packed weight stack: [L, H/4, ceil(K_r/2), 8]."""
+    """Shape of a packed weight stack for the plan's streamed step:
+    pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/32), 64, 8]."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
     i = plan.info()
     kr, H = i["k_rank"][point], i["hidden"]
-    return (n_layers, H // 4, (kr + 1) // 2, 8)
+    if i["packed_kind"] == 1:
+        return (n_layers, H // 4, (kr + 1) // 2, 8)
+    if i["packed_kind"] == 2:
+        return (n_layers, H // 16, (kr + 31) // 32, 64, 8)
+    raise TPError(TP_ERR_UNSUPPORTED, "packed_shape")
 
 
 def tp_pack_weights(plan: Plan, point, w, w_packed):

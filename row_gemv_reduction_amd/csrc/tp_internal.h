@@ -60,6 +60,7 @@ struct tp_plan_s {
     int32_t target_wgs = 0;
     int32_t segment_loads = 0;  // 16-byte loads per lane per bank of the streamed step (0 = 4)
     int32_t serial_points = 0;  // streamed step: point j+1 waits for all of point j
+    int32_t stream_kind = 0;    // 0 = automatic, 1 = pair strips (VALU), 2 = MFMA tiles
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -93,5 +94,19 @@ struct StreamGeom {
     int32_t xoff1, xdwords, lds_bytes;
 };
 bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
-int tp_strip_loads(const tp_plan_s* p);  // nonzero if the streamed step can run the plan
+
+// Geometry of the MFMA streamed decode step (tp_mfma_stream.hip).
+struct MfmaGeom {
+    int32_t grid, block, wps, bt, sl;
+    int32_t nkb0, nkb1, bpw0, bpw1;
+    int32_t red_floats, oth_floats, lds_bytes;
+};
+bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g);
+tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
+                        void* stream);
+tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,
+                                const void* x_attn, const void* w_o_tiles, const void* x_ffn,
+                                const void* w_down_tiles, float* slots, float* hidden, void* stream);
+// Packed layout (and streamed kernel) the plan uses: 0 none, 1 pair strips, 2 MFMA tiles.
+int tp_packed_kind(const tp_plan_s* p);
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections

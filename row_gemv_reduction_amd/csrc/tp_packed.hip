@@ -465,9 +465,18 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
     return g->lds_bytes <= kStreamMaxLdsBytes;
 }
 
-int tp_strip_loads(const tp_plan_s* p) {
-    StreamGeom g;
-    return tp_stream_geometry(p, &g) ? 1 : 0;
+// Automatic choice: the vector-ALU stream (pair strips) up to 4 tokens, the
+// matrix-core stream (MFMA tiles) from 5 tokens on, each where it fits.
+int tp_packed_kind(const tp_plan_s* p) {
+    StreamGeom sg;
+    MfmaGeom mg;
+    const bool valu = tp_stream_geometry(p, &sg);
+    const bool mfma = tp_mfma_geometry(p, &mg);
+    if (p->stream_kind == 1) return valu ? 1 : 0;
+    if (p->stream_kind == 2) return mfma ? 2 : 0;
+    if (valu && p->batch <= 4) return 1;
+    if (mfma) return 2;
+    return valu ? 1 : 0;
 }
 
 extern "C" {
@@ -478,7 +487,9 @@ tp_status tp_pack_weights(tp_plan_t p, int32_t point, int32_t n_layers, const vo
     if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
     if (w == w_packed) return TP_ERR_INVALID_ARG;
-    if (p->hidden % 4) return TP_ERR_UNSUPPORTED;
+    const int kind = tp_packed_kind(p);
+    if (kind == 0) return TP_ERR_UNSUPPORTED;
+    if (kind == 2) return tp_pack_tiles(p, point, n_layers, w, w_packed, stream);
     const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
     const int64_t total = (int64_t)n_layers * ((K + 1) / 2) * (p->hidden / 4);
     if (total == 0) return TP_OK;
@@ -499,6 +510,13 @@ tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, c
     if (!aligned16(x_attn) || !aligned16(w_o_packed) || !aligned16(x_ffn) ||
         !aligned16(w_down_packed) || !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
         return TP_ERR_ALIGNMENT;
+    const int kind = tp_packed_kind(p);
+    if (kind == 0) return TP_ERR_UNSUPPORTED;
+    if (kind == 2) {
+        if (p->serial_points) return TP_ERR_UNSUPPORTED;  // the serial order: vector-ALU stream only
+        return tp_decode_mfma_stream(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
+                                     slots, hidden, stream);
+    }
     StreamGeom geo;
     if (!tp_stream_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * 2 >= ((int64_t)1 << 30)) return TP_ERR_UNSUPPORTED;

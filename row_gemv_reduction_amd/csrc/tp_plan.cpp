@@ -141,6 +141,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "segment_loads")) {
         if (value != 0 && value != 4 && value != 8) return TP_ERR_INVALID_ARG;
         p->segment_loads = (int32_t)value;
+    } else if (!strcmp(key, "stream_kind")) {
+        if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
+        p->stream_kind = (int32_t)value;
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
@@ -177,7 +180,7 @@ tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
     o->local_experts = p->ep ? p->n_experts / p->ep : 0;
     o->moe_inter = p->moe_inter;
     o->max_tokens = p->max_tokens;
-    o->packed_step = tp_strip_loads(p);
+    o->packed_kind = tp_packed_kind(p);
     return TP_OK;
 }
 

@@ -393,8 +393,8 @@ def pack_dev(plan, point, w_bits_host_or_dev):
 
 
 def test_pack_weights_is_the_pair_strip_layout():
-    # P[l][s][kp][c][q] = W[l][2kp+q][4s+c], rows past K zero (k = 321 is odd)
-    L, n, H, ka, ki = 3, 2, 1032, 642, 2000
+    # P[l][s][kp][c][q] = W[l][2kp+q][4s+c]
+    L, n, H, ka, ki = 3, 2, 1032, 640, 2000
     plan = tp.Plan(H, ki, n, 1, k_attn=ka)
     say("pack layout")
     for point, k in ((0, ka // n), (1, ki // n)):
@@ -409,8 +409,34 @@ def test_pack_weights_is_the_pair_strip_layout():
                           "packed point %d" % point)
 
 
+def test_pack_weights_is_the_mfma_tile_layout():
+    # T[l][s][kb][lane][i] = W[l][32kb + 8(lane/16) + i][16s + lane%16], rows past K zero
+    L, n, H, ka, ki = 2, 2, 1040, 656, 2000
+    plan = tp.Plan(H, ki, n, 16, k_attn=ka)
+    assert plan.info()["packed_kind"] == 2
+    say("pack layout, MFMA tiles")
+    for point, k in ((0, ka // n), (1, ki // n)):
+        w = synth.normal_bf16((L, k, H), synth.WEIGHT_STD, seed=5, tensor="w", layer=point)
+        p = pack_dev(plan, point, w)
+        torch.cuda.synchronize()
+        nkb = (k + 31) // 32
+        wz = np.zeros((L, 32 * nkb, H), np.uint16)
+        wz[:, :k] = w
+        # [l][kb][g][i][s][c] -> [l][s][kb][g][c][i], lane = 16 g + c
+        want = wz.reshape(L, nkb, 4, 8, H // 16, 16).transpose(0, 4, 1, 2, 5, 3)
+        assert_bits_equal(bf16_bits_host(p), np.ascontiguousarray(want).reshape(L, H // 16, nkb, 64, 8),
+                          "tiles point %d" % point)
+
+
 def run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
-    """Both point orders on the same inputs; they must give the same bits."""
+    """Both point orders on the same inputs; they must give the same bits.
+    (The serial order exists on the vector-ALU stream only.)"""
+    if plan.info()["packed_kind"] == 2:
+        plan.tune("serial_points", 1)
+        with pytest.raises(tp.TPError):
+            _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps)
+        plan.tune("serial_points", 0)
+        return _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps)
     outs = []
     for serial in (0, 1):
         plan.tune("serial_points", serial)
@@ -433,14 +459,25 @@ def _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
     return host(S), host(Hd)
 
 
-@pytest.mark.parametrize("n,b,h,ka,ki,rank", [(4, 1, 1032, 640, 2048, 0), (4, 1, 5120, 5120, 17408, 3),
-                                              (2, 3, 520, 512, 1376, 1), (8, 8, 4096, 4096, 12288, 7),
-                                              (1, 2, 64, 64, 128, 0), (3, 4, 24, 24, 48, 2)])
-def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank):
+PACKED_CASES = [
+    # (n, b, hidden, k_attn, inter, rank, kind): kind 1 = vector-ALU stream on
+    # pair strips, 2 = matrix-core stream on MFMA tiles (0 = the automatic one)
+    (4, 1, 1032, 640, 2048, 0, 1), (4, 1, 5120, 5120, 17408, 3, 1), (2, 3, 520, 512, 1376, 1, 1),
+    (8, 8, 4096, 4096, 12288, 7, 1), (1, 2, 64, 64, 128, 0, 1), (3, 4, 24, 24, 48, 2, 1),
+    (8, 8, 4096, 4096, 12288, 7, 2), (4, 5, 1040, 640, 2048, 1, 2), (2, 16, 528, 512, 1376, 0, 2),
+    (4, 17, 1024, 1024, 4096, 2, 2), (8, 33, 512, 512, 1024, 5, 2), (4, 64, 1024, 2048, 4096, 3, 2),
+    (1, 20, 256, 256, 512, 0, 2), (3, 7, 48, 48, 96, 1, 2), (4, 1, 1024, 1024, 2048, 2, 2),
+    (2, 48, 4112, 256, 512, 1, 2),
+]
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,kind", PACKED_CASES)
+def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank, kind):
     L = 3
-    say("packed decode n=%d b=%d h=%d ka=%d ki=%d rank=%d" % (n, b, h, ka, ki, rank))
+    say("packed decode n=%d b=%d h=%d ka=%d ki=%d rank=%d kind=%d" % (n, b, h, ka, ki, rank, kind))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 31, rank)
-    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind})
+    assert plan.info()["packed_kind"] == kind
     s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
     for l in range(L):
         assert_partial_close(s_gpu[l, 0, rank], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
@@ -453,8 +490,9 @@ def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank):
     assert err <= 2 * L * 1e-5 * rms_p + 4 * np.spacing(np.abs(h_or).max()), err
 
 
-def test_packed_decode_bit_exact_when_partials_are_exact():
-    L, n, b, h, ka, ki, rank = 4, 4, 2, 256, 64, 128, 1
+@pytest.mark.parametrize("b", [2, 16])
+def test_packed_decode_bit_exact_when_partials_are_exact(b):
+    L, n, h, ka, ki, rank = 4, 4, 256, 64, 128, 1
     g = np.random.default_rng(18)
     xa = synth.f32_to_bf16_bits(g.integers(-4, 5, (L, b, ka // n)).astype(np.float32))
     wo = synth.f32_to_bf16_bits(g.integers(-4, 5, (L, ka // n, h)).astype(np.float32))
@@ -470,18 +508,33 @@ def test_packed_decode_bit_exact_when_partials_are_exact():
     assert_bits_equal(h_gpu, h_or, "hidden")
 
 
-def test_packed_page1_full_size_sampled_and_deterministic():
-    w = workloads.PAGE1
-    say("packed page-1 stack N=4 b=1, 64 layers, sampled columns")
+FULL_SIZE = [
+    # (workload, layers checked, rank): the benchmarked shapes in the launch
+    # configuration bench.py times (the automatic stream kind)
+    (workloads.PAGE1, None, 0),
+    (workloads.page1_n2(8), 2, 1),
+    (workloads.page1_n2(16), 2, 1),
+    (workloads.page1_n2(32), 2, 0),
+    (workloads.h4096(8, 64), 2, 5),
+    (workloads.h4096(4, 8), 2, 3),
+]
+
+
+@pytest.mark.parametrize("w,layers,rank", FULL_SIZE, ids=[c[0].name for c in FULL_SIZE])
+def test_packed_full_size_sampled_and_deterministic(w, layers, rank):
+    if layers is not None:
+        w = w.with_(layers=layers)
+    say("packed %s (%d layers), sampled columns" % (w.name, w.layers))
     plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn)
-    xa, wo, xf, wd, slots, h0 = device_stack(w, 0)
+    assert plan.info()["packed_kind"] in (1, 2)
+    xa, wo, xf, wd, slots, h0 = device_stack(w, rank)
     po, pd = pack_dev(plan, 0, wo), pack_dev(plan, 1, wd)
     ws = plan.new_workspace()
     outs = []
     for _ in range(3):
         S = slots.clone()
         Hd = h0.clone()
-        tp.tp_decode_layers_packed(plan, w.layers, 0, xa, po, xf, pd, S, Hd, ws)
+        tp.tp_decode_layers_packed(plan, w.layers, rank, xa, po, xf, pd, S, Hd, ws)
         torch.cuda.synchronize()
         outs.append((host(S), host(Hd)))
     assert tp.tp_workspace_status(plan, ws) == 0
@@ -497,10 +550,10 @@ def test_packed_page1_full_size_sampled_and_deterministic():
     for l in range(w.layers):
         for pt, (xh, Wt) in enumerate(((xa_h, wo), (xf_h, wd))):
             ref64, ref32 = oracle.partial(xh[l], bf16_bits_host(Wt[l].index_select(1, ci)))
-            assert_partial_close(s_got[l, pt, 0][:, cols], ref64, "l=%d pt=%d" % (l, pt))
-            P[l, pt, 0] = 0.0
-            P[l, pt, 0][:, cols] = ref32
+            assert_partial_close(s_got[l, pt, rank][:, cols], ref64, "l=%d pt=%d" % (l, pt))
+            P[l, pt, rank] = 0.0
+            P[l, pt, rank][:, cols] = ref32
             h_or = oracle.ring_reduce(P[l, pt], h_or)
-    rms_p = np.sqrt(np.mean(s_got[:, :, 0][..., cols].astype(np.float64) ** 2))
+    rms_p = np.sqrt(np.mean(s_got[:, :, rank][..., cols].astype(np.float64) ** 2))
     err = np.abs(outs[0][1][:, cols].astype(np.float64) - h_or[:, cols]).max()
     assert err <= 2 * w.layers * 1e-5 * rms_p + 8 * np.spacing(np.abs(h_or).max()), err
