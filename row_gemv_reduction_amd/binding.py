@@ -237,7 +237,7 @@ def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slo
 
 def packed_shape(plan: Plan, point, n_layers):
     """Shape of a packed weight stack for the plan's streamed step:
-    pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/32), 64, 8]."""
+    pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/64), 2, 64, 8]."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
     i = plan.info()
@@ -245,7 +245,7 @@ def packed_shape(plan: Plan, point, n_layers):
     if i["packed_kind"] == 1:
         return (n_layers, H // 4, (kr + 1) // 2, 8)
     if i["packed_kind"] == 2:
-        return (n_layers, H // 16, (kr + 31) // 32, 64, 8)
+        return (n_layers, H // 16, (kr + 63) // 64, 2, 64, 8)
     raise TPError(TP_ERR_UNSUPPORTED, "packed_shape")
 
 

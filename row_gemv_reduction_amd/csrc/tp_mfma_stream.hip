@@ -10,12 +10,15 @@
 // instruction). The step stays bound by streaming the weights from HBM.
 //
 // Layout ("MFMA tiles"): a rank's slice W_r[K][H] is stored once, at load
-// time, as 1 KB tiles of 32 rows x 16 columns in the matrix-core operand
-// order:
-//     T[s][kb][l][i] = W_r[32kb + 8(l/16) + i][16s + l%16]
-//     s < H/16, kb < ceil(K/32), lane l < 64, i < 8   (rows past K are zero)
-// so one 16-byte load per lane hands lane l exactly its B operand (8
-// consecutive rows of one column).
+// time, as 2 KB tiles of 64 rows x 16 columns, each two halves of the
+// matrix-core B operand:
+//     T[s][kb][h][l][i] = W_r[64kb + 16(l/16) + 8h + i][16s + l%16]
+//     s < H/16, kb < ceil(K/64), h < 2, lane l < 64, i < 8   (rows past K are zero)
+// One 16-byte load per lane and half hands lane l its B operand (8
+// consecutive rows of one column). The two halves of lane group g = l/16
+// hold rows 16g .. 16g+15, so the A operands of the two MFMAs of a tile
+// (x rows 16g+8h .. +8) cover, per token, one whole 128-byte line of x
+// between them: the second load of the line hits L1.
 //
 // decode_stream_mfma: one launch per step; workgroup s owns the 16-column
 // strip s for every point (one workgroup per strip; at most two per CU).
@@ -46,22 +49,23 @@ using namespace tpdev;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kTileBytes = 1024;   // 32 rows x 16 columns of bf16
+constexpr int kTileBytes = 2048;   // 64 rows x 16 columns of bf16, two operand halves
+constexpr int kTileRows = 64;
 
-// T[l][s][kb][lane][i] = W[l][32kb + 8(lane/16) + i][16s + lane%16]
+// T[l][s][kb][h][lane][i] = W[l][64kb + 16(lane/16) + 8h + i][16s + lane%16]
 __global__ void pack_tiles_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
                                   int64_t layers, int64_t K, int64_t H) {
-    const int64_t strips = H / 16, nkb = (K + 31) / 32;
-    const int64_t per_layer = strips * nkb * 64;
+    const int64_t strips = H / 16, nkb = (K + kTileRows - 1) / kTileRows;
+    const int64_t per_layer = strips * nkb * 128;
     const int64_t total = layers * per_layer;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
          v += (int64_t)gridDim.x * blockDim.x) {
         const int64_t l = v / per_layer;
         int64_t rem = v - l * per_layer;
-        const int64_t s = rem / (nkb * 64);
-        rem -= s * nkb * 64;
-        const int64_t kb = rem / 64, lane = rem % 64;
-        const int64_t k0 = 32 * kb + 8 * (lane / 16), n = 16 * s + lane % 16;
+        const int64_t s = rem / (nkb * 128);
+        rem -= s * nkb * 128;
+        const int64_t kb = rem / 128, h = (rem / 64) % 2, lane = rem % 64;
+        const int64_t k0 = kTileRows * kb + 16 * (lane / 16) + 8 * h, n = 16 * s + lane % 16;
         uint16_t e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = k0 + i < K ? w[(l * K + k0 + i) * H + n] : (uint16_t)0;
@@ -77,8 +81,8 @@ __global__ void pack_tiles_kernel(const uint16_t* __restrict__ w, uint16_t* __re
 struct MfmaArgs {
     const uint16_t* x0;     // x_attn [L][B][K0]
     const uint16_t* x1;     // x_ffn  [L][B][K1]
-    const uint16_t* w0;     // tiles of w_o    [L][H/16][nkb0][64][8]
-    const uint16_t* w1;     // tiles of w_down [L][H/16][nkb1][64][8]
+    const uint16_t* w0;     // tiles of w_o    [L][H/16][nkb0][2][64][8]
+    const uint16_t* w1;     // tiles of w_down [L][H/16][nkb1][2][64][8]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
     int32_t H, S16, WPS, batch;
@@ -168,9 +172,9 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             cu.m0 += SL;
             if (cu.m0 >= bpw(cu.j)) { cu.j += 1; cu.m0 = 0; }
         };
-        // A operand of lane l: token 16*tt + l%16, rows 8*(l/16) .. +7 of the tile
-        const int xo = lane & 15, xk = 8 * (lane >> 4);
-        auto issue = [&](u32x4_t (&wv)[SL], u32x4_t (&xv)[SL][BT], const Cursor& cu) {
+        // A operand of lane l: token 16*tt + l%16, rows 16*(l/16) + 8h .. +7 of the tile
+        const int xo = lane & 15, xk = 16 * (lane >> 4);
+        auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& cu) {
             const int t = cu.j & 1, l = cu.j >> 1;
             const bool live = cu.j < n_points;
             const int K = t ? a.K1 : a.K0, nkb = t ? a.nkb1 : a.nkb0;
@@ -182,28 +186,45 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? xb : a.x0), (short)0, live ? B * K * 2 : 0,
                 kBufferRsrcWord3);
+            // Workgroups start their walk over a point's tiles at different
+            // places (a rotation by whole rounds of WPS tiles), so that they do
+            // not all read the same rows of x at the same moment. Slots past
+            // the wave's bpw tiles (the tail of the last segment) stay past the
+            // span, which reads zero.
+            const int bpw = t ? a.bpw1 : a.bpw0;
+            const int span = bpw * a.WPS;
+            const int rot = (s % bpw) * a.WPS;
 #pragma unroll
             for (int i = 0; i < SL; ++i) {
-                const int kb = wi + (cu.m0 + i) * a.WPS;
-                wv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        wr, kb * kTileBytes + lane * 16, 0, kCachePolicyNT));
+                int kb = wi + (cu.m0 + i) * a.WPS + rot;
+                kb = cu.m0 + i >= bpw ? span : kb >= span ? kb - span : kb;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               wr, kb * kTileBytes + h * 1024 + lane * 16, 0,
+                                                               kCachePolicyNT));
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt)
-                    xv[i][tt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                xr, ((16 * tt + xo) * K + 32 * kb + xk) * 2, 0, 0));
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        xv[i][h][tt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                       xr, ((16 * tt + xo) * K + kTileRows * kb + xk + 8 * h) * 2,
+                                                                       0, 0));
             }
         };
         floatx4_t acc[BT];
 #pragma unroll
         for (int tt = 0; tt < BT; ++tt) acc[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        auto consume = [&](const u32x4_t (&wv)[SL], const u32x4_t (&xv)[SL][BT]) {
+        auto consume = [&](const u32x4_t (&wv)[SL][2], const u32x4_t (&xv)[SL][2][BT]) {
 #pragma unroll
             for (int i = 0; i < SL; ++i)
 #pragma unroll
-                for (int tt = 0; tt < BT; ++tt)
-                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, xv[i][tt]), __builtin_bit_cast(bf16x8_t, wv[i]),
-                        acc[tt], 0, 0, 0);
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int tt = 0; tt < BT; ++tt)
+                        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xv[i][h][tt]), __builtin_bit_cast(bf16x8_t, wv[i][h]),
+                            acc[tt], 0, 0, 0);
         };
         auto point_end = [&](int j) {
             float* rj = red + (j & 1) * a.red_floats + wi * BT * 256;
@@ -215,7 +236,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             __syncthreads();  // P_j
         };
 
-        u32x4_t w0[SL], w1[SL], x0[SL][BT], x1[SL][BT];
+        u32x4_t w0[SL][2], w1[SL][2], x0[SL][2][BT], x1[SL][2][BT];
         Cursor ci{0, 0}, cc{0, 0};
         issue(w0, x0, ci);
         advance(ci);
@@ -251,14 +272,14 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 
 typedef void (*mfma_stream_fn)(MfmaArgs);
 
-// Loads per bank: fewer for more token blocks (each tile also carries BT
+// Tiles per bank: fewer for more token blocks (each tile also carries 2*BT
 // A operands), so the banks fit the registers.
 mfma_stream_fn mfma_stream_kernel(int bt) {
     switch (bt) {
-        case 1: return decode_stream_mfma<1, 4>;
-        case 2: return decode_stream_mfma<2, 3>;
-        case 3: return decode_stream_mfma<3, 2>;
-        case 4: return decode_stream_mfma<4, 2>;
+        case 1: return decode_stream_mfma<1, 2>;
+        case 2: return decode_stream_mfma<2, 2>;
+        case 3: return decode_stream_mfma<3, 1>;
+        case 4: return decode_stream_mfma<4, 1>;
     }
     return nullptr;
 }
@@ -277,8 +298,8 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     const int per_cu = S16 > kTargetCUs ? 2 : 1;
     const int bt = (b + 15) / 16;
     int wps = per_cu == 2 ? 7 : (bt <= 2 ? 15 : 7);
-    const int sl = bt == 1 ? 4 : bt == 2 ? 3 : 2;
-    const int64_t nkb0 = (k0 + 31) / 32, nkb1 = (k1 + 31) / 32;
+    const int sl = bt <= 2 ? 2 : 1;
+    const int64_t nkb0 = (k0 + kTileRows - 1) / kTileRows, nkb1 = (k1 + kTileRows - 1) / kTileRows;
     g->red_floats = wps * bt * 256;
     g->oth_floats = (p->n_ranks - 1) * b * 16 > 0 ? ((p->n_ranks - 1) * b * 16 + 255) / 256 * 256 : 0;
     g->lds_bytes = (2 * g->red_floats + 2 * g->oth_floats + ((16 * b + 63) / 64) * 64) * 4;
@@ -301,7 +322,7 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream) {
     const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
-    const int64_t total = (int64_t)n_layers * (p->hidden / 16) * ((K + 31) / 32) * 64;
+    const int64_t total = (int64_t)n_layers * (p->hidden / 16) * ((K + kTileRows - 1) / kTileRows) * 128;
     if (total == 0) return TP_OK;
     const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
     hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,

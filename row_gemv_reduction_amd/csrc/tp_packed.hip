@@ -190,7 +190,12 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
             const uint16_t* src = (t ? a.x1 : a.x0) + (int64_t)l * B * K;
             const int n16 = B * K / 8;
             uint32_t* dst = xs + (t ? a.xoff1 : 0);
-            for (int v0 = 0; v0 < n16; v0 += 64) {
+            // start at a workgroup-dependent piece, so that the workgroups do
+            // not all read the same lines of x at the same moment
+            const int pieces = (n16 + 63) / 64;
+            const int rot = g % pieces;
+            for (int q = 0; q < pieces; ++q) {
+                const int v0 = (q + rot < pieces ? q + rot : q + rot - pieces) * 64;
                 int v = v0 + lane;
                 v = v < n16 ? v : n16 - 1;
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)v * 8),

@@ -410,7 +410,7 @@ def test_pack_weights_is_the_pair_strip_layout():
 
 
 def test_pack_weights_is_the_mfma_tile_layout():
-    # T[l][s][kb][lane][i] = W[l][32kb + 8(lane/16) + i][16s + lane%16], rows past K zero
+    # T[l][s][kb][h][lane][i] = W[l][64kb + 16(lane/16) + 8h + i][16s + lane%16], rows past K zero
     L, n, H, ka, ki = 2, 2, 1040, 656, 2000
     plan = tp.Plan(H, ki, n, 16, k_attn=ka)
     assert plan.info()["packed_kind"] == 2
@@ -419,12 +419,12 @@ def test_pack_weights_is_the_mfma_tile_layout():
         w = synth.normal_bf16((L, k, H), synth.WEIGHT_STD, seed=5, tensor="w", layer=point)
         p = pack_dev(plan, point, w)
         torch.cuda.synchronize()
-        nkb = (k + 31) // 32
-        wz = np.zeros((L, 32 * nkb, H), np.uint16)
+        nkb = (k + 63) // 64
+        wz = np.zeros((L, 64 * nkb, H), np.uint16)
         wz[:, :k] = w
-        # [l][kb][g][i][s][c] -> [l][s][kb][g][c][i], lane = 16 g + c
-        want = wz.reshape(L, nkb, 4, 8, H // 16, 16).transpose(0, 4, 1, 2, 5, 3)
-        assert_bits_equal(bf16_bits_host(p), np.ascontiguousarray(want).reshape(L, H // 16, nkb, 64, 8),
+        # rows 64kb + 16g + 8h + i, columns 16s + c -> [l][s][kb][h][g][c][i], lane = 16 g + c
+        want = wz.reshape(L, nkb, 4, 2, 8, H // 16, 16).transpose(0, 5, 1, 3, 2, 6, 4)
+        assert_bits_equal(bf16_bits_host(p), np.ascontiguousarray(want).reshape(L, H // 16, nkb, 2, 64, 8),
                           "tiles point %d" % point)
 
 
