@@ -124,6 +124,9 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  *                banks of tp_decode_layers_packed: 4 or 8; 0 = automatic,
  *                8 for batch <= 4, else 4; 8 only takes effect for
  *                batch <= 4),
+ * "stream_kind" (tp_decode_layers_packed: 0 = automatic, 1 = vector-ALU
+ *                stream on pair strips, 2 = matrix-core stream on MFMA tiles),
+ * "moe_variant" (tp_moe_partial's expert kernel: 0 = default, 1..7),
  * "serial_points" (tp_decode_layers_packed: 0 = each hidden-state element
  *                follows its own chain, 1 = point j+1 also waits for all of
  *                point j, see there).
@@ -299,8 +302,9 @@ tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packe
  * local experts' weighted rows in ascending expert order. Experts that no
  * token selected are not read. Expert ids outside this rank's range are
  * skipped. Uses the workspace (pair table and per-selection rows).
- * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8 or larger than
- * 4096, or E/ep > 8192.
+ * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8 or too large for
+ * the expert kernel's LDS (moe_inter <= 9600 with the default variant), or
+ * E/ep > 8192.
  */
 tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                          const float* sel_weight, int32_t tokens, const void* u,

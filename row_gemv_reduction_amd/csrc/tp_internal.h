@@ -61,6 +61,7 @@ struct tp_plan_s {
     int32_t segment_loads = 0;  // 16-byte loads per lane per bank of the streamed step (0 = 4)
     int32_t serial_points = 0;  // streamed step: point j+1 waits for all of point j
     int32_t stream_kind = 0;    // 0 = automatic, 1 = pair strips (VALU), 2 = MFMA tiles
+    int32_t moe_variant = 0;    // expert kernel variant (0 = default)
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;

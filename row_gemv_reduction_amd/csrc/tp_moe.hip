@@ -22,8 +22,8 @@
 //                  slot holds which row, never any arithmetic.
 //   moe_expert     one workgroup per (local expert, block of 256 columns):
 //                  the expert's rows are staged in LDS as bf16 pairs, each lane
-//                  owns 4 columns and accumulates over its waves' share of
-//                  the expert's K rows (no cross-lane reduction), the 4 waves'
+//                  owns 4 columns and accumulates over its wave's share of
+//                  the expert's K rows (no cross-lane reduction), the waves'
 //                  K shares are summed in LDS in wave order, and the rows'
 //                  projections land in Y[slot].
 //   moe_combine    part[t, n] = sum over the token's selections s, in order
@@ -47,10 +47,7 @@ using namespace tpdev;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRouteMaxPerLane = 32;   // experts per lane in the routing wave (E <= 2048)
-constexpr int kMoeWaves = 4;           // waves per expert workgroup (K split)
 constexpr int kMoeCols = 256;          // columns per expert workgroup: 64 lanes x 4
-constexpr int kMoeRows = 8;            // activation rows per pass (more rows: more passes)
-constexpr int kMoeSL = 8;              // loads per lane per register bank
 
 // ------------------------------------------------------------- routing --
 
@@ -71,6 +68,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+template <int EPL>  // experts per lane (E <= 64 * EPL)
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int tokens,
                                                         int E, int top_k, int renorm,
                                                         int32_t* __restrict__ sel_expert,
@@ -79,11 +77,11 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= tokens) return;
     const float* z = logits + (int64_t)t * E;
-    float zl[kRouteMaxPerLane];
+    float zl[EPL];
     uint32_t taken = 0;
     float zmax = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         zl[i] = e < E ? z[e] : -__builtin_inff();
         zmax = e < E && zl[i] > zmax ? zl[i] : zmax;
@@ -92,12 +90,6 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         int dummy = 0;
         wave_argmax(zmax, dummy);
     }
-    // softmax denominator over all experts (double)
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i)
-        if (lane + 64 * i < E) part += exp((double)zl[i] - (double)zmax);
-    const double denom_all = wave_sum_f64(part);
     // top_k rounds of arg-max over the experts not yet taken
     int my_e = 0x7fffffff;
     float my_z = 0.f;
@@ -105,7 +97,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         float bv = -__builtin_inff();
         int be = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < kRouteMaxPerLane; ++i) {
+        for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
             if (e < E && !(taken >> i & 1u) && (zl[i] > bv || be == 0x7fffffff)) {
                 bv = zl[i];
@@ -118,7 +110,17 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     }
     const bool mine = lane < top_k;
     const double p = mine ? exp((double)my_z - (double)zmax) : 0.0;
-    const double denom = renorm ? wave_sum_f64(p) : denom_all;
+    double denom;
+    if (renorm) {
+        denom = wave_sum_f64(p);
+    } else {
+        // softmax denominator over all experts (double)
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane + 64 * i < E) part += exp((double)zl[i] - (double)zmax);
+        denom = wave_sum_f64(part);
+    }
     // ascending expert order: the rank of my expert among the selected ones
     int rank = 0;
     for (int s = 0; s < top_k; ++s) {
@@ -129,6 +131,17 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         sel_expert[(int64_t)t * top_k + rank] = my_e;
         sel_weight[(int64_t)t * top_k + rank] = (float)(p / denom);
     }
+}
+
+typedef void (*route_fn)(const float*, int, int, int, int, int32_t*, float*);
+route_fn route_kernel(int E) {
+    if (E <= 64) return moe_route_kernel<1>;
+    if (E <= 128) return moe_route_kernel<2>;
+    if (E <= 256) return moe_route_kernel<4>;
+    if (E <= 512) return moe_route_kernel<8>;
+    if (E <= 1024) return moe_route_kernel<16>;
+    if (E <= 2048) return moe_route_kernel<32>;
+    return nullptr;
 }
 
 // ---------------------------------------------------------- pair table --
@@ -184,8 +197,12 @@ struct ExpertArgs {
     int32_t col_blocks;      // ceil(G4 / 64)
 };
 
-template <int MT>
-__global__ __launch_bounds__(kMoeWaves * 64) void moe_expert_kernel(ExpertArgs a) {
+// MT activation rows per pass (more rows: more passes over the weights),
+// NW waves per workgroup (the K split), SL loads per lane per register bank.
+template <int MT, int NW, int SL>
+__global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
+    constexpr int kMoeWaves = NW;
+    constexpr int kMoeSL = SL;
     // x rows of the pass as bf16 pairs [MT][Kh]; reused afterwards for the
     // waves' column sums [kMoeWaves][MT][kMoeCols]
     extern __shared__ __align__(16) uint32_t sh[];
@@ -325,6 +342,22 @@ __global__ void pack_experts_kernel(const uint16_t* __restrict__ w, uint16_t* __
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+struct ExpertVariant {
+    int mt, nw, sl;
+    void (*fn)(ExpertArgs);
+};
+// The plan knob "moe_variant" picks one (1-based; 0 = the first, the
+// fastest measured at 128 experts of 1536 x 4096, 64 tokens, top-8, EP=4).
+const ExpertVariant kExpertVariants[] = {
+    {8, 8, 4, moe_expert_kernel<8, 8, 4>},
+    {8, 4, 4, moe_expert_kernel<8, 4, 4>},
+    {8, 4, 8, moe_expert_kernel<8, 4, 8>},
+    {4, 4, 8, moe_expert_kernel<4, 4, 8>},
+    {4, 8, 8, moe_expert_kernel<4, 8, 8>},
+    {8, 16, 4, moe_expert_kernel<8, 16, 4>},
+    {8, 16, 2, moe_expert_kernel<8, 16, 2>},
+};
+
 MoeTable table_in(const tp_plan_s* p, void* ws) {
     const int64_t pairs = (int64_t)p->max_tokens * p->top_k;
     const int64_t el = p->n_experts / p->ep;
@@ -359,9 +392,11 @@ tp_status tp_moe_route(tp_plan_t p, const float* logits, int32_t tokens, int32_t
     if (!aligned16(logits) || !aligned16(sel_expert) || !aligned16(sel_weight)) return TP_ERR_ALIGNMENT;
     if (p->n_experts > 64 * kRouteMaxPerLane || p->top_k > 64) return TP_ERR_UNSUPPORTED;
     if (tokens == 0) return TP_OK;
-    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0,
-                       (hipStream_t)stream, logits, (int)tokens, (int)p->n_experts, (int)p->top_k,
-                       (int)(renorm != 0), sel_expert, sel_weight);
+    route_fn k = route_kernel((int)p->n_experts);
+    if (!k) return TP_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, (hipStream_t)stream, logits,
+                       (int)tokens, (int)p->n_experts, (int)p->top_k, (int)(renorm != 0), sel_expert,
+                       sel_weight);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
@@ -391,11 +426,12 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
     const int64_t I = p->moe_inter, H = p->hidden, el = p->n_experts / p->ep;
     if (I % 8) return TP_ERR_UNSUPPORTED;
     const int64_t kh = I / 2;
-    // LDS: the pass's rows (kMoeRows x I bf16) and the waves' sums
-    const int64_t lds_x = (int64_t)kMoeRows * kh * 4;
-    const int64_t lds_red = (int64_t)kMoeWaves * kMoeRows * kMoeCols * 4;
+    const ExpertVariant v = kExpertVariants[p->moe_variant > 0 ? p->moe_variant - 1 : 0];
+    // LDS: the pass's rows (MT x I bf16) and the waves' sums
+    const int64_t lds_x = (int64_t)v.mt * kh * 4;
+    const int64_t lds_red = (int64_t)v.nw * v.mt * kMoeCols * 4;
     const int64_t lds = lds_x > lds_red ? lds_x : lds_red;
-    if (lds > 64 * 1024 || el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
+    if (lds > 150 * 1024 || el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
     if (kh * (H / 4) * 16 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
     if (tokens == 0) return TP_OK;
     hipStream_t st = (hipStream_t)stream;
@@ -412,12 +448,15 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
     a.G4 = (int32_t)(H / 4);
     a.I = (int32_t)I;
     a.Kh = (int32_t)kh;
-    const int64_t per_wave = (kh + kMoeWaves - 1) / kMoeWaves;
-    a.rows_per_wave = (int32_t)((per_wave + 2 * kMoeSL - 1) / (2 * kMoeSL) * (2 * kMoeSL));
+    const int64_t per_wave = (kh + v.nw - 1) / v.nw;
+    a.rows_per_wave = (int32_t)((per_wave + 2 * v.sl - 1) / (2 * v.sl) * (2 * v.sl));
     a.col_blocks = (int32_t)((H / 4 + 63) / 64);
     const int64_t grid = el * a.col_blocks;
-    hipLaunchKernelGGL(moe_expert_kernel<kMoeRows>, dim3((unsigned)grid), dim3(kMoeWaves * 64),
-                       (unsigned)lds, st, a);
+    if (lds > 64 * 1024 && hipFuncSetAttribute(reinterpret_cast<const void*>(v.fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds) != hipSuccess)
+        return TP_ERR_DEVICE;
+    hipLaunchKernelGGL(v.fn, dim3((unsigned)grid), dim3(v.nw * 64), (unsigned)lds, st, a);
     if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
     const int64_t n_out = (int64_t)tokens * H;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st,

@@ -39,6 +39,10 @@ PointGeom tp_geom_for(const tp_plan_s* p, int64_t k_r, int32_t batch, int32_t sp
     int64_t target = p->target_wgs ? p->target_wgs : 2 * kTargetCUs;
     int64_t s = splits_user > 0 ? splits_user
                                 : (target + g.col_tiles / 2) / g.col_tiles;
+    // On the matrix-core path every split writes and re-reads a b x cols fp32
+    // partial; keep at least 256 rows per split so that this traffic stays a
+    // fraction of the weights' (b <= 64: at most half).
+    if (g.path == TP_PATH_MFMA && splits_user <= 0 && s > ceil_div(k_r, 256)) s = ceil_div(k_r, 256);
     if (s < 1) s = 1;
     int64_t s_max = ceil_div(k_r, gran);
     if (s > s_max) s = s_max;
@@ -141,6 +145,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "segment_loads")) {
         if (value != 0 && value != 4 && value != 8) return TP_ERR_INVALID_ARG;
         p->segment_loads = (int32_t)value;
+    } else if (!strcmp(key, "moe_variant")) {
+        if (value < 0 || value > 7) return TP_ERR_INVALID_ARG;
+        p->moe_variant = (int32_t)value;
     } else if (!strcmp(key, "stream_kind")) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->stream_kind = (int32_t)value;
