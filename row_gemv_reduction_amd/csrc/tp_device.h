@@ -42,6 +42,23 @@ __device__ __forceinline__ u32x4_t load_stream16(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
+// 16-byte device-coherent (sc1) accesses through a raw buffer descriptor
+// over [base, base + bytes): four consecutive fp32 values exchanged between
+// workgroups in one access instead of four.
+constexpr int kCachePolicyDevice = 16;  // sc1: coherent at device scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferRsrcWord3);
+}
+__device__ __forceinline__ floatx4_t ld_dev4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+    return __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0,
+                                                                                kCachePolicyDevice));
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, floatx4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, byte_off, 0,
+                                           kCachePolicyDevice);
+}
+
 // Device-coherent accesses for data exchanged inside one launch.
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -90,26 +107,6 @@ __device__ __forceinline__ float ring_element(const float* slots, int64_t len, i
         }
     }
     return s + residual;
-}
-
-// Sum of the split partials src[s * stride], s = 0..S-1, in split order,
-// with up to 8 device-coherent loads in flight at once.
-__device__ __forceinline__ float sum_splits(const float* src, int splits, int64_t stride) {
-#pragma clang fp contract(off)
-    float v = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-        float l[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            int sp = s0 + u < splits ? s0 + u : splits - 1;
-            l[u] = ld_dev(src + (int64_t)sp * stride);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (s0 + u < splits) v = (s0 + u == 0) ? l[u] : v + l[u];
-        }
-    }
-    return v;
 }
 
 // Thread 0 waits until *ctr >= target; bounded. On timeout (or if another

@@ -62,16 +62,21 @@ struct Epilogue {
 
 // Publish this split's partial tile [batch][COLS] (LDS) and find out whether
 // this workgroup arrived last for its column tile. Returns true for the
-// last arrival (and always when there is a single split).
+// last arrival (and always when there is a single split). Four columns per
+// device-coherent 16-byte store (H and COLS are multiples of 4).
 template <int COLS, int NT>
 __device__ bool publish_split(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
                               int sp, int tid, int* s_flag) {
     if (e.splits == 1) return true;
     const int64_t n0 = (int64_t)ct * COLS;
-    for (int idx = tid; idx < batch * COLS; idx += NT) {
-        int bb = idx / COLS, c = idx - bb * COLS;
-        int64_t n = n0 + c;
-        if (n < H) st_dev(e.ws_part + ((int64_t)sp * batch + bb) * H + n, tile[idx]);
+    const __amdgpu_buffer_rsrc_t rs =
+        dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * batch * H * 4));
+    for (int idx = tid; idx < batch * COLS / 4; idx += NT) {
+        const int bb = idx / (COLS / 4), c = (idx - bb * (COLS / 4)) * 4;
+        const int64_t n = n0 + c;
+        if (n < H)
+            st_dev4(rs, (uint32_t)((((int64_t)sp * batch + bb) * H + n) * 4),
+                    *reinterpret_cast<const floatx4_t*>(tile + bb * COLS + c));
     }
     wait_mem();
     __syncthreads();
@@ -86,22 +91,46 @@ __device__ bool publish_split(const Epilogue& e, const float* tile, int batch, i
 
 // Last arrival: sum the splits in split order, write the partial and, with
 // the ring epilogue, the ring-order sum + residual into the hidden state.
+// Four columns at a time; every element is still summed in split order.
 template <int COLS, int NT>
 __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
                            int tid) {
+#pragma clang fp contract(off)
     const int64_t n0 = (int64_t)ct * COLS;
     const int64_t len = (int64_t)batch * H;
-    for (int idx = tid; idx < batch * COLS; idx += NT) {
-        int bb = idx / COLS, c = idx - bb * COLS;
-        int64_t n = n0 + c;
+    const __amdgpu_buffer_rsrc_t rp = dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * len * 4));
+    const __amdgpu_buffer_rsrc_t rh = dev_rsrc(e.hidden, (uint32_t)(len * 4));
+    for (int idx = tid; idx < batch * COLS / 4; idx += NT) {
+        const int bb = idx / (COLS / 4), c = (idx - bb * (COLS / 4)) * 4;
+        const int64_t n = n0 + c;
         if (n >= H) continue;
         const int64_t i = (int64_t)bb * H + n;
         // the residual load goes out with the split loads (one round trip)
-        const float res = e.ring_slots ? ld_dev(e.hidden + i) : 0.f;
-        const float v = e.splits > 1 ? sum_splits(e.ws_part + i, e.splits, len) : tile[idx];
-        e.p[i] = v;
-        if (e.ring_slots)
-            st_dev(e.hidden + i, ring_element(e.ring_slots, len, i, e.chunk, e.n_ranks, e.rank, v, res));
+        const floatx4_t res = e.ring_slots ? ld_dev4(rh, (uint32_t)(i * 4)) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+        floatx4_t v;
+        if (e.splits > 1) {
+            floatx4_t l[8];
+            for (int s0 = 0; s0 < e.splits; s0 += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sp = s0 + u < e.splits ? s0 + u : e.splits - 1;
+                    l[u] = ld_dev4(rp, (uint32_t)(((int64_t)sp * len + i) * 4));
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < e.splits) v = (s0 + u == 0) ? l[u] : v + l[u];
+            }
+        } else {
+            v = *reinterpret_cast<const floatx4_t*>(tile + bb * COLS + c);
+        }
+        *reinterpret_cast<floatx4_t*>(e.p + i) = v;
+        if (e.ring_slots) {
+            floatx4_t o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], res[k]);
+            st_dev4(rh, (uint32_t)(i * 4), o);
+        }
     }
     if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
     wait_mem();
@@ -126,7 +155,7 @@ struct ValuShared {
     static constexpr int XS = valu_rows_max(B, COLS) * B;
     float xs[XS];
     float red[kValuWaves * COLS];
-    float tile[B * COLS];
+    __attribute__((aligned(16))) float tile[B * COLS];
     int flag;
 };
 
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int bat
     constexpr int NT = kMfmaWaves * 64;
     constexpr int COLS = kMfmaCols;
     __shared__ float red[kMfmaWaves * 16 * COLS];  // 32 KB
-    __shared__ float tile[BT * 16 * COLS];
+    __shared__ __align__(16) float tile[BT * 16 * COLS];
     __shared__ int s_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -514,6 +543,7 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
     a.epi = epi;
     // host-side checks of what the kernels assume
     if (g.splits < 1 || g.col_tiles < 1 || (int64_t)g.rows * g.splits < g.k_r) return TP_ERR_INVALID_ARG;
+    if ((int64_t)g.splits * batch * p->hidden * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
     if (g.col_tiles > kMaxCounters) return TP_ERR_UNSUPPORTED;
     if (g.path == TP_PATH_VALU) {
         if (batch < 1 || batch > kValuMaxBatch || g.rows > valu_rows_max(batch, g.cols))
@@ -553,6 +583,8 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
             (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
             return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * 2 * geo[0].col_tiles >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
+    for (int pt = 0; pt < 2; ++pt)
+        if ((int64_t)geo[pt].splits * b * p->hidden * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
     step_fn k = step_kernel(b, geo[0].cols);
     if (!k) return TP_ERR_UNSUPPORTED;
     StepArgs a;
