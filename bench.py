@@ -180,8 +180,9 @@ def dense_run(args, w, tune):
 
         def step():
             tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
-        kernel = "%s (one launch per step, %d reconciliation points)" % (
-            "decode_stream" if info["packed_kind"] == 1 else "decode_stream_mfma", 2 * w.layers)
+        name = "decode_stream" if info["packed_kind"] == 1 else (
+            "decode_stream_mfma (%d workgroups sharing the tiles)" % info["stream_wgs"])
+        kernel = "%s (one launch per step, %d reconciliation points)" % (name, 2 * w.layers)
     else:
         def step():
             tp.tp_decode_layers(plan, w.layers, args.rank, xa, wo, xf, wd, slots, hidden, ws)

@@ -85,6 +85,7 @@ typedef struct {
     int32_t packed_kind;     /* layout of tp_pack_weights / kernel of tp_decode_layers_packed:
                                 0 = the plan is not supported, 1 = pair strips (vector ALU),
                                 2 = MFMA tiles (matrix cores) */
+    int32_t stream_wgs;      /* packed_kind 2: workgroups of the matrix-core step (0 otherwise) */
 } tp_plan_info;
 
 /*
@@ -126,6 +127,8 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  *                batch <= 4),
  * "stream_kind" (tp_decode_layers_packed: 0 = automatic, 1 = vector-ALU
  *                stream on pair strips, 2 = matrix-core stream on MFMA tiles),
+ * "stream_wgs" (matrix-core stream: workgroups sharing the tiles, 0 = one
+ *                per compute unit; at most 256 and H/16, at least H/32),
  * "moe_variant" (tp_moe_partial's expert kernel: 0 = default, 1..7),
  * "serial_points" (tp_decode_layers_packed: 0 = each hidden-state element
  *                follows its own chain, 1 = point j+1 also waits for all of

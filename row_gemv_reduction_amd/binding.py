@@ -38,6 +38,7 @@ class tp_plan_info(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("ep", ctypes.c_int32),
         ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
         ("max_tokens", ctypes.c_int32), ("packed_kind", ctypes.c_int32),
+        ("stream_wgs", ctypes.c_int32),
     ]
 
 

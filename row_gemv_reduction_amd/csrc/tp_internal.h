@@ -10,8 +10,9 @@
 constexpr int kTargetCUs = 256;
 constexpr int kXCDs = 8;
 
-// Workspace layout: [column-tile counters | step sync words][split-K partials][MoE scratch]
-constexpr int64_t kCounterBytes = 128 * 1024;
+// Workspace layout: [column-tile counters | step sync words | split stream counters]
+//                   [split-K partials][split stream slice partials][MoE scratch]
+constexpr int64_t kCounterBytes = 256 * 1024;
 constexpr int kCounterStride = 16;            // one counter per 64-byte line
 constexpr int kMaxCounters = 1024;            // column-tile arrival counters (64 KiB)
 constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, error
@@ -46,6 +47,14 @@ constexpr int kStreamMaxLdsBytes = 150 * 1024;  // x buffers (dynamic LDS)
 // completion words of the serial point order (byte offset in the workspace)
 constexpr int64_t kStreamFlagOffset = kSyncOffset + 16 * 1024;
 
+// MFMA stream: strips cut between two workgroups hand a partial over through
+// device memory: kXchgRing buffers per kind of point and strip, and per kind
+// and strip a "published" and an "acknowledged" word, then the exit counter
+constexpr int kXchgRing = 4;
+constexpr int kXchgMaxStrips = 512;
+constexpr int64_t kXchgFlagOffset = 128 * 1024;
+constexpr int64_t kXchgExitOffset = kXchgFlagOffset + 4 * kXchgMaxStrips * 4;
+
 // MoE
 constexpr int kMoeMaxTopK = 32;
 constexpr int kMoeMaxTokens = 4096;
@@ -62,6 +71,7 @@ struct tp_plan_s {
     int32_t serial_points = 0;  // streamed step: point j+1 waits for all of point j
     int32_t stream_kind = 0;    // 0 = automatic, 1 = pair strips (VALU), 2 = MFMA tiles
     int32_t moe_variant = 0;    // expert kernel variant (0 = default)
+    int32_t stream_wgs = 0;     // MFMA stream: workgroups (0 = one per CU, at most H/16)
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -98,16 +108,20 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
 
 // Geometry of the MFMA streamed decode step (tp_mfma_stream.hip).
 struct MfmaGeom {
-    int32_t grid, block, wps, bt, sl;
-    int32_t nkb0, nkb1, bpw0, bpw1;
-    int32_t red_floats, oth_floats, lds_bytes;
+    int32_t grid, block, wps, bt;
+    int32_t nkb0, nkb1;
+    int32_t oth_strip, own_max;    // other ranks' values per owned strip (floats); owned strips
+    int32_t lds_bytes;             // dynamic LDS
 };
 bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g);
+int64_t tp_xchg_bytes(const tp_plan_s* p);  // exchange buffers of the MFMA stream
+int64_t tp_ws_xchg_offset(const tp_plan_s* p);
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,
                                 const void* x_attn, const void* w_o_tiles, const void* x_ffn,
-                                const void* w_down_tiles, float* slots, float* hidden, void* stream);
+                                const void* w_down_tiles, float* slots, float* hidden, void* ws,
+                                void* stream);
 // Packed layout (and streamed kernel) the plan uses: 0 none, 1 pair strips, 2 MFMA tiles.
 int tp_packed_kind(const tp_plan_s* p);
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections

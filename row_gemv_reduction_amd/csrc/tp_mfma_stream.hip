@@ -20,22 +20,31 @@
 // (x rows 16g+8h .. +8) cover, per token, one whole 128-byte line of x
 // between them: the second load of the line hits L1.
 //
-// decode_stream_mfma: one launch per step; workgroup s owns the 16-column
-// strip s for every point (one workgroup per strip; at most two per CU).
-//   - WPS compute waves interleave the strip's tiles. Each wave streams its
-//     tiles through two register banks of SL tiles: the weight tile and, per
-//     16-token block, the matching A operand (the x rows, 16 bytes per lane,
-//     read straight from x; x is small and shared by every workgroup, so it
-//     comes from L2). Loads are never conditional (empty buffer ranges read
-//     zero), so consuming one bank never waits for the other. Tokens past b
-//     and rows past K read zero.
-//   - one control wave: at each point's end sums the waves' D tiles in wave
-//     order, writes the rank's partial to its slot and forms the ring-order
-//     sum with the other ranks' values (staged into LDS a point ahead with
-//     direct global->LDS loads) plus the residual, which stays in LDS for the
-//     whole step.
+// decode_stream_mfma: one launch per step, G workgroups (one per CU).
+// Work is balanced by tiles, not by strips: per point the S16 * nkb tiles,
+// taken in strip-major order, are cut into G equal contiguous ranges, one
+// per workgroup (with H = 5120 there are 320 strips for 256 CUs, so whole
+// strips would leave a quarter of the CUs doing twice the work). A range
+// falls into segments, one per strip it touches; a strip cut between two
+// workgroups is owned by the one that holds its first tile (that owner is
+// the same for both kinds of point), and the other one, its contributor,
+// hands over the partial of the remaining rows through device memory.
+//   - WPS compute waves interleave each segment's tiles. Each wave streams
+//     its tiles through two register banks of SL tiles: the weight tile and,
+//     per 16-token block, the matching A operand (the x rows, 16 bytes per
+//     lane, read straight from x, which every workgroup reads and L2 keeps).
+//     Loads are never conditional (empty buffer ranges read zero), so
+//     consuming one bank never waits for the other. Tokens past b and rows
+//     past K read zero. At a segment's end a wave stores its D tiles to LDS,
+//     counts itself and streams on (no barrier).
+//   - one control wave takes the segments in order: sums the waves' D tiles
+//     in wave order; a contributor publishes that partial; an owner adds the
+//     contributor's partial (its own rows first), writes the rank's partial
+//     to its slot and forms the ring-order sum with the other ranks' values
+//     (staged into LDS a point ahead with direct global->LDS loads) plus the
+//     residual, which stays in LDS for the whole step.
 // Point order: as decode_stream's default (each hidden-state element follows
-// its own chain; no grid-wide synchronisation).
+// its own chain, kept by the strip's owner; no grid-wide synchronisation).
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -85,100 +94,326 @@ struct MfmaArgs {
     const uint16_t* w1;     // tiles of w_down [L][H/16][nkb1][2][64][8]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
-    int32_t H, S16, WPS, batch;
-    int32_t K0, K1, nkb0, nkb1, bpw0, bpw1;
+    float* xpart;           // [2][kXchgRing][S16][BT][64][4] contributors' partials
+    uint32_t* pub;          // [2][S16] contributor has published point j: j + 1
+    uint32_t* ack;          // [2][S16] owner has read point j: j + 1
+    uint32_t* exit_ctr;     // workgroups that have left
+    uint32_t* err;          // error word (bit 0: an exchange wait timed out, bit 1: a wave wait)
+    int32_t H, S16, G, batch;
+    int32_t K0, K1, nkb0, nkb1;
     int32_t layers, n_ranks, rank, chunk;
-    int32_t red_floats;     // LDS floats of one parity of the waves' D tiles
-    int32_t oth_floats;     // LDS floats of one parity of the other ranks' values
+    int32_t oth_strip;      // LDS floats of the other ranks' values per owned strip
+    int32_t own_max;        // owned strips per workgroup at most (their buffers per parity)
+    uint32_t spin_limit;
 };
+
+// A workgroup's work for one kind of point: up to kMaxSeg segments (strip,
+// first tile, tiles, role).
+constexpr int kMaxSeg = 4;
+constexpr int kMaxOwn = 2;  // strips whose hidden state a workgroup keeps
+enum { kFull = 0, kOwnerPart = 1, kContrib = 2 };
+
+// Tiles u = s * nkb + kb of one kind of point, in strip-major order; workgroup
+// g takes u in [ceil(g T / G), ceil((g+1) T / G)), T = S16 * nkb. The tile
+// kb = 0 of strip s falls to workgroup floor(s G / S16) whatever nkb is, so
+// a strip has the same owner for both kinds of point; with G <= S16 every
+// range holds at least nkb tiles, so a strip is cut at most once.
+__device__ int wg_segments(int g, int G, int S16, int nkb, int (*out)[4]) {
+    const int64_t T = (int64_t)S16 * nkb;
+    const int64_t u0 = ((int64_t)g * T + G - 1) / G, u1 = ((int64_t)(g + 1) * T + G - 1) / G;
+    int n = 0;
+    for (int64_t u = u0; u < u1 && n < kMaxSeg;) {
+        const int s = (int)(u / nkb);
+        const int kb0 = (int)(u - (int64_t)s * nkb);
+        const int64_t e = u1 < (int64_t)(s + 1) * nkb ? u1 : (int64_t)(s + 1) * nkb;
+        out[n][0] = s;
+        out[n][1] = kb0;
+        out[n][2] = (int)(e - u);
+        out[n][3] = kb0 > 0 ? kContrib : (e - u == nkb ? kFull : kOwnerPart);
+        ++n;
+        u = e;
+    }
+    return n;
+}
 
 struct Cursor {
-    int j, m0;
+    int j, i, m0;            // point, segment, first slot of the bank
+    int s, kb0, len, bpw, rot;  // the segment's strip, tiles, slots per wave, walk rotation
 };
 
-template <int BT, int SL>
+// LDS word loads/stores that the compiler neither caches nor reorders with
+// respect to each other (flags between the waves of one workgroup).
+__device__ __forceinline__ int lds_ld(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_add(int* p, int v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// This wave's LDS accesses have completed (and a compiler barrier).
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until the LDS flag reaches `target`. Bounded (far beyond any real
+// wait): on timeout the error word is set and the wave goes on, so the
+// launch always ends.
+constexpr int kWaveSpinLimit = 1 << 22;
+__device__ __forceinline__ void wait_flag(const int* f, int target, uint32_t* err) {
+    for (int n = 0; lds_ld(f) < target; ++n) {
+        if (n >= kWaveSpinLimit) {
+            __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// The waves of a workgroup meet through LDS flags, not barriers: a compute
+// wave stores its D tiles of segment e, counts itself in arrivals[e & 1] and
+// goes on streaming; the control wave starts on segment e once all WPS waves
+// have counted, and publishes `consumed` = e + 1 once it has read their
+// tiles, which frees that parity's buffer for segment e + 2. So no wave ever
+// waits for the slowest of its siblings, only (rarely) for the control wave
+// to fall two segments behind.
+template <int BT, int SL, int WPS, int NSTG>
 __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
-    // [2][WPS][BT][64][4] D tiles | [2][(N-1) * B][16] other ranks | [B][16] hidden
-    extern __shared__ __align__(16) float sh[];
-    float* red = sh;
-    float* oth = sh + 2 * a.red_floats;
-    float* hs = oth + 2 * a.oth_floats;
+    constexpr int kRed = WPS * BT * 256;                  // floats of one parity
+    __shared__ __align__(16) float red[2 * kRed];          // [2][WPS][BT][64][4] D tiles
+    __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, D-tile layout
+    __shared__ __align__(16) float vs[BT * 256];           // a segment's partial, D-tile layout
+    __shared__ __align__(16) float vr[BT * 256];           // the same, [token][16 columns]
+    __shared__ int flags[8];                               // arrivals[2], consumed, staged[2], oth_free
+    __shared__ int segtab[2][kMaxSeg][4];
+    __shared__ int nseg[2];
+    __shared__ int s_last;
+    extern __shared__ __align__(16) float oth[];           // [2][own][(N-1) * B][16] other ranks
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = blockIdx.x;
+    const int g = blockIdx.x;
     const int n_points = 2 * a.layers;
     const int B = a.batch;
     const int len = B * a.H;
+    // lane l of a D tile holds tokens 16tt + 4(l/16) + k (k < 4) of column l % 16
+    const int col = lane & 15, tq = 4 * (lane >> 4);
+    // strips whose kb = 0 tile is ours: [own0, own0 + nown)
+    const int own0 = (int)(((int64_t)g * a.S16 + a.G - 1) / a.G);
+    const int nown = (int)(((int64_t)(g + 1) * a.S16 + a.G - 1) / a.G) - own0;
+
+    if (tid == 0) {
+        nseg[0] = wg_segments(g, a.G, a.S16, a.nkb0, segtab[0]);
+        nseg[1] = wg_segments(g, a.G, a.S16, a.nkb1, segtab[1]);
+        for (int f = 0; f < 8; ++f) flags[f] = 0;
+    }
 
     if (wave == 0) {
         // ---------------------------------------------------- control wave
         __builtin_amdgcn_s_setprio(3);
-        const int n_el = 16 * B;
-        for (int e = lane; e < n_el; e += 64) hs[e] = a.hidden[(e >> 4) * a.H + 16 * s + (e & 15)];
-        // the other ranks' 16 values per token, rows ordered (other rank, token)
-        auto stage_others = [&](int j) {
+        for (int o = 0; o < nown; ++o)
+#pragma unroll
+            for (int tt = 0; tt < BT; ++tt) {
+                floatx4_t h;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int tok = 16 * tt + tq + k;
+                    h[k] = tok < B ? a.hidden[(int64_t)tok * a.H + 16 * (own0 + o) + col] : 0.f;
+                }
+                *reinterpret_cast<floatx4_t*>(hs + ((o * BT + tt) * 64 + lane) * 4) = h;
+            }
+        const uint32_t xbytes = (uint32_t)((int64_t)2 * kXchgRing * a.S16 * BT * 1024);
+        const __amdgpu_buffer_rsrc_t rx = dev_rsrc(a.xpart, xbytes);
+        int ok = 1;
+        __syncthreads();  // start: segment tables, flags and hidden columns are in LDS
+        int e = 0;
+        for (int j = 0; j < n_points; ++j) {
+            const int t = j & 1;
+            const int ns = nseg[t];
+            bool staged = false;
+            for (int i = 0; i < ns; ++i, ++e) {
+                const int s = segtab[t][i][0], role = segtab[t][i][3];
+                wait_flag(&flags[e & 1], (e / 2 + 1) * WPS, a.err);
+                lds_wait();
+                // the segment's partial: the waves' D tiles summed in wave order
+                const float* re = red + (e & 1) * kRed;
+#pragma unroll
+                for (int tt = 0; tt < BT; ++tt) {
+                    floatx4_t part[WPS];
+#pragma unroll
+                    for (int wi = 0; wi < WPS; ++wi)
+                        part[wi] = *reinterpret_cast<const floatx4_t*>(re + (wi * BT + tt) * 256 + lane * 4);
+                    floatx4_t v = part[0];
+#pragma unroll
+                    for (int wi = 1; wi < WPS; ++wi) v = v + part[wi];
+                    *reinterpret_cast<floatx4_t*>(vs + (tt * 64 + lane) * 4) = v;
+                }
+                lds_wait();
+                if (lane == 0) lds_st(&flags[2], e + 1);  // red[e & 1] may be rewritten (segment e + 2)
+                // exchange buffer of this kind of point and strip: slot (j/2) mod R,
+                // last used at point j - 2R
+                const int jj = j >> 1;
+                const uint32_t xoff = (uint32_t)((((int64_t)t * kXchgRing + jj % kXchgRing) * a.S16 + s) * BT * 1024);
+                uint32_t* pub = a.pub + t * a.S16 + s;
+                uint32_t* ack = a.ack + t * a.S16 + s;
+                if (role == kContrib) {
+                    if (jj >= kXchgRing && ok) {
+                        if (lane == 0) ok = wait_at_least(ack, (uint32_t)(j - 2 * kXchgRing + 1), a.err, a.spin_limit);
+                        ok = __builtin_amdgcn_readfirstlane(ok);
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < BT; ++tt)
+                        st_dev4(rx, xoff + (uint32_t)((tt * 64 + lane) * 16),
+                                *reinterpret_cast<const floatx4_t*>(vs + (tt * 64 + lane) * 4));
+                    wait_mem();
+                    if (lane == 0) st_dev_u32(pub, (uint32_t)(j + 1));
+                    continue;
+                }
+                if (role == kOwnerPart) {
+                    // the contributor's rows come after ours
+                    if (ok) {
+                        if (lane == 0) ok = wait_at_least(pub, (uint32_t)(j + 1), a.err, a.spin_limit);
+                        ok = __builtin_amdgcn_readfirstlane(ok);
+                    }
+                    floatx4_t c[BT];
+#pragma unroll
+                    for (int tt = 0; tt < BT; ++tt) c[tt] = ld_dev4(rx, xoff + (uint32_t)((tt * 64 + lane) * 16));
+                    wait_mem();
+                    if (lane == 0) st_dev_u32(ack, (uint32_t)(j + 1));
+#pragma unroll
+                    for (int tt = 0; tt < BT; ++tt) {
+                        float* vp = vs + (tt * 64 + lane) * 4;
+                        *reinterpret_cast<floatx4_t*>(vp) = *reinterpret_cast<const floatx4_t*>(vp) + c[tt];
+                    }
+                }
+                // ring order: chunk c starts at rank c, then c+1, ... (mod N); then the residual
+                if (!staged) {
+                    wait_flag(&flags[3 + t], NSTG * (jj + 1), a.err);  // point j's other values are in LDS
+                    lds_wait();
+                    staged = true;
+                }
+                const int o = s - own0;
+                const float* oj = oth + ((j & 1) * a.own_max + o) * a.oth_strip;
+                float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
+                float* hso = hs + o * BT * 256;
+#pragma unroll 1
+                for (int tt = 0; tt < BT; ++tt) {
+                    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(vs + (tt * 64 + lane) * 4);
+                    const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hso + (tt * 64 + lane) * 4);
+                    floatx4_t hn;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+#pragma clang fp contract(off)
+                        const int tok = 16 * tt + tq + k;
+                        const int tokc = tok < B ? tok : B - 1;
+                        const int idx = tokc * a.H + 16 * s + col;
+                        const int cidx = idx / a.chunk;
+                        float ov[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int uu = u < a.n_ranks ? u : a.n_ranks - 1;
+                            int r = cidx + uu;
+                            r = r >= a.n_ranks ? r - a.n_ranks : r;
+                            int ro = r < a.rank ? r : r - 1;
+                            ro = ro < 0 ? 0 : ro;
+                            const float ovv = oj[(ro * B + tokc) * 16 + col];
+                            ov[u] = r == a.rank ? v[k] : ovv;
+                        }
+                        float sum = ov[0];
+#pragma unroll
+                        for (int u = 1; u < 8; ++u)
+                            if (u < a.n_ranks) sum = sum + ov[u];
+                        hn[k] = tok < B ? sum + h[k] : 0.f;
+                        vr[(16 * tt + tq + k) * 16 + col] = v[k];
+                    }
+                    *reinterpret_cast<floatx4_t*>(hso + (tt * 64 + lane) * 4) = hn;
+                }
+                // the rank's partial to its slot, four columns of one token per lane
+                lds_wait();
+#pragma unroll 1
+                for (int tt = 0; tt < BT; ++tt) {
+                    const int tok = 16 * tt + (lane >> 2), c4 = 4 * (lane & 3);
+                    if (tok < B)
+                        *reinterpret_cast<floatx4_t*>(slot + (int64_t)tok * a.H + 16 * s + c4) =
+                            *reinterpret_cast<const floatx4_t*>(vr + tok * 16 + c4);
+                }
+            }
+            // the other values of point j have been read: their buffer may be refilled (point j + 2)
+            lds_wait();
+            if (lane == 0) lds_st(&flags[5], j + 1);
+        }
+        lds_wait();
+        for (int o = 0; o < nown; ++o)
+#pragma unroll
+            for (int tt = 0; tt < BT; ++tt) {
+                const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hs + ((o * BT + tt) * 64 + lane) * 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int tok = 16 * tt + tq + k;
+                    if (tok < B) a.hidden[(int64_t)tok * a.H + 16 * (own0 + o) + col] = h[k];
+                }
+            }
+        wait_mem();
+    } else if (wave <= NSTG) {
+        // ---------------------------------------------------- stager waves
+        // The other ranks' 16 values per token of each owned strip, rows
+        // ordered (other rank, token), staged with direct global->LDS loads
+        // into oth[j & 1] a point ahead; stager q issues every NSTG-th load.
+        // These waves issue nothing else, so their memory waits are short.
+        const int q = wave - 1;
+        __syncthreads();  // start
+        const int rows = (a.n_ranks - 1) * B;
+        const int per_strip = (rows + 15) / 16;
+        for (int j = 0; j < n_points; ++j) {
+            // oth[j & 1] was last read at point j - 2
+            wait_flag(&flags[5], j - 1, a.err);
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
-            float* dst = oth + (j & 1) * a.oth_floats;
-            const int rows = (a.n_ranks - 1) * B;
-            for (int r0 = 0; r0 < rows; r0 += 16) {
+            for (int n = q; n < nown * per_strip; n += NSTG) {
+                const int o = n / per_strip, r0 = (n - o * per_strip) * 16;
                 int row = r0 + lane / 4;
                 row = row < rows ? row : rows - 1;
                 const int ro = row / B, tok = row - ro * B;
                 const int r = ro < a.rank ? ro : ro + 1;
-                const float* src = slot + (int64_t)r * len + (int64_t)tok * a.H + 16 * s + 4 * (lane & 3);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                                 (lds_void_t*)(dst + r0 * 16), 16, 0, 0);
+                const float* src = slot + (int64_t)r * len + (int64_t)tok * a.H + 16 * (own0 + o) + 4 * (lane & 3);
+                float* dst = oth + ((j & 1) * a.own_max + o) * a.oth_strip + r0 * 16;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void_t*)dst, 16, 0, 0);
             }
-        };
-        if (a.n_ranks > 1) stage_others(0);
-        wait_mem();
-        __syncthreads();  // start: hidden columns and the first point's other values are in LDS
-        for (int j = 0; j < n_points; ++j) {
-            __syncthreads();  // P_j: the waves' D tiles of point j are in red[j & 1]
-            if (a.n_ranks > 1 && j + 1 < n_points) stage_others(j + 1);
-            const float* rj = red + (j & 1) * a.red_floats;
-            const float* oj = oth + (j & 1) * a.oth_floats;
-            float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
-            for (int e = lane; e < n_el; e += 64) {
-#pragma clang fp contract(off)
-                const int tok = e >> 4, col = e & 15;
-                const int tt = tok >> 4, m = tok & 15;
-                const int d = ((tt * 64) + 16 * (m >> 2) + col) * 4 + (m & 3);
-                float v = rj[d];
-                for (int wi = 1; wi < a.WPS; ++wi) v += rj[wi * BT * 256 + d];
-                const int i = tok * a.H + 16 * s + col;
-                slot[i] = v;
-                // ring order: chunk c starts at rank c, then c+1, ... (mod N)
-                const int cidx = i / a.chunk;
-                float sum = 0.f;
-                for (int u = 0; u < a.n_ranks; ++u) {
-                    int r = cidx + u;
-                    if (r >= a.n_ranks) r -= a.n_ranks;
-                    const int ro = r < a.rank ? r : r - 1;
-                    const float val = r == a.rank ? v : oj[(ro * B + tok) * 16 + col];
-                    sum = u == 0 ? val : sum + val;
-                }
-                hs[e] = sum + hs[e];
-            }
-            wait_mem();  // the next point's other values are staged before P_{j+1}
+            wait_mem();
+            if (lane == 0) lds_add(&flags[3 + (j & 1)], 1);
         }
-        for (int e = lane; e < n_el; e += 64) a.hidden[(e >> 4) * a.H + 16 * s + (e & 15)] = hs[e];
     } else {
         // --------------------------------------------------- compute waves
-        const int wi = wave - 1;
-        auto bpw = [&](int j) { return (j & 1) ? a.bpw1 : a.bpw0; };
-        auto advance = [&](Cursor& cu) {
-            cu.m0 += SL;
-            if (cu.m0 >= bpw(cu.j)) { cu.j += 1; cu.m0 = 0; }
+        const int wi = wave - 1 - NSTG;
+        __syncthreads();  // start: the segment tables are in LDS
+        auto set_seg = [&](Cursor& c) {
+            if (c.j >= n_points) return;
+            const int* tb = segtab[c.j & 1][c.i];
+            c.s = tb[0];
+            c.kb0 = tb[1];
+            c.len = tb[2];
+            c.bpw = (c.len + WPS - 1) / WPS;
+            // whole strips start their walk at different places (a rotation
+            // by whole rounds of WPS tiles), so that workgroups do not all
+            // read the same rows of x at the same moment
+            c.rot = tb[3] == kFull ? (g % c.bpw) * WPS : 0;
+        };
+        auto advance = [&](Cursor& c) {
+            c.m0 += SL;
+            if (c.m0 >= c.bpw) {
+                c.m0 = 0;
+                if (++c.i >= nseg[c.j & 1]) {
+                    c.i = 0;
+                    ++c.j;
+                }
+                set_seg(c);
+            }
         };
         // A operand of lane l: token 16*tt + l%16, rows 16*(l/16) + 8h .. +7 of the tile
         const int xo = lane & 15, xk = 16 * (lane >> 4);
-        auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& cu) {
-            const int t = cu.j & 1, l = cu.j >> 1;
-            const bool live = cu.j < n_points;
+        auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& c) {
+            const int t = c.j & 1, l = c.j >> 1;
+            const bool live = c.j < n_points;
             const int K = t ? a.K1 : a.K0, nkb = t ? a.nkb1 : a.nkb0;
-            const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + s) * nkb * (kTileBytes / 2);
+            const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
             const uint16_t* xb = (t ? a.x1 : a.x0) + (int64_t)l * B * K;
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
@@ -186,18 +421,13 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? xb : a.x0), (short)0, live ? B * K * 2 : 0,
                 kBufferRsrcWord3);
-            // Workgroups start their walk over a point's tiles at different
-            // places (a rotation by whole rounds of WPS tiles), so that they do
-            // not all read the same rows of x at the same moment. Slots past
-            // the wave's bpw tiles (the tail of the last segment) stay past the
-            // span, which reads zero.
-            const int bpw = t ? a.bpw1 : a.bpw0;
-            const int span = bpw * a.WPS;
-            const int rot = (s % bpw) * a.WPS;
+            // slots past the segment's tiles read zero (tile nkb is past the strip)
+            const int span = c.bpw * WPS;
 #pragma unroll
             for (int i = 0; i < SL; ++i) {
-                int kb = wi + (cu.m0 + i) * a.WPS + rot;
-                kb = cu.m0 + i >= bpw ? span : kb >= span ? kb - span : kb;
+                int kl = wi + (c.m0 + i) * WPS + c.rot;
+                kl = kl >= span ? kl - span : kl;
+                const int kb = (c.m0 + i < c.bpw && kl < c.len) ? c.kb0 + kl : nkb;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     wv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
@@ -226,65 +456,98 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                             __builtin_bit_cast(bf16x8_t, xv[i][h][tt]), __builtin_bit_cast(bf16x8_t, wv[i][h]),
                             acc[tt], 0, 0, 0);
         };
-        auto point_end = [&](int j) {
-            float* rj = red + (j & 1) * a.red_floats + wi * BT * 256;
+        int e = 0;
+        auto seg_end = [&]() {
+            // red[e & 1] is free once the control wave has read segment e - 2
+            wait_flag(&flags[2], e - 1, a.err);
+            float* re = red + (e & 1) * kRed + wi * BT * 256;
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
-                *reinterpret_cast<floatx4_t*>(rj + (tt * 64 + lane) * 4) = acc[tt];
+                *reinterpret_cast<floatx4_t*>(re + (tt * 64 + lane) * 4) = acc[tt];
                 acc[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }
-            __syncthreads();  // P_j
+            lds_wait();
+            if (lane == 0) lds_add(&flags[e & 1], 1);
+            ++e;
         };
 
         u32x4_t w0[SL][2], w1[SL][2], x0[SL][2][BT], x1[SL][2][BT];
-        Cursor ci{0, 0}, cc{0, 0};
+        Cursor ci{0, 0, 0, 0, 0, 0, 0, 0}, cc;
+        set_seg(ci);
+        cc = ci;
         issue(w0, x0, ci);
         advance(ci);
         issue(w1, x1, ci);
         advance(ci);
-        __syncthreads();  // start
         while (cc.j < n_points) {
             {
                 consume(w0, x0);
-                const int j = cc.j;
-                const bool last = cc.m0 + SL >= bpw(j);
+                const bool last = cc.m0 + SL >= cc.bpw;
                 advance(cc);
                 issue(w0, x0, ci);
                 advance(ci);
-                if (last) point_end(j);
+                if (last) seg_end();
             }
             {
                 const bool live = cc.j < n_points;
-                const int j = cc.j;
                 bool last = false;
                 if (live) {
                     consume(w1, x1);
-                    last = cc.m0 + SL >= bpw(j);
+                    last = cc.m0 + SL >= cc.bpw;
                     advance(cc);
                 }
                 issue(w1, x1, ci);
                 advance(ci);
-                if (last) point_end(j);
+                if (last) seg_end();
             }
         }
+    }
+    // The last workgroup to leave clears the exchange flags for the next
+    // launch (no workgroup reads them any more).
+    __syncthreads();
+    if (tid == 0) s_last = add_dev_u32(a.exit_ctr, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (s_last) {
+        for (int w = tid; w < 2 * a.S16; w += blockDim.x) {
+            st_dev_u32(a.pub + w, 0u);
+            st_dev_u32(a.ack + w, 0u);
+        }
+        if (tid == 0) st_dev_u32(a.exit_ctr, 0u);
     }
 }
 
 typedef void (*mfma_stream_fn)(MfmaArgs);
 
 // Tiles per bank: fewer for more token blocks (each tile also carries 2*BT
-// A operands), so the banks fit the registers.
+// A operands), so the banks fit the registers. Compute waves: 13, or 7 for
+// three and four token blocks (the LDS of their D tiles); stager waves: 2,
+// or 4 for the (N-1) * b rows of more tokens.
+constexpr int kWps[5] = {0, 13, 13, 7, 7};
+constexpr int kStagers[5] = {0, 2, 2, 4, 4};
 mfma_stream_fn mfma_stream_kernel(int bt) {
     switch (bt) {
-        case 1: return decode_stream_mfma<1, 2>;
-        case 2: return decode_stream_mfma<2, 2>;
-        case 3: return decode_stream_mfma<3, 1>;
-        case 4: return decode_stream_mfma<4, 1>;
+        case 1: return decode_stream_mfma<1, 2, kWps[1], kStagers[1]>;
+        case 2: return decode_stream_mfma<2, 2, kWps[2], kStagers[2]>;
+        case 3: return decode_stream_mfma<3, 1, kWps[3], kStagers[3]>;
+        case 4: return decode_stream_mfma<4, 1, kWps[4], kStagers[4]>;
     }
     return nullptr;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
 
 }  // namespace
 
@@ -294,29 +557,42 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     const int64_t k0 = p->k_attn / p->n_ranks, k1 = p->inter / p->n_ranks;
     if (k0 % 8 || k1 % 8) return false;
     const int64_t S16 = p->hidden / 16;
-    if (S16 > 2 * kTargetCUs) return false;  // one strip per workgroup, at most two per CU
-    const int per_cu = S16 > kTargetCUs ? 2 : 1;
+    int64_t G = p->stream_wgs > 0 ? p->stream_wgs : kTargetCUs;
+    if (G > S16) G = S16;
+    // every workgroup's range covers at least one strip's tiles and at most
+    // two strips' (at most kMaxSeg segments, kMaxOwn owned strips)
+    if (S16 > 2 * G || S16 > kXchgMaxStrips) return false;
     const int bt = (b + 15) / 16;
-    int wps = per_cu == 2 ? 7 : (bt <= 2 ? 15 : 7);
-    const int sl = bt <= 2 ? 2 : 1;
+    const int wps = kWps[bt], nstg = kStagers[bt];
     const int64_t nkb0 = (k0 + kTileRows - 1) / kTileRows, nkb1 = (k1 + kTileRows - 1) / kTileRows;
-    g->red_floats = wps * bt * 256;
-    g->oth_floats = (p->n_ranks - 1) * b * 16 > 0 ? ((p->n_ranks - 1) * b * 16 + 255) / 256 * 256 : 0;
-    g->lds_bytes = (2 * g->red_floats + 2 * g->oth_floats + ((16 * b + 63) / 64) * 64) * 4;
-    if (g->lds_bytes > (per_cu == 2 ? 76 : 152) * 1024) return false;
+    // static LDS: D tiles of both parities, owned hidden state, a segment's
+    // partial, tables; dynamic: the other ranks' values of the owned strips
+    // (room for one rank's values even with N = 1, so that the clamped reads
+    // of a single-rank plan stay inside the allocation)
+    const int own_max = (int)((S16 + G - 1) / G);
+    g->oth_strip = (int32_t)(((p->n_ranks > 1 ? p->n_ranks - 1 : 1) * b * 16 + 255) / 256 * 256);
+    g->own_max = own_max;
+    g->lds_bytes = 2 * own_max * g->oth_strip * 4;
+    const int64_t stat = (2 * wps * bt * 256 + kMaxOwn * bt * 256 + 2 * bt * 256) * 4 + 1024;
+    if (g->lds_bytes + stat > 152 * 1024) return false;
     // the largest buffer offsets must fit 32 bits
     if ((int64_t)b * (k0 > k1 ? k0 : k1) * 2 >= ((int64_t)1 << 31)) return false;
     if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes >= ((int64_t)1 << 31)) return false;
-    g->grid = (int32_t)S16;
+    if ((int64_t)b * p->hidden >= ((int64_t)1 << 31)) return false;
+    g->grid = (int32_t)G;
     g->wps = wps;
     g->bt = bt;
-    g->sl = sl;
-    g->block = (1 + wps) * 64;
+    g->block = (1 + nstg + wps) * 64;
     g->nkb0 = (int32_t)nkb0;
     g->nkb1 = (int32_t)nkb1;
-    g->bpw0 = (int32_t)((nkb0 + wps - 1) / wps);
-    g->bpw1 = (int32_t)((nkb1 + wps - 1) / wps);
     return true;
+}
+
+int64_t tp_xchg_bytes(const tp_plan_s* p) {
+    if (p->batch < 1 || p->batch > kMfmaMaxBatch || p->hidden % 16) return 0;
+    const int64_t S16 = p->hidden / 16;
+    if (S16 > kXchgMaxStrips) return 0;
+    return 2 * kXchgRing * S16 * ((p->batch + 15) / 16) * 1024;
 }
 
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
@@ -333,13 +609,13 @@ tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void*
 
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,
                                 const void* x_attn, const void* w_o_tiles, const void* x_ffn,
-                                const void* w_down_tiles, float* slots, float* hidden, void* stream) {
+                                const void* w_down_tiles, float* slots, float* hidden, void* ws,
+                                void* stream) {
     MfmaGeom geo;
     if (!tp_mfma_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
     if (!aligned16(x_attn) || !aligned16(x_ffn) || !aligned16(w_o_tiles) || !aligned16(w_down_tiles) ||
-        !aligned16(slots) || !aligned16(hidden))
+        !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
         return TP_ERR_ALIGNMENT;
-    if ((int64_t)p->batch * p->hidden >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
     if (n_layers == 0) return TP_OK;
     mfma_stream_fn k = mfma_stream_kernel(geo.bt);
     if (!k) return TP_ERR_UNSUPPORTED;
@@ -350,25 +626,34 @@ tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t ra
     a.w1 = static_cast<const uint16_t*>(w_down_tiles);
     a.slots = slots;
     a.hidden = hidden;
+    char* base = static_cast<char*>(ws);
+    a.xpart = reinterpret_cast<float*>(base + tp_ws_xchg_offset(p));
+    a.pub = reinterpret_cast<uint32_t*>(base + kXchgFlagOffset);
+    a.ack = a.pub + 2 * kXchgMaxStrips;
+    a.exit_ctr = reinterpret_cast<uint32_t*>(base + kXchgExitOffset);
+    a.err = reinterpret_cast<uint32_t*>(base + kSyncOffset) + kSyncErr;
     a.H = (int32_t)p->hidden;
     a.S16 = (int32_t)(p->hidden / 16);
-    a.WPS = geo.wps;
+    a.G = geo.grid;
     a.batch = p->batch;
     a.K0 = (int32_t)(p->k_attn / p->n_ranks);
     a.K1 = (int32_t)(p->inter / p->n_ranks);
     a.nkb0 = geo.nkb0;
     a.nkb1 = geo.nkb1;
-    a.bpw0 = geo.bpw0;
-    a.bpw1 = geo.bpw1;
     a.layers = n_layers;
     a.n_ranks = p->n_ranks;
     a.rank = rank;
     a.chunk = (int32_t)((int64_t)p->batch * p->hidden / p->n_ranks);
-    a.red_floats = geo.red_floats;
-    a.oth_floats = geo.oth_floats;
+    a.oth_strip = geo.oth_strip;
+    a.own_max = geo.own_max;
+    a.spin_limit = 1u << 20;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                             hipFuncAttributeMaxDynamicSharedMemorySize, geo.lds_bytes) != hipSuccess)
         return TP_ERR_DEVICE;
+    // The exchange waits need every workgroup resident at once: one per CU,
+    // so the device must have at least G of them (a partitioned device may
+    // have fewer). The waits are bounded either way.
+    if (geo.grid > device_cus()) return TP_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(k, dim3((unsigned)geo.grid), dim3((unsigned)geo.block), (unsigned)geo.lds_bytes,
                        (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;

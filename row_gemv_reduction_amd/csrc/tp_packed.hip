@@ -520,7 +520,7 @@ tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, c
     if (kind == 2) {
         if (p->serial_points) return TP_ERR_UNSUPPORTED;  // the serial order: vector-ALU stream only
         return tp_decode_mfma_stream(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
-                                     slots, hidden, stream);
+                                     slots, hidden, ws, stream);
     }
     StreamGeom geo;
     if (!tp_stream_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;

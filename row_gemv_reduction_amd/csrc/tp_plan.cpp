@@ -73,8 +73,12 @@ static int64_t partial_bytes(const tp_plan_s* p) {
     return round_up(m, 256);
 }
 
-int64_t tp_ws_moe_offset(const tp_plan_s* p) {
+int64_t tp_ws_xchg_offset(const tp_plan_s* p) {
     return tp_ws_partials_offset() + partial_bytes(p);
+}
+
+int64_t tp_ws_moe_offset(const tp_plan_s* p) {
+    return tp_ws_xchg_offset(p) + round_up(tp_xchg_bytes(p), 256);
 }
 
 int64_t tp_workspace_bytes(const tp_plan_s* p) {
@@ -151,6 +155,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "stream_kind")) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->stream_kind = (int32_t)value;
+    } else if (!strcmp(key, "stream_wgs")) {
+        if (value < 0 || value > kTargetCUs) return TP_ERR_INVALID_ARG;
+        p->stream_wgs = (int32_t)value;
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
@@ -188,6 +195,8 @@ tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
     o->moe_inter = p->moe_inter;
     o->max_tokens = p->max_tokens;
     o->packed_kind = tp_packed_kind(p);
+    MfmaGeom mg;
+    o->stream_wgs = o->packed_kind == 2 && tp_mfma_geometry(p, &mg) ? mg.grid : 0;
     return TP_OK;
 }
 

@@ -95,6 +95,27 @@ def test_plan_attn_dim_moe_and_tuning():
     assert Plan(4096, 4096, 4, 1, tune={"splits_attn": 3, "valu_cols": 512}).info()["splits"][0] == 11
 
 
+def test_matrix_core_stream_workgroups():
+    # the matrix-core stream shares each point's tiles among one workgroup per
+    # CU (at most one per 16-column strip, at least one per two strips)
+    assert Plan(5120, 17408, 2, 16).info()["stream_wgs"] == 256
+    assert Plan(1024, 4096, 4, 17).info()["stream_wgs"] == 64
+    assert Plan(5120, 17408, 2, 16, tune={"stream_wgs": 200}).info()["stream_wgs"] == 200
+    assert Plan(5120, 17408, 4, 1).info()["stream_wgs"] == 0  # vector-ALU stream
+    # 320 strips need at least 160 workgroups: b = 4 falls back to the
+    # vector-ALU stream, b = 16 has no streamed step
+    p = Plan(5120, 17408, 2, 4, tune={"stream_kind": 2, "stream_wgs": 100})
+    assert p.info()["packed_kind"] == 0
+    p = Plan(5120, 17408, 2, 4, tune={"stream_wgs": 100})
+    assert p.info()["packed_kind"] == 1 and p.info()["stream_wgs"] == 0
+    assert Plan(5120, 17408, 2, 16, tune={"stream_wgs": 100}).info()["packed_kind"] == 0
+    with pytest.raises(TPError):
+        Plan(5120, 17408, 2, 16, tune={"stream_wgs": 257})
+    # the workspace does not depend on the knob
+    a = Plan(4096, 12288, 8, 64).info()["workspace_bytes"]
+    assert Plan(4096, 12288, 8, 64, tune={"stream_wgs": 200}).info()["workspace_bytes"] == a
+
+
 def test_entry_points_validate_before_launching():
     """Null and misaligned pointers are rejected on the host; nothing is
     enqueued (these addresses are never dereferenced)."""

@@ -471,13 +471,7 @@ PACKED_CASES = [
 ]
 
 
-@pytest.mark.parametrize("n,b,h,ka,ki,rank,kind", PACKED_CASES)
-def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank, kind):
-    L = 3
-    say("packed decode n=%d b=%d h=%d ka=%d ki=%d rank=%d kind=%d" % (n, b, h, ka, ki, rank, kind))
-    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 31, rank)
-    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind})
-    assert plan.info()["packed_kind"] == kind
+def check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0):
     s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
     for l in range(L):
         assert_partial_close(s_gpu[l, 0, rank], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
@@ -488,6 +482,38 @@ def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank, kind):
     rms_p = np.sqrt(np.mean(s_gpu[:, :, rank].astype(np.float64) ** 2))
     err = np.abs(h_gpu.astype(np.float64) - h_or).max()
     assert err <= 2 * L * 1e-5 * rms_p + 4 * np.spacing(np.abs(h_or).max()), err
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,kind", PACKED_CASES)
+def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank, kind):
+    L = 3
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 31, rank)
+    say("packed decode n=%d b=%d h=%d ka=%d ki=%d rank=%d kind=%d" % (n, b, h, ka, ki, rank, kind))
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind})
+    assert plan.info()["packed_kind"] == kind
+    check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
+
+
+SEGMENT_CASES = [
+    # (n, b, hidden, k_attn, inter, rank, workgroups): the matrix-core stream
+    # with fewer workgroups than strips, so that ranges of tiles cut strips
+    # (owner + contributor) and a workgroup owns up to two strips; ragged row
+    # tiles, tokens past b, one rank
+    (2, 16, 5120, 1024, 2048, 1, 0), (4, 33, 1040, 640, 2048, 2, 48), (4, 64, 4096, 4096, 12288, 3, 200),
+    (4, 5, 1024, 1024, 4096, 0, 37), (1, 20, 256, 256, 512, 0, 9), (3, 7, 48, 48, 96, 1, 2),
+    (2, 48, 4112, 256, 512, 1, 0), (4, 17, 1024, 1024, 4096, 2, 33), (2, 16, 1040, 656, 2000, 0, 64),
+]
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,wgs", SEGMENT_CASES)
+def test_mfma_stream_segments_match_oracle(n, b, h, ka, ki, rank, wgs):
+    L = 3  # six points: every exchange buffer of the ring is reused
+    say("MFMA stream segments n=%d b=%d h=%d ka=%d ki=%d rank=%d wgs=%d" % (n, b, h, ka, ki, rank, wgs))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 37, rank)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 2, "stream_wgs": wgs})
+    want = min(wgs or 256, h // 16)
+    assert plan.info()["stream_wgs"] == want
+    check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
 
 
 @pytest.mark.parametrize("b", [2, 16])
@@ -513,7 +539,7 @@ FULL_SIZE = [
     # configuration bench.py times (the automatic stream kind)
     (workloads.PAGE1, None, 0),
     (workloads.page1_n2(8), 2, 1),
-    (workloads.page1_n2(16), 2, 1),
+    (workloads.page1_n2(16), 3, 1),
     (workloads.page1_n2(32), 2, 0),
     (workloads.h4096(8, 64), 2, 5),
     (workloads.h4096(4, 8), 2, 3),
