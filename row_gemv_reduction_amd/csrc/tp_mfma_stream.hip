@@ -180,9 +180,8 @@ template <int BT, int SL, int WPS, int NSTG>
 __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     constexpr int kRed = WPS * BT * 256;                  // floats of one parity
     __shared__ __align__(16) float red[2 * kRed];          // [2][WPS][BT][64][4] D tiles
-    __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, D-tile layout
-    __shared__ __align__(16) float vs[BT * 256];           // a segment's partial, D-tile layout
-    __shared__ __align__(16) float vr[BT * 256];           // the same, [token][16 columns]
+    __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, [token][16]
+    __shared__ __align__(16) float vr[BT * 256];           // a segment's partial, [token][16]
     __shared__ int flags[8];                               // arrivals[2], consumed, staged[2], oth_free
     __shared__ int segtab[2][kMaxSeg][4];
     __shared__ int nseg[2];
@@ -195,8 +194,6 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     const int n_points = 2 * a.layers;
     const int B = a.batch;
     const int len = B * a.H;
-    // lane l of a D tile holds tokens 16tt + 4(l/16) + k (k < 4) of column l % 16
-    const int col = lane & 15, tq = 4 * (lane >> 4);
     // strips whose kb = 0 tile is ours: [own0, own0 + nown)
     const int own0 = (int)(((int64_t)g * a.S16 + a.G - 1) / a.G);
     const int nown = (int)(((int64_t)(g + 1) * a.S16 + a.G - 1) / a.G) - own0;
@@ -209,20 +206,25 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 
     if (wave == 0) {
         // ---------------------------------------------------- control wave
+        // Works in the [token][16 columns] layout: lane l takes token
+        // 16tt + l/4 and columns 4(l%4) .. +3 of a strip (16-byte LDS and
+        // global accesses throughout).
         __builtin_amdgcn_s_setprio(3);
+        const int tl = lane >> 2, c4 = 4 * (lane & 3);
         for (int o = 0; o < nown; ++o)
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
-                floatx4_t h;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int tok = 16 * tt + tq + k;
-                    h[k] = tok < B ? a.hidden[(int64_t)tok * a.H + 16 * (own0 + o) + col] : 0.f;
-                }
-                *reinterpret_cast<floatx4_t*>(hs + ((o * BT + tt) * 64 + lane) * 4) = h;
+                const int tok = 16 * tt + tl;
+                floatx4_t h = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                if (tok < B)
+                    h = *reinterpret_cast<const floatx4_t*>(a.hidden + (int64_t)tok * a.H + 16 * (own0 + o) + c4);
+                *reinterpret_cast<floatx4_t*>(hs + (o * BT + tt) * 256 + lane * 4) = h;
             }
         const uint32_t xbytes = (uint32_t)((int64_t)2 * kXchgRing * a.S16 * BT * 1024);
         const __amdgpu_buffer_rsrc_t rx = dev_rsrc(a.xpart, xbytes);
+        const int N = a.n_ranks;
+        const int bs = B * 16;                 // LDS floats per other rank
+        const bool quad_chunks = a.chunk % 4 == 0;  // a lane's four columns lie in one chunk
         int ok = 1;
         __syncthreads();  // start: segment tables, flags and hidden columns are in LDS
         int e = 0;
@@ -234,7 +236,9 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 const int s = segtab[t][i][0], role = segtab[t][i][3];
                 wait_flag(&flags[e & 1], (e / 2 + 1) * WPS, a.err);
                 lds_wait();
-                // the segment's partial: the waves' D tiles summed in wave order
+                // the segment's partial: the waves' D tiles summed in wave order,
+                // stored to vr as [token][16 columns] (lane l of a D tile holds
+                // tokens 16tt + 4(l/16) + k of column l % 16)
                 const float* re = red + (e & 1) * kRed;
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt) {
@@ -245,7 +249,8 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     floatx4_t v = part[0];
 #pragma unroll
                     for (int wi = 1; wi < WPS; ++wi) v = v + part[wi];
-                    *reinterpret_cast<floatx4_t*>(vs + (tt * 64 + lane) * 4) = v;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) vr[(16 * tt + 4 * (lane >> 4) + k) * 16 + (lane & 15)] = v[k];
                 }
                 lds_wait();
                 if (lane == 0) lds_st(&flags[2], e + 1);  // red[e & 1] may be rewritten (segment e + 2)
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 #pragma unroll
                     for (int tt = 0; tt < BT; ++tt)
                         st_dev4(rx, xoff + (uint32_t)((tt * 64 + lane) * 16),
-                                *reinterpret_cast<const floatx4_t*>(vs + (tt * 64 + lane) * 4));
+                                *reinterpret_cast<const floatx4_t*>(vr + tt * 256 + lane * 4));
                     wait_mem();
                     if (lane == 0) st_dev_u32(pub, (uint32_t)(j + 1));
                     continue;
@@ -281,60 +286,76 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     if (lane == 0) st_dev_u32(ack, (uint32_t)(j + 1));
 #pragma unroll
                     for (int tt = 0; tt < BT; ++tt) {
-                        float* vp = vs + (tt * 64 + lane) * 4;
+                        float* vp = vr + tt * 256 + lane * 4;
                         *reinterpret_cast<floatx4_t*>(vp) = *reinterpret_cast<const floatx4_t*>(vp) + c[tt];
                     }
                 }
-                // ring order: chunk c starts at rank c, then c+1, ... (mod N); then the residual
                 if (!staged) {
                     wait_flag(&flags[3 + t], NSTG * (jj + 1), a.err);  // point j's other values are in LDS
                     lds_wait();
                     staged = true;
                 }
+                // Ring order: chunk c starts at rank c, then c+1, ... (mod N); then
+                // the residual. Along that order the other ranks come as a rotation
+                // of their rows 0 .. N-2 (row q = rank q, or q+1 past our rank)
+                // starting at row c (c - 1 past our rank; row 0 if that is N - 1),
+                // and our own value sits at position (rank - c) mod N.
                 const int o = s - own0;
                 const float* oj = oth + ((j & 1) * a.own_max + o) * a.oth_strip;
                 float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
                 float* hso = hs + o * BT * 256;
 #pragma unroll 1
                 for (int tt = 0; tt < BT; ++tt) {
-                    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(vs + (tt * 64 + lane) * 4);
-                    const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hso + (tt * 64 + lane) * 4);
-                    floatx4_t hn;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
 #pragma clang fp contract(off)
-                        const int tok = 16 * tt + tq + k;
-                        const int tokc = tok < B ? tok : B - 1;
-                        const int idx = tokc * a.H + 16 * s + col;
-                        const int cidx = idx / a.chunk;
-                        float ov[8];
+                    const int tok = 16 * tt + tl;
+                    const int tokc = tok < B ? tok : B - 1;
+                    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(vr + tt * 256 + lane * 4);
+                    const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hso + tt * 256 + lane * 4);
+                    const float* ob = oj + tokc * 16 + c4;
+                    const int idx = tokc * a.H + 16 * s + c4;
+                    floatx4_t sum;
+                    if (quad_chunks) {
+                        const int cc = idx / a.chunk;
+                        int p = a.rank - cc;
+                        p = p < 0 ? p + N : p;
+                        int q = cc > a.rank ? cc - 1 : cc;
+                        q = q == N - 1 ? 0 : q;
+                        sum = v;
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
-                            const int uu = u < a.n_ranks ? u : a.n_ranks - 1;
-                            int r = cidx + uu;
-                            r = r >= a.n_ranks ? r - a.n_ranks : r;
-                            int ro = r < a.rank ? r : r - 1;
-                            ro = ro < 0 ? 0 : ro;
-                            const float ovv = oj[(ro * B + tokc) * 16 + col];
-                            ov[u] = r == a.rank ? v[k] : ovv;
-                        }
-                        float sum = ov[0];
+                            if (u >= N) break;
+                            const floatx4_t x = *reinterpret_cast<const floatx4_t*>(ob + q * bs);
+                            const bool own = u == p;
+                            floatx4_t y;
 #pragma unroll
-                        for (int u = 1; u < 8; ++u)
-                            if (u < a.n_ranks) sum = sum + ov[u];
-                        hn[k] = tok < B ? sum + h[k] : 0.f;
-                        vr[(16 * tt + tq + k) * 16 + col] = v[k];
+                            for (int k = 0; k < 4; ++k) y[k] = own ? v[k] : x[k];
+                            if (u > 0) sum = sum + y;
+                            else sum = y;
+                            if (!own) q = q + 1 == N - 1 ? 0 : q + 1;
+                        }
+                    } else {
+                        // a chunk boundary may fall between a lane's columns
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int cc = (idx + k) / a.chunk;
+                            int p = a.rank - cc;
+                            p = p < 0 ? p + N : p;
+                            int q = cc > a.rank ? cc - 1 : cc;
+                            q = q == N - 1 ? 0 : q;
+                            float sk = v[k];
+                            for (int u = 0; u < N; ++u) {
+                                const bool own = u == p;
+                                const float y = own ? v[k] : ob[q * bs + k];
+                                sk = u > 0 ? sk + y : y;
+                                if (!own) q = q + 1 == N - 1 ? 0 : q + 1;
+                            }
+                            sum[k] = sk;
+                        }
                     }
-                    *reinterpret_cast<floatx4_t*>(hso + (tt * 64 + lane) * 4) = hn;
-                }
-                // the rank's partial to its slot, four columns of one token per lane
-                lds_wait();
-#pragma unroll 1
-                for (int tt = 0; tt < BT; ++tt) {
-                    const int tok = 16 * tt + (lane >> 2), c4 = 4 * (lane & 3);
-                    if (tok < B)
-                        *reinterpret_cast<floatx4_t*>(slot + (int64_t)tok * a.H + 16 * s + c4) =
-                            *reinterpret_cast<const floatx4_t*>(vr + tok * 16 + c4);
+                    if (tok < B) {
+                        *reinterpret_cast<floatx4_t*>(hso + tt * 256 + lane * 4) = sum + h;
+                        *reinterpret_cast<floatx4_t*>(slot + (int64_t)tok * a.H + 16 * s + c4) = v;
+                    }
                 }
             }
             // the other values of point j have been read: their buffer may be refilled (point j + 2)
@@ -345,12 +366,10 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
         for (int o = 0; o < nown; ++o)
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
-                const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hs + ((o * BT + tt) * 64 + lane) * 4);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int tok = 16 * tt + tq + k;
-                    if (tok < B) a.hidden[(int64_t)tok * a.H + 16 * (own0 + o) + col] = h[k];
-                }
+                const int tok = 16 * tt + tl;
+                if (tok < B)
+                    *reinterpret_cast<floatx4_t*>(a.hidden + (int64_t)tok * a.H + 16 * (own0 + o) + c4) =
+                        *reinterpret_cast<const floatx4_t*>(hs + (o * BT + tt) * 256 + lane * 4);
             }
         wait_mem();
     } else if (wave <= NSTG) {
@@ -573,7 +592,7 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     g->oth_strip = (int32_t)(((p->n_ranks > 1 ? p->n_ranks - 1 : 1) * b * 16 + 255) / 256 * 256);
     g->own_max = own_max;
     g->lds_bytes = 2 * own_max * g->oth_strip * 4;
-    const int64_t stat = (2 * wps * bt * 256 + kMaxOwn * bt * 256 + 2 * bt * 256) * 4 + 1024;
+    const int64_t stat = (2 * wps * bt * 256 + kMaxOwn * bt * 256 + bt * 256) * 4 + 1024;
     if (g->lds_bytes + stat > 152 * 1024) return false;
     // the largest buffer offsets must fit 32 bits
     if ((int64_t)b * (k0 > k1 ? k0 : k1) * 2 >= ((int64_t)1 << 31)) return false;

@@ -502,6 +502,8 @@ SEGMENT_CASES = [
     (2, 16, 5120, 1024, 2048, 1, 0), (4, 33, 1040, 640, 2048, 2, 48), (4, 64, 4096, 4096, 12288, 3, 200),
     (4, 5, 1024, 1024, 4096, 0, 37), (1, 20, 256, 256, 512, 0, 9), (3, 7, 48, 48, 96, 1, 2),
     (2, 48, 4112, 256, 512, 1, 0), (4, 17, 1024, 1024, 4096, 2, 33), (2, 16, 1040, 656, 2000, 0, 64),
+    # ring chunks of b*H/N = 42 and 130 elements: boundaries inside a lane's four columns
+    (8, 7, 48, 512, 1024, 3, 2), (8, 13, 80, 512, 1024, 6, 3),
 ]
 
 
