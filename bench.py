@@ -178,8 +178,16 @@ def dense_run(args, w, tune):
         tp.tp_pack_weights(plan, 1, wd, pd)
         torch.cuda.synchronize()
 
+        pa = torch.empty(tp.packed_act_shape(plan, 0, w.layers), dtype=torch.bfloat16, device="cuda")
+        pf = torch.empty(tp.packed_act_shape(plan, 1, w.layers), dtype=torch.bfloat16, device="cuda")
+
         def step():
-            tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
+            # the activations' layout for the stream is part of the step
+            if info["packed_kind"] == 2:
+                tp.tp_pack_activations(plan, xa, xf, pa, pf)
+                tp.tp_decode_layers_packed(plan, w.layers, args.rank, pa, po, pf, pd, slots, hidden, ws)
+            else:
+                tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
         name = "decode_stream" if info["packed_kind"] == 1 else (
             "decode_stream_mfma (%d workgroups sharing the tiles)" % info["stream_wgs"])
         kernel = "%s (one launch per step, %d reconciliation points)" % (name, 2 * w.layers)

@@ -214,48 +214,79 @@ tp_status tp_decode_layers(tp_plan_t plan, int32_t n_layers, int32_t rank,
                            float* slots, float* hidden, void* workspace, void* stream);
 
 /*
- * Pair-strip packed weights for the streamed decode step. A rank's weight
- * slice W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is
- * stored as
+ * Packed weights for the streamed decode step. A rank's weight slice
+ * W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is stored
+ * once, when the weights are loaded (not part of the decode step), in the
+ * layout of the plan's packed_kind (tp_plan_info):
+ *  1, pair strips (vector-ALU stream):
  *     P[s][kp][c][q] = W_r[2kp + q][4s + c]
  *     s < H/4, kp < ceil(K_r/2), c < 4, q < 2   (rows past K_r are zero)
- * i.e. H/4 strips of 4 columns; each 16-byte vector holds rows 2kp and
- * 2kp+1 of its strip as one bf16 pair per column, and a strip's rows are
- * contiguous. Same bytes as the row-major slice (plus one zero row when
- * K_r is odd). Packing is done once, when the weights are loaded; it is not
- * part of the decode step.
- *
- * tp_pack_weights: w bf16 [n_layers][K_r][hidden] -> w_packed bf16
- * [n_layers][hidden/4][ceil(K_r/2)][8] for `point`. w and w_packed must not
- * overlap. TP_ERR_UNSUPPORTED if hidden is not a multiple of 4.
+ *     H/4 strips of 4 columns; each 16-byte vector holds rows 2kp and 2kp+1
+ *     of its strip as one bf16 pair per column; a strip's rows are
+ *     contiguous. w_packed bf16 [n_layers][H/4][ceil(K_r/2)][8].
+ *  2, MFMA tiles (matrix-core stream, v_mfma_f32_16x16x32_bf16 B operands):
+ *     T[s][kb][h][l][i] = W_r[64kb + 16(l/16) + 8h + i][16s + l%16]
+ *     s < H/16, kb < ceil(K_r/64), h < 2, lane l < 64, i < 8 (rows past
+ *     K_r are zero): 2 KB tiles of 64 rows x 16 columns.
+ *     w_packed bf16 [n_layers][H/16][ceil(K_r/64)][2][64][8].
+ * tp_pack_weights: w bf16 [n_layers][K_r][hidden] -> w_packed for `point`.
+ * w and w_packed must not overlap. TP_ERR_UNSUPPORTED if packed_kind is 0.
  */
 tp_status tp_pack_weights(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w,
                           void* w_packed, void* stream);
 
 /*
- * The decode step of tp_decode_layers on pair-strip packed weights: same
- * arguments and results (the projections within their fp tolerance, the
- * ring stage the same binary32 additions in the same order). One launch
- * per step: each workgroup owns a set of 4-column strips for every point,
- * streams their weights over all of K_r, and keeps its columns of the
- * hidden state on chip between points; per point it writes the rank's
- * partial into its slot and sets hidden <- ring_sum(slot) + hidden for its
- * columns (lesson 9.9, Conceito).
+ * The activation slices of a step in the order tp_decode_layers_packed
+ * reads them (part of the decode step: call it once per step).
+ *  packed_kind 1: row-major, as given (the bytes are copied).
+ *  packed_kind 2: A-operand order of the matrix-core stream,
+ *     X[kb][tt][h][l][i] = x[16tt + l%16][64kb + 16(l/16) + 8h + i]
+ *     kb < ceil(K_r/64), tt < ceil(b/16), h < 2, lane l < 64, i < 8 (zero
+ *     for rows past K_r; entries of tokens past b are left unwritten and
+ *     never read): each 16-byte-per-lane load of the step then reads 1 KB
+ *     (b >= 16) of contiguous memory.
+ *     x*_packed bf16 [n_layers][ceil(K_r/64)][ceil(b/16)][2][64][8].
+ * x_attn bf16 [n_layers][batch][k_attn/N], x_ffn bf16 [n_layers][batch][inter/N]
+ * in; xa_packed, xf_packed out (distinct from each other and the inputs).
+ * TP_ERR_UNSUPPORTED if packed_kind is 0.
+ */
+tp_status tp_pack_activations(tp_plan_t plan, int32_t n_layers, const void* x_attn, const void* x_ffn,
+                              void* xa_packed, void* xf_packed, void* stream);
+
+/*
+ * The decode step of tp_decode_layers on packed weights and activations
+ * (tp_pack_weights, tp_pack_activations): same results (the projections
+ * within their fp tolerance, the ring stage the same binary32 additions in
+ * the same order). One launch per step; per point it writes the rank's
+ * partial into its slot and sets hidden <- ring_sum(slot) + hidden
+ * (lesson 9.9, Conceito), keeping its columns of the hidden state on chip
+ * between points.
+ *  packed_kind 1: each workgroup owns a set of 4-column strips for every
+ *     point and streams their weights over all of K_r.
+ *  packed_kind 2: each point's 64-row tiles, in strip-major order, are cut
+ *     into equal contiguous ranges, one per workgroup (one per CU; info
+ *     stream_wgs); a 16-column strip cut between two workgroups is summed
+ *     by the one holding its first rows, its own rows first, then the other
+ *     workgroup's partial (handed over through the workspace). The result
+ *     is deterministic for a given stream_wgs. Needs that many compute
+ *     units on the device (TP_ERR_UNSUPPORTED otherwise).
  *
  * Point order. Every element of the hidden state is updated point after
  * point, each update reading the previous one; since each point's
  * activation slice is an input, no point has to wait for other columns.
- * With the plan knob "serial_points" = 1 the step also emulates a model in
- * which a point's activation depends on the whole previous hidden state:
- * point j+1's activation is read only after every column of point j is
- * complete (a grid-wide wait per point; cooperative launch). Both orders
- * give the same bits. In the serial order the workspace's error word
+ * With the plan knob "serial_points" = 1 (packed_kind 1 only) the step also
+ * emulates a model in which a point's activation depends on the whole
+ * previous hidden state: point j+1's activation is read only after every
+ * column of point j is complete (a grid-wide wait per point; cooperative
+ * launch). Both orders give the same bits. The workspace's error word
  * (tp_workspace_status) reports a wait that timed out.
  *
- * TP_ERR_UNSUPPORTED unless batch <= 8, n_ranks <= 8, K_r is even for both
- * points, batch * K_r is a multiple of 8, the activation slices of a point
- * fit the on-chip buffers (2 * batch * K_r bytes per point kind, about
- * 150 KiB in all) and 16 * batch * ceil(hidden / 1024) <= 192.
+ * TP_ERR_UNSUPPORTED if packed_kind is 0 (packed_kind 1 needs batch <= 8,
+ * n_ranks <= 8, K_r even for both points, batch * K_r a multiple of 8, the
+ * activation slices of a point within about 150 KiB of on-chip buffers and
+ * 16 * batch * ceil(hidden / 1024) <= 192; packed_kind 2 needs batch <= 64,
+ * n_ranks <= 8, hidden a multiple of 16, K_r a multiple of 8 and
+ * hidden/16 <= 2 * stream_wgs), or with "serial_points" = 1 on packed_kind 2.
  */
 tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank,
                                   const void* x_attn, const void* w_o_packed,

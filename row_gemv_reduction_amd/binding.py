@@ -67,6 +67,7 @@ EXPORTS = {
                          + [ctypes.c_void_p] * 8),
     "tp_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "tp_pack_activations": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 5),
     "tp_decode_layers_packed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
                                 + [ctypes.c_void_p] * 8),
     "tp_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
@@ -250,8 +251,36 @@ def packed_shape(plan: Plan, point, n_layers):
     raise TPError(TP_ERR_UNSUPPORTED, "packed_shape")
 
 
+def packed_act_shape(plan: Plan, point, n_layers):
+    """Shape of a step's activation slices as tp_decode_layers_packed reads them:
+    row-major [L, b, K_r] (pair strips) or A-operand order
+    [L, ceil(K_r/64), ceil(b/16), 2, 64, 8] (MFMA tiles)."""
+    if point not in (0, 1):
+        raise ValueError("point must be 0 or 1")
+    i = plan.info()
+    kr, b = i["k_rank"][point], i["batch"]
+    if i["packed_kind"] == 1:
+        return (n_layers, b, kr)
+    if i["packed_kind"] == 2:
+        return (n_layers, (kr + 63) // 64, (b + 15) // 16, 2, 64, 8)
+    raise TPError(TP_ERR_UNSUPPORTED, "packed_act_shape")
+
+
+def tp_pack_activations(plan: Plan, x_attn, x_ffn, xa_packed, xf_packed):
+    """Lay a step's activation slices [L, b, K_r] out as packed_act_shape() (tp_pack_activations)."""
+    i = plan.info()
+    b = i["batch"]
+    ka, ki = i["k_rank"]
+    L = x_attn.shape[0]
+    _check(_lib().tp_pack_activations(plan.handle, L, _dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
+                                      _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
+                                      _dev(xa_packed, "xa_packed", torch.bfloat16, packed_act_shape(plan, 0, L)),
+                                      _dev(xf_packed, "xf_packed", torch.bfloat16, packed_act_shape(plan, 1, L)),
+                                      _stream()), "tp_pack_activations")
+
+
 def tp_pack_weights(plan: Plan, point, w, w_packed):
-    """Pair-strip pack a stack of row-major weight slices [L, K_r, H] -> packed_shape()."""
+    """Pack a stack of row-major weight slices [L, K_r, H] -> packed_shape()."""
     shape = packed_shape(plan, point, w.shape[0])
     L, kr, H = shape[0], plan.info()["k_rank"][point], plan.info()["hidden"]
     _check(_lib().tp_pack_weights(plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, kr, H)),
@@ -261,13 +290,14 @@ def tp_pack_weights(plan: Plan, point, w, w_packed):
 
 def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
                             slots, hidden, workspace):
+    """The streamed decode step; x_attn / x_ffn as tp_pack_activations lays them out."""
     i = plan.info()
     n, b, H = i["n_ranks"], i["batch"], i["hidden"]
     ka, ki = i["k_rank"]
     L = n_layers
-    args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
             _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
-            _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
             _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
             _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
             _dev(hidden, "hidden", torch.float32, (b, H)),

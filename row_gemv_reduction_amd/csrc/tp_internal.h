@@ -118,6 +118,8 @@ int64_t tp_xchg_bytes(const tp_plan_s* p);  // exchange buffers of the MFMA stre
 int64_t tp_ws_xchg_offset(const tp_plan_s* p);
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);
+tp_status tp_pack_acts(const tp_plan_s* p, int n_layers, const void* x_attn, const void* x_ffn,
+                       void* xa_packed, void* xf_packed, void* stream);
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,
                                 const void* x_attn, const void* w_o_tiles, const void* x_ffn,
                                 const void* w_down_tiles, float* slots, float* hidden, void* ws,

@@ -87,9 +87,40 @@ __global__ void pack_tiles_kernel(const uint16_t* __restrict__ w, uint16_t* __re
     }
 }
 
+// Activations in A-operand order, so that every 16-byte-per-lane load of
+// the step reads 1 KB of contiguous memory (row-major x would give each
+// load 16 tokens x 64 bytes, half of 16 different cache lines):
+//     X[l][kb][tt][h][lane][i] = x[l][16tt + lane%16][64kb + 16(lane/16) + 8h + i]
+// (zero for rows past K; entries of tokens past b are not written: the
+// step never reads them).
+__global__ void pack_acts_kernel(const uint16_t* __restrict__ x0, const uint16_t* __restrict__ x1,
+                                 uint16_t* __restrict__ p0, uint16_t* __restrict__ p1, int64_t layers,
+                                 int64_t B, int64_t K0, int64_t K1, int64_t bt) {
+    const int64_t nkb0 = (K0 + kTileRows - 1) / kTileRows, nkb1 = (K1 + kTileRows - 1) / kTileRows;
+    const int64_t per0 = nkb0 * bt * 128, per1 = nkb1 * bt * 128;  // 16-byte vectors per layer
+    const int64_t total = layers * (per0 + per1);
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const bool second = v >= layers * per0;
+        const int64_t w = second ? v - layers * per0 : v;
+        const int64_t per = second ? per1 : per0, K = second ? K1 : K0;
+        const int64_t l = w / per;
+        int64_t rem = w - l * per;
+        const int64_t kb = rem / (bt * 128);
+        rem -= kb * bt * 128;
+        const int64_t tt = rem / 128, h = (rem / 64) % 2, lane = rem % 64;
+        const int64_t tok = 16 * tt + lane % 16, k0 = kTileRows * kb + 16 * (lane / 16) + 8 * h;
+        if (tok >= B) continue;
+        u32x4_t out = u32x4_t{0u, 0u, 0u, 0u};
+        if (k0 < K)  // K is a multiple of 8: the 8 rows are all inside or all past
+            out = *reinterpret_cast<const u32x4_t*>((second ? x1 : x0) + (l * B + tok) * K + k0);
+        *reinterpret_cast<u32x4_t*>((second ? p1 : p0) + w * 8) = out;
+    }
+}
+
 struct MfmaArgs {
-    const uint16_t* x0;     // x_attn [L][B][K0]
-    const uint16_t* x1;     // x_ffn  [L][B][K1]
+    const uint16_t* x0;     // x_attn in A-operand order [L][nkb0][BT][2][64][8]
+    const uint16_t* x1;     // x_ffn  in A-operand order [L][nkb1][BT][2][64][8]
     const uint16_t* w0;     // tiles of w_o    [L][H/16][nkb0][2][64][8]
     const uint16_t* w1;     // tiles of w_down [L][H/16][nkb1][2][64][8]
     float* slots;           // [L][2][N][B][H]
@@ -170,19 +201,22 @@ __device__ __forceinline__ void wait_flag(const int* f, int target, uint32_t* er
 }
 
 // The waves of a workgroup meet through LDS flags, not barriers: a compute
-// wave stores its D tiles of segment e, counts itself in arrivals[e & 1] and
-// goes on streaming; the control wave starts on segment e once all WPS waves
-// have counted, and publishes `consumed` = e + 1 once it has read their
-// tiles, which frees that parity's buffer for segment e + 2. So no wave ever
-// waits for the slowest of its siblings, only (rarely) for the control wave
-// to fall two segments behind.
-template <int BT, int SL, int WPS, int NSTG>
+// wave stores its D tiles of segment e into buffer e % NBUF, counts itself
+// in that buffer's arrivals and goes on streaming; the control wave starts
+// on segment e once all WPS waves have counted, and publishes `consumed` =
+// e + 1 once it has read their tiles, which frees the buffer for segment
+// e + NBUF. So a wave waits for its slowest sibling only when it is NBUF
+// segments ahead of it.
+constexpr int kFlagArrived = 0, kFlagConsumed = 4, kFlagStaged = 5, kFlagOthFree = 7, kFlagCount = 8;
+template <int BT, int SL, int WPS, int NSTG, int NBUF>
 __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
-    constexpr int kRed = WPS * BT * 256;                  // floats of one parity
-    __shared__ __align__(16) float red[2 * kRed];          // [2][WPS][BT][64][4] D tiles
+    constexpr int kRed = WPS * BT * 256;                  // floats of one buffer
+    __shared__ __align__(16) float red[NBUF * kRed];       // [NBUF][WPS][BT][64][4] D tiles
     __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, [token][16]
     __shared__ __align__(16) float vr[BT * 256];           // a segment's partial, [token][16]
-    __shared__ int flags[8];                               // arrivals[2], consumed, staged[2], oth_free
+    // LDS flags: arrivals per D-tile buffer, segments consumed, stagers done
+    // per parity of point, points whose other values have been read
+    __shared__ int flags[kFlagCount];
     __shared__ int segtab[2][kMaxSeg][4];
     __shared__ int nseg[2];
     __shared__ int s_last;
@@ -201,7 +235,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     if (tid == 0) {
         nseg[0] = wg_segments(g, a.G, a.S16, a.nkb0, segtab[0]);
         nseg[1] = wg_segments(g, a.G, a.S16, a.nkb1, segtab[1]);
-        for (int f = 0; f < 8; ++f) flags[f] = 0;
+        for (int f = 0; f < kFlagCount; ++f) flags[f] = 0;
     }
 
     if (wave == 0) {
@@ -234,12 +268,12 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             bool staged = false;
             for (int i = 0; i < ns; ++i, ++e) {
                 const int s = segtab[t][i][0], role = segtab[t][i][3];
-                wait_flag(&flags[e & 1], (e / 2 + 1) * WPS, a.err);
+                wait_flag(&flags[kFlagArrived + e % NBUF], (e / NBUF + 1) * WPS, a.err);
                 lds_wait();
                 // the segment's partial: the waves' D tiles summed in wave order,
                 // stored to vr as [token][16 columns] (lane l of a D tile holds
                 // tokens 16tt + 4(l/16) + k of column l % 16)
-                const float* re = red + (e & 1) * kRed;
+                const float* re = red + (e % NBUF) * kRed;
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt) {
                     floatx4_t part[WPS];
@@ -253,7 +287,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     for (int k = 0; k < 4; ++k) vr[(16 * tt + 4 * (lane >> 4) + k) * 16 + (lane & 15)] = v[k];
                 }
                 lds_wait();
-                if (lane == 0) lds_st(&flags[2], e + 1);  // red[e & 1] may be rewritten (segment e + 2)
+                if (lane == 0) lds_st(&flags[kFlagConsumed], e + 1);  // its D-tile buffer is free again
                 // exchange buffer of this kind of point and strip: slot (j/2) mod R,
                 // last used at point j - 2R
                 const int jj = j >> 1;
@@ -291,7 +325,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     }
                 }
                 if (!staged) {
-                    wait_flag(&flags[3 + t], NSTG * (jj + 1), a.err);  // point j's other values are in LDS
+                    wait_flag(&flags[kFlagStaged + t], NSTG * (jj + 1), a.err);  // point j's other values are in LDS
                     lds_wait();
                     staged = true;
                 }
@@ -360,7 +394,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             }
             // the other values of point j have been read: their buffer may be refilled (point j + 2)
             lds_wait();
-            if (lane == 0) lds_st(&flags[5], j + 1);
+            if (lane == 0) lds_st(&flags[kFlagOthFree], j + 1);
         }
         lds_wait();
         for (int o = 0; o < nown; ++o)
@@ -384,7 +418,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
         const int per_strip = (rows + 15) / 16;
         for (int j = 0; j < n_points; ++j) {
             // oth[j & 1] was last read at point j - 2
-            wait_flag(&flags[5], j - 1, a.err);
+            wait_flag(&flags[kFlagOthFree], j - 1, a.err);
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
             for (int n = q; n < nown * per_strip; n += NSTG) {
                 const int o = n / per_strip, r0 = (n - o * per_strip) * 16;
@@ -397,7 +431,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void_t*)dst, 16, 0, 0);
             }
             wait_mem();
-            if (lane == 0) lds_add(&flags[3 + (j & 1)], 1);
+            if (lane == 0) lds_add(&flags[kFlagStaged + (j & 1)], 1);
         }
     } else {
         // --------------------------------------------------- compute waves
@@ -426,21 +460,23 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 set_seg(c);
             }
         };
-        // A operand of lane l: token 16*tt + l%16, rows 16*(l/16) + 8h .. +7 of the tile
-        const int xo = lane & 15, xk = 16 * (lane >> 4);
+        // A operand of lane l: token 16*tt + l%16, rows 16*(l/16) + 8h .. +7 of
+        // the tile, 16 contiguous bytes of the packed activations
         auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& c) {
             const int t = c.j & 1, l = c.j >> 1;
             const bool live = c.j < n_points;
-            const int K = t ? a.K1 : a.K0, nkb = t ? a.nkb1 : a.nkb0;
+            const int nkb = t ? a.nkb1 : a.nkb0;
             const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
-            const uint16_t* xb = (t ? a.x1 : a.x0) + (int64_t)l * B * K;
+            const uint16_t* xb = (t ? a.x1 : a.x0) + (int64_t)l * nkb * BT * 1024;
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
                 kBufferRsrcWord3);
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(live ? xb : a.x0), (short)0, live ? B * K * 2 : 0,
+                const_cast<uint16_t*>(live ? xb : a.x0), (short)0, live ? nkb * BT * 2048 : 0,
                 kBufferRsrcWord3);
-            // slots past the segment's tiles read zero (tile nkb is past the strip)
+            // slots past the segment's tiles read zero (tile nkb is past the
+            // strip), and so do the lanes of tokens past b (an offset past the
+            // range: their packed entries are never read)
             const int span = c.bpw * WPS;
 #pragma unroll
             for (int i = 0; i < SL; ++i) {
@@ -457,7 +493,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
                         xv[i][h][tt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                       xr, ((16 * tt + xo) * K + kTileRows * kb + xk + 8 * h) * 2,
+                                                                       xr, 16 * tt + (lane & 15) < B ? ((kb * BT + tt) * 2 + h) * 1024 + lane * 16 : 0x7ffffff0,
                                                                        0, 0));
             }
         };
@@ -477,16 +513,16 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
         };
         int e = 0;
         auto seg_end = [&]() {
-            // red[e & 1] is free once the control wave has read segment e - 2
-            wait_flag(&flags[2], e - 1, a.err);
-            float* re = red + (e & 1) * kRed + wi * BT * 256;
+            // D-tile buffer e % NBUF is free once the control wave has read segment e - NBUF
+            wait_flag(&flags[kFlagConsumed], e - (NBUF - 1), a.err);
+            float* re = red + (e % NBUF) * kRed + wi * BT * 256;
 #pragma unroll
             for (int tt = 0; tt < BT; ++tt) {
                 *reinterpret_cast<floatx4_t*>(re + (tt * 64 + lane) * 4) = acc[tt];
                 acc[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }
             lds_wait();
-            if (lane == 0) lds_add(&flags[e & 1], 1);
+            if (lane == 0) lds_add(&flags[kFlagArrived + e % NBUF], 1);
             ++e;
         };
 
@@ -540,15 +576,17 @@ typedef void (*mfma_stream_fn)(MfmaArgs);
 // Tiles per bank: fewer for more token blocks (each tile also carries 2*BT
 // A operands), so the banks fit the registers. Compute waves: 13, or 7 for
 // three and four token blocks (the LDS of their D tiles); stager waves: 2,
-// or 4 for the (N-1) * b rows of more tokens.
+// or 4 for the (N-1) * b rows of more tokens; D-tile buffers: 4, or fewer where
+// the LDS is short.
 constexpr int kWps[5] = {0, 13, 13, 7, 7};
 constexpr int kStagers[5] = {0, 2, 2, 4, 4};
+constexpr int kDBufs[5] = {0, 4, 3, 2, 2};  // D-tile buffers (LDS)
 mfma_stream_fn mfma_stream_kernel(int bt) {
     switch (bt) {
-        case 1: return decode_stream_mfma<1, 2, kWps[1], kStagers[1]>;
-        case 2: return decode_stream_mfma<2, 2, kWps[2], kStagers[2]>;
-        case 3: return decode_stream_mfma<3, 1, kWps[3], kStagers[3]>;
-        case 4: return decode_stream_mfma<4, 1, kWps[4], kStagers[4]>;
+        case 1: return decode_stream_mfma<1, 2, kWps[1], kStagers[1], kDBufs[1]>;
+        case 2: return decode_stream_mfma<2, 2, kWps[2], kStagers[2], kDBufs[2]>;
+        case 3: return decode_stream_mfma<3, 1, kWps[3], kStagers[3], kDBufs[3]>;
+        case 4: return decode_stream_mfma<4, 1, kWps[4], kStagers[4], kDBufs[4]>;
     }
     return nullptr;
 }
@@ -592,11 +630,10 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     g->oth_strip = (int32_t)(((p->n_ranks > 1 ? p->n_ranks - 1 : 1) * b * 16 + 255) / 256 * 256);
     g->own_max = own_max;
     g->lds_bytes = 2 * own_max * g->oth_strip * 4;
-    const int64_t stat = (2 * wps * bt * 256 + kMaxOwn * bt * 256 + bt * 256) * 4 + 1024;
+    const int64_t stat = (kDBufs[bt] * wps * bt * 256 + kMaxOwn * bt * 256 + bt * 256) * 4 + 1024;
     if (g->lds_bytes + stat > 152 * 1024) return false;
     // the largest buffer offsets must fit 32 bits
-    if ((int64_t)b * (k0 > k1 ? k0 : k1) * 2 >= ((int64_t)1 << 31)) return false;
-    if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes >= ((int64_t)1 << 31)) return false;
+    if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes * bt >= ((int64_t)1 << 31)) return false;
     if ((int64_t)b * p->hidden >= ((int64_t)1 << 31)) return false;
     g->grid = (int32_t)G;
     g->wps = wps;
@@ -612,6 +649,20 @@ int64_t tp_xchg_bytes(const tp_plan_s* p) {
     const int64_t S16 = p->hidden / 16;
     if (S16 > kXchgMaxStrips) return 0;
     return 2 * kXchgRing * S16 * ((p->batch + 15) / 16) * 1024;
+}
+
+tp_status tp_pack_acts(const tp_plan_s* p, int n_layers, const void* x_attn, const void* x_ffn,
+                       void* xa_packed, void* xf_packed, void* stream) {
+    const int64_t K0 = p->k_attn / p->n_ranks, K1 = p->inter / p->n_ranks;
+    const int64_t bt = (p->batch + 15) / 16;
+    const int64_t total = (int64_t)n_layers * ((K0 + kTileRows - 1) / kTileRows + (K1 + kTileRows - 1) / kTileRows) * bt * 128;
+    if (total == 0) return TP_OK;
+    const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+    hipLaunchKernelGGL(pack_acts_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint16_t*>(x_attn), static_cast<const uint16_t*>(x_ffn),
+                       static_cast<uint16_t*>(xa_packed), static_cast<uint16_t*>(xf_packed),
+                       (int64_t)n_layers, (int64_t)p->batch, K0, K1, bt);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,

@@ -505,6 +505,25 @@ tp_status tp_pack_weights(tp_plan_t p, int32_t point, int32_t n_layers, const vo
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
+tp_status tp_pack_activations(tp_plan_t p, int32_t n_layers, const void* x_attn, const void* x_ffn,
+                              void* xa_packed, void* xf_packed, void* stream) {
+    if (!p || !x_attn || !x_ffn || !xa_packed || !xf_packed || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x_attn) || !aligned16(x_ffn) || !aligned16(xa_packed) || !aligned16(xf_packed))
+        return TP_ERR_ALIGNMENT;
+    if (x_attn == xa_packed || x_ffn == xf_packed || xa_packed == xf_packed) return TP_ERR_INVALID_ARG;
+    const int kind = tp_packed_kind(p);
+    if (kind == 0) return TP_ERR_UNSUPPORTED;
+    if (kind == 2) return tp_pack_acts(p, n_layers, x_attn, x_ffn, xa_packed, xf_packed, stream);
+    // the vector-ALU stream reads row-major activations: the same bytes
+    const int64_t per = (int64_t)n_layers * p->batch * 2;
+    if (hipMemcpyAsync(xa_packed, x_attn, per * (p->k_attn / p->n_ranks), hipMemcpyDeviceToDevice,
+                       (hipStream_t)stream) != hipSuccess ||
+        hipMemcpyAsync(xf_packed, x_ffn, per * (p->inter / p->n_ranks), hipMemcpyDeviceToDevice,
+                       (hipStream_t)stream) != hipSuccess)
+        return TP_ERR_DEVICE;
+    return TP_OK;
+}
+
 tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, const void* x_attn,
                                   const void* w_o_packed, const void* x_ffn,
                                   const void* w_down_packed, float* slots, float* hidden,

@@ -428,6 +428,55 @@ def test_pack_weights_is_the_mfma_tile_layout():
                           "tiles point %d" % point)
 
 
+def pack_acts_dev(plan, xa, xf):
+    """A step's activations as tp_decode_layers_packed reads them (tp_pack_activations)."""
+    xa = xa if isinstance(xa, torch.Tensor) else to_dev_bf16(xa)
+    xf = xf if isinstance(xf, torch.Tensor) else to_dev_bf16(xf)
+    L = xa.shape[0]
+    pa = torch.empty(tp.packed_act_shape(plan, 0, L), dtype=torch.bfloat16, device="cuda")
+    pf = torch.empty(tp.packed_act_shape(plan, 1, L), dtype=torch.bfloat16, device="cuda")
+    tp.tp_pack_activations(plan, xa, xf, pa, pf)
+    return pa, pf
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki", [(2, 16, 528, 512, 1376), (4, 37, 1040, 672, 2016), (8, 5, 64, 64, 128)])
+def test_pack_activations_is_the_a_operand_order(n, b, h, ka, ki):
+    # X[l][kb][tt][hh][lane][i] = x[l][16tt + lane%16][64kb + 16(lane/16) + 8hh + i], zero past K;
+    # entries of tokens past b are not written (compared only where tokens < b)
+    L = 2
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 2})
+    assert plan.info()["packed_kind"] == 2
+    say("pack activations n=%d b=%d" % (n, b))
+    xs = [synth.normal_bf16((L, b, k // n), 1.0, seed=6, tensor="x", layer=pt) for pt, k in ((0, ka), (1, ki))]
+    got = [bf16_bits_host(p) for p in pack_acts_dev(plan, xs[0], xs[1])]
+    torch.cuda.synchronize()
+    bt = (b + 15) // 16
+    for pt, x in enumerate(xs):
+        k = x.shape[2]
+        nkb = (k + 63) // 64
+        xz = np.zeros((L, 16 * bt, 64 * nkb), np.uint16)
+        xz[:, :b, :k] = x
+        # tokens 16tt + c, rows 64kb + 16g + 8hh + i -> [l][kb][tt][hh][g][c][i], lane = 16 g + c
+        want = xz.reshape(L, bt, 16, nkb, 4, 2, 8).transpose(0, 3, 1, 5, 4, 2, 6)
+        want = np.ascontiguousarray(want).reshape(L, nkb, bt, 2, 64, 8)
+        tok = 16 * np.arange(bt)[:, None] + np.arange(64)[None, :] % 16  # [tt][lane]
+        valid = np.broadcast_to((tok < b)[None, None, :, None, :, None], want.shape)
+        assert_bits_equal(got[pt][valid], want[valid], "point %d" % pt)
+
+
+def test_pack_activations_copies_for_the_vector_alu_stream():
+    L, n, b, h, ka, ki = 2, 2, 3, 1032, 640, 2016
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 1})
+    assert plan.info()["packed_kind"] == 1
+    say("pack activations, row-major")
+    xa = synth.normal_bf16((L, b, ka // n), 1.0, seed=7, tensor="x", layer=0)
+    xf = synth.normal_bf16((L, b, ki // n), 1.0, seed=7, tensor="x", layer=1)
+    pa, pf = pack_acts_dev(plan, xa, xf)
+    torch.cuda.synchronize()
+    assert_bits_equal(bf16_bits_host(pa), xa, "x_attn")
+    assert_bits_equal(bf16_bits_host(pf), xf, "x_ffn")
+
+
 def run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
     """Both point orders on the same inputs; they must give the same bits.
     (The serial order exists on the vector-ALU stream only.)"""
@@ -453,7 +502,8 @@ def _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
     Hd = to_dev_f32(h0)
     po, pd = pack_dev(plan, 0, wo), pack_dev(plan, 1, wd)
     for _ in range(steps):
-        tp.tp_decode_layers_packed(plan, L, rank, to_dev_bf16(xa), po, to_dev_bf16(xf), pd, S, Hd, ws)
+        pa, pf = pack_acts_dev(plan, xa, xf)
+        tp.tp_decode_layers_packed(plan, L, rank, pa, po, pf, pd, S, Hd, ws)
     torch.cuda.synchronize()
     assert tp.tp_workspace_status(plan, ws) == 0
     return host(S), host(Hd)
@@ -562,7 +612,8 @@ def test_packed_full_size_sampled_and_deterministic(w, layers, rank):
     for _ in range(3):
         S = slots.clone()
         Hd = h0.clone()
-        tp.tp_decode_layers_packed(plan, w.layers, rank, xa, po, xf, pd, S, Hd, ws)
+        pa, pf = pack_acts_dev(plan, xa, xf)
+        tp.tp_decode_layers_packed(plan, w.layers, rank, pa, po, pf, pd, S, Hd, ws)
         torch.cuda.synchronize()
         outs.append((host(S), host(Hd)))
     assert tp.tp_workspace_status(plan, ws) == 0
