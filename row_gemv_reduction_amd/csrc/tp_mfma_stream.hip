@@ -574,12 +574,14 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 typedef void (*mfma_stream_fn)(MfmaArgs);
 
 // Tiles per bank: fewer for more token blocks (each tile also carries 2*BT
-// A operands), so the banks fit the registers. Compute waves: 13, or 7 for
-// three and four token blocks (the LDS of their D tiles); stager waves: 2,
-// or 4 for the (N-1) * b rows of more tokens; D-tile buffers: 4, or fewer where
-// the LDS is short.
-constexpr int kWps[5] = {0, 13, 13, 7, 7};
-constexpr int kStagers[5] = {0, 2, 2, 4, 4};
+// A operands), so the banks fit the registers. The waves of a workgroup are
+// spread over the CU's four SIMDs in turn, and on each SIMD the oldest wave
+// is served first: with one control or stager wave per SIMD and the same
+// number of compute waves on every SIMD (12, or 8 for three and four token
+// blocks, where the LDS of their D tiles is short), no SIMD carries more of
+// the stream than another. D-tile buffers: 4, or fewer where the LDS is short.
+constexpr int kWps[5] = {0, 12, 12, 8, 8};
+constexpr int kStagers[5] = {0, 3, 3, 3, 3};
 constexpr int kDBufs[5] = {0, 4, 3, 2, 2};  // D-tile buffers (LDS)
 mfma_stream_fn mfma_stream_kernel(int bt) {
     switch (bt) {
