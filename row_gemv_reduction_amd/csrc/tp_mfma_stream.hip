@@ -167,6 +167,14 @@ __device__ int wg_segments(int g, int G, int S16, int nkb, int (*out)[4]) {
     return n;
 }
 
+// Index of workgroup w among the G when those on XCD x = w % 8 take the
+// x-th block of consecutive indices (blocks of G/8, the first G % 8 one
+// larger). A bijection of [0, G).
+__device__ __forceinline__ int xcd_range_index(int w, int G) {
+    const int x = w % kXCDs, q = G / kXCDs, r = G % kXCDs;
+    return x * q + (x < r ? x : r) + w / kXCDs;
+}
+
 struct Cursor {
     int j, i, m0;            // point, segment, first slot of the bank
     int s, kb0, len, bpw, rot;  // the segment's strip, tiles, slots per wave, walk rotation
@@ -224,7 +232,12 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup w runs on XCD
+    // w % 8); neighbouring ranges of tiles go to the same XCD, so that the
+    // 128-byte lines that two neighbouring strips share (16 columns are 64
+    // bytes of a row of the fp32 slots and of the hidden state) are fetched
+    // into one L2 rather than two.
+    const int g = xcd_range_index((int)blockIdx.x, (int)gridDim.x);
     const int n_points = 2 * a.layers;
     const int B = a.batch;
     const int len = B * a.H;
