@@ -479,7 +479,14 @@ int tp_packed_kind(const tp_plan_s* p) {
     const bool mfma = tp_mfma_geometry(p, &mg);
     if (p->stream_kind == 1) return valu ? 1 : 0;
     if (p->stream_kind == 2) return mfma ? 2 : 0;
-    if (valu && p->batch <= 4) return 1;
+    // Measured on MI355X: the matrix-core stream is the faster one from b = 5
+    // on, and from b = 2 (or b = 1 with short FFN slices, K_r < 2048) when
+    // every 16-column strip stays within one workgroup (H/16 <= its
+    // workgroups); where strips are cut between workgroups (H = 5120 on 256
+    // CUs) the vector-ALU stream is faster up to b = 4.
+    const bool whole = mfma && p->hidden / 16 <= mg.grid;
+    const bool short_k = p->inter / p->n_ranks < 2048;
+    if (valu && p->batch <= 4 && !(whole && (p->batch >= 2 || short_k))) return 1;
     if (mfma) return 2;
     return valu ? 1 : 0;
 }

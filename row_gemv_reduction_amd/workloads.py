@@ -71,10 +71,15 @@ def page1_n2(batch: int) -> Workload:
     return PAGE1_N2.with_(name="page1-h5120-i17408-l64-n2-b%d" % batch, batch=batch)
 
 
+def page1_n4(batch: int) -> Workload:
+    return PAGE1.with_(name="page1-h5120-i17408-l64-n4-b%d" % batch, batch=batch)
+
+
 def h4096(n_ranks: int, batch: int) -> Workload:
     return H4096.with_(name="h4096-i12288-l48-n%d-b%d" % (n_ranks, batch),
                        n_ranks=n_ranks, batch=batch)
 
 
-ALL = {w.name: w for w in [TINY, PAGE1] + [page1_n2(b) for b in (1, 8, 16, 32)]
+ALL = {w.name: w for w in [TINY, PAGE1] + [page1_n4(b) for b in (2, 4, 8, 16)]
+       + [page1_n2(b) for b in (1, 2, 4, 8, 16, 32)]
        + [h4096(n, b) for n in (4, 8) for b in (1, 2, 4, 8, 16, 32, 64)] + [MOE]}
