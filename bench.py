@@ -270,11 +270,9 @@ def moe_run(args, w, tune):
         c = it[0] % copies
         it[0] += 1
         L = layers[c]
-        tp.tp_rowparallel_partial(plan, 0, L["xa"], L["wo"], slots[c, 0, rank], ws)
-        tp.tp_ring_reduce(plan, slots[c, 0], hidden, hidden)
+        tp.tp_decode_point(plan, 0, rank, L["xa"], L["wo"], slots[c, 0], hidden, ws)
         tp.tp_moe_route(plan, L["logits"], se, sw)
-        tp.tp_moe_partial(plan, rank, se, sw, L["u"], L["wp"], slots[c, 1, rank], ws)
-        tp.tp_ring_reduce(plan, slots[c, 1], hidden, hidden)
+        tp.tp_moe_decode(plan, rank, se, sw, L["u"], L["wp"], slots[c, 1], hidden, ws)
 
     ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream())
     # algorithmic bytes of one layer share (averaged over the rotated copies)
@@ -302,8 +300,10 @@ def moe_run(args, w, tune):
               "layers": 1, "active_local_experts_mean": active_total / copies,
               "weight_layout": "row-major attention slice, pair-row packed experts",
               "weight_copies_rotated": copies}
-    kernel = "MoE layer share (attention slice MFMA, ring sums, routing, expert GEMV, combine)"
-    return ms, T, step_bytes, kernel, config, cpu, {}
+    kernel = ("MoE layer share (attention slice MFMA + ring sum, routing, expert GEMV, "
+              "combine + ring sum)")
+    extra = {}
+    return ms, T, step_bytes, kernel, config, cpu, extra
 
 
 def moe_cpu_baseline(w, rank, L, slots, h0, plan, budget_s):

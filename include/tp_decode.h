@@ -214,6 +214,21 @@ tp_status tp_decode_layers(tp_plan_t plan, int32_t n_layers, int32_t rank,
                            float* slots, float* hidden, void* workspace, void* stream);
 
 /*
+ * One reconciliation point: the rank's partial of `point` into its slot, then
+ * hidden <- ring_sum(slots) + hidden (lesson 9.9, Conceito). For batch < 16
+ * in one launch (a split-K projection's last-arriving split does the ring
+ * for its columns); for batch >= 16 the ring is a second launch, which is
+ * faster there.
+ *   x bf16 [batch][K_r], w bf16 [K_r][hidden] (row-major slice),
+ *   slots fp32 [N][batch][hidden]: the other N-1 ranks' partials are inputs,
+ *   entry [rank] is overwritten; hidden fp32 [batch][hidden], in/out.
+ * Same results as tp_rowparallel_partial followed by tp_ring_reduce, bit
+ * for bit. Errors as tp_rowparallel_partial.
+ */
+tp_status tp_decode_point(tp_plan_t plan, int32_t point, int32_t rank, const void* x, const void* w,
+                          float* slots, float* hidden, void* workspace, void* stream);
+
+/*
  * Packed weights for the streamed decode step. A rank's weight slice
  * W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is stored
  * once, when the weights are loaded (not part of the decode step), in the
@@ -343,6 +358,24 @@ tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packe
 tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                          const float* sel_weight, int32_t tokens, const void* u,
                          const void* w_packed, float* part, void* workspace, void* stream);
+
+/*
+ * The MoE share's reconciliation point: tp_moe_partial for the plan's batch
+ * of tokens (the rank's experts), with the combine writing the rank's
+ * partial into its slot and, in the same launch, hidden <- ring_sum(slots) +
+ * hidden (lesson 9.9, Conceito; "Hosting Qwen on Blackwell", MoE
+ * Dispatch-Combine: the combine's all-reduce).
+ *   sel_expert, sel_weight [batch][top_k] (tp_moe_route), u bf16
+ *   [batch][top_k][moe_inter], w_packed as tp_moe_partial,
+ *   slots fp32 [N][batch][hidden] (entry [rank] overwritten), hidden fp32
+ *   [batch][hidden] in/out.
+ * The partial equals tp_moe_partial's bit for bit and the ring stage
+ * tp_ring_reduce's. TP_ERR_INVALID_ARG also if ep != n_ranks or batch >
+ * max_tokens.
+ */
+tp_status tp_moe_decode(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
+                        const float* sel_weight, const void* u, const void* w_packed,
+                        float* slots, float* hidden, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

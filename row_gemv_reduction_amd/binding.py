@@ -65,6 +65,8 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tp_decode_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
                          + [ctypes.c_void_p] * 8),
+    "tp_decode_point": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                        + [ctypes.c_void_p] * 6),
     "tp_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tp_pack_activations": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 5),
@@ -79,6 +81,7 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]),
+    "tp_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 8),
 }
 
 
@@ -237,6 +240,20 @@ def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slo
     _check(_lib().tp_decode_layers(plan.handle, L, rank, *args, _stream()), "tp_decode_layers")
 
 
+def tp_decode_point(plan: Plan, point, rank, x, w, slots, hidden, workspace):
+    """One reconciliation point: partial into slots[rank], then hidden <- ring_sum(slots) + hidden."""
+    i = plan.info()
+    if point not in (0, 1):
+        raise ValueError("point must be 0 (attention out) or 1 (FFN down)")
+    n, b, H, kr = i["n_ranks"], i["batch"], i["hidden"], i["k_rank"][point]
+    args = (_dev(x, "x", torch.bfloat16, (b, kr)), _dev(w, "w", torch.bfloat16, (kr, H)),
+            _dev(slots, "slots", torch.float32, (n, b, H)), _dev(hidden, "hidden", torch.float32, (b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_decode_point(plan.handle, point, rank, *args, _stream()), "tp_decode_point")
+
+
 def packed_shape(plan: Plan, point, n_layers):
     """Shape of a packed weight stack for the plan's streamed step:
     pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/64), 2, 64, 8]."""
@@ -345,3 +362,19 @@ def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, part, 
     if workspace.numel() < i["workspace_bytes"]:
         raise ValueError("workspace too small")
     _check(_lib().tp_moe_partial(plan.handle, rank, *args, t, *rest, _stream()), "tp_moe_partial")
+
+
+def tp_moe_decode(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, slots, hidden, workspace):
+    """The MoE point: the rank's experts for the plan's batch, the combine into slots[rank], then
+    hidden <- ring_sum(slots) + hidden."""
+    i = plan.info()
+    n, b, k, mi, H = i["n_ranks"], i["batch"], i["top_k"], i["moe_inter"], i["hidden"]
+    args = (_dev(sel_expert, "sel_expert", torch.int32, (b, k)),
+            _dev(sel_weight, "sel_weight", torch.float32, (b, k)),
+            _dev(u, "u", torch.bfloat16, (b, k, mi)),
+            _dev(w_packed, "w_packed", torch.bfloat16, moe_packed_shape(plan)),
+            _dev(slots, "slots", torch.float32, (n, b, H)), _dev(hidden, "hidden", torch.float32, (b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_moe_decode(plan.handle, rank, *args, _stream()), "tp_moe_decode")

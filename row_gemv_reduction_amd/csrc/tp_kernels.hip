@@ -674,6 +674,38 @@ tp_status tp_ring_reduce(tp_plan_t p, const float* partials, const float* residu
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
+tp_status tp_decode_point(tp_plan_t p, int32_t point, int32_t rank, const void* x, const void* w,
+                          float* slots, float* hidden, void* ws, void* stream) {
+    if (!p || !x || !w || !slots || !hidden || !ws) return TP_ERR_INVALID_ARG;
+    if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
+    if (rank < 0 || rank >= p->n_ranks) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    const int64_t b = p->batch, len = b * p->hidden, N = p->n_ranks;
+    const PointGeom g = tp_point_geom(p, point);
+    Epilogue e{};
+    e.p = slots + rank * len;
+    e.ws_part = ws_partials(ws);
+    e.counters = ws_counters(ws);
+    e.splits = g.splits;
+    if (g.path == TP_PATH_MFMA) {
+        // Measured: at b >= 16 the ring is faster as its own pass than in
+        // the last-arriving split's epilogue (64 tokens, K_r = 2048, H = 4096:
+        // 20 us against 40 us).
+        tp_status s = launch_projection(p, g, (int)b, static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(w), e, (hipStream_t)stream);
+        if (s != TP_OK) return s;
+        return tp_ring_reduce(p, slots, hidden, hidden, nullptr, stream);
+    }
+    e.ring_slots = slots;
+    e.hidden = hidden;
+    e.n_ranks = (int32_t)N;
+    e.rank = rank;
+    e.chunk = len / N;
+    return launch_projection(p, g, (int)b, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                             e, (hipStream_t)stream);
+}
+
 tp_status tp_decode_layers(tp_plan_t p, int32_t n_layers, int32_t rank, const void* x_attn,
                            const void* w_o, const void* x_ffn, const void* w_down, float* slots,
                            float* hidden, void* ws, void* stream) {

@@ -312,6 +312,26 @@ __global__ void moe_combine_kernel(const float* __restrict__ sel_weight, MoeTabl
     part[i] = acc;
 }
 
+// The same combine, then the rank's partial to its slot and the ring-order
+// sum of the N ranks' values of the point plus the residual (lesson 9.9
+// "Interconnects e clusters", section 01 · Conceito), one element per thread.
+__global__ void moe_combine_ring_kernel(const float* __restrict__ sel_weight, MoeTable tb, int tokens,
+                                        int top_k, int H, float* __restrict__ slots, float* hidden,
+                                        int n_ranks, int rank, int64_t chunk) {
+#pragma clang fp contract(off)
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t len = (int64_t)tokens * H;
+    if (i >= len) return;
+    const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
+    float acc = 0.f;
+    for (int s = 0; s < top_k; ++s) {
+        const int q = tb.slot[t * top_k + s];
+        if (q >= 0) acc = __builtin_fmaf(sel_weight[t * top_k + s], tb.y[(int64_t)q * H + n], acc);
+    }
+    slots[(int64_t)rank * len + i] = acc;
+    hidden[i] = ring_element(slots, len, i, chunk, n_ranks, rank, acc, hidden[i]);
+}
+
 // ------------------------------------------------------------- packing --
 
 // P[e][kp][g][c][q] = W[e][2kp+q][4g+c]: one 16-byte output vector per thread.
@@ -414,15 +434,14 @@ tp_status tp_moe_pack_experts(tp_plan_t p, const void* w_local, void* w_packed, 
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
-tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
-                         const float* sel_weight, int32_t tokens, const void* u,
-                         const void* w_packed, float* part, void* ws, void* stream) {
-    if (!p || !sel_expert || !sel_weight || !u || !w_packed || !part || !ws) return TP_ERR_INVALID_ARG;
-    if (!p->n_experts) return TP_ERR_INVALID_ARG;
-    if (rank < 0 || rank >= p->ep || tokens < 0 || tokens > p->max_tokens) return TP_ERR_INVALID_ARG;
-    if (!aligned16(sel_expert) || !aligned16(sel_weight) || !aligned16(u) || !aligned16(w_packed) ||
-        !aligned16(part) || !aligned16(ws))
-        return TP_ERR_ALIGNMENT;
+}  // extern "C"
+
+namespace {
+
+// The rank's expert rows y (pair table, then the grouped GEMV) for tokens
+// 0 .. tokens-1; the caller combines them.
+tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_expert, int32_t tokens,
+                      const void* u, const void* w_packed, void* ws, hipStream_t st, MoeTable* tb_out) {
     const int64_t I = p->moe_inter, H = p->hidden, el = p->n_experts / p->ep;
     if (I % 8) return TP_ERR_UNSUPPORTED;
     const int64_t kh = I / 2;
@@ -433,9 +452,9 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
     const int64_t lds = lds_x > lds_red ? lds_x : lds_red;
     if (lds > 150 * 1024 || el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
     if (kh * (H / 4) * 16 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
-    if (tokens == 0) return TP_OK;
-    hipStream_t st = (hipStream_t)stream;
     MoeTable tb = table_in(p, ws);
+    *tb_out = tb;
+    if (tokens == 0) return TP_OK;
     const int n_pairs = tokens * p->top_k;
     hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(1024), (unsigned)(el * 8), st, sel_expert,
                        n_pairs, (int)(rank * el), (int)el, tb);
@@ -457,10 +476,53 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
                                                (int)lds) != hipSuccess)
         return TP_ERR_DEVICE;
     hipLaunchKernelGGL(v.fn, dim3((unsigned)grid), dim3(v.nw * 64), (unsigned)lds, st, a);
-    if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
-    const int64_t n_out = (int64_t)tokens * H;
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
+                         const float* sel_weight, int32_t tokens, const void* u,
+                         const void* w_packed, float* part, void* ws, void* stream) {
+    if (!p || !sel_expert || !sel_weight || !u || !w_packed || !part || !ws) return TP_ERR_INVALID_ARG;
+    if (!p->n_experts) return TP_ERR_INVALID_ARG;
+    if (rank < 0 || rank >= p->ep || tokens < 0 || tokens > p->max_tokens) return TP_ERR_INVALID_ARG;
+    if (!aligned16(sel_expert) || !aligned16(sel_weight) || !aligned16(u) || !aligned16(w_packed) ||
+        !aligned16(part) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    hipStream_t st = (hipStream_t)stream;
+    MoeTable tb;
+    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st, &tb);
+    if (s != TP_OK || tokens == 0) return s;
+    const int64_t H = p->hidden, n_out = (int64_t)tokens * H;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st,
                        sel_weight, tb, (int)tokens, (int)p->top_k, (int)H, part);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, const float* sel_weight,
+                        const void* u, const void* w_packed, float* slots, float* hidden, void* ws,
+                        void* stream) {
+    if (!p || !sel_expert || !sel_weight || !u || !w_packed || !slots || !hidden || !ws)
+        return TP_ERR_INVALID_ARG;
+    if (!p->n_experts) return TP_ERR_INVALID_ARG;
+    // the ring spans the plan's N ranks; the experts are spread over ep of them
+    if (p->ep != p->n_ranks || rank < 0 || rank >= p->ep || p->batch > p->max_tokens)
+        return TP_ERR_INVALID_ARG;
+    if (!aligned16(sel_expert) || !aligned16(sel_weight) || !aligned16(u) || !aligned16(w_packed) ||
+        !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    hipStream_t st = (hipStream_t)stream;
+    MoeTable tb;
+    const int32_t tokens = p->batch;
+    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st, &tb);
+    if (s != TP_OK) return s;
+    const int64_t H = p->hidden, len = (int64_t)tokens * H;
+    hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st,
+                       sel_weight, tb, (int)tokens, (int)p->top_k, (int)H, slots, hidden,
+                       (int)p->n_ranks, (int)rank, len / p->n_ranks);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 

@@ -170,3 +170,33 @@ def test_moe_config_full_size_sampled_columns():
     wcols = bf16_bits_host(wdev[:, :, torch.from_numpy(cols).cuda()].contiguous())
     ref64, _ = oracle.moe_partial(se, sw.astype(np.float64), rank * el, u, wcols, nthreads=8)
     assert_partial_close(got[:, cols], ref64, "sampled columns")
+
+
+@pytest.mark.parametrize("T,E,k,I,H,ep", [(10, 16, 4, 64, 256, 2), (64, 128, 8, 1536, 1032, 4)])
+def test_moe_decode_equals_partial_then_ring_bitwise(T, E, k, I, H, ep):
+    say("moe decode T=%d E=%d k=%d I=%d H=%d ep=%d" % (T, E, k, I, H, ep))
+    plan = tp.Plan(H, 8 * ep, ep, T, moe=dict(n_experts=E, top_k=k, ep=ep, moe_inter=I, max_tokens=T))
+    logits, u, w = moe_inputs(T, E, k, I, H, ep, 17)
+    se, sw = gpu_route(plan, logits)
+    el = E // ep
+    rank = ep - 1
+    g = np.random.default_rng(19)
+    slots = (g.standard_normal((ep, T, H)) * 0.5).astype(np.float32)
+    h0 = g.standard_normal((T, H)).astype(np.float32)
+    wr = to_dev_bf16(w[rank * el:(rank + 1) * el])
+    packed = torch.empty(tp.moe_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
+    tp.tp_moe_pack_experts(plan, wr, packed)
+    ws = plan.new_workspace()
+    sed, swd, ud = torch.from_numpy(se).cuda(), torch.from_numpy(sw).cuda(), to_dev_bf16(u)
+    # fused point
+    S, hd = to_dev_f32(slots), to_dev_f32(h0)
+    tp.tp_moe_decode(plan, rank, sed, swd, ud, packed, S, hd, ws)
+    # composition
+    P, hc = to_dev_f32(slots), to_dev_f32(h0)
+    tp.tp_moe_partial(plan, rank, sed, swd, ud, packed, P[rank], ws)
+    tp.tp_ring_reduce(plan, P, hc, hc)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(S), host(P), "slots")
+    assert_bits_equal(host(hd), host(hc), "hidden")
+    ref64, _ = oracle.moe_partial(se, sw.astype(np.float64), rank * el, u, w[rank * el:(rank + 1) * el])
+    assert_partial_close(host(S)[rank], ref64, "partial")

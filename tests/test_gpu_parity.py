@@ -242,6 +242,31 @@ def test_decode_equals_partial_then_ring_bitwise():
     assert_bits_equal(host(hd), h_gpu, "hidden")
 
 
+@pytest.mark.parametrize("n,b,h,ka,ki,rank", [(4, 3, 1032, 512, 1536, 2), (2, 16, 520, 640, 1376, 1),
+                                              (8, 64, 1024, 2048, 4096, 6), (1, 5, 64, 64, 128, 0)])
+def test_decode_point_equals_partial_then_ring_bitwise(n, b, h, ka, ki, rank):
+    L = 1
+    say("decode point n=%d b=%d h=%d" % (n, b, h))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 9, rank)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    ws = plan.new_workspace()
+    for pt, (x, w) in enumerate(((xa[0], wo[0]), (xf[0], wd[0]))):
+        # fused point
+        S = to_dev_f32(slots[0, pt])
+        hd = to_dev_f32(h0)
+        tp.tp_decode_point(plan, pt, rank, to_dev_bf16(x), to_dev_bf16(w), S, hd, ws)
+        # composition
+        P = to_dev_f32(slots[0, pt])
+        hc = to_dev_f32(h0)
+        tp.tp_rowparallel_partial(plan, pt, to_dev_bf16(x), to_dev_bf16(w), P[rank], ws)
+        tp.tp_ring_reduce(plan, P, hc, hc)
+        torch.cuda.synchronize()
+        assert_bits_equal(host(S), host(P), "slots pt=%d" % pt)
+        assert_bits_equal(host(hd), host(hc), "hidden pt=%d" % pt)
+        assert_partial_close(host(S)[rank], oracle.partial(x, w)[0], "partial pt=%d" % pt)
+    assert tp.tp_workspace_status(plan, ws) == 0
+
+
 # ---------------------------------------- benchmark-sized, sampled columns --
 
 def sampled_columns(h, cols_per_tile=256, count=40, seed=0):
