@@ -366,20 +366,25 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                         int p = a.rank - cc;
                         p = p < 0 ? p + N : p;
                         int q = cc > a.rank ? cc - 1 : cc;
-                        q = q == N - 1 ? 0 : q;
-                        sum = v;
+                        q = q >= N - 1 ? 0 : q;
+                        // all eight loads are issued before the first add (q stays
+                        // within rows 0 .. max(N - 2, 0); positions u >= N are unused)
+                        floatx4_t x[8];
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
-                            if (u >= N) break;
-                            const floatx4_t x = *reinterpret_cast<const floatx4_t*>(ob + q * bs);
-                            const bool own = u == p;
-                            floatx4_t y;
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) y[k] = own ? v[k] : x[k];
-                            if (u > 0) sum = sum + y;
-                            else sum = y;
-                            if (!own) q = q + 1 == N - 1 ? 0 : q + 1;
+                            x[u] = *reinterpret_cast<const floatx4_t*>(ob + q * bs);
+                            if (u != p) q = q + 1 >= N - 1 ? 0 : q + 1;
                         }
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) sum[k] = p == 0 ? v[k] : x[0][k];
+#pragma unroll
+                        for (int u = 1; u < 8; ++u)
+                            if (u < N) {
+                                floatx4_t y;
+#pragma unroll
+                                for (int k = 0; k < 4; ++k) y[k] = u == p ? v[k] : x[u][k];
+                                sum = sum + y;
+                            }
                     } else {
                         // a chunk boundary may fall between a lane's columns
 #pragma unroll
