@@ -326,11 +326,12 @@ tp_status tp_moe_route(tp_plan_t plan, const float* logits, int32_t tokens, int3
 /*
  * Pack one rank's experts for tp_moe_partial, once, at load time:
  *     w_local  bf16 [E/ep][moe_inter][hidden] (row-major, as trained)
- *     w_packed bf16 [E/ep][ceil(moe_inter/2)][hidden/4][8], with
- *     w_packed[e][kp][g][2c + q] = w_local[e][2kp + q][4g + c]
- * (rows past moe_inter are zero): each 16-byte vector is a pair of rows of
- * 4 columns, one bf16 pair per column, and a row pair of an expert is
- * contiguous across all columns. Same bytes as the row-major experts.
+ *     w_packed bf16 [E/ep][hidden/16][ceil(moe_inter/64)][1024], with
+ *     w_packed[e][s][kb][512h + 8l + i] = w_local[e][64kb + 16(l/16) + 8h + i][16s + l%16]
+ *     (h < 2, l < 64, i < 8; rows past moe_inter are zero)
+ * the matrix-core tiles of the dense decode step (tp_pack_weights with
+ * packed_kind 2), one expert per matrix: 2 KB per 64 rows x 16 columns.
+ * TP_ERR_UNSUPPORTED if hidden is not a multiple of 16.
  */
 tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packed, void* stream);
 
@@ -351,9 +352,8 @@ tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packe
  * local experts' weighted rows in ascending expert order. Experts that no
  * token selected are not read. Expert ids outside this rank's range are
  * skipped. Uses the workspace (pair table and per-selection rows).
- * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8 or too large for
- * the expert kernel's LDS (moe_inter <= 9600 with the default variant), or
- * E/ep > 8192.
+ * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8, hidden not a
+ * multiple of 16, one expert's packed tiles reach 2 GiB, or E/ep > 8192.
  */
 tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                          const float* sel_weight, int32_t tokens, const void* u,

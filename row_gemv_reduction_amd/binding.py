@@ -337,9 +337,10 @@ def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):
 
 
 def moe_packed_shape(plan: Plan):
-    """Shape of a rank's packed experts: [E/ep, ceil(moe_inter/2), H/4, 8]."""
+    """Shape of a rank's packed experts: [E/ep, H/16, ceil(moe_inter/64), 1024]
+    (2 KB matrix-core tiles of 64 rows x 16 columns)."""
     i = plan.info()
-    return (i["local_experts"], (i["moe_inter"] + 1) // 2, i["hidden"] // 4, 8)
+    return (i["local_experts"], i["hidden"] // 16, (i["moe_inter"] + 63) // 64, 1024)
 
 
 def tp_moe_pack_experts(plan: Plan, w_local, w_packed):

@@ -123,6 +123,11 @@ int64_t tp_xchg_bytes(const tp_plan_s* p);  // exchange buffers of the MFMA stre
 int64_t tp_ws_xchg_offset(const tp_plan_s* p);
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);
+// The MFMA tile layout of n_mats row-major bf16 matrices [K][H] (H a
+// multiple of 16): T[m][s][kb][h][l][i] = W[m][64kb + 16(l/16) + 8h + i][16s + l%16],
+// rows past K zero; 2 KB per tile.
+tp_status tp_pack_tile_stack(int64_t n_mats, int64_t K, int64_t H, const void* w, void* w_packed,
+                             void* stream);
 tp_status tp_pack_acts(const tp_plan_s* p, int n_layers, const void* x_attn, const void* x_ffn,
                        void* xa_packed, void* xf_packed, void* stream);
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,

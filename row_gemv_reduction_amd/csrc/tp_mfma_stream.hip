@@ -685,16 +685,20 @@ tp_status tp_pack_acts(const tp_plan_s* p, int n_layers, const void* x_attn, con
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
-tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
-                        void* stream) {
-    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
-    const int64_t total = (int64_t)n_layers * (p->hidden / 16) * ((K + kTileRows - 1) / kTileRows) * 128;
+tp_status tp_pack_tile_stack(int64_t n_mats, int64_t K, int64_t H, const void* w, void* w_packed,
+                             void* stream) {
+    const int64_t total = n_mats * (H / 16) * ((K + kTileRows - 1) / kTileRows) * 128;
     if (total == 0) return TP_OK;
     const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
     hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       static_cast<const uint16_t*>(w), static_cast<uint16_t*>(w_packed),
-                       (int64_t)n_layers, K, p->hidden);
+                       static_cast<const uint16_t*>(w), static_cast<uint16_t*>(w_packed), n_mats, K, H);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
+                        void* stream) {
+    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    return tp_pack_tile_stack(n_layers, K, p->hidden, w, w_packed, stream);
 }
 
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,

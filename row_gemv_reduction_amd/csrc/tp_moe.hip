@@ -20,19 +20,25 @@
 //                  by local expert: counts, offsets and a slot per pair. The
 //                  order of pairs inside an expert's group only decides which
 //                  slot holds which row, never any arithmetic.
-//   moe_expert     one workgroup per (local expert, block of 256 columns):
-//                  the expert's rows are staged in LDS as bf16 pairs, each lane
-//                  owns 4 columns and accumulates over its wave's share of
-//                  the expert's K rows (no cross-lane reduction), the waves'
-//                  K shares are summed in LDS in wave order, and the rows'
-//                  projections land in Y[slot].
+//   moe_expert     one workgroup per (local expert, block of 8 16-column
+//                  strips): up to 16 of the expert's rows at a time as the
+//                  A operand of v_mfma_f32_16x16x32_bf16 (each weight tile is
+//                  read once per 16 rows; an expert has 4 rows on average),
+//                  the waves split the expert's K rows, their D tiles are
+//                  summed in LDS in wave order, and the rows' projections
+//                  land in Y[slot]. A dot-product (vector ALU) version of the
+//                  same GEMV spent more time in its multiply-adds than in
+//                  streaming the weights; the matrix cores take them off the
+//                  issue slots.
 //   moe_combine    part[t, n] = sum over the token's selections s, in order
 //                  (ascending expert), of weight * Y[slot(t, s), n] for the
 //                  local ones.
 //
-// Expert weights are packed once at load time ("pair rows"):
-//     P[e][kp][g][c][q] = W_e[2kp + q][4g + c]     kp < ceil(I/2), g < H/4
-// so a wave streams one row pair across 256 columns per 1 KB load.
+// Expert weights are packed once at load time as the matrix-core tiles of
+// the dense decode step (one expert per matrix):
+//     T[e][s][kb][h][l][i] = W_e[64kb + 16(l/16) + 8h + i][16s + l%16]
+// (rows past I zero), so that one 16-byte load per lane and half hands each
+// lane its B operand and a tile is 2 KB of contiguous memory.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -44,10 +50,8 @@ namespace {
 
 using namespace tpdev;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRouteMaxPerLane = 32;   // experts per lane in the routing wave (E <= 2048)
-constexpr int kMoeCols = 256;          // columns per expert workgroup: 64 lanes x 4
 
 // ------------------------------------------------------------- routing --
 
@@ -190,109 +194,116 @@ __global__ __launch_bounds__(1024) void moe_table_kernel(const int32_t* __restri
 
 struct ExpertArgs {
     const uint16_t* u;       // [T][k][I] bf16, row of pair p at u + p * I
-    const uint16_t* w;       // packed [EL][Kh][H/4][8]
+    const uint16_t* w;       // tiles [EL][S16][nkb][2][64][8]
     MoeTable tb;
-    int32_t H, G4, I, Kh;    // G4 = H / 4 column groups
-    int32_t rows_per_wave;   // row pairs per wave (multiple of 2 * kMoeSL)
-    int32_t col_blocks;      // ceil(G4 / 64)
+    int32_t H, S16, I, nkb;
+    int32_t col_blocks;      // ceil(S16 / SB)
 };
 
-// MT activation rows per pass (more rows: more passes over the weights),
-// NW waves per workgroup (the K split), SL loads per lane per register bank.
-template <int MT, int NW, int SL>
+constexpr int kMoeTileBytes = 2048;  // 64 rows x 16 columns of bf16
+
+// One workgroup per (local expert, block of SB 16-column strips); a pass
+// takes up to 16 of the expert's rows (its slots, in table order) as the A
+// operand (token m = lane % 16). Wave w takes the row tiles kb = w, w + NW,
+// ... of the expert and, per tile, the block's SB strips in two register
+// banks of SL = SB/2 tiles, loading each A operand once per 64 rows and the
+// next tile's operands while it multiplies the current ones. The waves' D
+// tiles are then summed in wave order in LDS and the pass's rows land in
+// Y[slot]. Strips past the block's last and rows past the expert's read
+// zero (offsets past the buffer range); A operands of empty token slots and
+// of rows past I are zero.
+template <int SB, int NW>
 __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
-    constexpr int kMoeWaves = NW;
-    constexpr int kMoeSL = SL;
-    // x rows of the pass as bf16 pairs [MT][Kh]; reused afterwards for the
-    // waves' column sums [kMoeWaves][MT][kMoeCols]
-    extern __shared__ __align__(16) uint32_t sh[];
+    constexpr int SL = SB / 2;
+    __shared__ __align__(16) float red[NW * SB * 256];  // [NW][SB][64][4] D tiles
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int le = blockIdx.x / a.col_blocks, cb = blockIdx.x % a.col_blocks;
     const int q0 = a.tb.off[le], n_rows = a.tb.off[le + 1] - q0;
     if (n_rows == 0) return;  // expert not selected by any token: not read
-    const int g = cb * 64 + lane;  // this lane's column group
-    const int kp0 = wave * a.rows_per_wave;
-    const int64_t slab = (int64_t)a.Kh * a.G4 * 16;  // bytes of one expert
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.w) + (int64_t)le * a.Kh * a.G4 * 8, (short)0, (int)slab,
-        kBufferRsrcWord3);
-    // lanes past the last column group read the next row's columns (or
-    // zeros at the end of the slab); their sums are never stored
-    const int voff = (kp0 * a.G4 + g) * 16;
-    const int rstride = a.G4 * 16;
-    float* red = reinterpret_cast<float*>(sh);
+    const int s0 = cb * SB;
+    const int ns = a.S16 - s0 < SB ? a.S16 - s0 : SB;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.w) + ((int64_t)le * a.S16 + s0) * a.nkb * (kMoeTileBytes / 2), (short)0,
+        ns * a.nkb * kMoeTileBytes, kBufferRsrcWord3);
+    const int past = ns * a.nkb * kMoeTileBytes;  // an offset past the range: reads zero
+    const int nkw = a.nkb > wave ? (a.nkb - wave + NW - 1) / NW : 0;  // this wave's row tiles
+    const int g16 = 16 * (lane >> 4);
 
-    for (int r0 = 0; r0 < n_rows; r0 += MT) {
-        const int nr = n_rows - r0 < MT ? n_rows - r0 : MT;
-        __syncthreads();  // the previous pass is done with the LDS
-        // stage the pass's rows: [row][kp] dwords, 16 bytes per thread step
-        for (int v = tid; v < nr * (a.I / 8); v += kMoeWaves * 64) {
-            const int row = v / (a.I / 8), c = v - row * (a.I / 8);
-            const int p = a.tb.pair[q0 + r0 + row];
-            const u32x4_t val = *reinterpret_cast<const u32x4_t*>(a.u + (int64_t)p * a.I + c * 8);
-            *reinterpret_cast<u32x4_t*>(sh + row * a.Kh + c * 4) = val;
-        }
-        __syncthreads();
-
-        float acc[MT][4];
+    for (int r0 = 0; r0 < n_rows; r0 += 16) {
+        const int nr = n_rows - r0 < 16 ? n_rows - r0 : 16;
+        const int m = lane & 15;
+        const int pr = m < nr ? a.tb.pair[q0 + r0 + m] : -1;
+        const uint16_t* up = a.u + (int64_t)(pr < 0 ? 0 : pr) * a.I;
+        // B operands of bank j (strips j*SL .. j*SL + SL - 1) of row tile kb (< 0: none)
+        auto issue_w = [&](u32x4_t (&bv)[SL][2], int j, int kb) {
 #pragma unroll
-        for (int r = 0; r < MT; ++r)
+            for (int i = 0; i < SL; ++i) {
+                const int s = j * SL + i;
+                const int off = kb >= 0 && s < ns ? (s * a.nkb + kb) * kMoeTileBytes : past;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-        u32x4_t bank0[kMoeSL], bank1[kMoeSL];
-        auto issue = [&](u32x4_t (&bank)[kMoeSL], int k) {
-#pragma unroll
-            for (int i = 0; i < kMoeSL; ++i)
-                bank[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          rs, voff + (k + i) * rstride, 0, kCachePolicyNT));
-        };
-        // row pairs past Kh read zero weights; their x index is clamped to the
-        // last staged pair, so the product is zero (x is finite)
-        auto consume = [&](const u32x4_t (&bank)[kMoeSL], int k) {
-#pragma unroll
-            for (int i = 0; i < kMoeSL; ++i) {
-                const u32x4_t wq = bank[i];
-                const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
-                int kp = kp0 + k + i;
-                kp = kp < a.Kh ? kp : a.Kh - 1;
-#pragma unroll
-                for (int r = 0; r < MT; ++r) {
-                    if (r < nr) {
-                        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, sh[r * a.Kh + kp]);
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            acc[r][c] = __builtin_amdgcn_fdot2_f32_bf16(
-                                __builtin_bit_cast(bf16x2_t, wd[c]), xv, acc[r][c], false);
-                    }
-                }
+                for (int h = 0; h < 2; ++h)
+                    bv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               wr, off + h * 1024 + lane * 16, 0, kCachePolicyNT));
             }
         };
-        const int n = a.rows_per_wave;  // multiple of 2 * kMoeSL
-        issue(bank0, 0);
-        issue(bank1, kMoeSL);
-        for (int k = 0; k < n; k += 2 * kMoeSL) {
-            consume(bank0, k);
-            issue(bank0, k + 2 * kMoeSL < n ? k + 2 * kMoeSL : a.Kh);
-            consume(bank1, k + kMoeSL);
-            issue(bank1, k + 3 * kMoeSL < n ? k + 3 * kMoeSL : a.Kh);
+        // A operands of row tile kb: token m, rows 64kb + 16(lane/16) + 8h .. +7
+        auto issue_x = [&](u32x4_t (&xv)[2], int kb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k0 = 64 * kb + g16 + 8 * h;
+                xv[h] = kb >= 0 && pr >= 0 && k0 < a.I ? *reinterpret_cast<const u32x4_t*>(up + k0)
+                                                       : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        };
+        floatx4_t acc[SB];
+#pragma unroll
+        for (int s = 0; s < SB; ++s) acc[s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        auto consume = [&](const u32x4_t (&bv)[SL][2], const u32x4_t (&xv)[2], int j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < SL; ++i)
+                    acc[j * SL + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xv[h]), __builtin_bit_cast(bf16x8_t, bv[i][h]),
+                        acc[j * SL + i], 0, 0, 0);
+        };
+        u32x4_t b0[SL][2], b1[SL][2], xa[2], xb[2];
+        const int kb_first = nkw > 0 ? wave : -1;
+        issue_x(xa, kb_first);
+        issue_w(b0, 0, kb_first);
+        issue_w(b1, 1, kb_first);
+        // row tile n of this wave: its operands are in (xc, b0, b1); the next
+        // tile's are loaded behind them into (xn, b0, b1)
+        auto step = [&](u32x4_t (&xc)[2], u32x4_t (&xn)[2], int n) {
+            const int kbn = n + 1 < nkw ? wave + (n + 1) * NW : -1;
+            issue_x(xn, kbn);
+            consume(b0, xc, 0);
+            issue_w(b0, 0, kbn);
+            consume(b1, xc, 1);
+            issue_w(b1, 1, kbn);
+        };
+        int n = 0;
+        for (; n + 1 < nkw; n += 2) {
+            step(xa, xb, n);
+            step(xb, xa, n + 1);
         }
-        __syncthreads();  // every wave is done reading x: reuse the LDS
+        if (n < nkw) step(xa, xb, n);
+        // the waves' D tiles (lane l: tokens 4(l/16) + q of column l % 16),
+        // summed in wave order
+        if (r0 > 0) __syncthreads();  // the previous pass has read red
 #pragma unroll
-        for (int r = 0; r < MT; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                red[(wave * MT + r) * kMoeCols + lane * 4 + c] = acc[r][c];
+        for (int s = 0; s < SB; ++s)
+            *reinterpret_cast<floatx4_t*>(red + (wave * SB + s) * 256 + lane * 4) = acc[s];
         __syncthreads();
-        // sum the waves' K shares in wave order; store the pass's rows
-        for (int idx = tid; idx < nr * kMoeCols; idx += kMoeWaves * 64) {
-            const int r = idx / kMoeCols, col = idx - r * kMoeCols;
-            const int n_col = cb * kMoeCols + col;
-            if (n_col >= a.H) continue;
-            float v = red[r * kMoeCols + col];
+        for (int idx = tid; idx < ns * nr * 16; idx += NW * 64) {
+            const int s = idx / (nr * 16), rem = idx - s * nr * 16;
+            const int row = rem >> 4, col = rem & 15;
+            const int e = (16 * (row >> 2) + col) * 4 + (row & 3);
+            float v = red[s * 256 + e];
 #pragma unroll
-            for (int w = 1; w < kMoeWaves; ++w) v += red[(w * MT + r) * kMoeCols + col];
-            a.tb.y[(int64_t)(q0 + r0 + r) * a.H + n_col] = v;
+            for (int w = 1; w < NW; ++w) v += red[(w * SB + s) * 256 + e];
+            a.tb.y[(int64_t)(q0 + r0 + row) * a.H + 16 * (s0 + s) + col] = v;
         }
     }
 }
@@ -332,50 +343,22 @@ __global__ void moe_combine_ring_kernel(const float* __restrict__ sel_weight, Mo
     hidden[i] = ring_element(slots, len, i, chunk, n_ranks, rank, acc, hidden[i]);
 }
 
-// ------------------------------------------------------------- packing --
-
-// P[e][kp][g][c][q] = W[e][2kp+q][4g+c]: one 16-byte output vector per thread.
-__global__ void pack_experts_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
-                                    int64_t experts, int64_t I, int64_t H) {
-    const int64_t g4 = H / 4, kh = (I + 1) / 2;
-    const int64_t total = experts * kh * g4;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
-         v += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t e = v / (kh * g4);
-        const int64_t rem = v - e * kh * g4;
-        const int64_t kp = rem / g4, gg = rem - kp * g4;
-        const uint16_t* r0 = w + (e * I + 2 * kp) * H + 4 * gg;
-        uint16_t lo[4], hi[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            lo[c] = r0[c];
-            hi[c] = 2 * kp + 1 < I ? r0[H + c] : (uint16_t)0;
-        }
-        u32x4_t out;
-        out.x = lo[0] | ((uint32_t)hi[0] << 16);
-        out.y = lo[1] | ((uint32_t)hi[1] << 16);
-        out.z = lo[2] | ((uint32_t)hi[2] << 16);
-        out.w = lo[3] | ((uint32_t)hi[3] << 16);
-        *reinterpret_cast<u32x4_t*>(p + v * 8) = out;
-    }
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 struct ExpertVariant {
-    int mt, nw, sl;
+    int sb, nw;
     void (*fn)(ExpertArgs);
 };
 // The plan knob "moe_variant" picks one (1-based; 0 = the first, the
 // fastest measured at 128 experts of 1536 x 4096, 64 tokens, top-8, EP=4).
 const ExpertVariant kExpertVariants[] = {
-    {8, 8, 4, moe_expert_kernel<8, 8, 4>},
-    {8, 4, 4, moe_expert_kernel<8, 4, 4>},
-    {8, 4, 8, moe_expert_kernel<8, 4, 8>},
-    {4, 4, 8, moe_expert_kernel<4, 4, 8>},
-    {4, 8, 8, moe_expert_kernel<4, 8, 8>},
-    {8, 16, 4, moe_expert_kernel<8, 16, 4>},
-    {8, 16, 2, moe_expert_kernel<8, 16, 2>},
+    {8, 4, moe_expert_kernel<8, 4>},
+    {4, 4, moe_expert_kernel<4, 4>},
+    {6, 4, moe_expert_kernel<6, 4>},
+    {8, 8, moe_expert_kernel<8, 8>},
+    {4, 8, moe_expert_kernel<4, 8>},
+    {8, 2, moe_expert_kernel<8, 2>},
+    {16, 4, moe_expert_kernel<16, 4>},
 };
 
 MoeTable table_in(const tp_plan_s* p, void* ws) {
@@ -425,13 +408,8 @@ tp_status tp_moe_pack_experts(tp_plan_t p, const void* w_local, void* w_packed, 
     if (!p->n_experts) return TP_ERR_INVALID_ARG;
     if (!aligned16(w_local) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
     if (w_local == w_packed) return TP_ERR_INVALID_ARG;
-    const int64_t el = p->n_experts / p->ep;
-    const int64_t total = el * ((p->moe_inter + 1) / 2) * (p->hidden / 4);
-    const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
-    hipLaunchKernelGGL(pack_experts_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       static_cast<const uint16_t*>(w_local), static_cast<uint16_t*>(w_packed), el,
-                       p->moe_inter, p->hidden);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    if (p->hidden % 16) return TP_ERR_UNSUPPORTED;
+    return tp_pack_tile_stack(p->n_experts / p->ep, p->moe_inter, p->hidden, w_local, w_packed, stream);
 }
 
 }  // extern "C"
@@ -443,15 +421,11 @@ namespace {
 tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_expert, int32_t tokens,
                       const void* u, const void* w_packed, void* ws, hipStream_t st, MoeTable* tb_out) {
     const int64_t I = p->moe_inter, H = p->hidden, el = p->n_experts / p->ep;
-    if (I % 8) return TP_ERR_UNSUPPORTED;
-    const int64_t kh = I / 2;
+    if (I % 8 || H % 16) return TP_ERR_UNSUPPORTED;
+    const int64_t S16 = H / 16, nkb = (I + 63) / 64;
     const ExpertVariant v = kExpertVariants[p->moe_variant > 0 ? p->moe_variant - 1 : 0];
-    // LDS: the pass's rows (MT x I bf16) and the waves' sums
-    const int64_t lds_x = (int64_t)v.mt * kh * 4;
-    const int64_t lds_red = (int64_t)v.nw * v.mt * kMoeCols * 4;
-    const int64_t lds = lds_x > lds_red ? lds_x : lds_red;
-    if (lds > 150 * 1024 || el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
-    if (kh * (H / 4) * 16 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
+    if (el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
+    if (S16 * nkb * kMoeTileBytes >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
     MoeTable tb = table_in(p, ws);
     *tb_out = tb;
     if (tokens == 0) return TP_OK;
@@ -464,18 +438,12 @@ tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_exper
     a.w = static_cast<const uint16_t*>(w_packed);
     a.tb = tb;
     a.H = (int32_t)H;
-    a.G4 = (int32_t)(H / 4);
+    a.S16 = (int32_t)S16;
     a.I = (int32_t)I;
-    a.Kh = (int32_t)kh;
-    const int64_t per_wave = (kh + v.nw - 1) / v.nw;
-    a.rows_per_wave = (int32_t)((per_wave + 2 * v.sl - 1) / (2 * v.sl) * (2 * v.sl));
-    a.col_blocks = (int32_t)((H / 4 + 63) / 64);
+    a.nkb = (int32_t)nkb;
+    a.col_blocks = (int32_t)((S16 + v.sb - 1) / v.sb);
     const int64_t grid = el * a.col_blocks;
-    if (lds > 64 * 1024 && hipFuncSetAttribute(reinterpret_cast<const void*>(v.fn),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds) != hipSuccess)
-        return TP_ERR_DEVICE;
-    hipLaunchKernelGGL(v.fn, dim3((unsigned)grid), dim3(v.nw * 64), (unsigned)lds, st, a);
+    hipLaunchKernelGGL(v.fn, dim3((unsigned)grid), dim3(v.nw * 64), 0, st, a);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 

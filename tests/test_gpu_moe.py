@@ -91,8 +91,8 @@ def gpu_moe_partial(plan, rank, se, sw, u_bits, w_rank_dev):
     return host(part)
 
 
-@pytest.mark.parametrize("T,E,k,I,H,ep", [(10, 16, 4, 64, 256, 2), (64, 128, 8, 1536, 1032, 4),
-                                          (3, 8, 2, 24, 8, 1), (33, 32, 8, 520, 2048, 4)])
+@pytest.mark.parametrize("T,E,k,I,H,ep", [(10, 16, 4, 64, 256, 2), (64, 128, 8, 1536, 1040, 4),
+                                          (3, 8, 2, 24, 16, 1), (33, 32, 8, 520, 2048, 4)])
 def test_moe_partial_matches_oracle_every_rank(T, E, k, I, H, ep):
     say("moe partial T=%d E=%d k=%d I=%d H=%d ep=%d" % (T, E, k, I, H, ep))
     plan = moe_plan(H, E, k, ep, I, T)
@@ -111,9 +111,10 @@ def test_moe_partial_matches_oracle_every_rank(T, E, k, I, H, ep):
 
 
 def test_moe_expert_with_many_tokens_and_tokens_without_local_experts():
-    # tokens 0..18 all pick expert 1 (19 rows: three passes of at most 8
-    # rows); tokens 19..23 pick only rank 1's experts
-    T, E, k, I, H, ep = 24, 8, 3, 40, 520, 2
+    # tokens 0..18 all pick expert 1 (19 rows: two passes of at most 16
+    # rows); tokens 19..23 pick only rank 1's experts; 33 strips of 16
+    # columns (a last block of one strip)
+    T, E, k, I, H, ep = 24, 8, 3, 40, 528, 2
     say("moe crafted routing")
     plan = moe_plan(H, E, k, ep, I, T)
     _, u, w = moe_inputs(T, E, k, I, H, ep, 12)
@@ -172,7 +173,7 @@ def test_moe_config_full_size_sampled_columns():
     assert_partial_close(got[:, cols], ref64, "sampled columns")
 
 
-@pytest.mark.parametrize("T,E,k,I,H,ep", [(10, 16, 4, 64, 256, 2), (64, 128, 8, 1536, 1032, 4)])
+@pytest.mark.parametrize("T,E,k,I,H,ep", [(10, 16, 4, 64, 256, 2), (64, 128, 8, 1536, 1040, 4)])
 def test_moe_decode_equals_partial_then_ring_bitwise(T, E, k, I, H, ep):
     say("moe decode T=%d E=%d k=%d I=%d H=%d ep=%d" % (T, E, k, I, H, ep))
     plan = tp.Plan(H, 8 * ep, ep, T, moe=dict(n_experts=E, top_k=k, ep=ep, moe_inter=I, max_tokens=T))
