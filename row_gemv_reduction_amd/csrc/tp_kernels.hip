@@ -58,6 +58,12 @@ struct Epilogue {
     float* hidden;            // [B][H] residual stream, updated in place
     int32_t n_ranks, rank;
     int64_t chunk;            // B*H / N
+    // spread fix-up: every split's workgroup is resident (cooperative
+    // launch) and sums a share of its column tile (0: the last arrival sums
+    // all of it)
+    int32_t spread;
+    uint32_t* err;            // error word (bounded waits)
+    uint32_t spin_limit;
 };
 
 // Publish this split's partial tile [batch][COLS] (LDS) and find out whether
@@ -89,13 +95,47 @@ __device__ bool publish_split(const Epilogue& e, const float* tile, int batch, i
     return *s_flag != 0;
 }
 
+// One 16-byte vector (4 columns) of the final partial: the splits summed in
+// split order, written to the partial and, with the ring epilogue, the
+// ring-order sum + residual into the hidden state. The residual load goes
+// out with the split loads (one round trip).
+__device__ __forceinline__ void fixup_vector(const Epilogue& e, const float* tile_vec, int64_t i,
+                                             int64_t len, __amdgpu_buffer_rsrc_t rp,
+                                             __amdgpu_buffer_rsrc_t rh) {
+#pragma clang fp contract(off)
+    const floatx4_t res = e.ring_slots ? ld_dev4(rh, (uint32_t)(i * 4)) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+    floatx4_t v;
+    if (e.splits > 1) {
+        floatx4_t l[8];
+        for (int s0 = 0; s0 < e.splits; s0 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + u < e.splits ? s0 + u : e.splits - 1;
+                l[u] = ld_dev4(rp, (uint32_t)(((int64_t)sp * len + i) * 4));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < e.splits) v = (s0 + u == 0) ? l[u] : v + l[u];
+        }
+    } else {
+        v = *reinterpret_cast<const floatx4_t*>(tile_vec);
+    }
+    *reinterpret_cast<floatx4_t*>(e.p + i) = v;
+    if (e.ring_slots) {
+        floatx4_t o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            o[k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], res[k]);
+        st_dev4(rh, (uint32_t)(i * 4), o);
+    }
+}
+
 // Last arrival: sum the splits in split order, write the partial and, with
 // the ring epilogue, the ring-order sum + residual into the hidden state.
 // Four columns at a time; every element is still summed in split order.
 template <int COLS, int NT>
 __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
                            int tid) {
-#pragma clang fp contract(off)
     const int64_t n0 = (int64_t)ct * COLS;
     const int64_t len = (int64_t)batch * H;
     const __amdgpu_buffer_rsrc_t rp = dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * len * 4));
@@ -104,36 +144,43 @@ __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int6
         const int bb = idx / (COLS / 4), c = (idx - bb * (COLS / 4)) * 4;
         const int64_t n = n0 + c;
         if (n >= H) continue;
-        const int64_t i = (int64_t)bb * H + n;
-        // the residual load goes out with the split loads (one round trip)
-        const floatx4_t res = e.ring_slots ? ld_dev4(rh, (uint32_t)(i * 4)) : floatx4_t{0.f, 0.f, 0.f, 0.f};
-        floatx4_t v;
-        if (e.splits > 1) {
-            floatx4_t l[8];
-            for (int s0 = 0; s0 < e.splits; s0 += 8) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int sp = s0 + u < e.splits ? s0 + u : e.splits - 1;
-                    l[u] = ld_dev4(rp, (uint32_t)(((int64_t)sp * len + i) * 4));
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (s0 + u < e.splits) v = (s0 + u == 0) ? l[u] : v + l[u];
-            }
-        } else {
-            v = *reinterpret_cast<const floatx4_t*>(tile + bb * COLS + c);
-        }
-        *reinterpret_cast<floatx4_t*>(e.p + i) = v;
-        if (e.ring_slots) {
-            floatx4_t o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                o[k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], res[k]);
-            st_dev4(rh, (uint32_t)(i * 4), o);
-        }
+        fixup_vector(e, tile + bb * COLS + c, (int64_t)bb * H + n, len, rp, rh);
     }
     if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
     wait_mem();
+}
+
+// Spread fix-up (all of a column tile's splits resident): once every split
+// has published, split sp's workgroup takes the sp-th of S equal shares of
+// the tile's vectors (each still summed in split order, so the result is
+// the last-arrival fix-up's, bit for bit); the last one to finish clears
+// the tile's counters for the next launch. The arrival wait is bounded.
+template <int COLS, int NT>
+__device__ void spread_fixup(const Epilogue& e, int batch, int64_t H, int ct, int sp, int tid) {
+    uint32_t* arrive = &e.counters[ct * kCounterStride];
+    uint32_t* leave = arrive + 1;
+    if (tid == 0) wait_at_least(arrive, (uint32_t)e.splits, e.err, e.spin_limit);
+    __syncthreads();
+    compiler_barrier();
+    const int64_t n0 = (int64_t)ct * COLS;
+    const int64_t len = (int64_t)batch * H;
+    const __amdgpu_buffer_rsrc_t rp = dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * len * 4));
+    const __amdgpu_buffer_rsrc_t rh = dev_rsrc(e.hidden, (uint32_t)(len * 4));
+    const int total = batch * COLS / 4;
+    const int share = (total + e.splits - 1) / e.splits;
+    const int hi = (sp + 1) * share < total ? (sp + 1) * share : total;
+    for (int idx = sp * share + tid; idx < hi; idx += NT) {
+        const int bb = idx / (COLS / 4), c = (idx - bb * (COLS / 4)) * 4;
+        const int64_t n = n0 + c;
+        if (n >= H) continue;
+        fixup_vector(e, nullptr, (int64_t)bb * H + n, len, rp, rh);
+    }
+    wait_mem();
+    __syncthreads();
+    if (tid == 0 && add_dev_u32(leave, 1u) == (uint32_t)(e.splits - 1)) {
+        st_dev_u32(arrive, 0u);
+        st_dev_u32(leave, 0u);
+    }
 }
 
 // ------------------------------------------------------------ VALU tile --
@@ -368,14 +415,22 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int bat
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[bt][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int step = wave * 32; step < rows; step += kMfmaWaves * 32) {
+    // The wave's 32-row steps. Once a step's weight rows are rearranged into
+    // B operands, the next step's rows (s + 4*32) are loaded into the same
+    // registers while this step is multiplied (rows past the split read
+    // nothing and give zeros).
+    auto load_w = [&](u32x4_t (&wv)[8], int step) {
         const int64_t kr = k0 + step + 8 * g;  // first of this lane's 8 rows
-        u32x4_t wv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bool ok = col_ok && (step + 8 * g + j) < rows;
+            const bool ok = col_ok && (step + 8 * g + j) < rows;
             wv[j] = ok ? load_stream16(a.w + (kr + j) * a.H + n) : u32x4_t{0u, 0u, 0u, 0u};
         }
+    };
+    u32x4_t wv[8];
+    load_w(wv, wave * 32);
+    for (int step = wave * 32; step < rows; step += kMfmaWaves * 32) {
+        const int64_t kr = k0 + step + 8 * g;
         // A operands: x[bt*16 + i][kr .. kr+7]
         bf16x8_t xa[BT];
 #pragma unroll
@@ -400,22 +455,23 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int bat
             xa[bt] = __builtin_bit_cast(bf16x8_t, xv);
         }
         // B operands: for each of the lane's 8 columns c, its 8 rows as k-major bf16x8
+        bf16x8_t bop[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const bool hi = c & 1;
-            uint32_t w0[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w0[j] = wv[j][c >> 1];
             u32x4_t bw;
-            bw.x = pair_rows(w0[0], w0[1], hi);
-            bw.y = pair_rows(w0[2], w0[3], hi);
-            bw.z = pair_rows(w0[4], w0[5], hi);
-            bw.w = pair_rows(w0[6], w0[7], hi);
-            bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bw);
+            bw.x = pair_rows(wv[0][c >> 1], wv[1][c >> 1], hi);
+            bw.y = pair_rows(wv[2][c >> 1], wv[3][c >> 1], hi);
+            bw.z = pair_rows(wv[4][c >> 1], wv[5][c >> 1], hi);
+            bw.w = pair_rows(wv[6][c >> 1], wv[7][c >> 1], hi);
+            bop[c] = __builtin_bit_cast(bf16x8_t, bw);
+        }
+        load_w(wv, step + kMfmaWaves * 32);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int bt = 0; bt < BT; ++bt)
-                acc[bt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[bt], bop, acc[bt][c], 0, 0, 0);
-        }
+                acc[bt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[bt], bop[c], acc[bt][c], 0, 0, 0);
     }
 
     // D layout of a 16x16 fp32 MFMA tile: lane holds rows 4*(lane/16)+q,
@@ -436,7 +492,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int bat
         }
         __syncthreads();
     }
-    if (publish_split<COLS, NT>(a.epi, tile, batch, a.H, ct, sp, tid, &s_flag))
+    const bool last = publish_split<COLS, NT>(a.epi, tile, batch, a.H, ct, sp, tid, &s_flag);
+    if (a.epi.spread && a.epi.splits > 1)
+        spread_fixup<COLS, NT>(a.epi, batch, a.H, ct, sp, tid);
+    else if (last)
         fixup_tile<COLS, NT>(a.epi, tile, batch, a.H, ct, tid);
 }
 
@@ -530,6 +589,38 @@ float* ws_partials(void* ws) {
     return reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + tp_ws_partials_offset());
 }
 
+// Resident workgroups of a kernel on the current device (cooperative grid).
+int resident_grid(const void* kernel, int block) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+    return per_cu * cus;
+}
+
+// Whether the matrix-core projection of geometry g spreads its split-K
+// fix-up over all splits: only where every workgroup of the grid can be
+// resident at once on an idle device (the kernel's occupancy, cached per
+// device and token blocks), since a split waits for the others' partials.
+// The wait is bounded: should other work hold CUs for long, the error word
+// is set and the launch still ends. (A cooperative launch would guarantee
+// residency but costs more host time per launch than the fix-up saves.)
+bool mfma_spread(const PointGeom& g, int batch) {
+    if (g.path != TP_PATH_MFMA || g.splits < 2) return false;
+    const int bt = (batch + 15) / 16;
+    if (bt < 1 || bt > 4) return false;
+    static int cap[16][5];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return false;
+    if (cap[dev][bt] == 0) {
+        const int c = resident_grid(reinterpret_cast<const void*>(mfma_kernel(batch)), kMfmaWaves * 64);
+        cap[dev][bt] = c > 0 ? c : -1;
+    }
+    return g.grid <= cap[dev][bt];
+}
+
 // Launch one projection (and its optional ring epilogue).
 tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, const void* x,
                             const void* w, const Epilogue& epi, hipStream_t st) {
@@ -541,6 +632,9 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
     a.rows = g.rows;
     a.col_tiles = g.col_tiles;
     a.epi = epi;
+    a.epi.err = ws_sync(epi.counters) + kSyncErr;
+    a.epi.spin_limit = 1u << 21;
+    a.epi.spread = mfma_spread(g, batch) ? 1 : 0;
     // host-side checks of what the kernels assume
     if (g.splits < 1 || g.col_tiles < 1 || (int64_t)g.rows * g.splits < g.k_r) return TP_ERR_INVALID_ARG;
     if ((int64_t)g.splits * batch * p->hidden * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
@@ -558,17 +652,6 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
         hipLaunchKernelGGL(k, dim3(g.grid), dim3(kMfmaWaves * 64), 0, st, a, batch);
     }
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
-}
-
-// Resident workgroups of a kernel on the current device (cooperative grid).
-int resident_grid(const void* kernel, int block) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
-    return per_cu * cus;
 }
 
 tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
@@ -688,10 +771,11 @@ tp_status tp_decode_point(tp_plan_t p, int32_t point, int32_t rank, const void* 
     e.ws_part = ws_partials(ws);
     e.counters = ws_counters(ws);
     e.splits = g.splits;
-    if (g.path == TP_PATH_MFMA) {
+    if (g.path == TP_PATH_MFMA && !mfma_spread(g, (int)b)) {
         // Measured: at b >= 16 the ring is faster as its own pass than in
         // the last-arriving split's epilogue (64 tokens, K_r = 2048, H = 4096:
-        // 20 us against 40 us).
+        // 20 us against 40 us); with the fix-up spread over all splits the
+        // epilogue carries it.
         tp_status s = launch_projection(p, g, (int)b, static_cast<const uint16_t*>(x),
                                         static_cast<const uint16_t*>(w), e, (hipStream_t)stream);
         if (s != TP_OK) return s;
