@@ -56,10 +56,23 @@ constexpr int kRouteMaxPerLane = 32;   // experts per lane in the routing wave (
 // ------------------------------------------------------------- routing --
 
 // (value, index) arg-max over the wave: larger value wins, ties go to the
-// lower index. Every lane ends with the same pair.
+// lower index. Every lane ends with the same pair. The combine is
+// associative and commutative, so any pairing of lane groups gives the same
+// result: within rows of 16 lanes the partners come from DPP permutes
+// (quads, then half-rows and rows mirrored), across rows from two shuffles.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& e) {
+    const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    const int oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
+    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& e) {
+    argmax_dpp<0xB1>(v, e);   // quad_perm 1,0,3,2
+    argmax_dpp<0x4E>(v, e);   // quad_perm 2,3,0,1
+    argmax_dpp<0x141>(v, e);  // row_half_mirror: quad 0 with quad 1 of each half-row
+    argmax_dpp<0x140>(v, e);  // row_mirror: the two half-rows
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
+    for (int m = 16; m < 64; m <<= 1) {
         const float ov = __shfl_xor(v, m);
         const int oe = __shfl_xor(e, m);
         if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
