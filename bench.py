@@ -298,10 +298,10 @@ def moe_run(args, w, tune):
     config = {"workload": w.name, "hidden": H, "k_attn": w.k_attn, "n_ranks": w.n_ranks,
               "rank": rank, "tokens": T, "n_experts": E, "top_k": k, "ep": ep, "moe_inter": I,
               "layers": 1, "active_local_experts_mean": active_total / copies,
-              "weight_layout": "row-major attention slice, pair-row packed experts",
+              "weight_layout": "row-major attention slice, experts packed as MFMA tiles",
               "weight_copies_rotated": copies}
-    kernel = ("MoE layer share (attention slice MFMA + ring sum, routing, expert GEMV, "
-              "combine + ring sum)")
+    kernel = ("MoE layer share (attention slice: MFMA projection with the ring sum in its split-K "
+              "fix-up; routing; expert MFMA GEMV; combine + ring sum)")
     extra = {}
     return ms, T, step_bytes, kernel, config, cpu, extra
 
