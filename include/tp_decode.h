@@ -351,9 +351,9 @@ tp_status tp_moe_pack_experts(tp_plan_t plan, const void* w_local, void* w_packe
  * Each projection accumulates in fp32 (fixed order); the combine adds the
  * local experts' weighted rows in ascending expert order. Experts that no
  * token selected are not read. Expert ids outside this rank's range are
- * skipped. Uses the workspace (pair table and per-selection rows).
+ * skipped. Uses the workspace (one projected row per selection).
  * TP_ERR_UNSUPPORTED if moe_inter is not a multiple of 8, hidden not a
- * multiple of 16, one expert's packed tiles reach 2 GiB, or E/ep > 8192.
+ * multiple of 16, or one expert's packed tiles reach 2 GiB.
  */
 tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                          const float* sel_weight, int32_t tokens, const void* u,

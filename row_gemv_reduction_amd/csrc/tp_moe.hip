@@ -16,23 +16,21 @@
 //   moe_route      one wave per token: softmax over the experts' logits (in
 //                  double), top_k by logit with ties to the lower index,
 //                  optional renormalisation, listed in ascending expert order.
-//   moe_table      one workgroup: the local pairs (token, selection) grouped
-//                  by local expert: counts, offsets and a slot per pair. The
-//                  order of pairs inside an expert's group only decides which
-//                  slot holds which row, never any arithmetic.
 //   moe_expert     one workgroup per (local expert, block of 8 16-column
-//                  strips): up to 16 of the expert's rows at a time as the
-//                  A operand of v_mfma_f32_16x16x32_bf16 (each weight tile is
-//                  read once per 16 rows; an expert has 4 rows on average),
-//                  the waves split the expert's K rows, their D tiles are
-//                  summed in LDS in wave order, and the rows' projections
-//                  land in Y[slot]. A dot-product (vector ALU) version of the
-//                  same GEMV spent more time in its multiply-adds than in
-//                  streaming the weights; the matrix cores take them off the
-//                  issue slots.
+//                  strips): the expert's rows are the (token, selection)
+//                  pairs that chose it, found by scanning the selections in
+//                  pair order (no table launch); up to 16 of them at a time
+//                  are the A operand of v_mfma_f32_16x16x32_bf16 (each weight
+//                  tile is read once per 16 rows; an expert has 4 rows on
+//                  average), the waves split the expert's K rows, their D
+//                  tiles are summed in LDS in wave order, and pair p's
+//                  projection lands in Y[p]. A dot-product (vector ALU)
+//                  version of the same GEMV spent more time in its
+//                  multiply-adds than in streaming the weights; the matrix
+//                  cores take them off the issue slots.
 //   moe_combine    part[t, n] = sum over the token's selections s, in order
-//                  (ascending expert), of weight * Y[slot(t, s), n] for the
-//                  local ones.
+//                  (ascending expert), of weight * Y[t * top_k + s, n] for
+//                  the local ones.
 //
 // Expert weights are packed once at load time as the matrix-core tiles of
 // the dense decode step (one expert per matrix):
@@ -161,78 +159,52 @@ route_fn route_kernel(int E) {
     return nullptr;
 }
 
-// ---------------------------------------------------------- pair table --
-
-struct MoeTable {
-    int32_t* off;       // [EL + 1] start of each local expert's slots
-    int32_t* slot;      // [T * k] slot of each pair, -1 if its expert is not local
-    int32_t* pair;      // [T * k] pair id (t * k + s) of each slot
-    float* y;           // [T * k][H] projection of each slot's row
-};
-
-__global__ __launch_bounds__(1024) void moe_table_kernel(const int32_t* __restrict__ sel_expert,
-                                                         int n_pairs, int e0, int EL, MoeTable tb) {
-    extern __shared__ int32_t cnt[];  // [EL] counts, then [EL] cursors
-    int32_t* cur = cnt + EL;
-    for (int e = threadIdx.x; e < EL; e += blockDim.x) cnt[e] = 0;
-    __syncthreads();
-    for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
-        const int le = sel_expert[p] - e0;
-        if (le >= 0 && le < EL) atomicAdd(&cnt[le], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < EL; ++e) {
-            tb.off[e] = run;
-            cur[e] = run;
-            run += cnt[e];
-        }
-        tb.off[EL] = run;
-    }
-    __syncthreads();
-    for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
-        const int ex = sel_expert[p];
-        const int le = ex - e0;
-        int s = -1;
-        if (le >= 0 && le < EL) {
-            s = atomicAdd(&cur[le], 1);
-            tb.pair[s] = p;
-        }
-        tb.slot[p] = s;  // ids of other ranks' experts (or invalid ids) are skipped
-    }
-}
-
 // ------------------------------------------------------- expert GEMV --
 
 struct ExpertArgs {
-    const uint16_t* u;       // [T][k][I] bf16, row of pair p at u + p * I
+    const uint16_t* u;       // [T][k][I] bf16, row of pair p = t * k + s at u + p * I
     const uint16_t* w;       // tiles [EL][S16][nkb][2][64][8]
-    MoeTable tb;
+    const int32_t* sel;      // [T * k] selected expert of each pair
+    float* y;                // [T * k][H] projection of each local pair's row
+    int32_t n_pairs, e0;     // pairs; global id of local expert 0
     int32_t H, S16, I, nkb;
     int32_t col_blocks;      // ceil(S16 / SB)
 };
 
 constexpr int kMoeTileBytes = 2048;  // 64 rows x 16 columns of bf16
 
-// One workgroup per (local expert, block of SB 16-column strips); a pass
-// takes up to 16 of the expert's rows (its slots, in table order) as the A
-// operand (token m = lane % 16). Wave w takes the row tiles kb = w, w + NW,
+// One workgroup per (local expert, block of SB 16-column strips). The
+// expert's rows are the pairs that selected it, in ascending pair order
+// (found by scanning the selections: ranks from wave ballots); a pass takes
+// up to 16 of them as the A operand (token m = lane % 16), and row p's
+// projection lands in Y[p] (so the combine needs no table). Wave w takes the row tiles kb = w, w + NW,
 // ... of the expert and, per tile, the block's SB strips in two register
 // banks of SL = SB/2 tiles, loading each A operand once per 64 rows and the
 // next tile's operands while it multiplies the current ones. The waves' D
-// tiles are then summed in wave order in LDS and the pass's rows land in
-// Y[slot]. Strips past the block's last and rows past the expert's read
+// tiles are then summed in wave order in LDS. Strips past the block's last and rows past the expert's read
 // zero (offsets past the buffer range); A operands of empty token slots and
 // of rows past I are zero.
 template <int SB, int NW>
 __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
     constexpr int SL = SB / 2;
+    constexpr int NT = NW * 64;
     __shared__ __align__(16) float red[NW * SB * 256];  // [NW][SB][64][4] D tiles
+    __shared__ int rows[16];                            // the pass's pairs
+    __shared__ int wcount[NW];
+    __shared__ int s_rows;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int le = blockIdx.x / a.col_blocks, cb = blockIdx.x % a.col_blocks;
-    const int q0 = a.tb.off[le], n_rows = a.tb.off[le + 1] - q0;
+    const int eg = a.e0 + le;
+    if (tid == 0) s_rows = 0;
+    __syncthreads();
+    {
+        int c = 0;
+        for (int p = tid; p < a.n_pairs; p += NT) c += a.sel[p] == eg;
+        if (c) atomicAdd(&s_rows, c);
+    }
+    __syncthreads();
+    const int n_rows = s_rows;
     if (n_rows == 0) return;  // expert not selected by any token: not read
     const int s0 = cb * SB;
     const int ns = a.S16 - s0 < SB ? a.S16 - s0 : SB;
@@ -245,8 +217,26 @@ __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
 
     for (int r0 = 0; r0 < n_rows; r0 += 16) {
         const int nr = n_rows - r0 < 16 ? n_rows - r0 : 16;
+        // the pass's rows: the expert's pairs of rank r0 .. r0 + 15
+        if (r0 > 0) __syncthreads();  // the previous pass has read rows
+        int base = 0;  // matches before the chunk
+        for (int c0 = 0; c0 < a.n_pairs && base < r0 + 16; c0 += NT) {
+            const int p = c0 + tid;
+            const bool hit = p < a.n_pairs && a.sel[p] == eg;
+            const uint64_t bal = __ballot(hit);
+            if (lane == 0) wcount[wave] = __popcll(bal);
+            __syncthreads();
+            int rank = base + __popcll(bal & ((1ull << lane) - 1)), total = base;
+            for (int w = 0; w < NW; ++w) {
+                rank += w < wave ? wcount[w] : 0;
+                total += wcount[w];
+            }
+            if (hit && rank >= r0 && rank < r0 + 16) rows[rank - r0] = p;
+            __syncthreads();  // wcount is rewritten by the next chunk
+            base = total;
+        }
         const int m = lane & 15;
-        const int pr = m < nr ? a.tb.pair[q0 + r0 + m] : -1;
+        const int pr = m < nr ? rows[m] : -1;
         const uint16_t* up = a.u + (int64_t)(pr < 0 ? 0 : pr) * a.I;
         // B operands of bank j (strips j*SL .. j*SL + SL - 1) of row tile kb (< 0: none)
         auto issue_w = [&](u32x4_t (&bv)[SL][2], int j, int kb) {
@@ -316,22 +306,24 @@ __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
             float v = red[s * 256 + e];
 #pragma unroll
             for (int w = 1; w < NW; ++w) v += red[(w * SB + s) * 256 + e];
-            a.tb.y[(int64_t)(q0 + r0 + row) * a.H + 16 * (s0 + s) + col] = v;
+            a.y[(int64_t)rows[row] * a.H + 16 * (s0 + s) + col] = v;
         }
     }
 }
 
 // ------------------------------------------------------------ combine --
 
-__global__ void moe_combine_kernel(const float* __restrict__ sel_weight, MoeTable tb, int tokens,
-                                   int top_k, int H, float* __restrict__ part) {
+__global__ void moe_combine_kernel(const int32_t* __restrict__ sel_expert, const float* __restrict__ sel_weight,
+                                   const float* __restrict__ y, int e0, int el, int tokens, int top_k, int H,
+                                   float* __restrict__ part) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)tokens * H) return;
     const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
     float acc = 0.f;
     for (int s = 0; s < top_k; ++s) {
-        const int q = tb.slot[t * top_k + s];
-        if (q >= 0) acc = __builtin_fmaf(sel_weight[t * top_k + s], tb.y[(int64_t)q * H + n], acc);
+        const int q = t * top_k + s;
+        const int le = sel_expert[q] - e0;
+        if (le >= 0 && le < el) acc = __builtin_fmaf(sel_weight[q], y[(int64_t)q * H + n], acc);
     }
     part[i] = acc;
 }
@@ -339,9 +331,11 @@ __global__ void moe_combine_kernel(const float* __restrict__ sel_weight, MoeTabl
 // The same combine, then the rank's partial to its slot and the ring-order
 // sum of the N ranks' values of the point plus the residual (lesson 9.9
 // "Interconnects e clusters", section 01 · Conceito), one element per thread.
-__global__ void moe_combine_ring_kernel(const float* __restrict__ sel_weight, MoeTable tb, int tokens,
-                                        int top_k, int H, float* __restrict__ slots, float* hidden,
-                                        int n_ranks, int rank, int64_t chunk) {
+__global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
+                                        const float* __restrict__ sel_weight, const float* __restrict__ y,
+                                        int e0, int el, int tokens, int top_k, int H,
+                                        float* __restrict__ slots, float* hidden, int n_ranks, int rank,
+                                        int64_t chunk) {
 #pragma clang fp contract(off)
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t len = (int64_t)tokens * H;
@@ -349,8 +343,9 @@ __global__ void moe_combine_ring_kernel(const float* __restrict__ sel_weight, Mo
     const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
     float acc = 0.f;
     for (int s = 0; s < top_k; ++s) {
-        const int q = tb.slot[t * top_k + s];
-        if (q >= 0) acc = __builtin_fmaf(sel_weight[t * top_k + s], tb.y[(int64_t)q * H + n], acc);
+        const int q = t * top_k + s;
+        const int le = sel_expert[q] - e0;
+        if (le >= 0 && le < el) acc = __builtin_fmaf(sel_weight[q], y[(int64_t)q * H + n], acc);
     }
     slots[(int64_t)rank * len + i] = acc;
     hidden[i] = ring_element(slots, len, i, chunk, n_ranks, rank, acc, hidden[i]);
@@ -374,19 +369,9 @@ const ExpertVariant kExpertVariants[] = {
     {16, 4, moe_expert_kernel<16, 4>},
 };
 
-MoeTable table_in(const tp_plan_s* p, void* ws) {
-    const int64_t pairs = (int64_t)p->max_tokens * p->top_k;
-    const int64_t el = p->n_experts / p->ep;
-    char* base = static_cast<char*>(ws) + tp_ws_moe_offset(p);
-    MoeTable t;
-    t.off = reinterpret_cast<int32_t*>(base);
-    base += (el + 1 + 63) / 64 * 256;
-    t.slot = reinterpret_cast<int32_t*>(base);
-    base += (pairs + 63) / 64 * 256;
-    t.pair = reinterpret_cast<int32_t*>(base);
-    base += (pairs + 63) / 64 * 256;
-    t.y = reinterpret_cast<float*>(base);
-    return t;
+// Projections of the pairs' rows, [T * k][H] fp32, in the workspace.
+float* moe_rows(const tp_plan_s* p, void* ws) {
+    return reinterpret_cast<float*>(static_cast<char*>(ws) + tp_ws_moe_offset(p));
 }
 
 }  // namespace
@@ -394,8 +379,7 @@ MoeTable table_in(const tp_plan_s* p, void* ws) {
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p) {
     if (!p->n_experts) return 0;
     const int64_t pairs = (int64_t)p->max_tokens * p->top_k;
-    const int64_t el = p->n_experts / p->ep;
-    return (el + 1 + 63) / 64 * 256 + 2 * ((pairs + 63) / 64 * 256) + pairs * p->hidden * 4;
+    return pairs * p->hidden * 4;
 }
 
 extern "C" {
@@ -429,27 +413,23 @@ tp_status tp_moe_pack_experts(tp_plan_t p, const void* w_local, void* w_packed, 
 
 namespace {
 
-// The rank's expert rows y (pair table, then the grouped GEMV) for tokens
-// 0 .. tokens-1; the caller combines them.
+// The projections of the local pairs' rows (the grouped GEMV) for tokens
+// 0 .. tokens-1, into moe_rows; the caller combines them.
 tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_expert, int32_t tokens,
-                      const void* u, const void* w_packed, void* ws, hipStream_t st, MoeTable* tb_out) {
+                      const void* u, const void* w_packed, void* ws, hipStream_t st) {
     const int64_t I = p->moe_inter, H = p->hidden, el = p->n_experts / p->ep;
     if (I % 8 || H % 16) return TP_ERR_UNSUPPORTED;
     const int64_t S16 = H / 16, nkb = (I + 63) / 64;
     const ExpertVariant v = kExpertVariants[p->moe_variant > 0 ? p->moe_variant - 1 : 0];
-    if (el * 8 > 64 * 1024) return TP_ERR_UNSUPPORTED;
     if (S16 * nkb * kMoeTileBytes >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
-    MoeTable tb = table_in(p, ws);
-    *tb_out = tb;
     if (tokens == 0) return TP_OK;
-    const int n_pairs = tokens * p->top_k;
-    hipLaunchKernelGGL(moe_table_kernel, dim3(1), dim3(1024), (unsigned)(el * 8), st, sel_expert,
-                       n_pairs, (int)(rank * el), (int)el, tb);
-    if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
     ExpertArgs a;
     a.u = static_cast<const uint16_t*>(u);
     a.w = static_cast<const uint16_t*>(w_packed);
-    a.tb = tb;
+    a.sel = sel_expert;
+    a.y = moe_rows(p, ws);
+    a.n_pairs = tokens * p->top_k;
+    a.e0 = (int32_t)(rank * el);
     a.H = (int32_t)H;
     a.S16 = (int32_t)S16;
     a.I = (int32_t)I;
@@ -474,12 +454,12 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
         !aligned16(part) || !aligned16(ws))
         return TP_ERR_ALIGNMENT;
     hipStream_t st = (hipStream_t)stream;
-    MoeTable tb;
-    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st, &tb);
+    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st);
     if (s != TP_OK || tokens == 0) return s;
-    const int64_t H = p->hidden, n_out = (int64_t)tokens * H;
+    const int64_t H = p->hidden, n_out = (int64_t)tokens * H, el = p->n_experts / p->ep;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st,
-                       sel_weight, tb, (int)tokens, (int)p->top_k, (int)H, part);
+                       sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
+                       (int)p->top_k, (int)H, part);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
@@ -496,14 +476,13 @@ tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, co
         !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
         return TP_ERR_ALIGNMENT;
     hipStream_t st = (hipStream_t)stream;
-    MoeTable tb;
     const int32_t tokens = p->batch;
-    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st, &tb);
+    tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st);
     if (s != TP_OK) return s;
-    const int64_t H = p->hidden, len = (int64_t)tokens * H;
+    const int64_t H = p->hidden, len = (int64_t)tokens * H, el = p->n_experts / p->ep;
     hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st,
-                       sel_weight, tb, (int)tokens, (int)p->top_k, (int)H, slots, hidden,
-                       (int)p->n_ranks, (int)rank, len / p->n_ranks);
+                       sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
+                       (int)p->top_k, (int)H, slots, hidden, (int)p->n_ranks, (int)rank, len / p->n_ranks);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
