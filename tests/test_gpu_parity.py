@@ -93,6 +93,23 @@ def test_partial_split_counts_and_determinism(splits):
     assert_partial_close(a, oracle.partial(x, W)[0], "splits=%d" % splits)
 
 
+@pytest.mark.parametrize("splits", [8, 9])
+def test_partial_mfma_fixups(splits):
+    """64 tokens over 32 column tiles: 8 splits (256 workgroups) fit on the
+    device at once and spread the split-K fix-up over all splits; 9 splits
+    (288) fall back to the last arrival summing each tile."""
+    hidden, k, batch = 4096, 2304, 64
+    say("mfma fix-up splits=%d" % splits)
+    plan = tp.Plan(hidden, k, 1, batch, tune={"splits_ffn": splits})
+    assert plan.info()["splits"][1] == splits
+    x = synth.normal_bf16((batch, k), 1.0, seed=4, tensor="x")
+    W = synth.normal_bf16((k, hidden), synth.WEIGHT_STD, seed=4, tensor="w")
+    a = run_partial(plan, 1, x, W)
+    b = run_partial(plan, 1, x, W)
+    assert_bits_equal(a, b, "repeat run")
+    assert_partial_close(a, oracle.partial(x, W)[0], "splits=%d" % splits)
+
+
 @pytest.mark.parametrize("cols", [128, 256, 512])
 def test_partial_column_tilings(cols):
     hidden, k, batch = 1544, 700, 2
@@ -243,8 +260,12 @@ def test_decode_equals_partial_then_ring_bitwise():
 
 
 @pytest.mark.parametrize("n,b,h,ka,ki,rank", [(4, 3, 1032, 512, 1536, 2), (2, 16, 520, 640, 1376, 1),
-                                              (8, 64, 1024, 2048, 4096, 6), (1, 5, 64, 64, 128, 0)])
+                                              (8, 64, 1024, 2048, 4096, 6), (1, 5, 64, 64, 128, 0),
+                                              (4, 64, 4096, 8192, 9216, 2)])
 def test_decode_point_equals_partial_then_ring_bitwise(n, b, h, ka, ki, rank):
+    """The last case: the attention point (K_r 2048, 8 splits x 32 column
+    tiles) carries the ring in its spread fix-up, the FFN point (K_r 2304,
+    9 splits: too many workgroups to be resident at once) does not."""
     L = 1
     say("decode point n=%d b=%d h=%d" % (n, b, h))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 9, rank)
