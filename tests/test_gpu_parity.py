@@ -259,17 +259,17 @@ def test_decode_equals_partial_then_ring_bitwise():
     assert_bits_equal(host(hd), h_gpu, "hidden")
 
 
-@pytest.mark.parametrize("n,b,h,ka,ki,rank", [(4, 3, 1032, 512, 1536, 2), (2, 16, 520, 640, 1376, 1),
-                                              (8, 64, 1024, 2048, 4096, 6), (1, 5, 64, 64, 128, 0),
-                                              (4, 64, 4096, 8192, 9216, 2)])
-def test_decode_point_equals_partial_then_ring_bitwise(n, b, h, ka, ki, rank):
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,ffn_splits", [
+    (4, 3, 1032, 512, 1536, 2, 0), (2, 16, 520, 640, 1376, 1, 0), (8, 64, 1024, 2048, 4096, 6, 0),
+    (1, 5, 64, 64, 128, 0, 0), (4, 64, 4096, 8192, 9216, 2, 9)])
+def test_decode_point_equals_partial_then_ring_bitwise(n, b, h, ka, ki, rank, ffn_splits):
     """The last case: the attention point (K_r 2048, 8 splits x 32 column
-    tiles) carries the ring in its spread fix-up, the FFN point (K_r 2304,
-    9 splits: too many workgroups to be resident at once) does not."""
+    tiles) carries the ring in its spread fix-up; the FFN point, forced to 9
+    splits (288 workgroups, more than can be resident at once), does not."""
     L = 1
     say("decode point n=%d b=%d h=%d" % (n, b, h))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 9, rank)
-    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"splits_ffn": ffn_splits} if ffn_splits else None)
     ws = plan.new_workspace()
     for pt, (x, w) in enumerate(((xa[0], wo[0]), (xf[0], wd[0]))):
         # fused point
