@@ -37,11 +37,13 @@
 //     consuming one bank never waits for the other. Tokens past b and rows
 //     past K read zero. At a segment's end a wave stores its D tiles to LDS,
 //     counts itself and streams on (no barrier).
-//   - one control wave takes the segments in order: sums the waves' D tiles
-//     in wave order; a contributor publishes that partial; an owner adds the
-//     contributor's partial (its own rows first), writes the rank's partial
-//     to its slot and forms the ring-order sum with the other ranks' values
-//     (staged into LDS a point ahead with direct global->LDS loads) plus the
+//   - a reducer wave sums each segment's D tiles in wave order into one of
+//     two LDS partial buffers and frees the D-tile buffer at once;
+//   - the control wave takes the segments' partials in order: a contributor
+//     publishes its partial; an owner adds the contributor's partial (its
+//     own rows first), writes the rank's partial to its slot and forms the
+//     ring-order sum with the other ranks' values (staged into LDS a point
+//     ahead by two stager waves with direct global->LDS loads) plus the
 //     residual, which stays in LDS for the whole step.
 // Point order: as decode_stream's default (each hidden-state element follows
 // its own chain, kept by the strip's owner; no grid-wide synchronisation).
@@ -215,13 +217,14 @@ __device__ __forceinline__ void wait_flag(const int* f, int target, uint32_t* er
 // e + 1 once it has read their tiles, which frees the buffer for segment
 // e + NBUF. So a wave waits for its slowest sibling only when it is NBUF
 // segments ahead of it.
-constexpr int kFlagArrived = 0, kFlagConsumed = 4, kFlagStaged = 5, kFlagOthFree = 7, kFlagCount = 8;
+constexpr int kFlagArrived = 0, kFlagConsumed = 4, kFlagStaged = 5, kFlagOthFree = 7, kFlagReduced = 8,
+              kFlagDone = 9, kFlagCount = 10;
 template <int BT, int SL, int WPS, int NSTG, int NBUF>
 __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     constexpr int kRed = WPS * BT * 256;                  // floats of one buffer
     __shared__ __align__(16) float red[NBUF * kRed];       // [NBUF][WPS][BT][64][4] D tiles
     __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, [token][16]
-    __shared__ __align__(16) float vr[BT * 256];           // a segment's partial, [token][16]
+    __shared__ __align__(16) float vr[2 * BT * 256];       // segment e's partial in vr[e & 1], [token][16]
     // LDS flags: arrivals per D-tile buffer, segments consumed, stagers done
     // per parity of point, points whose other values have been read
     __shared__ int flags[kFlagCount];
@@ -252,11 +255,48 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     }
 
     if (wave == 0) {
+        // ---------------------------------------------------- reducer wave
+        // Sums each segment's D tiles in wave order into vr[e & 1] as
+        // [token][16 columns] (lane l of a D tile holds tokens 16tt +
+        // 4(l/16) + k of column l % 16) and frees the D-tile buffer at once;
+        // the control wave takes the partial from there, so the compute
+        // waves never wait on the ring.
+        __builtin_amdgcn_s_setprio(3);
+        __syncthreads();  // start
+        int e = 0;
+        for (int j = 0; j < n_points; ++j) {
+            const int ns = nseg[j & 1];
+            for (int i = 0; i < ns; ++i, ++e) {
+                wait_flag(&flags[kFlagArrived + e % NBUF], (e / NBUF + 1) * WPS, a.err);
+                wait_flag(&flags[kFlagDone], e - 1, a.err);  // vr[e & 1] was read for segment e - 2
+                lds_wait();
+                const float* re = red + (e % NBUF) * kRed;
+                float* ve = vr + (e & 1) * BT * 256;
+#pragma unroll
+                for (int tt = 0; tt < BT; ++tt) {
+                    floatx4_t part[WPS];
+#pragma unroll
+                    for (int wi = 0; wi < WPS; ++wi)
+                        part[wi] = *reinterpret_cast<const floatx4_t*>(re + (wi * BT + tt) * 256 + lane * 4);
+                    floatx4_t v = part[0];
+#pragma unroll
+                    for (int wi = 1; wi < WPS; ++wi) v = v + part[wi];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) ve[(16 * tt + 4 * (lane >> 4) + k) * 16 + (lane & 15)] = v[k];
+                }
+                lds_wait();
+                if (lane == 0) {
+                    lds_st(&flags[kFlagConsumed], e + 1);  // its D-tile buffer is free again
+                    lds_st(&flags[kFlagReduced], e + 1);
+                }
+            }
+        }
+    } else if (wave == 1) {
         // ---------------------------------------------------- control wave
         // Works in the [token][16 columns] layout: lane l takes token
         // 16tt + l/4 and columns 4(l%4) .. +3 of a strip (16-byte LDS and
         // global accesses throughout).
-        __builtin_amdgcn_s_setprio(3);
+        __builtin_amdgcn_s_setprio(2);
         const int tl = lane >> 2, c4 = 4 * (lane & 3);
         for (int o = 0; o < nown; ++o)
 #pragma unroll
@@ -281,26 +321,9 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             bool staged = false;
             for (int i = 0; i < ns; ++i, ++e) {
                 const int s = segtab[t][i][0], role = segtab[t][i][3];
-                wait_flag(&flags[kFlagArrived + e % NBUF], (e / NBUF + 1) * WPS, a.err);
+                wait_flag(&flags[kFlagReduced], e + 1, a.err);  // segment e's partial is in vr[e & 1]
                 lds_wait();
-                // the segment's partial: the waves' D tiles summed in wave order,
-                // stored to vr as [token][16 columns] (lane l of a D tile holds
-                // tokens 16tt + 4(l/16) + k of column l % 16)
-                const float* re = red + (e % NBUF) * kRed;
-#pragma unroll
-                for (int tt = 0; tt < BT; ++tt) {
-                    floatx4_t part[WPS];
-#pragma unroll
-                    for (int wi = 0; wi < WPS; ++wi)
-                        part[wi] = *reinterpret_cast<const floatx4_t*>(re + (wi * BT + tt) * 256 + lane * 4);
-                    floatx4_t v = part[0];
-#pragma unroll
-                    for (int wi = 1; wi < WPS; ++wi) v = v + part[wi];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) vr[(16 * tt + 4 * (lane >> 4) + k) * 16 + (lane & 15)] = v[k];
-                }
-                lds_wait();
-                if (lane == 0) lds_st(&flags[kFlagConsumed], e + 1);  // its D-tile buffer is free again
+                float* ve = vr + (e & 1) * BT * 256;
                 // exchange buffer of this kind of point and strip: slot (j/2) mod R,
                 // last used at point j - 2R
                 const int jj = j >> 1;
@@ -315,9 +338,12 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 #pragma unroll
                     for (int tt = 0; tt < BT; ++tt)
                         st_dev4(rx, xoff + (uint32_t)((tt * 64 + lane) * 16),
-                                *reinterpret_cast<const floatx4_t*>(vr + tt * 256 + lane * 4));
+                                *reinterpret_cast<const floatx4_t*>(ve + tt * 256 + lane * 4));
                     wait_mem();
-                    if (lane == 0) st_dev_u32(pub, (uint32_t)(j + 1));
+                    if (lane == 0) {
+                        st_dev_u32(pub, (uint32_t)(j + 1));
+                        lds_st(&flags[kFlagDone], e + 1);  // vr[e & 1] may be refilled
+                    }
                     continue;
                 }
                 if (role == kOwnerPart) {
@@ -333,7 +359,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     if (lane == 0) st_dev_u32(ack, (uint32_t)(j + 1));
 #pragma unroll
                     for (int tt = 0; tt < BT; ++tt) {
-                        float* vp = vr + tt * 256 + lane * 4;
+                        float* vp = ve + tt * 256 + lane * 4;
                         *reinterpret_cast<floatx4_t*>(vp) = *reinterpret_cast<const floatx4_t*>(vp) + c[tt];
                     }
                 }
@@ -356,7 +382,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 #pragma clang fp contract(off)
                     const int tok = 16 * tt + tl;
                     const int tokc = tok < B ? tok : B - 1;
-                    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(vr + tt * 256 + lane * 4);
+                    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(ve + tt * 256 + lane * 4);
                     const floatx4_t h = *reinterpret_cast<const floatx4_t*>(hso + tt * 256 + lane * 4);
                     const float* ob = oj + tokc * 16 + c4;
                     const int idx = tokc * a.H + 16 * s + c4;
@@ -409,6 +435,8 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                         *reinterpret_cast<floatx4_t*>(slot + (int64_t)tok * a.H + 16 * s + c4) = v;
                     }
                 }
+                lds_wait();
+                if (lane == 0) lds_st(&flags[kFlagDone], e + 1);  // vr[e & 1] may be refilled
             }
             // the other values of point j have been read: their buffer may be refilled (point j + 2)
             lds_wait();
@@ -424,13 +452,13 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                         *reinterpret_cast<const floatx4_t*>(hs + (o * BT + tt) * 256 + lane * 4);
             }
         wait_mem();
-    } else if (wave <= NSTG) {
+    } else if (wave <= 1 + NSTG) {
         // ---------------------------------------------------- stager waves
         // The other ranks' 16 values per token of each owned strip, rows
         // ordered (other rank, token), staged with direct global->LDS loads
         // into oth[j & 1] a point ahead; stager q issues every NSTG-th load.
         // These waves issue nothing else, so their memory waits are short.
-        const int q = wave - 1;
+        const int q = wave - 2;
         __syncthreads();  // start
         const int rows = (a.n_ranks - 1) * B;
         const int per_strip = (rows + 15) / 16;
@@ -453,7 +481,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
         }
     } else {
         // --------------------------------------------------- compute waves
-        const int wi = wave - 1 - NSTG;
+        const int wi = wave - 2 - NSTG;
         __syncthreads();  // start: the segment tables are in LDS
         auto set_seg = [&](Cursor& c) {
             if (c.j >= n_points) return;
@@ -594,12 +622,12 @@ typedef void (*mfma_stream_fn)(MfmaArgs);
 // Tiles per bank: fewer for more token blocks (each tile also carries 2*BT
 // A operands), so the banks fit the registers. The waves of a workgroup are
 // spread over the CU's four SIMDs in turn, and on each SIMD the oldest wave
-// is served first: with one control or stager wave per SIMD and the same
+// is served first: with one reducer, control or stager wave per SIMD and the same
 // number of compute waves on every SIMD (12, or 8 for three and four token
 // blocks, where the LDS of their D tiles is short), no SIMD carries more of
 // the stream than another. D-tile buffers: 4, or fewer where the LDS is short.
 constexpr int kWps[5] = {0, 12, 12, 8, 8};
-constexpr int kStagers[5] = {0, 3, 3, 3, 3};
+constexpr int kStagers[5] = {0, 2, 2, 2, 2};
 constexpr int kDBufs[5] = {0, 4, 3, 2, 2};  // D-tile buffers (LDS)
 mfma_stream_fn mfma_stream_kernel(int bt) {
     switch (bt) {
@@ -650,7 +678,7 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     g->oth_strip = (int32_t)(((p->n_ranks > 1 ? p->n_ranks - 1 : 1) * b * 16 + 255) / 256 * 256);
     g->own_max = own_max;
     g->lds_bytes = 2 * own_max * g->oth_strip * 4;
-    const int64_t stat = (kDBufs[bt] * wps * bt * 256 + kMaxOwn * bt * 256 + bt * 256) * 4 + 1024;
+    const int64_t stat = (kDBufs[bt] * wps * bt * 256 + kMaxOwn * bt * 256 + 2 * bt * 256) * 4 + 1024;
     if (g->lds_bytes + stat > 152 * 1024) return false;
     // the largest buffer offsets must fit 32 bits
     if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes * bt >= ((int64_t)1 << 31)) return false;
@@ -658,7 +686,7 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     g->grid = (int32_t)G;
     g->wps = wps;
     g->bt = bt;
-    g->block = (1 + nstg + wps) * 64;
+    g->block = (2 + nstg + wps) * 64;
     g->nkb0 = (int32_t)nkb0;
     g->nkb1 = (int32_t)nkb1;
     return true;
