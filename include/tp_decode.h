@@ -151,10 +151,17 @@ tp_status tp_workspace_init(tp_plan_t plan, void* workspace, void* stream);
 
 /*
  * Read the workspace's error word (synchronous: waits for the device).
- * *flags = 0 after successful calls. Bit 0 is set if a decode step's
- * bounded wait for the previous reconciliation point timed out (the step
- * then drains without completing and its outputs are not valid).
- * tp_workspace_init clears it.
+ * *flags = 0 after successful calls. Bit 0 is set if a bounded wait between
+ * workgroups timed out: a decode step's wait for the previous
+ * reconciliation point, a matrix-core stream's wait for a cut strip's other
+ * piece, or a matrix-core projection's wait for its column tile's other
+ * split-K partials (bit 1: a wait between the waves of one workgroup). The
+ * launch then drains without completing and its outputs are not valid.
+ * Those waits assume that all of the launch's workgroups are resident at
+ * once, which the library checks against the device's occupancy before it
+ * launches; other work holding compute units for longer than a wait's
+ * bound (about a million polls of the flag, well over 0.1 s) can still make
+ * it time out. tp_workspace_init clears the word.
  */
 tp_status tp_workspace_status(tp_plan_t plan, const void* workspace, int32_t* flags);
 
