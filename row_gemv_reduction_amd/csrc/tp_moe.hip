@@ -313,42 +313,81 @@ __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
 
 // ------------------------------------------------------------ combine --
 
-__global__ void moe_combine_kernel(const int32_t* __restrict__ sel_expert, const float* __restrict__ sel_weight,
-                                   const float* __restrict__ y, int e0, int el, int tokens, int top_k, int H,
-                                   float* __restrict__ part) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)tokens * H) return;
-    const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
-    float acc = 0.f;
+// Four columns per thread (H is a multiple of 16): each element sums the
+// token's local selections in order, as one fused multiply-add each.
+__device__ __forceinline__ floatx4_t combine4(const int32_t* __restrict__ sel_expert,
+                                              const float* __restrict__ sel_weight,
+                                              const float* __restrict__ y, int e0, int el, int t,
+                                              int top_k, int H, int n) {
+    floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < top_k; ++s) {
         const int q = t * top_k + s;
         const int le = sel_expert[q] - e0;
-        if (le >= 0 && le < el) acc = __builtin_fmaf(sel_weight[q], y[(int64_t)q * H + n], acc);
+        if (le >= 0 && le < el) {
+            const float w = sel_weight[q];
+            const floatx4_t yv = *reinterpret_cast<const floatx4_t*>(y + (int64_t)q * H + n);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(w, yv[k], acc[k]);
+        }
     }
-    part[i] = acc;
+    return acc;
+}
+
+__global__ void moe_combine_kernel(const int32_t* __restrict__ sel_expert, const float* __restrict__ sel_weight,
+                                   const float* __restrict__ y, int e0, int el, int tokens, int top_k, int H,
+                                   float* __restrict__ part) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int H4 = H / 4;
+    if (v >= (int64_t)tokens * H4) return;
+    const int t = (int)(v / H4), n = 4 * (int)(v - (int64_t)t * H4);
+    *reinterpret_cast<floatx4_t*>(part + (int64_t)t * H + n) =
+        combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
 }
 
 // The same combine, then the rank's partial to its slot and the ring-order
 // sum of the N ranks' values of the point plus the residual (lesson 9.9
-// "Interconnects e clusters", section 01 · Conceito), one element per thread.
+// "Interconnects e clusters", section 01 · Conceito). Four elements per
+// thread: where they lie in one ring chunk (chunk a multiple of 4) the
+// ranks' values come as 16-byte loads, all issued before the first add;
+// otherwise element by element.
 __global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
                                         const float* __restrict__ sel_weight, const float* __restrict__ y,
                                         int e0, int el, int tokens, int top_k, int H,
                                         float* __restrict__ slots, float* hidden, int n_ranks, int rank,
                                         int64_t chunk) {
 #pragma clang fp contract(off)
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t len = (int64_t)tokens * H;
-    if (i >= len) return;
-    const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
-    float acc = 0.f;
-    for (int s = 0; s < top_k; ++s) {
-        const int q = t * top_k + s;
-        const int le = sel_expert[q] - e0;
-        if (le >= 0 && le < el) acc = __builtin_fmaf(sel_weight[q], y[(int64_t)q * H + n], acc);
+    const int H4 = H / 4;
+    if (v >= (int64_t)tokens * H4) return;
+    const int t = (int)(v / H4), n = 4 * (int)(v - (int64_t)t * H4);
+    const int64_t i = (int64_t)t * H + n;
+    const floatx4_t acc = combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
+    *reinterpret_cast<floatx4_t*>(slots + (int64_t)rank * len + i) = acc;
+    const floatx4_t res = *reinterpret_cast<const floatx4_t*>(hidden + i);
+    floatx4_t out;
+    if (chunk % 4 == 0) {
+        const int c = (int)(i / chunk);
+        floatx4_t sum = acc;
+        for (int u0 = 0; u0 < n_ranks; u0 += 8) {
+            floatx4_t x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                int r = c + (u0 + u < n_ranks ? u0 + u : n_ranks - 1);
+                r = r >= n_ranks ? r - n_ranks : r;
+                x[u] = r == rank ? acc : *reinterpret_cast<const floatx4_t*>(slots + (int64_t)r * len + i);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u0 + u < n_ranks) sum = u0 + u == 0 ? x[u] : sum + x[u];
+        }
+        out = sum + res;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            out[k] = ring_element(slots, len, i + k, chunk, n_ranks, rank, acc[k], res[k]);
     }
-    slots[(int64_t)rank * len + i] = acc;
-    hidden[i] = ring_element(slots, len, i, chunk, n_ranks, rank, acc, hidden[i]);
+    *reinterpret_cast<floatx4_t*>(hidden + i) = out;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -457,7 +496,7 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
     tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st);
     if (s != TP_OK || tokens == 0) return s;
     const int64_t H = p->hidden, n_out = (int64_t)tokens * H, el = p->n_experts / p->ep;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out / 4 + 255) / 256)), dim3(256), 0, st,
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
                        (int)p->top_k, (int)H, part);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
@@ -480,7 +519,7 @@ tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, co
     tp_status s = moe_experts(p, rank, sel_expert, tokens, u, w_packed, ws, st);
     if (s != TP_OK) return s;
     const int64_t H = p->hidden, len = (int64_t)tokens * H, el = p->n_experts / p->ep;
-    hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len / 4 + 255) / 256)), dim3(256), 0, st,
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
                        (int)p->top_k, (int)H, slots, hidden, (int)p->n_ranks, (int)rank, len / p->n_ranks);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
