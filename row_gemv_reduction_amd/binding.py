@@ -132,6 +132,7 @@ class Plan:
         h = ctypes.c_void_p()
         _check(_lib().tp_plan(hidden, inter, n_ranks, batch, ctypes.byref(h)), "tp_plan")
         self._h = h
+        self._info = None  # tp_plan_info, read once per state of the plan
         try:
             if k_attn is not None:
                 _check(_lib().tp_plan_set_attn_dim(h, k_attn), "tp_plan_set_attn_dim")
@@ -147,6 +148,7 @@ class Plan:
 
     def tune(self, key, value):
         """Set a tuning knob (tp_plan_tune)."""
+        self._info = None
         _check(_lib().tp_plan_tune(self.handle, key.encode(), int(value)), "tp_plan_tune(%s)" % key)
 
     @property
@@ -156,17 +158,25 @@ class Plan:
         return self._h
 
     def info(self) -> dict:
-        i = tp_plan_info()
-        _check(_lib().tp_plan_info_get(self.handle, ctypes.byref(i)), "tp_plan_info_get")
-        d = {}
-        for name, _ in tp_plan_info._fields_:
-            v = getattr(i, name)
-            d[name] = list(v) if hasattr(v, "__len__") else v
-        return d
+        """tp_plan_info as a dict (a copy the caller may change)."""
+        return {k: (list(v) if isinstance(v, list) else v) for k, v in self._plan_info().items()}
+
+    def _plan_info(self) -> dict:
+        # The binding's calls read the plan's info on every call; it only
+        # changes with tune(), so it is fetched once per state.
+        if self._info is None:
+            i = tp_plan_info()
+            _check(_lib().tp_plan_info_get(self.handle, ctypes.byref(i)), "tp_plan_info_get")
+            d = {}
+            for name, _ in tp_plan_info._fields_:
+                v = getattr(i, name)
+                d[name] = list(v) if hasattr(v, "__len__") else v
+            self._info = d
+        return self._info
 
     def new_workspace(self, device="cuda"):
         """Allocate (torch) and prepare a workspace for this plan."""
-        nbytes = max(self.info()["workspace_bytes"], 256)
+        nbytes = max(self._plan_info()["workspace_bytes"], 256)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         tp_workspace_init(self, ws)
         return ws
@@ -200,7 +210,7 @@ def tp_workspace_status(plan: Plan, workspace) -> int:
 
 
 def tp_rowparallel_partial(plan: Plan, point, x, w, p, workspace):
-    i = plan.info()
+    i = plan._plan_info()
     b, H, kr = i["batch"], i["hidden"], i["k_rank"][point] if point in (0, 1) else -1
     if point not in (0, 1):
         raise ValueError("point must be 0 (attention out) or 1 (FFN down)")
@@ -213,7 +223,7 @@ def tp_rowparallel_partial(plan: Plan, point, x, w, p, workspace):
 
 
 def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):
-    i = plan.info()
+    i = plan._plan_info()
     n, b, H = i["n_ranks"], i["batch"], i["hidden"]
     ob = None if out_bf16 is None else _dev(out_bf16, "out_bf16", torch.bfloat16, (b, H))
     _check(_lib().tp_ring_reduce(plan.handle, _dev(partials, "partials", torch.float32, (n, b, H)),
@@ -224,7 +234,7 @@ def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):
 
 def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slots, hidden,
                      workspace):
-    i = plan.info()
+    i = plan._plan_info()
     n, b, H = i["n_ranks"], i["batch"], i["hidden"]
     ka, ki = i["k_rank"]
     L = n_layers
@@ -242,7 +252,7 @@ def tp_decode_layers(plan: Plan, n_layers, rank, x_attn, w_o, x_ffn, w_down, slo
 
 def tp_decode_point(plan: Plan, point, rank, x, w, slots, hidden, workspace):
     """One reconciliation point: partial into slots[rank], then hidden <- ring_sum(slots) + hidden."""
-    i = plan.info()
+    i = plan._plan_info()
     if point not in (0, 1):
         raise ValueError("point must be 0 (attention out) or 1 (FFN down)")
     n, b, H, kr = i["n_ranks"], i["batch"], i["hidden"], i["k_rank"][point]
@@ -259,7 +269,7 @@ def packed_shape(plan: Plan, point, n_layers):
     pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/64), 2, 64, 8]."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
-    i = plan.info()
+    i = plan._plan_info()
     kr, H = i["k_rank"][point], i["hidden"]
     if i["packed_kind"] == 1:
         return (n_layers, H // 4, (kr + 1) // 2, 8)
@@ -274,7 +284,7 @@ def packed_act_shape(plan: Plan, point, n_layers):
     [L, ceil(K_r/64), ceil(b/16), 2, 64, 8] (MFMA tiles)."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
-    i = plan.info()
+    i = plan._plan_info()
     kr, b = i["k_rank"][point], i["batch"]
     if i["packed_kind"] == 1:
         return (n_layers, b, kr)
@@ -285,7 +295,7 @@ def packed_act_shape(plan: Plan, point, n_layers):
 
 def tp_pack_activations(plan: Plan, x_attn, x_ffn, xa_packed, xf_packed):
     """Lay a step's activation slices [L, b, K_r] out as packed_act_shape() (tp_pack_activations)."""
-    i = plan.info()
+    i = plan._plan_info()
     b = i["batch"]
     ka, ki = i["k_rank"]
     L = x_attn.shape[0]
@@ -299,7 +309,7 @@ def tp_pack_activations(plan: Plan, x_attn, x_ffn, xa_packed, xf_packed):
 def tp_pack_weights(plan: Plan, point, w, w_packed):
     """Pack a stack of row-major weight slices [L, K_r, H] -> packed_shape()."""
     shape = packed_shape(plan, point, w.shape[0])
-    L, kr, H = shape[0], plan.info()["k_rank"][point], plan.info()["hidden"]
+    L, kr, H = shape[0], plan._plan_info()["k_rank"][point], plan._plan_info()["hidden"]
     _check(_lib().tp_pack_weights(plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, kr, H)),
                                   _dev(w_packed, "w_packed", torch.bfloat16, shape),
                                   _stream()), "tp_pack_weights")
@@ -308,7 +318,7 @@ def tp_pack_weights(plan: Plan, point, w, w_packed):
 def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
                             slots, hidden, workspace):
     """The streamed decode step; x_attn / x_ffn as tp_pack_activations lays them out."""
-    i = plan.info()
+    i = plan._plan_info()
     n, b, H = i["n_ranks"], i["batch"], i["hidden"]
     ka, ki = i["k_rank"]
     L = n_layers
@@ -326,7 +336,7 @@ def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ff
 
 
 def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):
-    i = plan.info()
+    i = plan._plan_info()
     t = logits.shape[0]
     k, e = i["top_k"], i["n_experts"]
     _check(_lib().tp_moe_route(plan.handle, _dev(logits, "logits", torch.float32, (t, e)), t,
@@ -339,12 +349,12 @@ def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):
 def moe_packed_shape(plan: Plan):
     """Shape of a rank's packed experts: [E/ep, H/16, ceil(moe_inter/64), 1024]
     (2 KB matrix-core tiles of 64 rows x 16 columns)."""
-    i = plan.info()
+    i = plan._plan_info()
     return (i["local_experts"], i["hidden"] // 16, (i["moe_inter"] + 63) // 64, 1024)
 
 
 def tp_moe_pack_experts(plan: Plan, w_local, w_packed):
-    i = plan.info()
+    i = plan._plan_info()
     le, mi, H = i["local_experts"], i["moe_inter"], i["hidden"]
     _check(_lib().tp_moe_pack_experts(plan.handle, _dev(w_local, "w_local", torch.bfloat16, (le, mi, H)),
                                       _dev(w_packed, "w_packed", torch.bfloat16, moe_packed_shape(plan)),
@@ -352,7 +362,7 @@ def tp_moe_pack_experts(plan: Plan, w_local, w_packed):
 
 
 def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, part, workspace):
-    i = plan.info()
+    i = plan._plan_info()
     t = sel_expert.shape[0]
     k, mi, H = i["top_k"], i["moe_inter"], i["hidden"]
     args = (_dev(sel_expert, "sel_expert", torch.int32, (t, k)),
@@ -368,7 +378,7 @@ def tp_moe_partial(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, part, 
 def tp_moe_decode(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, slots, hidden, workspace):
     """The MoE point: the rank's experts for the plan's batch, the combine into slots[rank], then
     hidden <- ring_sum(slots) + hidden."""
-    i = plan.info()
+    i = plan._plan_info()
     n, b, k, mi, H = i["n_ranks"], i["batch"], i["top_k"], i["moe_inter"], i["hidden"]
     args = (_dev(sel_expert, "sel_expert", torch.int32, (b, k)),
             _dev(sel_weight, "sel_weight", torch.float32, (b, k)),
