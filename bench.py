@@ -199,7 +199,8 @@ def dense_run(args, w, tune):
             else "persistent VALU step")
     log("weight layout: %s" % layout)
     ms = time_steps(step, args.steps, args.warmup, stream)
-    if layout == "packed" and not args.no_serial and info["packed_kind"] == 1:
+    serial_knob = (info["packed_kind"] == 1) if layout == "packed" else (w.batch < 16)
+    if not args.no_serial and serial_knob:
         # the same step with the grid-wide wait per point (serial point order)
         plan.tune("serial_points", 1)
         ms_serial = time_steps(step, args.steps, args.warmup, stream)

@@ -130,9 +130,11 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "stream_wgs" (matrix-core stream: workgroups sharing the tiles, 0 = one
  *                per compute unit; at most 256 and H/16, at least H/32),
  * "moe_variant" (tp_moe_partial's expert kernel: 0 = default, 1..7),
- * "serial_points" (tp_decode_layers_packed: 0 = each hidden-state element
- *                follows its own chain, 1 = point j+1 also waits for all of
- *                point j, see there).
+ * "serial_points" (tp_decode_layers and tp_decode_layers_packed: 0 = each
+ *                hidden-state element follows its own chain, 1 = point j+1
+ *                also waits for all of point j, see there),
+ * "step_rows" (tp_decode_layers, batch < 16: most rows per tile of the
+ *                persistent step, 0 = automatic, 2048).
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
@@ -203,17 +205,24 @@ tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* res
  * (lesson 9.9, Conceito: two reconciliation points per layer, each an
  * all-reduce of one hidden vector per decoded token). Each point's
  * activation slice is an input (the operations between the points are
- * not part of this path), and each point's work starts only after the
- * previous point's hidden state is complete.
+ * not part of this path).
  *   x_attn bf16 [L][batch][k_attn/N]   w_o    bf16 [L][k_attn/N][hidden]
  *   x_ffn  bf16 [L][batch][inter/N]    w_down bf16 [L][inter/N][hidden]
  *   slots  fp32 [L][2][N][batch][hidden]: the other N-1 ranks' partials are
  *          inputs; entry [l][point][rank] is overwritten with this rank's
  *   hidden fp32 [batch][hidden], in/out (the residual stream)
- * Results equal tp_rowparallel_partial followed by tp_ring_reduce at each
+ * For batch >= 16 (or "decode_mode" = 1) each point is one launch, and the
+ * results equal tp_rowparallel_partial followed by tp_ring_reduce at each
  * point, bit for bit. For batch < 16 the whole step is one cooperative
- * (persistent) launch; the workspace's error word (tp_workspace_status)
- * reports a wait that timed out.
+ * (persistent) launch whose tiles are 128 columns ("valu_cols") by long row
+ * ranges (at most "step_rows" rows and 8192 / batch, as few splits of K_r as
+ * that allows), streamed; with the same tiles as the per-point launches
+ * (valu_cols and splits_attn / splits_ffn set so that both take the same
+ * rows) the bits are the same too. Point order as in
+ * tp_decode_layers_packed: by default each hidden-state element follows its
+ * own chain; "serial_points" = 1 makes every point wait for all of the
+ * previous one. Both give the same bits. The workspace's error word
+ * (tp_workspace_status) reports a wait that timed out.
  */
 tp_status tp_decode_layers(tp_plan_t plan, int32_t n_layers, int32_t rank,
                            const void* x_attn, const void* w_o,

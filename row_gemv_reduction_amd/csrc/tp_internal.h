@@ -17,6 +17,15 @@ constexpr int kCounterStride = 16;            // one counter per 64-byte line
 constexpr int kMaxCounters = 1024;            // column-tile arrival counters (64 KiB)
 constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, error
 constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
+// Persistent row-major decode step (decode_step): points completed per
+// column tile (stride kCounterStride), the x slice of a tile staged in LDS,
+// the split buffer / arrival counter sets (points in flight), default tile
+// width and tile length.
+constexpr int64_t kFixedOffset = 192 * 1024;
+constexpr int kStepXsFloats = 8192;
+constexpr int kStepBufs = 8;
+constexpr int kStepCols = 128;
+constexpr int kStepMaxRows = 2048;
 // VALU GEMV geometry limits
 constexpr int kValuWaves = 4;        // waves per workgroup
 constexpr int kValuMaxRows = 512;    // rows of x staged in LDS per workgroup
@@ -68,10 +77,11 @@ struct tp_plan_s {
     int32_t decode_mode = 0;
     int32_t target_wgs = 0;
     int32_t segment_loads = 0;  // 16-byte loads per lane per bank of the streamed step (0 = 4)
-    int32_t serial_points = 0;  // streamed step: point j+1 waits for all of point j
+    int32_t serial_points = 0;  // decode step: point j+1 waits for all of point j
     int32_t stream_kind = 0;    // 0 = automatic, 1 = pair strips (VALU), 2 = MFMA tiles
     int32_t moe_variant = 0;    // expert kernel variant (0 = default)
     int32_t stream_wgs = 0;     // MFMA stream: workgroups (0 = one per CU, at most H/16)
+    int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -93,6 +103,13 @@ PointGeom tp_point_geom(const tp_plan_s* p, int point);
 PointGeom tp_geom_for(const tp_plan_s* p, int64_t k_r, int32_t batch, int32_t splits_user);
 int64_t tp_workspace_bytes(const tp_plan_s* p);
 int64_t tp_ws_partials_offset();
+// Bytes of one split-K partial buffer of the per-point launches.
+int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p);
+// Geometry of the persistent decode step's tiles (long row ranges, streamed)
+// and the bytes of one of its kStepBufs split buffers (the workspace holds
+// all of them when the step can run, batch < 16).
+PointGeom tp_step_geom(const tp_plan_s* p, int point);
+int64_t tp_step_partial_buffer_bytes(const tp_plan_s* p);
 int64_t tp_ws_moe_offset(const tp_plan_s* p);
 int tp_decode_mode(const tp_plan_s* p);
 

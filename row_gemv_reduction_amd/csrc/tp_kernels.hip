@@ -204,36 +204,72 @@ struct ValuShared {
     float red[kValuWaves * COLS];
     __attribute__((aligned(16))) float tile[B * COLS];
     int flag;
+    int wflag;  // outcome of the decode step's waits
 };
 
-// One VALU tile: columns [ct*COLS, +COLS) x rows [k0, k0+nr) of W[K][H],
-// x [B][K]. `before_compute` runs after the weight loads are issued and
-// before x is read (the decode step waits there for the previous point).
-// Leaves the workgroup's partial in sh.tile. Returns false if
-// before_compute asked to abandon the tile.
-template <int B, int COLS, typename Hook>
-__device__ bool valu_tile(ValuShared<B, COLS>& sh, const uint16_t* x, const uint16_t* w,
-                          int64_t K, int64_t H, int64_t k0, int nr, int ct, Hook before_compute) {
-    constexpr int NT = kValuWaves * 64;
+// Issue the weight loads of one VALU tile: columns [ct*COLS, +COLS) x rows
+// [k0, k0+nr) of W[K][H]. Every 16-byte vector (8 columns) of the lane's
+// rows goes out at once; lanes past the tile get zeros.
+template <int B, int COLS>
+__device__ __forceinline__ void valu_issue(u32x4_t (&wv)[kValuLoadsPerLane], const uint16_t* w,
+                                           int64_t H, int64_t k0, int nr, int ct) {
     constexpr int LPR = COLS / 8;   // lanes per row segment
     constexpr int RPW = 64 / LPR;   // row groups per wave
     constexpr int RSTEP = kValuWaves * RPW;
-    constexpr int NI = kValuLoadsPerLane;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n = (int64_t)ct * COLS + (lane % LPR) * 8;
     const bool col_ok = n < H;
     const int r0 = wave * RPW + lane / LPR;
-
-    // every weight vector of this lane's rows, in flight at once
-    u32x4_t wv[NI];
     const uint16_t* wp = w + (k0 + r0) * H + n;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < kValuLoadsPerLane; ++i) {
         if (col_ok && r0 + i * RSTEP < nr) wv[i] = load_stream16(wp + (int64_t)i * RSTEP * H);
         else wv[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
+}
 
-    if (!before_compute()) return false;
+// Sum a tile's per-lane accumulators (lane rows r0 + i*RSTEP, summed in i
+// order) into tile[B][COLS]: first the wave's row groups (lanes that share
+// columns; an xor pair adds the same two values, so both lanes hold
+// identical bits), then the waves in wave order, one batch row at a time.
+template <int B, int COLS>
+__device__ __forceinline__ void reduce_tile(float (&acc)[B][8], float* red, float* tile) {
+    constexpr int NT = kValuWaves * 64;
+    constexpr int LPR = COLS / 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[bb][j] += __shfl_xor(acc[bb][j], m);
+    for (int bb = 0; bb < B; ++bb) {
+        if (lane < LPR) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) red[wave * COLS + lane * 8 + j] = acc[bb][j];
+        }
+        __syncthreads();
+        for (int c = tid; c < COLS; c += NT) {
+            float s = red[c];
+#pragma unroll
+            for (int wq = 1; wq < kValuWaves; ++wq) s += red[wq * COLS + c];
+            tile[bb * COLS + c] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// Finish one VALU tile whose loads valu_issue put in `wv`, x [B][K]: stage
+// x as fp32 in LDS, multiply, and leave the workgroup's partial in sh.tile.
+template <int B, int COLS>
+__device__ void valu_finish(ValuShared<B, COLS>& sh, const u32x4_t (&wv)[kValuLoadsPerLane],
+                            const uint16_t* x, int64_t K, int64_t k0, int nr) {
+    constexpr int NT = kValuWaves * 64;
+    constexpr int LPR = COLS / 8;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RSTEP = kValuWaves * RPW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = wave * RPW + lane / LPR;
 
     for (int i = tid; i < nr * B; i += NT) {
         int bb = i / nr, r = i - bb * nr;
@@ -247,36 +283,11 @@ __device__ bool valu_tile(ValuShared<B, COLS>& sh, const uint16_t* x, const uint
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[bb][j] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < kValuLoadsPerLane; ++i) {
         int r = r0 + i * RSTEP;
         if (r < nr) fma_row<B>(acc, wv[i], &sh.xs[r * B]);
     }
-
-    // Sum the wave's row groups (lanes that share columns); an xor pair
-    // adds the same two values, so both lanes hold identical bits.
-#pragma unroll
-    for (int m = LPR; m < 64; m <<= 1)
-#pragma unroll
-        for (int bb = 0; bb < B; ++bb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[bb][j] += __shfl_xor(acc[bb][j], m);
-
-    // Sum the waves in wave order, one batch row at a time.
-    for (int bb = 0; bb < B; ++bb) {
-        if (lane < LPR) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sh.red[wave * COLS + lane * 8 + j] = acc[bb][j];
-        }
-        __syncthreads();
-        for (int c = tid; c < COLS; c += NT) {
-            float s = sh.red[c];
-#pragma unroll
-            for (int wq = 1; wq < kValuWaves; ++wq) s += sh.red[wq * COLS + c];
-            sh.tile[bb * COLS + c] = s;
-        }
-        __syncthreads();
-    }
-    return true;
+    reduce_tile<B, COLS>(acc, sh.red, sh.tile);
 }
 
 struct GemvArgs {
@@ -296,7 +307,9 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_gemv(GemvArgs a) {
     const int sp = blockIdx.x / a.col_tiles;
     const int64_t k0 = (int64_t)sp * a.rows;
     const int nr = (int)(a.K - k0 < a.rows ? a.K - k0 : a.rows);
-    valu_tile<B, COLS>(sh, a.x, a.w, a.K, a.H, k0, nr, ct, [] { return true; });
+    u32x4_t wv[kValuLoadsPerLane];
+    valu_issue<B, COLS>(wv, a.w, a.H, k0, nr, ct);
+    valu_finish<B, COLS>(sh, wv, a.x, a.K, k0, nr);
     if (publish_split<COLS, NT>(a.epi, sh.tile, B, a.H, ct, sp, threadIdx.x, &sh.flag))
         fixup_tile<COLS, NT>(a.epi, sh.tile, B, a.H, ct, threadIdx.x);
 }
@@ -308,26 +321,111 @@ struct StepArgs {
     const uint16_t* w[2];   // w_o [L][K0][H], w_down [L][K1][H]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
-    float* ws_part;
-    uint32_t* counters;     // column-tile arrival counters
+    float* ws_part;         // kStepBufs split-partial buffers
+    int64_t part_stride;    // floats between two buffers
+    uint32_t* counters;     // column-tile arrival counters, kStepBufs sets
+    uint32_t* fixed;        // per column tile: points whose fix-up is done
     uint32_t* sync;         // done / exit / error words
     int64_t H, K[2];
     int32_t rows[2], splits[2], tiles[2];
     int32_t col_tiles, layers, n_ranks, rank;
+    int32_t serial;         // 1: point j+1 reads its activation after all of point j
     int64_t chunk;
     uint32_t spin_limit;
 };
 
 template <int B, int COLS>
+struct StepShared {
+    float xs[kStepXsFloats];  // the tile's x slice, fp32, [row][B]
+    float red[kValuWaves * COLS];
+    __attribute__((aligned(16))) float tile[B * COLS];
+    int flag;
+    int wflag;  // outcome of the waits
+};
+
+// 16-byte weight loads per lane in each of the two register banks.
+constexpr int step_bank_loads(int b) { return b <= 4 ? 12 : 8; }
+
+// Stream rows [k0, k0+nr) of a column tile through two register banks of
+// NB loads per lane: while one bank is multiplied the other is in flight,
+// and the oldest loads are always the ones waited for. The lane's rows are
+// r0 + i*RSTEP for i = 0, 1, ... in order, as in valu_finish, so a tile of
+// the same rows gives the same bits.
+template <int B, int COLS, int NB>
+__device__ __forceinline__ void stream_rows(const float* xs, const uint16_t* w, int64_t H,
+                                            int64_t k0, int nr, int ct, float (&acc)[B][8]) {
+    constexpr int LPR = COLS / 8;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RSTEP = kValuWaves * RPW;
+    constexpr int BR = RSTEP * NB;  // rows per bank
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n = (int64_t)ct * COLS + (lane % LPR) * 8;
+    const bool col_ok = n < H;
+    const int r0 = wave * RPW + lane / LPR;
+    const uint16_t* wp = w + (k0 + r0) * H + n;
+    auto load_bank = [&](u32x4_t (&v)[NB], int base) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int r = base + i * RSTEP;
+            v[i] = (col_ok && r0 + r < nr) ? load_stream16(wp + (int64_t)r * H)
+                                           : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    auto fma_bank = [&](const u32x4_t (&v)[NB], int base) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int r = r0 + base + i * RSTEP;
+            if (r < nr) fma_row<B>(acc, v[i], &xs[r * B]);
+        }
+    };
+    u32x4_t va[NB], vb[NB];
+    load_bank(va, 0);
+    load_bank(vb, BR);
+    for (int base = 0; base < nr; base += 2 * BR) {
+        fma_bank(va, base);
+        if (base + 2 * BR < nr) load_bank(va, base + 2 * BR);
+        fma_bank(vb, base + BR);
+        if (base + 3 * BR < nr) load_bank(vb, base + 3 * BR);
+    }
+}
+
+// The whole decode step in one cooperative launch. Tiles are (point,
+// column tile, split), walked in point order with a grid stride; a tile
+// covers a long row range, streamed, with its x slice staged in LDS.
+//
+// Point order. The residual chain runs element by element: the fix-up of
+// (point j, column tile c) reads the hidden-state columns of tile c that
+// (j-1, c) wrote, and nothing else of earlier points, so by default a
+// workgroup waits only for that (per-tile `fixed` counters) and tiles of
+// later points stream while earlier ones are reduced. Points rotate over
+// kStepBufs sets of split buffers and arrival counters; a split of point j
+// publishes only once (j - kStepBufs, c) has been fixed, which frees its
+// set. With `serial` the step also emulates a model whose activation at
+// point j depends on the whole hidden state after j-1: every tile of point
+// j waits, before it reads x, until all column tiles of j-1 are fixed. Each
+// wait targets tiles earlier in the grid-stride order, and the launch is
+// cooperative (all workgroups resident), so the earliest pending tile
+// always proceeds. Both orders sum the same values in the same order: the
+// bits do not depend on it.
+template <int B, int COLS>
 __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
     constexpr int NT = kValuWaves * 64;
-    __shared__ ValuShared<B, COLS> sh;
+    constexpr int NB = step_bank_loads(B);
+    __shared__ StepShared<B, COLS> sh;
     const int tid = threadIdx.x;
     uint32_t* done = a.sync + kSyncDone;
     uint32_t* err = a.sync + kSyncErr;
     const int64_t len = (int64_t)B * a.H;
     const int per_layer = a.tiles[0] + a.tiles[1];
     const int64_t total = (int64_t)a.layers * per_layer;
+
+    // tid 0 waits until *ctr >= target; every thread gets the outcome
+    auto wait_all = [&](uint32_t* ctr, uint32_t target) -> bool {
+        if (tid == 0) sh.wflag = wait_at_least(ctr, target, err, a.spin_limit);
+        __syncthreads();
+        compiler_barrier();
+        return sh.wflag != 0;
+    };
 
     for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
         const int l = (int)(q / per_layer);
@@ -341,41 +439,85 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         const int nr = (int)(K - k0 < a.rows[pt] ? K - k0 : a.rows[pt]);
         const uint16_t* x = a.x[pt] + (int64_t)l * B * K;
         const uint16_t* w = a.w[pt] + (int64_t)l * K * a.H;
+        const int splits = a.splits[pt];
+        uint32_t* fixed = a.fixed + ct * kCounterStride;
 
         __syncthreads();  // LDS of the previous tile is no longer read
-        // Point j reads its activation only once point j-1's hidden state is
-        // complete (all column tiles of j-1 reduced).
-        auto wait_prev = [&]() -> bool {
-            if (tid == 0) sh.flag = wait_at_least(done, (uint32_t)j * a.col_tiles, err, a.spin_limit);
-            __syncthreads();
-            compiler_barrier();
-            return sh.flag != 0;
-        };
-        if (!valu_tile<B, COLS>(sh, x, w, K, a.H, k0, nr, ct, wait_prev)) continue;
+        // A failed wait (error word set) ends the workgroup's walk; every
+        // later wait fails at once, so the grid drains.
+        if (a.serial && !wait_all(done, (uint32_t)j * a.col_tiles)) break;
+
+        // x[:, k0 .. k0+nr) as fp32, [row][B]; 16-byte loads where the
+        // slice starts 16-byte aligned in every row of x
+        if ((K & 7) == 0 && (k0 & 7) == 0) {
+            const int per_b = nr >> 3;
+            for (int i = tid; i < per_b * B; i += NT) {
+                const int bb = i / per_b, r = (i - bb * per_b) * 8;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)bb * K + k0 + r);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    sh.xs[(r + 2 * h) * B + bb] = bf16_lo(u[h]);
+                    sh.xs[(r + 2 * h + 1) * B + bb] = bf16_hi(u[h]);
+                }
+            }
+            for (int i = tid; i < (nr & 7) * B; i += NT) {
+                const int bb = i / (nr & 7), r = (nr & ~7) + i - bb * (nr & 7);
+                sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
+            }
+        } else {
+            for (int i = tid; i < nr * B; i += NT) {
+                const int bb = i / nr, r = i - bb * nr;
+                sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
+            }
+        }
+        __syncthreads();
+
+        float acc[B][8];
+#pragma unroll
+        for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[bb][c] = 0.f;
+        stream_rows<B, COLS, NB>(sh.xs, w, a.H, k0, nr, ct, acc);
+        reduce_tile<B, COLS>(acc, sh.red, sh.tile);
+
+        // the split set of point j was last used by point j - kStepBufs (a
+        // single split uses none; the wait before its fix-up covers it)
+        const int set = j % kStepBufs;
+        if (!a.serial && splits > 1 && j >= kStepBufs &&
+            !wait_all(fixed, (uint32_t)(j - kStepBufs + 1)))
+            break;
 
         float* slot = a.slots + (int64_t)j * a.n_ranks * len;
-        Epilogue e;
+        Epilogue e{};
         e.p = slot + (int64_t)a.rank * len;
-        e.ws_part = a.ws_part;
-        e.counters = a.counters;
-        e.splits = a.splits[pt];
+        e.ws_part = a.ws_part + (int64_t)set * a.part_stride;
+        e.counters = a.counters + (int64_t)set * a.col_tiles * kCounterStride;
+        e.splits = splits;
         e.ring_slots = slot;
         e.hidden = a.hidden;
         e.n_ranks = a.n_ranks;
         e.rank = a.rank;
         e.chunk = a.chunk;
         if (publish_split<COLS, NT>(e, sh.tile, B, a.H, ct, sp, tid, &sh.flag)) {
+            // the residual columns of this tile are those (j-1, ct) wrote
+            if (!a.serial && j >= 1 && !wait_all(fixed, (uint32_t)j)) break;
             fixup_tile<COLS, NT>(e, sh.tile, B, a.H, ct, tid);
             __syncthreads();
-            if (tid == 0) add_dev_u32(done, 1u);
+            if (tid == 0) {
+                add_dev_u32(a.serial ? done : fixed, 1u);
+                wait_mem();
+            }
         }
     }
     // The last workgroup to leave resets the step's sync words for the next
     // launch (no workgroup waits on them any more).
     __syncthreads();
-    if (tid == 0) {
-        uint32_t prev = add_dev_u32(a.sync + kSyncExit, 1u);
-        if (prev == gridDim.x - 1) {
+    if (tid == 0) sh.flag = add_dev_u32(a.sync + kSyncExit, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (sh.flag) {
+        for (int c = tid; c < a.col_tiles; c += NT) st_dev_u32(a.fixed + c * kCounterStride, 0u);
+        if (tid == 0) {
             st_dev_u32(done, 0u);
             st_dev_u32(a.sync + kSyncExit, 0u);
         }
@@ -658,16 +800,21 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
                             const void* w_o, const void* x_ffn, const void* w_down, float* slots,
                             float* hidden, void* ws, hipStream_t st) {
     const int b = p->batch;
-    PointGeom geo[2] = {tp_point_geom(p, 0), tp_point_geom(p, 1)};
+    if (b < 1 || b > kValuMaxBatch) return TP_ERR_UNSUPPORTED;
+    PointGeom geo[2] = {tp_step_geom(p, 0), tp_step_geom(p, 1)};
     if (geo[0].cols != geo[1].cols || geo[0].col_tiles != geo[1].col_tiles) return TP_ERR_UNSUPPORTED;
-    if (geo[0].col_tiles > kMaxCounters) return TP_ERR_UNSUPPORTED;
+    // kStepBufs sets of arrival counters in [0, kSyncOffset); the fixed
+    // counters in [kFixedOffset, kCounterBytes)
+    if ((int64_t)kStepBufs * geo[0].col_tiles > kMaxCounters ||
+        kFixedOffset + (int64_t)geo[0].col_tiles * kCounterStride * 4 > kCounterBytes)
+        return TP_ERR_UNSUPPORTED;
     for (int pt = 0; pt < 2; ++pt)
-        if (geo[pt].path != TP_PATH_VALU || geo[pt].rows > valu_rows_max(b, geo[pt].cols) ||
+        if (geo[pt].rows < 1 || (int64_t)geo[pt].rows * b > kStepXsFloats ||
             (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
             return TP_ERR_UNSUPPORTED;
-    if ((int64_t)n_layers * 2 * geo[0].col_tiles >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
-    for (int pt = 0; pt < 2; ++pt)
-        if ((int64_t)geo[pt].splits * b * p->hidden * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
+    if ((int64_t)n_layers * (geo[0].grid + geo[1].grid) >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
+    const int64_t part_stride = tp_step_partial_buffer_bytes(p) / 4;
+    if (part_stride * 4 * kStepBufs >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
     step_fn k = step_kernel(b, geo[0].cols);
     if (!k) return TP_ERR_UNSUPPORTED;
     StepArgs a;
@@ -678,8 +825,11 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     a.slots = slots;
     a.hidden = hidden;
     a.ws_part = ws_partials(ws);
+    a.part_stride = part_stride;
     a.counters = ws_counters(ws);
+    a.fixed = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kFixedOffset);
     a.sync = ws_sync(ws);
+    a.serial = p->serial_points ? 1 : 0;
     a.H = p->hidden;
     for (int pt = 0; pt < 2; ++pt) {
         a.K[pt] = geo[pt].k_r;
@@ -696,8 +846,10 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     if (n_layers == 0) return TP_OK;
     int cap = resident_grid(reinterpret_cast<const void*>(k), kValuWaves * 64);
     if (cap < 1) return TP_ERR_DEVICE;
-    int want = geo[0].grid > geo[1].grid ? geo[0].grid : geo[1].grid;
-    int grid = want < cap ? want : cap;
+    // Every resident workgroup: the tiles of later points are taken up while
+    // earlier ones are reduced (the waits order what must be ordered).
+    const int64_t total = (int64_t)n_layers * (geo[0].grid + geo[1].grid);
+    int grid = total < cap ? (int)total : cap;
     void* args[] = {&a};
     if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid),
                                    dim3(kValuWaves * 64), args, 0, st) != hipSuccess)

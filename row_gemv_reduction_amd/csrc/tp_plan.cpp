@@ -66,7 +66,7 @@ PointGeom tp_point_geom(const tp_plan_s* p, int point) {
 
 int64_t tp_ws_partials_offset() { return kCounterBytes; }
 
-static int64_t partial_bytes(const tp_plan_s* p) {
+int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p) {
     int64_t m = 0;
     for (int pt = 0; pt < 2; ++pt) {
         PointGeom g = tp_point_geom(p, pt);
@@ -74,6 +74,56 @@ static int64_t partial_bytes(const tp_plan_s* p) {
         if (b > m) m = b;
     }
     return round_up(m, 256);
+}
+
+// Persistent decode step: 128-column tiles (256-byte row segments) over
+// long row ranges, as few splits as the LDS copy of the tile's x slice
+// (kStepXsFloats) and the tile length cap allow, so most points need no
+// split exchange at all. With splits_user the rows follow the same rule as
+// the per-point launches (equal tiles give equal bits).
+PointGeom tp_step_geom(const tp_plan_s* p, int point) {
+    PointGeom g{};
+    g.k_r = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    g.path = TP_PATH_VALU;
+    g.cols = p->valu_cols ? p->valu_cols : kStepCols;
+    g.col_tiles = (int32_t)ceil_div(p->hidden, g.cols);
+    const int64_t gran = (int64_t)kValuWaves * (64 / (g.cols / 8));
+    const int b = p->batch > 0 ? p->batch : 1;
+    int64_t max_rows = kStepXsFloats / b;
+    const int64_t cap = p->step_rows > 0 ? p->step_rows : kStepMaxRows;
+    if (max_rows > cap) max_rows = cap;
+    max_rows -= max_rows % gran;
+    if (max_rows < gran) max_rows = gran;
+    const int32_t su = p->splits_user[point];
+    int64_t s = su > 0 ? su : ceil_div(g.k_r, max_rows);
+    int64_t s_max = ceil_div(g.k_r, gran);
+    if (s > s_max) s = s_max;
+    if (s < 1) s = 1;
+    int64_t rows = round_up(ceil_div(g.k_r, s), gran);
+    if (rows > max_rows) rows = max_rows;
+    g.rows = (int32_t)rows;
+    g.splits = (int32_t)ceil_div(g.k_r, rows);
+    g.grid = g.col_tiles * g.splits;
+    return g;
+}
+
+int64_t tp_step_partial_buffer_bytes(const tp_plan_s* p) {
+    int64_t m = 0;
+    for (int pt = 0; pt < 2; ++pt) {
+        PointGeom g = tp_step_geom(p, pt);
+        int64_t b = g.splits > 1 ? (int64_t)g.splits * p->batch * p->hidden * 4 : 0;
+        if (b > m) m = b;
+    }
+    return round_up(m, 256);
+}
+
+static int64_t partial_bytes(const tp_plan_s* p) {
+    int64_t m = tp_ws_partial_buffer_bytes(p);
+    if (p->batch < kMfmaMinBatch) {
+        int64_t s = kStepBufs * tp_step_partial_buffer_bytes(p);
+        if (s > m) m = s;
+    }
+    return m;
 }
 
 int64_t tp_ws_xchg_offset(const tp_plan_s* p) {
@@ -164,6 +214,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
+    } else if (!strcmp(key, "step_rows")) {
+        if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
+        p->step_rows = (int32_t)value;
     } else if (!strcmp(key, "target_wgs")) {
         if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
         p->target_wgs = (int32_t)value;

@@ -245,7 +245,8 @@ def test_decode_equals_partial_then_ring_bitwise():
     L, n, b, h, ka, ki, rank = 2, 4, 3, 1032, 512, 1536, 2
     say("decode vs composition")
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 8, rank)
-    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    # the same tiles for the decode step and the single projection
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"valu_cols": 128, "splits_attn": 1, "splits_ffn": 2})
     s_gpu, h_gpu = run_decode(plan, L, rank, xa, wo, xf, wd, slots, h0)
     hd = to_dev_f32(h0)
     for l in range(L):
@@ -371,18 +372,25 @@ def test_h4096_sampled(n, batch):
 
 # ------------------------------------------- persistent decode step --
 
-@pytest.mark.parametrize("n,b,cols", [(4, 1, 256), (2, 3, 128), (8, 8, 512), (4, 15, 256)])
-def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols):
-    """The one-launch decode step and the launch-per-point path run the same
-    tiles in the same order, so every slot and the hidden state agree bit for
-    bit; repeated runs agree too (the fence-free split exchange is
-    deterministic), and the workspace error word stays clear."""
+@pytest.mark.parametrize("n,b,cols,splits_attn,splits_ffn", [
+    (4, 1, 256, 1, 3), (4, 1, 256, 2, 4), (2, 3, 128, 1, 3), (8, 8, 512, 1, 3), (4, 15, 256, 2, 3)])
+def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols, splits_attn, splits_ffn):
+    """With the same tiles (column width and splits forced alike), the
+    one-launch decode step, in the dataflow and in the serial point order,
+    and the launch-per-point path sum every element in the same order, so
+    every slot and the hidden state agree bit for bit; repeated runs agree
+    too (the fence-free split exchange is deterministic), and the workspace
+    error word stays clear. splits_attn=1 covers a point without split
+    buffers."""
     L, h, ka, ki, rank = 5, 1032, 640, 2048, n - 1
-    say("persistent vs per-point n=%d b=%d cols=%d" % (n, b, cols))
+    say("persistent vs per-point n=%d b=%d cols=%d splits=%d/%d" % (n, b, cols, splits_attn, splits_ffn))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 21, rank)
     outs = []
-    for mode in (1, 2, 2):
-        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"decode_mode": mode, "valu_cols": cols})
+    for mode, serial in ((1, 0), (2, 0), (2, 1), (2, 0)):
+        plan = tp.Plan(h, ki, n, b, k_attn=ka,
+                       tune={"decode_mode": mode, "valu_cols": cols, "serial_points": serial,
+                             "splits_attn": splits_attn, "splits_ffn": splits_ffn})
+        assert plan.info()["splits"] == [splits_attn, splits_ffn]
         ws = plan.new_workspace()
         S = to_dev_f32(slots)
         Hd = to_dev_f32(h0)
@@ -406,11 +414,46 @@ def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols):
     assert err <= 4 * L * 1e-5 * rms_p + 8 * np.spacing(np.abs(h2).max()), err
 
 
+@pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 1, 1032, 1024, 17408, 6), (2, 8, 1032, 2048, 8192, 5),
+                                           (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 3)])
+def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
+    """The step's own tiles (long row ranges; splits only where the x slice
+    or the tile length cap asks for them): both point orders give the same
+    bits, more points than split-buffer sets run through the rotation, and
+    the result matches the oracle (two chained steps)."""
+    rank = n // 2
+    say("persistent default tiles n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 33, rank)
+    outs = []
+    for serial in (0, 1):
+        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"serial_points": serial})
+        ws = plan.new_workspace()
+        S = to_dev_f32(slots)
+        Hd = to_dev_f32(h0)
+        for _ in range(2):
+            tp.tp_decode_layers(plan, L, rank, to_dev_bf16(xa), to_dev_bf16(wo), to_dev_bf16(xf),
+                                to_dev_bf16(wd), S, Hd, ws)
+        torch.cuda.synchronize()
+        assert tp.tp_workspace_status(plan, ws) == 0
+        outs.append((host(S), host(Hd)))
+    assert_bits_equal(outs[1][0], outs[0][0], "slots")
+    assert_bits_equal(outs[1][1], outs[0][1], "hidden")
+    _, h1 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
+    _, h2 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h1)
+    for l in range(L):
+        assert_partial_close(outs[0][0][l, 0, rank], oracle.partial(xa[l], wo[l])[0], "attn")
+        assert_partial_close(outs[0][0][l, 1, rank], oracle.partial(xf[l], wd[l])[0], "ffn")
+    rms_p = np.sqrt(np.mean(outs[0][0][:, :, rank].astype(np.float64) ** 2))
+    err = np.abs(outs[0][1].astype(np.float64) - h2).max()
+    assert err <= 4 * L * 1e-5 * rms_p + 8 * np.spacing(np.abs(h2).max()), err
+
+
 def test_persistent_step_repeated_runs_are_identical():
     """Race check for the in-launch split exchange: 20 steps of the page-1
-    shape (rank 0 of 4, batch 1) on the same inputs give identical bits."""
-    w = workloads.PAGE1.with_(layers=4)
-    say("persistent determinism, page-1 shape, 4 layers x 20 runs")
+    shape (rank 0 of 4, batch 1; 12 points, more than the step's split-buffer
+    sets) on the same inputs give identical bits."""
+    w = workloads.PAGE1.with_(layers=6)
+    say("persistent determinism, page-1 shape, 6 layers x 20 runs")
     plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch)
     xa, wo, xf, wd, slots, h0 = device_stack(w, 0)
     ws = plan.new_workspace()
