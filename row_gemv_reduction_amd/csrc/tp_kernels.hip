@@ -150,6 +150,67 @@ __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int6
     wait_mem();
 }
 
+// Last arrival of a persistent-step tile (point j, column tile ct): the
+// splits summed in split order, the rank's slot written and the ring-order
+// sum over the N ranks formed in registers (ring_element with a residual of
+// -0.0, which leaves every value as it is), all before `wait_prev` waits for
+// (j-1, ct); only the residual's read, one addition and the store of the
+// hidden state follow it. Same bits as fixup_tile. Returns false if the
+// wait failed.
+template <int B, int COLS, int NT, typename Wait>
+__device__ bool step_fixup(const Epilogue& e, const float* tile, int64_t H, int ct, int tid,
+                           Wait wait_prev) {
+#pragma clang fp contract(off)
+    constexpr int NV = B * COLS / 4;  // 16-byte vectors in the tile
+    constexpr int VPT = (NV + NT - 1) / NT;
+    const int64_t n0 = (int64_t)ct * COLS;
+    const int64_t len = (int64_t)B * H;
+    const __amdgpu_buffer_rsrc_t rp = dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * len * 4));
+    const __amdgpu_buffer_rsrc_t rh = dev_rsrc(e.hidden, (uint32_t)(len * 4));
+    floatx4_t ring[VPT];
+    int64_t at[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int idx = tid + u * NT;
+        at[u] = -1;
+        if (idx >= NV) continue;
+        const int bb = idx / (COLS / 4), c = (idx - bb * (COLS / 4)) * 4;
+        if (n0 + c >= H) continue;
+        const int64_t i = (int64_t)bb * H + n0 + c;
+        at[u] = i;
+        floatx4_t v;
+        if (e.splits > 1) {
+            floatx4_t l[8];
+            for (int s0 = 0; s0 < e.splits; s0 += 8) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int sp = s0 + k < e.splits ? s0 + k : e.splits - 1;
+                    l[k] = ld_dev4(rp, (uint32_t)(((int64_t)sp * len + i) * 4));
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (s0 + k < e.splits) v = (s0 + k == 0) ? l[k] : v + l[k];
+            }
+        } else {
+            v = *reinterpret_cast<const floatx4_t*>(tile + bb * COLS + c);
+        }
+        *reinterpret_cast<floatx4_t*>(e.p + i) = v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            ring[u][k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], -0.0f);
+    }
+    if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
+    if (!wait_prev()) return false;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        if (at[u] < 0) continue;
+        const floatx4_t res = ld_dev4(rh, (uint32_t)(at[u] * 4));
+        st_dev4(rh, (uint32_t)(at[u] * 4), ring[u] + res);
+    }
+    wait_mem();
+    return true;
+}
+
 // Spread fix-up (all of a column tile's splits resident): once every split
 // has published, split sp's workgroup takes the sp-th of S equal shares of
 // the tile's vectors (each still summed in split order, so the result is
@@ -501,8 +562,10 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         e.chunk = a.chunk;
         if (publish_split<COLS, NT>(e, sh.tile, B, a.H, ct, sp, tid, &sh.flag)) {
             // the residual columns of this tile are those (j-1, ct) wrote
-            if (!a.serial && j >= 1 && !wait_all(fixed, (uint32_t)j)) break;
-            fixup_tile<COLS, NT>(e, sh.tile, B, a.H, ct, tid);
+            auto wait_prev = [&]() -> bool {
+                return a.serial || j == 0 || wait_all(fixed, (uint32_t)j);
+            };
+            if (!step_fixup<B, COLS, NT>(e, sh.tile, a.H, ct, tid, wait_prev)) break;
             __syncthreads();
             if (tid == 0) {
                 add_dev_u32(a.serial ? done : fixed, 1u);
