@@ -246,22 +246,59 @@ __device__ void spread_fixup(const Epilogue& e, int batch, int64_t H, int ct, in
 
 // ------------------------------------------------------------ VALU tile --
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// Select the low (even column) or high (odd column) bf16 of two row words
+// into one k-major pair: result = {row0 half, row1 half}.
+__device__ __forceinline__ uint32_t pair_rows(uint32_t row0, uint32_t row1, bool high) {
+    return __builtin_amdgcn_perm(row1, row0, high ? 0x07060302u : 0x05040100u);
+}
+
+// Two of a lane's rows (ra, rb; 8 columns each) against x at those rows:
+// per column and batch row, one v_dot2c_f32_bf16 adds both exact bf16
+// products to the fp32 accumulator. xp[bb] = {x[bb][ra], x[bb][rb]}.
 template <int B>
-__device__ __forceinline__ void fma_row(float (&acc)[B][8], const u32x4_t& wv, const float* xr) {
-    float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                   bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+__device__ __forceinline__ void dot2_rows(float (&acc)[B][8], const u32x4_t& ra, const u32x4_t& rb,
+                                          const uint32_t* xp) {
+    const uint32_t pr[8] = {pair_rows(ra.x, rb.x, false), pair_rows(ra.x, rb.x, true),
+                            pair_rows(ra.y, rb.y, false), pair_rows(ra.y, rb.y, true),
+                            pair_rows(ra.z, rb.z, false), pair_rows(ra.z, rb.z, true),
+                            pair_rows(ra.w, rb.w, false), pair_rows(ra.w, rb.w, true)};
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) {
-        float xv = xr[bb];
+        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xp[bb]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[bb][j] = __builtin_fmaf(xv, wf[j], acc[bb][j]);
+        for (int j = 0; j < 8; ++j)
+            acc[bb][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr[j]), xv,
+                                                         acc[bb][j], false);
+    }
+}
+
+// Stage x[:, k0 .. k0+nr) for dot2_rows: a lane's rows are r0 + i*RSTEP,
+// taken in pairs (i even, i+1), so the pair of row a (a / RSTEP even) is
+// stored at xp[a*B + bb] = {x[bb][k0+a], x[bb][k0+a+RSTEP]}; a partner row
+// past the tile reads as zero (its weights are zero too, and nothing stale
+// in LDS is ever multiplied).
+template <int B, int RSTEP, int NT>
+__device__ __forceinline__ void stage_x_pairs(uint32_t* xp, const uint16_t* x, int64_t K, int64_t k0,
+                                              int nr) {
+    const int nblk = (nr + 2 * RSTEP - 1) / (2 * RSTEP);
+    const int per_b = nblk * RSTEP;
+    for (int i = threadIdx.x; i < per_b * B; i += NT) {
+        const int bb = i / per_b, rem = i - bb * per_b;
+        const int ra = (rem / RSTEP) * 2 * RSTEP + rem % RSTEP;
+        if (ra >= nr) continue;
+        const uint16_t* xr = x + (int64_t)bb * K + k0;
+        const uint32_t lo = xr[ra];
+        const uint32_t hi = ra + RSTEP < nr ? xr[ra + RSTEP] : 0u;
+        xp[ra * B + bb] = lo | (hi << 16);
     }
 }
 
 template <int B, int COLS>
 struct ValuShared {
     static constexpr int XS = valu_rows_max(B, COLS) * B;
-    float xs[XS];
+    uint32_t xs[XS];  // x row pairs, see stage_x_pairs
     float red[kValuWaves * COLS];
     __attribute__((aligned(16))) float tile[B * COLS];
     int flag;
@@ -289,8 +326,8 @@ __device__ __forceinline__ void valu_issue(u32x4_t (&wv)[kValuLoadsPerLane], con
     }
 }
 
-// Sum a tile's per-lane accumulators (lane rows r0 + i*RSTEP, summed in i
-// order) into tile[B][COLS]: first the wave's row groups (lanes that share
+// Sum a tile's per-lane accumulators (lane rows r0 + i*RSTEP, taken in
+// pairs in i order) into tile[B][COLS]: first the wave's row groups (lanes that share
 // columns; an xor pair adds the same two values, so both lanes hold
 // identical bits), then the waves in wave order, one batch row at a time.
 template <int B, int COLS>
@@ -321,7 +358,8 @@ __device__ __forceinline__ void reduce_tile(float (&acc)[B][8], float* red, floa
 }
 
 // Finish one VALU tile whose loads valu_issue put in `wv`, x [B][K]: stage
-// x as fp32 in LDS, multiply, and leave the workgroup's partial in sh.tile.
+// x row pairs in LDS, multiply (rows in pairs, dot2_rows), and leave the
+// workgroup's partial in sh.tile.
 template <int B, int COLS>
 __device__ void valu_finish(ValuShared<B, COLS>& sh, const u32x4_t (&wv)[kValuLoadsPerLane],
                             const uint16_t* x, int64_t K, int64_t k0, int nr) {
@@ -329,13 +367,10 @@ __device__ void valu_finish(ValuShared<B, COLS>& sh, const u32x4_t (&wv)[kValuLo
     constexpr int LPR = COLS / 8;
     constexpr int RPW = 64 / LPR;
     constexpr int RSTEP = kValuWaves * RPW;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r0 = wave * RPW + lane / LPR;
 
-    for (int i = tid; i < nr * B; i += NT) {
-        int bb = i / nr, r = i - bb * nr;
-        sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
-    }
+    stage_x_pairs<B, RSTEP, NT>(sh.xs, x, K, k0, nr);
     __syncthreads();
 
     float acc[B][8];
@@ -343,10 +378,11 @@ __device__ void valu_finish(ValuShared<B, COLS>& sh, const u32x4_t (&wv)[kValuLo
     for (int bb = 0; bb < B; ++bb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[bb][j] = 0.f;
+    static_assert(kValuLoadsPerLane % 2 == 0, "rows are taken in pairs");
 #pragma unroll
-    for (int i = 0; i < kValuLoadsPerLane; ++i) {
+    for (int i = 0; i < kValuLoadsPerLane; i += 2) {
         int r = r0 + i * RSTEP;
-        if (r < nr) fma_row<B>(acc, wv[i], &sh.xs[r * B]);
+        if (r < nr) dot2_rows<B>(acc, wv[i], wv[i + 1], &sh.xs[r * B]);
     }
     reduce_tile<B, COLS>(acc, sh.red, sh.tile);
 }
@@ -397,7 +433,7 @@ struct StepArgs {
 
 template <int B, int COLS>
 struct StepShared {
-    float xs[kStepXsFloats];  // the tile's x slice, fp32, [row][B]
+    uint32_t xs[kStepXsFloats];  // the tile's x row pairs, see stage_x_pairs
     float red[kValuWaves * COLS];
     __attribute__((aligned(16))) float tile[B * COLS];
     int flag;
@@ -405,48 +441,77 @@ struct StepShared {
 };
 
 // 16-byte weight loads per lane in each of the two register banks.
-constexpr int step_bank_loads(int b) { return b <= 4 ? 12 : 8; }
+constexpr int step_bank_loads(int b) { return b <= 8 ? 12 : b <= 10 ? 8 : b <= 11 ? 6 : 4; }
 
 // Stream rows [k0, k0+nr) of a column tile through two register banks of
 // NB loads per lane: while one bank is multiplied the other is in flight,
 // and the oldest loads are always the ones waited for. The lane's rows are
-// r0 + i*RSTEP for i = 0, 1, ... in order, as in valu_finish, so a tile of
-// the same rows gives the same bits.
-template <int B, int COLS, int NB>
-__device__ __forceinline__ void stream_rows(const float* xs, const uint16_t* w, int64_t H,
-                                            int64_t k0, int nr, int ct, float (&acc)[B][8]) {
-    constexpr int LPR = COLS / 8;
-    constexpr int RPW = 64 / LPR;
-    constexpr int RSTEP = kValuWaves * RPW;
-    constexpr int BR = RSTEP * NB;  // rows per bank
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n = (int64_t)ct * COLS + (lane % LPR) * 8;
-    const bool col_ok = n < H;
-    const int r0 = wave * RPW + lane / LPR;
-    const uint16_t* wp = w + (k0 + r0) * H + n;
-    auto load_bank = [&](u32x4_t (&v)[NB], int base) {
+// r0 + i*RSTEP for i = 0, 1, ..., in pairs in order, as in valu_finish, so a
+// tile of the same rows gives the same bits. stream_issue loads a tile's
+// first two banks (the decode step issues them for its next tile before it
+// reduces the current one); stream_run multiplies the tile, streaming the
+// rest, and leaves both banks consumed.
+template <int COLS>
+struct LaneRows {
+    static constexpr int LPR = COLS / 8;
+    static constexpr int RPW = 64 / LPR;
+    static constexpr int RSTEP = kValuWaves * RPW;
+    // Rows [k0, k0+nr) of the matrix as a raw buffer: a 16-byte load past
+    // row nr reads zero. The lane's byte offset of its first row and
+    // column; lanes past column H start beyond the buffer (reads are zero).
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff, row_bytes;
+    int r0, nr;
+    __device__ __forceinline__ LaneRows(const uint16_t* w, int64_t H, int64_t k0, int nr_, int ct) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int64_t n = (int64_t)ct * COLS + (lane % LPR) * 8;
+        r0 = wave * RPW + lane / LPR;
+        nr = nr_;
+        row_bytes = (uint32_t)(H * 2);
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w + k0 * H), (short)0,
+                                               (int)((int64_t)nr * H * 2), kBufferRsrcWord3);
+        voff = n < H ? (uint32_t)(r0 * H + n) * 2u : 0x80000000u;
+    }
+};
+
+template <int COLS, int NB>
+__device__ __forceinline__ void stream_bank(u32x4_t (&v)[NB], const LaneRows<COLS>& t, int64_t H,
+                                            int base) {
+    constexpr int RSTEP = LaneRows<COLS>::RSTEP;
+    (void)H;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int r = base + i * RSTEP;
-            v[i] = (col_ok && r0 + r < nr) ? load_stream16(wp + (int64_t)r * H)
-                                           : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
+    for (int i = 0; i < NB; ++i)
+        v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               t.rs, t.voff + (uint32_t)(base + i * RSTEP) * t.row_bytes,
+                                               0, kCachePolicyNT));
+}
+
+template <int COLS, int NB>
+__device__ __forceinline__ void stream_issue(u32x4_t (&va)[NB], u32x4_t (&vb)[NB],
+                                             const LaneRows<COLS>& t, int64_t H) {
+    stream_bank<COLS, NB>(va, t, H, 0);
+    stream_bank<COLS, NB>(vb, t, H, LaneRows<COLS>::RSTEP * NB);
+}
+
+template <int B, int COLS, int NB>
+__device__ __forceinline__ void stream_run(u32x4_t (&va)[NB], u32x4_t (&vb)[NB],
+                                           const LaneRows<COLS>& t, int64_t H, const uint32_t* xs,
+                                           float (&acc)[B][8]) {
+    constexpr int RSTEP = LaneRows<COLS>::RSTEP;
+    constexpr int BR = RSTEP * NB;  // rows per bank
+    static_assert(NB % 2 == 0, "rows are taken in pairs");
     auto fma_bank = [&](const u32x4_t (&v)[NB], int base) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int r = r0 + base + i * RSTEP;
-            if (r < nr) fma_row<B>(acc, v[i], &xs[r * B]);
+        for (int i = 0; i < NB; i += 2) {
+            const int r = t.r0 + base + i * RSTEP;
+            if (r < t.nr) dot2_rows<B>(acc, v[i], v[i + 1], &xs[r * B]);
         }
     };
-    u32x4_t va[NB], vb[NB];
-    load_bank(va, 0);
-    load_bank(vb, BR);
-    for (int base = 0; base < nr; base += 2 * BR) {
+    for (int base = 0; base < t.nr; base += 2 * BR) {
         fma_bank(va, base);
-        if (base + 2 * BR < nr) load_bank(va, base + 2 * BR);
+        if (base + 2 * BR < t.nr) stream_bank<COLS, NB>(va, t, H, base + 2 * BR);
         fma_bank(vb, base + BR);
-        if (base + 3 * BR < nr) load_bank(vb, base + 3 * BR);
+        if (base + 3 * BR < t.nr) stream_bank<COLS, NB>(vb, t, H, base + 3 * BR);
     }
 }
 
@@ -488,18 +553,40 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         return sh.wflag != 0;
     };
 
-    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+    // Tile q of the step: point kind, column tile, split, rows.
+    struct Tile {
+        int pt, ct, sp, j, nr;
+        int64_t K, k0;
+        const uint16_t* x;
+        const uint16_t* w;
+    };
+    auto tile_of = [&](int64_t q) -> Tile {
+        Tile t;
         const int l = (int)(q / per_layer);
         const int rem = (int)(q - (int64_t)l * per_layer);
-        const int pt = rem >= a.tiles[0];
-        const int t = pt ? rem - a.tiles[0] : rem;
-        const int ct = t % a.col_tiles, sp = t / a.col_tiles;
-        const int j = 2 * l + pt;  // point index in the step
-        const int64_t K = a.K[pt];
-        const int64_t k0 = (int64_t)sp * a.rows[pt];
-        const int nr = (int)(K - k0 < a.rows[pt] ? K - k0 : a.rows[pt]);
-        const uint16_t* x = a.x[pt] + (int64_t)l * B * K;
-        const uint16_t* w = a.w[pt] + (int64_t)l * K * a.H;
+        t.pt = rem >= a.tiles[0];
+        const int r = t.pt ? rem - a.tiles[0] : rem;
+        t.ct = r % a.col_tiles;
+        t.sp = r / a.col_tiles;
+        t.j = 2 * l + t.pt;  // point index in the step
+        t.K = a.K[t.pt];
+        t.k0 = (int64_t)t.sp * a.rows[t.pt];
+        t.nr = (int)(t.K - t.k0 < a.rows[t.pt] ? t.K - t.k0 : a.rows[t.pt]);
+        t.x = a.x[t.pt] + (int64_t)l * B * t.K;
+        t.w = a.w[t.pt] + (int64_t)l * t.K * a.H;
+        return t;
+    };
+
+    // The workgroup's tiles q = blockIdx.x + m*gridDim.x. A tile's first two
+    // banks are issued before the previous tile is reduced and published.
+    u32x4_t va[NB], vb[NB];
+    if ((int64_t)blockIdx.x < total) {
+        const Tile t0 = tile_of(blockIdx.x);
+        stream_issue<COLS, NB>(va, vb, LaneRows<COLS>(t0.w, a.H, t0.k0, t0.nr, t0.ct), a.H);
+    }
+    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const Tile tq = tile_of(q);
+        const int pt = tq.pt, ct = tq.ct, sp = tq.sp, j = tq.j;
         const int splits = a.splits[pt];
         uint32_t* fixed = a.fixed + ct * kCounterStride;
 
@@ -508,30 +595,8 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         // later wait fails at once, so the grid drains.
         if (a.serial && !wait_all(done, (uint32_t)j * a.col_tiles)) break;
 
-        // x[:, k0 .. k0+nr) as fp32, [row][B]; 16-byte loads where the
-        // slice starts 16-byte aligned in every row of x
-        if ((K & 7) == 0 && (k0 & 7) == 0) {
-            const int per_b = nr >> 3;
-            for (int i = tid; i < per_b * B; i += NT) {
-                const int bb = i / per_b, r = (i - bb * per_b) * 8;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)bb * K + k0 + r);
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    sh.xs[(r + 2 * h) * B + bb] = bf16_lo(u[h]);
-                    sh.xs[(r + 2 * h + 1) * B + bb] = bf16_hi(u[h]);
-                }
-            }
-            for (int i = tid; i < (nr & 7) * B; i += NT) {
-                const int bb = i / (nr & 7), r = (nr & ~7) + i - bb * (nr & 7);
-                sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
-            }
-        } else {
-            for (int i = tid; i < nr * B; i += NT) {
-                const int bb = i / nr, r = i - bb * nr;
-                sh.xs[r * B + bb] = bf16_to_f32(x[(int64_t)bb * K + k0 + r]);
-            }
-        }
+        constexpr int RSTEP = LaneRows<COLS>::RSTEP;
+        stage_x_pairs<B, RSTEP, NT>(sh.xs, tq.x, tq.K, tq.k0, tq.nr);
         __syncthreads();
 
         float acc[B][8];
@@ -539,7 +604,11 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         for (int bb = 0; bb < B; ++bb)
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[bb][c] = 0.f;
-        stream_rows<B, COLS, NB>(sh.xs, w, a.H, k0, nr, ct, acc);
+        stream_run<B, COLS, NB>(va, vb, LaneRows<COLS>(tq.w, a.H, tq.k0, tq.nr, ct), a.H, sh.xs, acc);
+        if (q + gridDim.x < total) {
+            const Tile tn = tile_of(q + gridDim.x);
+            stream_issue<COLS, NB>(va, vb, LaneRows<COLS>(tn.w, a.H, tn.k0, tn.nr, tn.ct), a.H);
+        }
         reduce_tile<B, COLS>(acc, sh.red, sh.tile);
 
         // the split set of point j was last used by point j - kStepBufs (a
@@ -588,12 +657,6 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
 }
 
 // ------------------------------------------------------------ MFMA GEMM --
-
-// Select the low (even column) or high (odd column) bf16 of two row words
-// into one k-major pair: result = {row0 half, row1 half}.
-__device__ __forceinline__ uint32_t pair_rows(uint32_t row0, uint32_t row1, bool high) {
-    return __builtin_amdgcn_perm(row1, row0, high ? 0x07060302u : 0x05040100u);
-}
 
 template <int BT>  // batch tiles of 16 rows
 __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm(GemvArgs a, int batch) {
@@ -872,7 +935,10 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
         kFixedOffset + (int64_t)geo[0].col_tiles * kCounterStride * 4 > kCounterBytes)
         return TP_ERR_UNSUPPORTED;
     for (int pt = 0; pt < 2; ++pt)
+        // (the lanes' 32-bit buffer offsets, rows read ahead included, stay
+        // below 2^31, so that a lane past column H stays out of range)
         if (geo[pt].rows < 1 || (int64_t)geo[pt].rows * b > kStepXsFloats ||
+            (int64_t)(geo[pt].rows + 1024) * p->hidden * 2 >= ((int64_t)1 << 31) ||
             (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
             return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * (geo[0].grid + geo[1].grid) >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
