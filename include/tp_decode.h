@@ -215,10 +215,10 @@ tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* res
  * results equal tp_rowparallel_partial followed by tp_ring_reduce at each
  * point, bit for bit. For batch < 16 the whole step is one cooperative
  * (persistent) launch whose tiles are 128 columns ("valu_cols") by long row
- * ranges (at most "step_rows" rows and 8192 / batch, as few splits of K_r as
- * that allows), streamed; with the same tiles as the per-point launches
- * (valu_cols and splits_attn / splits_ffn set so that both take the same
- * rows) the bits are the same too. Point order as in
+ * ranges (at most "step_rows" rows and about 16384 / batch; as few splits
+ * of K_r as that allows), streamed; with the same tiles as the per-point
+ * launches (valu_cols and splits_attn / splits_ffn set so that both take
+ * the same rows) the bits are the same too. Point order as in
  * tp_decode_layers_packed: by default each hidden-state element follows its
  * own chain; "serial_points" = 1 makes every point wait for all of the
  * previous one. Both give the same bits. The workspace's error word

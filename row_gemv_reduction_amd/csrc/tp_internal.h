@@ -22,7 +22,7 @@ constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
 // the split buffer / arrival counter sets (points in flight), default tile
 // width and tile length.
 constexpr int64_t kFixedOffset = 192 * 1024;
-constexpr int kStepXsFloats = 8192;
+constexpr int kStepXsWords = 8192;
 constexpr int kStepBufs = 8;
 constexpr int kStepCols = 128;
 constexpr int kStepMaxRows = 2048;

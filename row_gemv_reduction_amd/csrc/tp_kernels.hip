@@ -275,25 +275,30 @@ __device__ __forceinline__ void dot2_rows(float (&acc)[B][8], const u32x4_t& ra,
 }
 
 // Stage x[:, k0 .. k0+nr) for dot2_rows: a lane's rows are r0 + i*RSTEP,
-// taken in pairs (i even, i+1), so the pair of row a (a / RSTEP even) is
-// stored at xp[a*B + bb] = {x[bb][k0+a], x[bb][k0+a+RSTEP]}; a partner row
-// past the tile reads as zero (its weights are zero too, and nothing stale
-// in LDS is ever multiplied).
+// taken in pairs (i even, i+1). Rows a with a / RSTEP even start a pair;
+// pair p = (a / (2*RSTEP))*RSTEP + a % RSTEP is stored densely at
+// xp[p*B + bb] = {x[bb][k0+a], x[bb][k0+a+RSTEP]} (pair_index gives p). A
+// partner row past the tile reads as zero (its weights are zero too, and
+// nothing stale in LDS is ever multiplied).
 template <int B, int RSTEP, int NT>
 __device__ __forceinline__ void stage_x_pairs(uint32_t* xp, const uint16_t* x, int64_t K, int64_t k0,
                                               int nr) {
     const int nblk = (nr + 2 * RSTEP - 1) / (2 * RSTEP);
     const int per_b = nblk * RSTEP;
     for (int i = threadIdx.x; i < per_b * B; i += NT) {
-        const int bb = i / per_b, rem = i - bb * per_b;
-        const int ra = (rem / RSTEP) * 2 * RSTEP + rem % RSTEP;
+        const int bb = i / per_b, p = i - bb * per_b;
+        const int ra = (p / RSTEP) * 2 * RSTEP + p % RSTEP;
         if (ra >= nr) continue;
         const uint16_t* xr = x + (int64_t)bb * K + k0;
         const uint32_t lo = xr[ra];
         const uint32_t hi = ra + RSTEP < nr ? xr[ra + RSTEP] : 0u;
-        xp[ra * B + bb] = lo | (hi << 16);
+        xp[p * B + bb] = lo | (hi << 16);
     }
 }
+
+// Pair index of the pair starting at row r0 + m*RSTEP (m even, r0 < RSTEP).
+template <int RSTEP>
+__device__ __forceinline__ int pair_index(int r0, int m) { return (m / 2) * RSTEP + r0; }
 
 template <int B, int COLS>
 struct ValuShared {
@@ -382,7 +387,7 @@ __device__ void valu_finish(ValuShared<B, COLS>& sh, const u32x4_t (&wv)[kValuLo
 #pragma unroll
     for (int i = 0; i < kValuLoadsPerLane; i += 2) {
         int r = r0 + i * RSTEP;
-        if (r < nr) dot2_rows<B>(acc, wv[i], wv[i + 1], &sh.xs[r * B]);
+        if (r < nr) dot2_rows<B>(acc, wv[i], wv[i + 1], &sh.xs[pair_index<RSTEP>(r0, i) * B]);
     }
     reduce_tile<B, COLS>(acc, sh.red, sh.tile);
 }
@@ -433,7 +438,7 @@ struct StepArgs {
 
 template <int B, int COLS>
 struct StepShared {
-    uint32_t xs[kStepXsFloats];  // the tile's x row pairs, see stage_x_pairs
+    uint32_t xs[kStepXsWords];  // the tile's x row pairs (dense), see stage_x_pairs
     float red[kValuWaves * COLS];
     __attribute__((aligned(16))) float tile[B * COLS];
     int flag;
@@ -501,10 +506,11 @@ __device__ __forceinline__ void stream_run(u32x4_t (&va)[NB], u32x4_t (&vb)[NB],
     constexpr int BR = RSTEP * NB;  // rows per bank
     static_assert(NB % 2 == 0, "rows are taken in pairs");
     auto fma_bank = [&](const u32x4_t (&v)[NB], int base) {
+        // base is a multiple of 2*RSTEP (banks hold an even number of loads)
 #pragma unroll
         for (int i = 0; i < NB; i += 2) {
             const int r = t.r0 + base + i * RSTEP;
-            if (r < t.nr) dot2_rows<B>(acc, v[i], v[i + 1], &xs[r * B]);
+            if (r < t.nr) dot2_rows<B>(acc, v[i], v[i + 1], &xs[pair_index<RSTEP>(t.r0, base / RSTEP + i) * B]);
         }
     };
     for (int base = 0; base < t.nr; base += 2 * BR) {
@@ -937,7 +943,7 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     for (int pt = 0; pt < 2; ++pt)
         // (the lanes' 32-bit buffer offsets, rows read ahead included, stay
         // below 2^31, so that a lane past column H stays out of range)
-        if (geo[pt].rows < 1 || (int64_t)geo[pt].rows * b > kStepXsFloats ||
+        if (geo[pt].rows < 1 || (int64_t)(geo[pt].rows / 2 + 16) * b > kStepXsWords ||
             (int64_t)(geo[pt].rows + 1024) * p->hidden * 2 >= ((int64_t)1 << 31) ||
             (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
             return TP_ERR_UNSUPPORTED;
