@@ -197,6 +197,8 @@ def dense_run(args, w, tune):
         kernel = "decode step on row-major weights (%s)" % (
             "MFMA skinny GEMM + ring epilogue, one launch per point" if w.batch >= 16
             else "persistent VALU step")
+    if args.op != "step":
+        return single_op_run(args, w, plan, info, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
     ms = time_steps(step, args.steps, args.warmup, stream)
     serial_knob = (info["packed_kind"] == 1) if layout == "packed" else (w.batch < 16)
@@ -219,6 +221,55 @@ def dense_run(args, w, tune):
               "weight_bytes_per_step": w.weight_bytes_per_step()}
     extra["traffic"] = measured_traffic(w, layout)
     return ms, w.batch, w.algorithmic_bytes_per_step(), kernel, config, cpu, extra
+
+
+def single_op_run(args, w, plan, info, inputs, ws, stream):
+    """One entry point on its own, once per reconciliation point of the
+    stack (2L calls per pass, each its own launch, weights from HBM):
+    "partial" = tp_rowparallel_partial (row-major slice), "ring" =
+    tp_ring_reduce (ring-order sum of the N partials + residual)."""
+    import torch
+
+    import row_gemv_reduction_amd as tp
+    xa, wo, xf, wd, slots, hidden = inputs
+    b, H, N, L = w.batch, w.hidden, w.n_ranks, w.layers
+    if args.op == "partial":
+        def step():
+            for l in range(L):
+                tp.tp_rowparallel_partial(plan, 0, xa[l], wo[l], slots[l, 0, args.rank], ws)
+                tp.tp_rowparallel_partial(plan, 1, xf[l], wd[l], slots[l, 1, args.rank], ws)
+        # weights + x slices + the fp32 partials written
+        nbytes = L * ((w.ka_r + w.ki_r) * H * 2 + b * (w.ka_r + w.ki_r) * 2 + 2 * b * H * 4)
+        path = "MFMA skinny GEMM (mfma_gemm)" if b >= 16 else "VALU GEMV (valu_gemv)"
+        kernel = "tp_rowparallel_partial, %s, splits %s, one launch per point" % (path, info["splits"])
+    else:
+        def step():
+            for l in range(L):
+                tp.tp_ring_reduce(plan, slots[l, 0], hidden, hidden)
+                tp.tp_ring_reduce(plan, slots[l, 1], hidden, hidden)
+        # N partials and the residual read, the sum written
+        nbytes = 2 * L * (N + 2) * b * H * 4
+        kernel = "tp_ring_reduce (ring_reduce_kernel), one launch per point"
+    log("op %s: %d launches per pass" % (args.op, 2 * L))
+    # Issued one call at a time, the pass measures the host's launch rate
+    # (about 10 us per call through the binding); captured once into a HIP
+    # graph and replayed, it measures the kernels.
+    ms_eager = time_steps(step, args.steps, args.warmup, stream)
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    ms = time_steps(graph.replay, args.steps, args.warmup, stream)
+    config = {"workload": w.name, "op": args.op, "hidden": H, "inter": w.inter, "k_attn": w.k_attn,
+              "layers": L, "n_ranks": N, "rank": args.rank, "batch": b,
+              "launches_per_pass": 2 * L, "us_per_launch": round(ms * 1e3 / (2 * L), 3),
+              "timing": "HIP graph of the pass, replayed",
+              "us_per_launch_eager": round(ms_eager * 1e3 / (2 * L), 3),
+              "weight_layout": "rowmajor"}
+    assert tp.tp_workspace_status(plan, ws) == 0
+    return ms, b, nbytes, kernel, config, None, {"traffic": None}
 
 
 def moe_build(w, rank, copies, seed=0):
@@ -390,6 +441,9 @@ def main():
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
+    ap.add_argument("--op", choices=["step", "partial", "ring"], default="step",
+                    help="what a timed pass runs: the whole decode step (default), or one entry "
+                         "point per reconciliation point (tp_rowparallel_partial, tp_ring_reduce)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -409,6 +463,8 @@ def main():
     for kv in args.tune:
         k, v = kv.split("=")
         tune[k] = int(v)
+    if w.n_experts and args.op != "step":
+        raise SystemExit("--op applies to the dense workloads")
     run = moe_run if w.n_experts else dense_run
     ms, tokens, step_bytes, kernel, config, cpu, extra = run(args, w, tune)
     if args.copy_calibration:
