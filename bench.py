@@ -224,16 +224,29 @@ def dense_run(args, w, tune):
 
 
 def single_op_run(args, w, plan, info, inputs, ws, stream):
-    """One entry point on its own, once per reconciliation point of the
-    stack (2L calls per pass, each its own launch, weights from HBM):
-    "partial" = tp_rowparallel_partial (row-major slice), "ring" =
-    tp_ring_reduce (ring-order sum of the N partials + residual)."""
+    """One entry point on its own over the stack, weights from HBM:
+    "partials" = tp_rowparallel_partials (the 2L partial projections in
+    layer order, one call); "partial" = tp_rowparallel_partial and "ring" =
+    tp_ring_reduce (ring-order sum of the N partials + residual), once per
+    reconciliation point (2L calls per pass, each its own launch)."""
     import torch
 
     import row_gemv_reduction_amd as tp
     xa, wo, xf, wd, slots, hidden = inputs
     b, H, N, L = w.batch, w.hidden, w.n_ranks, w.layers
-    if args.op == "partial":
+    graph_ok = True
+    if args.op == "partials":
+        def step():
+            tp.tp_rowparallel_partials(plan, L, xa, wo, xf, wd, pstack, ws)
+        pstack = torch.empty((L, 2, b, H), dtype=torch.float32, device="cuda")
+        nbytes = L * ((w.ka_r + w.ki_r) * H * 2 + b * (w.ka_r + w.ki_r) * 2 + 2 * b * H * 4)
+        if b < 16:
+            graph_ok = False  # one cooperative launch per pass
+            kernel = ("tp_rowparallel_partials: the persistent step's tiles without ring or "
+                      "residual (decode_step), one launch per pass")
+        else:
+            kernel = "tp_rowparallel_partials: mfma_gemm, one launch per point"
+    elif args.op == "partial":
         def step():
             for l in range(L):
                 tp.tp_rowparallel_partial(plan, 0, xa[l], wo[l], slots[l, 0, args.rank], ws)
@@ -255,19 +268,24 @@ def single_op_run(args, w, plan, info, inputs, ws, stream):
     # (about 10 us per call through the binding); captured once into a HIP
     # graph and replayed, it measures the kernels.
     ms_eager = time_steps(step, args.steps, args.warmup, stream)
-    step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    ms = time_steps(graph.replay, args.steps, args.warmup, stream)
+    launches = 1 if not graph_ok else 2 * L
     config = {"workload": w.name, "op": args.op, "hidden": H, "inter": w.inter, "k_attn": w.k_attn,
               "layers": L, "n_ranks": N, "rank": args.rank, "batch": b,
-              "launches_per_pass": 2 * L, "us_per_launch": round(ms * 1e3 / (2 * L), 3),
-              "timing": "HIP graph of the pass, replayed",
-              "us_per_launch_eager": round(ms_eager * 1e3 / (2 * L), 3),
-              "weight_layout": "rowmajor"}
+              "launches_per_pass": launches, "weight_layout": "rowmajor"}
+    if graph_ok:
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        ms = time_steps(graph.replay, args.steps, args.warmup, stream)
+        config.update({"us_per_launch": round(ms * 1e3 / launches, 3),
+                       "timing": "HIP graph of the pass, replayed",
+                       "us_per_launch_eager": round(ms_eager * 1e3 / launches, 3)})
+    else:
+        ms = ms_eager
+        config.update({"us_per_launch": round(ms * 1e3, 3), "timing": "eager, one launch"})
     assert tp.tp_workspace_status(plan, ws) == 0
     return ms, b, nbytes, kernel, config, None, {"traffic": None}
 
@@ -441,9 +459,11 @@ def main():
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
-    ap.add_argument("--op", choices=["step", "partial", "ring"], default="step",
-                    help="what a timed pass runs: the whole decode step (default), or one entry "
-                         "point per reconciliation point (tp_rowparallel_partial, tp_ring_reduce)")
+    ap.add_argument("--op", choices=["step", "partials", "partial", "ring"], default="step",
+                    help="what a timed pass runs: the whole decode step (default); the stack's "
+                         "2L partial projections in one call (tp_rowparallel_partials); or one "
+                         "entry point per reconciliation point (tp_rowparallel_partial, "
+                         "tp_ring_reduce)")
     args = ap.parse_args()
 
     if args.gpus != 1:

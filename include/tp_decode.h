@@ -183,6 +183,27 @@ tp_status tp_rowparallel_partial(tp_plan_t plan, int32_t point, const void* x, c
                                  float* p, void* workspace, void* stream);
 
 /*
+ * The partial projections of a whole layer stack, in layer order, in one
+ * call (lesson 9.9, Conceito: the rank's partial at each of a layer's two
+ * reconciliation points; no reduction, no residual):
+ *     p[l][0] = x_attn[l] . w_o[l],   p[l][1] = x_ffn[l] . w_down[l]
+ *   x_attn bf16 [L][batch][k_attn/N]   w_o    bf16 [L][k_attn/N][hidden]
+ *   x_ffn  bf16 [L][batch][inter/N]    w_down bf16 [L][inter/N][hidden]
+ *   p      fp32 [L][2][batch][hidden] (output)
+ * For batch < 16 one cooperative launch with the tiles of the persistent
+ * decode step (tp_decode_layers): p[l][point] equals the slot that
+ * tp_decode_layers writes for this rank with the same plan, bit for bit.
+ * For batch >= 16 (or "decode_mode" = 1) one launch per point, equal to
+ * tp_rowparallel_partial's. n_layers = 0 does nothing (the pointers may
+ * then be null). Errors as tp_rowparallel_partial, and TP_ERR_INVALID_ARG
+ * for n_layers < 0, TP_ERR_ALIGNMENT if batch * K_r is not a multiple of 8
+ * for either point (the stacked slices must stay 16-byte aligned).
+ */
+tp_status tp_rowparallel_partials(tp_plan_t plan, int32_t n_layers, const void* x_attn,
+                                  const void* w_o, const void* x_ffn, const void* w_down,
+                                  float* p, void* workspace, void* stream);
+
+/*
  * Ring-ordered all-reduce sum of the N partials plus the residual
  * (lesson 9.9, Conceito; "Hosting Qwen on Blackwell", All-Reduce). The
  * payload is the flattened [batch x hidden] vector cut into N chunks of

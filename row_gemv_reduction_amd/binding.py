@@ -61,6 +61,8 @@ EXPORTS = {
     "tp_rowparallel_partial": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+    "tp_rowparallel_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
+                                + [ctypes.c_void_p] * 7),
     "tp_ring_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tp_decode_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
@@ -220,6 +222,24 @@ def tp_rowparallel_partial(plan: Plan, point, x, w, p, workspace):
         raise ValueError("workspace too small")
     _check(_lib().tp_rowparallel_partial(plan.handle, point, *args, _stream()),
            "tp_rowparallel_partial")
+
+
+def tp_rowparallel_partials(plan: Plan, n_layers, x_attn, w_o, x_ffn, w_down, p, workspace):
+    """The 2L partials of a layer stack in one call: p [L][2][batch][hidden]."""
+    i = plan._plan_info()
+    b, H = i["batch"], i["hidden"]
+    ka, ki = i["k_rank"]
+    L = n_layers
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, b, ka)),
+            _dev(w_o, "w_o", torch.bfloat16, (L, ka, H)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, (L, b, ki)),
+            _dev(w_down, "w_down", torch.bfloat16, (L, ki, H)),
+            _dev(p, "p", torch.float32, (L, 2, b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_rowparallel_partials(plan.handle, L, *args, _stream()),
+           "tp_rowparallel_partials")
 
 
 def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):

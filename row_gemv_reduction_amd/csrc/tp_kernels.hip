@@ -155,7 +155,8 @@ __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int6
 // sum over the N ranks formed in registers (ring_element with a residual of
 // -0.0, which leaves every value as it is), all before `wait_prev` waits for
 // (j-1, ct); only the residual's read, one addition and the store of the
-// hidden state follow it. Same bits as fixup_tile. Returns false if the
+// hidden state follow it. Same bits as fixup_tile. Without ring slots
+// (partials only) it writes the partial and returns. Returns false if the
 // wait failed.
 template <int B, int COLS, int NT, typename Wait>
 __device__ bool step_fixup(const Epilogue& e, const float* tile, int64_t H, int ct, int tid,
@@ -195,11 +196,16 @@ __device__ bool step_fixup(const Epilogue& e, const float* tile, int64_t H, int 
             v = *reinterpret_cast<const floatx4_t*>(tile + bb * COLS + c);
         }
         *reinterpret_cast<floatx4_t*>(e.p + i) = v;
+        if (!e.ring_slots) continue;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             ring[u][k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], -0.0f);
     }
     if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
+    if (!e.ring_slots) {  // partials only: no residual chain
+        wait_mem();
+        return true;
+    }
     if (!wait_prev()) return false;
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -423,6 +429,7 @@ struct StepArgs {
     const uint16_t* w[2];   // w_o [L][K0][H], w_down [L][K1][H]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
+    float* partials;        // partials only (no ring, no residual): [L][2][B][H]
     float* ws_part;         // kStepBufs split-partial buffers
     int64_t part_stride;    // floats between two buffers
     uint32_t* counters;     // column-tile arrival counters, kStepBufs sets
@@ -532,7 +539,9 @@ __device__ __forceinline__ void stream_run(u32x4_t (&va)[NB], u32x4_t (&vb)[NB],
 // later points stream while earlier ones are reduced. Points rotate over
 // kStepBufs sets of split buffers and arrival counters; a split of point j
 // publishes only once (j - kStepBufs, c) has been fixed, which frees its
-// set. With `serial` the step also emulates a model whose activation at
+// set (counted per set and column tile, so that this holds also where
+// fix-ups complete out of point order: the partials-only mode has no
+// residual chain). With `serial` the step also emulates a model whose activation at
 // point j depends on the whole hidden state after j-1: every tile of point
 // j waits, before it reads x, until all column tiles of j-1 are fixed. Each
 // wait targets tiles earlier in the grid-stride order, and the launch is
@@ -617,16 +626,17 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         }
         reduce_tile<B, COLS>(acc, sh.red, sh.tile);
 
-        // the split set of point j was last used by point j - kStepBufs (a
-        // single split uses none; the wait before its fix-up covers it)
+        // The split set of point j was last used by point j - kStepBufs:
+        // publish once this set's earlier rounds are fixed for this column
+        // tile (word 2 of the tile's counter line counts them, in whatever
+        // order the points' fix-ups complete). A single split uses no set.
         const int set = j % kStepBufs;
-        if (!a.serial && splits > 1 && j >= kStepBufs &&
-            !wait_all(fixed, (uint32_t)(j - kStepBufs + 1)))
-            break;
+        uint32_t* rounds = a.counters + ((int64_t)set * a.col_tiles + ct) * kCounterStride + 2;
+        if (splits > 1 && j >= kStepBufs && !wait_all(rounds, (uint32_t)(j / kStepBufs))) break;
 
-        float* slot = a.slots + (int64_t)j * a.n_ranks * len;
+        float* slot = a.partials ? nullptr : a.slots + (int64_t)j * a.n_ranks * len;
         Epilogue e{};
-        e.p = slot + (int64_t)a.rank * len;
+        e.p = a.partials ? a.partials + (int64_t)j * len : slot + (int64_t)a.rank * len;
         e.ws_part = a.ws_part + (int64_t)set * a.part_stride;
         e.counters = a.counters + (int64_t)set * a.col_tiles * kCounterStride;
         e.splits = splits;
@@ -640,9 +650,12 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
             auto wait_prev = [&]() -> bool {
                 return a.serial || j == 0 || wait_all(fixed, (uint32_t)j);
             };
+            // (partials only: step_fixup returns before wait_prev, and the
+            // fixed counters order nothing)
             if (!step_fixup<B, COLS, NT>(e, sh.tile, a.H, ct, tid, wait_prev)) break;
             __syncthreads();
             if (tid == 0) {
+                if (splits > 1) add_dev_u32(rounds, 1u);  // after the arrival counter's reset
                 add_dev_u32(a.serial ? done : fixed, 1u);
                 wait_mem();
             }
@@ -655,6 +668,8 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
     __syncthreads();
     if (sh.flag) {
         for (int c = tid; c < a.col_tiles; c += NT) st_dev_u32(a.fixed + c * kCounterStride, 0u);
+        for (int c = tid; c < kStepBufs * a.col_tiles; c += NT)
+            st_dev_u32(a.counters + (int64_t)c * kCounterStride + 2, 0u);
         if (tid == 0) {
             st_dev_u32(done, 0u);
             st_dev_u32(a.sync + kSyncExit, 0u);
@@ -928,9 +943,11 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
+// The persistent step; with `partials` set, only the 2L partials (no ring,
+// no residual) into partials [L][2][b][H].
 tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
                             const void* w_o, const void* x_ffn, const void* w_down, float* slots,
-                            float* hidden, void* ws, hipStream_t st) {
+                            float* hidden, float* partials, void* ws, hipStream_t st) {
     const int b = p->batch;
     if (b < 1 || b > kValuMaxBatch) return TP_ERR_UNSUPPORTED;
     PointGeom geo[2] = {tp_step_geom(p, 0), tp_step_geom(p, 1)};
@@ -959,12 +976,13 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     a.w[1] = static_cast<const uint16_t*>(w_down);
     a.slots = slots;
     a.hidden = hidden;
+    a.partials = partials;
     a.ws_part = ws_partials(ws);
     a.part_stride = part_stride;
     a.counters = ws_counters(ws);
     a.fixed = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kFixedOffset);
     a.sync = ws_sync(ws);
-    a.serial = p->serial_points ? 1 : 0;
+    a.serial = p->serial_points && !partials ? 1 : 0;
     a.H = p->hidden;
     for (int pt = 0; pt < 2; ++pt) {
         a.K[pt] = geo[pt].k_r;
@@ -1028,6 +1046,41 @@ tp_status tp_rowparallel_partial(tp_plan_t p, int32_t point, const void* x, cons
     e.counters = ws_counters(ws);
     e.splits = g.splits;
     return launch_projection(p, g, p->batch, x, w, e, (hipStream_t)stream);
+}
+
+tp_status tp_rowparallel_partials(tp_plan_t p, int32_t n_layers, const void* x_attn, const void* w_o,
+                                  const void* x_ffn, const void* w_down, float* out, void* ws,
+                                  void* stream) {
+    if (!p || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (n_layers == 0) return TP_OK;  // nothing is read or written
+    if (!x_attn || !w_o || !x_ffn || !w_down || !out || !ws) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x_attn) || !aligned16(w_o) || !aligned16(x_ffn) || !aligned16(w_down) ||
+        !aligned16(out) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    const int64_t b = p->batch, H = p->hidden, len = b * H;
+    PointGeom geo[2] = {tp_point_geom(p, 0), tp_point_geom(p, 1)};
+    // every slice of the stacked inputs must stay 16-byte aligned
+    for (int pt = 0; pt < 2; ++pt)
+        if ((b * geo[pt].k_r) % 8) return TP_ERR_ALIGNMENT;
+    hipStream_t st = (hipStream_t)stream;
+    if (tp_decode_mode(p) == 2)
+        return decode_persistent(p, n_layers, 0, x_attn, w_o, x_ffn, w_down, nullptr, nullptr, out,
+                                 ws, st);
+    for (int32_t l = 0; l < n_layers; ++l)
+        for (int pt = 0; pt < 2; ++pt) {
+            const PointGeom& g = geo[pt];
+            const uint16_t* xb = static_cast<const uint16_t*>(pt == 0 ? x_attn : x_ffn);
+            const uint16_t* wb = static_cast<const uint16_t*>(pt == 0 ? w_o : w_down);
+            Epilogue e{};
+            e.p = out + ((int64_t)l * 2 + pt) * len;
+            e.ws_part = ws_partials(ws);
+            e.counters = ws_counters(ws);
+            e.splits = g.splits;
+            tp_status s = launch_projection(p, g, (int)b, xb + (int64_t)l * b * g.k_r,
+                                            wb + (int64_t)l * g.k_r * H, e, st);
+            if (s != TP_OK) return s;
+        }
+    return TP_OK;
 }
 
 tp_status tp_ring_reduce(tp_plan_t p, const float* partials, const float* residual, float* out,
@@ -1094,7 +1147,8 @@ tp_status tp_decode_layers(tp_plan_t p, int32_t n_layers, int32_t rank, const vo
         if ((b * geo[pt].k_r) % 8) return TP_ERR_ALIGNMENT;
     hipStream_t st = (hipStream_t)stream;
     if (tp_decode_mode(p) == 2)
-        return decode_persistent(p, n_layers, rank, x_attn, w_o, x_ffn, w_down, slots, hidden, ws, st);
+        return decode_persistent(p, n_layers, rank, x_attn, w_o, x_ffn, w_down, slots, hidden,
+                                 nullptr, ws, st);
     for (int32_t l = 0; l < n_layers; ++l) {
         for (int pt = 0; pt < 2; ++pt) {
             const PointGeom& g = geo[pt];

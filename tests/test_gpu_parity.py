@@ -448,6 +448,49 @@ def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
     assert err <= 4 * L * 1e-5 * rms_p + 8 * np.spacing(np.abs(h2).max()), err
 
 
+@pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 1, 1032, 1024, 17408, 3), (2, 8, 1032, 2048, 8192, 5),
+                                           (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 2),
+                                           (4, 16, 1032, 1024, 4096, 2), (2, 40, 520, 640, 1376, 2)])
+def test_partials_stack(n, b, h, ka, ki, L):
+    """tp_rowparallel_partials: every p[l][point] against the oracle; bit for
+    bit equal to the rank's slot of tp_decode_layers with the same plan (the
+    same tiles, b < 16) or to tp_rowparallel_partial (b >= 16); repeated
+    calls give the same bits."""
+    rank = n - 1
+    say("partials stack n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 41, rank)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    ws = plan.new_workspace()
+    X = [to_dev_bf16(a) for a in (xa, wo, xf, wd)]
+    P = torch.empty((L, 2, b, h), dtype=torch.float32, device="cuda")
+    tp.tp_rowparallel_partials(plan, L, *X, P, ws)
+    P2 = torch.full_like(P, float("nan"))
+    tp.tp_rowparallel_partials(plan, L, *X, P2, ws)
+    torch.cuda.synchronize()
+    assert tp.tp_workspace_status(plan, ws) == 0
+    got = host(P)
+    assert_bits_equal(host(P2), got, "repeat")
+    for l in range(L):
+        assert_partial_close(got[l, 0], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
+        assert_partial_close(got[l, 1], oracle.partial(xf[l], wd[l])[0], "ffn l=%d" % l)
+    if b < 16:
+        S = to_dev_f32(slots)
+        Hd = to_dev_f32(h0)
+        tp.tp_decode_layers(plan, L, rank, *X, S, Hd, ws)
+        torch.cuda.synchronize()
+        assert_bits_equal(got, host(S)[:, :, rank], "decode slots")
+    else:
+        for l in range(L):
+            for pt, (x, w) in enumerate(((X[0][l], X[1][l]), (X[2][l], X[3][l]))):
+                Q = torch.empty((b, h), dtype=torch.float32, device="cuda")
+                tp.tp_rowparallel_partial(plan, pt, x, w, Q, ws)
+                torch.cuda.synchronize()
+                assert_bits_equal(got[l, pt], host(Q), "partial l=%d pt=%d" % (l, pt))
+    # an empty stack is a no-op
+    tp.tp_rowparallel_partials(plan, 0, *[t[:0] for t in X], P[:0], ws)
+    torch.cuda.synchronize()
+
+
 def test_persistent_step_repeated_runs_are_identical():
     """Race check for the in-launch split exchange: 20 steps of the page-1
     shape (rank 0 of 4, batch 1; 12 points, more than the step's split-buffer
