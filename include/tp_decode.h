@@ -116,7 +116,10 @@ tp_status tp_plan_set_attn_dim(tp_plan_t plan, int64_t k_attn);
 tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int32_t ep,
                           int64_t moe_inter, int32_t max_tokens);
 
-/* Tuning knobs (advanced; the defaults are tuned for MI355X). Known keys:
+/* Tuning knobs (advanced; the defaults are tuned for MI355X). A knob that
+ * changes the tiles ("splits_*", "valu_cols", "step_rows", "stream_wgs",
+ * "target_wgs") can change info.workspace_bytes: size the workspace after
+ * tuning ("serial_points" changes no tile). Known keys:
  * "splits_attn", "splits_ffn" (split-K factor, 0 = automatic),
  * "valu_cols" (columns per VALU workgroup: 128, 256 or 512),
  * "decode_mode" (0 = automatic, 1 = one launch per point,
@@ -133,8 +136,12 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "serial_points" (tp_decode_layers and tp_decode_layers_packed: 0 = each
  *                hidden-state element follows its own chain, 1 = point j+1
  *                also waits for all of point j, see there),
+ * "target_wgs" (per-point launches: workgroups a point's split-K grid
+ *                aims at, 0 = automatic: one per CU for the matrix cores,
+ *                two for the vector ALU),
  * "step_rows" (tp_decode_layers, batch < 16: most rows per tile of the
- *                persistent step, 0 = automatic, 2048).
+ *                persistent step, 0 = automatic: 2048 for 512-column tiles,
+ *                1024 for narrower ones).
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
@@ -235,9 +242,10 @@ tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* res
  * For batch >= 16 (or "decode_mode" = 1) each point is one launch, and the
  * results equal tp_rowparallel_partial followed by tp_ring_reduce at each
  * point, bit for bit. For batch < 16 the whole step is one cooperative
- * (persistent) launch whose tiles are 128 columns ("valu_cols") by long row
- * ranges (at most "step_rows" rows and about 16384 / batch; as few splits
- * of K_r as that allows), streamed; with the same tiles as the per-point
+ * (persistent) launch whose tiles are 512 columns (256 where hidden < 5120;
+ * "valu_cols") by long row ranges (at most "step_rows" rows, 2048 for 512
+ * columns and 1024 for 256, and about 16384 / batch; as few splits of K_r
+ * as that allows), streamed; with the same tiles as the per-point
  * launches (valu_cols and splits_attn / splits_ffn set so that both take
  * the same rows) the bits are the same too. Point order as in
  * tp_decode_layers_packed: by default each hidden-state element follows its

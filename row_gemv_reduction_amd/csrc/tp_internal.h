@@ -19,13 +19,14 @@ constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, er
 constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
 // Persistent row-major decode step (decode_step): points completed per
 // column tile (stride kCounterStride), the x slice of a tile staged in LDS,
-// the split buffer / arrival counter sets (points in flight), default tile
-// width and tile length.
+// the split buffer / arrival counter sets (points in flight), and the
+// default tiles: 512 columns by up to 2048 rows where that still gives at
+// least kStepWideTiles column tiles, else 256 by up to 1024 (measured at
+// H = 5120 and 4096, b = 1 and 8).
 constexpr int64_t kFixedOffset = 192 * 1024;
 constexpr int kStepXsWords = 8192;
 constexpr int kStepBufs = 8;
-constexpr int kStepCols = 128;
-constexpr int kStepMaxRows = 2048;
+constexpr int kStepWideTiles = 10;
 // VALU GEMV geometry limits
 constexpr int kValuWaves = 4;        // waves per workgroup
 constexpr int kValuMaxRows = 512;    // rows of x staged in LDS per workgroup

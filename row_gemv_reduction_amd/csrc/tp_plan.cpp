@@ -76,22 +76,24 @@ int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p) {
     return round_up(m, 256);
 }
 
-// Persistent decode step: 128-column tiles (256-byte row segments) over
-// long row ranges, as few splits as the LDS copy of the tile's x slice
-// (kStepXsWords words of bf16 pairs) and the tile length cap allow, so most points need no
-// split exchange at all. With splits_user the rows follow the same rule as
-// the per-point launches (equal tiles give equal bits).
+// Persistent decode step: 512- or 256-column tiles (1 KB or 512-byte row
+// segments) over long row ranges, as few splits as the LDS copy of the
+// tile's x slice (kStepXsWords words of bf16 pairs) and the tile length cap
+// allow, so most points need no split exchange at all. With splits_user
+// the rows follow the same rule as the per-point launches (equal tiles
+// give equal bits).
 PointGeom tp_step_geom(const tp_plan_s* p, int point) {
     PointGeom g{};
     g.k_r = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
     g.path = TP_PATH_VALU;
-    g.cols = p->valu_cols ? p->valu_cols : kStepCols;
+    const bool wide = p->hidden / 512 >= kStepWideTiles;
+    g.cols = p->valu_cols ? p->valu_cols : (wide ? 512 : 256);
     g.col_tiles = (int32_t)ceil_div(p->hidden, g.cols);
     const int64_t gran = (int64_t)kValuWaves * (64 / (g.cols / 8));
     const int b = p->batch > 0 ? p->batch : 1;
     // x is staged as bf16 pairs: (rows/2 + 16) * b of the kStepXsWords words
     int64_t max_rows = 2 * (kStepXsWords / b - 16);
-    const int64_t cap = p->step_rows > 0 ? p->step_rows : kStepMaxRows;
+    const int64_t cap = p->step_rows > 0 ? p->step_rows : (g.cols >= 512 ? 2048 : 1024);
     if (max_rows > cap) max_rows = cap;
     max_rows -= max_rows % gran;
     if (max_rows < gran) max_rows = gran;

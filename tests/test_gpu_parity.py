@@ -415,7 +415,8 @@ def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols, splits_a
 
 
 @pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 1, 1032, 1024, 17408, 6), (2, 8, 1032, 2048, 8192, 5),
-                                           (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 3)])
+                                           (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 3),
+                                           (2, 3, 5120, 1024, 8192, 5)])
 def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
     """The step's own tiles (long row ranges; splits only where the x slice
     or the tile length cap asks for them): both point orders give the same
@@ -450,7 +451,8 @@ def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
 
 @pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 1, 1032, 1024, 17408, 3), (2, 8, 1032, 2048, 8192, 5),
                                            (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 2),
-                                           (4, 16, 1032, 1024, 4096, 2), (2, 40, 520, 640, 1376, 2)])
+                                           (4, 16, 1032, 1024, 4096, 2), (2, 40, 520, 640, 1376, 2),
+                                           (2, 3, 5120, 1024, 8192, 5)])
 def test_partials_stack(n, b, h, ka, ki, L):
     """tp_rowparallel_partials: every p[l][point] against the oracle; bit for
     bit equal to the rank's slot of tp_decode_layers with the same plan (the
