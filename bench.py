@@ -194,11 +194,14 @@ def dense_run(args, w, tune):
     else:
         def step():
             tp.tp_decode_layers(plan, w.layers, args.rank, xa, wo, xf, wd, slots, hidden, ws)
-        kernel = "decode step on row-major weights (%s)" % (
-            "MFMA skinny GEMM + ring epilogue, one launch per point" if w.batch >= 16
-            else "persistent VALU step")
+        if tune.get("decode_mode", 0) == 1:
+            kernel = "decode step on row-major weights (one launch per point: %s + ring epilogue)" % (
+                "mfma_gemm" if w.batch >= 16 else "valu_gemv")
+        else:
+            kernel = "decode step on row-major weights (one persistent launch: %s)" % (
+                "decode_step_mfma" if w.batch >= 16 else "decode_step")
     if args.op != "step":
-        return single_op_run(args, w, plan, info, (xa, wo, xf, wd, slots, hidden), ws, stream)
+        return single_op_run(args, w, plan, info, tune, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
     ms = time_steps(step, args.steps, args.warmup, stream)
     serial_knob = (info["packed_kind"] == 1) if layout == "packed" else (w.batch < 16)
@@ -223,7 +226,7 @@ def dense_run(args, w, tune):
     return ms, w.batch, w.algorithmic_bytes_per_step(), kernel, config, cpu, extra
 
 
-def single_op_run(args, w, plan, info, inputs, ws, stream):
+def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
     """One entry point on its own over the stack, weights from HBM:
     "partials" = tp_rowparallel_partials (the 2L partial projections in
     layer order, one call); "partial" = tp_rowparallel_partial and "ring" =
@@ -240,12 +243,14 @@ def single_op_run(args, w, plan, info, inputs, ws, stream):
             tp.tp_rowparallel_partials(plan, L, xa, wo, xf, wd, pstack, ws)
         pstack = torch.empty((L, 2, b, H), dtype=torch.float32, device="cuda")
         nbytes = L * ((w.ka_r + w.ki_r) * H * 2 + b * (w.ka_r + w.ki_r) * 2 + 2 * b * H * 4)
-        if b < 16:
+        if tune.get("decode_mode", 0) != 1:
             graph_ok = False  # one cooperative launch per pass
             kernel = ("tp_rowparallel_partials: the persistent step's tiles without ring or "
-                      "residual (decode_step), one launch per pass")
+                      "residual (%s), one launch per pass"
+                      % ("decode_step_mfma" if b >= 16 else "decode_step"))
         else:
-            kernel = "tp_rowparallel_partials: mfma_gemm, one launch per point"
+            kernel = "tp_rowparallel_partials: %s, one launch per point" % (
+                "mfma_gemm" if b >= 16 else "valu_gemv")
     elif args.op == "partial":
         def step():
             for l in range(L):

@@ -139,9 +139,9 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "target_wgs" (per-point launches: workgroups a point's split-K grid
  *                aims at, 0 = automatic: one per CU for the matrix cores,
  *                two for the vector ALU),
- * "step_rows" (tp_decode_layers, batch < 16: most rows per tile of the
- *                persistent step, 0 = automatic: 2048 for 512-column tiles,
- *                1024 for narrower ones).
+ * "step_rows" (tp_decode_layers: most rows per tile of the persistent
+ *                step, 0 = automatic: 2048 for 512-column and matrix-core
+ *                tiles, 1024 for narrower vector-ALU ones).
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
@@ -197,11 +197,10 @@ tp_status tp_rowparallel_partial(tp_plan_t plan, int32_t point, const void* x, c
  *   x_attn bf16 [L][batch][k_attn/N]   w_o    bf16 [L][k_attn/N][hidden]
  *   x_ffn  bf16 [L][batch][inter/N]    w_down bf16 [L][inter/N][hidden]
  *   p      fp32 [L][2][batch][hidden] (output)
- * For batch < 16 one cooperative launch with the tiles of the persistent
- * decode step (tp_decode_layers): p[l][point] equals the slot that
- * tp_decode_layers writes for this rank with the same plan, bit for bit.
- * For batch >= 16 (or "decode_mode" = 1) one launch per point, equal to
- * tp_rowparallel_partial's. n_layers = 0 does nothing (the pointers may
+ * One cooperative launch with the tiles of the persistent decode step
+ * (tp_decode_layers): p[l][point] equals the slot that tp_decode_layers
+ * writes for this rank with the same plan, bit for bit. With "decode_mode"
+ * = 1, one launch per point, equal to tp_rowparallel_partial's. n_layers = 0 does nothing (the pointers may
  * then be null). Errors as tp_rowparallel_partial, and TP_ERR_INVALID_ARG
  * for n_layers < 0, TP_ERR_ALIGNMENT if batch * K_r is not a multiple of 8
  * for either point (the stacked slices must stay 16-byte aligned).
@@ -239,15 +238,18 @@ tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* res
  *   slots  fp32 [L][2][N][batch][hidden]: the other N-1 ranks' partials are
  *          inputs; entry [l][point][rank] is overwritten with this rank's
  *   hidden fp32 [batch][hidden], in/out (the residual stream)
- * For batch >= 16 (or "decode_mode" = 1) each point is one launch, and the
- * results equal tp_rowparallel_partial followed by tp_ring_reduce at each
- * point, bit for bit. For batch < 16 the whole step is one cooperative
- * (persistent) launch whose tiles are 512 columns (256 where hidden < 5120;
- * "valu_cols") by long row ranges (at most "step_rows" rows, 2048 for 512
- * columns and 1024 for 256, and about 16384 / batch; as few splits of K_r
- * as that allows), streamed; with the same tiles as the per-point
- * launches (valu_cols and splits_attn / splits_ffn set so that both take
- * the same rows) the bits are the same too. Point order as in
+ * The whole step is one cooperative (persistent) launch over tiles of long
+ * row ranges, streamed. For batch < 16: vector-ALU tiles of 512 columns
+ * (256 where hidden < 5120; "valu_cols") by at most "step_rows" rows (2048
+ * for 512 columns, 1024 for 256) and about 16384 / batch; with the same
+ * tiles as the per-point launches (valu_cols and splits_attn / splits_ffn
+ * set so that both take the same rows) the bits equal those of
+ * tp_rowparallel_partial followed by tp_ring_reduce at each point. For
+ * batch >= 16: matrix-core tiles of 128 columns by at most 2048 rows
+ * ("step_rows"), whose fp32 sums are ordered differently from
+ * tp_rowparallel_partial's (both within the partial tolerance). With
+ * "decode_mode" = 1 each point is one launch and the results equal
+ * tp_rowparallel_partial followed by tp_ring_reduce, bit for bit. Point order as in
  * tp_decode_layers_packed: by default each hidden-state element follows its
  * own chain; "serial_points" = 1 makes every point wait for all of the
  * previous one. Both give the same bits. The workspace's error word

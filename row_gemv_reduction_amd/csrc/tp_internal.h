@@ -27,6 +27,8 @@ constexpr int64_t kFixedOffset = 192 * 1024;
 constexpr int kStepXsWords = 8192;
 constexpr int kStepBufs = 8;
 constexpr int kStepWideTiles = 10;
+// matrix-core decode step (b >= 16): waves per workgroup
+constexpr int kStepMfmaWaves = 8;
 // VALU GEMV geometry limits
 constexpr int kValuWaves = 4;        // waves per workgroup
 constexpr int kValuMaxRows = 512;    // rows of x staged in LDS per workgroup

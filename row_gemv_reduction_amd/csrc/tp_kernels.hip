@@ -158,14 +158,14 @@ __device__ void fixup_tile(const Epilogue& e, const float* tile, int batch, int6
 // hidden state follow it. Same bits as fixup_tile. Without ring slots
 // (partials only) it writes the partial and returns. Returns false if the
 // wait failed.
-template <int B, int COLS, int NT, typename Wait>
-__device__ bool step_fixup(const Epilogue& e, const float* tile, int64_t H, int ct, int tid,
-                           Wait wait_prev) {
+template <int BMAX, int COLS, int NT, typename Wait>
+__device__ bool step_fixup(const Epilogue& e, const float* tile, int batch, int64_t H, int ct,
+                           int tid, Wait wait_prev) {
 #pragma clang fp contract(off)
-    constexpr int NV = B * COLS / 4;  // 16-byte vectors in the tile
-    constexpr int VPT = (NV + NT - 1) / NT;
+    constexpr int VPT = (BMAX * COLS / 4 + NT - 1) / NT;
+    const int NV = batch * COLS / 4;  // 16-byte vectors in the tile
     const int64_t n0 = (int64_t)ct * COLS;
-    const int64_t len = (int64_t)B * H;
+    const int64_t len = (int64_t)batch * H;
     const __amdgpu_buffer_rsrc_t rp = dev_rsrc(e.ws_part, (uint32_t)((int64_t)e.splits * len * 4));
     const __amdgpu_buffer_rsrc_t rh = dev_rsrc(e.hidden, (uint32_t)(len * 4));
     floatx4_t ring[VPT];
@@ -425,11 +425,11 @@ __global__ __launch_bounds__(kValuWaves * 64) void valu_gemv(GemvArgs a) {
 // ------------------------------------------------------- decode step --
 
 struct StepArgs {
-    const uint16_t* x[2];   // x_attn [L][B][K0], x_ffn [L][B][K1]
+    const uint16_t* x[2];   // x_attn [L][b][K0], x_ffn [L][b][K1]
     const uint16_t* w[2];   // w_o [L][K0][H], w_down [L][K1][H]
-    float* slots;           // [L][2][N][B][H]
-    float* hidden;          // [B][H]
-    float* partials;        // partials only (no ring, no residual): [L][2][B][H]
+    float* slots;           // [L][2][N][b][H]
+    float* hidden;          // [b][H]
+    float* partials;        // partials only (no ring, no residual): [L][2][b][H]
     float* ws_part;         // kStepBufs split-partial buffers
     int64_t part_stride;    // floats between two buffers
     uint32_t* counters;     // column-tile arrival counters, kStepBufs sets
@@ -438,10 +438,102 @@ struct StepArgs {
     int64_t H, K[2];
     int32_t rows[2], splits[2], tiles[2];
     int32_t col_tiles, layers, n_ranks, rank;
+    int32_t batch;
     int32_t serial;         // 1: point j+1 reads its activation after all of point j
     int64_t chunk;
     uint32_t spin_limit;
 };
+
+// Tile q of a step: (layer, point kind) in order, then split-major over the
+// column tiles.
+struct StepTile {
+    int pt, ct, sp, j, nr, splits;
+    int64_t K, k0;
+    const uint16_t* x;  // the point's x [b][K]
+    const uint16_t* w;  // the point's W [K][H]
+};
+__device__ __forceinline__ StepTile step_tile(const StepArgs& a, int64_t q) {
+    StepTile t;
+    const int per_layer = a.tiles[0] + a.tiles[1];
+    const int l = (int)(q / per_layer);
+    const int rem = (int)(q - (int64_t)l * per_layer);
+    t.pt = rem >= a.tiles[0];
+    const int r = t.pt ? rem - a.tiles[0] : rem;
+    t.ct = r % a.col_tiles;
+    t.sp = r / a.col_tiles;
+    t.j = 2 * l + t.pt;  // point index in the step
+    t.K = a.K[t.pt];
+    t.k0 = (int64_t)t.sp * a.rows[t.pt];
+    t.nr = (int)(t.K - t.k0 < a.rows[t.pt] ? t.K - t.k0 : a.rows[t.pt]);
+    t.splits = a.splits[t.pt];
+    t.x = a.x[t.pt] + (int64_t)l * a.batch * t.K;
+    t.w = a.w[t.pt] + (int64_t)l * t.K * a.H;
+    return t;
+}
+
+// After a tile's partial is in LDS (tile[b][COLS]): publish it to this
+// point's split set, and the last arrival fixes the column tile (splits in
+// split order, the rank's slot, the ring and the residual, or the partial
+// alone). `wait_all(ctr, target)` is the workgroup's bounded wait. Returns
+// false if a wait failed (the caller stops its walk).
+template <int BMAX, int COLS, int NT, typename WaitAll>
+__device__ bool step_tile_epilogue(const StepArgs& a, const StepTile& t, const float* tile,
+                                   int* s_flag, WaitAll wait_all) {
+    const int tid = threadIdx.x, j = t.j, ct = t.ct;
+    const int64_t len = (int64_t)a.batch * a.H;
+    uint32_t* fixed = a.fixed + ct * kCounterStride;
+    // The split set of point j was last used by point j - kStepBufs:
+    // publish once this set's earlier rounds are fixed for this column tile
+    // (word 2 of the tile's counter line counts them, in whatever order the
+    // points' fix-ups complete). A single split uses no set.
+    const int set = j % kStepBufs;
+    uint32_t* rounds = a.counters + ((int64_t)set * a.col_tiles + ct) * kCounterStride + 2;
+    if (t.splits > 1 && j >= kStepBufs && !wait_all(rounds, (uint32_t)(j / kStepBufs))) return false;
+
+    float* slot = a.partials ? nullptr : a.slots + (int64_t)j * a.n_ranks * len;
+    Epilogue e{};
+    e.p = a.partials ? a.partials + (int64_t)j * len : slot + (int64_t)a.rank * len;
+    e.ws_part = a.ws_part + (int64_t)set * a.part_stride;
+    e.counters = a.counters + (int64_t)set * a.col_tiles * kCounterStride;
+    e.splits = t.splits;
+    e.ring_slots = slot;
+    e.hidden = a.hidden;
+    e.n_ranks = a.n_ranks;
+    e.rank = a.rank;
+    e.chunk = a.chunk;
+    if (publish_split<COLS, NT>(e, tile, a.batch, a.H, ct, t.sp, tid, s_flag)) {
+        // the residual columns of this tile are those (j-1, ct) wrote
+        // (partials only: step_fixup returns before waiting)
+        auto wait_prev = [&]() -> bool { return a.serial || j == 0 || wait_all(fixed, (uint32_t)j); };
+        if (!step_fixup<BMAX, COLS, NT>(e, tile, a.batch, a.H, ct, tid, wait_prev)) return false;
+        __syncthreads();
+        if (tid == 0) {
+            if (t.splits > 1) add_dev_u32(rounds, 1u);  // after the arrival counter's reset
+            add_dev_u32(a.serial ? a.sync + kSyncDone : fixed, 1u);
+            wait_mem();
+        }
+    }
+    return true;
+}
+
+// The last workgroup to leave resets the step's sync words for the next
+// launch (no workgroup waits on them any more).
+template <int NT>
+__device__ void step_exit(const StepArgs& a, int* s_flag) {
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if (tid == 0) *s_flag = add_dev_u32(a.sync + kSyncExit, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (*s_flag) {
+        for (int c = tid; c < a.col_tiles; c += NT) st_dev_u32(a.fixed + c * kCounterStride, 0u);
+        for (int c = tid; c < kStepBufs * a.col_tiles; c += NT)
+            st_dev_u32(a.counters + (int64_t)c * kCounterStride + 2, 0u);
+        if (tid == 0) {
+            st_dev_u32(a.sync + kSyncDone, 0u);
+            st_dev_u32(a.sync + kSyncExit, 0u);
+        }
+    }
+}
 
 template <int B, int COLS>
 struct StepShared {
@@ -554,61 +646,30 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
     constexpr int NB = step_bank_loads(B);
     __shared__ StepShared<B, COLS> sh;
     const int tid = threadIdx.x;
-    uint32_t* done = a.sync + kSyncDone;
-    uint32_t* err = a.sync + kSyncErr;
-    const int64_t len = (int64_t)B * a.H;
-    const int per_layer = a.tiles[0] + a.tiles[1];
-    const int64_t total = (int64_t)a.layers * per_layer;
+    const int64_t total = (int64_t)a.layers * (a.tiles[0] + a.tiles[1]);
 
     // tid 0 waits until *ctr >= target; every thread gets the outcome
     auto wait_all = [&](uint32_t* ctr, uint32_t target) -> bool {
-        if (tid == 0) sh.wflag = wait_at_least(ctr, target, err, a.spin_limit);
+        if (tid == 0) sh.wflag = wait_at_least(ctr, target, a.sync + kSyncErr, a.spin_limit);
         __syncthreads();
         compiler_barrier();
         return sh.wflag != 0;
-    };
-
-    // Tile q of the step: point kind, column tile, split, rows.
-    struct Tile {
-        int pt, ct, sp, j, nr;
-        int64_t K, k0;
-        const uint16_t* x;
-        const uint16_t* w;
-    };
-    auto tile_of = [&](int64_t q) -> Tile {
-        Tile t;
-        const int l = (int)(q / per_layer);
-        const int rem = (int)(q - (int64_t)l * per_layer);
-        t.pt = rem >= a.tiles[0];
-        const int r = t.pt ? rem - a.tiles[0] : rem;
-        t.ct = r % a.col_tiles;
-        t.sp = r / a.col_tiles;
-        t.j = 2 * l + t.pt;  // point index in the step
-        t.K = a.K[t.pt];
-        t.k0 = (int64_t)t.sp * a.rows[t.pt];
-        t.nr = (int)(t.K - t.k0 < a.rows[t.pt] ? t.K - t.k0 : a.rows[t.pt]);
-        t.x = a.x[t.pt] + (int64_t)l * B * t.K;
-        t.w = a.w[t.pt] + (int64_t)l * t.K * a.H;
-        return t;
     };
 
     // The workgroup's tiles q = blockIdx.x + m*gridDim.x. A tile's first two
     // banks are issued before the previous tile is reduced and published.
     u32x4_t va[NB], vb[NB];
     if ((int64_t)blockIdx.x < total) {
-        const Tile t0 = tile_of(blockIdx.x);
+        const StepTile t0 = step_tile(a, blockIdx.x);
         stream_issue<COLS, NB>(va, vb, LaneRows<COLS>(t0.w, a.H, t0.k0, t0.nr, t0.ct), a.H);
     }
     for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
-        const Tile tq = tile_of(q);
-        const int pt = tq.pt, ct = tq.ct, sp = tq.sp, j = tq.j;
-        const int splits = a.splits[pt];
-        uint32_t* fixed = a.fixed + ct * kCounterStride;
+        const StepTile tq = step_tile(a, q);
 
         __syncthreads();  // LDS of the previous tile is no longer read
         // A failed wait (error word set) ends the workgroup's walk; every
         // later wait fails at once, so the grid drains.
-        if (a.serial && !wait_all(done, (uint32_t)j * a.col_tiles)) break;
+        if (a.serial && !wait_all(a.sync + kSyncDone, (uint32_t)tq.j * a.col_tiles)) break;
 
         constexpr int RSTEP = LaneRows<COLS>::RSTEP;
         stage_x_pairs<B, RSTEP, NT>(sh.xs, tq.x, tq.K, tq.k0, tq.nr);
@@ -619,62 +680,144 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         for (int bb = 0; bb < B; ++bb)
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[bb][c] = 0.f;
-        stream_run<B, COLS, NB>(va, vb, LaneRows<COLS>(tq.w, a.H, tq.k0, tq.nr, ct), a.H, sh.xs, acc);
+        stream_run<B, COLS, NB>(va, vb, LaneRows<COLS>(tq.w, a.H, tq.k0, tq.nr, tq.ct), a.H, sh.xs, acc);
         if (q + gridDim.x < total) {
-            const Tile tn = tile_of(q + gridDim.x);
+            const StepTile tn = step_tile(a, q + gridDim.x);
             stream_issue<COLS, NB>(va, vb, LaneRows<COLS>(tn.w, a.H, tn.k0, tn.nr, tn.ct), a.H);
         }
         reduce_tile<B, COLS>(acc, sh.red, sh.tile);
+        if (!step_tile_epilogue<B, COLS, NT>(a, tq, sh.tile, &sh.flag, wait_all)) break;
+    }
+    step_exit<NT>(a, &sh.flag);
+}
 
-        // The split set of point j was last used by point j - kStepBufs:
-        // publish once this set's earlier rounds are fixed for this column
-        // tile (word 2 of the tile's counter line counts them, in whatever
-        // order the points' fix-ups complete). A single split uses no set.
-        const int set = j % kStepBufs;
-        uint32_t* rounds = a.counters + ((int64_t)set * a.col_tiles + ct) * kCounterStride + 2;
-        if (splits > 1 && j >= kStepBufs && !wait_all(rounds, (uint32_t)(j / kStepBufs))) break;
+// The matrix-core decode step (b = 16..64, BT tiles of 16 tokens), on the
+// same tiles, point order, split sets and epilogue as decode_step. A tile
+// is 128 columns by up to 2048 rows. Each of the kStepMfmaWaves waves takes
+// 32-row steps (wave w: steps w, w + NW, ...): per lane 8 rows x 16 bytes
+// of weights, transposed with v_perm into k-major B operands, and one
+// 16-byte A operand (8 rows of x) per 16 tokens, both loaded one step
+// ahead, multiplied on v_mfma_f32_16x16x32_bf16. Each row of x is read
+// once per tile (b/128 bytes per weight byte), as staging it would read
+// it, without the staging's wait or its bound on the tile length. The
+// waves' D tiles are summed in wave order in LDS.
+template <int BT>
+struct StepMfmaShared {
+    float red[kStepMfmaWaves * 16 * kMfmaCols];
+    __attribute__((aligned(16))) float tile[BT * 16 * kMfmaCols];
+    int flag;
+    int wflag;
+};
 
-        float* slot = a.partials ? nullptr : a.slots + (int64_t)j * a.n_ranks * len;
-        Epilogue e{};
-        e.p = a.partials ? a.partials + (int64_t)j * len : slot + (int64_t)a.rank * len;
-        e.ws_part = a.ws_part + (int64_t)set * a.part_stride;
-        e.counters = a.counters + (int64_t)set * a.col_tiles * kCounterStride;
-        e.splits = splits;
-        e.ring_slots = slot;
-        e.hidden = a.hidden;
-        e.n_ranks = a.n_ranks;
-        e.rank = a.rank;
-        e.chunk = a.chunk;
-        if (publish_split<COLS, NT>(e, sh.tile, B, a.H, ct, sp, tid, &sh.flag)) {
-            // the residual columns of this tile are those (j-1, ct) wrote
-            auto wait_prev = [&]() -> bool {
-                return a.serial || j == 0 || wait_all(fixed, (uint32_t)j);
-            };
-            // (partials only: step_fixup returns before wait_prev, and the
-            // fixed counters order nothing)
-            if (!step_fixup<B, COLS, NT>(e, sh.tile, a.H, ct, tid, wait_prev)) break;
-            __syncthreads();
-            if (tid == 0) {
-                if (splits > 1) add_dev_u32(rounds, 1u);  // after the arrival counter's reset
-                add_dev_u32(a.serial ? done : fixed, 1u);
-                wait_mem();
+template <int BT>
+__global__ __launch_bounds__(kStepMfmaWaves * 64) void decode_step_mfma(StepArgs a) {
+    constexpr int NW = kStepMfmaWaves;
+    constexpr int NT = NW * 64;
+    constexpr int COLS = kMfmaCols;
+    __shared__ StepMfmaShared<BT> sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4;   // k group: rows 8g .. 8g+7 of a 32-row step
+    const int i = lane & 15;   // column group (B operand) / token row (A operand)
+    const int64_t total = (int64_t)a.layers * (a.tiles[0] + a.tiles[1]);
+
+    auto wait_all = [&](uint32_t* ctr, uint32_t target) -> bool {
+        if (tid == 0) sh.wflag = wait_at_least(ctr, target, a.sync + kSyncErr, a.spin_limit);
+        __syncthreads();
+        compiler_barrier();
+        return sh.wflag != 0;
+    };
+
+    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const StepTile tq = step_tile(a, q);
+        const int nr = tq.nr;
+
+        __syncthreads();  // LDS of the previous tile is no longer read
+        if (a.serial && !wait_all(a.sync + kSyncDone, (uint32_t)tq.j * a.col_tiles)) break;
+
+        // The tile's weight rows as a raw buffer (rows past nr and columns
+        // past H read zero); x [b][K] as another (tokens past b read zero).
+        const int64_t n = (int64_t)tq.ct * COLS + i * 8;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(tq.w + tq.k0 * a.H), (short)0, (int)((int64_t)nr * a.H * 2),
+            kBufferRsrcWord3);
+        const uint32_t row_bytes = (uint32_t)(a.H * 2);
+        const uint32_t voff = n < a.H ? (uint32_t)((8 * g) * a.H + n) * 2u : 0x80000000u;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(tq.x), (short)0, (int)((int64_t)a.batch * tq.K * 2), kBufferRsrcWord3);
+        const bool x_vec = (tq.K & 7) == 0;
+        auto load_step = [&](u32x4_t (&wv)[8], u32x4_t (&xv)[BT], int step) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                wv[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rw, voff + (uint32_t)(step + r) * row_bytes, 0,
+                                                        kCachePolicyNT));
+            // A operands: x[bt*16 + i][k0 + step + 8g .. +7]; rows past the
+            // tile read as zero (their weights are zero too)
+            const int r0 = step + 8 * g;
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+                const uint32_t xo = (uint32_t)(((int64_t)(bt * 16 + i) * tq.K + tq.k0 + r0) * 2);
+                if (x_vec && r0 + 8 <= nr) {
+                    xv[bt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        h[u] = r0 + u < nr ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, xo + 2 * u, 0, 0)
+                                           : 0u;
+                    xv[bt] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                     h[6] | (h[7] << 16)};
+                }
             }
+        };
+
+        floatx4_t acc[BT][8];
+#pragma unroll
+        for (int bt = 0; bt < BT; ++bt)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[bt][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        u32x4_t wv[8], xv[BT];
+        if (wave * 32 < nr) load_step(wv, xv, wave * 32);
+        for (int step = wave * 32; step < nr; step += NW * 32) {
+            // column c's B operand (its 8 rows, k-major) just before its MFMAs
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const bool hi = c & 1;
+                u32x4_t bw;
+                bw.x = pair_rows(wv[0][c >> 1], wv[1][c >> 1], hi);
+                bw.y = pair_rows(wv[2][c >> 1], wv[3][c >> 1], hi);
+                bw.z = pair_rows(wv[4][c >> 1], wv[5][c >> 1], hi);
+                bw.w = pair_rows(wv[6][c >> 1], wv[7][c >> 1], hi);
+                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+                for (int bt = 0; bt < BT; ++bt)
+                    acc[bt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xv[bt]), bop, acc[bt][c], 0, 0, 0);
+            }
+            if (step + NW * 32 < nr) load_step(wv, xv, step + NW * 32);
         }
-    }
-    // The last workgroup to leave resets the step's sync words for the next
-    // launch (no workgroup waits on them any more).
-    __syncthreads();
-    if (tid == 0) sh.flag = add_dev_u32(a.sync + kSyncExit, 1u) == gridDim.x - 1;
-    __syncthreads();
-    if (sh.flag) {
-        for (int c = tid; c < a.col_tiles; c += NT) st_dev_u32(a.fixed + c * kCounterStride, 0u);
-        for (int c = tid; c < kStepBufs * a.col_tiles; c += NT)
-            st_dev_u32(a.counters + (int64_t)c * kCounterStride + 2, 0u);
-        if (tid == 0) {
-            st_dev_u32(done, 0u);
-            st_dev_u32(a.sync + kSyncExit, 0u);
+
+        // D layout of a 16x16 fp32 MFMA tile: lane holds rows 4*(lane/16)+q,
+        // column lane%16; here rows are tokens and MFMA column i' is tile
+        // column 8*i' + c. Waves summed in wave order.
+        for (int bt = 0; bt < BT; ++bt) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    sh.red[(wave * 16 + 4 * g + qq) * COLS + i * 8 + c] = acc[bt][c][qq];
+            __syncthreads();
+            for (int idx = tid; idx < 16 * COLS; idx += NT) {
+                float sum = sh.red[idx];
+#pragma unroll
+                for (int wq = 1; wq < NW; ++wq) sum += sh.red[wq * 16 * COLS + idx];
+                sh.tile[bt * 16 * COLS + idx] = sum;
+            }
+            __syncthreads();
         }
+        if (!step_tile_epilogue<BT * 16, COLS, NT>(a, tq, sh.tile, &sh.flag, wait_all)) break;
     }
+    step_exit<NT>(a, &sh.flag);
 }
 
 // ------------------------------------------------------------ MFMA GEMM --
@@ -839,6 +982,16 @@ step_fn step_kernel_for(int b) {
     return nullptr;
 }
 
+step_fn step_mfma_kernel(int b) {
+    switch ((b + 15) / 16) {
+        case 1: return decode_step_mfma<1>;
+        case 2: return decode_step_mfma<2>;
+        case 3: return decode_step_mfma<3>;
+        case 4: return decode_step_mfma<4>;
+    }
+    return nullptr;
+}
+
 valu_fn valu_kernel(int b, int cols) {
     switch (cols) {
         case 128: return valu_kernel_for<128>(b);
@@ -949,7 +1102,8 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
                             const void* w_o, const void* x_ffn, const void* w_down, float* slots,
                             float* hidden, float* partials, void* ws, hipStream_t st) {
     const int b = p->batch;
-    if (b < 1 || b > kValuMaxBatch) return TP_ERR_UNSUPPORTED;
+    if (b < 1 || b > kMfmaMaxBatch) return TP_ERR_UNSUPPORTED;
+    const bool mfma = b >= kMfmaMinBatch;
     PointGeom geo[2] = {tp_step_geom(p, 0), tp_step_geom(p, 1)};
     if (geo[0].cols != geo[1].cols || geo[0].col_tiles != geo[1].col_tiles) return TP_ERR_UNSUPPORTED;
     // kStepBufs sets of arrival counters in [0, kSyncOffset); the fixed
@@ -957,19 +1111,25 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     if ((int64_t)kStepBufs * geo[0].col_tiles > kMaxCounters ||
         kFixedOffset + (int64_t)geo[0].col_tiles * kCounterStride * 4 > kCounterBytes)
         return TP_ERR_UNSUPPORTED;
+    // the matrix-core step reads x through a buffer of b*K*2 bytes
+    if (mfma && ((int64_t)b * geo[1].k_r * 2 >= ((int64_t)1 << 31) ||
+                 (int64_t)b * geo[0].k_r * 2 >= ((int64_t)1 << 31)))
+        return TP_ERR_UNSUPPORTED;
     for (int pt = 0; pt < 2; ++pt)
         // (the lanes' 32-bit buffer offsets, rows read ahead included, stay
         // below 2^31, so that a lane past column H stays out of range)
-        if (geo[pt].rows < 1 || (int64_t)(geo[pt].rows / 2 + 16) * b > kStepXsWords ||
+        if (geo[pt].rows < 1 || (!mfma && (int64_t)(geo[pt].rows / 2 + 16) * b > kStepXsWords) ||
             (int64_t)(geo[pt].rows + 1024) * p->hidden * 2 >= ((int64_t)1 << 31) ||
             (int64_t)geo[pt].rows * geo[pt].splits < geo[pt].k_r)
             return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * (geo[0].grid + geo[1].grid) >= (int64_t)1 << 31) return TP_ERR_UNSUPPORTED;
     const int64_t part_stride = tp_step_partial_buffer_bytes(p) / 4;
     if (part_stride * 4 * kStepBufs >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
-    step_fn k = step_kernel(b, geo[0].cols);
+    step_fn k = mfma ? step_mfma_kernel(b) : step_kernel(b, geo[0].cols);
+    const int block = mfma ? kStepMfmaWaves * 64 : kValuWaves * 64;
     if (!k) return TP_ERR_UNSUPPORTED;
     StepArgs a;
+    a.batch = b;
     a.x[0] = static_cast<const uint16_t*>(x_attn);
     a.x[1] = static_cast<const uint16_t*>(x_ffn);
     a.w[0] = static_cast<const uint16_t*>(w_o);
@@ -997,15 +1157,15 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     a.chunk = (int64_t)b * p->hidden / p->n_ranks;
     a.spin_limit = 1u << 21;
     if (n_layers == 0) return TP_OK;
-    int cap = resident_grid(reinterpret_cast<const void*>(k), kValuWaves * 64);
+    int cap = resident_grid(reinterpret_cast<const void*>(k), block);
     if (cap < 1) return TP_ERR_DEVICE;
     // Every resident workgroup: the tiles of later points are taken up while
     // earlier ones are reduced (the waits order what must be ordered).
     const int64_t total = (int64_t)n_layers * (geo[0].grid + geo[1].grid);
     int grid = total < cap ? (int)total : cap;
     void* args[] = {&a};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid),
-                                   dim3(kValuWaves * 64), args, 0, st) != hipSuccess)
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(block), args,
+                                   0, st) != hipSuccess)
         return TP_ERR_DEVICE;
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }

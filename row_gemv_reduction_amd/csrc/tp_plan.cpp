@@ -85,6 +85,25 @@ int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p) {
 PointGeom tp_step_geom(const tp_plan_s* p, int point) {
     PointGeom g{};
     g.k_r = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    if (p->batch >= kMfmaMinBatch) {
+        // matrix-core step: 128 columns, 32-row steps, up to 2048 rows
+        g.path = TP_PATH_MFMA;
+        g.cols = kMfmaCols;
+        g.col_tiles = (int32_t)ceil_div(p->hidden, g.cols);
+        int64_t max_rows = p->step_rows > 0 ? p->step_rows : 2048;
+        max_rows -= max_rows % kMfmaKStep;
+        if (max_rows < kMfmaKStep) max_rows = kMfmaKStep;
+        const int32_t su = p->splits_user[point];
+        int64_t s = su > 0 ? su : ceil_div(g.k_r, max_rows);
+        if (s > ceil_div(g.k_r, kMfmaKStep)) s = ceil_div(g.k_r, kMfmaKStep);
+        if (s < 1) s = 1;
+        int64_t rows = round_up(ceil_div(g.k_r, s), kMfmaKStep);
+        if (rows > max_rows) rows = max_rows;
+        g.rows = (int32_t)rows;
+        g.splits = (int32_t)ceil_div(g.k_r, rows);
+        g.grid = g.col_tiles * g.splits;
+        return g;
+    }
     g.path = TP_PATH_VALU;
     const bool wide = p->hidden / 512 >= kStepWideTiles;
     g.cols = p->valu_cols ? p->valu_cols : (wide ? 512 : 256);
@@ -122,7 +141,7 @@ int64_t tp_step_partial_buffer_bytes(const tp_plan_s* p) {
 
 static int64_t partial_bytes(const tp_plan_s* p) {
     int64_t m = tp_ws_partial_buffer_bytes(p);
-    if (p->batch < kMfmaMinBatch) {
+    if (p->batch <= kMfmaMaxBatch) {
         int64_t s = kStepBufs * tp_step_partial_buffer_bytes(p);
         if (s > m) m = s;
     }
@@ -143,7 +162,7 @@ int64_t tp_workspace_bytes(const tp_plan_s* p) {
 
 int tp_decode_mode(const tp_plan_s* p) {
     if (p->decode_mode) return p->decode_mode;
-    return p->batch < kMfmaMinBatch ? 2 : 1;  // persistent step for the VALU path
+    return 2;  // the persistent step (vector ALU below 16 tokens, matrix cores from 16)
 }
 
 extern "C" {

@@ -291,7 +291,7 @@ def test_decode_point_equals_partial_then_ring_bitwise(n, b, h, ka, ki, rank, ff
 
 # ---------------------------------------- benchmark-sized, sampled columns --
 
-def sampled_columns(h, cols_per_tile=256, count=40, seed=0):
+def sampled_columns(h, cols_per_tile=128, count=40, seed=0):
     g = np.random.default_rng(seed)
     edges = {0, h - 1}
     for t in range(0, h, cols_per_tile):
@@ -456,8 +456,9 @@ def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
 def test_partials_stack(n, b, h, ka, ki, L):
     """tp_rowparallel_partials: every p[l][point] against the oracle; bit for
     bit equal to the rank's slot of tp_decode_layers with the same plan (the
-    same tiles, b < 16) or to tp_rowparallel_partial (b >= 16); repeated
-    calls give the same bits."""
+    persistent step's tiles); with decode_mode 1 (one launch per point) bit
+    for bit equal to tp_rowparallel_partial; repeated calls give the same
+    bits."""
     rank = n - 1
     say("partials stack n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 41, rank)
@@ -475,22 +476,64 @@ def test_partials_stack(n, b, h, ka, ki, L):
     for l in range(L):
         assert_partial_close(got[l, 0], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
         assert_partial_close(got[l, 1], oracle.partial(xf[l], wd[l])[0], "ffn l=%d" % l)
-    if b < 16:
-        S = to_dev_f32(slots)
-        Hd = to_dev_f32(h0)
-        tp.tp_decode_layers(plan, L, rank, *X, S, Hd, ws)
-        torch.cuda.synchronize()
-        assert_bits_equal(got, host(S)[:, :, rank], "decode slots")
-    else:
-        for l in range(L):
-            for pt, (x, w) in enumerate(((X[0][l], X[1][l]), (X[2][l], X[3][l]))):
-                Q = torch.empty((b, h), dtype=torch.float32, device="cuda")
-                tp.tp_rowparallel_partial(plan, pt, x, w, Q, ws)
-                torch.cuda.synchronize()
-                assert_bits_equal(got[l, pt], host(Q), "partial l=%d pt=%d" % (l, pt))
+    S = to_dev_f32(slots)
+    Hd = to_dev_f32(h0)
+    tp.tp_decode_layers(plan, L, rank, *X, S, Hd, ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, host(S)[:, :, rank], "decode slots")
+    plan1 = tp.Plan(h, ki, n, b, k_attn=ka, tune={"decode_mode": 1})
+    ws1 = plan1.new_workspace()
+    P1 = torch.empty_like(P)
+    tp.tp_rowparallel_partials(plan1, L, *X, P1, ws1)
+    for l in range(L):
+        for pt, (x, w) in enumerate(((X[0][l], X[1][l]), (X[2][l], X[3][l]))):
+            Q = torch.empty((b, h), dtype=torch.float32, device="cuda")
+            tp.tp_rowparallel_partial(plan1, pt, x, w, Q, ws1)
+            torch.cuda.synchronize()
+            assert_bits_equal(host(P1)[l, pt], host(Q), "partial l=%d pt=%d" % (l, pt))
     # an empty stack is a no-op
     tp.tp_rowparallel_partials(plan, 0, *[t[:0] for t in X], P[:0], ws)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 16, 1032, 1024, 4096, 5), (2, 40, 520, 640, 1376, 9),
+                                           (8, 64, 1024, 2048, 8192, 3), (1, 17, 264, 264, 1000, 2),
+                                           (1, 24, 264, 264, 1001, 2), (2, 16, 5120, 1024, 8192, 3)])
+def test_persistent_mfma_step(n, b, h, ka, ki, L):
+    """The matrix-core persistent step (decode_mode 2, b >= 16): both point
+    orders give the same bits, two chained steps match the oracle, and
+    tp_rowparallel_partials with the same plan gives the rank's slots bit
+    for bit. Ragged token tiles (b = 17, 40), odd K (the element-wise x
+    staging), multi-split points and more points than split sets."""
+    rank = n // 2
+    say("persistent mfma n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 57, rank)
+    X = [to_dev_bf16(t) for t in (xa, wo, xf, wd)]
+    outs = []
+    for serial in (0, 1):
+        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"decode_mode": 2, "serial_points": serial})
+        ws = plan.new_workspace()
+        S = to_dev_f32(slots)
+        Hd = to_dev_f32(h0)
+        for _ in range(2):
+            tp.tp_decode_layers(plan, L, rank, *X, S, Hd, ws)
+        torch.cuda.synchronize()
+        assert tp.tp_workspace_status(plan, ws) == 0
+        outs.append((host(S), host(Hd)))
+    assert_bits_equal(outs[1][0], outs[0][0], "slots")
+    assert_bits_equal(outs[1][1], outs[0][1], "hidden")
+    P = torch.empty((L, 2, b, h), dtype=torch.float32, device="cuda")
+    tp.tp_rowparallel_partials(plan, L, *X, P, ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(P), outs[0][0][:, :, rank], "partials vs slots")
+    _, h1 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
+    _, h2 = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h1)
+    for l in range(L):
+        assert_partial_close(outs[0][0][l, 0, rank], oracle.partial(xa[l], wo[l])[0], "attn")
+        assert_partial_close(outs[0][0][l, 1, rank], oracle.partial(xf[l], wd[l])[0], "ffn")
+    rms_p = np.sqrt(np.mean(outs[0][0][:, :, rank].astype(np.float64) ** 2))
+    err = np.abs(outs[0][1].astype(np.float64) - h2).max()
+    assert err <= 4 * L * 1e-5 * rms_p + 8 * np.spacing(np.abs(h2).max()), err
 
 
 def test_persistent_step_repeated_runs_are_identical():
