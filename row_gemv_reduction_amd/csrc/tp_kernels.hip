@@ -197,9 +197,32 @@ __device__ bool step_fixup(const Epilogue& e, const float* tile, int batch, int6
         }
         *reinterpret_cast<floatx4_t*>(e.p + i) = v;
         if (!e.ring_slots) continue;
+        const int c0 = (int)(i / e.chunk);
+        if (c0 == (int)((i + 3) / e.chunk)) {
+            // the four elements share a ring chunk: the other ranks' values
+            // as 16-byte loads, a group of up to 8 ranks in flight at once,
+            // summed in ring order (element-wise, as ring_element)
+            floatx4_t sum;
+            for (int j0 = 0; j0 < e.n_ranks; j0 += 8) {
+                floatx4_t t[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            ring[u][k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], -0.0f);
+                for (int k = 0; k < 8; ++k) {
+                    const int jj = j0 + k < e.n_ranks ? j0 + k : e.n_ranks - 1;
+                    int r = c0 + jj;
+                    if (r >= e.n_ranks) r -= e.n_ranks;
+                    t[k] = r == e.rank ? v
+                                       : *reinterpret_cast<const floatx4_t*>(e.ring_slots + (int64_t)r * len + i);
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (j0 + k < e.n_ranks) sum = (j0 + k == 0) ? t[k] : sum + t[k];
+            }
+            ring[u] = sum;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                ring[u][k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], -0.0f);
+        }
     }
     if (e.splits > 1 && tid == 0) st_dev_u32(&e.counters[ct * kCounterStride], 0u);
     if (!e.ring_slots) {  // partials only: no residual chain
