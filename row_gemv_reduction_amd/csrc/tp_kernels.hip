@@ -95,6 +95,30 @@ __device__ bool publish_split(const Epilogue& e, const float* tile, int batch, i
     return *s_flag != 0;
 }
 
+// Ring-order sum (no residual) of four consecutive elements i..i+3 that
+// share ring chunk c0: the other ranks' values as 16-byte loads, a group of
+// up to 8 ranks in flight at once, added in ring order element by element
+// (the same bits as ring_element for each). `own` is this rank's vector.
+__device__ __forceinline__ floatx4_t ring_vector(const float* slots, int64_t len, int64_t i, int c0,
+                                                 int n_ranks, int rank, floatx4_t own) {
+#pragma clang fp contract(off)
+    floatx4_t sum;
+    for (int j0 = 0; j0 < n_ranks; j0 += 8) {
+        floatx4_t t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int jj = j0 + k < n_ranks ? j0 + k : n_ranks - 1;
+            int r = c0 + jj;
+            if (r >= n_ranks) r -= n_ranks;
+            t[k] = r == rank ? own : *reinterpret_cast<const floatx4_t*>(slots + (int64_t)r * len + i);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (j0 + k < n_ranks) sum = (j0 + k == 0) ? t[k] : sum + t[k];
+    }
+    return sum;
+}
+
 // One 16-byte vector (4 columns) of the final partial: the splits summed in
 // split order, written to the partial and, with the ring epilogue, the
 // ring-order sum + residual into the hidden state. The residual load goes
@@ -123,9 +147,14 @@ __device__ __forceinline__ void fixup_vector(const Epilogue& e, const float* til
     *reinterpret_cast<floatx4_t*>(e.p + i) = v;
     if (e.ring_slots) {
         floatx4_t o;
+        const int c0 = (int)(i / e.chunk);
+        if (c0 == (int)((i + 3) / e.chunk)) {
+            o = ring_vector(e.ring_slots, len, i, c0, e.n_ranks, e.rank, v) + res;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            o[k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], res[k]);
+            for (int k = 0; k < 4; ++k)
+                o[k] = ring_element(e.ring_slots, len, i + k, e.chunk, e.n_ranks, e.rank, v[k], res[k]);
+        }
         st_dev4(rh, (uint32_t)(i * 4), o);
     }
 }
@@ -199,25 +228,7 @@ __device__ bool step_fixup(const Epilogue& e, const float* tile, int batch, int6
         if (!e.ring_slots) continue;
         const int c0 = (int)(i / e.chunk);
         if (c0 == (int)((i + 3) / e.chunk)) {
-            // the four elements share a ring chunk: the other ranks' values
-            // as 16-byte loads, a group of up to 8 ranks in flight at once,
-            // summed in ring order (element-wise, as ring_element)
-            floatx4_t sum;
-            for (int j0 = 0; j0 < e.n_ranks; j0 += 8) {
-                floatx4_t t[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int jj = j0 + k < e.n_ranks ? j0 + k : e.n_ranks - 1;
-                    int r = c0 + jj;
-                    if (r >= e.n_ranks) r -= e.n_ranks;
-                    t[k] = r == e.rank ? v
-                                       : *reinterpret_cast<const floatx4_t*>(e.ring_slots + (int64_t)r * len + i);
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (j0 + k < e.n_ranks) sum = (j0 + k == 0) ? t[k] : sum + t[k];
-            }
-            ring[u] = sum;
+            ring[u] = ring_vector(e.ring_slots, len, i, c0, e.n_ranks, e.rank, v);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
