@@ -139,6 +139,9 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "target_wgs" (per-point launches: workgroups a point's split-K grid
  *                aims at, 0 = automatic: one per CU for the matrix cores,
  *                two for the vector ALU),
+ * "step_kind" (tp_decode_layers, tp_rowparallel_partials, batch < 16: the
+ *                persistent step's kind, 0 = automatic, 1 = vector ALU,
+ *                2 = matrix cores; from 16 tokens always matrix cores),
  * "step_rows" (tp_decode_layers: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core
  *                tiles, 1024 for narrower vector-ALU ones).
@@ -239,13 +242,16 @@ tp_status tp_ring_reduce(tp_plan_t plan, const float* partials, const float* res
  *          inputs; entry [l][point][rank] is overwritten with this rank's
  *   hidden fp32 [batch][hidden], in/out (the residual stream)
  * The whole step is one cooperative (persistent) launch over tiles of long
- * row ranges, streamed. For batch < 16: vector-ALU tiles of 512 columns
+ * row ranges, streamed. Below 16 tokens the vector-ALU step, unless the
+ * points are small (an FFN slice of at most 2048 rows, or batch >= 8 with
+ * hidden < 5120; "step_kind"), where the matrix-core step is faster. The
+ * vector-ALU step: tiles of 512 columns
  * (256 where hidden < 5120; "valu_cols") by at most "step_rows" rows (2048
  * for 512 columns, 1024 for 256) and about 16384 / batch; with the same
  * tiles as the per-point launches (valu_cols and splits_attn / splits_ffn
  * set so that both take the same rows) the bits equal those of
- * tp_rowparallel_partial followed by tp_ring_reduce at each point. For
- * batch >= 16: matrix-core tiles of 128 columns by at most 2048 rows
+ * tp_rowparallel_partial followed by tp_ring_reduce at each point. The
+ * matrix-core step: tiles of 128 columns by at most 2048 rows
  * ("step_rows"), whose fp32 sums are ordered differently from
  * tp_rowparallel_partial's (both within the partial tolerance). With
  * "decode_mode" = 1 each point is one launch and the results equal

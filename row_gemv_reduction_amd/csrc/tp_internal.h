@@ -85,6 +85,7 @@ struct tp_plan_s {
     int32_t moe_variant = 0;    // expert kernel variant (0 = default)
     int32_t stream_wgs = 0;     // MFMA stream: workgroups (0 = one per CU, at most H/16)
     int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)
+    int32_t step_kind = 0;      // persistent step: 0 = automatic, 1 = vector ALU (b < 16), 2 = matrix cores
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -112,6 +113,7 @@ int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p);
 // and the bytes of one of its kStepBufs split buffers (the workspace holds
 // all of them when the step can run, batch < 16).
 PointGeom tp_step_geom(const tp_plan_s* p, int point);
+bool tp_step_mfma(const tp_plan_s* p);  // the persistent step runs on the matrix cores
 int64_t tp_step_partial_buffer_bytes(const tp_plan_s* p);
 int64_t tp_ws_moe_offset(const tp_plan_s* p);
 int tp_decode_mode(const tp_plan_s* p);

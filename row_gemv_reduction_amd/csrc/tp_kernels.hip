@@ -1137,7 +1137,7 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
                             float* hidden, float* partials, void* ws, hipStream_t st) {
     const int b = p->batch;
     if (b < 1 || b > kMfmaMaxBatch) return TP_ERR_UNSUPPORTED;
-    const bool mfma = b >= kMfmaMinBatch;
+    const bool mfma = tp_step_mfma(p);
     PointGeom geo[2] = {tp_step_geom(p, 0), tp_step_geom(p, 1)};
     if (geo[0].cols != geo[1].cols || geo[0].col_tiles != geo[1].col_tiles) return TP_ERR_UNSUPPORTED;
     // kStepBufs sets of arrival counters in [0, kSyncOffset); the fixed

@@ -82,10 +82,22 @@ int64_t tp_ws_partial_buffer_bytes(const tp_plan_s* p) {
 // allow, so most points need no split exchange at all. With splits_user
 // the rows follow the same rule as the per-point launches (equal tiles
 // give equal bits).
+// The persistent step's kind. Measured on row-major weights (H = 5120 and
+// 4096, b = 1..8): below 16 tokens the matrix-core step's 128-column tiles
+// win where the points are small (an FFN slice of at most 2048 rows, as at
+// H = 4096, N = 8) or at b >= 8 with H < 5120; the vector-ALU step's wide
+// tiles win elsewhere.
+bool tp_step_mfma(const tp_plan_s* p) {
+    if (p->batch >= kMfmaMinBatch || p->step_kind == 2) return true;
+    if (p->step_kind == 1) return false;
+    const int64_t ki_r = p->inter / p->n_ranks;
+    return ki_r <= 2048 || (p->batch >= 8 && p->hidden < 5120);
+}
+
 PointGeom tp_step_geom(const tp_plan_s* p, int point) {
     PointGeom g{};
     g.k_r = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
-    if (p->batch >= kMfmaMinBatch) {
+    if (tp_step_mfma(p)) {
         // matrix-core step: 128 columns, 32-row steps, up to 2048 rows
         g.path = TP_PATH_MFMA;
         g.cols = kMfmaCols;
@@ -236,6 +248,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
+    } else if (!strcmp(key, "step_kind")) {
+        if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
+        p->step_kind = (int32_t)value;
     } else if (!strcmp(key, "step_rows")) {
         if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
         p->step_rows = (int32_t)value;

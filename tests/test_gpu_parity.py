@@ -246,7 +246,8 @@ def test_decode_equals_partial_then_ring_bitwise():
     say("decode vs composition")
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 8, rank)
     # the same tiles for the decode step and the single projection
-    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"valu_cols": 128, "splits_attn": 1, "splits_ffn": 2})
+    plan = tp.Plan(h, ki, n, b, k_attn=ka,
+                   tune={"valu_cols": 128, "splits_attn": 1, "splits_ffn": 2, "step_kind": 1})
     s_gpu, h_gpu = run_decode(plan, L, rank, xa, wo, xf, wd, slots, h0)
     hd = to_dev_f32(h0)
     for l in range(L):
@@ -389,7 +390,7 @@ def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols, splits_a
     for mode, serial in ((1, 0), (2, 0), (2, 1), (2, 0)):
         plan = tp.Plan(h, ki, n, b, k_attn=ka,
                        tune={"decode_mode": mode, "valu_cols": cols, "serial_points": serial,
-                             "splits_attn": splits_attn, "splits_ffn": splits_ffn})
+                             "splits_attn": splits_attn, "splits_ffn": splits_ffn, "step_kind": 1})
         assert plan.info()["splits"] == [splits_attn, splits_ffn]
         ws = plan.new_workspace()
         S = to_dev_f32(slots)
@@ -417,17 +418,19 @@ def test_persistent_step_matches_per_point_launches_bitwise(n, b, cols, splits_a
 @pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 1, 1032, 1024, 17408, 6), (2, 8, 1032, 2048, 8192, 5),
                                            (8, 15, 520, 2048, 8192, 9), (1, 8, 264, 264, 1001, 3),
                                            (2, 3, 5120, 1024, 8192, 5)])
-def test_persistent_step_default_tiles(n, b, h, ka, ki, L):
+@pytest.mark.parametrize("kind", [0, 1])
+def test_persistent_step_default_tiles(n, b, h, ka, ki, L, kind):
     """The step's own tiles (long row ranges; splits only where the x slice
-    or the tile length cap asks for them): both point orders give the same
-    bits, more points than split-buffer sets run through the rotation, and
-    the result matches the oracle (two chained steps)."""
+    or the tile length cap asks for them), with the automatic choice of the
+    step's kind (0) and the vector-ALU step (1): both point orders give the
+    same bits, more points than split-buffer sets run through the rotation,
+    and the result matches the oracle (two chained steps)."""
     rank = n // 2
-    say("persistent default tiles n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
+    say("persistent default tiles n=%d b=%d h=%d ka=%d ki=%d L=%d kind=%d" % (n, b, h, ka, ki, L, kind))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 33, rank)
     outs = []
     for serial in (0, 1):
-        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"serial_points": serial})
+        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"serial_points": serial, "step_kind": kind})
         ws = plan.new_workspace()
         S = to_dev_f32(slots)
         Hd = to_dev_f32(h0)
@@ -498,20 +501,23 @@ def test_partials_stack(n, b, h, ka, ki, L):
 
 @pytest.mark.parametrize("n,b,h,ka,ki,L", [(4, 16, 1032, 1024, 4096, 5), (2, 40, 520, 640, 1376, 9),
                                            (8, 64, 1024, 2048, 8192, 3), (1, 17, 264, 264, 1000, 2),
-                                           (1, 24, 264, 264, 1001, 2), (2, 16, 5120, 1024, 8192, 3)])
+                                           (1, 24, 264, 264, 1001, 2), (2, 16, 5120, 1024, 8192, 3),
+                                           (8, 1, 1024, 2048, 8192, 5), (4, 7, 520, 1024, 4096, 3)])
 def test_persistent_mfma_step(n, b, h, ka, ki, L):
-    """The matrix-core persistent step (decode_mode 2, b >= 16): both point
-    orders give the same bits, two chained steps match the oracle, and
-    tp_rowparallel_partials with the same plan gives the rank's slots bit
-    for bit. Ragged token tiles (b = 17, 40), odd K (the element-wise x
-    staging), multi-split points and more points than split sets."""
+    """The matrix-core persistent step (decode_mode 2, step_kind 2; b = 1
+    and 7 too): both point orders give the same bits, two chained steps
+    match the oracle, and tp_rowparallel_partials with the same plan gives
+    the rank's slots bit for bit. Ragged token tiles (b = 1, 7, 17, 40), odd
+    K (the element-wise x loads), multi-split points and more points than
+    split sets."""
     rank = n // 2
     say("persistent mfma n=%d b=%d h=%d ka=%d ki=%d L=%d" % (n, b, h, ka, ki, L))
     xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 57, rank)
     X = [to_dev_bf16(t) for t in (xa, wo, xf, wd)]
     outs = []
     for serial in (0, 1):
-        plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"decode_mode": 2, "serial_points": serial})
+        plan = tp.Plan(h, ki, n, b, k_attn=ka,
+                       tune={"decode_mode": 2, "serial_points": serial, "step_kind": 2})
         ws = plan.new_workspace()
         S = to_dev_f32(slots)
         Hd = to_dev_f32(h0)
