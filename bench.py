@@ -168,7 +168,9 @@ def dense_run(args, w, tune):
     stream = torch.cuda.current_stream()
     layout = args.layout
     if layout == "auto":
-        layout = "packed" if info["packed_kind"] else "rowmajor"
+        # (the packed partials exist on the vector-ALU stream only)
+        packed_ok = info["packed_kind"] == 1 if args.op == "partials" else info["packed_kind"] != 0
+        layout = "packed" if packed_ok else "rowmajor"
     extra = {}
     if layout == "packed":
         # load-time layout change, outside the timed region
@@ -200,7 +202,25 @@ def dense_run(args, w, tune):
         else:
             kernel = "decode step on row-major weights (one persistent launch: %s)" % (
                 "decode_step_mfma" if w.batch >= 16 else "decode_step")
+    if args.op == "partials" and layout == "packed":
+        if info["packed_kind"] != 1:
+            raise SystemExit("packed partials need packed_kind 1 (the vector-ALU stream)")
+        pstack = torch.empty((w.layers, 2, w.batch, w.hidden), dtype=torch.float32, device="cuda")
+
+        def step():
+            tp.tp_rowparallel_partials_packed(plan, w.layers, xa, po, xf, pd, pstack, ws)
+        ms = time_steps(step, args.steps, args.warmup, stream)
+        nbytes = w.layers * ((w.ka_r + w.ki_r) * w.hidden * 2 + w.batch * (w.ka_r + w.ki_r) * 2
+                             + 2 * w.batch * w.hidden * 4)
+        config = {"workload": w.name, "op": "partials", "hidden": w.hidden, "inter": w.inter,
+                  "k_attn": w.k_attn, "layers": w.layers, "n_ranks": w.n_ranks, "rank": args.rank,
+                  "batch": w.batch, "launches_per_pass": 1, "us_per_launch": round(ms * 1e3, 3),
+                  "timing": "eager, one launch", "weight_layout": "packed"}
+        kernel = "tp_rowparallel_partials_packed: decode_stream, partials only, one launch per pass"
+        return ms, w.batch, nbytes, kernel, config, None, {"traffic": None}
     if args.op != "step":
+        if layout != "rowmajor":
+            raise SystemExit("--op %s runs on row-major weights (--layout rowmajor)" % args.op)
         return single_op_run(args, w, plan, info, tune, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
     ms = time_steps(step, args.steps, args.warmup, stream)

@@ -362,6 +362,24 @@ tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank
                                   float* slots, float* hidden, void* workspace, void* stream);
 
 /*
+ * The partial projections of a layer stack on weights packed by
+ * tp_pack_weights, in layer order, in one call (lesson 9.9, Conceito; as
+ * tp_rowparallel_partials, no reduction, no residual): the vector-ALU
+ * stream of tp_decode_layers_packed with packed_kind 1, writing each
+ * point's partial instead of the ring sum.
+ *   x_attn, w_o_packed, x_ffn, w_down_packed as tp_decode_layers_packed
+ *   p fp32 [L][2][batch][hidden] (output)
+ * p[l][point] equals the slot tp_decode_layers_packed writes for this rank
+ * with the same plan, bit for bit. n_layers = 0 does nothing (the pointers
+ * may then be null). TP_ERR_UNSUPPORTED unless packed_kind is 1; other
+ * errors as tp_decode_layers_packed.
+ */
+tp_status tp_rowparallel_partials_packed(tp_plan_t plan, int32_t n_layers, const void* x_attn,
+                                         const void* w_o_packed, const void* x_ffn,
+                                         const void* w_down_packed, float* p, void* workspace,
+                                         void* stream);
+
+/*
  * Top-k routing of decode tokens ("Hosting Qwen on Blackwell", Prefillers:
  * each token goes to top_k of the experts). Per token: softmax over the
  * experts' logits (computed in double), the top_k experts by probability

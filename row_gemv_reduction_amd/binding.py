@@ -74,6 +74,8 @@ EXPORTS = {
     "tp_pack_activations": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 5),
     "tp_decode_layers_packed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
                                 + [ctypes.c_void_p] * 8),
+    "tp_rowparallel_partials_packed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
+                                       + [ctypes.c_void_p] * 7),
     "tp_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]),
@@ -353,6 +355,25 @@ def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ff
         raise ValueError("workspace too small")
     _check(_lib().tp_decode_layers_packed(plan.handle, L, rank, *args, _stream()),
            "tp_decode_layers_packed")
+
+
+def tp_rowparallel_partials_packed(plan: Plan, n_layers, x_attn, w_o_packed, x_ffn, w_down_packed,
+                                   p, workspace):
+    """The 2L partials of a stack on packed weights in one call (packed_kind 1):
+    p [L][2][batch][hidden]."""
+    i = plan._plan_info()
+    b, H = i["batch"], i["hidden"]
+    L = n_layers
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
+            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
+            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
+            _dev(p, "p", torch.float32, (L, 2, b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_rowparallel_partials_packed(plan.handle, L, *args, _stream()),
+           "tp_rowparallel_partials_packed")
 
 
 def tp_moe_route(plan: Plan, logits, sel_expert, sel_weight, renorm=True):

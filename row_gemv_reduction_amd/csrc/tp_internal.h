@@ -129,9 +129,11 @@ struct StreamGeom {
 bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
 tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);
+// (partials != nullptr: the partials only, into partials [L][2][b][H]; slots
+// and hidden unused)
 tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
                            const void* w_o_packed, const void* x_ffn, const void* w_down_packed,
-                           float* slots, float* hidden, void* ws, void* stream);
+                           float* slots, float* hidden, float* partials, void* ws, void* stream);
 
 // Geometry of the MFMA streamed decode step (tp_mfma_stream.hip).
 struct MfmaGeom {

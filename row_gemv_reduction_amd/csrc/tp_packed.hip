@@ -133,7 +133,10 @@ struct Cursor {
     int j, m0;
 };
 
-template <int B, int SL, bool SERIAL>
+// PART: the partials only (tp_rowparallel_partials_packed): the control wave
+// writes each point's partial to slots[j] ([L][2][b][H]) and forms no ring
+// sum; the hidden state is neither read nor written.
+template <int B, int SL, bool SERIAL, bool PART = false>
 __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs a) {
     extern __shared__ __align__(16) uint32_t xs[];             // two x buffers, bf16 pairs
     __shared__ float red[2][kStreamMaxWaves - 1][B * 4];        // per point parity
@@ -166,9 +169,10 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
             const int s = g + si * G;
             valid[q] = e < n_el && s < a.S;
             idx[q] = valid[q] ? b * a.H + 4 * s + c : 0;
-            h[q] = valid[q] ? a.hidden[idx[q]] : 0.f;
+            h[q] = valid[q] && !PART ? a.hidden[idx[q]] : 0.f;
         }
         auto fetch_others = [&](int j) {
+            if (PART) return;
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
 #pragma unroll
             for (int q = 0; q < EQ_MAX; ++q) {
@@ -234,7 +238,8 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
 
         for (int j = 0; j < n_points; ++j) {
             __syncthreads();  // P_j: the compute waves' sums of point j are in red[j & 1]
-            float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
+            float* slot = PART ? a.slots + (int64_t)j * len
+                               : a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
 #pragma unroll
             for (int q = 0; q < EQ_MAX; ++q) {
 #pragma clang fp contract(off)
@@ -244,6 +249,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 float v = red[j & 1][si * a.WPS][b * 4 + c];
                 for (int wi = 1; wi < a.WPS; ++wi) v += red[j & 1][si * a.WPS + wi][b * 4 + c];
                 slot[idx[q]] = v;
+                if (PART) continue;
                 // ring order: chunk c starts at rank c, then c+1, ... (mod N)
                 const int cidx = idx[q] / a.chunk;
                 float sum = 0.f;
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
         }
 #pragma unroll
         for (int q = 0; q < EQ_MAX; ++q)
-            if (valid[q]) a.hidden[idx[q]] = h[q];
+            if (valid[q] && !PART) a.hidden[idx[q]] = h[q];
         if (SERIAL) {
             // the last workgroup to leave clears the flags for the next launch
             wait_mem();
@@ -389,37 +395,41 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
 
 typedef void (*stream_fn)(StreamArgs);
 
-template <int SL, bool SERIAL>
+template <int SL, bool SERIAL, bool PART>
 stream_fn stream_kernel_for(int b) {
-    static_assert(SL == 4, "8-load banks: stream_kernel_sl8");
     switch (b) {
-        case 1: return decode_stream<1, SL, SERIAL>;
-        case 2: return decode_stream<2, SL, SERIAL>;
-        case 3: return decode_stream<3, SL, SERIAL>;
-        case 4: return decode_stream<4, SL, SERIAL>;
-        case 5: return decode_stream<5, SL, SERIAL>;
-        case 6: return decode_stream<6, SL, SERIAL>;
-        case 7: return decode_stream<7, SL, SERIAL>;
-        case 8: return decode_stream<8, SL, SERIAL>;
+        case 1: return decode_stream<1, SL, SERIAL, PART>;
+        case 2: return decode_stream<2, SL, SERIAL, PART>;
+        case 3: return decode_stream<3, SL, SERIAL, PART>;
+        case 4: return decode_stream<4, SL, SERIAL, PART>;
+        case 5: return decode_stream<5, SL, SERIAL, PART>;
+        case 6: return decode_stream<6, SL, SERIAL, PART>;
+        case 7: return decode_stream<7, SL, SERIAL, PART>;
+        case 8: return decode_stream<8, SL, SERIAL, PART>;
     }
     return nullptr;
 }
 
 // 8-load banks only for batch <= 4 (beyond, the registers would spill).
-template <bool SERIAL>
+template <bool SERIAL, bool PART>
 stream_fn stream_kernel_sl8(int b) {
     switch (b) {
-        case 1: return decode_stream<1, 8, SERIAL>;
-        case 2: return decode_stream<2, 8, SERIAL>;
-        case 3: return decode_stream<3, 8, SERIAL>;
-        case 4: return decode_stream<4, 8, SERIAL>;
+        case 1: return decode_stream<1, 8, SERIAL, PART>;
+        case 2: return decode_stream<2, 8, SERIAL, PART>;
+        case 3: return decode_stream<3, 8, SERIAL, PART>;
+        case 4: return decode_stream<4, 8, SERIAL, PART>;
     }
     return nullptr;
 }
 
-stream_fn stream_kernel(int b, int sl, bool serial) {
-    if (sl == 4) return serial ? stream_kernel_for<4, true>(b) : stream_kernel_for<4, false>(b);
-    if (sl == 8) return serial ? stream_kernel_sl8<true>(b) : stream_kernel_sl8<false>(b);
+// mode 0: dataflow point order, 1: serial point order, 2: partials only
+stream_fn stream_kernel(int b, int sl, int mode) {
+    if (sl == 4)
+        return mode == 1 ? stream_kernel_for<4, true, false>(b)
+                         : mode == 2 ? stream_kernel_for<4, false, true>(b) : stream_kernel_for<4, false, false>(b);
+    if (sl == 8)
+        return mode == 1 ? stream_kernel_sl8<true, false>(b)
+                         : mode == 2 ? stream_kernel_sl8<false, true>(b) : stream_kernel_sl8<false, false>(b);
     return nullptr;
 }
 
@@ -484,7 +494,7 @@ tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void*
 
 tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
                            const void* w_o_packed, const void* x_ffn, const void* w_down_packed,
-                           float* slots, float* hidden, void* ws, void* stream) {
+                           float* slots, float* hidden, float* partials, void* ws, void* stream) {
     StreamGeom geo;
     if (!tp_stream_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * 2 >= ((int64_t)1 << 30)) return TP_ERR_UNSUPPORTED;
@@ -494,15 +504,15 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
         return TP_ERR_UNSUPPORTED;
     if (geo.grid > 1024) return TP_ERR_UNSUPPORTED;  // completion words of the serial order
     if (n_layers == 0) return TP_OK;
-    const bool serial = p->serial_points != 0;
-    stream_fn k = stream_kernel(p->batch, geo.sl, serial);
+    const bool serial = p->serial_points != 0 && !partials;
+    stream_fn k = stream_kernel(p->batch, geo.sl, partials ? 2 : serial ? 1 : 0);
     if (!k) return TP_ERR_UNSUPPORTED;
     StreamArgs a;
     a.x0 = static_cast<const uint16_t*>(x_attn);
     a.x1 = static_cast<const uint16_t*>(x_ffn);
     a.w0 = static_cast<const uint16_t*>(w_o_packed);
     a.w1 = static_cast<const uint16_t*>(w_down_packed);
-    a.slots = slots;
+    a.slots = partials ? partials : slots;
     a.hidden = hidden;
     a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kStreamFlagOffset);
     a.err = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSyncOffset) + kSyncErr;

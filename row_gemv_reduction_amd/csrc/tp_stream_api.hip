@@ -83,7 +83,22 @@ tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, c
                                      slots, hidden, ws, stream);
     }
     return tp_decode_stream(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed, slots,
-                            hidden, ws, stream);
+                            hidden, nullptr, ws, stream);
+}
+
+tp_status tp_rowparallel_partials_packed(tp_plan_t p, int32_t n_layers, const void* x_attn,
+                                         const void* w_o_packed, const void* x_ffn,
+                                         const void* w_down_packed, float* out, void* ws,
+                                         void* stream) {
+    if (!p || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (n_layers == 0) return TP_OK;  // nothing is read or written
+    if (!x_attn || !w_o_packed || !x_ffn || !w_down_packed || !out || !ws) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x_attn) || !aligned16(w_o_packed) || !aligned16(x_ffn) ||
+        !aligned16(w_down_packed) || !aligned16(out) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    if (tp_packed_kind(p) != 1) return TP_ERR_UNSUPPORTED;
+    return tp_decode_stream(p, n_layers, 0, x_attn, w_o_packed, x_ffn, w_down_packed, nullptr,
+                            nullptr, out, ws, stream);
 }
 
 }  // extern "C"

@@ -727,6 +727,37 @@ def test_packed_decode_matches_oracle(n, b, h, ka, ki, rank, kind):
     check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
 
 
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,kind", PACKED_CASES)
+def test_partials_packed(n, b, h, ka, ki, rank, kind):
+    """tp_rowparallel_partials_packed (packed_kind 1): every partial against
+    the oracle and bit for bit equal to the rank's slot that
+    tp_decode_layers_packed writes with the same plan; other kinds are
+    refused."""
+    L = 3
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 31, rank)
+    say("packed partials n=%d b=%d h=%d ka=%d ki=%d kind=%d" % (n, b, h, ka, ki, kind))
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind})
+    ws = plan.new_workspace()
+    po, pd = pack_dev(plan, 0, wo), pack_dev(plan, 1, wd)
+    pa, pf = pack_acts_dev(plan, xa, xf)
+    P = torch.full((L, 2, b, h), float("nan"), dtype=torch.float32, device="cuda")
+    if kind != 1:
+        with pytest.raises(tp.TPError):
+            tp.tp_rowparallel_partials_packed(plan, L, pa, po, pf, pd, P, ws)
+        return
+    tp.tp_rowparallel_partials_packed(plan, L, pa, po, pf, pd, P, ws)
+    S = to_dev_f32(slots)
+    Hd = to_dev_f32(h0)
+    tp.tp_decode_layers_packed(plan, L, rank, pa, po, pf, pd, S, Hd, ws)
+    torch.cuda.synchronize()
+    assert tp.tp_workspace_status(plan, ws) == 0
+    got = host(P)
+    assert_bits_equal(got, host(S)[:, :, rank], "partials vs decode slots")
+    for l in range(L):
+        assert_partial_close(got[l, 0], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
+        assert_partial_close(got[l, 1], oracle.partial(xf[l], wd[l])[0], "ffn l=%d" % l)
+
+
 SEGMENT_CASES = [
     # (n, b, hidden, k_attn, inter, rank, workgroups): the matrix-core stream
     # with fewer workgroups than strips, so that ranges of tiles cut strips
