@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe_partial.argtypes = [i32, i32, vp, vp, i32, i32, vp, vp, i64, i64,
                                          vp, vp, ctypes.c_int]
         L.oracle_moe_partial.restype = ctypes.c_int
+        L.oracle_gate_up_swiglu.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int]
+        L.oracle_gate_up_swiglu.restype = ctypes.c_int
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -180,6 +182,28 @@ def moe_partial(sel_expert, sel_weight, e_begin, u_bits, w_local_bits, nthreads:
     if rc != 0:
         raise ValueError("moe_partial: bad sizes")
     return p64, p32
+
+
+def gate_up_swiglu(x_bits, w_gate_bits, w_up_bits, nthreads: int = 1):
+    """a = silu(x . W_gate) * (x . W_up); returns (double array, bf16 bits).
+
+    x_bits: uint16 [batch, hidden]; w_gate_bits, w_up_bits: uint16
+    [hidden, cols] (bf16).
+    """
+    x = _c(x_bits, np.uint16)
+    wg = _c(w_gate_bits, np.uint16)
+    wu = _c(w_up_bits, np.uint16)
+    b, h = x.shape
+    if wg.shape != wu.shape or wg.shape[0] != h:
+        raise ValueError("x, w_gate and w_up disagree")
+    c = wg.shape[1]
+    a64 = np.empty((b, c), np.float64)
+    abf = np.empty((b, c), np.uint16)
+    rc = lib().oracle_gate_up_swiglu(_ptr(x), _ptr(wg), _ptr(wu), b, h, c, _ptr(a64), _ptr(abf),
+                                     nthreads)
+    if rc != 0:
+        raise ValueError("gate_up_swiglu: bad sizes")
+    return a64, abf
 
 
 def bf16_to_f32(bits) -> float:

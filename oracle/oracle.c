@@ -432,3 +432,53 @@ int oracle_moe_partial(int32_t tokens, int32_t top_k, const int32_t* sel_expert,
     for_columns(moe_cols, &c, hidden, nthreads);
     return 0;
 }
+
+/* -------------------------------------- column-parallel up projection -- */
+
+/*
+ * Column-parallel FFN up projection with its activation [P1, Conceito:
+ * under tensor parallelism the FFN's up projection is split over the ranks
+ * the other way from its down projection, so rank r holds its columns of
+ * the up projection and computes, with no reduction, its own slice of the
+ * down projection's input]. The pages name no activation; the reading taken
+ * is SwiGLU, with a gate and an up matrix split by the same columns:
+ *
+ *     g = x . W_gate,  u = x . W_up           (double, ascending k)
+ *     a = silu(g) * u,  silu(z) = z / (1 + e^(-z))          (double)
+ *     a_bf16 = bf16(float(a))       (nearest-even both times, as stored)
+ *
+ *   x              bf16 [batch][hidden]
+ *   w_gate, w_up   bf16 [hidden][cols] row-major (the rank's columns)
+ *   a64            double [batch][cols] (optional)
+ *   a_bf16         bf16 bits [batch][cols] (optional)
+ *
+ * Pins: zero gate weights give a = 0 (silu(0) = 0); a 1x1 case gives
+ * silu(1) = sigma(1) = 0.7310585786300049...; negating the gate weights
+ * changes a by exactly g*u (silu(z) - silu(-z) = z), with g and u from
+ * oracle_partial; a large gate gives a -> g*u.
+ */
+int oracle_gate_up_swiglu(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                          int64_t batch, int64_t hidden, int64_t cols, double* a64,
+                          uint16_t* a_bf16, int nthreads)
+{
+    if (batch < 0 || hidden < 0 || cols < 0) return -1;
+    size_t n = (size_t)(batch * cols);
+    double* g = (double*)malloc((n ? n : 1) * sizeof(double));
+    double* u = (double*)malloc((n ? n : 1) * sizeof(double));
+    if (!g || !u) {
+        free(g);
+        free(u);
+        return -1;
+    }
+    oracle_partial(x, hidden, w_gate, batch, hidden, cols, g, NULL, nthreads);
+    oracle_partial(x, hidden, w_up, batch, hidden, cols, u, NULL, nthreads);
+    for (size_t i = 0; i < n; ++i) {
+        double silu = g[i] / (1.0 + exp(-g[i]));
+        double a = silu * u[i];
+        if (a64) a64[i] = a;
+        if (a_bf16) a_bf16[i] = float_to_bf16_bits((float)a);
+    }
+    free(g);
+    free(u);
+    return 0;
+}

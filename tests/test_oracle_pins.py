@@ -388,3 +388,67 @@ def test_moe_partial_exact_bruteforce_tiny():
                           for kk in range(mi))
                 ex += Fraction(float(sw[ti, s])) * dot
             assert abs(Fraction(float(p64[ti, n])) - ex) <= Fraction(1, 2 ** 40) * (1 + abs(ex))
+
+
+# ------------------------------------------ column-parallel up projection --
+
+def _bf16(v):
+    return synth.f32_to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_swiglu_zero_gate_gives_zero():
+    # silu(0) = 0: with every gate weight zero the activation is 0 whatever u is
+    g = np.random.default_rng(70)
+    x = _bf16(g.standard_normal((3, 40)))
+    wg = np.zeros((40, 24), np.uint16)
+    wu = _bf16(g.standard_normal((40, 24)))
+    a64, abf = oracle.gate_up_swiglu(x, wg, wu)
+    assert np.all(a64 == 0.0)
+    assert np.all((abf & 0x7FFF) == 0)
+
+
+def test_swiglu_sigma_of_one():
+    # 1x1: g = u = 1 -> a = silu(1) = 1 / (1 + e^-1) = 0.7310585786300049 (the
+    # logistic function at 1); with u = 2 twice that
+    one = _bf16([[1.0]])
+    a64, abf = oracle.gate_up_swiglu(one, one, one)
+    assert abs(a64[0, 0] - 0.7310585786300049) < 1e-15
+    a64, _ = oracle.gate_up_swiglu(one, one, _bf16([[2.0]]))
+    assert abs(a64[0, 0] - 2 * 0.7310585786300049) < 2e-15
+    # the stored value is that number rounded to bf16: 0.73046875 (0x3F3B)
+    assert abf[0, 0] == 0x3F3B
+
+
+@pytest.mark.parametrize("b,h,c,seed", [(1, 33, 17, 71), (4, 128, 40, 72)])
+def test_swiglu_odd_part_is_g_times_u(b, h, c, seed):
+    # silu(z) - silu(-z) = z, so negating the gate weights changes a by g*u,
+    # with g and u the (separately pinned) projections of oracle.partial; a
+    # swapped gate and up, or a dropped factor, fails this
+    g = np.random.default_rng(seed)
+    x = _bf16(g.standard_normal((b, h)))
+    wg = _bf16(g.standard_normal((h, c)) * 0.05)
+    wu = _bf16(g.standard_normal((h, c)) * 0.05)
+    a_pos, _ = oracle.gate_up_swiglu(x, wg, wu)
+    a_neg, _ = oracle.gate_up_swiglu(x, wg ^ np.uint16(0x8000), wu)
+    gate, _ = oracle.partial(x, wg)
+    up, _ = oracle.partial(x, wu)
+    assert np.allclose(a_pos - a_neg, gate * up, rtol=0, atol=1e-12 * max(1.0, np.abs(gate * up).max()))
+    # and the gate enters through silu, the up linearly: doubling the up
+    # weights doubles a exactly (a power-of-two scale of bf16 is exact)
+    wu2 = _bf16(synth.bf16_bits_to_f32(wu) * 2.0)
+    a2, _ = oracle.gate_up_swiglu(x, wg, wu2)
+    assert np.array_equal(a2, 2.0 * a_pos)
+
+
+def test_swiglu_large_gate_tends_to_g_times_u():
+    # silu(z) = z (1 - e^-z + ...) for z >> 0: at g >= 40 the factor is 1
+    # to within e^-40 ~ 4e-18, below double precision
+    g = np.random.default_rng(73)
+    x = _bf16(np.abs(g.standard_normal((2, 16))) + 1.0)
+    wg = _bf16(np.full((16, 8), 4.0))
+    wu = _bf16(g.standard_normal((16, 8)))
+    a64, _ = oracle.gate_up_swiglu(x, wg, wu)
+    gate, _ = oracle.partial(x, wg)
+    up, _ = oracle.partial(x, wu)
+    assert gate.min() >= 40.0
+    assert np.allclose(a64, gate * up, rtol=1e-15, atol=0)
