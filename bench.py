@@ -219,7 +219,7 @@ def dense_run(args, w, tune):
         kernel = "tp_rowparallel_partials_packed: decode_stream, partials only, one launch per pass"
         return ms, w.batch, nbytes, kernel, config, None, {"traffic": None}
     if args.op != "step":
-        if layout != "rowmajor":
+        if layout != "rowmajor" and args.op != "swiglu":
             raise SystemExit("--op %s runs on row-major weights (--layout rowmajor)" % args.op)
         return single_op_run(args, w, plan, info, tune, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
@@ -251,14 +251,35 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
     "partials" = tp_rowparallel_partials (the 2L partial projections in
     layer order, one call); "partial" = tp_rowparallel_partial and "ring" =
     tp_ring_reduce (ring-order sum of the N partials + residual), once per
-    reconciliation point (2L calls per pass, each its own launch)."""
+    reconciliation point (2L calls per pass, each its own launch);
+    "swiglu" = tp_gate_up_swiglu (the stack's column-parallel up
+    projections with SwiGLU, one call)."""
     import torch
 
     import row_gemv_reduction_amd as tp
     xa, wo, xf, wd, slots, hidden = inputs
     b, H, N, L = w.batch, w.hidden, w.n_ranks, w.layers
     graph_ok = True
-    if args.op == "partials":
+    if args.op == "swiglu":
+        # the column-parallel up projection of the same stack: gate and up
+        # weights [L][H][I/N] each, the layer's full hidden state as x
+        from row_gemv_reduction_amd import synth
+        C = w.ki_r
+        kw = dict(seed=0, workload=w.name, rank=args.rank)
+        xin = synth.device_normal((L, b, H), 1.0, torch.bfloat16, tensor="x_ffn_in", **kw)
+        wg = synth.device_normal((L, H, C), synth.WEIGHT_STD, torch.bfloat16, tensor="w_gate", **kw)
+        wu = synth.device_normal((L, H, C), synth.WEIGHT_STD, torch.bfloat16, tensor="w_up", **kw)
+        act = torch.empty((L, b, C), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            tp.tp_gate_up_swiglu(plan, L, xin, wg, wu, act, ws)
+        graph_ok = False  # one cooperative launch per layer, issued from C
+        # gate and up weights, x and the bf16 activation written
+        nbytes = L * (2 * H * C * 2 + b * H * 2 + b * C * 2)
+        kernel = ("tp_gate_up_swiglu: the persistent step's tiles (gate and up as the two "
+                  "points of each layer) + swiglu_kernel, over as many layers per launch as "
+                  "32 MiB of fp32 sums hold")
+    elif args.op == "partials":
         def step():
             tp.tp_rowparallel_partials(plan, L, xa, wo, xf, wd, pstack, ws)
         pstack = torch.empty((L, 2, b, H), dtype=torch.float32, device="cuda")
@@ -310,7 +331,8 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
                        "us_per_launch_eager": round(ms_eager * 1e3 / launches, 3)})
     else:
         ms = ms_eager
-        config.update({"us_per_launch": round(ms * 1e3, 3), "timing": "eager, one launch"})
+        config.update({"us_per_launch": round(ms * 1e3 / launches, 3),
+                       "timing": "eager, launches issued from the library"})
     assert tp.tp_workspace_status(plan, ws) == 0
     return ms, b, nbytes, kernel, config, None, {"traffic": None}
 
@@ -484,11 +506,12 @@ def main():
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
-    ap.add_argument("--op", choices=["step", "partials", "partial", "ring"], default="step",
+    ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu"], default="step",
                     help="what a timed pass runs: the whole decode step (default); the stack's "
-                         "2L partial projections in one call (tp_rowparallel_partials); or one "
+                         "2L partial projections in one call (tp_rowparallel_partials); one "
                          "entry point per reconciliation point (tp_rowparallel_partial, "
-                         "tp_ring_reduce)")
+                         "tp_ring_reduce); or the stack's column-parallel up projections with "
+                         "SwiGLU (tp_gate_up_swiglu)")
     args = ap.parse_args()
 
     if args.gpus != 1:

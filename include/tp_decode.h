@@ -142,6 +142,8 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "step_kind" (tp_decode_layers, tp_rowparallel_partials, batch < 16: the
  *                persistent step's kind, 0 = automatic, 1 = vector ALU,
  *                2 = matrix cores; from 16 tokens always matrix cores),
+ * "swiglu_layers" (tp_gate_up_swiglu: most layers per launch, 0 =
+ *                automatic: as many as 32 MiB of fp32 gate and up sums hold),
  * "step_rows" (tp_decode_layers: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core
  *                tiles, 1024 for narrower vector-ALU ones).
@@ -211,6 +213,29 @@ tp_status tp_rowparallel_partial(tp_plan_t plan, int32_t point, const void* x, c
 tp_status tp_rowparallel_partials(tp_plan_t plan, int32_t n_layers, const void* x_attn,
                                   const void* w_o, const void* x_ffn, const void* w_down,
                                   float* p, void* workspace, void* stream);
+
+/*
+ * Column-parallel FFN up projection with its activation, for a layer stack
+ * (lesson 9.9, Conceito: the FFN's up projection is split over the ranks
+ * the other way from its down projection, so each rank computes its own
+ * columns, and with them its slice of the down projection's input, with no
+ * reduction). The pages name no activation; this is SwiGLU, with a gate and
+ * an up matrix split by the same columns:
+ *     a[l] = bf16( silu(x[l] . w_gate[l]) * (x[l] . w_up[l]) ),
+ *     silu(z) = z / (1 + e^-z)
+ *   x       bf16 [L][batch][hidden] (the full hidden state of each layer)
+ *   w_gate, w_up  bf16 [L][hidden][inter/N] row-major (the rank's columns)
+ *   out     bf16 [L][batch][inter/N] (output: the down projection's x slice)
+ * The two projections accumulate in fp32 (the persistent step's tiles, the
+ * gate and up matrices as the two points of each layer, as many layers per
+ * launch as "swiglu_layers" allows), then silu and the product in fp32,
+ * rounded to bf16 nearest-even (a second launch). n_layers = 0 does nothing (the pointers may then be null).
+ * TP_ERR_UNSUPPORTED if inter/N is not a multiple of 8; TP_ERR_ALIGNMENT
+ * for pointers not 16-byte aligned or batch*inter/N not a multiple of 8;
+ * TP_ERR_INVALID_ARG for a null pointer or n_layers < 0.
+ */
+tp_status tp_gate_up_swiglu(tp_plan_t plan, int32_t n_layers, const void* x, const void* w_gate,
+                            const void* w_up, void* out, void* workspace, void* stream);
 
 /*
  * Ring-ordered all-reduce sum of the N partials plus the residual

@@ -63,6 +63,7 @@ EXPORTS = {
                                               ctypes.c_void_p]),
     "tp_rowparallel_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
                                 + [ctypes.c_void_p] * 7),
+    "tp_gate_up_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 6),
     "tp_ring_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tp_decode_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
@@ -242,6 +243,22 @@ def tp_rowparallel_partials(plan: Plan, n_layers, x_attn, w_o, x_ffn, w_down, p,
         raise ValueError("workspace too small")
     _check(_lib().tp_rowparallel_partials(plan.handle, L, *args, _stream()),
            "tp_rowparallel_partials")
+
+
+def tp_gate_up_swiglu(plan: Plan, n_layers, x, w_gate, w_up, out, workspace):
+    """out[l] = bf16(silu(x[l] . w_gate[l]) * (x[l] . w_up[l])), the rank's columns."""
+    i = plan._plan_info()
+    b, H, n = i["batch"], i["hidden"], i["n_ranks"]
+    C = i["inter"] // n
+    L = n_layers
+    args = (_dev(x, "x", torch.bfloat16, (L, b, H)),
+            _dev(w_gate, "w_gate", torch.bfloat16, (L, H, C)),
+            _dev(w_up, "w_up", torch.bfloat16, (L, H, C)),
+            _dev(out, "out", torch.bfloat16, (L, b, C)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_gate_up_swiglu(plan.handle, L, *args, _stream()), "tp_gate_up_swiglu")
 
 
 def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):

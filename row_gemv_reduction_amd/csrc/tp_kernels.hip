@@ -854,6 +854,21 @@ __global__ __launch_bounds__(kStepMfmaWaves * 64) void decode_step_mfma(StepArgs
     step_exit<NT>(a, &sh.flag);
 }
 
+// -------------------------------------------- column-parallel SwiGLU --
+
+// a = silu(g) * u elementwise, rounded to bf16 nearest-even (the down
+// projection's x slice), for `layers` layers: sums fp32 [layers][2][len]
+// (the gate's, then the up's), out bf16 [layers][len].
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* sums, uint16_t* out, int64_t len,
+                                                     int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int64_t l = i / len, e = i - l * len;
+    const float gv = sums[(2 * l) * len + e];
+    const float silu = gv / (1.0f + expf(-gv));
+    out[i] = f32_to_bf16_rne(silu * sums[(2 * l + 1) * len + e]);
+}
+
 // ------------------------------------------------------------ MFMA GEMM --
 
 template <int BT>  // batch tiles of 16 rows
@@ -1240,6 +1255,37 @@ tp_status tp_rowparallel_partial(tp_plan_t p, int32_t point, const void* x, cons
     e.counters = ws_counters(ws);
     e.splits = g.splits;
     return launch_projection(p, g, p->batch, x, w, e, (hipStream_t)stream);
+}
+
+tp_status tp_gate_up_swiglu(tp_plan_t p, int32_t n_layers, const void* x, const void* w_gate,
+                            const void* w_up, void* out, void* ws, void* stream) {
+    if (!p || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (n_layers == 0) return TP_OK;  // nothing is read or written
+    if (!x || !w_gate || !w_up || !out || !ws) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(out) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    if (!tp_swiglu_ok(p)) return TP_ERR_UNSUPPORTED;
+    const int64_t b = p->batch, H = p->hidden, C = p->inter / p->n_ranks;
+    if ((b * C) % 8) return TP_ERR_ALIGNMENT;  // each layer's output slice stays 16-byte aligned
+    const tp_plan_s q = tp_swiglu_plan(p);
+    float* gu = reinterpret_cast<float*>(static_cast<char*>(ws) + tp_ws_swiglu_offset(p));
+    const int32_t per = tp_swiglu_layers_per_launch(p);
+    hipStream_t st = (hipStream_t)stream;
+    for (int32_t l0 = 0; l0 < n_layers; l0 += per) {
+        const int32_t nl = n_layers - l0 < per ? n_layers - l0 : per;
+        const uint16_t* xl = static_cast<const uint16_t*>(x) + (int64_t)l0 * b * H;
+        const uint16_t* wg = static_cast<const uint16_t*>(w_gate) + (int64_t)l0 * H * C;
+        const uint16_t* wu = static_cast<const uint16_t*>(w_up) + (int64_t)l0 * H * C;
+        // the gate and up sums of nl layers: the two points of each layer of
+        // one persistent partials launch (x is the same for both)
+        tp_status s = decode_persistent(&q, nl, 0, xl, wg, xl, wu, nullptr, nullptr, gu, ws, st);
+        if (s != TP_OK) return s;
+        const int64_t total = (int64_t)nl * b * C;
+        hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, gu,
+                           static_cast<uint16_t*>(out) + (int64_t)l0 * b * C, b * C, total);
+        if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
+    }
+    return TP_OK;
 }
 
 tp_status tp_rowparallel_partials(tp_plan_t p, int32_t n_layers, const void* x_attn, const void* w_o,

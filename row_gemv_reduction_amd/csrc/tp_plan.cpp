@@ -160,6 +160,42 @@ static int64_t partial_bytes(const tp_plan_s* p) {
     return m;
 }
 
+// The column-parallel up projection (tp_gate_up_swiglu) as a persistent
+// partials step: both "points" read x [b][H]; point 0 is the gate, point 1
+// the up matrix, each [H][I/N]; the output width is I/N; one rank.
+tp_plan_s tp_swiglu_plan(const tp_plan_s* p) {
+    tp_plan_s q = *p;
+    q.hidden = p->inter / p->n_ranks;
+    q.k_attn = p->hidden;
+    q.inter = p->hidden;
+    q.n_ranks = 1;
+    q.splits_user[0] = q.splits_user[1] = 0;
+    q.decode_mode = 2;
+    q.serial_points = 0;
+    q.n_experts = q.top_k = q.ep = 0;
+    q.moe_inter = 0;
+    return q;
+}
+
+bool tp_swiglu_ok(const tp_plan_s* p) {
+    return p->inter % p->n_ranks == 0 && (p->inter / p->n_ranks) % 8 == 0 &&
+           p->batch >= 1 && p->batch <= kMfmaMaxBatch;
+}
+
+int64_t tp_ws_swiglu_offset(const tp_plan_s* p) {
+    tp_plan_s q = tp_swiglu_plan(p);
+    return kCounterBytes + partial_bytes(&q);
+}
+
+// Layers per launch of tp_gate_up_swiglu: as many as keep the fp32 gate and
+// up sums ([layers][2][b][I/N]) within kSwigluSumsBytes (at least one).
+int32_t tp_swiglu_layers_per_launch(const tp_plan_s* p) {
+    const int64_t per_layer = 2 * (int64_t)p->batch * (p->inter / p->n_ranks) * 4;
+    int64_t n = per_layer > 0 ? kSwigluSumsBytes / per_layer : 1;
+    if (p->swiglu_layers > 0 && n > p->swiglu_layers) n = p->swiglu_layers;
+    return (int32_t)(n < 1 ? 1 : n > 4096 ? 4096 : n);
+}
+
 int64_t tp_ws_xchg_offset(const tp_plan_s* p) {
     return tp_ws_partials_offset() + partial_bytes(p);
 }
@@ -169,7 +205,16 @@ int64_t tp_ws_moe_offset(const tp_plan_s* p) {
 }
 
 int64_t tp_workspace_bytes(const tp_plan_s* p) {
-    return tp_ws_moe_offset(p) + round_up(tp_moe_workspace_bytes(p), 256);
+    int64_t m = tp_ws_moe_offset(p) + round_up(tp_moe_workspace_bytes(p), 256);
+    if (tp_swiglu_ok(p)) {
+        // the gate and up sums, fp32 [2][b][I/N], after the derived step's buffers
+        const int64_t s = tp_ws_swiglu_offset(p) +
+                          round_up((int64_t)tp_swiglu_layers_per_launch(p) * 2 * p->batch *
+                                       (p->inter / p->n_ranks) * 4,
+                                   256);
+        if (s > m) m = s;
+    }
+    return m;
 }
 
 int tp_decode_mode(const tp_plan_s* p) {
@@ -248,6 +293,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
+    } else if (!strcmp(key, "swiglu_layers")) {
+        if (value < 0 || value > 4096) return TP_ERR_INVALID_ARG;
+        p->swiglu_layers = (int32_t)value;
     } else if (!strcmp(key, "step_kind")) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->step_kind = (int32_t)value;
