@@ -273,7 +273,7 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
 
         def step():
             tp.tp_gate_up_swiglu(plan, L, xin, wg, wu, act, ws)
-        graph_ok = False  # one cooperative launch per layer, issued from C
+        graph_ok = False  # cooperative launches, issued from C
         # gate and up weights, x and the bf16 activation written
         nbytes = L * (2 * H * C * 2 + b * H * 2 + b * C * 2)
         kernel = ("tp_gate_up_swiglu: the persistent step's tiles (gate and up as the two "

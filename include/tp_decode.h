@@ -144,9 +144,11 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  *                2 = matrix cores; from 16 tokens always matrix cores),
  * "swiglu_layers" (tp_gate_up_swiglu: most layers per launch, 0 =
  *                automatic: as many as 32 MiB of fp32 gate and up sums hold),
- * "step_rows" (tp_decode_layers: most rows per tile of the persistent
+ * "step_rows" (tp_decode_layers, tp_rowparallel_partials,
+ *                tp_gate_up_swiglu: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core
- *                tiles, 1024 for narrower vector-ALU ones).
+ *                tiles, 1024 for narrower vector-ALU ones; the whole K for
+ *                matrix-core tiles of tp_gate_up_swiglu).
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
@@ -228,7 +230,9 @@ tp_status tp_rowparallel_partials(tp_plan_t plan, int32_t n_layers, const void* 
  *   out     bf16 [L][batch][inter/N] (output: the down projection's x slice)
  * The two projections accumulate in fp32 (the persistent step's tiles, the
  * gate and up matrices as the two points of each layer, as many layers per
- * launch as "swiglu_layers" allows), then silu and the product in fp32,
+ * launch as "swiglu_layers" allows, spread evenly over the launches; with
+ * matrix-core tiles and "step_rows" unset, one tile spans the whole K of
+ * a column tile, so no split partials are written), then silu and the product in fp32,
  * rounded to bf16 nearest-even (a second launch). n_layers = 0 does nothing (the pointers may then be null).
  * TP_ERR_UNSUPPORTED if inter/N is not a multiple of 8; TP_ERR_ALIGNMENT
  * for pointers not 16-byte aligned or batch*inter/N not a multiple of 8;

@@ -727,7 +727,8 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
 
 // The matrix-core decode step (b = 16..64, BT tiles of 16 tokens), on the
 // same tiles, point order, split sets and epilogue as decode_step. A tile
-// is 128 columns by up to 2048 rows. Each of the kStepMfmaWaves waves takes
+// is 128 columns by the plan's tile length in rows (2048 by default, a
+// whole K in the up projection). Each of the kStepMfmaWaves waves takes
 // 32-row steps (wave w: steps w, w + NW, ...): per lane 8 rows x 16 bytes
 // of weights, transposed with v_perm into k-major B operands, and one
 // 16-byte A operand (8 rows of x) per 16 tokens, both loaded one step
@@ -1270,9 +1271,13 @@ tp_status tp_gate_up_swiglu(tp_plan_t p, int32_t n_layers, const void* x, const 
     const tp_plan_s q = tp_swiglu_plan(p);
     float* gu = reinterpret_cast<float*>(static_cast<char*>(ws) + tp_ws_swiglu_offset(p));
     const int32_t per = tp_swiglu_layers_per_launch(p);
+    // as few launches as the sums region allows, with the layers spread
+    // evenly over them (no short last launch that leaves the chip idle)
+    const int32_t launches = (n_layers + per - 1) / per;
     hipStream_t st = (hipStream_t)stream;
-    for (int32_t l0 = 0; l0 < n_layers; l0 += per) {
-        const int32_t nl = n_layers - l0 < per ? n_layers - l0 : per;
+    for (int32_t k = 0; k < launches; ++k) {
+        const int32_t l0 = (int32_t)((int64_t)k * n_layers / launches);
+        const int32_t nl = (int32_t)((int64_t)(k + 1) * n_layers / launches) - l0;
         const uint16_t* xl = static_cast<const uint16_t*>(x) + (int64_t)l0 * b * H;
         const uint16_t* wg = static_cast<const uint16_t*>(w_gate) + (int64_t)l0 * H * C;
         const uint16_t* wu = static_cast<const uint16_t*>(w_up) + (int64_t)l0 * H * C;

@@ -174,6 +174,13 @@ tp_plan_s tp_swiglu_plan(const tp_plan_s* p) {
     q.serial_points = 0;
     q.n_experts = q.top_k = q.ep = 0;
     q.moe_inter = 0;
+    // The up projection's points are independent (no residual chain), so
+    // the matrix-core step takes a column tile's whole K as one tile: no
+    // split partials, and no tile waits for a free split set. Kept within
+    // the step's 32-bit buffer offsets.
+    const int64_t k_all = round_up(q.k_attn, kMfmaKStep);
+    if (p->step_rows <= 0 && tp_step_mfma(&q) && (k_all + 1024) * q.hidden * 2 < (int64_t(1) << 31))
+        q.step_rows = (int32_t)k_all;
     return q;
 }
 

@@ -39,22 +39,24 @@ CASES = [
     # steps, ragged column tiles, one split and several, tokens past 16
     (2, 1, 520, 1040, 2), (4, 3, 1024, 4352, 2), (1, 8, 264, 1000, 2),
     (4, 16, 1032, 2080, 2), (8, 64, 512, 2048, 1), (2, 5, 2048, 4096, 1),
-    (4, 40, 1024, 4352, 1),
+    (4, 40, 1024, 4352, 1), (2, 24, 4104, 1024, 1),
 ]
 
 
-@pytest.mark.parametrize("n,b,h,inter,L,per", [c + (0,) for c in CASES] +
-                         [(2, 3, 520, 1040, 5, 2), (4, 17, 1024, 2080, 3, 1)])
-def test_gate_up_swiglu_matches_oracle(n, b, h, inter, L, per):
+@pytest.mark.parametrize("n,b,h,inter,L,per,rows", [c + (0, 0) for c in CASES] +
+                         [(2, 3, 520, 1040, 5, 2, 0), (4, 17, 1024, 2080, 3, 1, 0),
+                          (2, 24, 4104, 1024, 2, 0, 512), (1, 16, 2048, 640, 1, 0, 512)])
+def test_gate_up_swiglu_matches_oracle(n, b, h, inter, L, per, rows):
     """per > 0 caps the layers per launch (swiglu_layers), so that a stack
-    takes several launches, the last one shorter."""
+    takes several launches; rows > 0 caps the tile length (step_rows), so
+    that the matrix-core tiles split K instead of spanning it."""
     C = inter // n
-    say("gate/up swiglu n=%d b=%d h=%d inter=%d L=%d per=%d" % (n, b, h, inter, L, per))
+    say("gate/up swiglu n=%d b=%d h=%d inter=%d L=%d per=%d rows=%d" % (n, b, h, inter, L, per, rows))
     kw = dict(seed=61, workload="swiglu")
     x = synth.normal_bf16((L, b, h), 1.0, tensor="x_ffn_in", **kw)
     wg = synth.normal_bf16((L, h, C), synth.WEIGHT_STD, tensor="w_gate", **kw)
     wu = synth.normal_bf16((L, h, C), synth.WEIGHT_STD, tensor="w_up", **kw)
-    plan = tp.Plan(h, inter, n, b, tune={"swiglu_layers": per})
+    plan = tp.Plan(h, inter, n, b, tune={"swiglu_layers": per, "step_rows": rows})
     ws = plan.new_workspace()
     X, WG, WU = to_dev_bf16(x), to_dev_bf16(wg), to_dev_bf16(wu)
     out = torch.empty((L, b, C), dtype=torch.bfloat16, device="cuda")
