@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_moe_partial.restype = ctypes.c_int
         L.oracle_gate_up_swiglu.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_int]
         L.oracle_gate_up_swiglu.restype = ctypes.c_int
+        L.oracle_qkv_proj.argtypes = [vp, vp, i64, i64, i64, vp, vp, ctypes.c_int]
+        L.oracle_qkv_proj.restype = ctypes.c_int
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -203,6 +205,25 @@ def gate_up_swiglu(x_bits, w_gate_bits, w_up_bits, nthreads: int = 1):
                                      nthreads)
     if rc != 0:
         raise ValueError("gate_up_swiglu: bad sizes")
+    return a64, abf
+
+
+def qkv_proj(x_bits, w_bits, nthreads: int = 1):
+    """a = x . W_qkv (the rank's columns); returns (double array, bf16 bits).
+
+    x_bits: uint16 [batch, hidden]; w_bits: uint16 [hidden, cols] (bf16).
+    """
+    x = _c(x_bits, np.uint16)
+    w = _c(w_bits, np.uint16)
+    b, h = x.shape
+    if w.shape[0] != h:
+        raise ValueError("x and w disagree on hidden")
+    c = w.shape[1]
+    a64 = np.empty((b, c), np.float64)
+    abf = np.empty((b, c), np.uint16)
+    rc = lib().oracle_qkv_proj(_ptr(x), _ptr(w), b, h, c, _ptr(a64), _ptr(abf), nthreads)
+    if rc != 0:
+        raise ValueError("qkv_proj: bad sizes")
     return a64, abf
 
 

@@ -482,3 +482,36 @@ int oracle_gate_up_swiglu(const uint16_t* x, const uint16_t* w_gate, const uint1
     free(u);
     return 0;
 }
+
+/*
+ * Column-parallel mixer input projection of one rank (lesson 9.9, Conceito:
+ * the attention heads are split over the ranks by columns, so a rank
+ * computes its heads' Q, K and V columns from the full hidden state, with no
+ * reduction; "Hosting Qwen on Blackwell", Prefillers: with fewer key-value
+ * heads than ranks the K and V columns are replicated, which only changes
+ * which columns a rank holds):
+ *     a[b, n] = sum_{h < hidden} x[b, h] * w[h, n]
+ * the exact sum (oracle_partial's fp64 accumulation) rounded to bf16
+ * nearest-even through binary32, as the activation is stored.
+ *   x bf16 [batch][hidden], w bf16 [hidden][cols] (the rank's columns)
+ *   a64 [batch][cols] (may be NULL), a_bf16 [batch][cols] (may be NULL)
+ * Pins: a permutation matrix gives a column permutation of x (bits equal),
+ * small-integer inputs give the exact integer sums of a brute-force loop,
+ * and the columns of a wide matrix split into slices give the slices of the
+ * wide result.
+ */
+int oracle_qkv_proj(const uint16_t* x, const uint16_t* w, int64_t batch, int64_t hidden,
+                    int64_t cols, double* a64, uint16_t* a_bf16, int nthreads)
+{
+    if (batch < 0 || hidden < 0 || cols < 0) return -1;
+    size_t n = (size_t)(batch * cols);
+    double* y = (double*)malloc((n ? n : 1) * sizeof(double));
+    if (!y) return -1;
+    oracle_partial(x, hidden, w, batch, hidden, cols, y, NULL, nthreads);
+    for (size_t i = 0; i < n; ++i) {
+        if (a64) a64[i] = y[i];
+        if (a_bf16) a_bf16[i] = float_to_bf16_bits((float)y[i]);
+    }
+    free(y);
+    return 0;
+}

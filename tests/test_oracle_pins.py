@@ -452,3 +452,51 @@ def test_swiglu_large_gate_tends_to_g_times_u():
     up, _ = oracle.partial(x, wu)
     assert gate.min() >= 40.0
     assert np.allclose(a64, gate * up, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------ column-parallel QKV projection --
+
+def test_qkv_permutation_matrix_permutes_columns():
+    # W[h, n] = 1 where h = perm[n]: a[:, n] = x[:, perm[n]], bit for bit (one
+    # nonzero product per sum). A transposed W would give perm's inverse.
+    g = np.random.default_rng(80)
+    h = 24
+    x = _bf16(g.standard_normal((3, h)))
+    perm = g.permutation(h)
+    assert not np.array_equal(perm, np.argsort(perm))  # not its own inverse
+    w = np.zeros((h, h), np.uint16)
+    w[perm, np.arange(h)] = 0x3F80  # bf16 1.0
+    a64, abf = oracle.qkv_proj(x, w)
+    assert np.array_equal(abf, x[:, perm])
+    assert np.array_equal(a64, synth.bf16_bits_to_f32(x[:, perm]).astype(np.float64))
+
+
+def test_qkv_small_integers_match_brute_force():
+    # integer inputs in [-3, 3]: every product and sum is exact in double and
+    # below 256 in magnitude, so exact in bf16 too; a plain loop decides
+    g = np.random.default_rng(81)
+    b, h, c = 2, 5, 4
+    xi = g.integers(-3, 4, (b, h))
+    wi = g.integers(-3, 4, (h, c))
+    a64, abf = oracle.qkv_proj(_bf16(xi), _bf16(wi))
+    for i in range(b):
+        for n in range(c):
+            ex = 0
+            for k in range(h):
+                ex += int(xi[i, k]) * int(wi[k, n])
+            assert a64[i, n] == ex
+            assert abf[i, n] == _bf16([float(ex)])[0]
+
+
+def test_qkv_column_slices_give_slices_of_the_wide_result():
+    # the rank's slice of a wide W gives that slice of the wide projection,
+    # so the columns of w are read with the slice's own row stride
+    g = np.random.default_rng(82)
+    b, h, c = 4, 40, 9
+    x = _bf16(g.standard_normal((b, h)))
+    wide = _bf16(g.standard_normal((h, 3 * c)) * 0.1)
+    a_wide, bits_wide = oracle.qkv_proj(x, wide)
+    for r in range(3):
+        a_r, bits_r = oracle.qkv_proj(x, np.ascontiguousarray(wide[:, r * c:(r + 1) * c]))
+        assert np.array_equal(a_r, a_wide[:, r * c:(r + 1) * c])
+        assert np.array_equal(bits_r, bits_wide[:, r * c:(r + 1) * c])
