@@ -120,6 +120,21 @@ def measured_traffic(w, layout):
     return int(m_bytes.group(1))
 
 
+# Key-value heads and head width of the QKV projection's synthetic width:
+# four key-value heads ("Hosting Qwen on Blackwell", Prefillers, for its
+# model); a head of 128 columns is a reading.
+QKV_KV_HEADS = 4
+QKV_HEAD_DIM = 128
+
+
+def qkv_cols(k_attn, n_ranks):
+    """The rank's Q, K and V columns: its k_attn / N query columns, and its
+    share of the key-value heads for K and V, one head each where the ranks
+    outnumber the heads (the heads are then replicated)."""
+    kv = max(QKV_KV_HEADS // n_ranks, 1) * QKV_HEAD_DIM
+    return k_attn // n_ranks + 2 * kv
+
+
 def time_steps(step, steps, warmup, stream):
     """W untimed steps, then K timed steps between two HIP events recorded
     on the stream the library launches on. Returns ms per step."""
@@ -219,7 +234,7 @@ def dense_run(args, w, tune):
         kernel = "tp_rowparallel_partials_packed: decode_stream, partials only, one launch per pass"
         return ms, w.batch, nbytes, kernel, config, None, {"traffic": None}
     if args.op != "step":
-        if layout != "rowmajor" and args.op != "swiglu":
+        if layout != "rowmajor" and args.op not in ("swiglu", "qkv"):
             raise SystemExit("--op %s runs on row-major weights (--layout rowmajor)" % args.op)
         return single_op_run(args, w, plan, info, tune, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
@@ -253,7 +268,8 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
     tp_ring_reduce (ring-order sum of the N partials + residual), once per
     reconciliation point (2L calls per pass, each its own launch);
     "swiglu" = tp_gate_up_swiglu (the stack's column-parallel up
-    projections with SwiGLU, one call)."""
+    projections with SwiGLU, one call); "qkv" = tp_qkv_proj (the stack's
+    column-parallel mixer input projections, one call)."""
     import torch
 
     import row_gemv_reduction_amd as tp
@@ -279,6 +295,25 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
         kernel = ("tp_gate_up_swiglu: the persistent step's tiles (gate and up as the two "
                   "points of each layer) + swiglu_kernel, over as many layers per launch as "
                   "32 MiB of fp32 sums hold")
+    elif args.op == "qkv":
+        # the column-parallel mixer input projection of the same stack: Q
+        # columns = the mixer output's K / N, K and V = QKV_KV_HEADS heads of
+        # QKV_HEAD_DIM each, replicated where ranks outnumber them
+        from row_gemv_reduction_amd import synth
+        C = qkv_cols(w.k_attn, N)
+        plan = tp.Plan(H, w.inter, N, b, k_attn=w.k_attn, tune=tune, qkv_cols=C)
+        ws = plan.new_workspace()
+        kw = dict(seed=0, workload=w.name, rank=args.rank)
+        xin = synth.device_normal((L, b, H), 1.0, torch.bfloat16, tensor="x_qkv_in", **kw)
+        wq = synth.device_normal((L, H, C), synth.WEIGHT_STD, torch.bfloat16, tensor="w_qkv", **kw)
+        qkv = torch.empty((L, b, C), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            tp.tp_qkv_proj(plan, L, xin, wq, qkv, ws)
+        graph_ok = False  # cooperative launches, issued from C
+        nbytes = L * (H * C * 2 + b * H * 2 + b * C * 2)
+        kernel = ("tp_qkv_proj: the persistent step's tiles (two layers as its two points, "
+                  "%d columns per rank) + round_bf16_kernel" % C)
     elif args.op == "partials":
         def step():
             tp.tp_rowparallel_partials(plan, L, xa, wo, xf, wd, pstack, ws)
@@ -506,7 +541,7 @@ def main():
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
-    ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu"], default="step",
+    ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu", "qkv"], default="step",
                     help="what a timed pass runs: the whole decode step (default); the stack's "
                          "2L partial projections in one call (tp_rowparallel_partials); one "
                          "entry point per reconciliation point (tp_rowparallel_partial, "

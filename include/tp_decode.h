@@ -113,6 +113,16 @@ tp_status tp_plan_set_attn_dim(tp_plan_t plan, int64_t k_attn);
  * and Expert Parallel). Must be called before first use.
  * TP_ERR_INVALID_ARG on sizes < 1, top_k > n_experts or ep not dividing
  * n_experts; TP_ERR_UNSUPPORTED if top_k > 32 or max_tokens > 4096. */
+/*
+ * Give the plan the width of the rank's mixer input projection: `cols` =
+ * the Q, K and V columns this rank holds (its heads' columns, with K and V
+ * replicated where there are fewer key-value heads than ranks: "Hosting
+ * Qwen on Blackwell", Prefillers). Needed by tp_qkv_proj; widens
+ * info.workspace_bytes to cover it. TP_ERR_INVALID_ARG unless cols >= 8
+ * and cols is a multiple of 8; TP_ERR_UNSUPPORTED above 2^24.
+ */
+tp_status tp_plan_set_qkv_dim(tp_plan_t plan, int64_t cols);
+
 tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int32_t ep,
                           int64_t moe_inter, int32_t max_tokens);
 
@@ -142,8 +152,9 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "step_kind" (tp_decode_layers, tp_rowparallel_partials, batch < 16: the
  *                persistent step's kind, 0 = automatic, 1 = vector ALU,
  *                2 = matrix cores; from 16 tokens always matrix cores),
- * "swiglu_layers" (tp_gate_up_swiglu: most layers per launch, 0 =
- *                automatic: as many as 32 MiB of fp32 gate and up sums hold),
+ * "swiglu_layers" (tp_gate_up_swiglu, tp_qkv_proj: most layers per
+ *                launch, 0 = automatic: as many as 32 MiB of fp32 sums hold;
+ *                tp_qkv_proj rounds it down to an even number, at least 2),
  * "step_rows" (tp_decode_layers, tp_rowparallel_partials,
  *                tp_gate_up_swiglu: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core
@@ -240,6 +251,26 @@ tp_status tp_rowparallel_partials(tp_plan_t plan, int32_t n_layers, const void* 
  */
 tp_status tp_gate_up_swiglu(tp_plan_t plan, int32_t n_layers, const void* x, const void* w_gate,
                             const void* w_up, void* out, void* workspace, void* stream);
+
+/*
+ * Column-parallel mixer input projection for a layer stack (lesson 9.9,
+ * Conceito: the attention heads are split over the ranks by columns, so a
+ * rank computes its heads' Q, K and V columns from the full hidden state,
+ * with no reduction):
+ *     a[l] = bf16( x[l] . w_qkv[l] )
+ *   x      bf16 [L][batch][hidden] (the full hidden state of each layer)
+ *   w_qkv  bf16 [L][hidden][cols] row-major, cols = tp_plan_set_qkv_dim's
+ *   out    bf16 [L][batch][cols] (output)
+ * fp32 accumulation on the persistent step's tiles (two consecutive layers
+ * as its two points, an odd last layer in a launch of its own; matrix-core
+ * tiles span the whole K unless "step_rows" is set), rounded to bf16
+ * nearest-even by a second launch. n_layers = 0 does nothing (the pointers
+ * may then be null). TP_ERR_UNSUPPORTED if tp_plan_set_qkv_dim was not
+ * called; TP_ERR_ALIGNMENT for pointers not 16-byte aligned;
+ * TP_ERR_INVALID_ARG for a null pointer or n_layers < 0.
+ */
+tp_status tp_qkv_proj(tp_plan_t plan, int32_t n_layers, const void* x, const void* w_qkv, void* out,
+                      void* workspace, void* stream);
 
 /*
  * Ring-ordered all-reduce sum of the N partials plus the residual

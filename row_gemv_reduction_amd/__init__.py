@@ -8,7 +8,7 @@ from . import synth, workloads  # noqa: F401
 from .binding import (  # noqa: F401
     TP_PATH_MFMA, TP_PATH_VALU, TP_POINT_ATTN_OUT, TP_POINT_FFN_DOWN, Plan, TPError,
     moe_packed_shape, packed_act_shape, packed_shape, tp_decode_layers, tp_decode_layers_packed,
-    tp_decode_point, tp_gate_up_swiglu, tp_moe_decode, tp_pack_activations,
+    tp_decode_point, tp_gate_up_swiglu, tp_moe_decode, tp_pack_activations, tp_qkv_proj,
     tp_moe_pack_experts, tp_moe_partial, tp_moe_route, tp_pack_weights,
     tp_plan, tp_ring_reduce, tp_rowparallel_partial, tp_rowparallel_partials,
     tp_rowparallel_partials_packed, tp_workspace_init,

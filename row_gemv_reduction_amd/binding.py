@@ -49,6 +49,7 @@ EXPORTS = {
     "tp_plan": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                ctypes.POINTER(ctypes.c_void_p)]),
     "tp_plan_set_attn_dim": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "tp_plan_set_qkv_dim": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
     "tp_plan_set_moe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "tp_plan_tune": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int64]),
@@ -64,6 +65,7 @@ EXPORTS = {
     "tp_rowparallel_partials": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
                                 + [ctypes.c_void_p] * 7),
     "tp_gate_up_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 6),
+    "tp_qkv_proj": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 5),
     "tp_ring_reduce": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "tp_decode_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
@@ -133,12 +135,16 @@ class Plan:
     """Owns a tp_plan_t. Sizes follow tp_plan(); optional k_attn, MoE share
     and tuning knobs are applied before first use."""
 
-    def __init__(self, hidden, inter, n_ranks, batch, k_attn=None, moe=None, tune=None):
+    def __init__(self, hidden, inter, n_ranks, batch, k_attn=None, moe=None, tune=None,
+                 qkv_cols=None):
         h = ctypes.c_void_p()
         _check(_lib().tp_plan(hidden, inter, n_ranks, batch, ctypes.byref(h)), "tp_plan")
         self._h = h
         self._info = None  # tp_plan_info, read once per state of the plan
+        self.qkv_cols = qkv_cols  # the rank's Q, K and V columns (tp_plan_set_qkv_dim)
         try:
+            if qkv_cols is not None:
+                _check(_lib().tp_plan_set_qkv_dim(h, qkv_cols), "tp_plan_set_qkv_dim")
             if k_attn is not None:
                 _check(_lib().tp_plan_set_attn_dim(h, k_attn), "tp_plan_set_attn_dim")
             if moe is not None:
@@ -259,6 +265,22 @@ def tp_gate_up_swiglu(plan: Plan, n_layers, x, w_gate, w_up, out, workspace):
     if workspace.numel() < i["workspace_bytes"]:
         raise ValueError("workspace too small")
     _check(_lib().tp_gate_up_swiglu(plan.handle, L, *args, _stream()), "tp_gate_up_swiglu")
+
+
+def tp_qkv_proj(plan: Plan, n_layers, x, w_qkv, out, workspace):
+    """out[l] = bf16(x[l] . w_qkv[l]), the rank's Q, K and V columns."""
+    if plan.qkv_cols is None:
+        raise ValueError("the plan has no QKV width (Plan(..., qkv_cols=...))")
+    i = plan._plan_info()
+    b, H, C = i["batch"], i["hidden"], plan.qkv_cols
+    L = n_layers
+    args = (_dev(x, "x", torch.bfloat16, (L, b, H)),
+            _dev(w_qkv, "w_qkv", torch.bfloat16, (L, H, C)),
+            _dev(out, "out", torch.bfloat16, (L, b, C)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_qkv_proj(plan.handle, L, *args, _stream()), "tp_qkv_proj")
 
 
 def tp_ring_reduce(plan: Plan, partials, residual, out, out_bf16=None):

@@ -87,6 +87,7 @@ struct tp_plan_s {
     int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)
     int32_t step_kind = 0;      // persistent step: 0 = automatic, 1 = vector ALU (b < 16), 2 = matrix cores
     int32_t swiglu_layers = 0;  // tp_gate_up_swiglu: most layers per launch (0 = automatic)
+    int64_t qkv_cols = 0;       // tp_qkv_proj: the rank's Q, K and V columns (0 = not set)
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -148,11 +149,17 @@ int64_t tp_xchg_bytes(const tp_plan_s* p);  // exchange buffers of the MFMA stre
 // The column-parallel up projection: its derived plan (a persistent
 // partials step with the gate and up matrices as the two points), whether
 // the plan supports it, and where its fp32 sums sit in the workspace.
+tp_plan_s tp_colproj_plan(const tp_plan_s* p, int64_t cols);
 tp_plan_s tp_swiglu_plan(const tp_plan_s* p);
 bool tp_swiglu_ok(const tp_plan_s* p);
 int64_t tp_ws_swiglu_offset(const tp_plan_s* p);
 constexpr int64_t kSwigluSumsBytes = 32 << 20;  // fp32 gate and up sums per launch
 int32_t tp_swiglu_layers_per_launch(const tp_plan_s* p);
+// The column-parallel QKV projection: the same derived step with two
+// consecutive layers as its two points, and its fp32 sums.
+bool tp_qkv_ok(const tp_plan_s* p);
+int64_t tp_ws_qkv_offset(const tp_plan_s* p);
+int32_t tp_qkv_layers_per_launch(const tp_plan_s* p);
 int64_t tp_ws_xchg_offset(const tp_plan_s* p);
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);

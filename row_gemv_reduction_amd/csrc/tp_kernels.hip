@@ -474,6 +474,8 @@ struct StepArgs {
     int32_t col_tiles, layers, n_ranks, rank;
     int32_t batch;
     int32_t serial;         // 1: point j+1 reads its activation after all of point j
+    int32_t lstep;          // layers of x and W between two layers of the step (1, or 2
+                            // when two consecutive layers are its two points)
     int64_t chunk;
     uint32_t spin_limit;
 };
@@ -500,8 +502,8 @@ __device__ __forceinline__ StepTile step_tile(const StepArgs& a, int64_t q) {
     t.k0 = (int64_t)t.sp * a.rows[t.pt];
     t.nr = (int)(t.K - t.k0 < a.rows[t.pt] ? t.K - t.k0 : a.rows[t.pt]);
     t.splits = a.splits[t.pt];
-    t.x = a.x[t.pt] + (int64_t)l * a.batch * t.K;
-    t.w = a.w[t.pt] + (int64_t)l * t.K * a.H;
+    t.x = a.x[t.pt] + (int64_t)l * a.lstep * a.batch * t.K;
+    t.w = a.w[t.pt] + (int64_t)l * a.lstep * t.K * a.H;
     return t;
 }
 
@@ -870,6 +872,13 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* sums, uint16_t
     out[i] = f32_to_bf16_rne(silu * sums[(2 * l + 1) * len + e]);
 }
 
+// fp32 sums rounded to bf16 nearest-even (the QKV projection's output).
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float* sums, uint16_t* out,
+                                                         int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < total) out[i] = f32_to_bf16_rne(sums[i]);
+}
+
 // ------------------------------------------------------------ MFMA GEMM --
 
 template <int BT>  // batch tiles of 16 rows
@@ -1150,7 +1159,8 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
 // no residual) into partials [L][2][b][H].
 tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
                             const void* w_o, const void* x_ffn, const void* w_down, float* slots,
-                            float* hidden, float* partials, void* ws, hipStream_t st) {
+                            float* hidden, float* partials, void* ws, hipStream_t st,
+                            int32_t lstep = 1) {
     const int b = p->batch;
     if (b < 1 || b > kMfmaMaxBatch) return TP_ERR_UNSUPPORTED;
     const bool mfma = tp_step_mfma(p);
@@ -1202,6 +1212,7 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     }
     a.col_tiles = geo[0].col_tiles;
     a.layers = n_layers;
+    a.lstep = lstep;
     a.n_ranks = p->n_ranks;
     a.rank = rank;
     a.chunk = (int64_t)b * p->hidden / p->n_ranks;
@@ -1290,6 +1301,53 @@ tp_status tp_gate_up_swiglu(tp_plan_t p, int32_t n_layers, const void* x, const 
                            static_cast<uint16_t*>(out) + (int64_t)l0 * b * C, b * C, total);
         if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
     }
+    return TP_OK;
+}
+
+tp_status tp_qkv_proj(tp_plan_t p, int32_t n_layers, const void* x, const void* w_qkv, void* out,
+                      void* ws, void* stream) {
+    if (!p || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (n_layers == 0) return TP_OK;  // nothing is read or written
+    if (!x || !w_qkv || !out || !ws) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(out) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    if (!tp_qkv_ok(p)) return TP_ERR_UNSUPPORTED;
+    const int64_t b = p->batch, H = p->hidden, C = p->qkv_cols;
+    if ((b * C) % 8) return TP_ERR_ALIGNMENT;  // each layer's output slice stays 16-byte aligned
+    const tp_plan_s q = tp_colproj_plan(p, C);
+    float* sums = reinterpret_cast<float*>(static_cast<char*>(ws) + tp_ws_qkv_offset(p));
+    const int32_t per = tp_qkv_layers_per_launch(p);  // even
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* wb = static_cast<const uint16_t*>(w_qkv);
+    uint16_t* ob = static_cast<uint16_t*>(out);
+    hipStream_t st = (hipStream_t)stream;
+    // Layers 2u and 2u+1 of a launch are the two points of the step's layer
+    // u (layer stride 2), so their sums land in layer order. An odd last
+    // layer takes a launch of its own, as both points (the second's sums
+    // are not used).
+    const int32_t even = n_layers - n_layers % 2;
+    const int32_t launches = (even + per - 1) / per;
+    auto run = [&](int32_t l0, int32_t units, int32_t lstep) -> tp_status {
+        const uint16_t* x0 = xb + (int64_t)l0 * b * H;
+        const uint16_t* w0 = wb + (int64_t)l0 * H * C;
+        const uint16_t* x1 = lstep == 2 ? x0 + b * H : x0;
+        const uint16_t* w1 = lstep == 2 ? w0 + H * C : w0;
+        tp_status s = decode_persistent(&q, units, 0, x0, w0, x1, w1, nullptr, nullptr, sums, ws, st,
+                                        lstep);
+        if (s != TP_OK) return s;
+        const int64_t total = (int64_t)(lstep == 2 ? 2 * units : 1) * b * C;
+        hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, sums,
+                           ob + (int64_t)l0 * b * C, total);
+        return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    };
+    for (int32_t k = 0; k < launches; ++k) {
+        // layer pairs spread evenly over the launches
+        const int32_t u0 = (int32_t)((int64_t)k * (even / 2) / launches);
+        const int32_t u1 = (int32_t)((int64_t)(k + 1) * (even / 2) / launches);
+        tp_status s = run(2 * u0, u1 - u0, 2);
+        if (s != TP_OK) return s;
+    }
+    if (n_layers % 2) return run(n_layers - 1, 1, 1);
     return TP_OK;
 }
 

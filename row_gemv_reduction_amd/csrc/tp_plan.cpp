@@ -163,9 +163,12 @@ static int64_t partial_bytes(const tp_plan_s* p) {
 // The column-parallel up projection (tp_gate_up_swiglu) as a persistent
 // partials step: both "points" read x [b][H]; point 0 is the gate, point 1
 // the up matrix, each [H][I/N]; the output width is I/N; one rank.
-tp_plan_s tp_swiglu_plan(const tp_plan_s* p) {
+// A column-parallel projection from the full hidden state to `cols`
+// columns of this rank, as a persistent partials step of its own: K = H,
+// output width cols, one rank.
+tp_plan_s tp_colproj_plan(const tp_plan_s* p, int64_t cols) {
     tp_plan_s q = *p;
-    q.hidden = p->inter / p->n_ranks;
+    q.hidden = cols;
     q.k_attn = p->hidden;
     q.inter = p->hidden;
     q.n_ranks = 1;
@@ -182,6 +185,29 @@ tp_plan_s tp_swiglu_plan(const tp_plan_s* p) {
     if (p->step_rows <= 0 && tp_step_mfma(&q) && (k_all + 1024) * q.hidden * 2 < (int64_t(1) << 31))
         q.step_rows = (int32_t)k_all;
     return q;
+}
+
+tp_plan_s tp_swiglu_plan(const tp_plan_s* p) { return tp_colproj_plan(p, p->inter / p->n_ranks); }
+
+bool tp_qkv_ok(const tp_plan_s* p) {
+    return p->qkv_cols > 0 && p->qkv_cols % 8 == 0 && p->batch >= 1 && p->batch <= kMfmaMaxBatch;
+}
+
+int64_t tp_ws_qkv_offset(const tp_plan_s* p) {
+    tp_plan_s q = tp_colproj_plan(p, p->qkv_cols);
+    return kCounterBytes + partial_bytes(&q);
+}
+
+// Layers per launch of tp_qkv_proj: an even number (two layers are the
+// step's two points) whose fp32 sums [layers][b][cols] fit kSwigluSumsBytes,
+// at least two, at most "swiglu_layers" when that is set.
+int32_t tp_qkv_layers_per_launch(const tp_plan_s* p) {
+    const int64_t per_layer = (int64_t)p->batch * p->qkv_cols * 4;
+    int64_t n = per_layer > 0 ? kSwigluSumsBytes / per_layer : 2;
+    if (p->swiglu_layers > 0 && n > p->swiglu_layers) n = p->swiglu_layers;
+    if (n > 4096) n = 4096;
+    n -= n % 2;
+    return (int32_t)(n < 2 ? 2 : n);
 }
 
 bool tp_swiglu_ok(const tp_plan_s* p) {
@@ -221,6 +247,11 @@ int64_t tp_workspace_bytes(const tp_plan_s* p) {
                                    256);
         if (s > m) m = s;
     }
+    if (tp_qkv_ok(p)) {
+        const int64_t s = tp_ws_qkv_offset(p) +
+                          round_up((int64_t)tp_qkv_layers_per_launch(p) * p->batch * p->qkv_cols * 4, 256);
+        if (s > m) m = s;
+    }
     return m;
 }
 
@@ -256,6 +287,13 @@ tp_status tp_plan_set_attn_dim(tp_plan_t p, int64_t k_attn) {
     if (!p || k_attn < 1 || k_attn % p->n_ranks) return TP_ERR_INVALID_ARG;
     if (k_attn > (int64_t)1 << 24) return TP_ERR_UNSUPPORTED;
     p->k_attn = k_attn;
+    return TP_OK;
+}
+
+tp_status tp_plan_set_qkv_dim(tp_plan_t p, int64_t cols) {
+    if (!p || cols < 8 || cols % 8) return TP_ERR_INVALID_ARG;
+    if (cols > (int64_t)1 << 24) return TP_ERR_UNSUPPORTED;
+    p->qkv_cols = cols;
     return TP_OK;
 }
 

@@ -29,7 +29,7 @@ WEIGHT_STD = 0.02
 TENSOR_IDS = {
     "x": 1, "w": 2, "x_attn": 3, "w_o": 4, "x_ffn": 5, "w_down": 6,
     "residual": 7, "slots": 8, "logits": 9, "u": 10, "w_expert": 11,
-    "partials": 12, "x_ffn_in": 13, "w_gate": 14, "w_up": 15,
+    "partials": 12, "x_ffn_in": 13, "w_gate": 14, "w_up": 15, "x_qkv_in": 16, "w_qkv": 17,
 }
 
 

@@ -1,0 +1,92 @@
+"""GPU parity of the column-parallel QKV projection (tp_qkv_proj) against
+the CPU oracle.
+
+The output is bf16, so the bar is the bf16-output reading of the tolerance:
+every element within max(1e-2 * rms, one bf16 ulp) of the oracle's double
+value, and nearly all of them rounded as the oracle rounds (the GPU rounds
+its fp32 sum, the oracle the exact sum, so only values next to a rounding
+boundary can differ).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from row_gemv_reduction_amd import binding as tp
+from row_gemv_reduction_amd import synth
+from tests.gpu_helpers import assert_bits_equal, bf16_bits_host, say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(v), np.float64(2.0 ** -126))
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+# (n_ranks, batch, hidden, cols, layers, swiglu_layers, step_rows): vector-ALU
+# and matrix-core steps, odd and even stacks, several launches ending on a
+# lone odd layer, one tile per K and split K with a ragged 32-row step
+CASES = [
+    (1, 1, 520, 264, 3, 0, 0), (4, 3, 1024, 1536, 4, 0, 0), (2, 8, 264, 1000, 2, 0, 0),
+    (4, 16, 1032, 776, 5, 2, 0), (8, 64, 512, 384, 2, 0, 0), (2, 24, 4104, 520, 3, 0, 512),
+    (1, 5, 2048, 1024, 1, 0, 0), (4, 40, 1024, 2048, 6, 4, 0),
+]
+
+
+@pytest.mark.parametrize("n,b,h,cols,L,per,rows", CASES)
+def test_qkv_proj_matches_oracle(n, b, h, cols, L, per, rows):
+    say("qkv n=%d b=%d h=%d cols=%d L=%d per=%d rows=%d" % (n, b, h, cols, L, per, rows))
+    kw = dict(seed=91, workload="qkv")
+    x = synth.normal_bf16((L, b, h), 1.0, tensor="x_qkv_in", **kw)
+    w = synth.normal_bf16((L, h, cols), synth.WEIGHT_STD, tensor="w_qkv", **kw)
+    plan = tp.Plan(h, 2048, n, b, qkv_cols=cols, tune={"swiglu_layers": per, "step_rows": rows})
+    ws = plan.new_workspace()
+    X, W = to_dev_bf16(x), to_dev_bf16(w)
+    out = torch.empty((L, b, cols), dtype=torch.bfloat16, device="cuda")
+    tp.tp_qkv_proj(plan, L, X, W, out, ws)
+    out2 = torch.empty_like(out)
+    tp.tp_qkv_proj(plan, L, X, W, out2, ws)
+    torch.cuda.synchronize()
+    assert tp.tp_workspace_status(plan, ws) == 0
+    got = bf16_bits_host(out)
+    assert_bits_equal(bf16_bits_host(out2), got, "repeat")
+    for l in range(L):
+        a64, abf = oracle.qkv_proj(x[l], w[l])
+        gotf = synth.bf16_bits_to_f32(got[l]).astype(np.float64)
+        rms = float(np.sqrt(np.mean(a64 ** 2)))
+        bound = np.maximum(1e-2 * rms, bf16_ulp(a64))
+        err = np.abs(gotf - a64)
+        assert np.all(err <= bound), "layer %d: max excess %.3e" % (l, float((err - bound).max()))
+        same = float(np.mean(got[l] == abf))
+        assert same >= 0.99, "layer %d: only %.3f of the elements round as the oracle's" % (l, same)
+
+
+def test_qkv_proj_needs_width_and_empty_stack():
+    """Without tp_plan_set_qkv_dim the call is refused; an empty stack does
+    nothing."""
+    b, h, cols = 2, 520, 264
+    plan = tp.Plan(h, 2048, 2, b)
+    plan.qkv_cols = cols  # the Python side only: the library still has none
+    ws = plan.new_workspace()
+    x = torch.zeros((1, b, h), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((1, h, cols), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, b, cols), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tp.TPError):
+        tp.tp_qkv_proj(plan, 1, x, w, out, ws)
+    plan2 = tp.Plan(h, 2048, 2, b, qkv_cols=cols)
+    ws2 = plan2.new_workspace()
+    tp.tp_qkv_proj(plan2, 0, torch.empty((0, b, h), dtype=torch.bfloat16, device="cuda"),
+                   torch.empty((0, h, cols), dtype=torch.bfloat16, device="cuda"),
+                   torch.empty((0, b, cols), dtype=torch.bfloat16, device="cuda"), ws2)
+    torch.cuda.synchronize()
