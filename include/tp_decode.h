@@ -155,6 +155,11 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * "swiglu_layers" (tp_gate_up_swiglu, tp_qkv_proj: most layers per
  *                launch, 0 = automatic: as many as 32 MiB of fp32 sums hold;
  *                tp_qkv_proj rounds it down to an even number, at least 2),
+ * "xcd_walk" (the persistent step: 1 = each XCD's workgroups take
+ *                contiguous tiles of every round, so that a point's column
+ *                tiles share an L2; the same bits; 0 = off, the default:
+ *                it pays only where narrow points read a wide x, as the
+ *                QKV projection at 16+ tokens),
  * "step_rows" (tp_decode_layers, tp_rowparallel_partials,
  *                tp_gate_up_swiglu: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core

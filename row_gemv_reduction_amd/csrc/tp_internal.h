@@ -87,6 +87,7 @@ struct tp_plan_s {
     int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)
     int32_t step_kind = 0;      // persistent step: 0 = automatic, 1 = vector ALU (b < 16), 2 = matrix cores
     int32_t swiglu_layers = 0;  // tp_gate_up_swiglu: most layers per launch (0 = automatic)
+    int32_t xcd_walk = 0;       // persistent step: 1 = XCD-contiguous tile walk
     int64_t qkv_cols = 0;       // tp_qkv_proj: the rank's Q, K and V columns (0 = not set)
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;

@@ -474,6 +474,7 @@ struct StepArgs {
     int32_t col_tiles, layers, n_ranks, rank;
     int32_t batch;
     int32_t serial;         // 1: point j+1 reads its activation after all of point j
+    int32_t xcd_walk;       // 1: each XCD's workgroups take contiguous tiles per round
     int32_t lstep;          // layers of x and W between two layers of the step (1, or 2
                             // when two consecutive layers are its two points)
     int64_t chunk;
@@ -505,6 +506,21 @@ __device__ __forceinline__ StepTile step_tile(const StepArgs& a, int64_t q) {
     t.x = a.x[t.pt] + (int64_t)l * a.lstep * a.batch * t.K;
     t.w = a.w[t.pt] + (int64_t)l * a.lstep * t.K * a.H;
     return t;
+}
+
+// The first tile of a workgroup's walk (then every gridDim.x-th). The
+// hardware deals workgroups to the 8 XCDs round-robin (blockIdx.x mod 8),
+// each XCD with its own L2. With xcd_walk set, each XCD's workgroups take a
+// contiguous range of the tile indices of every round, so that neighbouring
+// column tiles of a point, which read the same x, share one L2. Every
+// workgroup still walks its tiles in increasing order, one per round, so
+// the waits between points resolve as in the plain walk, and no sum
+// changes order.
+__device__ __forceinline__ int64_t step_first_tile(const StepArgs& a) {
+    constexpr int kXcds = 8;
+    const int g = (int)gridDim.x, bid = (int)blockIdx.x;
+    if (!a.xcd_walk || g % kXcds) return bid;
+    return (int64_t)(bid % kXcds) * (g / kXcds) + bid / kXcds;
 }
 
 // After a tile's partial is in LDS (tile[b][COLS]): publish it to this
@@ -692,14 +708,15 @@ __global__ __launch_bounds__(kValuWaves * 64) void decode_step(StepArgs a) {
         return sh.wflag != 0;
     };
 
-    // The workgroup's tiles q = blockIdx.x + m*gridDim.x. A tile's first two
+    // The workgroup's tiles q = q0 + m*gridDim.x. A tile's first two
     // banks are issued before the previous tile is reduced and published.
     u32x4_t va[NB], vb[NB];
-    if ((int64_t)blockIdx.x < total) {
-        const StepTile t0 = step_tile(a, blockIdx.x);
+    const int64_t q0 = step_first_tile(a);
+    if (q0 < total) {
+        const StepTile t0 = step_tile(a, q0);
         stream_issue<COLS, NB>(va, vb, LaneRows<COLS>(t0.w, a.H, t0.k0, t0.nr, t0.ct), a.H);
     }
-    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+    for (int64_t q = q0; q < total; q += gridDim.x) {
         const StepTile tq = step_tile(a, q);
 
         __syncthreads();  // LDS of the previous tile is no longer read
@@ -764,7 +781,7 @@ __global__ __launch_bounds__(kStepMfmaWaves * 64) void decode_step_mfma(StepArgs
         return sh.wflag != 0;
     };
 
-    for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+    for (int64_t q = step_first_tile(a); q < total; q += gridDim.x) {
         const StepTile tq = step_tile(a, q);
         const int nr = tq.nr;
 
@@ -1213,6 +1230,7 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     a.col_tiles = geo[0].col_tiles;
     a.layers = n_layers;
     a.lstep = lstep;
+    a.xcd_walk = p->xcd_walk;
     a.n_ranks = p->n_ranks;
     a.rank = rank;
     a.chunk = (int64_t)b * p->hidden / p->n_ranks;

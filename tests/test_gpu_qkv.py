@@ -90,3 +90,29 @@ def test_qkv_proj_needs_width_and_empty_stack():
                    torch.empty((0, h, cols), dtype=torch.bfloat16, device="cuda"),
                    torch.empty((0, b, cols), dtype=torch.bfloat16, device="cuda"), ws2)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("b,h,cols,L", [(1, 1024, 768, 4), (64, 512, 384, 3)])
+def test_xcd_walk_gives_the_same_bits(b, h, cols, L):
+    """The XCD-contiguous tile walk ("xcd_walk") only changes which workgroup
+    takes which tile: the vector-ALU (b = 1) and matrix-core (b = 64) steps
+    give the same bits either way, for the QKV projection and for the up
+    projection with SwiGLU."""
+    say("xcd_walk b=%d h=%d cols=%d L=%d" % (b, h, cols, L))
+    kw = dict(seed=93, workload="qkv")
+    x = to_dev_bf16(synth.normal_bf16((L, b, h), 1.0, tensor="x_qkv_in", **kw))
+    w = to_dev_bf16(synth.normal_bf16((L, h, cols), synth.WEIGHT_STD, tensor="w_qkv", **kw))
+    wu = to_dev_bf16(synth.normal_bf16((L, h, cols), synth.WEIGHT_STD, tensor="w_up", **kw))
+    got = {}
+    for walk in (0, 1):
+        plan = tp.Plan(h, 2 * cols, 2, b, qkv_cols=cols, tune={"xcd_walk": walk})
+        ws = plan.new_workspace()
+        q = torch.empty((L, b, cols), dtype=torch.bfloat16, device="cuda")
+        a = torch.empty((L, b, cols), dtype=torch.bfloat16, device="cuda")
+        tp.tp_qkv_proj(plan, L, x, w, q, ws)
+        tp.tp_gate_up_swiglu(plan, L, x, w, wu, a, ws)
+        torch.cuda.synchronize()
+        assert tp.tp_workspace_status(plan, ws) == 0
+        got[walk] = (bf16_bits_host(q), bf16_bits_host(a))
+    assert_bits_equal(got[1][0], got[0][0], "qkv")
+    assert_bits_equal(got[1][1], got[0][1], "swiglu")
