@@ -58,3 +58,30 @@ def assert_bits_equal(got, want, what=""):
     bad = np.flatnonzero(gb.ravel() != wb.ravel())
     assert bad.size == 0, "%s: %d elements differ, first at %d: %r vs %r" % (
         what, bad.size, bad[0], got.ravel()[bad[0]], want.ravel()[bad[0]])
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 at |v| (8 significant bits; subnormal spacing below 2^-126)."""
+    a = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), np.float64(2.0 ** -126))
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def assert_bf16_rounding(got_bits, a64, slack, what=""):
+    """A bf16 output rounded once from a GPU fp32 value v: got = RNE_bf16(v)
+    with |v - a64| <= slack (per element, a bound on the fp32 value's error
+    against the exact a64). Then |got - a64| <= slack + half a bf16 ulp (at
+    the larger of the two magnitudes, for values next to a power of two).
+    Returns the fraction of elements equal to RNE_bf16 of the exact value's
+    fp32 rounding (reported, not a bar)."""
+    from row_gemv_reduction_amd import synth
+    got = synth.bf16_bits_to_f32(got_bits).astype(np.float64)
+    a64 = np.asarray(a64, dtype=np.float64)
+    half = 0.5 * np.maximum(bf16_ulp(a64), bf16_ulp(got))
+    bound = np.asarray(slack, dtype=np.float64) + half
+    err = np.abs(got - a64)
+    bad = np.flatnonzero(~(err <= bound))
+    assert bad.size == 0, "%s: %d elements beyond slack + half ulp, first at %d: got %r exact %r " \
+        "(slack %r)" % (what, bad.size, bad[0], got.ravel()[bad[0]], a64.ravel()[bad[0]],
+                        np.broadcast_to(slack, a64.shape).ravel()[bad[0]])
+    rne = synth.f32_to_bf16_bits(a64.astype(np.float32))
+    return float(np.mean(np.asarray(got_bits) == rne))

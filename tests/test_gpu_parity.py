@@ -333,6 +333,7 @@ def check_stack_sampled(w, rank=0, layers=None):
     P = host(slots).copy()
     h_or = host(h0).copy()
     s_got = host(S)
+    h_ring = ring_chain(s_got, host(h0))
     xa_h, xf_h = bf16_bits_host(xa), bf16_bits_host(xf)
     for l in range(w.layers):
         for pt, (xh, Wt) in enumerate(((xa_h, wo), (xf_h, wd))):
@@ -344,6 +345,8 @@ def check_stack_sampled(w, rank=0, layers=None):
             P[l, pt, rank] = 0.0
             P[l, pt, rank][:, cols] = ref32
             h_or = oracle.ring_reduce(P[l, pt], h_or)
+    # the fused ring stage on the GPU's own partials: bit for bit, every column
+    assert_bits_equal(host(Hd), h_ring, "%s: hidden vs the oracle's ring chain" % w.name)
     h_got = host(Hd)[:, cols].astype(np.float64)
     rms_p = np.sqrt(np.mean(s_got[:, :, rank][..., cols].astype(np.float64) ** 2))
     err = np.abs(h_got - h_or[:, cols]).max()
@@ -704,6 +707,17 @@ PACKED_CASES = [
 ]
 
 
+def ring_chain(slots_gpu, h0):
+    """The oracle's ring-order sum plus residual, chained over every point of
+    a step, on the slots the GPU left (its own partials included): given
+    identical partials the ring stage must match bit for bit."""
+    h = np.array(h0, dtype=np.float32, copy=True)
+    for l in range(slots_gpu.shape[0]):
+        for pt in range(2):
+            h = oracle.ring_reduce(slots_gpu[l, pt], h)
+    return h
+
+
 def check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0):
     s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
     for l in range(L):
@@ -711,6 +725,8 @@ def check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0):
         assert_partial_close(s_gpu[l, 1, rank], oracle.partial(xf[l], wd[l])[0], "ffn l=%d" % l)
     others = [r for r in range(n) if r != rank]
     assert_bits_equal(s_gpu[:, :, others], slots[:, :, others], "other ranks' slots untouched")
+    # the fused ring stage, bit for bit, on the GPU's own partials
+    assert_bits_equal(h_gpu, ring_chain(s_gpu, h0), "hidden vs the oracle's ring chain")
     _, h_or = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
     rms_p = np.sqrt(np.mean(s_gpu[:, :, rank].astype(np.float64) ** 2))
     err = np.abs(h_gpu.astype(np.float64) - h_or).max()
@@ -782,9 +798,23 @@ def test_mfma_stream_segments_match_oracle(n, b, h, ka, ki, rank, wgs):
     check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
 
 
-@pytest.mark.parametrize("b", [2, 16])
-def test_packed_decode_bit_exact_when_partials_are_exact(b):
-    L, n, h, ka, ki, rank = 4, 4, 256, 64, 128, 1
+EXACT_PACKED_CASES = [
+    # (kind, n, b, hidden, k_attn, inter, rank, workgroups): both streams;
+    # ring chunks b*H/N of 128 (aligned), 66 and 198 (= 2 mod 4: a chunk
+    # boundary inside a 4-column strip of the vector-ALU stream), 42 and 130
+    # (inside a lane's four columns of the matrix-core stream)
+    (1, 4, 2, 256, 64, 128, 1, 0), (1, 4, 1, 264, 64, 128, 2, 0), (1, 4, 3, 264, 64, 128, 3, 0),
+    (1, 8, 8, 264, 128, 256, 5, 0), (2, 4, 2, 256, 64, 128, 1, 0), (2, 4, 16, 256, 64, 128, 1, 0),
+    (2, 8, 7, 48, 512, 1024, 3, 2), (2, 8, 13, 80, 512, 1024, 6, 3), (2, 4, 33, 1040, 640, 2048, 2, 48),
+]
+
+
+@pytest.mark.parametrize("kind,n,b,h,ka,ki,rank,wgs", EXACT_PACKED_CASES)
+def test_packed_decode_bit_exact_when_partials_are_exact(kind, n, b, h, ka, ki, rank, wgs):
+    """Integer-valued x and W keep every partial exact on both sides, so
+    the whole step (the fused ring stage of either stream included) must
+    match the oracle bit for bit."""
+    L = 4
     g = np.random.default_rng(18)
     xa = synth.f32_to_bf16_bits(g.integers(-4, 5, (L, b, ka // n)).astype(np.float32))
     wo = synth.f32_to_bf16_bits(g.integers(-4, 5, (L, ka // n, h)).astype(np.float32))
@@ -792,8 +822,9 @@ def test_packed_decode_bit_exact_when_partials_are_exact(b):
     wd = synth.f32_to_bf16_bits(g.integers(-4, 5, (L, ki // n, h)).astype(np.float32))
     slots = (g.standard_normal((L, 2, n, b, h)) * 1e3).astype(np.float32)
     h0 = (g.standard_normal((b, h)) * 1e7).astype(np.float32)
-    say("packed decode exact")
-    plan = tp.Plan(h, ki, n, b, k_attn=ka)
+    say("packed decode exact kind=%d n=%d b=%d h=%d rank=%d wgs=%d" % (kind, n, b, h, rank, wgs))
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind, "stream_wgs": wgs})
+    assert plan.info()["packed_kind"] == kind
     s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
     s_or, h_or = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
     assert_bits_equal(s_gpu, s_or, "slots")
@@ -839,6 +870,8 @@ def test_packed_full_size_sampled_and_deterministic(w, layers, rank):
     P = host(slots).copy()
     h_or = host(h0).copy()
     s_got = outs[0][0]
+    # the fused ring stage on the GPU's own partials: bit for bit, every column
+    assert_bits_equal(outs[0][1], ring_chain(s_got, host(h0)), "hidden vs the oracle's ring chain")
     xa_h, xf_h = bf16_bits_host(xa), bf16_bits_host(xf)
     for l in range(w.layers):
         for pt, (xh, Wt) in enumerate(((xa_h, wo), (xf_h, wd))):
@@ -850,3 +883,97 @@ def test_packed_full_size_sampled_and_deterministic(w, layers, rank):
     rms_p = np.sqrt(np.mean(s_got[:, :, rank][..., cols].astype(np.float64) ** 2))
     err = np.abs(outs[0][1][:, cols].astype(np.float64) - h_or[:, cols]).max()
     assert err <= 2 * w.layers * 1e-5 * rms_p + 8 * np.spacing(np.abs(h_or).max()), err
+
+
+def _host_threads():
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def test_page1_every_rank_full_columns():
+    """The headline shape (hidden 5120, FFN 17408, 64 layers, N = 4, b = 1)
+    in the launch configuration bench.py times, run once per rank: at
+    layers 0, 32 and 63 every column of both points' partials against the
+    oracle, and the sum of the four ranks' partials against the unsharded
+    product; each rank's whole hidden-state chain bit for bit against the
+    oracle's ring chain on that rank's partials."""
+    w = workloads.PAGE1
+    check = (0, w.layers // 2, w.layers - 1)
+    nt = _host_threads()
+    plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn)
+    assert plan.info()["packed_kind"] == 1
+    ws = plan.new_workspace()
+    parts, xs, Ws = {}, {}, {}
+    for rank in range(w.n_ranks):
+        say("page-1 N=4 b=1, rank %d of 4: 64 layers, all columns at layers %s" % (rank, check))
+        xa, wo, xf, wd, slots, h0 = device_stack(w, rank)
+        po, pd = pack_dev(plan, 0, wo), pack_dev(plan, 1, wd)
+        pa, pf = pack_acts_dev(plan, xa, xf)
+        S = slots.clone()
+        Hd = h0.clone()
+        tp.tp_decode_layers_packed(plan, w.layers, rank, pa, po, pf, pd, S, Hd, ws)
+        torch.cuda.synchronize()
+        assert tp.tp_workspace_status(plan, ws) == 0
+        s_got = host(S)
+        others = [r for r in range(w.n_ranks) if r != rank]
+        assert_bits_equal(s_got[:, :, others], host(slots)[:, :, others], "other ranks' slots")
+        assert_bits_equal(host(Hd), ring_chain(s_got, host(h0)), "rank %d: hidden vs ring chain" % rank)
+        for l in check:
+            for pt, (x, W) in enumerate(((xa, wo), (xf, wd))):
+                xb, Wb = bf16_bits_host(x[l]), bf16_bits_host(W[l])
+                ref64, _ = oracle.partial(xb, Wb, nthreads=nt)
+                assert_partial_close(s_got[l, pt, rank], ref64, "rank %d l=%d pt=%d" % (rank, l, pt))
+                parts.setdefault((l, pt), []).append(s_got[l, pt, rank].astype(np.float64))
+                xs.setdefault((l, pt), []).append(xb)
+                Ws.setdefault((l, pt), []).append(Wb)
+        del xa, wo, xf, wd, slots, h0, po, pd, pa, pf, S, Hd
+        torch.cuda.empty_cache()
+    for (l, pt), ps in sorted(parts.items()):
+        y64, _ = oracle.partial(np.concatenate(xs[(l, pt)], axis=1), np.concatenate(Ws[(l, pt)], axis=0),
+                                nthreads=nt)
+        r = assert_partial_close(sum(ps), y64, "sum of the ranks' partials l=%d pt=%d" % (l, pt))
+        say("l=%d pt=%d: sum of 4 ranks vs unsharded product, max|d| = %.2e rms" % (l, pt, r))
+
+
+@pytest.mark.parametrize("kind,n,b,h,ka,ki,L", [(1, 4, 1, 1024, 1024, 8192, 400),
+                                                (2, 2, 16, 1024, 2048, 8192, 200)])
+def test_xcd_walk_persistent_step_same_bits(kind, n, b, h, ka, ki, L):
+    """The XCD-contiguous tile walk ("xcd_walk") of tp_decode_layers' persistent
+    step, vector-ALU (kind 1) and matrix-core (kind 2) tiles: about 4800
+    tiles, several times the resident grid (a multiple of 8 workgroups on a
+    256-CU device), so every workgroup walks several rounds; the FFN point
+    has two splits per column tile, so the split sets, the residual chain's
+    waits and, in the serial order, the grid-wide waits all run under both
+    walks. Both walks and both point orders give the same bits, and the
+    first and last layers' partials match the oracle."""
+    rank = n - 1
+    say("xcd_walk persistent step kind=%d n=%d b=%d h=%d L=%d" % (kind, n, b, h, L))
+    kw = dict(seed=71, workload="xcdwalk", rank=rank)
+    xa = synth.device_normal((L, b, ka // n), 1.0, torch.bfloat16, tensor="x_attn", **kw)
+    wo = synth.device_normal((L, ka // n, h), synth.WEIGHT_STD, torch.bfloat16, tensor="w_o", **kw)
+    xf = synth.device_normal((L, b, ki // n), 1.0, torch.bfloat16, tensor="x_ffn", **kw)
+    wd = synth.device_normal((L, ki // n, h), synth.WEIGHT_STD, torch.bfloat16, tensor="w_down", **kw)
+    slots = synth.device_normal((L, 2, n, b, h), 0.3, torch.float32, tensor="slots", seed=71,
+                                workload="xcdwalk")
+    h0 = synth.device_normal((b, h), 1.0, torch.float32, tensor="residual", seed=71, workload="xcdwalk")
+    outs = {}
+    for walk in (0, 1):
+        for serial in (0, 1):
+            plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"step_kind": kind, "xcd_walk": walk,
+                                                          "serial_points": serial})
+            ws = plan.new_workspace()
+            S = slots.clone()
+            Hd = h0.clone()
+            tp.tp_decode_layers(plan, L, rank, xa, wo, xf, wd, S, Hd, ws)
+            torch.cuda.synchronize()
+            assert tp.tp_workspace_status(plan, ws) == 0
+            outs[(walk, serial)] = (host(S), host(Hd))
+    ref = outs[(0, 0)]
+    for key, (s_, h_) in outs.items():
+        assert_bits_equal(s_, ref[0], "slots walk=%d serial=%d" % key)
+        assert_bits_equal(h_, ref[1], "hidden walk=%d serial=%d" % key)
+    assert_bits_equal(ref[1], ring_chain(ref[0], host(h0)), "hidden vs the oracle's ring chain")
+    for l in (0, L - 1):
+        for pt, (x, W) in enumerate(((xa, wo), (xf, wd))):
+            ref64, _ = oracle.partial(bf16_bits_host(x[l]), bf16_bits_host(W[l]))
+            assert_partial_close(ref[0][l, pt, rank], ref64, "l=%d pt=%d" % (l, pt))
