@@ -91,10 +91,64 @@ def cpu_baseline(w, rank, xa, wo, xf, wd, slots, h0, budget_s):
         reps += 1
     per_layer = total / (reps * nl)
     tok_s = w.batch / (per_layer * w.layers)
-    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d run(s) of the first %d of %d layers of the same stack (rank %d, both "
-                      "points, ring reductions), %.1f s in all, scaled linearly to %d layers"
-                      % (reps, nl, w.layers, rank, total, w.layers)}
+    out = {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%d run(s) of the first %d of %d layers of the same stack (rank %d, both "
+                     "points, ring reductions), %.1f s in all, scaled linearly to %d layers"
+                     % (reps, nl, w.layers, rank, total, w.layers)}
+    # the same oracle on one thread: a bounded sample of layers, scaled
+    t0 = time.perf_counter()
+    oracle.decode_layers(rank, bits(xa[:1]), bits(wo[:1]), bits(xf[:1]), bits(wd[:1]),
+                         slots[:1].cpu().numpy(), h0.cpu().numpy(), nthreads=1)
+    t_one = time.perf_counter() - t0
+    n1 = int(max(1, min(w.layers, math.floor(budget_s / 2 / max(t_one, 1e-6)))))
+    t0 = time.perf_counter()
+    oracle.decode_layers(rank, bits(xa[:n1]), bits(wo[:n1]), bits(xf[:n1]), bits(wd[:n1]),
+                         slots[:n1].cpu().numpy(), h0.cpu().numpy(), nthreads=1)
+    t_n1 = time.perf_counter() - t0
+    out["single_thread"] = {
+        "value": w.batch / (t_n1 / n1 * w.layers), "unit": "tokens/s", "cores": 1,
+        "sample": "the first %d of %d layers on one thread, %.1f s, scaled linearly" % (n1, w.layers, t_n1)}
+    return out
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def tiny_single_thread(budget_s=2.0):
+    """The oracle on one thread over the tiny config (hidden 512, FFN 1376,
+    N = 2, b = 1, one layer: both points and their ring sums), repeated for
+    about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+    from row_gemv_reduction_amd import synth, workloads
+    w = workloads.TINY
+    kw = dict(seed=0, workload=w.name, rank=0)
+    xa = synth.normal_bf16((1, w.batch, w.ka_r), 1.0, tensor="x_attn", **kw)
+    wo = synth.normal_bf16((1, w.ka_r, w.hidden), synth.WEIGHT_STD, tensor="w_o", **kw)
+    xf = synth.normal_bf16((1, w.batch, w.ki_r), 1.0, tensor="x_ffn", **kw)
+    wd = synth.normal_bf16((1, w.ki_r, w.hidden), synth.WEIGHT_STD, tensor="w_down", **kw)
+    slots = synth.normal_f32((1, 2, w.n_ranks, w.batch, w.hidden), synth.WEIGHT_STD * np.sqrt(w.ki_r),
+                             tensor="slots", seed=0, workload=w.name)
+    h0 = synth.normal_f32((w.batch, w.hidden), 1.0, tensor="residual", seed=0, workload=w.name)
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        oracle.decode_layers(0, xa, wo, xf, wd, slots, h0, nthreads=1)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"workload": w.name, "value": w.batch * reps / t, "unit": "tokens/s", "cores": 1,
+            "sample": "%d whole steps, %.1f s" % (reps, t)}
 
 
 def measured_traffic(w, layout):
@@ -135,13 +189,17 @@ def qkv_cols(k_attn, n_ranks):
     return k_attn // n_ranks + 2 * kv
 
 
-def time_steps(step, steps, warmup, stream):
+def time_steps(step, steps, warmup, stream, check=None):
     """W untimed steps, then K timed steps between two HIP events recorded
-    on the stream the library launches on. Returns ms per step."""
+    on the stream the library launches on. Returns ms per step. `check`
+    (if given) runs after the warm-up and after the timed steps, and must
+    raise if the steps were not valid (a timed-out wait)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if check:
+        check()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -154,7 +212,22 @@ def time_steps(step, steps, warmup, stream):
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / steps
     log("timed %d steps: %.4f ms/step (events), wall %.4f ms/step" % (steps, ms, wall * 1e3 / steps))
+    if check:
+        check()
     return ms
+
+
+def ws_check(plan, ws, what):
+    """A check for time_steps: the workspace's error word must be clear (a
+    bounded wait that timed out would leave the timed steps invalid)."""
+    import row_gemv_reduction_amd as tp
+
+    def check():
+        flags = tp.tp_workspace_status(plan, ws)
+        if flags != 0:
+            raise SystemExit("%s: the workspace reports a timed-out wait (flags %d): timing invalid"
+                             % (what, flags))
+    return check
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -173,6 +246,7 @@ def dense_run(args, w, tune):
     import torch
 
     import row_gemv_reduction_amd as tp
+    from row_gemv_reduction_amd import workloads
     plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn, tune=tune)
     info = plan.info()
     log("workload %s: K_r = %s, splits %s, path %s" % (w.name, info["k_rank"], info["splits"],
@@ -224,31 +298,35 @@ def dense_run(args, w, tune):
 
         def step():
             tp.tp_rowparallel_partials_packed(plan, w.layers, xa, po, xf, pd, pstack, ws)
-        ms = time_steps(step, args.steps, args.warmup, stream)
-        nbytes = w.layers * ((w.ka_r + w.ki_r) * w.hidden * 2 + w.batch * (w.ka_r + w.ki_r) * 2
-                             + 2 * w.batch * w.hidden * 4)
+        ms = time_steps(step, args.steps, args.warmup, stream, ws_check(plan, ws, "packed partials"))
+        nbytes = w.projection_bytes_per_step()
         config = {"workload": w.name, "op": "partials", "hidden": w.hidden, "inter": w.inter,
                   "k_attn": w.k_attn, "layers": w.layers, "n_ranks": w.n_ranks, "rank": args.rank,
                   "batch": w.batch, "launches_per_pass": 1, "us_per_launch": round(ms * 1e3, 3),
                   "timing": "eager, one launch", "weight_layout": "packed"}
         kernel = "tp_rowparallel_partials_packed: decode_stream, partials only, one launch per pass"
-        return ms, w.batch, nbytes, kernel, config, None, {"traffic": None}
+        plan.close()
+        return ms, w.batch, nbytes, kernel, config, None, {"traffic": None,
+                                                           "weight_bytes": w.weight_bytes_per_step()}
     if args.op != "step":
         if layout != "rowmajor" and args.op not in ("swiglu", "qkv"):
             raise SystemExit("--op %s runs on row-major weights (--layout rowmajor)" % args.op)
         return single_op_run(args, w, plan, info, tune, (xa, wo, xf, wd, slots, hidden), ws, stream)
     log("weight layout: %s" % layout)
-    ms = time_steps(step, args.steps, args.warmup, stream)
+    ms = time_steps(step, args.steps, args.warmup, stream, ws_check(plan, ws, "decode step"))
     serial_knob = (info["packed_kind"] == 1) if layout == "packed" else (w.batch < 16)
     if not args.no_serial and serial_knob:
         # the same step with the grid-wide wait per point (serial point order)
         plan.tune("serial_points", 1)
-        ms_serial = time_steps(step, args.steps, args.warmup, stream)
+        ms_serial = time_steps(step, args.steps, args.warmup, stream,
+                               ws_check(plan, ws, "serial point order"))
         plan.tune("serial_points", 0)
-        b_serial = w.algorithmic_bytes_per_step() / (ms_serial * 1e-3) / 1e9
+        b_serial = w.projection_bytes_per_step() / (ms_serial * 1e-3) / 1e9
+        b_serial_all = w.algorithmic_bytes_per_step() / (ms_serial * 1e-3) / 1e9
         extra["serial_point_order"] = {
             "ms_per_step": round(ms_serial, 5), "tokens_per_s": round(w.batch / (ms_serial * 1e-3), 3),
             "achieved_gbs": round(b_serial, 2), "frac": round(b_serial / HBM_PEAK_GBS, 4),
+            "frac_incl_reduce_io": round(b_serial_all / HBM_PEAK_GBS, 4),
             "note": "point j+1 reads its activation only after every column of point j is complete"}
     cpu = None
     if not args.no_cpu_baseline:
@@ -258,7 +336,12 @@ def dense_run(args, w, tune):
               "reductions_per_token": 2 * w.layers, "weight_layout": layout,
               "weight_bytes_per_step": w.weight_bytes_per_step()}
     extra["traffic"] = measured_traffic(w, layout)
-    return ms, w.batch, w.algorithmic_bytes_per_step(), kernel, config, cpu, extra
+    extra["reduce_io_bytes"] = w.reduce_io_bytes_per_step()
+    extra["weight_bytes"] = w.weight_bytes_per_step()
+    if cpu is not None and w.name == workloads.PAGE1.name:
+        cpu["tiny_single_thread"] = tiny_single_thread()
+    plan.close()
+    return ms, w.batch, w.projection_bytes_per_step(), kernel, config, cpu, extra
 
 
 def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
@@ -348,7 +431,7 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
     # Issued one call at a time, the pass measures the host's launch rate
     # (about 10 us per call through the binding); captured once into a HIP
     # graph and replayed, it measures the kernels.
-    ms_eager = time_steps(step, args.steps, args.warmup, stream)
+    ms_eager = time_steps(step, args.steps, args.warmup, stream, ws_check(plan, ws, "op " + args.op))
     launches = 1 if not graph_ok else 2 * L
     config = {"workload": w.name, "op": args.op, "hidden": H, "inter": w.inter, "k_attn": w.k_attn,
               "layers": L, "n_ranks": N, "rank": args.rank, "batch": b,
@@ -360,7 +443,8 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        ms = time_steps(graph.replay, args.steps, args.warmup, stream)
+        ms = time_steps(graph.replay, args.steps, args.warmup, stream,
+                        ws_check(plan, ws, "op %s (graph)" % args.op))
         config.update({"us_per_launch": round(ms * 1e3 / launches, 3),
                        "timing": "HIP graph of the pass, replayed",
                        "us_per_launch_eager": round(ms_eager * 1e3 / launches, 3)})
@@ -368,8 +452,35 @@ def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
         ms = ms_eager
         config.update({"us_per_launch": round(ms * 1e3 / launches, 3),
                        "timing": "eager, launches issued from the library"})
-    assert tp.tp_workspace_status(plan, ws) == 0
+    plan.close()
     return ms, b, nbytes, kernel, config, None, {"traffic": None}
+
+
+def stream_read_run(args, w):
+    """The device's streaming-read ceiling: the library's read probe over as
+    many bytes as one decode step of workload w streams (its weight slices),
+    at a few grid sizes; the fastest is reported."""
+    import torch
+
+    import row_gemv_reduction_amd as tp
+    nbytes = w.weight_bytes_per_step()
+    nbytes -= nbytes % 16
+    buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    buf.fill_(1.0)
+    best = None
+    for wgs in (256, 512, 768, 1024, 2048):
+        sink = torch.zeros(wgs, dtype=torch.uint32, device="cuda")
+        ms = time_steps(lambda: tp.tp_stream_read_probe(buf, sink), args.steps, args.warmup,
+                        torch.cuda.current_stream())
+        log("stream read: %d workgroups, %.4f ms, %.1f GB/s" % (wgs, ms, nbytes / ms / 1e6))
+        if best is None or ms < best[0]:
+            best = (ms, wgs)
+    ms, wgs = best
+    config = {"workload": w.name, "op": "stream_read", "bytes": nbytes, "workgroups": wgs,
+              "timing": "eager, one launch per pass"}
+    kernel = ("tp_stream_read_probe (stream_read_kernel: grid-stride 16-byte nontemporal loads, %d "
+              "workgroups of 512 threads)" % wgs)
+    return ms, 0, nbytes, kernel, config, None, {"traffic": None}
 
 
 def moe_build(w, rank, copies, seed=0):
@@ -426,7 +537,8 @@ def moe_run(args, w, tune):
         tp.tp_moe_route(plan, L["logits"], se, sw)
         tp.tp_moe_decode(plan, rank, se, sw, L["u"], L["wp"], slots[c, 1], hidden, ws)
 
-    ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream())
+    ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream(),
+                    ws_check(plan, ws, "MoE share"))
     # algorithmic bytes of one layer share (averaged over the rotated copies)
     el = E // ep
     step_bytes = 0
@@ -454,8 +566,10 @@ def moe_run(args, w, tune):
               "weight_copies_rotated": copies}
     kernel = ("MoE layer share (attention slice: MFMA projection with the ring sum in its split-K "
               "fix-up; routing; expert MFMA GEMV; combine + ring sum)")
-    extra = {}
-    return ms, T, step_bytes, kernel, config, cpu, extra
+    reduce_io = 2 * (w.n_ranks + 2) * T * H * 4
+    extra = {"reduce_io_bytes": reduce_io}
+    plan.close()
+    return ms, T, step_bytes - reduce_io, kernel, config, cpu, extra
 
 
 def moe_cpu_baseline(w, rank, L, slots, h0, plan, budget_s):
@@ -541,12 +655,14 @@ def main():
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
-    ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu", "qkv"], default="step",
+    ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu", "qkv", "stream_read"],
+                    default="step",
                     help="what a timed pass runs: the whole decode step (default); the stack's "
                          "2L partial projections in one call (tp_rowparallel_partials); one "
                          "entry point per reconciliation point (tp_rowparallel_partial, "
-                         "tp_ring_reduce); or the stack's column-parallel up projections with "
-                         "SwiGLU (tp_gate_up_swiglu)")
+                         "tp_ring_reduce); the stack's column-parallel up projections with "
+                         "SwiGLU (tp_gate_up_swiglu) or QKV projections (tp_qkv_proj); or the "
+                         "device's streaming-read ceiling over the step's weight bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -566,10 +682,13 @@ def main():
     for kv in args.tune:
         k, v = kv.split("=")
         tune[k] = int(v)
-    if w.n_experts and args.op != "step":
+    if w.n_experts and args.op not in ("step", "stream_read"):
         raise SystemExit("--op applies to the dense workloads")
-    run = moe_run if w.n_experts else dense_run
-    ms, tokens, step_bytes, kernel, config, cpu, extra = run(args, w, tune)
+    if args.op == "stream_read":
+        ms, tokens, step_bytes, kernel, config, cpu, extra = stream_read_run(args, w)
+    else:
+        run = moe_run if w.n_experts else dense_run
+        ms, tokens, step_bytes, kernel, config, cpu, extra = run(args, w, tune)
     if args.copy_calibration:
         copy_calibration()
 
@@ -580,6 +699,15 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": extra.pop("traffic", None),
         "kernel": kernel, "algorithmic_bytes_per_launch": step_bytes,
     }
+    # the emulated ring reductions' I/O, reported beside the projection bytes
+    reduce_io = extra.pop("reduce_io_bytes", 0)
+    if reduce_io:
+        roofline["reduce_io_bytes_per_launch"] = reduce_io
+        roofline["frac_incl_reduce_io"] = round((step_bytes + reduce_io) / (ms * 1e-3) / 1e9
+                                                / HBM_PEAK_GBS, 4)
+    wbytes = extra.pop("weight_bytes", 0)
+    if wbytes:
+        roofline["weights_only_frac"] = round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     out = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

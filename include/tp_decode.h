@@ -65,7 +65,10 @@ typedef enum {
 
 typedef struct tp_plan_s* tp_plan_t;
 
-typedef struct {
+/* What a plan resolved to (tp_plan_info). The struct is named by its tag,
+ * `struct tp_plan_info`, or by the typedef tp_plan_info_t: in C a typedef
+ * and a function share one namespace, and the function carries the name. */
+typedef struct tp_plan_info {
     int64_t hidden;          /* H */
     int64_t inter;           /* FFN intermediate size I */
     int64_t k_attn;          /* K of the mixer output projection (default H) */
@@ -86,7 +89,7 @@ typedef struct {
                                 0 = the plan is not supported, 1 = pair strips (vector ALU),
                                 2 = MFMA tiles (matrix cores) */
     int32_t stream_wgs;      /* packed_kind 2: workgroups of the matrix-core step (0 otherwise) */
-} tp_plan_info;
+} tp_plan_info_t;
 
 /*
  * Create a plan for hidden size H, FFN intermediate size I, N ranks and a
@@ -106,13 +109,6 @@ tp_status tp_plan(int64_t hidden, int64_t inter, int32_t n_ranks, int32_t batch,
  * or N does not divide it. */
 tp_status tp_plan_set_attn_dim(tp_plan_t plan, int64_t k_attn);
 
-/* Enable the expert-parallel MoE share: n_experts experts of intermediate
- * size moe_inter, top_k per token, spread over ep ranks (rank r owns the
- * contiguous experts [r*E/ep, (r+1)*E/ep)), for up to max_tokens tokens
- * ("Hosting Qwen on Blackwell", sections Prefillers, MoE Dispatch-Combine
- * and Expert Parallel). Must be called before first use.
- * TP_ERR_INVALID_ARG on sizes < 1, top_k > n_experts or ep not dividing
- * n_experts; TP_ERR_UNSUPPORTED if top_k > 32 or max_tokens > 4096. */
 /*
  * Give the plan the width of the rank's mixer input projection: `cols` =
  * the Q, K and V columns this rank holds (its heads' columns, with K and V
@@ -123,6 +119,13 @@ tp_status tp_plan_set_attn_dim(tp_plan_t plan, int64_t k_attn);
  */
 tp_status tp_plan_set_qkv_dim(tp_plan_t plan, int64_t cols);
 
+/* Enable the expert-parallel MoE share: n_experts experts of intermediate
+ * size moe_inter, top_k per token, spread over ep ranks (rank r owns the
+ * contiguous experts [r*E/ep, (r+1)*E/ep)), for up to max_tokens tokens
+ * ("Hosting Qwen on Blackwell", sections Prefillers, MoE Dispatch-Combine
+ * and Expert Parallel). Must be called before first use.
+ * TP_ERR_INVALID_ARG on sizes < 1, top_k > n_experts or ep not dividing
+ * n_experts; TP_ERR_UNSUPPORTED if top_k > 32 or max_tokens > 4096. */
 tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int32_t ep,
                           int64_t moe_inter, int32_t max_tokens);
 
@@ -168,7 +171,17 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * TP_ERR_INVALID_ARG for an unknown key or an out-of-range value. */
 tp_status tp_plan_tune(tp_plan_t plan, const char* key, int64_t value);
 
-tp_status tp_plan_info_get(tp_plan_t plan, tp_plan_info* out);
+/*
+ * The plan's resolved sizes: K_r per point, the ring chunk length C = b*H/N,
+ * the wire bytes per rank per reduction, 2(N-1)*C*e for the pages' bf16
+ * payload (e = 2) and for the fp32 payload emulated here (e = 4) (lesson
+ * 9.9, Conceito: 2(N-1)/N of the payload on each rank's wire), the
+ * workspace bytes the entry points need, and the kernel family of each
+ * point. Host-only. TP_ERR_INVALID_ARG for a null argument.
+ */
+tp_status tp_plan_info(tp_plan_t plan, struct tp_plan_info* out);
+/* The same as tp_plan_info (the name this library first exported). */
+tp_status tp_plan_info_get(tp_plan_t plan, struct tp_plan_info* out);
 void tp_plan_destroy(tp_plan_t plan);
 const char* tp_status_str(tp_status status);
 
@@ -350,7 +363,7 @@ tp_status tp_decode_point(tp_plan_t plan, int32_t point, int32_t rank, const voi
  * Packed weights for the streamed decode step. A rank's weight slice
  * W_r[K_r][H] (row-major, as tp_rowparallel_partial takes it) is stored
  * once, when the weights are loaded (not part of the decode step), in the
- * layout of the plan's packed_kind (tp_plan_info):
+ * layout of the plan's packed_kind (see tp_plan_info):
  *  1, pair strips (vector-ALU stream):
  *     P[s][kp][c][q] = W_r[2kp + q][4s + c]
  *     s < H/4, kp < ceil(K_r/2), c < 4, q < 2   (rows past K_r are zero)
@@ -512,6 +525,20 @@ tp_status tp_moe_partial(tp_plan_t plan, int32_t rank, const int32_t* sel_expert
 tp_status tp_moe_decode(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                         const float* sel_weight, const void* u, const void* w_packed,
                         float* slots, float* hidden, void* workspace, void* stream);
+
+/*
+ * Measurement: the device's streaming-read ceiling. Reads `bytes` of `buf`
+ * with 16-byte nontemporal loads (the access the decode kernels make of
+ * their weights: "Hosting Qwen on Blackwell", Decoders, a decode matmul
+ * costs what loading its weights costs), `workgroups` workgroups of 512
+ * threads in a grid-stride walk (16 loads in flight per thread), and stores one XOR fold of the data per
+ * workgroup into sink[0 .. workgroups) so that no load is dropped. No
+ * arithmetic of the method. bytes a multiple of 16, buf and sink 16-byte
+ * aligned (TP_ERR_ALIGNMENT); TP_ERR_INVALID_ARG for a null pointer,
+ * bytes < 0 or workgroups outside 1 .. 65536.
+ */
+tp_status tp_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                               void* stream);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,7 @@ EXPORTS = {
     "tp_plan_set_moe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "tp_plan_tune": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int64]),
+    "tp_plan_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(tp_plan_info)]),
     "tp_plan_info_get": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(tp_plan_info)]),
     "tp_plan_destroy": (None, [ctypes.c_void_p]),
     "tp_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -89,6 +90,8 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]),
     "tp_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 8),
+    "tp_stream_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_int32, ctypes.c_void_p]),
 }
 
 
@@ -177,7 +180,7 @@ class Plan:
         # changes with tune(), so it is fetched once per state.
         if self._info is None:
             i = tp_plan_info()
-            _check(_lib().tp_plan_info_get(self.handle, ctypes.byref(i)), "tp_plan_info_get")
+            _check(_lib().tp_plan_info(self.handle, ctypes.byref(i)), "tp_plan_info")
             d = {}
             for name, _ in tp_plan_info._fields_:
                 v = getattr(i, name)
@@ -469,3 +472,15 @@ def tp_moe_decode(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, slots, 
     if workspace.numel() < i["workspace_bytes"]:
         raise ValueError("workspace too small")
     _check(_lib().tp_moe_decode(plan.handle, rank, *args, _stream()), "tp_moe_decode")
+
+
+def tp_stream_read_probe(buf, sink):
+    """Read all of `buf` (any dtype, contiguous, on the GPU) with the library's
+    streaming-read probe; `sink` is a uint32 tensor with one word per
+    workgroup (its length is the workgroup count)."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib().tp_stream_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                       _dev(sink, "sink", torch.uint32), sink.numel(), _stream()),
+           "tp_stream_read_probe")

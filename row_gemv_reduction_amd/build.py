@@ -32,17 +32,24 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel, `jobs` at a time; 0 = the host's
+    cores, at most 8) and link them; every call compiles everything."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     plan_o = os.path.join(BUILD, "tp_plan.o")
-    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "tp_plan.cpp"), "-o", plan_o], verbose)
+    cmds.append(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "tp_plan.cpp"), "-o", plan_o])
     objs.append(plan_o)
     for src in sorted(os.listdir(CSRC)):
         if src.endswith(".hip"):
             o = os.path.join(BUILD, src[:-4] + ".o")
-            _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", o], verbose)
+            cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", o])
             objs.append(o)
+    n = jobs or max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

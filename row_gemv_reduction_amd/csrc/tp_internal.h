@@ -175,6 +175,15 @@ tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t ra
                                 const void* x_attn, const void* w_o_tiles, const void* x_ffn,
                                 const void* w_down_tiles, float* slots, float* hidden, void* ws,
                                 void* stream);
+// The same with the exchange buffers (tp_xchg_bytes(p) bytes) at `xpart`
+// instead of at the workspace's exchange offset; `ws` still holds the
+// fixed region (exchange words, exit counter, error word).
+tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t rank,
+                                   const void* x_attn, const void* w_o_tiles, const void* x_ffn,
+                                   const void* w_down_tiles, float* slots, float* hidden, void* ws,
+                                   float* xpart, void* stream);
+// Fill n words at p with v (a kernel: capturable into a HIP graph).
+tp_status tp_fill_u32(uint32_t* p, int64_t n, uint32_t v, void* stream);
 // Packed layout (and streamed kernel) the plan uses: 0 none, 1 pair strips, 2 MFMA tiles.
 int tp_packed_kind(const tp_plan_s* p);
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections

@@ -1251,6 +1251,13 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
 
 }  // namespace
 
+tp_status tp_fill_u32(uint32_t* p, int64_t n, uint32_t v, void* stream) {
+    if (n <= 0) return TP_OK;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, p, n, v);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
 extern "C" {
 
 tp_status tp_workspace_init(tp_plan_t p, void* ws, void* stream) {

@@ -733,10 +733,20 @@ tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t ra
                                 const void* x_attn, const void* w_o_tiles, const void* x_ffn,
                                 const void* w_down_tiles, float* slots, float* hidden, void* ws,
                                 void* stream) {
+    return tp_decode_mfma_stream_at(p, n_layers, rank, x_attn, w_o_tiles, x_ffn, w_down_tiles, slots,
+                                    hidden, ws,
+                                    reinterpret_cast<float*>(static_cast<char*>(ws) + tp_ws_xchg_offset(p)),
+                                    stream);
+}
+
+tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t rank,
+                                   const void* x_attn, const void* w_o_tiles, const void* x_ffn,
+                                   const void* w_down_tiles, float* slots, float* hidden, void* ws,
+                                   float* xpart, void* stream) {
     MfmaGeom geo;
     if (!tp_mfma_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
     if (!aligned16(x_attn) || !aligned16(x_ffn) || !aligned16(w_o_tiles) || !aligned16(w_down_tiles) ||
-        !aligned16(slots) || !aligned16(hidden) || !aligned16(ws))
+        !aligned16(slots) || !aligned16(hidden) || !aligned16(ws) || !aligned16(xpart))
         return TP_ERR_ALIGNMENT;
     if (n_layers == 0) return TP_OK;
     mfma_stream_fn k = mfma_stream_kernel(geo.bt);
@@ -749,7 +759,7 @@ tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t ra
     a.slots = slots;
     a.hidden = hidden;
     char* base = static_cast<char*>(ws);
-    a.xpart = reinterpret_cast<float*>(base + tp_ws_xchg_offset(p));
+    a.xpart = xpart;
     a.pub = reinterpret_cast<uint32_t*>(base + kXchgFlagOffset);
     a.ack = a.pub + 2 * kXchgMaxStrips;
     a.exit_ctr = reinterpret_cast<uint32_t*>(base + kXchgExitOffset);

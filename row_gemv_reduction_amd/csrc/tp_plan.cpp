@@ -359,7 +359,7 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     return TP_OK;
 }
 
-tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
+tp_status tp_plan_info(tp_plan_t p, struct tp_plan_info* o) {
     if (!p || !o) return TP_ERR_INVALID_ARG;
     memset(o, 0, sizeof *o);
     o->hidden = p->hidden;
@@ -388,6 +388,8 @@ tp_status tp_plan_info_get(tp_plan_t p, tp_plan_info* o) {
     o->stream_wgs = o->packed_kind == 2 && tp_mfma_geometry(p, &mg) ? mg.grid : 0;
     return TP_OK;
 }
+
+tp_status tp_plan_info_get(tp_plan_t p, struct tp_plan_info* o) { return tp_plan_info(p, o); }
 
 void tp_plan_destroy(tp_plan_t p) { delete p; }
 

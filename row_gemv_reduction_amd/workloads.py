@@ -39,17 +39,24 @@ class Workload:
         """bf16 weight bytes one rank streams per decode step (2L points)."""
         return self.layers * (self.ka_r + self.ki_r) * self.hidden * 2
 
-    def algorithmic_bytes_per_step(self) -> int:
-        """Bytes the path must move per step: per point the rank's weight
-        slice, its activation slice and its fp32 partial; plus, per point,
-        the emulated ring reduction reading N partials and the residual and
-        writing the result."""
+    def projection_bytes_per_step(self) -> int:
+        """Bytes the rank's 2L partial projections must move per step: per
+        point its weight slice (bf16), its activation slice (bf16) and its
+        fp32 partial written."""
         b, h = self.batch, self.hidden
-        per_point = 0
+        per_layer = 0
         for kr in (self.ka_r, self.ki_r):
-            per_point += kr * h * 2 + b * kr * 2 + b * h * 4
-        reduce_io = 2 * (self.n_ranks + 2) * b * h * 4
-        return self.layers * (per_point + reduce_io)
+            per_layer += kr * h * 2 + b * kr * 2 + b * h * 4
+        return self.layers * per_layer
+
+    def reduce_io_bytes_per_step(self) -> int:
+        """Bytes of the emulated ring reductions per step: per point the N
+        partials and the residual read and the sum written, fp32."""
+        return self.layers * 2 * (self.n_ranks + 2) * self.batch * self.hidden * 4
+
+    def algorithmic_bytes_per_step(self) -> int:
+        """Both of the above: every byte the fused step moves at least."""
+        return self.projection_bytes_per_step() + self.reduce_io_bytes_per_step()
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
