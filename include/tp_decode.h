@@ -196,6 +196,8 @@ tp_status tp_workspace_init(tp_plan_t plan, void* workspace, void* stream);
 
 /*
  * Read the workspace's error word (synchronous: waits for the device).
+ * workspace = NULL reads the error word of tp_decode_layers_packed_noalloc's
+ * scratch on the current device instead (0 if it was never used there).
  * *flags = 0 after successful calls. Bit 0 is set if a bounded wait between
  * workgroups timed out: a decode step's wait for the previous
  * reconciliation point, a matrix-core stream's wait for a cut strip's other
@@ -438,6 +440,33 @@ tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank
                                   const void* x_attn, const void* w_o_packed,
                                   const void* x_ffn, const void* w_down_packed,
                                   float* slots, float* hidden, void* workspace, void* stream);
+
+/*
+ * tp_decode_layers_packed without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, kernels and
+ * results (bit for bit) as tp_decode_layers_packed, minus `workspace`.
+ * Instead of a workspace the kernels use a scratch array the library keeps
+ * in device memory, one per GPU, held until the process ends: 8.25 MiB
+ * (a 256 KiB region of completion, exchange and error words, and 8 MiB of
+ * exchange buffers for the matrix-core stream). The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on
+ * a GPU looks the array up and clears its words with a kernel on `stream`.
+ * Each call clears the array's error word (a kernel, in stream order) and
+ * the kernels leave every other word ready for the next call.
+ * All calls on one GPU share that GPU's array: calls that overlap in time
+ * on one GPU (on different streams or threads) race on it and must not be
+ * issued. tp_workspace_status(plan, NULL, &flags) reads the error word of
+ * the latest call on the current device.
+ * Errors as tp_decode_layers_packed, and TP_ERR_UNSUPPORTED where the plan
+ * needs more scratch than the array holds: packed_kind 2 with
+ * 2 * 4 * (hidden/16) * ceil(batch/16) KiB of exchange buffers above 8 MiB
+ * (e.g. hidden 5120 with batch > 48; hidden 4096 fits every batch).
+ */
+tp_status tp_decode_layers_packed_noalloc(tp_plan_t plan, int32_t n_layers, int32_t rank,
+                                          const void* x_attn, const void* w_o_packed,
+                                          const void* x_ffn, const void* w_down_packed,
+                                          float* slots, float* hidden, void* stream);
 
 /*
  * The partial projections of a layer stack on weights packed by

@@ -80,6 +80,8 @@ EXPORTS = {
                                 + [ctypes.c_void_p] * 8),
     "tp_rowparallel_partials_packed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
                                        + [ctypes.c_void_p] * 7),
+    "tp_decode_layers_packed_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                                        + [ctypes.c_void_p] * 7),
     "tp_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]),
@@ -217,9 +219,11 @@ def tp_workspace_init(plan: Plan, workspace):
 
 
 def tp_workspace_status(plan: Plan, workspace) -> int:
+    """The workspace's error word; workspace=None reads that of the no-alloc
+    entry point's scratch on the current device."""
     flags = ctypes.c_int32(0)
-    _check(_lib().tp_workspace_status(plan.handle, _dev(workspace, "workspace", torch.uint8),
-                                      ctypes.byref(flags)), "tp_workspace_status")
+    ws = None if workspace is None else _dev(workspace, "workspace", torch.uint8)
+    _check(_lib().tp_workspace_status(plan.handle, ws, ctypes.byref(flags)), "tp_workspace_status")
     return flags.value
 
 
@@ -397,6 +401,22 @@ def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ff
         raise ValueError("workspace too small")
     _check(_lib().tp_decode_layers_packed(plan.handle, L, rank, *args, _stream()),
            "tp_decode_layers_packed")
+
+
+def tp_decode_layers_packed_noalloc(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ffn,
+                                    w_down_packed, slots, hidden):
+    """tp_decode_layers_packed with the library's per-GPU scratch instead of a workspace."""
+    i = plan._plan_info()
+    n, b, H = i["n_ranks"], i["batch"], i["hidden"]
+    L = n_layers
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
+            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
+            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
+            _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
+            _dev(hidden, "hidden", torch.float32, (b, H)))
+    _check(_lib().tp_decode_layers_packed_noalloc(plan.handle, L, rank, *args, _stream()),
+           "tp_decode_layers_packed_noalloc")
 
 
 def tp_rowparallel_partials_packed(plan: Plan, n_layers, x_attn, w_o_packed, x_ffn, w_down_packed,

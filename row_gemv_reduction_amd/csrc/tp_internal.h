@@ -184,6 +184,9 @@ tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t
                                    float* xpart, void* stream);
 // Fill n words at p with v (a kernel: capturable into a HIP graph).
 tp_status tp_fill_u32(uint32_t* p, int64_t n, uint32_t v, void* stream);
+// The error word of the no-alloc entry point's scratch on the current
+// device (0 if that scratch was never used there).
+tp_status tp_scratch_status(int32_t* flags);
 // Packed layout (and streamed kernel) the plan uses: 0 none, 1 pair strips, 2 MFMA tiles.
 int tp_packed_kind(const tp_plan_s* p);
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections

@@ -1270,7 +1270,8 @@ tp_status tp_workspace_init(tp_plan_t p, void* ws, void* stream) {
 }
 
 tp_status tp_workspace_status(tp_plan_t p, const void* ws, int32_t* flags) {
-    if (!p || !ws || !flags) return TP_ERR_INVALID_ARG;
+    if (!p || !flags) return TP_ERR_INVALID_ARG;
+    if (!ws) return tp_scratch_status(flags);  // the no-alloc entry point's scratch
     if (!aligned16(ws)) return TP_ERR_ALIGNMENT;
     uint32_t v = 0;
     if (hipMemcpy(&v, static_cast<const char*>(ws) + kSyncOffset + 4 * kSyncErr, 4,

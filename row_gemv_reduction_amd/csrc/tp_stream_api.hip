@@ -5,11 +5,68 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tp_internal.h"
 
 namespace {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Scratch of tp_decode_layers_packed_noalloc, one copy per device, held
+// until the process ends: the workspace's fixed region (completion words of
+// the serial point order, the matrix-core stream's exchange words and exit
+// counter, the error word), then the matrix-core stream's exchange buffers.
+constexpr int64_t kScratchFixedBytes = kCounterBytes;       // 256 KiB
+constexpr int64_t kScratchXchgBytes = (int64_t)8 << 20;     // 8 MiB
+constexpr int64_t kScratchBytes = kScratchFixedBytes + kScratchXchgBytes;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+// Host code never passes `scratch` itself (its host-side name is not a
+// device address): each device's copy is looked up once, with that device
+// current, and its address kept here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices];
+
+// The current device's scratch, set up on first use: its address, and its
+// fixed region cleared by a kernel on `stream` (ahead of the caller's
+// launch on the same stream). Null on failure.
+unsigned char* device_scratch(void* stream, tp_status* st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = TP_ERR_DEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            *st = TP_ERR_DEVICE;
+            return nullptr;
+        }
+        *st = tp_fill_u32(static_cast<uint32_t*>(ptr), kScratchFixedBytes / 4, 0u, stream);
+        if (*st != TP_OK) return nullptr;
+        g_scratch[dev] = static_cast<unsigned char*>(ptr);
+    }
+    *st = TP_OK;
+    return g_scratch[dev];
+}
 }  // namespace
+
+tp_status tp_scratch_status(int32_t* flags) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TP_ERR_DEVICE;
+    unsigned char* base;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        base = g_scratch[dev];
+    }
+    uint32_t v = 0;
+    if (base && hipMemcpy(&v, base + kSyncOffset + 4 * kSyncErr, 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return TP_ERR_DEVICE;
+    *flags = (int32_t)v;
+    return TP_OK;
+}
 
 // The plan's packed layout and stream: the knob "stream_kind", else the
 // one measured faster where both fit.
@@ -84,6 +141,34 @@ tp_status tp_decode_layers_packed(tp_plan_t p, int32_t n_layers, int32_t rank, c
     }
     return tp_decode_stream(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed, slots,
                             hidden, nullptr, ws, stream);
+}
+
+tp_status tp_decode_layers_packed_noalloc(tp_plan_t p, int32_t n_layers, int32_t rank,
+                                          const void* x_attn, const void* w_o_packed,
+                                          const void* x_ffn, const void* w_down_packed,
+                                          float* slots, float* hidden, void* stream) {
+    if (!p || !x_attn || !w_o_packed || !x_ffn || !w_down_packed || !slots || !hidden)
+        return TP_ERR_INVALID_ARG;
+    if (n_layers < 0 || rank < 0 || rank >= p->n_ranks) return TP_ERR_INVALID_ARG;
+    if (!aligned16(x_attn) || !aligned16(w_o_packed) || !aligned16(x_ffn) ||
+        !aligned16(w_down_packed) || !aligned16(slots) || !aligned16(hidden))
+        return TP_ERR_ALIGNMENT;
+    const int kind = tp_packed_kind(p);
+    if (kind == 0) return TP_ERR_UNSUPPORTED;
+    if (kind == 2 && (p->serial_points || tp_xchg_bytes(p) > kScratchXchgBytes)) return TP_ERR_UNSUPPORTED;
+    tp_status st;
+    unsigned char* base = device_scratch(stream, &st);
+    if (!base) return st;
+    if (n_layers == 0) return TP_OK;
+    // the error word reports this call: clear it first (a kernel, in stream order)
+    st = tp_fill_u32(reinterpret_cast<uint32_t*>(base + kSyncOffset) + kSyncErr, 1, 0u, stream);
+    if (st != TP_OK) return st;
+    if (kind == 2)
+        return tp_decode_mfma_stream_at(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed,
+                                        slots, hidden, base,
+                                        reinterpret_cast<float*>(base + kScratchFixedBytes), stream);
+    return tp_decode_stream(p, n_layers, rank, x_attn, w_o_packed, x_ffn, w_down_packed, slots,
+                            hidden, nullptr, base, stream);
 }
 
 tp_status tp_rowparallel_partials_packed(tp_plan_t p, int32_t n_layers, const void* x_attn,
