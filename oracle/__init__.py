@@ -66,6 +66,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_gate_up_swiglu.restype = ctypes.c_int
         L.oracle_qkv_proj.argtypes = [vp, vp, i64, i64, i64, vp, vp, ctypes.c_int]
         L.oracle_qkv_proj.restype = ctypes.c_int
+        L.oracle_mx_element_value.argtypes = [i32, ctypes.c_uint32]
+        L.oracle_mx_element_value.restype = ctypes.c_double
+        L.oracle_mx_quantize.argtypes = [i32, vp, i64, i64, vp, vp]
+        L.oracle_mx_quantize.restype = ctypes.c_int
+        L.oracle_mx_partial.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, ctypes.c_int]
+        L.oracle_mx_partial.restype = ctypes.c_int
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -233,3 +239,47 @@ def bf16_to_f32(bits) -> float:
 
 def f32_to_bf16(value) -> int:
     return int(lib().oracle_f32_to_bf16(float(np.float32(value))))
+
+
+MXFP8, MXFP4 = 1, 2
+MX_BLOCK = 32
+
+
+def mx_element_value(fmt: int, code: int) -> float:
+    """Value of one MX element code (fmt 1: FP8 E4M3, fmt 2: FP4 E2M1)."""
+    return float(lib().oracle_mx_element_value(fmt, int(code)))
+
+
+def mx_codes_shape(fmt: int, k: int, h: int):
+    return (k, h) if fmt == MXFP8 else (k // 2, h)
+
+
+def mx_quantize(fmt: int, w_bits):
+    """bf16 weights [K, H] -> (codes uint8, scales uint8 [K/32, H]) in the MX
+    interchange layout (fmt 1: codes [K, H]; fmt 2: [K/2, H], two rows of a
+    column per byte, the even row in the low nibble)."""
+    w = _c(w_bits, np.uint16)
+    k, h = w.shape
+    codes = np.empty(mx_codes_shape(fmt, k, h), np.uint8)
+    scales = np.empty((k // MX_BLOCK, h), np.uint8)
+    if lib().oracle_mx_quantize(fmt, _ptr(w), k, h, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("mx_quantize: bad format or size (K must be a multiple of 32)")
+    return codes, scales
+
+
+def mx_partial(fmt: int, x_bits, codes, scales, nthreads: int = 1):
+    """p = x . W for MX weights W (codes, scales as mx_quantize gives them);
+    returns (double, float) arrays [batch, H]."""
+    x = _c(x_bits, np.uint16)
+    c = _c(codes, np.uint8)
+    sc = _c(scales, np.uint8)
+    b, k = x.shape
+    h = sc.shape[1]
+    if sc.shape[0] * MX_BLOCK != k or c.shape != mx_codes_shape(fmt, k, h):
+        raise ValueError("mx_partial: codes / scales do not match x")
+    y64 = np.empty((b, h), np.float64)
+    y32 = np.empty((b, h), np.float32)
+    if lib().oracle_mx_partial(fmt, _ptr(x), b, k, h, _ptr(c), _ptr(sc), _ptr(y64), _ptr(y32),
+                               nthreads) != 0:
+        raise ValueError("mx_partial: bad format or size")
+    return y64, y32

@@ -515,3 +515,195 @@ int oracle_qkv_proj(const uint16_t* x, const uint16_t* w, int64_t batch, int64_t
     free(y);
     return 0;
 }
+
+/* ------------------------------------------ microscaled (MX) weights -- */
+
+/*
+ * Block-scaled weights [P2, Quantization]: the pages deploy their model with
+ * its weights converted once, statically, to MXFP8, and weigh MXFP4 as well.
+ * The pages give the format names only; the reading taken here is the
+ * microscaling (MX) layout those names denote: the weights are cut into
+ * blocks of 32 consecutive elements along K (the reduction dimension, rows
+ * of W[K, H]), each block shares one 8-bit power-of-two scale
+ * E (value 2^(E-127); E = 255 means NaN), and each element is a small float:
+ *
+ *   fmt 1, MXFP8: FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa
+ *                 bits; no infinities; S.1111.111 is NaN; largest 448)
+ *   fmt 2, MXFP4: FP4 E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa
+ *                 bit; no infinities or NaN; largest 6)
+ *
+ * A weight is element * 2^(E-127), held exactly in double here.
+ */
+#define MX_BLOCK 32
+
+/* The value of one element code, from its sign, exponent and mantissa
+ * fields. */
+static double mx_elem_value(int fmt, unsigned code)
+{
+    if (fmt == 1) {
+        const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+        if (e == 15 && m == 7) return NAN;
+        /* normal: (1 + m/8) 2^(e-7); subnormal (e = 0): (m/8) 2^-6 */
+        const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+        return s ? -v : v;
+    } else {
+        const int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+        /* normal: (1 + m/2) 2^(e-1); subnormal (e = 0): m/2 */
+        const double v = e == 0 ? 0.5 * m : ldexp((double)(2 + m), e - 2);
+        return s ? -v : v;
+    }
+}
+
+double oracle_mx_element_value(int32_t fmt, uint32_t code)
+{
+    if (fmt != 1 && fmt != 2) return NAN;
+    return mx_elem_value(fmt, code & (fmt == 1 ? 0xffu : 0xfu));
+}
+
+/* Exponent of the element format's largest binade (448 = 1.75 * 2^8,
+ * 6 = 1.5 * 2^2). */
+static int mx_emax(int fmt) { return fmt == 1 ? 8 : 2; }
+
+/* Round v (already divided by the block's scale) to the nearest element
+ * value: the non-negative codes are listed in increasing value, so the
+ * candidates are the largest code not above |v| and the next one; a tie
+ * goes to the even code (an even mantissa); |v| beyond the largest finite
+ * value saturates to it. The sign of v is kept (so -0 for a negative v
+ * that rounds to zero). */
+static unsigned mx_round(int fmt, double v)
+{
+    const unsigned ncodes = fmt == 1 ? 0x7fu : 0x8u; /* finite non-negative codes */
+    const double a = fabs(v);
+    unsigned lo = 0;
+    for (unsigned c = 1; c < ncodes; ++c)
+        if (mx_elem_value(fmt, c) <= a) lo = c;
+    unsigned code = lo;
+    if (lo + 1 < ncodes) {
+        const double dl = a - mx_elem_value(fmt, lo), dh = mx_elem_value(fmt, lo + 1) - a;
+        if (dh < dl || (dh == dl && (lo & 1u))) code = lo + 1;
+    }
+    return code | (signbit(v) ? (fmt == 1 ? 0x80u : 0x8u) : 0u);
+}
+
+/*
+ * Static conversion of bf16 weights to an MX format, block by block:
+ *   amax = max |w| over the block's 32 rows (one column);
+ *   E = floor(log2(amax)) - emax + 127, clamped to [0, 254]  (so that
+ *       amax / 2^(E-127) lies in the element format's top binade,
+ *       [2^emax, 2^(emax+1)), unless clamped);
+ *   E = 0 for an all-zero block; E = 255 (NaN) if the block holds a NaN or
+ *       infinity, with every element code 0;
+ *   element = mx_round(w / 2^(E-127)).
+ * Layouts (K a multiple of 32):
+ *   w      bf16 [K][H] row-major
+ *   codes  fmt 1: uint8 [K][H], one E4M3 code per weight;
+ *          fmt 2: uint8 [K/2][H], byte [kk][n] = code(2kk, n) | code(2kk+1, n) << 4
+ *   scales uint8 [K/32][H], E of rows [32kb, 32kb+32) of column n
+ * Returns 0, or 1 for a bad format or size.
+ *
+ * Pins: element values of every code (E4M3 against an independent
+ * conversion library, E2M1 against the format's table of values); blocks
+ * built from representable values round-trip exactly; the scaled block
+ * maximum lands in the top binade; saturation and ties on hand-made
+ * blocks; the quantisation error of each element is within half an element
+ * spacing.
+ */
+int oracle_mx_quantize(int32_t fmt, const uint16_t* w, int64_t K, int64_t H, uint8_t* codes,
+                       uint8_t* scales)
+{
+    if ((fmt != 1 && fmt != 2) || K < MX_BLOCK || K % MX_BLOCK || H < 1) return 1;
+    if (fmt == 2) memset(codes, 0, (size_t)(K / 2 * H));
+    for (int64_t kb = 0; kb < K / MX_BLOCK; ++kb)
+        for (int64_t n = 0; n < H; ++n) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int i = 0; i < MX_BLOCK; ++i) {
+                const double v = (double)bf16_bits_to_float(w[(kb * MX_BLOCK + i) * H + n]);
+                if (!isfinite(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            unsigned E;
+            if (!finite) {
+                E = 255;
+            } else if (amax == 0.0) {
+                E = 0;
+            } else {
+                int e2;
+                frexp(amax, &e2); /* amax = f 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+                const long se = (long)(e2 - 1) - mx_emax(fmt) + 127;
+                E = se < 0 ? 0u : se > 254 ? 254u : (unsigned)se;
+            }
+            scales[kb * H + n] = (uint8_t)E;
+            for (int i = 0; i < MX_BLOCK; ++i) {
+                const int64_t k = kb * MX_BLOCK + i;
+                const double v = (double)bf16_bits_to_float(w[k * H + n]);
+                const unsigned c = E == 255 ? 0u : mx_round(fmt, ldexp(v, 127 - (int)E));
+                if (fmt == 1)
+                    codes[k * H + n] = (uint8_t)c;
+                else
+                    codes[(k / 2) * H + n] |= (uint8_t)(c << (k % 2 ? 4 : 0));
+            }
+        }
+    return 0;
+}
+
+/* Weight (k, n) of an MX matrix, exactly. */
+static double mx_weight(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t H,
+                        int64_t k, int64_t n)
+{
+    const unsigned E = scales[(k / MX_BLOCK) * H + n];
+    if (E == 255) return NAN;
+    unsigned c;
+    if (fmt == 1)
+        c = codes[k * H + n];
+    else
+        c = (codes[(k / 2) * H + n] >> (k % 2 ? 4 : 0)) & 0xfu;
+    return ldexp(mx_elem_value(fmt, c), (int)E - 127);
+}
+
+typedef struct {
+    int fmt;
+    const uint16_t* x;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int64_t batch, k, hidden;
+    double* y64;
+    float* y32;
+} mx_ctx;
+
+static void mx_cols(void* p, int64_t n0, int64_t n1)
+{
+    mx_ctx* c = (mx_ctx*)p;
+    for (int64_t b = 0; b < c->batch; ++b)
+        for (int64_t n = n0; n < n1; ++n) {
+            /* y[b,n] = sum over k of x[b,k] * W[k,n], ascending k, in double:
+             * each product of a bf16 and an MX weight is exact */
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < c->k; ++kk)
+                acc += (double)bf16_bits_to_float(c->x[b * c->k + kk]) *
+                       mx_weight(c->fmt, c->codes, c->scales, c->hidden, kk, n);
+            if (c->y64) c->y64[b * c->hidden + n] = acc;
+            if (c->y32) c->y32[b * c->hidden + n] = (float)acc;
+        }
+}
+
+/*
+ * The row-parallel partial projection [P1, Conceito] on MX weights:
+ * p[b, n] = sum_k x[b, k] * W[k, n], with W decoded exactly from codes and
+ * scales (layouts as oracle_mx_quantize), x bf16 [batch][K]; summed in
+ * double, rounded once to float. Returns 0, or 1 for a bad format or size.
+ *
+ * Pins: with every scale 127 and every element a bf16 value it equals
+ * oracle_partial on those values bit for bit; raising every scale by one
+ * doubles every output exactly; exact big-rational brute force on tiny
+ * shapes.
+ */
+int oracle_mx_partial(int32_t fmt, const uint16_t* x, int64_t batch, int64_t K, int64_t H,
+                      const uint8_t* codes, const uint8_t* scales, double* y64, float* y32,
+                      int nthreads)
+{
+    if ((fmt != 1 && fmt != 2) || K < MX_BLOCK || K % MX_BLOCK || H < 1 || batch < 1) return 1;
+    mx_ctx c = {fmt, x, codes, scales, batch, K, H, y64, y32};
+    for_columns(mx_cols, &c, H, nthreads);
+    return 0;
+}
