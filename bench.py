@@ -112,6 +112,46 @@ def cpu_baseline(w, rank, xa, wo, xf, wd, slots, h0, budget_s):
     return out
 
 
+WEIGHT_NAMES = {0: "bf16", 1: "mxfp8", 2: "mxfp4"}
+
+
+def cpu_baseline_mx(w, rank, fmt, xa, wo, xf, wd, slots, h0, budget_s):
+    """The oracle's MX decode step on a bounded sample of layers: per layer
+    both points' MX projections (the oracle's own static conversion of the
+    same bf16 weights, untimed) and their ring sums, threaded over columns;
+    scaled to the L-layer step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    h = h0.cpu().numpy()
+    spent, nl = 0.0, 0
+    wall0 = time.perf_counter()
+    # the sample is bounded by wall time: the oracle's conversion (untimed)
+    # takes seconds per layer
+    while nl < w.layers and (time.perf_counter() - wall0 < budget_s or nl == 0):
+        q = [oracle.mx_quantize(fmt, bits(W[nl])) for W in (wo, wd)]
+        log("cpu baseline: layer %d converted" % nl)
+        xs = (bits(xa[nl]), bits(xf[nl]))
+        s = slots[nl].cpu().numpy()
+        t0 = time.perf_counter()
+        for pt in range(2):
+            _, p32 = oracle.mx_partial(fmt, xs[pt], q[pt][0], q[pt][1], nthreads=cores)
+            s[pt, rank] = p32
+            h = oracle.ring_reduce(s[pt], h)
+        spent += time.perf_counter() - t0
+        nl += 1
+    return {"value": w.batch / (spent / nl * w.layers), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "the first %d of %d layers (both points' %s projections and ring sums), "
+                      "%.1f s, scaled linearly" % (nl, w.layers, WEIGHT_NAMES[fmt], spent)}
+
+
 def cpu_model():
     """The host CPU's model name (from /proc/cpuinfo), or None."""
     try:
@@ -247,7 +287,9 @@ def dense_run(args, w, tune):
 
     import row_gemv_reduction_amd as tp
     from row_gemv_reduction_amd import workloads
-    plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn, tune=tune)
+    fmt = args.weights
+    plan = tp.Plan(w.hidden, w.inter, w.n_ranks, w.batch, k_attn=w.k_attn, tune=tune,
+                   weight_format=fmt)
     info = plan.info()
     log("workload %s: K_r = %s, splits %s, path %s" % (w.name, info["k_rank"], info["splits"],
                                                       info["path"]))
@@ -261,12 +303,23 @@ def dense_run(args, w, tune):
         packed_ok = info["packed_kind"] == 1 if args.op == "partials" else info["packed_kind"] != 0
         layout = "packed" if packed_ok else "rowmajor"
     extra = {}
+    if fmt and layout != "packed":
+        raise SystemExit("MX weights run on the packed step (--layout packed or auto)")
     if layout == "packed":
-        # load-time layout change, outside the timed region
-        po = torch.empty(tp.packed_shape(plan, 0, w.layers), dtype=torch.bfloat16, device="cuda")
-        pd = torch.empty(tp.packed_shape(plan, 1, w.layers), dtype=torch.bfloat16, device="cuda")
-        tp.tp_pack_weights(plan, 0, wo, po)
-        tp.tp_pack_weights(plan, 1, wd, pd)
+        # load-time layout change (and for MX weights the static conversion),
+        # outside the timed region
+        po = torch.empty(tp.packed_shape(plan, 0, w.layers), dtype=tp.packed_dtype(plan), device="cuda")
+        pd = torch.empty(tp.packed_shape(plan, 1, w.layers), dtype=tp.packed_dtype(plan), device="cuda")
+        if fmt:
+            for pt, (W, P) in enumerate(((wo, po), (wd, pd))):
+                codes = torch.empty(tp.mx_codes_shape(plan, pt, w.layers), dtype=torch.uint8, device="cuda")
+                scales = torch.empty(tp.mx_scales_shape(plan, pt, w.layers), dtype=torch.uint8, device="cuda")
+                tp.tp_quantize_mx(plan, pt, W, codes, scales)
+                tp.tp_pack_weights_mx(plan, pt, codes, scales, P)
+                del codes, scales
+        else:
+            tp.tp_pack_weights(plan, 0, wo, po)
+            tp.tp_pack_weights(plan, 1, wd, pd)
         torch.cuda.synchronize()
 
         pa = torch.empty(tp.packed_act_shape(plan, 0, w.layers), dtype=torch.bfloat16, device="cuda")
@@ -281,6 +334,8 @@ def dense_run(args, w, tune):
                 tp.tp_decode_layers_packed(plan, w.layers, args.rank, xa, po, xf, pd, slots, hidden, ws)
         name = "decode_stream" if info["packed_kind"] == 1 else (
             "decode_stream_mfma (%d workgroups sharing the tiles)" % info["stream_wgs"])
+        if fmt:
+            name += " on %s weights" % WEIGHT_NAMES[fmt]
         kernel = "%s (one launch per step, %d reconciliation points)" % (name, 2 * w.layers)
     else:
         def step():
@@ -321,8 +376,8 @@ def dense_run(args, w, tune):
         ms_serial = time_steps(step, args.steps, args.warmup, stream,
                                ws_check(plan, ws, "serial point order"))
         plan.tune("serial_points", 0)
-        b_serial = w.projection_bytes_per_step() / (ms_serial * 1e-3) / 1e9
-        b_serial_all = w.algorithmic_bytes_per_step() / (ms_serial * 1e-3) / 1e9
+        b_serial = w.projection_bytes_per_step(fmt) / (ms_serial * 1e-3) / 1e9
+        b_serial_all = (w.projection_bytes_per_step(fmt) + w.reduce_io_bytes_per_step()) / (ms_serial * 1e-3) / 1e9
         extra["serial_point_order"] = {
             "ms_per_step": round(ms_serial, 5), "tokens_per_s": round(w.batch / (ms_serial * 1e-3), 3),
             "achieved_gbs": round(b_serial, 2), "frac": round(b_serial / HBM_PEAK_GBS, 4),
@@ -330,18 +385,22 @@ def dense_run(args, w, tune):
             "note": "point j+1 reads its activation only after every column of point j is complete"}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.rank, xa, wo, xf, wd, slots, h0, args.cpu_seconds)
+        if fmt:
+            cpu = cpu_baseline_mx(w, args.rank, fmt, xa, wo, xf, wd, slots, h0, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(w, args.rank, xa, wo, xf, wd, slots, h0, args.cpu_seconds)
     config = {"workload": w.name, "hidden": w.hidden, "inter": w.inter, "k_attn": w.k_attn,
               "layers": w.layers, "n_ranks": w.n_ranks, "rank": args.rank, "batch": w.batch,
               "reductions_per_token": 2 * w.layers, "weight_layout": layout,
-              "weight_bytes_per_step": w.weight_bytes_per_step()}
-    extra["traffic"] = measured_traffic(w, layout)
+              "weights": WEIGHT_NAMES[fmt],
+              "weight_bytes_per_step": w.weight_bytes_per_step(fmt)}
+    extra["traffic"] = measured_traffic(w, layout) if not fmt else None
     extra["reduce_io_bytes"] = w.reduce_io_bytes_per_step()
-    extra["weight_bytes"] = w.weight_bytes_per_step()
-    if cpu is not None and w.name == workloads.PAGE1.name:
+    extra["weight_bytes"] = w.weight_bytes_per_step(fmt)
+    if cpu is not None and w.name == workloads.PAGE1.name and not fmt:
         cpu["tiny_single_thread"] = tiny_single_thread()
     plan.close()
-    return ms, w.batch, w.projection_bytes_per_step(), kernel, config, cpu, extra
+    return ms, w.batch, w.projection_bytes_per_step(fmt), kernel, config, cpu, extra
 
 
 def single_op_run(args, w, plan, info, tune, inputs, ws, stream):
@@ -653,6 +712,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--tune", action="append", default=[], help="key=value plan knob")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "mxfp8", "mxfp4", "0", "1", "2"],
+                    help="element format of the packed step's weights: bf16, or microscaled "
+                         "MXFP8 / MXFP4 (converted once at load, untimed)")
     ap.add_argument("--layout", choices=["auto", "packed", "rowmajor"], default="auto",
                     help="weight layout: pair-strip packed (packed once at load, untimed) or row-major")
     ap.add_argument("--op", choices=["step", "partials", "partial", "ring", "swiglu", "qkv", "stream_read"],
@@ -664,6 +726,8 @@ def main():
                          "SwiGLU (tp_gate_up_swiglu) or QKV projections (tp_qkv_proj); or the "
                          "device's streaming-read ceiling over the step's weight bytes")
     args = ap.parse_args()
+    args.weights = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}.get(args.weights, None) \
+        if not args.weights.isdigit() else int(args.weights)
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the N virtual ranks are emulated on a single "
@@ -711,7 +775,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if not getattr(args, "weights", 0) else "bf16 x " + WEIGHT_NAMES[args.weights],
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
         "config": config,
         "roofline": roofline,

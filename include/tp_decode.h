@@ -63,6 +63,13 @@ typedef enum {
     TP_PATH_MFMA = 1  /* batch >= 16: bf16 matrix-core skinny GEMM */
 } tp_path;
 
+/* Element formats of the packed step's weights (tp_plan_set_weight_format). */
+typedef enum {
+    TP_WEIGHTS_BF16 = 0,  /* bf16 */
+    TP_WEIGHTS_MXFP8 = 1, /* microscaled FP8 E4M3, 32-row blocks, E8M0 scales */
+    TP_WEIGHTS_MXFP4 = 2  /* microscaled FP4 E2M1, 32-row blocks, E8M0 scales */
+} tp_weight_format;
+
 typedef struct tp_plan_s* tp_plan_t;
 
 /* What a plan resolved to (tp_plan_info). The struct is named by its tag,
@@ -89,6 +96,9 @@ typedef struct tp_plan_info {
                                 0 = the plan is not supported, 1 = pair strips (vector ALU),
                                 2 = MFMA tiles (matrix cores) */
     int32_t stream_wgs;      /* packed_kind 2: workgroups of the matrix-core step (0 otherwise) */
+    int32_t weight_format;   /* tp_weight_format of the packed step (tp_plan_set_weight_format) */
+    int32_t reserved0;
+    int64_t packed_layer_bytes[2]; /* packed_kind 1: bytes of one layer's packed weights per point */
 } tp_plan_info_t;
 
 /*
@@ -128,6 +138,20 @@ tp_status tp_plan_set_qkv_dim(tp_plan_t plan, int64_t cols);
  * n_experts; TP_ERR_UNSUPPORTED if top_k > 32 or max_tokens > 4096. */
 tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int32_t ep,
                           int64_t moe_inter, int32_t max_tokens);
+
+/*
+ * Choose the element format of the packed step's weights ("Hosting Qwen on
+ * Blackwell", Quantization: the weights are converted statically to MXFP8;
+ * MXFP4 is weighed too). TP_WEIGHTS_BF16 (the default), or microscaled
+ * TP_WEIGHTS_MXFP8 / TP_WEIGHTS_MXFP4: blocks of 32 consecutive rows (along
+ * K) of a column share one E8M0 scale 2^(E-127), elements FP8 E4M3 or FP4
+ * E2M1. With an MX format the packed step (tp_decode_layers_packed and its
+ * no-alloc and partials-only forms) runs the vector-ALU stream on weights
+ * packed by tp_pack_weights_mx, and needs K_r of both points to be
+ * multiples of 32 (packed_kind is 0 otherwise). Must be called before the
+ * plan is first used. TP_ERR_INVALID_ARG for another value.
+ */
+tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
 
 /* Tuning knobs (advanced; the defaults are tuned for MI355X). A knob that
  * changes the tiles ("splits_*", "valu_cols", "step_rows", "stream_wgs",
@@ -378,10 +402,40 @@ tp_status tp_decode_point(tp_plan_t plan, int32_t point, int32_t rank, const voi
  *     K_r are zero): 2 KB tiles of 64 rows x 16 columns.
  *     w_packed bf16 [n_layers][H/16][ceil(K_r/64)][2][64][8].
  * tp_pack_weights: w bf16 [n_layers][K_r][hidden] -> w_packed for `point`.
- * w and w_packed must not overlap. TP_ERR_UNSUPPORTED if packed_kind is 0.
+ * w and w_packed must not overlap. TP_ERR_UNSUPPORTED if packed_kind is 0
+ * or the plan's weights are MX (tp_quantize_mx, tp_pack_weights_mx).
  */
 tp_status tp_pack_weights(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w,
                           void* w_packed, void* stream);
+
+/*
+ * Static conversion of a point's bf16 weight stack to the plan's MX format
+ * ("Hosting Qwen on Blackwell", Quantization), block by block (32 rows of a
+ * column): the scale E = floor(log2(max |w|)) - emax + 127, emax = 8 (E4M3)
+ * or 2 (E2M1), clamped to [0, 254] (0 for an all-zero block; 255, NaN,
+ * with zero codes if the block holds a NaN or an infinity); each element
+ * w * 2^(127-E) rounded to the nearest element value, ties to the even
+ * code, saturating at the largest finite value (448 or 6), sign kept.
+ *   w      bf16 [n_layers][K_r][hidden] (the rank's slices, row-major)
+ *   codes  uint8, MXFP8: [n_layers][K_r][hidden]; MXFP4: [n_layers][K_r/2][hidden],
+ *          two rows of a column per byte, the even row in the low nibble
+ *   scales uint8 [n_layers][K_r/32][hidden] (E of rows 32kb..32kb+31)
+ * TP_ERR_UNSUPPORTED unless the plan's format is MX and 32 divides K_r.
+ */
+tp_status tp_quantize_mx(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w, void* codes,
+                         void* scales, void* stream);
+
+/*
+ * Pack a point's MX weight stack (tp_quantize_mx's layout) for the packed
+ * step, once, at load time: w_packed holds info.packed_layer_bytes[point] *
+ * n_layers bytes: first, for every layer, the 16-byte vectors
+ * [hidden/4][K_r/R][4 columns][R rows] (R = 4 FP8 codes, or 8 FP4 codes as
+ * 4 bytes of two rows each), then, for every layer, the scale words
+ * [hidden/4][K_r/32], the 4 columns' E in bytes 0..3. TP_ERR_UNSUPPORTED
+ * unless the plan's format is MX and packed_kind is 1.
+ */
+tp_status tp_pack_weights_mx(tp_plan_t plan, int32_t point, int32_t n_layers, const void* codes,
+                             const void* scales, void* w_packed, void* stream);
 
 /*
  * The activation slices of a step in the order tp_decode_layers_packed

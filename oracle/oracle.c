@@ -574,9 +574,14 @@ static unsigned mx_round(int fmt, double v)
 {
     const unsigned ncodes = fmt == 1 ? 0x7fu : 0x8u; /* finite non-negative codes */
     const double a = fabs(v);
-    unsigned lo = 0;
-    for (unsigned c = 1; c < ncodes; ++c)
-        if (mx_elem_value(fmt, c) <= a) lo = c;
+    /* the largest code whose value is not above a (values increase with the
+     * code): a binary search over [0, ncodes) */
+    unsigned lo = 0, hi = ncodes;
+    while (hi - lo > 1) {
+        const unsigned mid = (lo + hi) / 2;
+        if (mx_elem_value(fmt, mid) <= a) lo = mid;
+        else hi = mid;
+    }
     unsigned code = lo;
     if (lo + 1 < ncodes) {
         const double dl = a - mx_elem_value(fmt, lo), dh = mx_elem_value(fmt, lo + 1) - a;

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "libtpdecode.so")
 TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_ALIGNMENT, TP_ERR_DEVICE, TP_ERR_OOM = range(6)
 TP_POINT_ATTN_OUT, TP_POINT_FFN_DOWN = 0, 1
 TP_PATH_VALU, TP_PATH_MFMA = 0, 1
+TP_WEIGHTS_BF16, TP_WEIGHTS_MXFP8, TP_WEIGHTS_MXFP4 = 0, 1, 2
+MX_BLOCK = 32
 
 
 class TPError(RuntimeError):
@@ -38,7 +40,8 @@ class tp_plan_info(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("ep", ctypes.c_int32),
         ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
         ("max_tokens", ctypes.c_int32), ("packed_kind", ctypes.c_int32),
-        ("stream_wgs", ctypes.c_int32),
+        ("stream_wgs", ctypes.c_int32), ("weight_format", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("packed_layer_bytes", ctypes.c_int64 * 2),
     ]
 
 
@@ -53,6 +56,11 @@ EXPORTS = {
     "tp_plan_set_moe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "tp_plan_tune": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int64]),
+    "tp_plan_set_weight_format": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "tp_quantize_mx": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                       + [ctypes.c_void_p] * 4),
+    "tp_pack_weights_mx": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                           + [ctypes.c_void_p] * 4),
     "tp_plan_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(tp_plan_info)]),
     "tp_plan_info_get": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(tp_plan_info)]),
     "tp_plan_destroy": (None, [ctypes.c_void_p]),
@@ -141,7 +149,7 @@ class Plan:
     and tuning knobs are applied before first use."""
 
     def __init__(self, hidden, inter, n_ranks, batch, k_attn=None, moe=None, tune=None,
-                 qkv_cols=None):
+                 qkv_cols=None, weight_format=TP_WEIGHTS_BF16):
         h = ctypes.c_void_p()
         _check(_lib().tp_plan(hidden, inter, n_ranks, batch, ctypes.byref(h)), "tp_plan")
         self._h = h
@@ -152,6 +160,8 @@ class Plan:
                 _check(_lib().tp_plan_set_qkv_dim(h, qkv_cols), "tp_plan_set_qkv_dim")
             if k_attn is not None:
                 _check(_lib().tp_plan_set_attn_dim(h, k_attn), "tp_plan_set_attn_dim")
+            if weight_format != TP_WEIGHTS_BF16:
+                _check(_lib().tp_plan_set_weight_format(h, weight_format), "tp_plan_set_weight_format")
             if moe is not None:
                 _check(_lib().tp_plan_set_moe(h, moe["n_experts"], moe["top_k"], moe["ep"],
                                               moe["moe_inter"], moe["max_tokens"]),
@@ -332,13 +342,21 @@ def tp_decode_point(plan: Plan, point, rank, x, w, slots, hidden, workspace):
     _check(_lib().tp_decode_point(plan.handle, point, rank, *args, _stream()), "tp_decode_point")
 
 
+def packed_dtype(plan: Plan):
+    """bf16 for bf16 weights; uint8 bytes for MX weights."""
+    return torch.bfloat16 if plan._plan_info()["weight_format"] == TP_WEIGHTS_BF16 else torch.uint8
+
+
 def packed_shape(plan: Plan, point, n_layers):
     """Shape of a packed weight stack for the plan's streamed step:
-    pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/64), 2, 64, 8]."""
+    pair strips [L, H/4, ceil(K_r/2), 8] or MFMA tiles [L, H/16, ceil(K_r/64), 2, 64, 8]
+    (bf16); for MX weights the stack's bytes [L * packed_layer_bytes] (uint8)."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
     i = plan._plan_info()
     kr, H = i["k_rank"][point], i["hidden"]
+    if i["packed_kind"] == 1 and i["weight_format"] != TP_WEIGHTS_BF16:
+        return (n_layers * i["packed_layer_bytes"][point],)
     if i["packed_kind"] == 1:
         return (n_layers, H // 4, (kr + 1) // 2, 8)
     if i["packed_kind"] == 2:
@@ -374,12 +392,50 @@ def tp_pack_activations(plan: Plan, x_attn, x_ffn, xa_packed, xf_packed):
                                       _stream()), "tp_pack_activations")
 
 
+def mx_codes_shape(plan: Plan, point, n_layers):
+    """Interchange layout of a point's MX codes: [L, K_r, H] (MXFP8) or [L, K_r/2, H] (MXFP4)."""
+    i = plan._plan_info()
+    kr, H = i["k_rank"][point], i["hidden"]
+    return (n_layers, kr if i["weight_format"] == TP_WEIGHTS_MXFP8 else kr // 2, H)
+
+
+def mx_scales_shape(plan: Plan, point, n_layers):
+    i = plan._plan_info()
+    return (n_layers, i["k_rank"][point] // MX_BLOCK, i["hidden"])
+
+
+def tp_quantize_mx(plan: Plan, point, w, codes, scales):
+    """bf16 weights [L, K_r, H] -> MX codes and scales (the plan's format)."""
+    if point not in (0, 1):
+        raise ValueError("point must be 0 or 1")
+    L = w.shape[0]
+    i = plan._plan_info()
+    _check(_lib().tp_quantize_mx(plan.handle, point, L,
+                                 _dev(w, "w", torch.bfloat16, (L, i["k_rank"][point], i["hidden"])),
+                                 _dev(codes, "codes", torch.uint8, mx_codes_shape(plan, point, L)),
+                                 _dev(scales, "scales", torch.uint8, mx_scales_shape(plan, point, L)),
+                                 _stream()), "tp_quantize_mx")
+
+
+def tp_pack_weights_mx(plan: Plan, point, codes, scales, w_packed):
+    """MX codes and scales of a stack -> the packed step's layout (packed_shape, uint8)."""
+    if point not in (0, 1):
+        raise ValueError("point must be 0 or 1")
+    L = codes.shape[0]
+    _check(_lib().tp_pack_weights_mx(plan.handle, point, L,
+                                     _dev(codes, "codes", torch.uint8, mx_codes_shape(plan, point, L)),
+                                     _dev(scales, "scales", torch.uint8, mx_scales_shape(plan, point, L)),
+                                     _dev(w_packed, "w_packed", torch.uint8, packed_shape(plan, point, L)),
+                                     _stream()), "tp_pack_weights_mx")
+
+
 def tp_pack_weights(plan: Plan, point, w, w_packed):
     """Pack a stack of row-major weight slices [L, K_r, H] -> packed_shape()."""
-    shape = packed_shape(plan, point, w.shape[0])
-    L, kr, H = shape[0], plan._plan_info()["k_rank"][point], plan._plan_info()["hidden"]
+    L = w.shape[0]
+    shape = packed_shape(plan, point, L)
+    kr, H = plan._plan_info()["k_rank"][point], plan._plan_info()["hidden"]
     _check(_lib().tp_pack_weights(plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, kr, H)),
-                                  _dev(w_packed, "w_packed", torch.bfloat16, shape),
+                                  _dev(w_packed, "w_packed", packed_dtype(plan), shape),
                                   _stream()), "tp_pack_weights")
 
 
@@ -391,9 +447,9 @@ def tp_decode_layers_packed(plan: Plan, n_layers, rank, x_attn, w_o_packed, x_ff
     ka, ki = i["k_rank"]
     L = n_layers
     args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
-            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
+            _dev(w_o_packed, "w_o_packed", packed_dtype(plan), packed_shape(plan, 0, L)),
             _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
-            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
+            _dev(w_down_packed, "w_down_packed", packed_dtype(plan), packed_shape(plan, 1, L)),
             _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
             _dev(hidden, "hidden", torch.float32, (b, H)),
             _dev(workspace, "workspace", torch.uint8))
@@ -410,9 +466,9 @@ def tp_decode_layers_packed_noalloc(plan: Plan, n_layers, rank, x_attn, w_o_pack
     n, b, H = i["n_ranks"], i["batch"], i["hidden"]
     L = n_layers
     args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
-            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
+            _dev(w_o_packed, "w_o_packed", packed_dtype(plan), packed_shape(plan, 0, L)),
             _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
-            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
+            _dev(w_down_packed, "w_down_packed", packed_dtype(plan), packed_shape(plan, 1, L)),
             _dev(slots, "slots", torch.float32, (L, 2, n, b, H)),
             _dev(hidden, "hidden", torch.float32, (b, H)))
     _check(_lib().tp_decode_layers_packed_noalloc(plan.handle, L, rank, *args, _stream()),
@@ -427,9 +483,9 @@ def tp_rowparallel_partials_packed(plan: Plan, n_layers, x_attn, w_o_packed, x_f
     b, H = i["batch"], i["hidden"]
     L = n_layers
     args = (_dev(x_attn, "x_attn", torch.bfloat16, packed_act_shape(plan, 0, L)),
-            _dev(w_o_packed, "w_o_packed", torch.bfloat16, packed_shape(plan, 0, L)),
+            _dev(w_o_packed, "w_o_packed", packed_dtype(plan), packed_shape(plan, 0, L)),
             _dev(x_ffn, "x_ffn", torch.bfloat16, packed_act_shape(plan, 1, L)),
-            _dev(w_down_packed, "w_down_packed", torch.bfloat16, packed_shape(plan, 1, L)),
+            _dev(w_down_packed, "w_down_packed", packed_dtype(plan), packed_shape(plan, 1, L)),
             _dev(p, "p", torch.float32, (L, 2, b, H)),
             _dev(workspace, "workspace", torch.uint8))
     if workspace.numel() < i["workspace_bytes"]:

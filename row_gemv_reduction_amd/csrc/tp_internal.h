@@ -89,6 +89,7 @@ struct tp_plan_s {
     int32_t swiglu_layers = 0;  // tp_gate_up_swiglu: most layers per launch (0 = automatic)
     int32_t xcd_walk = 0;       // persistent step: 1 = XCD-contiguous tile walk
     int64_t qkv_cols = 0;       // tp_qkv_proj: the rank's Q, K and V columns (0 = not set)
+    int32_t weight_format = 0;  // packed step's weights: TP_WEIGHTS_BF16, _MXFP8 or _MXFP4
     // MoE
     int32_t n_experts = 0, top_k = 0, ep = 0;
     int64_t moe_inter = 0;
@@ -121,17 +122,35 @@ int64_t tp_step_partial_buffer_bytes(const tp_plan_s* p);
 int64_t tp_ws_moe_offset(const tp_plan_s* p);
 int tp_decode_mode(const tp_plan_s* p);
 
+// Microscaled weights: 32 rows of a column share one 8-bit scale.
+constexpr int kMxBlock = 32;
+// Rows of one column in a 16-byte vector of the vector-ALU stream's
+// layout: 2 bf16 pairs, 4 FP8 codes, 8 FP4 codes.
+constexpr int stream_rows_per_vec(int weight_format) {
+    return weight_format == TP_WEIGHTS_MXFP8 ? 4 : weight_format == TP_WEIGHTS_MXFP4 ? 8 : 2;
+}
+
 // Geometry of the streamed decode step (tp_packed.hip).
 struct StreamGeom {
     int32_t grid, block;  // workgroups (strip owners) and threads per workgroup
     int32_t ns, wps, sl;  // strips per workgroup, waves per strip, loads per bank
-    int32_t kh0, kh1;     // row pairs per point kind
+    int32_t kh0, kh1;     // row pairs per point kind (x is staged as bf16 pairs)
+    int32_t kv0, kv1;     // 16-byte weight vectors per strip per point kind
     int32_t bpw0, bpw1;   // 1 KB row blocks per compute wave per point kind
     int32_t xoff1, xdwords, lds_bytes;
 };
+// Bytes of one point's packed weight stack on the vector-ALU stream
+// (codes, then for MX weights the scales).
+int64_t tp_stream_packed_bytes(const tp_plan_s* p, int point, int64_t n_layers);
 bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g);
 tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
                         void* stream);
+// MX weights: bf16 [L][K][H] -> interchange codes and scales; interchange ->
+// the stream's packed layout.
+tp_status tp_mx_quantize(const tp_plan_s* p, int point, int n_layers, const void* w, void* codes,
+                         void* scales, void* stream);
+tp_status tp_mx_pack(const tp_plan_s* p, int point, int n_layers, const void* codes, const void* scales,
+                     void* w_packed, void* stream);
 // (partials != nullptr: the partials only, into partials [L][2][b][H]; slots
 // and hidden unused)
 tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,

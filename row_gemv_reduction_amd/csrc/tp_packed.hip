@@ -101,14 +101,17 @@ constexpr int kBlockBytes = 1024;     // one wave load: 64 lanes x 16 bytes = 12
 struct StreamArgs {
     const uint16_t* x0;     // x_attn [L][B][K0]
     const uint16_t* x1;     // x_ffn  [L][B][K1]
-    const uint16_t* w0;     // packed w_o    [L][S][Kh0][8]
-    const uint16_t* w1;     // packed w_down [L][S][Kh1][8]
+    const uint16_t* w0;     // packed w_o    [L][S][Kv0][8] (16-byte vectors)
+    const uint16_t* w1;     // packed w_down [L][S][Kv1][8]
+    const uint32_t* sc0;    // MX weights: scales of w_o [L][S][K0/32] (4 columns' E8M0 bytes)
+    const uint32_t* sc1;    // MX weights: scales of w_down [L][S][K1/32]
     float* slots;           // [L][2][N][B][H]
     float* hidden;          // [B][H]
     uint32_t* flags;        // serial order: G completion words, then the exit counter
     uint32_t* err;          // error word (bit 0: a bounded wait timed out)
     int32_t H, S, NS, WPS;
     int32_t K0, K1, Kh0, Kh1;
+    int32_t Kv0, Kv1;       // 16-byte weight vectors per strip per point kind
     int32_t bpw0, bpw1;     // row blocks per compute wave per point (same for every wave)
     int32_t layers, n_ranks, rank, chunk;
     int32_t xoff1;          // dword offset of the second x buffer in LDS
@@ -133,10 +136,21 @@ struct Cursor {
     int j, m0;
 };
 
+// An E8M0 block scale as the scale operand of gfx950's scaled conversions
+// (v_cvt_scalef32_pk_bf16_fp8 / _fp4). Those read only the binary32's
+// exponent field, as an E8M0 value: field E scales by 2^(E-127), field 0 by
+// 2^-127, field 255 gives NaN, and the mantissa is ignored; the product is
+// rounded to bf16 nearest-even (measured over every code at scales 2^-127 ..
+// 2^120). So the byte goes straight into the exponent field.
+__device__ __forceinline__ float mx_scale_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
 // PART: the partials only (tp_rowparallel_partials_packed): the control wave
 // writes each point's partial to slots[j] ([L][2][b][H]) and forms no ring
 // sum; the hidden state is neither read nor written.
-template <int B, int SL, bool SERIAL, bool PART = false>
+// WF: the weights' element format (tp_weight_format). A 16-byte vector holds
+// 4 columns of a strip and RV = 2 (bf16), 4 (FP8) or 8 (FP4) consecutive
+// rows per column; with MX weights every 32 rows of a column share a scale.
+template <int B, int SL, bool SERIAL, bool PART = false, int WF = TP_WEIGHTS_BF16>
 __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs a) {
     extern __shared__ __align__(16) uint32_t xs[];             // two x buffers, bf16 pairs
     __shared__ float red[2][kStreamMaxWaves - 1][B * 4];        // per point parity
@@ -302,47 +316,101 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                                                         // offset, which the range check covers
         const int stride = a.WPS * kBlockBytes;
 
+        constexpr int RV = WF == TP_WEIGHTS_MXFP8 ? 4 : WF == TP_WEIGHTS_MXFP4 ? 8 : 2;
+        constexpr int VPB = kMxBlock / RV;  // vectors per scale block (MX)
         auto bpw = [&](int j) { return (j & 1) ? a.bpw1 : a.bpw0; };
         auto advance = [&](Cursor& cu) {
             cu.m0 += SL;
             if (cu.m0 >= bpw(cu.j)) { cu.j += 1; cu.m0 = 0; }
         };
         // SL loads, always issued; a segment past the strip or the step has
-        // an empty range and reads zeros without a memory access
-        auto issue = [&](u32x4_t (&bank)[SL], const Cursor& cu) {
+        // an empty range and reads zeros without a memory access. MX weights
+        // also load each vector's scale word (its block's 4 column scales).
+        auto issue = [&](u32x4_t (&bank)[SL], uint32_t (&sbank)[SL], const Cursor& cu) {
             const int t = cu.j & 1, l = cu.j >> 1;
-            const int kh = t ? a.Kh1 : a.Kh0;
+            const int kv = t ? a.Kv1 : a.Kv0;
             const bool live = active && cu.j < n_points;
-            const uint16_t* base = (t ? a.w1 : a.w0) + ((int64_t)l * a.S + s) * kh * 8;
+            const uint16_t* base = (t ? a.w1 : a.w0) + ((int64_t)l * a.S + s) * kv * 8;
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(live ? base : a.w0), (short)0, live ? kh * 16 : 0,
+                const_cast<uint16_t*>(live ? base : a.w0), (short)0, live ? kv * 16 : 0,
                 kBufferRsrcWord3);
 #pragma unroll
             for (int i = 0; i < SL; ++i)
                 bank[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                           rs, voff + (cu.m0 + i) * stride, 0, kCachePolicyNT));
+            if constexpr (WF != TP_WEIGHTS_BF16) {
+                const int nblk = kv / VPB;
+                const uint32_t* sb = (t ? a.sc1 : a.sc0) + ((int64_t)l * a.S + s) * nblk;
+                const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint32_t*>(live ? sb : a.sc0), (short)0, live ? nblk * 4 : 0,
+                    kBufferRsrcWord3);
+#pragma unroll
+                for (int i = 0; i < SL; ++i) {
+                    const int v = (wi + (cu.m0 + i) * a.WPS) * 64 + lane;
+                    sbank[i] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (v / VPB) * 4, 0, 0);
+                }
+            }
         };
         float acc[B][4];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[b][c] = 0.f;
-        auto consume = [&](const u32x4_t (&bank)[SL], const Cursor& cu) {
+        auto consume = [&](const u32x4_t (&bank)[SL], const uint32_t (&sbank)[SL], const Cursor& cu) {
             const int t = cu.j & 1;
             const int kh = t ? a.Kh1 : a.Kh0;
             const uint32_t* xb = xs + (t ? a.xoff1 : 0);
 #pragma unroll
             for (int i = 0; i < SL; ++i) {
-                const int kp = (wi + (cu.m0 + i) * a.WPS) * 64 + lane;
+                const int v = (wi + (cu.m0 + i) * a.WPS) * 64 + lane;  // vector index in the strip
                 const u32x4_t wq = bank[i];
                 const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+                if constexpr (WF == TP_WEIGHTS_BF16) {
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xb[b * kh + kp]);
+                    for (int b = 0; b < B; ++b) {
+                        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, xb[b * kh + v]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        acc[b][c] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2_t, wd[c]), xv, acc[b][c], false);
+                        for (int c = 0; c < 4; ++c)
+                            acc[b][c] = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2_t, wd[c]), xv, acc[b][c], false);
+                    }
+                } else {
+                    // rows RV*v .. RV*v + RV-1 of each column: the codes widened
+                    // to bf16 pairs with the block scale applied (exact: a
+                    // power of two times at most 4 significant bits), then
+                    // the same pair products as the bf16 weights
+                    constexpr int NP = RV / 2;  // row pairs per vector
+                    // slots past the strip's vectors read zero weights: any
+                    // staged x will do, so the index is clamped into the buffer
+                    const int kvt = t ? a.Kv1 : a.Kv0;
+                    const int vx = v < kvt ? v : kvt - 1;
+                    // the vector's 4 columns widened once, then x token by token
+                    bf16x2_t wp[4][NP];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float sc = mx_scale_f32((sbank[i] >> (8 * c)) & 0xffu);
+                        if constexpr (WF == TP_WEIGHTS_MXFP8) {
+                            wp[c][0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[c], sc, false);
+                            wp[c][1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[c], sc, true);
+                        } else {
+                            wp[c][0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], sc, 0);
+                            wp[c][1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], sc, 1);
+                            wp[c][2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], sc, 2);
+                            wp[c][3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], sc, 3);
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        uint32_t xv[NP];
+#pragma unroll
+                        for (int q = 0; q < NP; ++q) xv[q] = xb[b * kh + NP * vx + q];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+#pragma unroll
+                            for (int q = 0; q < NP; ++q)
+                                acc[b][c] = __builtin_amdgcn_fdot2_f32_bf16(
+                                    wp[c][q], __builtin_bit_cast(bf16x2_t, xv[q]), acc[b][c], false);
+                    }
                 }
             }
         };
@@ -360,19 +428,20 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
         };
 
         u32x4_t bank0[SL], bank1[SL];
+        uint32_t sbank0[SL], sbank1[SL];  // MX scale words (unused for bf16)
         Cursor ci{0, 0}, cc{0, 0};
-        issue(bank0, ci);
+        issue(bank0, sbank0, ci);
         advance(ci);
-        issue(bank1, ci);
+        issue(bank1, sbank1, ci);
         advance(ci);
         __syncthreads();  // start
         while (cc.j < n_points) {
             {
-                consume(bank0, cc);
+                consume(bank0, sbank0, cc);
                 const int j = cc.j;
                 const bool last = cc.m0 + SL >= bpw(j);
                 advance(cc);
-                issue(bank0, ci);
+                issue(bank0, sbank0, ci);
                 advance(ci);
                 if (last) point_end(j);
             }
@@ -381,11 +450,11 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 int j = cc.j;
                 bool last = false;
                 if (live) {
-                    consume(bank1, cc);
+                    consume(bank1, sbank1, cc);
                     last = cc.m0 + SL >= bpw(j);
                     advance(cc);
                 }
-                issue(bank1, ci);
+                issue(bank1, sbank1, ci);
                 advance(ci);
                 if (last) point_end(j);
             }
@@ -395,42 +464,177 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
 
 typedef void (*stream_fn)(StreamArgs);
 
-template <int SL, bool SERIAL, bool PART>
+template <int SL, bool SERIAL, bool PART, int WF>
 stream_fn stream_kernel_for(int b) {
     switch (b) {
-        case 1: return decode_stream<1, SL, SERIAL, PART>;
-        case 2: return decode_stream<2, SL, SERIAL, PART>;
-        case 3: return decode_stream<3, SL, SERIAL, PART>;
-        case 4: return decode_stream<4, SL, SERIAL, PART>;
-        case 5: return decode_stream<5, SL, SERIAL, PART>;
-        case 6: return decode_stream<6, SL, SERIAL, PART>;
-        case 7: return decode_stream<7, SL, SERIAL, PART>;
-        case 8: return decode_stream<8, SL, SERIAL, PART>;
+        case 1: return decode_stream<1, SL, SERIAL, PART, WF>;
+        case 2: return decode_stream<2, SL, SERIAL, PART, WF>;
+        case 3: return decode_stream<3, SL, SERIAL, PART, WF>;
+        case 4: return decode_stream<4, SL, SERIAL, PART, WF>;
+        case 5: return decode_stream<5, SL, SERIAL, PART, WF>;
+        case 6: return decode_stream<6, SL, SERIAL, PART, WF>;
+        case 7: return decode_stream<7, SL, SERIAL, PART, WF>;
+        case 8: return decode_stream<8, SL, SERIAL, PART, WF>;
     }
     return nullptr;
 }
 
 // 8-load banks only for batch <= 4 (beyond, the registers would spill).
-template <bool SERIAL, bool PART>
+template <bool SERIAL, bool PART, int WF>
 stream_fn stream_kernel_sl8(int b) {
     switch (b) {
-        case 1: return decode_stream<1, 8, SERIAL, PART>;
-        case 2: return decode_stream<2, 8, SERIAL, PART>;
-        case 3: return decode_stream<3, 8, SERIAL, PART>;
-        case 4: return decode_stream<4, 8, SERIAL, PART>;
+        case 1: return decode_stream<1, 8, SERIAL, PART, WF>;
+        case 2: return decode_stream<2, 8, SERIAL, PART, WF>;
+        case 3: return decode_stream<3, 8, SERIAL, PART, WF>;
+        case 4: return decode_stream<4, 8, SERIAL, PART, WF>;
     }
     return nullptr;
 }
 
 // mode 0: dataflow point order, 1: serial point order, 2: partials only
-stream_fn stream_kernel(int b, int sl, int mode) {
+template <int WF>
+stream_fn stream_kernel_wf(int b, int sl, int mode) {
     if (sl == 4)
-        return mode == 1 ? stream_kernel_for<4, true, false>(b)
-                         : mode == 2 ? stream_kernel_for<4, false, true>(b) : stream_kernel_for<4, false, false>(b);
-    if (sl == 8)
-        return mode == 1 ? stream_kernel_sl8<true, false>(b)
-                         : mode == 2 ? stream_kernel_sl8<false, true>(b) : stream_kernel_sl8<false, false>(b);
+        return mode == 1 ? stream_kernel_for<4, true, false, WF>(b)
+                         : mode == 2 ? stream_kernel_for<4, false, true, WF>(b)
+                                     : stream_kernel_for<4, false, false, WF>(b);
+    if constexpr (WF == TP_WEIGHTS_BF16) {
+        if (sl == 8)
+            return mode == 1 ? stream_kernel_sl8<true, false, WF>(b)
+                             : mode == 2 ? stream_kernel_sl8<false, true, WF>(b)
+                                         : stream_kernel_sl8<false, false, WF>(b);
+    }
     return nullptr;
+}
+
+stream_fn stream_kernel(int b, int sl, int mode, int wf) {
+    switch (wf) {
+        case TP_WEIGHTS_BF16: return stream_kernel_wf<TP_WEIGHTS_BF16>(b, sl, mode);
+        case TP_WEIGHTS_MXFP8: return stream_kernel_wf<TP_WEIGHTS_MXFP8>(b, sl, mode);
+        case TP_WEIGHTS_MXFP4: return stream_kernel_wf<TP_WEIGHTS_MXFP4>(b, sl, mode);
+    }
+    return nullptr;
+}
+
+// ------------------------------------------------------- MX weights --
+
+// Static conversion of bf16 weights to an MX format ("Hosting Qwen on
+// Blackwell", Quantization: the weights are converted once to MXFP8). One
+// thread per block of 32 rows of a column: the block scale
+// E = floor(log2(max |w|)) - emax + 127 (clamped to [0, 254]; 0 for an
+// all-zero block; 255 and zero codes for a block holding a NaN or an
+// infinity), then each element w * 2^(127-E) rounded to the nearest
+// element value, ties to the even code, saturating at the largest finite
+// value, sign kept. Interchange layout: codes [L][K][H] (FP8) or
+// [L][K/2][H] (FP4, the even row in the low nibble), scales [L][K/32][H].
+template <int WF>
+__global__ void mx_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                   uint8_t* __restrict__ scales, int64_t layers, int64_t K, int64_t H) {
+    constexpr int emax = WF == TP_WEIGHTS_MXFP8 ? 8 : 2;
+    const int64_t nblk = K / kMxBlock;
+    const int64_t total = layers * nblk * H;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = t % H, kb = (t / H) % nblk, l = t / (H * nblk);
+        const uint16_t* col = w + (l * K + kb * kMxBlock) * H + n;
+        uint32_t amax = 0;  // |w| as binary32 bits: ordered like the values
+        bool finite = true;
+        for (int i = 0; i < kMxBlock; ++i) {
+            const uint32_t u = ((uint32_t)col[(int64_t)i * H] << 16) & 0x7fffffffu;
+            if (u >= 0x7f800000u) finite = false;
+            amax = u > amax ? u : amax;
+        }
+        uint32_t E;
+        if (!finite) {
+            E = 255;
+        } else if (amax == 0) {
+            E = 0;
+        } else {
+            // floor(log2(amax)): the exponent field, or for a subnormal the
+            // position of the top mantissa bit
+            const int fl = (amax >> 23) ? (int)(amax >> 23) - 127 : (31 - __clz((int)amax)) - 149;
+            const int se = fl - emax + 127;
+            E = se < 0 ? 0u : se > 254 ? 254u : (uint32_t)se;
+        }
+        scales[(l * nblk + kb) * H + n] = (uint8_t)E;
+        // 2^(127-E), an exact binary32 for E in [0, 254]
+        const float inv = __uint_as_float(E >= 1 && E <= 253 ? (254u - E) << 23 : E == 0 ? 0x7f000000u : 0x00400000u);
+        uint8_t prev = 0;
+        for (int i = 0; i < kMxBlock; ++i) {
+            const uint32_t wb = (uint32_t)col[(int64_t)i * H] << 16;
+            uint32_t code = 0;
+            if (E != 255) {
+                const float v = __uint_as_float(wb) * inv;  // exact: a power-of-two scaling
+                const uint32_t sign = __float_as_uint(v) >> 31;
+                const float av = __builtin_fabsf(v);
+                const uint32_t ua = __float_as_uint(av);
+                if (WF == TP_WEIGHTS_MXFP8) {
+                    if (av >= 448.0f) {
+                        code = 0x7e;
+                    } else if (av < 0.015625f) {  // below 2^-6: multiples of 2^-9
+                        code = (uint32_t)__builtin_rintf(av * 512.0f);
+                    } else {  // 3 mantissa bits, nearest even
+                        code = ((ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+                    }
+                    code |= sign << 7;
+                } else {
+                    if (av >= 6.0f) {
+                        code = 0x7;
+                    } else if (av < 1.0f) {  // below 1: multiples of 0.5
+                        code = (uint32_t)__builtin_rintf(av * 2.0f);
+                    } else {  // 1 mantissa bit, nearest even
+                        code = ((ua + 0x1fffffu + ((ua >> 22) & 1u)) >> 22) - (126u << 1);
+                    }
+                    code |= sign << 3;
+                }
+            }
+            const int64_t k = kb * kMxBlock + i;
+            if (WF == TP_WEIGHTS_MXFP8) {
+                codes[(l * K + k) * H + n] = (uint8_t)code;
+            } else if (i & 1) {
+                codes[(l * (K / 2) + k / 2) * H + n] = (uint8_t)(prev | (code << 4));
+            } else {
+                prev = (uint8_t)code;
+            }
+        }
+    }
+}
+
+// Interchange -> the stream's layout, per layer: the 16-byte code vectors
+// [S][Kv][4 columns][RV rows] (FP8: one byte per row; FP4: one byte per two
+// rows, the even row in the low nibble, as in the interchange), then the
+// scale words [S][K/32] holding the block's 4 column scales, column c in
+// byte c. One 16-byte vector or one scale word per thread.
+template <int WF>
+__global__ void mx_pack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                               uint8_t* __restrict__ out, int64_t layers, int64_t K, int64_t H) {
+    constexpr int RV = WF == TP_WEIGHTS_MXFP8 ? 4 : 8;
+    constexpr int BPV = WF == TP_WEIGHTS_MXFP8 ? 4 : 4;  // code bytes per column per vector
+    const int64_t S = H / 4, kv = K / RV, nblk = K / kMxBlock;
+    const int64_t nvec = layers * S * kv, total = nvec + layers * S * nblk;
+    const int64_t crow = WF == TP_WEIGHTS_MXFP8 ? K : K / 2;  // interchange code rows per layer
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        if (t < nvec) {
+            const int64_t v = t % kv, s = (t / kv) % S, l = t / (kv * S);
+            uint32_t d[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int j = 0; j < BPV; ++j)  // interchange row BPV*v + j of column 4s + c
+                    word |= (uint32_t)codes[(l * crow + BPV * v + j) * H + 4 * s + c] << (8 * j);
+                d[c] = word;
+            }
+            *reinterpret_cast<u32x4_t*>(out + t * 16) = u32x4_t{d[0], d[1], d[2], d[3]};
+        } else {
+            const int64_t u = t - nvec;
+            const int64_t kb = u % nblk, s = (u / nblk) % S, l = u / (nblk * S);
+            const uint8_t* e = scales + (l * nblk + kb) * H + 4 * s;
+            *reinterpret_cast<uint32_t*>(out + nvec * 16 + u * 4) =
+                (uint32_t)e[0] | ((uint32_t)e[1] << 8) | ((uint32_t)e[2] << 16) | ((uint32_t)e[3] << 24);
+        }
+    }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -443,6 +647,8 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
     if (p->hidden % 4) return false;
     const int64_t k0 = p->k_attn / p->n_ranks, k1 = p->inter / p->n_ranks;
     if (k0 < 2 || k1 < 2 || (k0 & 1) || (k1 & 1)) return false;
+    const int rv = stream_rows_per_vec(p->weight_format);
+    if (p->weight_format != TP_WEIGHTS_BF16 && (k0 % kMxBlock || k1 % kMxBlock)) return false;
     if ((k0 * p->batch) % 8 || (k1 * p->batch) % 8) return false;
     const int64_t S = p->hidden / 4;
     int64_t ns = (S + kTargetCUs - 1) / kTargetCUs;
@@ -450,18 +656,25 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
     const int64_t G = (S + ns - 1) / ns;
     if (ns * 4 * p->batch > 64 * stream_elems_per_lane(p->batch)) return false;
     const int wps = (int)((kStreamMaxWaves - 1) / ns);
-    // 8-load banks (more bytes in flight) where the registers allow it
-    const int sl = p->segment_loads == 4 || p->batch > 4 ? 4 : 8;
+    // 8-load banks (more bytes in flight) where the registers allow it (bf16
+    // weights up to 4 tokens; MX weights, whose vectors are widened in
+    // registers, always take 4)
+    const int sl = p->segment_loads == 4 || p->batch > 4 || p->weight_format != TP_WEIGHTS_BF16 ? 4 : 8;
     const int64_t kh0 = k0 / 2, kh1 = k1 / 2;
-    const int64_t nb0 = (kh0 + 63) / 64, nb1 = (kh1 + 63) / 64;
+    const int64_t kv0 = k0 / rv, kv1 = k1 / rv;  // (K even; a multiple of 32 for MX)
+    const int64_t nb0 = (kv0 + 63) / 64, nb1 = (kv1 + 63) / 64;
     const int64_t bpw0 = (nb0 + wps - 1) / wps, bpw1 = (nb1 + wps - 1) / wps;
     // x buffer t: B*Kh_t dwords staged in 1 KB pieces, and every pair index a
-    // compute lane reads (up to the last block of its last segment)
+    // compute lane reads (rv/2 pairs per vector, up to the last block of its
+    // last segment)
     auto xbuf = [&](int64_t kh, int64_t bpw) {
         const int64_t n16 = p->batch * kh * 4 / 16;
         const int64_t staged = (n16 + 63) / 64 * 256;
         const int64_t segs = (bpw + sl - 1) / sl;
-        const int64_t read = (p->batch - 1) * kh + ((wps - 1) + (segs * sl - 1) * wps) * 64 + 64;
+        // (MX weights: the compute lanes clamp their x index to the last vector)
+        const int64_t read = p->weight_format != TP_WEIGHTS_BF16
+                                 ? p->batch * kh
+                                 : (p->batch - 1) * kh + ((wps - 1) + (segs * sl - 1) * wps) * 64 + 64;
         const int64_t d = staged > read ? staged : read;
         return (d + 255) / 256 * 256;
     };
@@ -474,10 +687,52 @@ bool tp_stream_geometry(const tp_plan_s* p, StreamGeom* g) {
     g->block = (int32_t)(1 + ns * wps) * 64;
     g->kh0 = (int32_t)kh0;
     g->kh1 = (int32_t)kh1;
+    g->kv0 = (int32_t)kv0;
+    g->kv1 = (int32_t)kv1;
     g->bpw0 = (int32_t)bpw0;
     g->bpw1 = (int32_t)bpw1;
     g->lds_bytes = g->xdwords * 4;
     return g->lds_bytes <= kStreamMaxLdsBytes;
+}
+
+int64_t tp_stream_packed_bytes(const tp_plan_s* p, int point, int64_t n_layers) {
+    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    const int64_t S = p->hidden / 4;
+    if (p->weight_format == TP_WEIGHTS_BF16) return n_layers * S * ((K + 1) / 2) * 16;
+    const int rv = stream_rows_per_vec(p->weight_format);
+    return n_layers * S * (K / rv * 16 + K / kMxBlock * 4);
+}
+
+tp_status tp_mx_quantize(const tp_plan_s* p, int point, int n_layers, const void* w, void* codes,
+                         void* scales, void* stream) {
+    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    if (K % kMxBlock) return TP_ERR_UNSUPPORTED;
+    const int64_t total = (int64_t)n_layers * (K / kMxBlock) * p->hidden;
+    if (total == 0) return TP_OK;
+    const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+    auto k = p->weight_format == TP_WEIGHTS_MXFP8 ? mx_quantize_kernel<TP_WEIGHTS_MXFP8>
+                                                  : mx_quantize_kernel<TP_WEIGHTS_MXFP4>;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
+                       static_cast<uint8_t*>(scales), (int64_t)n_layers, K, p->hidden);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_mx_pack(const tp_plan_s* p, int point, int n_layers, const void* codes, const void* scales,
+                     void* w_packed, void* stream) {
+    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    if (K % kMxBlock || p->hidden % 4) return TP_ERR_UNSUPPORTED;
+    const int rv = stream_rows_per_vec(p->weight_format);
+    const int64_t S = p->hidden / 4;
+    const int64_t total = (int64_t)n_layers * S * (K / rv + K / kMxBlock);
+    if (total == 0) return TP_OK;
+    const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+    auto k = p->weight_format == TP_WEIGHTS_MXFP8 ? mx_pack_kernel<TP_WEIGHTS_MXFP8>
+                                                  : mx_pack_kernel<TP_WEIGHTS_MXFP4>;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                       static_cast<uint8_t*>(w_packed), (int64_t)n_layers, K, p->hidden);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
 tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
@@ -502,16 +757,22 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     if ((int64_t)n_layers * geo.grid * (int64_t)(geo.kh0 > geo.kh1 ? geo.kh0 : geo.kh1) * 8 >=
         ((int64_t)1 << 62))
         return TP_ERR_UNSUPPORTED;
+    if ((((uintptr_t)w_o_packed | (uintptr_t)w_down_packed) & 15) != 0) return TP_ERR_ALIGNMENT;
     if (geo.grid > 1024) return TP_ERR_UNSUPPORTED;  // completion words of the serial order
     if (n_layers == 0) return TP_OK;
     const bool serial = p->serial_points != 0 && !partials;
-    stream_fn k = stream_kernel(p->batch, geo.sl, partials ? 2 : serial ? 1 : 0);
+    stream_fn k = stream_kernel(p->batch, geo.sl, partials ? 2 : serial ? 1 : 0, p->weight_format);
     if (!k) return TP_ERR_UNSUPPORTED;
     StreamArgs a;
     a.x0 = static_cast<const uint16_t*>(x_attn);
     a.x1 = static_cast<const uint16_t*>(x_ffn);
     a.w0 = static_cast<const uint16_t*>(w_o_packed);
     a.w1 = static_cast<const uint16_t*>(w_down_packed);
+    // MX weights: each stack's scale words follow its code vectors
+    a.sc0 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(w_o_packed) +
+                                              (int64_t)n_layers * (p->hidden / 4) * geo.kv0 * 16);
+    a.sc1 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(w_down_packed) +
+                                              (int64_t)n_layers * (p->hidden / 4) * geo.kv1 * 16);
     a.slots = partials ? partials : slots;
     a.hidden = hidden;
     a.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kStreamFlagOffset);
@@ -524,6 +785,8 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     a.K1 = (int32_t)(p->inter / p->n_ranks);
     a.Kh0 = geo.kh0;
     a.Kh1 = geo.kh1;
+    a.Kv0 = geo.kv0;
+    a.Kv1 = geo.kv1;
     a.bpw0 = geo.bpw0;
     a.bpw1 = geo.bpw1;
     a.layers = n_layers;

@@ -297,6 +297,12 @@ tp_status tp_plan_set_qkv_dim(tp_plan_t p, int64_t cols) {
     return TP_OK;
 }
 
+tp_status tp_plan_set_weight_format(tp_plan_t p, int32_t fmt) {
+    if (!p || fmt < TP_WEIGHTS_BF16 || fmt > TP_WEIGHTS_MXFP4) return TP_ERR_INVALID_ARG;
+    p->weight_format = fmt;
+    return TP_OK;
+}
+
 tp_status tp_plan_set_moe(tp_plan_t p, int32_t n_experts, int32_t top_k, int32_t ep,
                           int64_t moe_inter, int32_t max_tokens) {
     if (!p || n_experts < 1 || top_k < 1 || ep < 1 || moe_inter < 1 || max_tokens < 1)
@@ -386,6 +392,9 @@ tp_status tp_plan_info(tp_plan_t p, struct tp_plan_info* o) {
     o->packed_kind = tp_packed_kind(p);
     MfmaGeom mg;
     o->stream_wgs = o->packed_kind == 2 && tp_mfma_geometry(p, &mg) ? mg.grid : 0;
+    o->weight_format = p->weight_format;
+    for (int pt = 0; pt < 2; ++pt)
+        o->packed_layer_bytes[pt] = o->packed_kind == 1 ? tp_stream_packed_bytes(p, pt, 1) : 0;
     return TP_OK;
 }
 

@@ -74,6 +74,7 @@ int tp_packed_kind(const tp_plan_s* p) {
     StreamGeom sg;
     MfmaGeom mg;
     const bool valu = tp_stream_geometry(p, &sg);
+    if (p->weight_format != TP_WEIGHTS_BF16) return valu ? 1 : 0;  // MX: the vector-ALU stream
     const bool mfma = tp_mfma_geometry(p, &mg);
     if (p->stream_kind == 1) return valu ? 1 : 0;
     if (p->stream_kind == 2) return mfma ? 2 : 0;
@@ -98,9 +99,27 @@ tp_status tp_pack_weights(tp_plan_t p, int32_t point, int32_t n_layers, const vo
     if (!aligned16(w) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
     if (w == w_packed) return TP_ERR_INVALID_ARG;
     const int kind = tp_packed_kind(p);
-    if (kind == 0) return TP_ERR_UNSUPPORTED;
+    if (kind == 0 || p->weight_format != TP_WEIGHTS_BF16) return TP_ERR_UNSUPPORTED;
     if (kind == 2) return tp_pack_tiles(p, point, n_layers, w, w_packed, stream);
     return tp_pack_pairs(p, point, n_layers, w, w_packed, stream);
+}
+
+tp_status tp_quantize_mx(tp_plan_t p, int32_t point, int32_t n_layers, const void* w, void* codes,
+                         void* scales, void* stream) {
+    if (!p || !w || !codes || !scales || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return TP_ERR_ALIGNMENT;
+    if (p->weight_format == TP_WEIGHTS_BF16) return TP_ERR_UNSUPPORTED;
+    return tp_mx_quantize(p, point, n_layers, w, codes, scales, stream);
+}
+
+tp_status tp_pack_weights_mx(tp_plan_t p, int32_t point, int32_t n_layers, const void* codes,
+                             const void* scales, void* w_packed, void* stream) {
+    if (!p || !codes || !scales || !w_packed || n_layers < 0) return TP_ERR_INVALID_ARG;
+    if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
+    if (p->weight_format == TP_WEIGHTS_BF16 || tp_packed_kind(p) != 1) return TP_ERR_UNSUPPORTED;
+    return tp_mx_pack(p, point, n_layers, codes, scales, w_packed, stream);
 }
 
 tp_status tp_pack_activations(tp_plan_t p, int32_t n_layers, const void* x_attn, const void* x_ffn,

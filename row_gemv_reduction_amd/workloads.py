@@ -35,18 +35,27 @@ class Workload:
     def ki_r(self) -> int:
         return self.inter // self.n_ranks
 
-    def weight_bytes_per_step(self) -> int:
-        """bf16 weight bytes one rank streams per decode step (2L points)."""
-        return self.layers * (self.ka_r + self.ki_r) * self.hidden * 2
+    def weight_bytes_per_step(self, weight_format: int = 0) -> int:
+        """Weight bytes one rank streams per decode step (2L points)."""
+        return self.layers * (self.weight_slice_bytes(self.ka_r, weight_format)
+                              + self.weight_slice_bytes(self.ki_r, weight_format))
 
-    def projection_bytes_per_step(self) -> int:
+    def weight_slice_bytes(self, kr: int, weight_format: int = 0) -> int:
+        """Bytes of one point's weight slice [kr x H]: bf16, or MX codes (1 or
+        1/2 byte per weight) plus one 8-bit scale per 32 rows of a column."""
+        h = self.hidden
+        if weight_format == 0:
+            return kr * h * 2
+        return kr * h // (1 if weight_format == 1 else 2) + (kr // 32) * h
+
+    def projection_bytes_per_step(self, weight_format: int = 0) -> int:
         """Bytes the rank's 2L partial projections must move per step: per
-        point its weight slice (bf16), its activation slice (bf16) and its
-        fp32 partial written."""
+        point its weight slice, its activation slice (bf16) and its fp32
+        partial written."""
         b, h = self.batch, self.hidden
         per_layer = 0
         for kr in (self.ka_r, self.ki_r):
-            per_layer += kr * h * 2 + b * kr * 2 + b * h * 4
+            per_layer += self.weight_slice_bytes(kr, weight_format) + b * kr * 2 + b * h * 4
         return self.layers * per_layer
 
     def reduce_io_bytes_per_step(self) -> int:

@@ -133,3 +133,26 @@ def test_entry_points_validate_before_launching():
     assert L.tp_decode_layers(h, -1, 0, *[vp(A)] * 8) == TP_ERR_INVALID_ARG
     assert L.tp_decode_layers(h, 1, 0, *[vp(A)] * 5, vp(M), vp(A), vp(A)) == TP_ERR_ALIGNMENT
     assert L.tp_workspace_init(h, None, None) == TP_ERR_INVALID_ARG
+
+
+def test_weight_format_plans():
+    """MX weight formats: the packed step needs K_r of both points to be a
+    multiple of 32 and runs on the vector-ALU stream; the packed stack's
+    bytes are the code vectors plus one scale byte per 32 rows of a column."""
+    for fmt, rows_per_vec in ((binding.TP_WEIGHTS_MXFP8, 4), (binding.TP_WEIGHTS_MXFP4, 8)):
+        i = Plan(5120, 17408, 4, 1, weight_format=fmt).info()
+        assert i["weight_format"] == fmt and i["packed_kind"] == 1
+        for pt, kr in enumerate((1280, 4352)):
+            assert i["packed_layer_bytes"][pt] == (5120 // 4) * (kr // rows_per_vec * 16 + kr // 32 * 4)
+            # codes + scales = K_r*H*(1 or 1/2) + K_r*H/32
+            assert i["packed_layer_bytes"][pt] == kr * 5120 * (2 if fmt == 1 else 1) // 2 + kr // 32 * 5120
+        assert Plan(512, 1040, 2, 1, weight_format=fmt).info()["packed_kind"] == 0  # K_r 520
+        assert Plan(4096, 12288, 8, 64, weight_format=fmt).info()["packed_kind"] == 0  # batch > 8
+    assert Plan(5120, 17408, 4, 1).info()["packed_layer_bytes"][1] == 5120 // 4 * 2176 * 16
+    L = binding._lib()
+    h = ctypes.c_void_p()
+    assert L.tp_plan(512, 512, 2, 1, ctypes.byref(h)) == TP_OK
+    assert L.tp_plan_set_weight_format(h, 3) == TP_ERR_INVALID_ARG
+    assert L.tp_plan_set_weight_format(h, -1) == TP_ERR_INVALID_ARG
+    assert L.tp_plan_set_weight_format(h, 1) == TP_OK
+    L.tp_plan_destroy(h)
