@@ -191,27 +191,33 @@ def tiny_single_thread(budget_s=2.0):
             "sample": "%d whole steps, %.1f s" % (reps, t)}
 
 
-def measured_traffic(w, layout):
-    """HBM bytes per launch of the decode kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), when it covers this
-    workload and the kernel source is the one the counters were taken on;
-    otherwise None."""
+def measured_traffic(key):
+    """HBM bytes per launch of the timed kernel from a committed counter
+    summary under profiles/ (FETCH_SIZE + WRITE_SIZE, copy-calibrated): the
+    one whose `traffic_key:` line is `key` (workload/layout/weights), when
+    the kernel source it names still has the hash the counters were taken
+    on; otherwise None."""
+    import glob
     import hashlib
     import re
 
-    from row_gemv_reduction_amd import workloads
-    if w.name != workloads.PAGE1.name or layout != "packed":
-        return None
-    try:
-        text = open(os.path.join(ROOT, "profiles", "decode_stream_page1_n4_b1.md")).read()
-        src = open(os.path.join(ROOT, "row_gemv_reduction_amd", "csrc", "tp_packed.hip"), "rb").read()
-    except OSError:
-        return None
-    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    m_sha = re.search(r"sha256 prefix ([0-9a-f]+)", text)
-    if not (m_bytes and m_sha) or not hashlib.sha256(src).hexdigest().startswith(m_sha.group(1)):
-        return None
-    return int(m_bytes.group(1))
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        m_key = re.search(r"^traffic_key: (\S+)\s*$", text, re.M)
+        if not m_key or m_key.group(1) != key:
+            continue
+        m_bytes = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+        m_src = re.search(r"^kernel_source: (\S+) sha256 prefix ([0-9a-f]+)", text, re.M)
+        if not (m_bytes and m_src):
+            return None
+        try:
+            src = open(os.path.join(ROOT, m_src.group(1)), "rb").read()
+        except OSError:
+            return None
+        if not hashlib.sha256(src).hexdigest().startswith(m_src.group(2)):
+            return None
+        return int(m_bytes.group(1))
+    return None
 
 
 # Key-value heads and head width of the QKV projection's synthetic width:
@@ -394,7 +400,7 @@ def dense_run(args, w, tune):
               "reductions_per_token": 2 * w.layers, "weight_layout": layout,
               "weights": WEIGHT_NAMES[fmt],
               "weight_bytes_per_step": w.weight_bytes_per_step(fmt)}
-    extra["traffic"] = measured_traffic(w, layout) if not fmt else None
+    extra["traffic"] = measured_traffic("%s/%s/%s" % (w.name, layout, WEIGHT_NAMES[fmt]))
     extra["reduce_io_bytes"] = w.reduce_io_bytes_per_step()
     extra["weight_bytes"] = w.weight_bytes_per_step(fmt)
     if cpu is not None and w.name == workloads.PAGE1.name and not fmt:
@@ -540,6 +546,97 @@ def stream_read_run(args, w):
     kernel = ("tp_stream_read_probe (stream_read_kernel: grid-stride 16-byte nontemporal loads, %d "
               "workgroups of 512 threads)" % wgs)
     return ms, 0, nbytes, kernel, config, None, {"traffic": None}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_run(args, w, tune):
+    """The prefill of a w.batch-token prompt through the stack (tp_prefill_layers):
+    per point the rank's T x H partial on the matrix cores, its slot, and the
+    ring sum + residual fused into the product's epilogue. One launch."""
+    import numpy as np
+    import torch
+
+    import row_gemv_reduction_amd as tp
+    from row_gemv_reduction_amd import synth
+    L, T, H, n, rank = w.layers, w.batch, w.hidden, w.n_ranks, args.rank
+    plan = tp.Plan(H, w.inter, n, 1, k_attn=w.k_attn, tune=tune)
+    kw = dict(seed=0, workload=w.name, rank=rank)
+    xa = synth.device_normal((L, T, w.ka_r), 1.0, torch.bfloat16, tensor="x_attn", **kw)
+    wo = synth.device_normal((L, w.ka_r, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_o", **kw)
+    xf = synth.device_normal((L, T, w.ki_r), 1.0, torch.bfloat16, tensor="x_ffn", **kw)
+    wd = synth.device_normal((L, w.ki_r, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_down", **kw)
+    slots = synth.device_normal((L, 2, n, T, H), synth.WEIGHT_STD * math.sqrt(w.ki_r), torch.float32,
+                                tensor="slots", seed=0, workload=w.name)
+    hidden = synth.device_normal((T, H), 1.0, torch.float32, tensor="residual", seed=0, workload=w.name)
+    po = torch.empty(tp.prefill_packed_shape(plan, 0, L), dtype=torch.bfloat16, device="cuda")
+    pd = torch.empty(tp.prefill_packed_shape(plan, 1, L), dtype=torch.bfloat16, device="cuda")
+    tp.tp_prefill_pack_weights(plan, 0, wo, po)
+    tp.tp_prefill_pack_weights(plan, 1, wd, pd)
+    ws = plan.new_workspace()
+    torch.cuda.synchronize()
+
+    def step():
+        tp.tp_prefill_layers(plan, L, rank, T, xa, po, xf, pd, slots, hidden, ws)
+    ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream(), ws_check(plan, ws, "prefill"))
+    flops = 2.0 * T * (w.ka_r + w.ki_r) * H * L
+    proj = w.projection_bytes_per_step()
+    reduce_io = w.reduce_io_bytes_per_step()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = prefill_cpu_baseline(w, rank, xa, wo, xf, wd, slots, hidden, args.cpu_seconds)
+    config = {"workload": w.name, "hidden": H, "inter": w.inter, "k_attn": w.k_attn, "layers": L,
+              "n_ranks": n, "rank": rank, "tokens": T, "reductions_per_prefill": 2 * L,
+              "weight_layout": "packed matrix-core tiles"}
+    kernel = ("prefill_step (one cooperative launch: 128 x 256 tiles of every point on the bf16 matrix "
+              "cores, ring sum + residual fused into the epilogue)")
+    t = ms * 1e-3
+    extra = {"mfma": {"achieved_tflops": round(flops / t / 1e12, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                      "frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "flops_per_launch": flops},
+             "prefill_bound_note": "at peak the step needs %.2f ms of HBM (projection + ring I/O) and %.2f ms "
+                                   "of matrix cores" % ((proj + reduce_io) / 8e12 * 1e3,
+                                                         flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3),
+             "reduce_io_bytes": reduce_io, "weight_bytes": w.weight_bytes_per_step(),
+             "traffic": measured_traffic("%s/prefill/bf16" % w.name),
+             "fused_bytes": proj + reduce_io}
+    plan.close()
+    return ms, T, proj, kernel, config, cpu, extra
+
+
+def prefill_cpu_baseline(w, rank, xa, wo, xf, wd, slots, hidden, budget_s):
+    """The oracle on a bounded sample of the prefill: the first m tokens of
+    the first layer (both points' projections and the ring sums of those
+    tokens' payloads), scaled to T tokens and L layers."""
+    import numpy as np
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    a, o, f, d = bits(xa[0]), bits(wo[0]), bits(xf[0]), bits(wd[0])
+    s = slots[0].cpu().numpy()
+    h = hidden.cpu().numpy()
+    m, spent = 8, 0.0
+    while True:
+        t0 = time.perf_counter()
+        for pt, (x, W) in enumerate(((a, o), (f, d))):
+            _, p32 = oracle.partial(x[:m], W, nthreads=cores)
+            part = s[pt, :, :m].copy()
+            part[rank] = p32
+            oracle.ring_reduce(part, h[:m])
+        spent = time.perf_counter() - t0
+        if spent * 2 > budget_s or m >= w.batch:
+            break
+        m = min(w.batch, m * 2)
+    per_token_layer = spent / m
+    return {"value": 1.0 / (per_token_layer * w.layers), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "the first %d of %d tokens of layer 0 (both points' projections and ring sums), "
+                      "%.1f s, scaled to %d layers" % (m, w.batch, spent, w.layers)}
 
 
 def moe_build(w, rank, copies, seed=0):
@@ -751,7 +848,7 @@ def main():
     if args.op == "stream_read":
         ms, tokens, step_bytes, kernel, config, cpu, extra = stream_read_run(args, w)
     else:
-        run = moe_run if w.n_experts else dense_run
+        run = moe_run if w.n_experts else (prefill_run if w.name == workloads.PREFILL.name else dense_run)
         ms, tokens, step_bytes, kernel, config, cpu, extra = run(args, w, tune)
     if args.copy_calibration:
         copy_calibration()
@@ -772,6 +869,15 @@ def main():
     wbytes = extra.pop("weight_bytes", 0)
     if wbytes:
         roofline["weights_only_frac"] = round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    fused = extra.pop("fused_bytes", 0)
+    if fused:
+        # prefill: the ring I/O is the kernel's own work and dominates its bytes;
+        # the HBM roofline takes all of them (the projection-only rate is kept)
+        roofline["projection_only_achieved"] = roofline["achieved"]
+        roofline["projection_only_frac"] = roofline["frac"]
+        roofline["achieved"] = round(fused / (ms * 1e-3) / 1e9, 2)
+        roofline["frac"] = round(fused / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        roofline["algorithmic_bytes_per_launch"] = fused
     out = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

@@ -541,6 +541,45 @@ tp_status tp_rowparallel_partials_packed(tp_plan_t plan, int32_t n_layers, const
                                          void* stream);
 
 /*
+ * Pack a point's bf16 weight stack for tp_prefill_layers, once, at load
+ * time: the matrix-core tile layout of tp_pack_weights' packed_kind 2,
+ *     T[l][s][kb][h][lane][i] = W[l][64kb + 16(lane/16) + 8h + i][16s + lane%16]
+ * (rows past K_r zero), whatever the plan's decode batch.
+ *   w bf16 [n_layers][K_r][hidden] -> w_packed bf16 [n_layers][hidden/16][ceil(K_r/64)][2][64][8]
+ * TP_ERR_UNSUPPORTED if hidden is not a multiple of 16.
+ */
+tp_status tp_prefill_pack_weights(tp_plan_t plan, int32_t point, int32_t n_layers, const void* w,
+                                  void* w_packed, void* stream);
+
+/*
+ * The prefill of a prompt of `tokens` tokens through the layer stack, for
+ * rank `rank`: the same two reconciliation points per layer as the decode
+ * step, each carrying one hidden vector per token (lesson 9.9, Conceito: a
+ * 4,096-token prompt runs every position at once, so every collective
+ * carries 4,096 hidden vectors and bandwidth, not latency, governs). Per
+ * point: the rank's partial P = X . W_r (T x hidden, fp32 accumulation on
+ * the bf16 matrix cores) into its slot, then hidden <- ring_sum(slot) +
+ * hidden, the ring order of tp_ring_reduce over the flattened [T x hidden]
+ * payload (chunks of T*hidden/N).
+ *   x_attn bf16 [L][tokens][k_attn/N]   x_ffn bf16 [L][tokens][inter/N]
+ *   w_o_packed, w_down_packed: tp_prefill_pack_weights' layout
+ *   slots  fp32 [L][2][N][tokens][hidden]: the other ranks' partials are
+ *          inputs; entry [l][point][rank] is overwritten
+ *   hidden fp32 [tokens][hidden], in/out
+ * One cooperative launch over tiles of 128 tokens x 256 columns of every
+ * point; a tile's ring sum waits (bounded) for the previous point's sum of
+ * the same tile; the workspace's error word reports a wait that timed out.
+ * Errors: TP_ERR_INVALID_ARG (null pointer, tokens < 1, rank out of range,
+ * N not dividing tokens*hidden), TP_ERR_ALIGNMENT, TP_ERR_UNSUPPORTED
+ * (hidden not a multiple of 16, K_r not a multiple of 8, n_ranks > 8, a
+ * point's X of 2 GiB or more, more than 1024 tiles per point).
+ */
+tp_status tp_prefill_layers(tp_plan_t plan, int32_t n_layers, int32_t rank, int32_t tokens,
+                            const void* x_attn, const void* w_o_packed, const void* x_ffn,
+                            const void* w_down_packed, float* slots, float* hidden, void* workspace,
+                            void* stream);
+
+/*
  * Top-k routing of decode tokens ("Hosting Qwen on Blackwell", Prefillers:
  * each token goes to top_k of the experts). Per token: softmax over the
  * experts' logits (computed in double), the top_k experts by probability

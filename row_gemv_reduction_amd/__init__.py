@@ -8,7 +8,7 @@ from . import synth, workloads  # noqa: F401
 from .binding import (  # noqa: F401
     TP_PATH_MFMA, TP_PATH_VALU, TP_POINT_ATTN_OUT, TP_POINT_FFN_DOWN, TP_WEIGHTS_BF16,
     TP_WEIGHTS_MXFP4, TP_WEIGHTS_MXFP8, Plan, TPError, mx_codes_shape, mx_scales_shape, packed_dtype,
-    tp_pack_weights_mx, tp_quantize_mx,
+    tp_pack_weights_mx, tp_quantize_mx, prefill_packed_shape, tp_prefill_pack_weights, tp_prefill_layers,
     moe_packed_shape, packed_act_shape, packed_shape, tp_decode_layers, tp_decode_layers_packed,
     tp_decode_layers_packed_noalloc,
     tp_decode_point, tp_gate_up_swiglu, tp_moe_decode, tp_pack_activations, tp_qkv_proj,

@@ -100,6 +100,10 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]),
     "tp_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 8),
+    "tp_prefill_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                                + [ctypes.c_void_p] * 3),
+    "tp_prefill_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                          + [ctypes.c_void_p] * 8),
     "tp_stream_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_int32, ctypes.c_void_p]),
 }
@@ -560,3 +564,41 @@ def tp_stream_read_probe(buf, sink):
     _check(_lib().tp_stream_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes,
                                        _dev(sink, "sink", torch.uint32), sink.numel(), _stream()),
            "tp_stream_read_probe")
+
+
+def prefill_packed_shape(plan: Plan, point, n_layers):
+    """Shape of a point's weight stack packed for tp_prefill_layers:
+    [L, H/16, ceil(K_r/64), 2, 64, 8] (bf16)."""
+    i = plan._plan_info()
+    return (n_layers, i["hidden"] // 16, (i["k_rank"][point] + 63) // 64, 2, 64, 8)
+
+
+def tp_prefill_pack_weights(plan: Plan, point, w, w_packed):
+    if point not in (0, 1):
+        raise ValueError("point must be 0 or 1")
+    i = plan._plan_info()
+    L = w.shape[0]
+    _check(_lib().tp_prefill_pack_weights(
+        plan.handle, point, L, _dev(w, "w", torch.bfloat16, (L, i["k_rank"][point], i["hidden"])),
+        _dev(w_packed, "w_packed", torch.bfloat16, prefill_packed_shape(plan, point, L)), _stream()),
+        "tp_prefill_pack_weights")
+
+
+def tp_prefill_layers(plan: Plan, n_layers, rank, tokens, x_attn, w_o_packed, x_ffn, w_down_packed,
+                      slots, hidden, workspace):
+    """The prefill of `tokens` tokens: per point the rank's partial into its slot, then
+    hidden <- ring_sum(slots) + hidden."""
+    i = plan._plan_info()
+    n, H = i["n_ranks"], i["hidden"]
+    ka, ki = i["k_rank"]
+    L, T = n_layers, tokens
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, (L, T, ka)),
+            _dev(w_o_packed, "w_o_packed", torch.bfloat16, prefill_packed_shape(plan, 0, L)),
+            _dev(x_ffn, "x_ffn", torch.bfloat16, (L, T, ki)),
+            _dev(w_down_packed, "w_down_packed", torch.bfloat16, prefill_packed_shape(plan, 1, L)),
+            _dev(slots, "slots", torch.float32, (L, 2, n, T, H)),
+            _dev(hidden, "hidden", torch.float32, (T, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_prefill_layers(plan.handle, L, rank, T, *args, _stream()), "tp_prefill_layers")

@@ -83,6 +83,11 @@ MOE = Workload("moe-h4096-attn8192-e128-top8-ep4-t64", hidden=4096, inter=0,
                top_k=8, ep=4, moe_inter=1536)
 
 
+# The prefill of "Interconnects e clusters" (lesson 9.9, Conceito): the
+# page-1 stack with a 4,096-token prompt (batch = tokens of one prefill).
+PREFILL = PAGE1.with_(name="prefill-page1-h5120-i17408-l64-n4-t4096", batch=4096)
+
+
 def page1_n2(batch: int) -> Workload:
     return PAGE1_N2.with_(name="page1-h5120-i17408-l64-n2-b%d" % batch, batch=batch)
 
@@ -98,4 +103,4 @@ def h4096(n_ranks: int, batch: int) -> Workload:
 
 ALL = {w.name: w for w in [TINY, PAGE1] + [page1_n4(b) for b in (2, 4, 8, 16)]
        + [page1_n2(b) for b in (1, 2, 4, 8, 16, 32)]
-       + [h4096(n, b) for n in (4, 8) for b in (1, 2, 4, 8, 16, 32, 64)] + [MOE]}
+       + [h4096(n, b) for n in (4, 8) for b in (1, 2, 4, 8, 16, 32, 64)] + [MOE, PREFILL]}
