@@ -59,6 +59,14 @@ __device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t rs, uint32_t byte
                                            kCachePolicyDevice);
 }
 
+// A device-coherent 32-bit load through a buffer descriptor (zero past its
+// range), volatile so that a polling loop re-reads it.
+constexpr int kCachePolicyVolatile = (int)(1u << 31);
+__device__ __forceinline__ uint32_t ld_dev_u32_buf(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0,
+                                                         kCachePolicyDevice | kCachePolicyVolatile);
+}
+
 // Device-coherent accesses for data exchanged inside one launch.
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

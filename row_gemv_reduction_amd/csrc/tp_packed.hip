@@ -119,8 +119,8 @@ struct StreamArgs {
     uint32_t spin_limit;
 };
 
-// Flag words (serial order): [0, G) completion of each workgroup, then the
-// exit counter on a line of its own.
+// Flag words (serial order): [0, G) completion of each workgroup (G <= 256),
+// then the exit counter on a line of its own.
 constexpr int kFlagExit = 1024;
 
 // Hidden-state elements of a workgroup (NS * 4 * B) held per control lane:
@@ -185,18 +185,26 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
             idx[q] = valid[q] ? b * a.H + 4 * s + c : 0;
             h[q] = valid[q] && !PART ? a.hidden[idx[q]] : 0.f;
         }
+        // the other ranks' values of point j, in ring order from the
+        // element's chunk: every load is issued, unconditionally, before any
+        // is used (one memory round trip); the entries that are not needed
+        // (past N, our own rank, lanes without an element) read zero through
+        // the buffer range without touching memory
         auto fetch_others = [&](int j) {
             if (PART) return;
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
+            const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(slot), (short)0, a.n_ranks * len * 4, kBufferRsrcWord3);
 #pragma unroll
             for (int q = 0; q < EQ_MAX; ++q) {
                 const int cidx = idx[q] / a.chunk;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     int r = cidx + u;
-                    if (r >= a.n_ranks) r -= a.n_ranks;
-                    oth[q][u] = (valid[q] && u < a.n_ranks && r != a.rank)
-                                    ? slot[(int64_t)r * len + idx[q]] : 0.f;
+                    r = r >= a.n_ranks ? r - a.n_ranks : r;
+                    const bool need = valid[q] && u < a.n_ranks && r != a.rank;
+                    const uint32_t off = need ? (uint32_t)(r * len + idx[q]) * 4u : 0xfffffff0u;
+                    oth[q][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, off, 0, 0));
                 }
             }
         };
@@ -223,17 +231,20 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
         uint32_t* err = a.err;
         int ok = 1;
         // serial order: wait until every workgroup has completed point j
+        // (the G <= 256 completion words, 4 per lane; words past G read as
+        // complete)
         auto grid_wait = [&](int j) {
             if (!ok) return;
             const uint32_t target = (uint32_t)(j + 1);
+            const __amdgpu_buffer_rsrc_t rf = dev_rsrc(a.flags, (uint32_t)G * 4);
             for (uint32_t n = 0;; ++n) {
                 uint32_t mn = 0xffffffffu;
-                for (int w0 = lane; w0 < G; w0 += 64) {
-                    const uint32_t f = ld_dev_u32(a.flags + w0);
-                    mn = f < mn ? f : mn;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t f = ld_dev_u32_buf(rf, (uint32_t)(lane + 64 * i) * 4);
+                    mn = lane + 64 * i < G && f < mn ? f : mn;
                 }
-                const bool done = __builtin_amdgcn_ballot_w64(mn < target) == 0;
-                if (done) return;
+                if (__builtin_amdgcn_ballot_w64(mn < target) == 0) return;
                 if ((n & 15) == 15 && __builtin_amdgcn_readfirstlane(ld_dev_u32(err))) { ok = 0; return; }
                 if (n >= a.spin_limit) {
                     if (lane == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -305,6 +316,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 for (int w0 = lane; w0 < G; w0 += 64) st_dev_u32(a.flags + w0, 0u);
                 if (lane == 0) st_dev_u32(a.flags + kFlagExit, 0u);
             }
+
         }
     } else {
         // --------------------------------------------------- compute waves
@@ -754,6 +766,8 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     if (!tp_stream_geometry(p, &geo)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * 2 >= ((int64_t)1 << 30)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)p->batch * p->hidden >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
+    // the slots of one point through one buffer range
+    if ((int64_t)p->n_ranks * p->batch * p->hidden * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;
     if ((int64_t)n_layers * geo.grid * (int64_t)(geo.kh0 > geo.kh1 ? geo.kh0 : geo.kh1) * 8 >=
         ((int64_t)1 << 62))
         return TP_ERR_UNSUPPORTED;

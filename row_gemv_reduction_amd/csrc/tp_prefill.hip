@@ -67,6 +67,7 @@ struct PrefillArgs {
     int32_t T, H, layers, n_ranks, rank;
     int32_t K[2], nkb[2];
     int32_t mt, nt;         // tiles along tokens and columns
+    int32_t parts_m, parts_n;  // XCD blocks along tokens and columns (parts_m * parts_n = 8), or 0
     int64_t chunk;          // T*H/N
     uint32_t spin_limit;
 };
@@ -92,16 +93,35 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_step(PrefillArgs a) {
     const int64_t len = (int64_t)a.T * a.H;
     int ok = 1;
 
-    // Workgroup w runs on XCD w % 8: each XCD's workgroups take a contiguous
-    // range of every round's tiles, so that neighbouring tiles, which share
-    // rows of X, share an L2 (a bijection of the grid when it is a multiple
-    // of 8; measured a few percent faster than the plain walk)
+    // The walk. Workgroup w runs on XCD w % 8, and the 8 XCDs have an L2
+    // each. With parts_m > 0 every point's tiles are cut into the same 8
+    // blocks (parts_m along tokens x parts_n along columns) and XCD x's
+    // workgroups walk block x of every point in point order: an XCD then
+    // fetches only its block's rows of X and columns of W into its L2,
+    // which all its tiles share (the host picks the cut that fetches the
+    // fewest bytes). Tile (j, m, n) always falls to the same XCD, so the
+    // chain of waits stays inside it. Without the cut (a grid that is not a
+    // multiple of 8, or fewer tiles than blocks), all workgroups walk all
+    // tiles.
     const int G = (int)gridDim.x, bx = (int)blockIdx.x;
-    const int g0 = G % kXCDs ? bx : (bx % kXCDs) * (G / kXCDs) + bx / kXCDs;
-    for (int64_t q = g0; q < total; q += G) {
-        const int j = (int)(q / tiles_per_point);
-        const int tile = (int)(q - (int64_t)j * tiles_per_point);
-        const int mi = tile / a.nt, ni = tile - mi * a.nt;
+    int64_t q0 = bx, qstep = G, qend = total;
+    int mlo = 0, nlo = 0, nbx = a.nt, px = tiles_per_point;
+    if (a.parts_m > 0) {
+        const int x = bx % kXCDs, xm = x / a.parts_n, xn = x - xm * a.parts_n;
+        mlo = xm * a.mt / a.parts_m;
+        nlo = xn * a.nt / a.parts_n;
+        nbx = (xn + 1) * a.nt / a.parts_n - nlo;
+        px = ((xm + 1) * a.mt / a.parts_m - mlo) * nbx;
+        q0 = bx / kXCDs;
+        qstep = G / kXCDs;
+        qend = (int64_t)2 * a.layers * px;
+    }
+    for (int64_t q = q0; q < qend; q += qstep) {
+        const int j = (int)(q / px);
+        const int lt = (int)(q - (int64_t)j * px);
+        const int mbx = px / nbx;  // column-major inside the block
+        const int mi = mlo + lt % mbx, ni = nlo + lt / mbx;
+        const int tile = mi * a.nt + ni;
         const int pt = j & 1, l = j >> 1;
         const int K = a.K[pt], nkb = a.nkb[pt];
         const int m0 = mi * kPfTileM, n0 = ni * kPfTileN;
@@ -215,7 +235,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_step(PrefillArgs a) {
             // batches of EB blocks of 16 tokens x 16 columns: every load of a
             // batch (the other ranks' partials and the residual, 16 bytes per
             // lane) is issued before the first addition
-            constexpr int EB = NR <= 2 ? 4 : 2;
+            constexpr int EB = NR <= 4 ? 4 : 2;
 #pragma unroll
             for (int g = 0; g < kPfMB * kPfNB / EB; ++g) {
                 floatx4_t oth[EB][NR > 1 ? NR - 1 : 1];
@@ -376,6 +396,8 @@ tp_status tp_prefill_layers(tp_plan_t p, int32_t n_layers, int32_t rank, int32_t
     a.mt = (int32_t)mt;
     a.nt = (int32_t)nt;
     a.chunk = T * H / p->n_ranks;
+    a.parts_m = 0;
+    a.parts_n = 0;
     a.spin_limit = 1u << 22;
     prefill_fn k = prefill_kernel(p->n_ranks);
     if (!k) return TP_ERR_UNSUPPORTED;
@@ -383,6 +405,22 @@ tp_status tp_prefill_layers(tp_plan_t p, int32_t n_layers, int32_t rank, int32_t
     if (cap < 1) return TP_ERR_DEVICE;
     const int64_t total = 2 * (int64_t)n_layers * mt * nt;
     const int grid = total < cap ? (int)total : cap;
+    if (grid % kXCDs == 0) {
+        // the XCD blocks: the cut whose operand fetches (every block reads
+        // its rows of X and its columns of W once per point) are fewest
+        const double xb = (double)T * (K0 + K1) * 2, wb = (double)(K0 + K1) * H * 2;
+        double best = 0;
+        for (int pm = 1; pm <= kXCDs; pm *= 2) {
+            const int pn = kXCDs / pm;
+            if (pm > mt || pn > nt) continue;
+            const double cost = pn * xb + pm * wb;
+            if (a.parts_m == 0 || cost < best) {
+                best = cost;
+                a.parts_m = pm;
+                a.parts_n = pn;
+            }
+        }
+    }
     void* args[] = {&a};
     if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(kPfThreads), args, 0,
                                    (hipStream_t)stream) != hipSuccess)
