@@ -82,6 +82,7 @@ struct tp_plan_s {
     int32_t segment_loads = 0;  // 16-byte loads per lane per bank of the streamed step (0 = 4)
     int32_t serial_points = 0;  // decode step: point j+1 waits for all of point j
     int32_t stream_kind = 0;    // 0 = automatic, 1 = pair strips (VALU), 2 = MFMA tiles
+    int32_t stream_flat = -1;   // pair-strip stream, dataflow order: banks across points (1) or a point per bank (0); -1 = automatic
     int32_t moe_variant = 0;    // expert kernel variant (0 = default)
     int32_t stream_wgs = 0;     // MFMA stream: workgroups (0 = one per CU, at most H/16)
     int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)

@@ -338,6 +338,9 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "stream_kind")) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->stream_kind = (int32_t)value;
+    } else if (!strcmp(key, "stream_flat")) {
+        if (value < -1 || value > 1) return TP_ERR_INVALID_ARG;
+        p->stream_flat = (int32_t)value;
     } else if (!strcmp(key, "stream_wgs")) {
         if (value < 0 || value > kTargetCUs) return TP_ERR_INVALID_ARG;
         p->stream_wgs = (int32_t)value;

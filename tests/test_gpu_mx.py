@@ -171,8 +171,19 @@ def test_mx_decode_matches_oracle(fmt, n, b, h, ka, ki, rank):
         assert tp.tp_workspace_status(plan, ws) == 0
         outs.append((host(S), host(Hd)))
     plan.tune("serial_points", 0)
-    assert_bits_equal(outs[1][0], outs[0][0], "slots, serial vs dataflow")
-    assert_bits_equal(outs[1][1], outs[0][1], "hidden, serial vs dataflow")
+    # the dataflow order with a point per bank and with banks across points
+    for flat in (0, 1):
+        plan.tune("stream_flat", flat)
+        ws = plan.new_workspace()
+        S, Hd = torch.from_numpy(slots).cuda(), torch.from_numpy(h0).cuda()
+        tp.tp_decode_layers_packed(plan, L, rank, XA, po, XF, pd, S, Hd, ws)
+        torch.cuda.synchronize()
+        assert tp.tp_workspace_status(plan, ws) == 0
+        outs.append((host(S), host(Hd)))
+    plan.tune("stream_flat", -1)
+    for o, what in ((outs[1], "serial"), (outs[2], "a point per bank"), (outs[3], "banks across points")):
+        assert_bits_equal(o[0], outs[0][0], "slots, %s vs dataflow" % what)
+        assert_bits_equal(o[1], outs[0][1], "hidden, %s vs dataflow" % what)
     s_gpu, h_gpu = outs[0]
     # no-alloc form and partials-only form: the same bits
     S2, H2 = torch.from_numpy(slots).cuda(), torch.from_numpy(h0).cuda()

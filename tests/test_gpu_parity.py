@@ -825,10 +825,15 @@ def test_packed_decode_bit_exact_when_partials_are_exact(kind, n, b, h, ka, ki, 
     say("packed decode exact kind=%d n=%d b=%d h=%d rank=%d wgs=%d" % (kind, n, b, h, rank, wgs))
     plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind, "stream_wgs": wgs})
     assert plan.info()["packed_kind"] == kind
-    s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
     s_or, h_or = oracle.decode_layers(rank, xa, wo, xf, wd, slots, h0)
-    assert_bits_equal(s_gpu, s_or, "slots")
-    assert_bits_equal(h_gpu, h_or, "hidden")
+    # the vector-ALU stream's two ways of banking its loads (a point per
+    # bank, banks across points), each bit for bit
+    for flat in ((-1, 0, 1) if kind == 1 else (-1,)):
+        plan.tune("stream_flat", flat)
+        s_gpu, h_gpu = run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0)
+        assert_bits_equal(s_gpu, s_or, "slots flat=%d" % flat)
+        assert_bits_equal(h_gpu, h_or, "hidden flat=%d" % flat)
+    plan.tune("stream_flat", -1)
 
 
 FULL_SIZE = [
