@@ -149,4 +149,32 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// LDS word loads/stores that the compiler neither caches nor reorders with
+// respect to each other (flags between the waves of one workgroup).
+__device__ __forceinline__ int lds_ld(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_add(int* p, int v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// This wave's LDS accesses have completed (and a compiler barrier).
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until the LDS flag reaches `target`. Bounded (far beyond any real
+// wait): on timeout bit 1 of the error word is set and the wave goes on, so
+// the launch always ends.
+constexpr int kWaveSpinLimit = 1 << 22;
+__device__ __forceinline__ void wait_flag(const int* f, int target, uint32_t* err) {
+    for (int n = 0; lds_ld(f) < target; ++n) {
+        if (n >= kWaveSpinLimit) {
+            __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 }  // namespace tpdev

@@ -115,7 +115,8 @@ struct StreamArgs {
     int32_t bpw0, bpw1;     // row blocks per compute wave per point (same for every wave)
     int32_t layers, n_ranks, rank, chunk;
     int32_t xoff1;          // dword offset of the second x buffer in LDS
-    int32_t xdwords;        // total LDS dwords of the two x buffers
+    int32_t xdwords;        // total LDS dwords of the x buffers
+    int32_t xpair;          // FLAT: dword offset of the second pair of x buffers
     uint32_t spin_limit;
 };
 
@@ -146,20 +147,31 @@ __device__ __forceinline__ float mx_scale_f32(uint32_t e) { return __uint_as_flo
 // rows per column; with MX weights every 32 rows of a column share a scale.
 template <int B, int SL, bool SERIAL, bool PART = false, int WF = TP_WEIGHTS_BF16, bool FLAT = false>
 __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs a) {
-    extern __shared__ __align__(16) uint32_t xs[];             // two x buffers, bf16 pairs
-    __shared__ float red[2][kStreamMaxWaves - 1][B * 4];        // per point parity
+    extern __shared__ __align__(16) uint32_t xs[];             // x buffers, bf16 pairs
+    // the compute waves' sums of a point: per point parity, or (FLAT) per
+    // point mod 4
+    constexpr int NRED = FLAT ? 4 : 2;
+    __shared__ float red[NRED][kStreamMaxWaves - 1][B * 4];
+    // FLAT: arrivals of the compute waves per red buffer, points consumed by
+    // the control wave, points whose x is staged
+    __shared__ int fl[6];
+    constexpr int kFlConsumed = 4, kFlXready = 5;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = blockIdx.x, G = gridDim.x;
     const int n_points = 2 * a.layers;
     const int len = B * a.H;
-    // the LDS x buffer of point j: one per kind
-    auto xoff_of = [&](int j) { return (j & 1) ? a.xoff1 : 0; };
+    // the LDS x buffer of point j: one per kind, or (FLAT) two per kind,
+    // used by every other point of that kind
+    auto xoff_of = [&](int j) {
+        return (j & 1 ? a.xoff1 : 0) + (FLAT && (j & 2) ? a.xpair : 0);
+    };
 
-    // zero both x buffers: rows past a point's K are multiplied by zero
+    // zero the x buffers: rows past a point's K are multiplied by zero
     // weights and must hold finite values
     for (int i = tid; i < a.xdwords; i += blockDim.x) xs[i] = 0u;
+    if (tid < 6) fl[tid] = 0;
     __syncthreads();
 
     if (wave == 0) {
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
         // is used (one memory round trip); the entries that are not needed
         // (past N, our own rank, lanes without an element) read zero through
         // the buffer range without touching memory
-        auto fetch_others = [&](int j) {
+        auto fetch_others = [&](int j, float (&oth)[EQ_MAX][8]) {
             if (PART) return;
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
             const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
@@ -251,14 +263,10 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
             }
         };
 
-        stage_x(0);
-        if (!SERIAL && n_points > 1) stage_x(1);
-        fetch_others(0);
-        wait_mem();
-        __syncthreads();  // start: x of the first point(s) is in LDS
-
-        for (int j = 0; j < n_points; ++j) {
-            __syncthreads();  // P_j: the compute waves' sums of point j are in red[j & 1]
+        // point j's partial from the compute waves' sums in red[rb], to the
+        // rank's slot, then the ring-order sum of the N ranks' values plus the
+        // residual
+        auto ring = [&](int j, int rb, const float (&oth)[EQ_MAX][8]) {
             float* slot = PART ? a.slots + (int64_t)j * len
                                : a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
 #pragma unroll
@@ -267,8 +275,8 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 if (!valid[q]) continue;
                 const int e = lane + 64 * q;
                 const int c = e & 3, si = (e >> 2) % a.NS, b = (e >> 2) / a.NS;
-                float v = red[j & 1][si * a.WPS][b * 4 + c];
-                for (int wi = 1; wi < a.WPS; ++wi) v += red[j & 1][si * a.WPS + wi][b * 4 + c];
+                float v = red[rb][si * a.WPS][b * 4 + c];
+                for (int wi = 1; wi < a.WPS; ++wi) v += red[rb][si * a.WPS + wi][b * 4 + c];
                 slot[idx[q]] = v;
                 if (PART) continue;
                 // ring order: chunk c starts at rank c, then c+1, ... (mod N)
@@ -285,7 +293,58 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 }
                 h[q] = sum + h[q];
             }
-            if (j + 1 < n_points) fetch_others(j + 1);
+        };
+
+        if constexpr (FLAT) {
+            // The compute waves deposit each point's sums in red[j % 4] and
+            // count themselves; nothing meets at a barrier. After point j's
+            // ring sum the wave issues x of point j+4 (into point j's buffer:
+            // every compute wave is done with it) and then the other ranks'
+            // values of point j+2, into the register set point j used. The
+            // ring sum of point j+2 waits for those values, and so (loads
+            // complete in order) for that x too: x of point j+4 is marked
+            // staged after it. Two points of work cover every round trip.
+            const int ncw = (int)(blockDim.x / 64) - 1;
+            const int npre = n_points < 4 ? n_points : 4;
+            float othA[EQ_MAX][8], othB[EQ_MAX][8];
+            for (int j = 0; j < npre; ++j) stage_x(j);
+            fetch_others(0, othA);
+            if (n_points > 1) fetch_others(1, othB);
+            wait_mem();
+            if (lane == 0) lds_st(&fl[kFlXready], npre);
+            __syncthreads();  // start
+            auto point = [&](int j, float (&o)[EQ_MAX][8]) {
+                wait_flag(&fl[j & 3], ncw * (j / 4 + 1), a.err);  // every compute wave's sums of point j
+                lds_wait();
+                ring(j, j & 3, o);
+                // the values are in (their first load waited for, and so
+                // everything issued before it)
+                asm volatile("" ::"v"(o[0][0]) : "memory");
+                lds_wait();
+                if (lane == 0) {
+                    lds_st(&fl[kFlConsumed], j + 1);  // red[j % 4] may be refilled
+                    // x of point j+2 (issued before the values just used)
+                    if (j >= 2 && j + 2 < n_points) lds_st(&fl[kFlXready], j + 3);
+                }
+                if (j + 4 < n_points) stage_x(j + 4);
+                if (j + 2 < n_points) fetch_others(j + 2, o);
+            };
+            for (int j = 0; j < n_points; j += 2) {
+                point(j, othA);
+                if (j + 1 < n_points) point(j + 1, othB);
+            }
+            wait_mem();
+        } else {
+        stage_x(0);
+        if (!SERIAL && n_points > 1) stage_x(1);
+        fetch_others(0, oth);
+        wait_mem();
+        __syncthreads();  // start: x of the first point(s) is in LDS
+
+        for (int j = 0; j < n_points; ++j) {
+            __syncthreads();  // P_j: the compute waves' sums of point j are in red[j & 1]
+            ring(j, j & 1, oth);
+            if (j + 1 < n_points) fetch_others(j + 1, oth);
             if (SERIAL) {
                 if (j + 1 < n_points) {
                     wait_mem();
@@ -299,6 +358,7 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 if (j + 2 < n_points) stage_x(j + 2);
                 wait_mem();  // x staged before P_{j+1}; needed from P_{j+1} on
             }
+        }
         }
 #pragma unroll
         for (int q = 0; q < EQ_MAX; ++q)
@@ -460,14 +520,43 @@ __global__ __launch_bounds__(kStreamMaxWaves * 64) void decode_stream(StreamArgs
                 if constexpr (WF != TP_WEIGHTS_BF16) sv = load_s(rsc, c.m);
                 step(c);
             };
+            // a point's end without a barrier: the sums go to red[j % 4] once
+            // the control wave has consumed point j-4, and the wave counts
+            // itself in that buffer's arrivals
+            auto deposit = [&](int j) {
+                float v[B][4];
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        v[b][c] = wave_sum(acc[b][c]);
+                        acc[b][c] = 0.f;
+                    }
+                wait_flag(&fl[kFlConsumed], j - 3, a.err);
+                lds_wait();
+                if (lane == 0) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) red[j & 3][cw][b * 4 + c] = v[b][c];
+                }
+                lds_wait();
+                if (lane == 0) lds_add(&fl[j & 3], 1);
+            };
+            int xchk = -1;  // the last point whose x was seen staged
             auto consume = [&](u32x4_t (&bank)[SL], uint32_t (&sbank)[SL], Pos& c, Pos& ci) {
 #pragma unroll
                 for (int i = 0; i < SL; ++i) {
                     const int j = c.j, t = j & 1;
+                    if (j > xchk && j < n_points) {
+                        wait_flag(&fl[kFlXready], j + 1, a.err);  // x of point j is in LDS
+                        lds_wait();
+                        xchk = j;
+                    }
                     block(bank[i], sbank[i], xs + xoff_of(j), t ? a.Kh1 : a.Kh0, t ? a.Kv1 : a.Kv0, c.m);
                     issue(bank[i], sbank[i], ci);
                     step(c);
-                    if (c.j != j && j < n_points) point_end(j);  // the point's last block
+                    if (c.j != j && j < n_points) deposit(j);  // the point's last block
                 }
             };
             Pos ci{0, 0}, cc{0, 0};
@@ -853,7 +942,14 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     // the dataflow order takes the stream block by block across points where
     // a layer's blocks fit one bank (small points: measured up to 33 %
     // faster; larger points, up to 5 % slower that way, keep a point per bank)
-    const bool flat = p->stream_flat >= 0 ? p->stream_flat == 1 : geo.bpw0 + geo.bpw1 <= geo.sl;
+    // FLAT keeps two x buffers per kind
+    const bool flat = !serial && !partials && 2 * (int64_t)geo.lds_bytes <= kStreamMaxLdsBytes &&
+                      (p->stream_flat >= 0 ? p->stream_flat == 1 : geo.bpw0 + geo.bpw1 <= geo.sl);
+    const int32_t xpair = geo.xdwords;
+    if (flat) {
+        geo.xdwords *= 2;
+        geo.lds_bytes *= 2;
+    }
     stream_fn k = stream_kernel(p->batch, geo.sl, partials ? 2 : serial ? 1 : flat ? 3 : 0, p->weight_format);
     if (!k) return TP_ERR_UNSUPPORTED;
     StreamArgs a;
@@ -888,6 +984,7 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     a.chunk = (int32_t)((int64_t)p->batch * p->hidden / p->n_ranks);
     a.xoff1 = geo.xoff1;
     a.xdwords = geo.xdwords;
+    a.xpair = xpair;
 
     a.spin_limit = 1u << 20;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
