@@ -674,27 +674,30 @@ def moe_run(args, w, tune):
                    moe=dict(n_experts=E, top_k=k, ep=ep, moe_inter=I, max_tokens=T))
     copies = 3  # 3 x ~400 MB of distinct weights per rotation: more than the 256 MB cache
     layers, slots, h0 = moe_build(w, rank, copies)
-    for L in layers:  # load-time expert packing (untimed)
+    for L in layers:  # load-time packing of the experts and the attention slice (untimed)
         L["wp"] = torch.empty(tp.moe_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
         tp.tp_moe_pack_experts(plan, L["we"], L["wp"])
         del L["we"]
+        L["wap"] = torch.empty(tp.moe_attn_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
+        tp.tp_moe_pack_attn(plan, L["wo"], L["wap"])
     torch.cuda.synchronize()
     ws = plan.new_workspace()
     hidden = h0.clone()
     se = torch.empty((T, k), dtype=torch.int32, device="cuda")
     sw = torch.empty((T, k), dtype=torch.float32, device="cuda")
     it = [0]
+    stream = torch.cuda.current_stream()
 
     def step():
+        # the whole layer share: routing, the attention slice and the
+        # rank's experts in one launch, both ring sums in a second
         c = it[0] % copies
         it[0] += 1
         L = layers[c]
-        tp.tp_decode_point(plan, 0, rank, L["xa"], L["wo"], slots[c, 0], hidden, ws)
-        tp.tp_moe_route(plan, L["logits"], se, sw)
-        tp.tp_moe_decode(plan, rank, se, sw, L["u"], L["wp"], slots[c, 1], hidden, ws)
+        tp.tp_moe_layer_decode(plan, rank, L["logits"], L["xa"], L["wap"], L["u"], L["wp"], se, sw,
+                               slots[c, 0], slots[c, 1], hidden, ws)
 
-    ms = time_steps(step, args.steps, args.warmup, torch.cuda.current_stream(),
-                    ws_check(plan, ws, "MoE share"))
+    ms = time_steps(step, args.steps, args.warmup, stream, ws_check(plan, ws, "MoE layer share"))
     # algorithmic bytes of one layer share (averaged over the rotated copies)
     el = E // ep
     step_bytes = 0
@@ -718,10 +721,11 @@ def moe_run(args, w, tune):
     config = {"workload": w.name, "hidden": H, "k_attn": w.k_attn, "n_ranks": w.n_ranks,
               "rank": rank, "tokens": T, "n_experts": E, "top_k": k, "ep": ep, "moe_inter": I,
               "layers": 1, "active_local_experts_mean": active_total / copies,
-              "weight_layout": "row-major attention slice, experts packed as MFMA tiles",
+              "weight_layout": "attention slice and experts packed as MFMA tiles",
+              "timing": "eager, tp_moe_layer_decode: two launches per step",
               "weight_copies_rotated": copies}
-    kernel = ("MoE layer share (attention slice: MFMA projection with the ring sum in its split-K "
-              "fix-up; routing; expert MFMA GEMV; combine + ring sum)")
+    kernel = ("tp_moe_layer_decode: moe_layer_kernel (routing, attention slice and expert MFMA "
+              "GEMV in one launch) + moe_layer_combine_kernel (local combine, both ring sums)")
     reduce_io = 2 * (w.n_ranks + 2) * T * H * 4
     extra = {"reduce_io_bytes": reduce_io}
     plan.close()

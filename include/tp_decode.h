@@ -649,6 +649,49 @@ tp_status tp_moe_decode(tp_plan_t plan, int32_t rank, const int32_t* sel_expert,
                         float* slots, float* hidden, void* workspace, void* stream);
 
 /*
+ * Pack the rank's attention output slice for tp_moe_layer_decode, once, at
+ * load time: w bf16 [k_attn/N][hidden] (row-major) -> w_packed bf16
+ * [hidden/16][ceil(k_attn/N / 64)][1024], the tile layout of
+ * tp_moe_pack_experts for a single matrix. TP_ERR_INVALID_ARG if the plan
+ * has no MoE share or no attention dimension; TP_ERR_UNSUPPORTED if hidden
+ * is not a multiple of 16.
+ */
+tp_status tp_moe_pack_attn(tp_plan_t plan, const void* w, void* w_packed, void* stream);
+
+/*
+ * One MoE layer's whole decode share for rank `rank` ("Hosting Qwen on
+ * Blackwell", MoE Dispatch-Combine and Expert Parallel; lesson 9.9,
+ * Conceito, for the two ring sums), for the plan's batch of T tokens:
+ *   1. routing (tp_moe_route): sel_expert, sel_weight [T][top_k] written;
+ *   2. the attention output slice's partial x_attn . W_attn into
+ *      slots_attn[rank], then hidden <- ring_sum(slots_attn) + hidden;
+ *   3. the rank's experts and local combine (tp_moe_partial) into
+ *      slots_moe[rank], then hidden <- ring_sum(slots_moe) + hidden.
+ *   logits fp32 [T][n_experts]; x_attn bf16 [T][k_attn/N];
+ *   w_attn_packed: tp_moe_pack_attn's tiles; u bf16 [T][top_k][moe_inter];
+ *   w_packed: tp_moe_pack_experts's tiles; slots_attn, slots_moe fp32
+ *   [N][T][hidden] (entry [rank] of each overwritten); hidden fp32
+ *   [T][hidden] in/out.
+ * Two launches: routing, the attention slice and the experts share one
+ * (the expert workgroups wait, bounded, for the routing workgroups, which
+ * come first in dispatch order; a timeout sets bit 0 of the workspace's
+ * error word), and one for both ring sums. The routing equals
+ * tp_moe_route's and slots_moe[rank] tp_moe_partial's bit for bit; the
+ * attention partial accumulates each column in fp32 over 64-row tiles
+ * split among four waves, then sums the waves in order; both ring stages
+ * equal tp_ring_reduce's bit for bit given the same slots. Calls that
+ * overlap on one workspace race. TP_ERR_INVALID_ARG also if ep != n_ranks,
+ * batch > max_tokens or the plan has no attention dimension;
+ * TP_ERR_UNSUPPORTED if n_experts > 512, top_k > 64, moe_inter or
+ * k_attn/N is not a multiple of 8, or hidden not a multiple of 16.
+ */
+tp_status tp_moe_layer_decode(tp_plan_t plan, int32_t rank, const float* logits, int32_t renorm,
+                              const void* x_attn, const void* w_attn_packed, const void* u,
+                              const void* w_packed, int32_t* sel_expert, float* sel_weight,
+                              float* slots_attn, float* slots_moe, float* hidden,
+                              void* workspace, void* stream);
+
+/*
  * Measurement: the device's streaming-read ceiling. Reads `bytes` of `buf`
  * with 16-byte nontemporal loads (the access the decode kernels make of
  * their weights: "Hosting Qwen on Blackwell", Decoders, a decode matmul

@@ -100,6 +100,9 @@ EXPORTS = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]),
     "tp_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 8),
+    "tp_moe_pack_attn": (ctypes.c_int, [ctypes.c_void_p] * 4),
+    "tp_moe_layer_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32]
+                            + [ctypes.c_void_p] * 11),
     "tp_prefill_pack_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
                                 + [ctypes.c_void_p] * 3),
     "tp_prefill_layers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
@@ -552,6 +555,46 @@ def tp_moe_decode(plan: Plan, rank, sel_expert, sel_weight, u, w_packed, slots, 
     if workspace.numel() < i["workspace_bytes"]:
         raise ValueError("workspace too small")
     _check(_lib().tp_moe_decode(plan.handle, rank, *args, _stream()), "tp_moe_decode")
+
+
+def moe_attn_packed_shape(plan: Plan):
+    """Shape of a rank's attention slice packed by tp_moe_pack_attn:
+    [H/16, ceil(k_attn/N / 64), 1024] (bf16)."""
+    i = plan._plan_info()
+    return (i["hidden"] // 16, (i["k_attn"] // i["n_ranks"] + 63) // 64, 1024)
+
+
+def tp_moe_pack_attn(plan: Plan, w, w_packed):
+    i = plan._plan_info()
+    ka = i["k_attn"] // i["n_ranks"]
+    _check(_lib().tp_moe_pack_attn(plan.handle, _dev(w, "w", torch.bfloat16, (ka, i["hidden"])),
+                                   _dev(w_packed, "w_packed", torch.bfloat16, moe_attn_packed_shape(plan)),
+                                   _stream()), "tp_moe_pack_attn")
+
+
+def tp_moe_layer_decode(plan: Plan, rank, logits, x_attn, w_attn_packed, u, w_packed, sel_expert,
+                        sel_weight, slots_attn, slots_moe, hidden, workspace, renorm=True):
+    """One MoE layer's decode share: routing, the attention slice's partial into
+    slots_attn[rank] and its ring sum into hidden, the rank's experts into
+    slots_moe[rank] and their ring sum into hidden."""
+    i = plan._plan_info()
+    n, b, k, mi, H = i["n_ranks"], i["batch"], i["top_k"], i["moe_inter"], i["hidden"]
+    ka = i["k_attn"] // n
+    lg = _dev(logits, "logits", torch.float32, (b, i["n_experts"]))
+    args = (_dev(x_attn, "x_attn", torch.bfloat16, (b, ka)),
+            _dev(w_attn_packed, "w_attn_packed", torch.bfloat16, moe_attn_packed_shape(plan)),
+            _dev(u, "u", torch.bfloat16, (b, k, mi)),
+            _dev(w_packed, "w_packed", torch.bfloat16, moe_packed_shape(plan)),
+            _dev(sel_expert, "sel_expert", torch.int32, (b, k)),
+            _dev(sel_weight, "sel_weight", torch.float32, (b, k)),
+            _dev(slots_attn, "slots_attn", torch.float32, (n, b, H)),
+            _dev(slots_moe, "slots_moe", torch.float32, (n, b, H)),
+            _dev(hidden, "hidden", torch.float32, (b, H)),
+            _dev(workspace, "workspace", torch.uint8))
+    if workspace.numel() < i["workspace_bytes"]:
+        raise ValueError("workspace too small")
+    _check(_lib().tp_moe_layer_decode(plan.handle, rank, lg, 1 if renorm else 0, *args, _stream()),
+           "tp_moe_layer_decode")
 
 
 def tp_stream_read_probe(buf, sink):

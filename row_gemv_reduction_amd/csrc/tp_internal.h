@@ -17,6 +17,7 @@ constexpr int kCounterStride = 16;            // one counter per 64-byte line
 constexpr int kMaxCounters = 1024;            // column-tile arrival counters (64 KiB)
 constexpr int64_t kSyncOffset = 64 * 1024;    // step sync words: done, exit, error
 constexpr int kSyncDone = 0, kSyncExit = 16, kSyncErr = 32;
+constexpr int kSyncMoeRoute = 48;  // MoE layer share: routing workgroups done
 // Persistent row-major decode step (decode_step): points completed per
 // column tile (stride kCounterStride), the x slice of a tile staged in LDS,
 // the split buffer / arrival counter sets (points in flight), and the

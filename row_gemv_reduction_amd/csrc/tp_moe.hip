@@ -83,14 +83,13 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-template <int EPL>  // experts per lane (E <= 64 * EPL)
-__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int tokens,
-                                                        int E, int top_k, int renorm,
-                                                        int32_t* __restrict__ sel_expert,
-                                                        float* __restrict__ sel_weight) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= tokens) return;
+// Token t's routing by one wave (lane = its lane). COHERENT: the
+// selections are stored at device scope (sc1), for workgroups of the same
+// launch on other XCDs.
+template <int EPL, bool COHERENT>  // experts per lane (E <= 64 * EPL)
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int top_k,
+                                            int renorm, int32_t* sel_expert, float* sel_weight,
+                                            int lane) {
     const float* z = logits + (int64_t)t * E;
     float zl[EPL];
     uint32_t taken = 0;
@@ -143,9 +142,25 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         rank += es < my_e;
     }
     if (mine) {
-        sel_expert[(int64_t)t * top_k + rank] = my_e;
-        sel_weight[(int64_t)t * top_k + rank] = (float)(p / denom);
+        const int64_t q = (int64_t)t * top_k + rank;
+        if (COHERENT) {
+            st_dev_u32(reinterpret_cast<uint32_t*>(sel_expert + q), (uint32_t)my_e);
+            st_dev(sel_weight + q, (float)(p / denom));
+        } else {
+            sel_expert[q] = my_e;
+            sel_weight[q] = (float)(p / denom);
+        }
     }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int tokens,
+                                                        int E, int top_k, int renorm,
+                                                        int32_t* __restrict__ sel_expert,
+                                                        float* __restrict__ sel_weight) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= tokens) return;
+    route_token<EPL, false>(logits, t, E, top_k, renorm, sel_expert, sel_weight, threadIdx.x & 63);
 }
 
 typedef void (*route_fn)(const float*, int, int, int, int, int32_t*, float*);
@@ -173,48 +188,147 @@ struct ExpertArgs {
 
 constexpr int kMoeTileBytes = 2048;  // 64 rows x 16 columns of bf16
 
-// One workgroup per (local expert, block of SB 16-column strips). The
-// expert's rows are the pairs that selected it, in ascending pair order
-// (found by scanning the selections: ranks from wave ballots); a pass takes
-// up to 16 of them as the A operand (token m = lane % 16), and row p's
-// projection lands in Y[p] (so the combine needs no table). Wave w takes the row tiles kb = w, w + NW,
-// ... of the expert and, per tile, the block's SB strips in two register
+// One pass of a block of the grouped GEMV: up to 16 A rows, named in LDS by
+// rows[0 .. nr) (A row r is the K bf16 values at a + rows[r] * K; token
+// slot m = lane % 16 of the MFMA), times the block's ns 16-column strips
+// (tiles of nkb 64-row tiles each, in wr). Wave w takes the row tiles
+// kb = w, w + NW, ... and, per tile, the block's SB strips in two register
 // banks of SL = SB/2 tiles, loading each A operand once per 64 rows and the
 // next tile's operands while it multiplies the current ones. The waves' D
-// tiles are then summed in wave order in LDS. Strips past the block's last and rows past the expert's read
-// zero (offsets past the buffer range); A operands of empty token slots and
-// of rows past I are zero.
+// tiles are then summed in wave order in LDS and row r's sums land in
+// out[rows[r] * H + col0 ..]. Strips past the block's last and rows past K
+// read zero (offsets past the buffer range); A operands of empty token slots
+// and of rows past K are zero. after_pass: a previous pass of this
+// workgroup may still read red.
 template <int SB, int NW>
-__global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
+__device__ __forceinline__ void project_pass(__amdgpu_buffer_rsrc_t wr, int ns, int nkb, int K,
+                                             const uint16_t* __restrict__ a, const int* rows, int nr,
+                                             float* __restrict__ out, int H, int col0, float* red,
+                                             bool after_pass) {
     constexpr int SL = SB / 2;
-    constexpr int NT = NW * 64;
-    __shared__ __align__(16) float red[NW * SB * 256];  // [NW][SB][64][4] D tiles
-    __shared__ int rows[16];                            // the pass's pairs
-    __shared__ int wcount[NW];
-    __shared__ int s_rows;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int le = blockIdx.x / a.col_blocks, cb = blockIdx.x % a.col_blocks;
+    const int past = ns * nkb * kMoeTileBytes;  // an offset past the range: reads zero
+    const int nkw = nkb > wave ? (nkb - wave + NW - 1) / NW : 0;  // this wave's row tiles
+    const int g16 = 16 * (lane >> 4);
+    const int m = lane & 15;
+    const int pr = m < nr ? rows[m] : -1;
+    const uint16_t* up = a + (int64_t)(pr < 0 ? 0 : pr) * K;
+    // B operands of bank j (strips j*SL .. j*SL + SL - 1) of row tile kb (< 0: none)
+    auto issue_w = [&](u32x4_t (&bv)[SL][2], int j, int kb) {
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+            const int s = j * SL + i;
+            const int off = kb >= 0 && s < ns ? (s * nkb + kb) * kMoeTileBytes : past;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                bv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           wr, off + h * 1024 + lane * 16, 0, kCachePolicyNT));
+        }
+    };
+    // A operands of row tile kb: token m, rows 64kb + 16(lane/16) + 8h .. +7
+    auto issue_x = [&](u32x4_t (&xv)[2], int kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k0 = 64 * kb + g16 + 8 * h;
+            xv[h] = kb >= 0 && pr >= 0 && k0 < K ? *reinterpret_cast<const u32x4_t*>(up + k0)
+                                                 : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    floatx4_t acc[SB];
+#pragma unroll
+    for (int s = 0; s < SB; ++s) acc[s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const u32x4_t (&bv)[SL][2], const u32x4_t (&xv)[2], int j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < SL; ++i)
+                acc[j * SL + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, xv[h]), __builtin_bit_cast(bf16x8_t, bv[i][h]),
+                    acc[j * SL + i], 0, 0, 0);
+    };
+    u32x4_t b0[SL][2], b1[SL][2], xa[2], xb[2];
+    const int kb_first = nkw > 0 ? wave : -1;
+    issue_x(xa, kb_first);
+    issue_w(b0, 0, kb_first);
+    issue_w(b1, 1, kb_first);
+    // row tile n of this wave: its operands are in (xc, b0, b1); the next
+    // tile's are loaded behind them into (xn, b0, b1)
+    auto step = [&](u32x4_t (&xc)[2], u32x4_t (&xn)[2], int n) {
+        const int kbn = n + 1 < nkw ? wave + (n + 1) * NW : -1;
+        issue_x(xn, kbn);
+        consume(b0, xc, 0);
+        issue_w(b0, 0, kbn);
+        consume(b1, xc, 1);
+        issue_w(b1, 1, kbn);
+    };
+    int n = 0;
+    for (; n + 1 < nkw; n += 2) {
+        step(xa, xb, n);
+        step(xb, xa, n + 1);
+    }
+    if (n < nkw) step(xa, xb, n);
+    // the waves' D tiles (lane l: tokens 4(l/16) + q of column l % 16),
+    // summed in wave order
+    if (after_pass) __syncthreads();  // the previous pass has read red
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+        *reinterpret_cast<floatx4_t*>(red + (wave * SB + s) * 256 + lane * 4) = acc[s];
+    __syncthreads();
+    for (int idx = tid; idx < ns * nr * 16; idx += NW * 64) {
+        const int s = idx / (nr * 16), rem = idx - s * nr * 16;
+        const int row = rem >> 4, col = rem & 15;
+        const int e = (16 * (row >> 2) + col) * 4 + (row & 3);
+        float v = red[s * 256 + e];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[(w * SB + s) * 256 + e];
+        out[(int64_t)rows[row] * H + col0 + 16 * s + col] = v;
+    }
+}
+
+// LDS of a grouped-GEMV workgroup.
+template <int SB, int NW>
+struct ProjShared {
+    float red[NW * SB * 256];  // [NW][SB][64][4] D tiles
+    int rows[16];              // the pass's rows
+    int wcount[NW];
+    int n_rows;
+    int ok;
+};
+
+// The selection of pair p; COHERENT: written in this launch by another
+// workgroup (device-scope load).
+template <bool COHERENT>
+__device__ __forceinline__ int32_t sel_at(const int32_t* sel, int p) {
+    return COHERENT ? (int32_t)ld_dev_u32(reinterpret_cast<const uint32_t*>(sel + p)) : sel[p];
+}
+
+// Local expert le, block cb of SB 16-column strips: the expert's rows are
+// the pairs that selected it, in ascending pair order (found by scanning
+// the selections: ranks from wave ballots); a pass takes up to 16 of them
+// and row p's projection lands in Y[p] (so the combine needs no table).
+// An expert that no pair selected is not read.
+template <int SB, int NW, bool COHERENT>
+__device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb, ProjShared<SB, NW>& sh) {
+    constexpr int NT = NW * 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int eg = a.e0 + le;
-    if (tid == 0) s_rows = 0;
+    if (tid == 0) sh.n_rows = 0;
     __syncthreads();
     {
         int c = 0;
-        for (int p = tid; p < a.n_pairs; p += NT) c += a.sel[p] == eg;
-        if (c) atomicAdd(&s_rows, c);
+        for (int p = tid; p < a.n_pairs; p += NT) c += sel_at<COHERENT>(a.sel, p) == eg;
+        if (c) atomicAdd(&sh.n_rows, c);
     }
     __syncthreads();
-    const int n_rows = s_rows;
+    const int n_rows = sh.n_rows;
     if (n_rows == 0) return;  // expert not selected by any token: not read
     const int s0 = cb * SB;
     const int ns = a.S16 - s0 < SB ? a.S16 - s0 : SB;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.w) + ((int64_t)le * a.S16 + s0) * a.nkb * (kMoeTileBytes / 2), (short)0,
         ns * a.nkb * kMoeTileBytes, kBufferRsrcWord3);
-    const int past = ns * a.nkb * kMoeTileBytes;  // an offset past the range: reads zero
-    const int nkw = a.nkb > wave ? (a.nkb - wave + NW - 1) / NW : 0;  // this wave's row tiles
-    const int g16 = 16 * (lane >> 4);
-
     for (int r0 = 0; r0 < n_rows; r0 += 16) {
         const int nr = n_rows - r0 < 16 ? n_rows - r0 : 16;
         // the pass's rows: the expert's pairs of rank r0 .. r0 + 15
@@ -222,93 +336,101 @@ __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
         int base = 0;  // matches before the chunk
         for (int c0 = 0; c0 < a.n_pairs && base < r0 + 16; c0 += NT) {
             const int p = c0 + tid;
-            const bool hit = p < a.n_pairs && a.sel[p] == eg;
+            const bool hit = p < a.n_pairs && sel_at<COHERENT>(a.sel, p) == eg;
             const uint64_t bal = __ballot(hit);
-            if (lane == 0) wcount[wave] = __popcll(bal);
+            if (lane == 0) sh.wcount[wave] = __popcll(bal);
             __syncthreads();
             int rank = base + __popcll(bal & ((1ull << lane) - 1)), total = base;
             for (int w = 0; w < NW; ++w) {
-                rank += w < wave ? wcount[w] : 0;
-                total += wcount[w];
+                rank += w < wave ? sh.wcount[w] : 0;
+                total += sh.wcount[w];
             }
-            if (hit && rank >= r0 && rank < r0 + 16) rows[rank - r0] = p;
+            if (hit && rank >= r0 && rank < r0 + 16) sh.rows[rank - r0] = p;
             __syncthreads();  // wcount is rewritten by the next chunk
             base = total;
         }
-        const int m = lane & 15;
-        const int pr = m < nr ? rows[m] : -1;
-        const uint16_t* up = a.u + (int64_t)(pr < 0 ? 0 : pr) * a.I;
-        // B operands of bank j (strips j*SL .. j*SL + SL - 1) of row tile kb (< 0: none)
-        auto issue_w = [&](u32x4_t (&bv)[SL][2], int j, int kb) {
-#pragma unroll
-            for (int i = 0; i < SL; ++i) {
-                const int s = j * SL + i;
-                const int off = kb >= 0 && s < ns ? (s * a.nkb + kb) * kMoeTileBytes : past;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    bv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               wr, off + h * 1024 + lane * 16, 0, kCachePolicyNT));
-            }
-        };
-        // A operands of row tile kb: token m, rows 64kb + 16(lane/16) + 8h .. +7
-        auto issue_x = [&](u32x4_t (&xv)[2], int kb) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k0 = 64 * kb + g16 + 8 * h;
-                xv[h] = kb >= 0 && pr >= 0 && k0 < a.I ? *reinterpret_cast<const u32x4_t*>(up + k0)
-                                                       : u32x4_t{0u, 0u, 0u, 0u};
-            }
-        };
-        floatx4_t acc[SB];
-#pragma unroll
-        for (int s = 0; s < SB; ++s) acc[s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        auto consume = [&](const u32x4_t (&bv)[SL][2], const u32x4_t (&xv)[2], int j) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < SL; ++i)
-                    acc[j * SL + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, xv[h]), __builtin_bit_cast(bf16x8_t, bv[i][h]),
-                        acc[j * SL + i], 0, 0, 0);
-        };
-        u32x4_t b0[SL][2], b1[SL][2], xa[2], xb[2];
-        const int kb_first = nkw > 0 ? wave : -1;
-        issue_x(xa, kb_first);
-        issue_w(b0, 0, kb_first);
-        issue_w(b1, 1, kb_first);
-        // row tile n of this wave: its operands are in (xc, b0, b1); the next
-        // tile's are loaded behind them into (xn, b0, b1)
-        auto step = [&](u32x4_t (&xc)[2], u32x4_t (&xn)[2], int n) {
-            const int kbn = n + 1 < nkw ? wave + (n + 1) * NW : -1;
-            issue_x(xn, kbn);
-            consume(b0, xc, 0);
-            issue_w(b0, 0, kbn);
-            consume(b1, xc, 1);
-            issue_w(b1, 1, kbn);
-        };
-        int n = 0;
-        for (; n + 1 < nkw; n += 2) {
-            step(xa, xb, n);
-            step(xb, xa, n + 1);
-        }
-        if (n < nkw) step(xa, xb, n);
-        // the waves' D tiles (lane l: tokens 4(l/16) + q of column l % 16),
-        // summed in wave order
-        if (r0 > 0) __syncthreads();  // the previous pass has read red
-#pragma unroll
-        for (int s = 0; s < SB; ++s)
-            *reinterpret_cast<floatx4_t*>(red + (wave * SB + s) * 256 + lane * 4) = acc[s];
-        __syncthreads();
-        for (int idx = tid; idx < ns * nr * 16; idx += NW * 64) {
-            const int s = idx / (nr * 16), rem = idx - s * nr * 16;
-            const int row = rem >> 4, col = rem & 15;
-            const int e = (16 * (row >> 2) + col) * 4 + (row & 3);
-            float v = red[s * 256 + e];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) v += red[(w * SB + s) * 256 + e];
-            a.y[(int64_t)rows[row] * a.H + 16 * (s0 + s) + col] = v;
-        }
+        project_pass<SB, NW>(wr, ns, a.nkb, a.I, a.u, sh.rows, nr, a.y, a.H, 16 * s0, sh.red, r0 > 0);
     }
+}
+
+// One workgroup per (local expert, block of SB 16-column strips).
+template <int SB, int NW>
+__global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
+    __shared__ __align__(16) ProjShared<SB, NW> sh;
+    expert_block<SB, NW, false>(a, blockIdx.x / a.col_blocks, blockIdx.x % a.col_blocks, sh);
+}
+
+// ------------------------------------------------- one layer's share --
+
+// The MoE layer's whole decode share in one launch, three kinds of
+// workgroups by index:
+//   [0, route_wgs)         routing, one wave per token (route_wgs is a
+//                          multiple of 8; every one of them, tokens or not,
+//                          counts itself done once its selections are
+//                          stored at device scope);
+//   [.., + attn_wgs)       the attention output slice: block cb of SB
+//                          strips for row groups g, g + G, ... of 16 tokens
+//                          (G = attn_groups); the G workgroups of a block
+//                          sit on one XCD (index % 8), so its tiles come
+//                          from HBM about once and from that L2 G-1 times;
+//   [.., + experts)        the experts' blocks, each after the routing is
+//                          done (a bounded wait: the routing workgroups come
+//                          first in dispatch order, so they are running).
+// The selections are read at device scope by the expert workgroups.
+struct LayerArgs {
+    ExpertArgs ex;               // ex.sel: the selections this launch writes
+    const float* logits;         // [T][E]
+    int32_t* sel_expert;         // [T][top_k] (== ex.sel)
+    float* sel_weight;           // [T][top_k]
+    int32_t E, top_k, renorm, tokens;
+    const uint16_t* xa;          // [T][KA] bf16
+    const uint16_t* wa;          // attention slice tiles [S16][nkba][1024]
+    float* slot_attn;            // this rank's attention partial [T][H]
+    int32_t KA, nkba;
+    int32_t route_wgs, attn_wgs, attn_groups;
+    uint32_t* ctr;               // routing workgroups done (zero at launch)
+    uint32_t* err;               // error word (bounded waits)
+    uint32_t spin_limit;
+};
+
+template <int SB, int NW, int EPL>
+__global__ __launch_bounds__(NW * 64) void moe_layer_kernel(LayerArgs a) {
+    __shared__ __align__(16) ProjShared<SB, NW> sh;
+    const int bx = blockIdx.x, tid = threadIdx.x;
+    if (bx < a.route_wgs) {
+        const int t = bx * NW + (tid >> 6);
+        if (t < a.tokens)
+            route_token<EPL, true>(a.logits, t, a.E, a.top_k, a.renorm, a.sel_expert, a.sel_weight, tid & 63);
+        wait_mem();  // this wave's selections are stored
+        __syncthreads();
+        if (tid == 0) add_dev_u32(a.ctr, 1u);
+        return;
+    }
+    const int ab = bx - a.route_wgs;
+    if (ab < a.attn_wgs) {
+        const int q = ab >> 3;
+        const int cb = (ab & 7) + 8 * (q / a.attn_groups), g = q % a.attn_groups;
+        if (cb >= a.ex.col_blocks) return;
+        const int s0 = cb * SB;
+        const int ns = a.ex.S16 - s0 < SB ? a.ex.S16 - s0 : SB;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.wa) + (int64_t)s0 * a.nkba * (kMoeTileBytes / 2), (short)0,
+            ns * a.nkba * kMoeTileBytes, kBufferRsrcWord3);
+        for (int r0 = 16 * g; r0 < a.tokens; r0 += 16 * a.attn_groups) {
+            if (r0 > 16 * g) __syncthreads();  // the previous pass has read rows
+            if (tid < 16) sh.rows[tid] = r0 + tid;
+            __syncthreads();
+            const int nr = a.tokens - r0 < 16 ? a.tokens - r0 : 16;
+            project_pass<SB, NW>(wr, ns, a.nkba, a.KA, a.xa, sh.rows, nr, a.slot_attn, a.ex.H, 16 * s0,
+                                 sh.red, r0 > 16 * g);
+        }
+        return;
+    }
+    const int eb = ab - a.attn_wgs;
+    if (tid == 0) sh.ok = wait_at_least(a.ctr, (uint32_t)a.route_wgs, a.err, a.spin_limit);
+    __syncthreads();
+    if (!sh.ok) return;
+    expert_block<SB, NW, true>(a.ex, eb / a.ex.col_blocks, eb % a.ex.col_blocks, sh);
 }
 
 // ------------------------------------------------------------ combine --
@@ -350,21 +472,13 @@ __global__ void moe_combine_kernel(const int32_t* __restrict__ sel_expert, const
 // thread: where they lie in one ring chunk (chunk a multiple of 4) the
 // ranks' values come as 16-byte loads, all issued before the first add;
 // otherwise element by element.
-__global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
-                                        const float* __restrict__ sel_weight, const float* __restrict__ y,
-                                        int e0, int el, int tokens, int top_k, int H,
-                                        float* __restrict__ slots, float* hidden, int n_ranks, int rank,
-                                        int64_t chunk) {
+// Elements i .. i+3 (one token's row): the rank's combined partial acc to
+// its slot, then the ring-order sum of the N ranks' values plus res.
+__device__ __forceinline__ floatx4_t slot_and_ring4(float* __restrict__ slots, int64_t len, int64_t i,
+                                                    int64_t chunk, int n_ranks, int rank, floatx4_t acc,
+                                                    floatx4_t res) {
 #pragma clang fp contract(off)
-    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t len = (int64_t)tokens * H;
-    const int H4 = H / 4;
-    if (v >= (int64_t)tokens * H4) return;
-    const int t = (int)(v / H4), n = 4 * (int)(v - (int64_t)t * H4);
-    const int64_t i = (int64_t)t * H + n;
-    const floatx4_t acc = combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
     *reinterpret_cast<floatx4_t*>(slots + (int64_t)rank * len + i) = acc;
-    const floatx4_t res = *reinterpret_cast<const floatx4_t*>(hidden + i);
     floatx4_t out;
     if (chunk % 4 == 0) {
         const int c = (int)(i / chunk);
@@ -387,7 +501,49 @@ __global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
         for (int k = 0; k < 4; ++k)
             out[k] = ring_element(slots, len, i + k, chunk, n_ranks, rank, acc[k], res[k]);
     }
-    *reinterpret_cast<floatx4_t*>(hidden + i) = out;
+    return out;
+}
+
+__global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
+                                        const float* __restrict__ sel_weight, const float* __restrict__ y,
+                                        int e0, int el, int tokens, int top_k, int H,
+                                        float* __restrict__ slots, float* hidden, int n_ranks, int rank,
+                                        int64_t chunk) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t len = (int64_t)tokens * H;
+    const int H4 = H / 4;
+    if (v >= (int64_t)tokens * H4) return;
+    const int t = (int)(v / H4), n = 4 * (int)(v - (int64_t)t * H4);
+    const int64_t i = (int64_t)t * H + n;
+    const floatx4_t acc = combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
+    const floatx4_t res = *reinterpret_cast<const floatx4_t*>(hidden + i);
+    *reinterpret_cast<floatx4_t*>(hidden + i) = slot_and_ring4(slots, len, i, chunk, n_ranks, rank, acc, res);
+}
+
+// The layer share's two reconciliation points after moe_layer_kernel: the
+// attention point's ring sum (every rank's value from slots_attn, this
+// rank's written by that launch) plus the residual, then the experts'
+// combine to this rank's slot of slots_moe and their ring sum on top: the
+// same operations, in the same order, as tp_ring_reduce followed by
+// tp_moe_decode. Also clears the routing counter for the next launch.
+__global__ void moe_layer_combine_kernel(const int32_t* __restrict__ sel_expert,
+                                         const float* __restrict__ sel_weight, const float* __restrict__ y,
+                                         int e0, int el, int tokens, int top_k, int H,
+                                         const float* __restrict__ slots_attn, float* __restrict__ slots_moe,
+                                         float* hidden, int n_ranks, int rank, int64_t chunk, uint32_t* ctr) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev_u32(ctr, 0u);
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t len = (int64_t)tokens * H;
+    const int H4 = H / 4;
+    if (v >= (int64_t)tokens * H4) return;
+    const int t = (int)(v / H4), n = 4 * (int)(v - (int64_t)t * H4);
+    const int64_t i = (int64_t)t * H + n;
+    const floatx4_t acc = combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
+    const floatx4_t res = *reinterpret_cast<const floatx4_t*>(hidden + i);
+    floatx4_t h1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h1[k] = ring_element(slots_attn, len, i + k, chunk, n_ranks, -1, 0.f, res[k]);
+    *reinterpret_cast<floatx4_t*>(hidden + i) = slot_and_ring4(slots_moe, len, i, chunk, n_ranks, rank, acc, h1);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -407,6 +563,18 @@ const ExpertVariant kExpertVariants[] = {
     {8, 2, moe_expert_kernel<8, 2>},
     {16, 4, moe_expert_kernel<16, 4>},
 };
+
+// The layer share's kernel (the first expert variant's blocks) by experts
+// per routing lane.
+typedef void (*layer_fn)(LayerArgs);
+constexpr int kLayerSB = 8, kLayerNW = 4;
+layer_fn layer_kernel(int E) {
+    if (E <= 64) return moe_layer_kernel<kLayerSB, kLayerNW, 1>;
+    if (E <= 128) return moe_layer_kernel<kLayerSB, kLayerNW, 2>;
+    if (E <= 256) return moe_layer_kernel<kLayerSB, kLayerNW, 4>;
+    if (E <= 512) return moe_layer_kernel<kLayerSB, kLayerNW, 8>;
+    return nullptr;
+}
 
 // Projections of the pairs' rows, [T * k][H] fp32, in the workspace.
 float* moe_rows(const tp_plan_s* p, void* ws) {
@@ -522,6 +690,86 @@ tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, co
     hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len / 4 + 255) / 256)), dim3(256), 0, st,
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
                        (int)p->top_k, (int)H, slots, hidden, (int)p->n_ranks, (int)rank, len / p->n_ranks);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+tp_status tp_moe_pack_attn(tp_plan_t p, const void* w, void* w_packed, void* stream) {
+    if (!p || !w || !w_packed) return TP_ERR_INVALID_ARG;
+    if (!p->n_experts || p->k_attn <= 0) return TP_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
+    if (w == w_packed) return TP_ERR_INVALID_ARG;
+    if (p->hidden % 16) return TP_ERR_UNSUPPORTED;
+    return tp_pack_tile_stack(1, p->k_attn / p->n_ranks, p->hidden, w, w_packed, stream);
+}
+
+tp_status tp_moe_layer_decode(tp_plan_t p, int32_t rank, const float* logits, int32_t renorm,
+                              const void* x_attn, const void* w_attn_packed, const void* u,
+                              const void* w_packed, int32_t* sel_expert, float* sel_weight,
+                              float* slots_attn, float* slots_moe, float* hidden, void* ws,
+                              void* stream) {
+    if (!p || !logits || !x_attn || !w_attn_packed || !u || !w_packed || !sel_expert || !sel_weight ||
+        !slots_attn || !slots_moe || !hidden || !ws)
+        return TP_ERR_INVALID_ARG;
+    if (!p->n_experts || p->k_attn <= 0) return TP_ERR_INVALID_ARG;
+    if (p->ep != p->n_ranks || rank < 0 || rank >= p->ep || p->batch > p->max_tokens)
+        return TP_ERR_INVALID_ARG;
+    if (!aligned16(logits) || !aligned16(x_attn) || !aligned16(w_attn_packed) || !aligned16(u) ||
+        !aligned16(w_packed) || !aligned16(sel_expert) || !aligned16(sel_weight) ||
+        !aligned16(slots_attn) || !aligned16(slots_moe) || !aligned16(hidden) || !aligned16(ws))
+        return TP_ERR_ALIGNMENT;
+    const int64_t H = p->hidden, I = p->moe_inter, T = p->batch, E = p->n_experts;
+    const int64_t el = E / p->ep, KA = p->k_attn / p->n_ranks;
+    // 16-byte A-operand loads: rows of u and x_attn start 16-byte aligned
+    if (I % 8 || H % 16 || KA % 8 || p->top_k > 64) return TP_ERR_UNSUPPORTED;
+    layer_fn k = layer_kernel((int)E);
+    if (!k) return TP_ERR_UNSUPPORTED;
+    const int64_t S16 = H / 16, nkb = (I + 63) / 64, nkba = (KA + 63) / 64;
+    // one expert's (and the attention slice's) tiles: 32-bit buffer offsets
+    if (S16 * nkb * kMoeTileBytes >= ((int64_t)1 << 31) || S16 * nkba * kMoeTileBytes >= ((int64_t)1 << 31))
+        return TP_ERR_UNSUPPORTED;
+    LayerArgs a;
+    a.ex.u = static_cast<const uint16_t*>(u);
+    a.ex.w = static_cast<const uint16_t*>(w_packed);
+    a.ex.sel = sel_expert;
+    a.ex.y = moe_rows(p, ws);
+    a.ex.n_pairs = (int32_t)(T * p->top_k);
+    a.ex.e0 = (int32_t)(rank * el);
+    a.ex.H = (int32_t)H;
+    a.ex.S16 = (int32_t)S16;
+    a.ex.I = (int32_t)I;
+    a.ex.nkb = (int32_t)nkb;
+    a.ex.col_blocks = (int32_t)((S16 + kLayerSB - 1) / kLayerSB);
+    a.logits = logits;
+    a.sel_expert = sel_expert;
+    a.sel_weight = sel_weight;
+    a.E = (int32_t)E;
+    a.top_k = p->top_k;
+    a.renorm = renorm != 0;
+    a.tokens = (int32_t)T;
+    a.xa = static_cast<const uint16_t*>(x_attn);
+    a.wa = static_cast<const uint16_t*>(w_attn_packed);
+    const int64_t len = T * H;
+    a.slot_attn = slots_attn + rank * len;
+    a.KA = (int32_t)KA;
+    a.nkba = (int32_t)nkba;
+    // routing: one wave per token, padded to a multiple of 8 workgroups so
+    // that the attention blocks' index % 8 is their XCD
+    a.route_wgs = (int32_t)(((T + kLayerNW - 1) / kLayerNW + 7) / 8 * 8);
+    const int64_t groups = (T + 15) / 16;
+    a.attn_groups = (int32_t)(groups < 4 ? groups : 4);
+    a.attn_wgs = 8 * a.attn_groups * ((a.ex.col_blocks + 7) / 8);
+    uint32_t* sync = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSyncOffset);
+    a.ctr = sync + kSyncMoeRoute;
+    a.err = sync + kSyncErr;
+    a.spin_limit = 1u << 21;
+    const int64_t grid = (int64_t)a.route_wgs + a.attn_wgs + el * a.ex.col_blocks;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kLayerNW * 64), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
+    hipLaunchKernelGGL(moe_layer_combine_kernel, dim3((unsigned)((len / 4 + 255) / 256)), dim3(256), 0, st,
+                       sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)T,
+                       (int)p->top_k, (int)H, slots_attn, slots_moe, hidden, (int)p->n_ranks, (int)rank,
+                       len / p->n_ranks, a.ctr);
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 

@@ -201,3 +201,127 @@ def test_moe_decode_equals_partial_then_ring_bitwise(T, E, k, I, H, ep):
     assert_bits_equal(host(hd), host(hc), "hidden")
     ref64, _ = oracle.moe_partial(se, sw.astype(np.float64), rank * el, u, w[rank * el:(rank + 1) * el])
     assert_partial_close(host(S)[rank], ref64, "partial")
+
+
+# ------------------------------------------------ the whole layer share --
+
+def layer_plan(T, E, k, I, H, ep, KA):
+    return tp.Plan(H, KA * ep, ep, T, k_attn=KA * ep,
+                   moe=dict(n_experts=E, top_k=k, ep=ep, moe_inter=I, max_tokens=T))
+
+
+def run_layer(plan, rank, logits, u, w_rank_dev, xa, wa_dev, slots_a, slots_m, h0, ws, renorm=True):
+    i = plan.info()
+    T, k = i["batch"], i["top_k"]
+    wp = torch.empty(tp.moe_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
+    tp.tp_moe_pack_experts(plan, w_rank_dev, wp)
+    wap = torch.empty(tp.moe_attn_packed_shape(plan), dtype=torch.bfloat16, device="cuda")
+    tp.tp_moe_pack_attn(plan, wa_dev, wap)
+    se = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    sw = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    SA, SM, hd = to_dev_f32(slots_a), to_dev_f32(slots_m), to_dev_f32(h0)
+    tp.tp_moe_layer_decode(plan, rank, to_dev_f32(logits), to_dev_bf16(xa), wap, to_dev_bf16(u), wp, se, sw,
+                           SA, SM, hd, ws, renorm=renorm)
+    torch.cuda.synchronize()
+    assert tp.tp_workspace_status(plan, ws) == 0, "a bounded wait timed out"
+    return host(se), host(sw), host(SA), host(SM), host(hd)
+
+
+def check_layer(T, E, k, I, H, ep, KA, rank, seed, renorm=True, ws=None, plan=None):
+    plan = plan or layer_plan(T, E, k, I, H, ep, KA)
+    ws = ws if ws is not None else plan.new_workspace()
+    logits, u, w = moe_inputs(T, E, k, I, H, ep, seed)
+    xa = synth.normal_bf16((T, KA), 1.0, seed=seed, tensor="x_attn")
+    wa = synth.normal_bf16((KA, H), synth.WEIGHT_STD, seed=seed, tensor="w_o")
+    el = E // ep
+    g = np.random.default_rng(seed)
+    slots_a = (g.standard_normal((ep, T, H)) * 0.5).astype(np.float32)
+    slots_m = (g.standard_normal((ep, T, H)) * 0.5).astype(np.float32)
+    h0 = g.standard_normal((T, H)).astype(np.float32)
+    wr = w[rank * el:(rank + 1) * el]
+    se, sw, SA, SM, hd = run_layer(plan, rank, logits, u, to_dev_bf16(wr), xa, to_dev_bf16(wa),
+                                   slots_a, slots_m, h0, ws, renorm)
+    # routing: the routing entry's bits, the oracle's choice
+    se_r, sw_r = gpu_route(plan, logits, renorm)
+    assert_bits_equal(se, se_r, "selected experts vs tp_moe_route")
+    assert_bits_equal(sw, sw_r, "routing weights vs tp_moe_route")
+    se_or, _ = oracle.moe_route(logits, k, renorm)
+    assert_bits_equal(se, se_or, "selected experts vs the oracle")
+    # the other ranks' slots are only read
+    for r in range(ep):
+        if r != rank:
+            assert_bits_equal(SA[r], slots_a[r], "attention slot %d" % r)
+            assert_bits_equal(SM[r], slots_m[r], "expert slot %d" % r)
+    # the attention slice's partial against the oracle
+    ref_a, _ = oracle.partial(xa, wa, nthreads=8)
+    assert_partial_close(SA[rank], ref_a, "attention partial")
+    # the experts: tp_moe_partial's bits, within tolerance of the oracle
+    part = gpu_moe_partial(plan, rank, se, sw, u, to_dev_bf16(wr))
+    assert_bits_equal(SM[rank], part, "expert partial vs tp_moe_partial")
+    ref_m, _ = oracle.moe_partial(se, sw.astype(np.float64), rank * el, u, wr, nthreads=8)
+    assert_partial_close(SM[rank], ref_m, "expert partial")
+    # both ring stages, bit for bit, on the slots as written
+    h1 = oracle.ring_reduce(SA, h0)
+    assert_bits_equal(hd, oracle.ring_reduce(SM, h1), "hidden")
+    return plan, ws
+
+
+@pytest.mark.parametrize("T,E,k,I,H,ep,KA,rank", [
+    (10, 16, 4, 64, 256, 2, 200, 1),       # one row group, a ragged last attention tile
+    (64, 128, 8, 1536, 1040, 4, 512, 3),   # 65 strips: a last block of one strip
+    (33, 100, 3, 520, 2048, 4, 264, 0),    # three row groups, 25 experts per rank
+    (49, 32, 2, 64, 512, 2, 64, 1),        # four row groups, the last of one token
+    (1, 8, 2, 24, 16, 1, 8, 0),            # one token, one rank, one strip
+])
+def test_moe_layer_share_matches_oracle_and_composition(T, E, k, I, H, ep, KA, rank):
+    say("moe layer T=%d E=%d k=%d I=%d H=%d ep=%d KA=%d rank=%d" % (T, E, k, I, H, ep, KA, rank))
+    check_layer(T, E, k, I, H, ep, KA, rank, 21)
+
+
+def test_moe_layer_share_repeats_on_one_workspace_without_renorm():
+    # the routing counter is cleared by each call's second launch: a second
+    # call on the same workspace (other inputs) waits for its own routing
+    T, E, k, I, H, ep, KA = 24, 64, 4, 128, 512, 4, 128
+    say("moe layer repeated")
+    plan, ws = check_layer(T, E, k, I, H, ep, KA, 2, 22)
+    check_layer(T, E, k, I, H, ep, KA, 1, 23, renorm=False, ws=ws, plan=plan)
+    check_layer(T, E, k, I, H, ep, KA, 0, 24, ws=ws, plan=plan)
+
+
+def test_moe_layer_share_full_size_sampled_columns():
+    """The layer share at its full size (hidden 4096, attention 8192 -> 4096
+    over 4 ranks, 128 experts of 1536, top-8, EP=4, 64 tokens), rank 2,
+    weights drawn on the device; the oracle computes sampled columns and
+    both ring stages in full."""
+    w = workloads.MOE
+    T, E, k, I, H, ep, KA = w.batch, w.n_experts, w.top_k, w.moe_inter, w.hidden, w.ep, w.ka_r
+    rank = 2
+    el = E // ep
+    say("moe layer full size, rank %d" % rank)
+    plan = layer_plan(T, E, k, I, H, ep, KA)
+    ws = plan.new_workspace()
+    kw = dict(seed=0, workload=w.name, rank=rank)
+    logits = synth.normal_f32((T, E), 1.0, seed=0, workload=w.name, tensor="logits")
+    u = synth.normal_bf16((T, k, I), 1.0, tensor="u", **kw)
+    xa = synth.normal_bf16((T, KA), 1.0, tensor="x_attn", **kw)
+    wdev = synth.device_normal((el, I, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_expert", **kw)
+    wadev = synth.device_normal((KA, H), synth.WEIGHT_STD, torch.bfloat16, tensor="w_o", **kw)
+    g = np.random.default_rng(25)
+    slots_a = (g.standard_normal((ep, T, H)) * 0.5).astype(np.float32)
+    slots_m = (g.standard_normal((ep, T, H)) * 0.5).astype(np.float32)
+    h0 = g.standard_normal((T, H)).astype(np.float32)
+    se, sw, SA, SM, hd = run_layer(plan, rank, logits, u, wdev, xa, wadev, slots_a, slots_m, h0, ws)
+    se_or, _ = oracle.moe_route(logits, k, True)
+    assert_bits_equal(se, se_or, "routing")
+    part = gpu_moe_partial(plan, rank, se, sw, u, wdev)
+    assert_bits_equal(SM[rank], part, "expert partial vs tp_moe_partial")
+    cols = np.array(sorted(set(np.random.default_rng(6).choice(H, 48, replace=False).tolist())
+                           | {0, 127, 128, H - 1}))
+    cdev = torch.from_numpy(cols).cuda()
+    ref_a, _ = oracle.partial(xa, bf16_bits_host(wadev[:, cdev].contiguous()), nthreads=8)
+    assert_partial_close(SA[rank][:, cols], ref_a, "attention partial, sampled columns")
+    ref_m, _ = oracle.moe_partial(se, sw.astype(np.float64), rank * el, u,
+                                  bf16_bits_host(wdev[:, :, cdev].contiguous()), nthreads=8)
+    assert_partial_close(SM[rank][:, cols], ref_m, "expert partial, sampled columns")
+    h1 = oracle.ring_reduce(SA, h0)
+    assert_bits_equal(hd, oracle.ring_reduce(SM, h1), "hidden")
