@@ -188,6 +188,44 @@ struct ExpertArgs {
 
 constexpr int kMoeTileBytes = 2048;  // 64 rows x 16 columns of bf16
 
+// The two register banks of B operands of a grouped-GEMV wave: bank j
+// holds strips j*SL .. j*SL + SL - 1 of one 64-row tile.
+template <int SB>
+struct Banks {
+    u32x4_t b[2][SB / 2][2];
+};
+
+// Load bank j of row tile kb (< 0: none; strips past ns and absent tiles
+// read zero through an offset past the buffer range).
+template <int SB>
+__device__ __forceinline__ void load_bank(Banks<SB>& bk, int j, __amdgpu_buffer_rsrc_t wr, int ns, int nkb,
+                                          int kb, int lane) {
+    constexpr int SL = SB / 2;
+    const int past = ns * nkb * kMoeTileBytes;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+        const int s = j * SL + i;
+        const int off = kb >= 0 && s < ns ? (s * nkb + kb) * kMoeTileBytes : past;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            bk.b[j][i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            wr, off + h * 1024 + lane * 16, 0, kCachePolicyNT));
+    }
+}
+
+// The first row tile of wave `wave` in a block of nkb row tiles (-1: none).
+template <int NW>
+__device__ __forceinline__ int first_tile(int nkb, int wave) { return nkb > wave ? wave : -1; }
+
+// Both banks of this wave's first row tile of the block.
+template <int SB, int NW>
+__device__ __forceinline__ void prime_banks(Banks<SB>& bk, __amdgpu_buffer_rsrc_t wr, int ns, int nkb) {
+    const int lane = threadIdx.x & 63;
+    const int kb = first_tile<NW>(nkb, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    load_bank<SB>(bk, 0, wr, ns, nkb, kb, lane);
+    load_bank<SB>(bk, 1, wr, ns, nkb, kb, lane);
+}
+
 // One pass of a block of the grouped GEMV: up to 16 A rows, named in LDS by
 // rows[0 .. nr) (A row r is the K bf16 values at a + rows[r] * K; token
 // slot m = lane % 16 of the MFMA), times the block's ns 16-column strips
@@ -199,33 +237,22 @@ constexpr int kMoeTileBytes = 2048;  // 64 rows x 16 columns of bf16
 // out[rows[r] * H + col0 ..]. Strips past the block's last and rows past K
 // read zero (offsets past the buffer range); A operands of empty token slots
 // and of rows past K are zero. after_pass: a previous pass of this
-// workgroup may still read red.
+// workgroup may still read red. bk holds the wave's first row tile, loaded
+// by the caller (prime_banks), which may do so early, e.g. while it waits
+// for the rows.
 template <int SB, int NW>
 __device__ __forceinline__ void project_pass(__amdgpu_buffer_rsrc_t wr, int ns, int nkb, int K,
                                              const uint16_t* __restrict__ a, const int* rows, int nr,
                                              float* __restrict__ out, int H, int col0, float* red,
-                                             bool after_pass) {
+                                             bool after_pass, Banks<SB>& bk) {
     constexpr int SL = SB / 2;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int past = ns * nkb * kMoeTileBytes;  // an offset past the range: reads zero
     const int nkw = nkb > wave ? (nkb - wave + NW - 1) / NW : 0;  // this wave's row tiles
     const int g16 = 16 * (lane >> 4);
     const int m = lane & 15;
     const int pr = m < nr ? rows[m] : -1;
     const uint16_t* up = a + (int64_t)(pr < 0 ? 0 : pr) * K;
-    // B operands of bank j (strips j*SL .. j*SL + SL - 1) of row tile kb (< 0: none)
-    auto issue_w = [&](u32x4_t (&bv)[SL][2], int j, int kb) {
-#pragma unroll
-        for (int i = 0; i < SL; ++i) {
-            const int s = j * SL + i;
-            const int off = kb >= 0 && s < ns ? (s * nkb + kb) * kMoeTileBytes : past;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                bv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           wr, off + h * 1024 + lane * 16, 0, kCachePolicyNT));
-        }
-    };
     // A operands of row tile kb: token m, rows 64kb + 16(lane/16) + 8h .. +7
     auto issue_x = [&](u32x4_t (&xv)[2], int kb) {
 #pragma unroll
@@ -238,29 +265,26 @@ __device__ __forceinline__ void project_pass(__amdgpu_buffer_rsrc_t wr, int ns, 
     floatx4_t acc[SB];
 #pragma unroll
     for (int s = 0; s < SB; ++s) acc[s] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    auto consume = [&](const u32x4_t (&bv)[SL][2], const u32x4_t (&xv)[2], int j) {
+    auto consume = [&](int j, const u32x4_t (&xv)[2]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < SL; ++i)
                 acc[j * SL + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xv[h]), __builtin_bit_cast(bf16x8_t, bv[i][h]),
+                    __builtin_bit_cast(bf16x8_t, xv[h]), __builtin_bit_cast(bf16x8_t, bk.b[j][i][h]),
                     acc[j * SL + i], 0, 0, 0);
     };
-    u32x4_t b0[SL][2], b1[SL][2], xa[2], xb[2];
-    const int kb_first = nkw > 0 ? wave : -1;
-    issue_x(xa, kb_first);
-    issue_w(b0, 0, kb_first);
-    issue_w(b1, 1, kb_first);
-    // row tile n of this wave: its operands are in (xc, b0, b1); the next
-    // tile's are loaded behind them into (xn, b0, b1)
+    u32x4_t xa[2], xb[2];
+    issue_x(xa, first_tile<NW>(nkb, wave));
+    // row tile n of this wave: its operands are in (xc, bank 0, bank 1); the
+    // next tile's are loaded behind them into (xn, bank 0, bank 1)
     auto step = [&](u32x4_t (&xc)[2], u32x4_t (&xn)[2], int n) {
         const int kbn = n + 1 < nkw ? wave + (n + 1) * NW : -1;
         issue_x(xn, kbn);
-        consume(b0, xc, 0);
-        issue_w(b0, 0, kbn);
-        consume(b1, xc, 1);
-        issue_w(b1, 1, kbn);
+        consume(0, xc);
+        load_bank<SB>(bk, 0, wr, ns, nkb, kbn, lane);
+        consume(1, xc);
+        load_bank<SB>(bk, 1, wr, ns, nkb, kbn, lane);
     };
     int n = 0;
     for (; n + 1 < nkw; n += 2) {
@@ -308,8 +332,19 @@ __device__ __forceinline__ int32_t sel_at(const int32_t* sel, int p) {
 // the selections: ranks from wave ballots); a pass takes up to 16 of them
 // and row p's projection lands in Y[p] (so the combine needs no table).
 // An expert that no pair selected is not read.
-template <int SB, int NW, bool COHERENT>
-__device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb, ProjShared<SB, NW>& sh) {
+// The block's tiles: a buffer over the block's strips of local expert le.
+template <int SB>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t expert_rsrc(const ExpertArgs& a, int le, int s0, int ns) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.w) + ((int64_t)le * a.S16 + s0) * a.nkb * (kMoeTileBytes / 2), (short)0,
+        ns * a.nkb * kMoeTileBytes, kBufferRsrcWord3);
+}
+
+// PRIMED: bk holds the wave's first row tile of the block (the first pass
+// uses it).
+template <int SB, int NW, bool COHERENT, bool PRIMED>
+__device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb, ProjShared<SB, NW>& sh,
+                                             Banks<SB>& bk) {
     constexpr int NT = NW * 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,9 +361,7 @@ __device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb
     if (n_rows == 0) return;  // expert not selected by any token: not read
     const int s0 = cb * SB;
     const int ns = a.S16 - s0 < SB ? a.S16 - s0 : SB;
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.w) + ((int64_t)le * a.S16 + s0) * a.nkb * (kMoeTileBytes / 2), (short)0,
-        ns * a.nkb * kMoeTileBytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wr = expert_rsrc<SB>(a, le, s0, ns);
     for (int r0 = 0; r0 < n_rows; r0 += 16) {
         const int nr = n_rows - r0 < 16 ? n_rows - r0 : 16;
         // the pass's rows: the expert's pairs of rank r0 .. r0 + 15
@@ -349,7 +382,8 @@ __device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb
             __syncthreads();  // wcount is rewritten by the next chunk
             base = total;
         }
-        project_pass<SB, NW>(wr, ns, a.nkb, a.I, a.u, sh.rows, nr, a.y, a.H, 16 * s0, sh.red, r0 > 0);
+        if (!PRIMED || r0 > 0) prime_banks<SB, NW>(bk, wr, ns, a.nkb);
+        project_pass<SB, NW>(wr, ns, a.nkb, a.I, a.u, sh.rows, nr, a.y, a.H, 16 * s0, sh.red, r0 > 0, bk);
     }
 }
 
@@ -357,7 +391,8 @@ __device__ __forceinline__ void expert_block(const ExpertArgs& a, int le, int cb
 template <int SB, int NW>
 __global__ __launch_bounds__(NW * 64) void moe_expert_kernel(ExpertArgs a) {
     __shared__ __align__(16) ProjShared<SB, NW> sh;
-    expert_block<SB, NW, false>(a, blockIdx.x / a.col_blocks, blockIdx.x % a.col_blocks, sh);
+    Banks<SB> bk;
+    expert_block<SB, NW, false, false>(a, blockIdx.x / a.col_blocks, blockIdx.x % a.col_blocks, sh, bk);
 }
 
 // ------------------------------------------------- one layer's share --
@@ -421,35 +456,64 @@ __global__ __launch_bounds__(NW * 64) void moe_layer_kernel(LayerArgs a) {
             if (tid < 16) sh.rows[tid] = r0 + tid;
             __syncthreads();
             const int nr = a.tokens - r0 < 16 ? a.tokens - r0 : 16;
+            Banks<SB> bk;
+            prime_banks<SB, NW>(bk, wr, ns, a.nkba);
             project_pass<SB, NW>(wr, ns, a.nkba, a.KA, a.xa, sh.rows, nr, a.slot_attn, a.ex.H, 16 * s0,
-                                 sh.red, r0 > 16 * g);
+                                 sh.red, r0 > 16 * g, bk);
         }
         return;
     }
+    // An expert block loads its first row tiles while the routing is being
+    // done (wasted only if no token chose the expert).
     const int eb = ab - a.attn_wgs;
+    const int le = eb / a.ex.col_blocks, cb = eb % a.ex.col_blocks;
+    const int s0 = cb * SB;
+    const int ns = a.ex.S16 - s0 < SB ? a.ex.S16 - s0 : SB;
+    const __amdgpu_buffer_rsrc_t wr = expert_rsrc<SB>(a.ex, le, s0, ns);
+    Banks<SB> bk;
+    prime_banks<SB, NW>(bk, wr, ns, a.ex.nkb);
     if (tid == 0) sh.ok = wait_at_least(a.ctr, (uint32_t)a.route_wgs, a.err, a.spin_limit);
     __syncthreads();
     if (!sh.ok) return;
-    expert_block<SB, NW, true>(a.ex, eb / a.ex.col_blocks, eb % a.ex.col_blocks, sh);
+    expert_block<SB, NW, true, true>(a.ex, le, cb, sh, bk);
 }
 
 // ------------------------------------------------------------ combine --
 
 // Four columns per thread (H is a multiple of 16): each element sums the
-// token's local selections in order, as one fused multiply-add each.
+// token's local selections in order, as one fused multiply-add each. The
+// selections are taken eight at a time with every load issued before the
+// first sum: the routing tables, then the projected rows through a buffer
+// over the token's rows, a non-local selection's offset lying past its
+// range (it reads zero and moves no data; its term is skipped).
 __device__ __forceinline__ floatx4_t combine4(const int32_t* __restrict__ sel_expert,
                                               const float* __restrict__ sel_weight,
                                               const float* __restrict__ y, int e0, int el, int t,
                                               int top_k, int H, int n) {
     floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < top_k; ++s) {
-        const int q = t * top_k + s;
-        const int le = sel_expert[q] - e0;
-        if (le >= 0 && le < el) {
-            const float w = sel_weight[q];
-            const floatx4_t yv = *reinterpret_cast<const floatx4_t*>(y + (int64_t)q * H + n);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(y) + (int64_t)t * top_k * H, (short)0, top_k * H * 4, kBufferRsrcWord3);
+    for (int s0 = 0; s0 < top_k; s0 += 8) {
+        int le[8];
+        float w[8];
+        floatx4_t yv[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(w, yv[k], acc[k]);
+        for (int u = 0; u < 8; ++u) {
+            const int q = t * top_k + (s0 + u < top_k ? s0 + u : top_k - 1);
+            le[u] = sel_expert[q] - e0;
+            w[u] = sel_weight[q];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool mine = s0 + u < top_k && le[u] >= 0 && le[u] < el;
+            const int off = mine ? ((s0 + u) * H + n) * 4 : top_k * H * 4;
+            yv[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool mine = s0 + u < top_k && le[u] >= 0 && le[u] < el;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = mine ? __builtin_fmaf(w[u], yv[u][k], acc[k]) : acc[k];
         }
     }
     return acc;
@@ -472,13 +536,13 @@ __global__ void moe_combine_kernel(const int32_t* __restrict__ sel_expert, const
 // thread: where they lie in one ring chunk (chunk a multiple of 4) the
 // ranks' values come as 16-byte loads, all issued before the first add;
 // otherwise element by element.
-// Elements i .. i+3 (one token's row): the rank's combined partial acc to
-// its slot, then the ring-order sum of the N ranks' values plus res.
-__device__ __forceinline__ floatx4_t slot_and_ring4(float* __restrict__ slots, int64_t len, int64_t i,
-                                                    int64_t chunk, int n_ranks, int rank, floatx4_t acc,
-                                                    floatx4_t res) {
+// Elements i .. i+3 (one token's row): the ring-order sum of the N ranks'
+// values plus res, rank `rank`'s values being acc (rank < 0: every value
+// from slots).
+__device__ __forceinline__ floatx4_t ring4(const float* __restrict__ slots, int64_t len, int64_t i,
+                                           int64_t chunk, int n_ranks, int rank, floatx4_t acc,
+                                           floatx4_t res) {
 #pragma clang fp contract(off)
-    *reinterpret_cast<floatx4_t*>(slots + (int64_t)rank * len + i) = acc;
     floatx4_t out;
     if (chunk % 4 == 0) {
         const int c = (int)(i / chunk);
@@ -502,6 +566,14 @@ __device__ __forceinline__ floatx4_t slot_and_ring4(float* __restrict__ slots, i
             out[k] = ring_element(slots, len, i + k, chunk, n_ranks, rank, acc[k], res[k]);
     }
     return out;
+}
+
+// The rank's combined partial acc to its slot, then ring4.
+__device__ __forceinline__ floatx4_t slot_and_ring4(float* __restrict__ slots, int64_t len, int64_t i,
+                                                    int64_t chunk, int n_ranks, int rank, floatx4_t acc,
+                                                    floatx4_t res) {
+    *reinterpret_cast<floatx4_t*>(slots + (int64_t)rank * len + i) = acc;
+    return ring4(slots, len, i, chunk, n_ranks, rank, acc, res);
 }
 
 __global__ void moe_combine_ring_kernel(const int32_t* __restrict__ sel_expert,
@@ -540,9 +612,7 @@ __global__ void moe_layer_combine_kernel(const int32_t* __restrict__ sel_expert,
     const int64_t i = (int64_t)t * H + n;
     const floatx4_t acc = combine4(sel_expert, sel_weight, y, e0, el, t, top_k, H, n);
     const floatx4_t res = *reinterpret_cast<const floatx4_t*>(hidden + i);
-    floatx4_t h1;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) h1[k] = ring_element(slots_attn, len, i + k, chunk, n_ranks, -1, 0.f, res[k]);
+    const floatx4_t h1 = ring4(slots_attn, len, i, chunk, n_ranks, -1, res, res);
     *reinterpret_cast<floatx4_t*>(hidden + i) = slot_and_ring4(slots_moe, len, i, chunk, n_ranks, rank, acc, h1);
 }
 
@@ -629,6 +699,7 @@ tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_exper
     const int64_t S16 = H / 16, nkb = (I + 63) / 64;
     const ExpertVariant v = kExpertVariants[p->moe_variant > 0 ? p->moe_variant - 1 : 0];
     if (S16 * nkb * kMoeTileBytes >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // one expert's bytes
+    if ((int64_t)p->top_k * H * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // a token's rows (combine)
     if (tokens == 0) return TP_OK;
     ExpertArgs a;
     a.u = static_cast<const uint16_t*>(u);
@@ -727,6 +798,7 @@ tp_status tp_moe_layer_decode(tp_plan_t p, int32_t rank, const float* logits, in
     // one expert's (and the attention slice's) tiles: 32-bit buffer offsets
     if (S16 * nkb * kMoeTileBytes >= ((int64_t)1 << 31) || S16 * nkba * kMoeTileBytes >= ((int64_t)1 << 31))
         return TP_ERR_UNSUPPORTED;
+    if ((int64_t)p->top_k * H * 4 >= ((int64_t)1 << 31)) return TP_ERR_UNSUPPORTED;  // a token's rows (combine)
     LayerArgs a;
     a.ex.u = static_cast<const uint16_t*>(u);
     a.ex.w = static_cast<const uint16_t*>(w_packed);
