@@ -727,7 +727,8 @@ def moe_run(args, w, tune):
     kernel = ("tp_moe_layer_decode: moe_layer_kernel (routing, attention slice and expert MFMA "
               "GEMV in one launch) + moe_layer_combine_kernel (local combine, both ring sums)")
     reduce_io = 2 * (w.n_ranks + 2) * T * H * 4
-    extra = {"reduce_io_bytes": reduce_io}
+    # both launches' HBM bytes (the ring sums' included), from the counters
+    extra = {"reduce_io_bytes": reduce_io, "traffic": measured_traffic("%s/layer/bf16" % w.name)}
     plan.close()
     return ms, T, step_bytes - reduce_io, kernel, config, cpu, extra
 
