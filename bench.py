@@ -785,6 +785,7 @@ def moe_cpu_baseline(w, rank, L, slots, h0, plan, budget_s):
         reps += 1
         per_share = spent / reps
     return {"value": w.batch / per_share, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d run(s) of one layer share: attention partial, ring sum and routing in "
                       "full; expert projections + combine on %d of %d columns, scaled to all "
                       "columns; %.1f s in all" % (reps, ncols, H, spent)}
