@@ -333,7 +333,8 @@ def dense_run(args, w, tune):
 
         def step():
             # the activations' layout for the stream is part of the step
-            if info["packed_kind"] == 2:
+            # (none where the stream reads them row-major, as given)
+            if info["packed_kind"] == 2 and info["acts_layout"] == 1:
                 tp.tp_pack_activations(plan, xa, xf, pa, pf)
                 tp.tp_decode_layers_packed(plan, w.layers, args.rank, pa, po, pf, pd, slots, hidden, ws)
             else:

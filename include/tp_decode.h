@@ -97,7 +97,9 @@ typedef struct tp_plan_info {
                                 2 = MFMA tiles (matrix cores) */
     int32_t stream_wgs;      /* packed_kind 2: workgroups of the matrix-core step (0 otherwise) */
     int32_t weight_format;   /* tp_weight_format of the packed step (tp_plan_set_weight_format) */
-    int32_t reserved0;
+    int32_t acts_layout;     /* activations of tp_decode_layers_packed (tp_pack_activations):
+                                0 = row-major [L][b][K_r] as given, 1 = the matrix-core
+                                stream's A-operand order (packed_kind 2 from 5 tokens on) */
     int64_t packed_layer_bytes[2]; /* packed_kind 1: bytes of one layer's packed weights per point */
 } tp_plan_info_t;
 
@@ -169,6 +171,19 @@ tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
  *                stream on pair strips, 2 = matrix-core stream on MFMA tiles),
  * "stream_wgs" (matrix-core stream: workgroups sharing the tiles, 0 = one
  *                per compute unit; at most 256 and H/16, at least H/32),
+ * "mfma_acts" (matrix-core stream: the activations' layout, 0 = automatic:
+ *                row-major up to 4 tokens, else A-operand order;
+ *                1 = row-major (up to 16 tokens), 2 = A-operand order;
+ *                see info.acts_layout),
+ * "mfma_sl", "mfma_wps" (matrix-core stream, up to 32 tokens: tiles per
+ *                register bank and compute waves, the pairs (2, 12) and
+ *                (3, 8); 0 = automatic: (3, 8) up to 16 tokens, else (2, 12)),
+ * "mfma_oth" (matrix-core stream: the other ranks' values are staged up
+ *                to this many points ahead, 2, 4 or 8; 0 = automatic: 2),
+ * "mfma_flat" (matrix-core stream, up to 32 tokens: -1 = automatic (1 from
+ *                8 to 16 tokens), 0 = a register bank per segment of a point,
+ *                1 = a ring of 2 mfma_sl tile slots running across
+ *                segments and points),
  * "moe_variant" (tp_moe_partial's expert kernel: 0 = default, 1..7),
  * "serial_points" (tp_decode_layers and tp_decode_layers_packed: 0 = each
  *                hidden-state element follows its own chain, 1 = point j+1
@@ -440,8 +455,11 @@ tp_status tp_pack_weights_mx(tp_plan_t plan, int32_t point, int32_t n_layers, co
 /*
  * The activation slices of a step in the order tp_decode_layers_packed
  * reads them (part of the decode step: call it once per step).
- *  packed_kind 1: row-major, as given (the bytes are copied).
- *  packed_kind 2: A-operand order of the matrix-core stream,
+ *  info.acts_layout 0 (packed_kind 1, and packed_kind 2 up to 4 tokens):
+ *     row-major, as given (the bytes are copied); the matrix-core stream
+ *     then reads each token's row directly.
+ *  info.acts_layout 1 (packed_kind 2 from 9 tokens on): A-operand order of
+ *     the matrix-core stream,
  *     X[kb][tt][h][l][i] = x[16tt + l%16][64kb + 16(l/16) + 8h + i]
  *     kb < ceil(K_r/64), tt < ceil(b/16), h < 2, lane l < 64, i < 8 (zero
  *     for rows past K_r; entries of tokens past b are left unwritten and

@@ -41,7 +41,7 @@ class tp_plan_info(ctypes.Structure):
         ("local_experts", ctypes.c_int32), ("moe_inter", ctypes.c_int64),
         ("max_tokens", ctypes.c_int32), ("packed_kind", ctypes.c_int32),
         ("stream_wgs", ctypes.c_int32), ("weight_format", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32), ("packed_layer_bytes", ctypes.c_int64 * 2),
+        ("acts_layout", ctypes.c_int32), ("packed_layer_bytes", ctypes.c_int64 * 2),
     ]
 
 
@@ -373,13 +373,13 @@ def packed_shape(plan: Plan, point, n_layers):
 
 def packed_act_shape(plan: Plan, point, n_layers):
     """Shape of a step's activation slices as tp_decode_layers_packed reads them:
-    row-major [L, b, K_r] (pair strips) or A-operand order
-    [L, ceil(K_r/64), ceil(b/16), 2, 64, 8] (MFMA tiles)."""
+    row-major [L, b, K_r] (info acts_layout 0) or the matrix-core stream's
+    A-operand order [L, ceil(K_r/64), ceil(b/16), 2, 64, 8] (acts_layout 1)."""
     if point not in (0, 1):
         raise ValueError("point must be 0 or 1")
     i = plan._plan_info()
     kr, b = i["k_rank"][point], i["batch"]
-    if i["packed_kind"] == 1:
+    if i["packed_kind"] == 1 or (i["packed_kind"] == 2 and i["acts_layout"] == 0):
         return (n_layers, b, kr)
     if i["packed_kind"] == 2:
         return (n_layers, (kr + 63) // 64, (b + 15) // 16, 2, 64, 8)

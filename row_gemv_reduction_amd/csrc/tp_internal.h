@@ -49,6 +49,8 @@ constexpr int valu_rows_max(int batch, int cols) {
 }
 constexpr int kMfmaMinBatch = 16;
 constexpr int kMfmaMaxBatch = 64;
+// The matrix-core stream reads row-major activations up to this batch (automatic choice).
+constexpr int kMfmaRowMajorActsMax = 4;
 constexpr int kMfmaCols = 128;       // columns per MFMA workgroup
 constexpr int kMfmaWaves = 4;
 constexpr int kMfmaKStep = 32;       // k rows per MFMA step
@@ -86,6 +88,11 @@ struct tp_plan_s {
     int32_t stream_flat = -1;   // pair-strip stream, dataflow order: banks across points (1) or a point per bank (0); -1 = automatic
     int32_t moe_variant = 0;    // expert kernel variant (0 = default)
     int32_t stream_wgs = 0;     // MFMA stream: workgroups (0 = one per CU, at most H/16)
+    int32_t mfma_acts = 0;      // MFMA stream: activations 0 = automatic, 1 = row-major, 2 = A-operand order
+    int32_t mfma_sl = 0;        // MFMA stream, up to 32 tokens: tiles per register bank (0 = automatic)
+    int32_t mfma_wps = 0;       // MFMA stream, up to 32 tokens: compute waves (0 = automatic)
+    int32_t mfma_oth = 0;       // MFMA stream: other ranks' values staged in 2, 4 or 8 buffers (0 = automatic)
+    int32_t mfma_flat = -1;     // MFMA stream, up to 32 tokens: register slots across segments (1) or banks per segment (0); -1 = automatic
     int32_t step_rows = 0;      // persistent step: most rows per tile (0 = automatic)
     int32_t step_kind = 0;      // persistent step: 0 = automatic, 1 = vector ALU (b < 16), 2 = matrix cores
     int32_t swiglu_layers = 0;  // tp_gate_up_swiglu: most layers per launch (0 = automatic)
@@ -162,8 +169,12 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
 // Geometry of the MFMA streamed decode step (tp_mfma_stream.hip).
 struct MfmaGeom {
     int32_t grid, block, wps, bt;
+    int32_t sl;                    // tiles per register bank
+    int32_t acts_rm;               // activations read row-major [L][b][K_r] (else A-operand order)
+    int32_t flat;                  // compute waves' register slots run across segments
     int32_t nkb0, nkb1;
     int32_t oth_strip, own_max;    // other ranks' values per owned strip (floats); owned strips
+    int32_t oth_lg;                // points staged ahead: 1 << oth_lg buffers
     int32_t lds_bytes;             // dynamic LDS
 };
 bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g);

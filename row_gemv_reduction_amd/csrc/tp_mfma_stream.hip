@@ -136,7 +136,8 @@ struct MfmaArgs {
     int32_t K0, K1, nkb0, nkb1;
     int32_t layers, n_ranks, rank, chunk;
     int32_t oth_strip;      // LDS floats of the other ranks' values per owned strip
-    int32_t own_max;        // owned strips per workgroup at most (their buffers per parity)
+    int32_t own_max;        // owned strips per workgroup at most (their buffers per staged point)
+    int32_t oth_lg;         // the other ranks' values are staged in 1 << oth_lg buffers
     uint32_t spin_limit;
 };
 
@@ -182,6 +183,16 @@ struct Cursor {
     int s, kb0, len, bpw, rot;  // the segment's strip, tiles, slots per wave, walk rotation
 };
 
+// A compute wave's place in its own stream of tiles, for register slots
+// that run across segment and point boundaries: the wave's m-th tile of
+// segment i of point j. nr = its tiles in the segment (wi + m WPS < len),
+// ns = max(nr, 1) slots (a segment without a tile of this wave still takes
+// one empty slot, so that the wave counts itself there), r0 = rotation.
+struct SlotCursor {
+    int j, i, m;
+    int s, kb0, nr, ns, r0;
+};
+
 // The waves of a workgroup meet through LDS flags, not barriers: a compute
 // wave stores its D tiles of segment e into buffer e % NBUF, counts itself
 // in that buffer's arrivals and goes on streaming; the control wave starts
@@ -189,10 +200,16 @@ struct Cursor {
 // e + 1 once it has read their tiles, which frees the buffer for segment
 // e + NBUF. So a wave waits for its slowest sibling only when it is NBUF
 // segments ahead of it.
-constexpr int kFlagArrived = 0, kFlagConsumed = 4, kFlagStaged = 5, kFlagOthFree = 7, kFlagReduced = 8,
-              kFlagDone = 9, kFlagCount = 10;
-template <int BT, int SL, int WPS, int NSTG, int NBUF>
-__global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
+// The other ranks' values are staged up to kMaxOth points ahead (a ring of
+// 1 << oth_lg LDS buffers, one staged count each).
+constexpr int kMaxOth = 8;
+constexpr int kMaxDBufs = 8;  // D-tile buffers (arrival counts) at most
+constexpr int kFlagArrived = 0, kFlagConsumed = kMaxDBufs, kFlagStaged = kMaxDBufs + 1,
+              kFlagOthFree = kFlagStaged + kMaxOth,
+              kFlagReduced = kFlagOthFree + 1, kFlagDone = kFlagOthFree + 2, kFlagCount = kFlagOthFree + 3;
+template <int BT, int SL, int WPS, int NSTG, int NBUF, bool XRM, bool FLAT>
+__global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(MfmaArgs a) {
+    static_assert(NBUF <= kMaxDBufs, "one arrival count per D-tile buffer");
     constexpr int kRed = WPS * BT * 256;                  // floats of one buffer
     __shared__ __align__(16) float red[NBUF * kRed];       // [NBUF][WPS][BT][64][4] D tiles
     __shared__ __align__(16) float hs[kMaxOwn * BT * 256]; // owned strips' hidden state, [token][16]
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     __shared__ int segtab[2][kMaxSeg][4];
     __shared__ int nseg[2];
     __shared__ int s_last;
-    extern __shared__ __align__(16) float oth[];           // [2][own][(N-1) * B][16] other ranks
+    extern __shared__ __align__(16) float oth[];           // [1 << oth_lg][own][(N-1) * B][16] other ranks
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,6 +233,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
     const int n_points = 2 * a.layers;
     const int B = a.batch;
     const int len = B * a.H;
+    const int noth = 1 << a.oth_lg;  // buffers of the other ranks' values (points staged ahead)
     // strips whose kb = 0 tile is ours: [own0, own0 + nown)
     const int own0 = (int)(((int64_t)g * a.S16 + a.G - 1) / a.G);
     const int nown = (int)(((int64_t)(g + 1) * a.S16 + a.G - 1) / a.G) - own0;
@@ -336,7 +354,9 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                     }
                 }
                 if (!staged) {
-                    wait_flag(&flags[kFlagStaged + t], NSTG * (jj + 1), a.err);  // point j's other values are in LDS
+                    // point j's other values are in LDS (every stager has counted
+                    // its buffer's rounds up to point j)
+                    wait_flag(&flags[kFlagStaged + (j & (noth - 1))], NSTG * ((j >> a.oth_lg) + 1), a.err);
                     lds_wait();
                     staged = true;
                 }
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 // starting at row c (c - 1 past our rank; row 0 if that is N - 1),
                 // and our own value sits at position (rank - c) mod N.
                 const int o = s - own0;
-                const float* oj = oth + ((j & 1) * a.own_max + o) * a.oth_strip;
+                const float* oj = oth + ((j & (noth - 1)) * a.own_max + o) * a.oth_strip;
                 float* slot = a.slots + (int64_t)j * a.n_ranks * len + (int64_t)a.rank * len;
                 float* hso = hs + o * BT * 256;
 #pragma unroll 1
@@ -410,7 +430,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 lds_wait();
                 if (lane == 0) lds_st(&flags[kFlagDone], e + 1);  // vr[e & 1] may be refilled
             }
-            // the other values of point j have been read: their buffer may be refilled (point j + 2)
+            // the other values of point j have been read: their buffer may be refilled (point j + noth)
             lds_wait();
             if (lane == 0) lds_st(&flags[kFlagOthFree], j + 1);
         }
@@ -428,15 +448,17 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
         // ---------------------------------------------------- stager waves
         // The other ranks' 16 values per token of each owned strip, rows
         // ordered (other rank, token), staged with direct global->LDS loads
-        // into oth[j & 1] a point ahead; stager q issues every NSTG-th load.
-        // These waves issue nothing else, so their memory waits are short.
+        // into buffer j mod noth, up to noth - 1 points ahead of the control
+        // wave (a load waits behind the weight stream's loads in flight,
+        // several microseconds, longer than two small points take); stager
+        // q issues every NSTG-th load.
         const int q = wave - 2;
         __syncthreads();  // start
         const int rows = (a.n_ranks - 1) * B;
         const int per_strip = (rows + 15) / 16;
         for (int j = 0; j < n_points; ++j) {
-            // oth[j & 1] was last read at point j - 2
-            wait_flag(&flags[kFlagOthFree], j - 1, a.err);
+            // buffer j mod noth was last read at point j - noth
+            wait_flag(&flags[kFlagOthFree], j - (noth - 1), a.err);
             const float* slot = a.slots + (int64_t)j * a.n_ranks * len;
             for (int n = q; n < nown * per_strip; n += NSTG) {
                 const int o = n / per_strip, r0 = (n - o * per_strip) * 16;
@@ -445,11 +467,11 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 const int ro = row / B, tok = row - ro * B;
                 const int r = ro < a.rank ? ro : ro + 1;
                 const float* src = slot + (int64_t)r * len + (int64_t)tok * a.H + 16 * (own0 + o) + 4 * (lane & 3);
-                float* dst = oth + ((j & 1) * a.own_max + o) * a.oth_strip + r0 * 16;
+                float* dst = oth + ((j & (noth - 1)) * a.own_max + o) * a.oth_strip + r0 * 16;
                 __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void_t*)dst, 16, 0, 0);
             }
             wait_mem();
-            if (lane == 0) lds_add(&flags[kFlagStaged + (j & 1)], 1);
+            if (lane == 0) lds_add(&flags[kFlagStaged + (j & (noth - 1))], 1);
         }
     } else {
         // --------------------------------------------------- compute waves
@@ -479,19 +501,22 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             }
         };
         // A operand of lane l: token 16*tt + l%16, rows 16*(l/16) + 8h .. +7 of
-        // the tile, 16 contiguous bytes of the packed activations
+        // the tile, 16 contiguous bytes of the packed activations (XRM: of
+        // the token's row of x; the 4 lanes of a token and both halves then
+        // read one 128-byte line)
         auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& c) {
             const int t = c.j & 1, l = c.j >> 1;
             const bool live = c.j < n_points;
             const int nkb = t ? a.nkb1 : a.nkb0;
+            const int K = t ? a.K1 : a.K0;
             const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
-            const uint16_t* xb = (t ? a.x1 : a.x0) + (int64_t)l * nkb * BT * 1024;
+            const uint16_t* xb = (t ? a.x1 : a.x0) + (XRM ? (int64_t)l * B * K : (int64_t)l * nkb * BT * 1024);
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
                 kBufferRsrcWord3);
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(live ? xb : a.x0), (short)0, live ? nkb * BT * 2048 : 0,
-                kBufferRsrcWord3);
+                const_cast<uint16_t*>(live ? xb : a.x0), (short)0,
+                live ? (XRM ? B * K * 2 : nkb * BT * 2048) : 0, kBufferRsrcWord3);
             // slots past the segment's tiles read zero (tile nkb is past the
             // strip), and so do the lanes of tokens past b (an offset past the
             // range: their packed entries are never read)
@@ -509,10 +534,16 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h) {
+                        // rows past K (K is a multiple of 8: a lane's 8 rows are all
+                        // inside or all past) and tokens past b read zero
+                        const int tok = 16 * tt + (lane & 15);
+                        const int k = kb * kTileRows + 16 * (lane >> 4) + 8 * h;
+                        const int off = XRM ? (tok < B && k < K ? (tok * K + k) * 2 : 0x7ffffff0)
+                                            : (tok < B ? ((kb * BT + tt) * 2 + h) * 1024 + lane * 16 : 0x7ffffff0);
                         xv[i][h][tt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                       xr, 16 * tt + (lane & 15) < B ? ((kb * BT + tt) * 2 + h) * 1024 + lane * 16 : 0x7ffffff0,
-                                                                       0, 0));
+                                                                       xr, off, 0, 0));
+                    }
             }
         };
         floatx4_t acc[BT];
@@ -544,6 +575,99 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
             ++e;
         };
 
+        if constexpr (FLAT) {
+            // A ring of 2 SL tile slots, each refilled with the wave's tile
+            // 2 SL further on as soon as it is consumed, across segment and
+            // point boundaries (small segments would leave most of a bank
+            // empty). Every slot issues the same loads (empty ranges past a
+            // segment's tiles or past the step), so the waits stay exact.
+            auto fset = [&](SlotCursor& c) {
+                if (c.j >= n_points) return;
+                const int* tb = segtab[c.j & 1][c.i];
+                c.s = tb[0];
+                c.kb0 = tb[1];
+                const int len = tb[2];
+                c.nr = len > wi ? (len - wi + WPS - 1) / WPS : 0;
+                c.ns = c.nr > 0 ? c.nr : 1;
+                c.r0 = tb[3] == kFull && c.nr > 0 ? g % c.nr : 0;
+            };
+            auto fadv = [&](SlotCursor& c) {
+                if (c.j >= n_points) return;
+                if (++c.m >= c.ns) {
+                    c.m = 0;
+                    if (++c.i >= nseg[c.j & 1]) {
+                        c.i = 0;
+                        ++c.j;
+                    }
+                    fset(c);
+                }
+            };
+            auto fissue = [&](u32x4_t (&wv)[2], u32x4_t (&xv)[2][BT], const SlotCursor& c) {
+                const int t = c.j & 1, l = c.j >> 1;
+                const bool live = c.j < n_points;
+                const int nkb = t ? a.nkb1 : a.nkb0;
+                const int K = t ? a.K1 : a.K0;
+                const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
+                const uint16_t* xb = (t ? a.x1 : a.x0) + (XRM ? (int64_t)l * B * K : (int64_t)l * nkb * BT * 1024);
+                const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
+                    kBufferRsrcWord3);
+                const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(live ? xb : a.x0), (short)0,
+                    live ? (XRM ? B * K * 2 : nkb * BT * 2048) : 0, kBufferRsrcWord3);
+                int kb = nkb;  // an empty slot: past the strip, reads zero
+                if (c.nr > 0) {
+                    int mm = c.m + c.r0;
+                    mm = mm >= c.nr ? mm - c.nr : mm;
+                    kb = c.kb0 + wi + mm * WPS;
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wv[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            wr, kb * kTileBytes + h * 1024 + lane * 16, 0,
+                                                            kCachePolicyNT));
+#pragma unroll
+                for (int tt = 0; tt < BT; ++tt)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int tok = 16 * tt + (lane & 15);
+                        const int k = kb * kTileRows + 16 * (lane >> 4) + 8 * h;
+                        const int off = XRM ? (tok < B && k < K ? (tok * K + k) * 2 : 0x7ffffff0)
+                                            : (tok < B ? ((kb * BT + tt) * 2 + h) * 1024 + lane * 16 : 0x7ffffff0);
+                        xv[h][tt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    xr, off, 0, 0));
+                    }
+            };
+            u32x4_t wr_[2 * SL][2], xr_[2 * SL][2][BT];
+            SlotCursor fi{0, 0, 0, 0, 0, 0, 0, 0}, fc;
+            fset(fi);
+            fc = fi;
+#pragma unroll
+            for (int q = 0; q < 2 * SL; ++q) {
+                fissue(wr_[q], xr_[q], fi);
+                fadv(fi);
+            }
+            while (fc.j < n_points) {
+#pragma unroll
+                for (int q = 0; q < 2 * SL; ++q) {
+                    bool last = false;
+                    if (fc.j < n_points) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int tt = 0; tt < BT; ++tt)
+                                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8_t, xr_[q][h][tt]),
+                                    __builtin_bit_cast(bf16x8_t, wr_[q][h]), acc[tt], 0, 0, 0);
+                        last = fc.m == fc.ns - 1;
+                        fadv(fc);
+                    }
+                    fissue(wr_[q], xr_[q], fi);
+                    fadv(fi);
+                    if (last) seg_end();
+                }
+            }
+        } else {
         u32x4_t w0[SL][2], w1[SL][2], x0[SL][2][BT], x1[SL][2][BT];
         Cursor ci{0, 0, 0, 0, 0, 0, 0, 0}, cc;
         set_seg(ci);
@@ -574,6 +698,7 @@ __global__ __launch_bounds__(1024) void decode_stream_mfma(MfmaArgs a) {
                 if (last) seg_end();
             }
         }
+        }
     }
     // The last workgroup to leave clears the exchange flags for the next
     // launch (no workgroup reads them any more).
@@ -598,15 +723,35 @@ typedef void (*mfma_stream_fn)(MfmaArgs);
 // number of compute waves on every SIMD (12, or 8 for three and four token
 // blocks, where the LDS of their D tiles is short), no SIMD carries more of
 // the stream than another. D-tile buffers: 4, or fewer where the LDS is short.
-constexpr int kWps[5] = {0, 12, 12, 8, 8};
+constexpr int kWps[5] = {0, 8, 12, 8, 8};
+constexpr int kSl[5] = {0, 3, 2, 1, 1};
+constexpr int kFlatFromBatch = 8;  // one token block: the slot ring from this batch on
 constexpr int kStagers[5] = {0, 2, 2, 2, 2};
 constexpr int kDBufs[5] = {0, 4, 3, 2, 2};  // D-tile buffers (LDS)
-mfma_stream_fn mfma_stream_kernel(int bt) {
-    switch (bt) {
-        case 1: return decode_stream_mfma<1, 2, kWps[1], kStagers[1], kDBufs[1]>;
-        case 2: return decode_stream_mfma<2, 2, kWps[2], kStagers[2], kDBufs[2]>;
-        case 3: return decode_stream_mfma<3, 1, kWps[3], kStagers[3], kDBufs[3]>;
-        case 4: return decode_stream_mfma<4, 1, kWps[4], kStagers[4], kDBufs[4]>;
+// One token block: tiles per bank and compute waves may be chosen (plan
+// knobs), and so may the activations' layout (row-major or A-operand order).
+// One and two token blocks: banks of 2 tiles on 12 compute waves, or of
+// 3 on 8 (fewer waves per SIMD, the same tiles in flight), each with a bank
+// per segment or a ring of slots across segments (FLAT); one token block may
+// read row-major activations (XRM).
+template <int BT, bool XRM, bool FLAT>
+mfma_stream_fn mfma_stream_kernel_v(int sl, int wps) {
+    if (wps == 12 && sl == 2) return decode_stream_mfma<BT, 2, 12, kStagers[BT], kDBufs[BT], XRM, FLAT>;
+    if (wps == 8 && sl == 3) return decode_stream_mfma<BT, 3, 8, kStagers[BT], kDBufs[BT], XRM, FLAT>;
+    return nullptr;
+}
+mfma_stream_fn mfma_stream_kernel(const MfmaGeom& g) {
+    switch (g.bt) {
+        case 1:
+            if (g.flat) return g.acts_rm ? mfma_stream_kernel_v<1, true, true>(g.sl, g.wps)
+                                         : mfma_stream_kernel_v<1, false, true>(g.sl, g.wps);
+            return g.acts_rm ? mfma_stream_kernel_v<1, true, false>(g.sl, g.wps)
+                             : mfma_stream_kernel_v<1, false, false>(g.sl, g.wps);
+        case 2:
+            return g.flat ? mfma_stream_kernel_v<2, false, true>(g.sl, g.wps)
+                          : mfma_stream_kernel_v<2, false, false>(g.sl, g.wps);
+        case 3: return decode_stream_mfma<3, kSl[3], kWps[3], kStagers[3], kDBufs[3], false, false>;
+        case 4: return decode_stream_mfma<4, kSl[4], kWps[4], kStagers[4], kDBufs[4], false, false>;
     }
     return nullptr;
 }
@@ -640,7 +785,17 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     // two strips' (at most kMaxSeg segments, kMaxOwn owned strips)
     if (S16 > 2 * G || S16 > kXchgMaxStrips) return false;
     const int bt = (b + 15) / 16;
-    const int wps = kWps[bt], nstg = kStagers[bt];
+    // knobs for one and two token blocks (the kernel has those variants only)
+    const bool knobs = bt <= 2;
+    const int wps = knobs && p->mfma_wps ? p->mfma_wps : kWps[bt], nstg = kStagers[bt];
+    const int sl = knobs && p->mfma_sl ? p->mfma_sl : kSl[bt];
+    if (knobs && !((wps == 12 && sl == 2) || (wps == 8 && sl == 3))) return false;
+    const int nbuf = kDBufs[bt];
+    const bool flat = knobs && (p->mfma_flat == 1 || (p->mfma_flat < 0 && bt == 1 && b >= kFlatFromBatch));
+    // activations: row-major up to 8 tokens (read directly, no layout
+    // launch per step), else in A-operand order (1 KB per operand load)
+    const bool acts_rm = p->mfma_acts == 1 || (p->mfma_acts == 0 && b <= kMfmaRowMajorActsMax);
+    if (acts_rm && bt != 1) return false;
     const int64_t nkb0 = (k0 + kTileRows - 1) / kTileRows, nkb1 = (k1 + kTileRows - 1) / kTileRows;
     // static LDS: D tiles of both parities, owned hidden state, a segment's
     // partial, tables; dynamic: the other ranks' values of the owned strips
@@ -649,15 +804,26 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     const int own_max = (int)((S16 + G - 1) / G);
     g->oth_strip = (int32_t)(((p->n_ranks > 1 ? p->n_ranks - 1 : 1) * b * 16 + 255) / 256 * 256);
     g->own_max = own_max;
-    g->lds_bytes = 2 * own_max * g->oth_strip * 4;
-    const int64_t stat = (kDBufs[bt] * wps * bt * 256 + kMaxOwn * bt * 256 + 2 * bt * 256) * 4 + 1024;
+    // staged points: the knob, else 2 (deeper staging measured no faster)
+    int noth = p->mfma_oth ? p->mfma_oth : 2;
+    g->lds_bytes = noth * own_max * g->oth_strip * 4;
+    const int64_t stat = (nbuf * wps * bt * 256 + kMaxOwn * bt * 256 + 2 * bt * 256) * 4 + 1024;
+    while (!p->mfma_oth && noth > 2 && g->lds_bytes + stat > 152 * 1024) {
+        noth /= 2;
+        g->lds_bytes = noth * own_max * g->oth_strip * 4;
+    }
     if (g->lds_bytes + stat > 152 * 1024) return false;
+    g->oth_lg = noth == 8 ? 3 : noth == 4 ? 2 : 1;
     // the largest buffer offsets must fit 32 bits
     if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes * bt >= ((int64_t)1 << 31)) return false;
     if ((int64_t)b * p->hidden >= ((int64_t)1 << 31)) return false;
+    if (acts_rm && (int64_t)b * (k0 > k1 ? k0 : k1) * 2 >= ((int64_t)1 << 31)) return false;
     g->grid = (int32_t)G;
     g->wps = wps;
     g->bt = bt;
+    g->sl = sl;
+    g->acts_rm = acts_rm ? 1 : 0;
+    g->flat = flat ? 1 : 0;
     g->block = (2 + nstg + wps) * 64;
     g->nkb0 = (int32_t)nkb0;
     g->nkb1 = (int32_t)nkb1;
@@ -721,7 +887,7 @@ tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t
         !aligned16(slots) || !aligned16(hidden) || !aligned16(ws) || !aligned16(xpart))
         return TP_ERR_ALIGNMENT;
     if (n_layers == 0) return TP_OK;
-    mfma_stream_fn k = mfma_stream_kernel(geo.bt);
+    mfma_stream_fn k = mfma_stream_kernel(geo);
     if (!k) return TP_ERR_UNSUPPORTED;
     MfmaArgs a;
     a.x0 = static_cast<const uint16_t*>(x_attn);
@@ -750,6 +916,7 @@ tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t
     a.chunk = (int32_t)((int64_t)p->batch * p->hidden / p->n_ranks);
     a.oth_strip = geo.oth_strip;
     a.own_max = geo.own_max;
+    a.oth_lg = geo.oth_lg;
     a.spin_limit = 1u << 20;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                             hipFuncAttributeMaxDynamicSharedMemorySize, geo.lds_bytes) != hipSuccess)

@@ -344,6 +344,21 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
     } else if (!strcmp(key, "stream_wgs")) {
         if (value < 0 || value > kTargetCUs) return TP_ERR_INVALID_ARG;
         p->stream_wgs = (int32_t)value;
+    } else if (!strcmp(key, "mfma_acts")) {
+        if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
+        p->mfma_acts = (int32_t)value;
+    } else if (!strcmp(key, "mfma_sl")) {
+        if (value != 0 && value != 2 && value != 3) return TP_ERR_INVALID_ARG;
+        p->mfma_sl = (int32_t)value;
+    } else if (!strcmp(key, "mfma_oth")) {
+        if (value != 0 && value != 2 && value != 4 && value != 8) return TP_ERR_INVALID_ARG;
+        p->mfma_oth = (int32_t)value;
+    } else if (!strcmp(key, "mfma_flat")) {
+        if (value < -1 || value > 1) return TP_ERR_INVALID_ARG;
+        p->mfma_flat = (int32_t)value;
+    } else if (!strcmp(key, "mfma_wps")) {
+        if (value != 0 && value != 8 && value != 12) return TP_ERR_INVALID_ARG;
+        p->mfma_wps = (int32_t)value;
     } else if (!strcmp(key, "serial_points")) {
         if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
         p->serial_points = (int32_t)value;
@@ -394,7 +409,9 @@ tp_status tp_plan_info(tp_plan_t p, struct tp_plan_info* o) {
     o->max_tokens = p->max_tokens;
     o->packed_kind = tp_packed_kind(p);
     MfmaGeom mg;
-    o->stream_wgs = o->packed_kind == 2 && tp_mfma_geometry(p, &mg) ? mg.grid : 0;
+    const bool mfma = o->packed_kind == 2 && tp_mfma_geometry(p, &mg);
+    o->stream_wgs = mfma ? mg.grid : 0;
+    o->acts_layout = mfma && !mg.acts_rm ? 1 : 0;
     o->weight_format = p->weight_format;
     for (int pt = 0; pt < 2; ++pt)
         o->packed_layer_bytes[pt] = o->packed_kind == 1 ? tp_stream_packed_bytes(p, pt, 1) : 0;

@@ -130,8 +130,11 @@ tp_status tp_pack_activations(tp_plan_t p, int32_t n_layers, const void* x_attn,
     if (x_attn == xa_packed || x_ffn == xf_packed || xa_packed == xf_packed) return TP_ERR_INVALID_ARG;
     const int kind = tp_packed_kind(p);
     if (kind == 0) return TP_ERR_UNSUPPORTED;
-    if (kind == 2) return tp_pack_acts(p, n_layers, x_attn, x_ffn, xa_packed, xf_packed, stream);
-    // the vector-ALU stream reads row-major activations: the same bytes
+    MfmaGeom mg;
+    if (kind == 2 && tp_mfma_geometry(p, &mg) && !mg.acts_rm)
+        return tp_pack_acts(p, n_layers, x_attn, x_ffn, xa_packed, xf_packed, stream);
+    // the vector-ALU stream, and the matrix-core stream for a few tokens,
+    // read row-major activations: the same bytes
     const int64_t per = (int64_t)n_layers * p->batch * 2;
     if (hipMemcpyAsync(xa_packed, x_attn, per * (p->k_attn / p->n_ranks), hipMemcpyDeviceToDevice,
                        (hipStream_t)stream) != hipSuccess ||

@@ -630,8 +630,8 @@ def test_pack_activations_is_the_a_operand_order(n, b, h, ka, ki):
     # X[l][kb][tt][hh][lane][i] = x[l][16tt + lane%16][64kb + 16(lane/16) + 8hh + i], zero past K;
     # entries of tokens past b are not written (compared only where tokens < b)
     L = 2
-    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 2})
-    assert plan.info()["packed_kind"] == 2
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 2, "mfma_acts": 2})
+    assert plan.info()["packed_kind"] == 2 and plan.info()["acts_layout"] == 1
     say("pack activations n=%d b=%d" % (n, b))
     xs = [synth.normal_bf16((L, b, k // n), 1.0, seed=6, tensor="x", layer=pt) for pt, k in ((0, ka), (1, ki))]
     got = [bf16_bits_host(p) for p in pack_acts_dev(plan, xs[0], xs[1])]
@@ -650,11 +650,14 @@ def test_pack_activations_is_the_a_operand_order(n, b, h, ka, ki):
         assert_bits_equal(got[pt][valid], want[valid], "point %d" % pt)
 
 
-def test_pack_activations_copies_for_the_vector_alu_stream():
-    L, n, b, h, ka, ki = 2, 2, 3, 1032, 640, 2016
-    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 1})
-    assert plan.info()["packed_kind"] == 1
-    say("pack activations, row-major")
+@pytest.mark.parametrize("kind,b", [(1, 3), (2, 3), (2, 4)])
+def test_pack_activations_copies_where_read_row_major(kind, b):
+    """The vector-ALU stream, and the matrix-core stream up to 4 tokens,
+    read the activations row-major: tp_pack_activations copies them."""
+    L, n, h, ka, ki = 2, 2, 1040, 640, 2016
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": kind})
+    assert plan.info()["packed_kind"] == kind and plan.info()["acts_layout"] == 0
+    say("pack activations, row-major, kind %d b=%d" % (kind, b))
     xa = synth.normal_bf16((L, b, ka // n), 1.0, seed=7, tensor="x", layer=0)
     xf = synth.normal_bf16((L, b, ki // n), 1.0, seed=7, tensor="x", layer=1)
     pa, pf = pack_acts_dev(plan, xa, xf)
@@ -772,6 +775,39 @@ def test_partials_packed(n, b, h, ka, ki, rank, kind):
     for l in range(L):
         assert_partial_close(got[l, 0], oracle.partial(xa[l], wo[l])[0], "attn l=%d" % l)
         assert_partial_close(got[l, 1], oracle.partial(xf[l], wd[l])[0], "ffn l=%d" % l)
+
+
+MFMA_VARIANTS = [
+    # (mfma_acts, mfma_sl, mfma_wps, mfma_flat, mfma_oth): the matrix-core
+    # stream's activation layouts (1 row-major, 2 A-operand order), register
+    # slots for one token block (0 / -1 = automatic), banks per segment
+    # (flat 0) or a ring of slots across segments (flat 1), other ranks'
+    # values staged 2, 4 or 8 points ahead
+    (1, 0, 0, -1, 0), (2, 0, 0, -1, 0), (1, 2, 12, 0, 2), (1, 2, 12, 1, 0), (1, 3, 8, 0, 8),
+    (1, 3, 8, 1, 2), (2, 3, 8, 1, 8), (2, 2, 12, 1, 4), (2, 3, 8, 0, 4),
+]
+MFMA_VARIANT_SHAPES = [
+    # (n, b, hidden, k_attn, inter, rank): the H4096 N=8 slices; K_r of 160
+    # and 504 rows (ragged row tiles) with 65 strips; 16 tokens row-major;
+    # a tiny stack
+    (8, 1, 4096, 4096, 12288, 7), (4, 5, 1040, 640, 2016, 1), (2, 16, 528, 512, 1376, 0),
+    (3, 7, 48, 48, 96, 1), (4, 27, 1040, 640, 2016, 2),
+]
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,acts,sl,wps,flat,oth",
+                         [c + v for c in MFMA_VARIANT_SHAPES for v in MFMA_VARIANTS
+                          if not (v[0] == 1 and c[1] > 16)])  # row-major: one token block only
+def test_mfma_stream_variants_match_oracle(n, b, h, ka, ki, rank, acts, sl, wps, flat, oth):
+    L = 5  # ten points: every staging buffer is reused
+    say("MFMA stream variant acts=%d sl=%d wps=%d flat=%d oth=%d n=%d b=%d h=%d ka=%d ki=%d"
+        % (acts, sl, wps, flat, oth, n, b, h, ka, ki))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 41, rank)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 2, "mfma_acts": acts, "mfma_sl": sl,
+                                                  "mfma_wps": wps, "mfma_flat": flat, "mfma_oth": oth})
+    assert plan.info()["packed_kind"] == 2
+    assert plan.info()["acts_layout"] == (1 if acts == 2 else 0)
+    check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
 
 
 SEGMENT_CASES = [
