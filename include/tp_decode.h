@@ -199,9 +199,10 @@ tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
  *                tp_qkv_proj rounds it down to an even number, at least 2),
  * "xcd_walk" (the persistent step: 1 = each XCD's workgroups take
  *                contiguous tiles of every round, so that a point's column
- *                tiles share an L2; the same bits; 0 = off, the default:
- *                it pays only where narrow points read a wide x, as the
- *                QKV projection at 16+ tokens),
+ *                tiles share an L2; the same bits; 0 = off; -1 = automatic,
+ *                the default: on for tp_qkv_proj from 16 tokens with at most
+ *                2048 columns, where narrow points read a wide x, off
+ *                elsewhere),
  * "step_rows" (tp_decode_layers, tp_rowparallel_partials,
  *                tp_gate_up_swiglu: most rows per tile of the persistent
  *                step, 0 = automatic: 2048 for 512-column and matrix-core

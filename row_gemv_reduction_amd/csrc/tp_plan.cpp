@@ -369,7 +369,7 @@ tp_status tp_plan_tune(tp_plan_t p, const char* key, int64_t value) {
         if (value < 0 || value > 2) return TP_ERR_INVALID_ARG;
         p->step_kind = (int32_t)value;
     } else if (!strcmp(key, "xcd_walk")) {
-        if (value != 0 && value != 1) return TP_ERR_INVALID_ARG;
+        if (value < -1 || value > 1) return TP_ERR_INVALID_ARG;
         p->xcd_walk = (int32_t)value;
     } else if (!strcmp(key, "step_rows")) {
         if (value < 0 || value > 65536) return TP_ERR_INVALID_ARG;
