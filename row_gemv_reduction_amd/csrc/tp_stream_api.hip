@@ -79,13 +79,12 @@ int tp_packed_kind(const tp_plan_s* p) {
     if (p->stream_kind == 1) return valu ? 1 : 0;
     if (p->stream_kind == 2) return mfma ? 2 : 0;
     // Measured on MI355X: the matrix-core stream is the faster one from b = 5
-    // on, and from b = 2 (or b = 1 with short FFN slices, K_r < 2048) when
-    // every 16-column strip stays within one workgroup (H/16 <= its
-    // workgroups); where strips are cut between workgroups (H = 5120 on 256
-    // CUs) the vector-ALU stream is faster up to b = 4.
+    // on, and at every batch when every 16-column strip stays within one
+    // workgroup (H/16 <= its workgroups: H = 4096, b = 1: 0.240 against
+    // 0.249 ms at N = 4); where strips are cut between workgroups (H = 5120
+    // on 256 CUs) the vector-ALU stream is faster up to b = 4.
     const bool whole = mfma && p->hidden / 16 <= mg.grid;
-    const bool short_k = p->inter / p->n_ranks < 2048;
-    if (valu && p->batch <= 4 && !(whole && (p->batch >= 2 || short_k))) return 1;
+    if (valu && p->batch <= 4 && !whole) return 1;
     if (mfma) return 2;
     return valu ? 1 : 0;
 }

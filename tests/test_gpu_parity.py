@@ -810,6 +810,29 @@ def test_mfma_stream_variants_match_oracle(n, b, h, ka, ki, rank, acts, sl, wps,
     check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
 
 
+VALU_VARIANTS = [
+    # (segment_loads, stream_flat): the vector-ALU stream's banks of 4 or 8
+    # loads, a point per bank (0) or banks across points (1), -1 = automatic
+    (8, -1), (4, -1), (4, 1), (8, 1), (4, 0), (8, 0),
+]
+VALU_VARIANT_SHAPES = [
+    # (n, b, hidden, k_attn, inter, rank)
+    (4, 1, 1032, 640, 2048, 0), (8, 1, 4096, 4096, 12288, 7), (2, 1, 520, 512, 1376, 1),
+    (4, 1, 5120, 5120, 17408, 3),
+]
+
+
+@pytest.mark.parametrize("n,b,h,ka,ki,rank,sl,flat",
+                         [c + v for c in VALU_VARIANT_SHAPES for v in VALU_VARIANTS])
+def test_valu_stream_variants_match_oracle(n, b, h, ka, ki, rank, sl, flat):
+    L = 3
+    say("VALU stream variant sl=%d flat=%d n=%d b=%d h=%d ka=%d ki=%d" % (sl, flat, n, b, h, ka, ki))
+    xa, wo, xf, wd, slots, h0 = make_stack(L, n, b, h, ka, ki, 43, rank)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, tune={"stream_kind": 1, "segment_loads": sl, "stream_flat": flat})
+    assert plan.info()["packed_kind"] == 1
+    check_packed_against_oracle(plan, L, n, rank, xa, wo, xf, wd, slots, h0)
+
+
 SEGMENT_CASES = [
     # (n, b, hidden, k_attn, inter, rank, workgroups): the matrix-core stream
     # with fewer workgroups than strips, so that ranges of tiles cut strips
