@@ -148,9 +148,12 @@ tp_status tp_plan_set_moe(tp_plan_t plan, int32_t n_experts, int32_t top_k, int3
  * TP_WEIGHTS_MXFP8 / TP_WEIGHTS_MXFP4: blocks of 32 consecutive rows (along
  * K) of a column share one E8M0 scale 2^(E-127), elements FP8 E4M3 or FP4
  * E2M1. With an MX format the packed step (tp_decode_layers_packed and its
- * no-alloc and partials-only forms) runs the vector-ALU stream on weights
- * packed by tp_pack_weights_mx, and needs K_r of both points to be
- * multiples of 32 (packed_kind is 0 otherwise). Must be called before the
+ * no-alloc and partials-only forms) runs the vector-ALU stream (packed_kind
+ * 1) or the matrix-core stream (packed_kind 2: up to 16 tokens, no
+ * partials-only form; chosen where 16-column strips stay whole, except
+ * MXFP4 at one token, and beyond 4 tokens; knob stream_kind), on weights packed by
+ * tp_pack_weights_mx, and needs K_r of both points to be multiples of 32
+ * (packed_kind is 0 otherwise). Must be called before the
  * plan is first used. TP_ERR_INVALID_ARG for another value.
  */
 tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
@@ -444,11 +447,17 @@ tp_status tp_quantize_mx(tp_plan_t plan, int32_t point, int32_t n_layers, const 
 /*
  * Pack a point's MX weight stack (tp_quantize_mx's layout) for the packed
  * step, once, at load time: w_packed holds info.packed_layer_bytes[point] *
- * n_layers bytes: first, for every layer, the 16-byte vectors
- * [hidden/4][K_r/R][4 columns][R rows] (R = 4 FP8 codes, or 8 FP4 codes as
- * 4 bytes of two rows each), then, for every layer, the scale words
- * [hidden/4][K_r/32], the 4 columns' E in bytes 0..3. TP_ERR_UNSUPPORTED
- * unless the plan's format is MX and packed_kind is 1.
+ * n_layers bytes.
+ *  packed_kind 1: first, for every layer, the 16-byte vectors
+ *   [hidden/4][K_r/R][4 columns][R rows] (R = 4 FP8 codes, or 8 FP4 codes as
+ *   4 bytes of two rows each), then, for every layer, the scale words
+ *   [hidden/4][K_r/32], the 4 columns' E in bytes 0..3.
+ *  packed_kind 2: tiles [n_layers][hidden/16][ceil(K_r/64)] of 64 rows x 16
+ *   columns: the codes lane-major, lane l holding rows 16(l/16) .. +15 of
+ *   column l%16 (16 FP8 bytes, or 8 bytes of two FP4 rows, the even row in
+ *   the low nibble), then 32 scale bytes [2 blocks][16 columns]; codes and
+ *   scales past K_r are zero (1056 bytes a tile for FP8, 544 for FP4).
+ * TP_ERR_UNSUPPORTED unless the plan's format is MX and packed_kind is 1 or 2.
  */
 tp_status tp_pack_weights_mx(tp_plan_t plan, int32_t point, int32_t n_layers, const void* codes,
                              const void* scales, void* w_packed, void* stream);

@@ -362,7 +362,7 @@ def packed_shape(plan: Plan, point, n_layers):
         raise ValueError("point must be 0 or 1")
     i = plan._plan_info()
     kr, H = i["k_rank"][point], i["hidden"]
-    if i["packed_kind"] == 1 and i["weight_format"] != TP_WEIGHTS_BF16:
+    if i["packed_kind"] in (1, 2) and i["weight_format"] != TP_WEIGHTS_BF16:
         return (n_layers * i["packed_layer_bytes"][point],)
     if i["packed_kind"] == 1:
         return (n_layers, H // 4, (kr + 1) // 2, 8)

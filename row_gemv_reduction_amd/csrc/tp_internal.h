@@ -172,6 +172,8 @@ struct MfmaGeom {
     int32_t sl;                    // tiles per register bank
     int32_t acts_rm;               // activations read row-major [L][b][K_r] (else A-operand order)
     int32_t flat;                  // compute waves' register slots run across segments
+    int32_t wf;                    // weight format (tp_weight_format)
+    int32_t tile_bytes;            // bytes of one packed tile (64 rows x 16 columns)
     int32_t nkb0, nkb1;
     int32_t oth_strip, own_max;    // other ranks' values per owned strip (floats); owned strips
     int32_t oth_lg;                // points staged ahead: 1 << oth_lg buffers
@@ -179,6 +181,11 @@ struct MfmaGeom {
 };
 bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g);
 int64_t tp_xchg_bytes(const tp_plan_s* p);  // exchange buffers of the MFMA stream
+// MX tiles of the matrix-core stream (tp_pack_weights_mx at packed_kind 2)
+// and the bytes of a point's packed stack (any weight format).
+tp_status tp_mx_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* codes,
+                           const void* scales, void* w_packed, void* stream);
+int64_t tp_mfma_packed_bytes(const tp_plan_s* p, int point, int64_t n_layers);
 // The column-parallel up projection: its derived plan (a persistent
 // partials step with the gate and up matrices as the two points), whether
 // the plan supports it, and where its fp32 sums sit in the workspace.

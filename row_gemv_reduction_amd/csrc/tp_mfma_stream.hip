@@ -63,6 +63,79 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kTileBytes = 2048;   // 64 rows x 16 columns of bf16, two operand halves
 constexpr int kTileRows = 64;
 
+// Microscaled weights on the matrix cores: a tile of 64 rows x 16 columns
+// holds the codes lane-major (lane l: the 16 consecutive rows 16(l/16) ..
+// +15 of column l%16, 16 bytes of FP8 or 8 of FP4, the even row of a byte in
+// its low nibble), then the 32 scale bytes of its two 32-row blocks
+// ([block][column]). Lane l's rows lie in block l/32. In registers each
+// half of a lane's rows is widened to the bf16 B operand by gfx950's scaled
+// conversions (the block scale as their scale operand), then multiplied on
+// the bf16 matrix cores like bf16 weights.
+template <int WF>
+constexpr int tile_bytes() {
+    return WF == TP_WEIGHTS_MXFP8 ? 1024 + 32 : WF == TP_WEIGHTS_MXFP4 ? 512 + 32 : kTileBytes;
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// One tile's weights for lane `lane` (tile kb of the range; past the range
+// it reads zero): bf16, both operand halves; MX, the codes and the scale.
+template <int WF>
+__device__ __forceinline__ void load_w_tile(__amdgpu_buffer_rsrc_t wr, int kb, int lane, u32x4_t (&wv)[2],
+                                            uint32_t& sv) {
+    constexpr int TB = tile_bytes<WF>();
+    if constexpr (WF == TP_WEIGHTS_BF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            wv[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    wr, kb * TB + h * 1024 + lane * 16, 0, kCachePolicyNT));
+        sv = 0u;
+    } else {
+        constexpr int CB = WF == TP_WEIGHTS_MXFP8 ? 16 : 8;  // code bytes per lane
+        if constexpr (WF == TP_WEIGHTS_MXFP8) {
+            wv[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    wr, kb * TB + lane * CB, 0, kCachePolicyNT));
+        } else {
+            const u32x2_t c = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                              wr, kb * TB + lane * CB, 0, kCachePolicyNT));
+            wv[0] = u32x4_t{c.x, c.y, 0u, 0u};
+        }
+        wv[1] = u32x4_t{0u, 0u, 0u, 0u};
+        sv = __builtin_amdgcn_raw_buffer_load_b8(wr, kb * TB + 64 * CB + (lane >> 5) * 16 + (lane & 15), 0,
+                                                 kCachePolicyNT);
+    }
+}
+
+// Half h (rows 8h .. 8h+7 of the lane's 16) as the bf16 B operand.
+template <int WF>
+__device__ __forceinline__ bf16x8_t b_operand(const u32x4_t (&wv)[2], uint32_t sv, int h) {
+    if constexpr (WF == TP_WEIGHTS_BF16) {
+        return __builtin_bit_cast(bf16x8_t, wv[h]);
+    } else {
+        // the E8M0 byte as the conversions' scale operand: they read the
+        // binary32's exponent field as E8M0 (the mantissa is ignored)
+        const float sc = __uint_as_float(sv << 23);
+        bf16x2_t q[4];
+        if constexpr (WF == TP_WEIGHTS_MXFP8) {
+            const uint32_t d0 = h ? wv[0].z : wv[0].x, d1 = h ? wv[0].w : wv[0].y;
+            q[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false);
+            q[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true);
+            q[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false);
+            q[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true);
+        } else {
+            const uint32_t d = h ? wv[0].y : wv[0].x;
+            q[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0);
+            q[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1);
+            q[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2);
+            q[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3);
+        }
+        const u32x4_t r{__builtin_bit_cast(uint32_t, q[0]), __builtin_bit_cast(uint32_t, q[1]),
+                        __builtin_bit_cast(uint32_t, q[2]), __builtin_bit_cast(uint32_t, q[3])};
+        return __builtin_bit_cast(bf16x8_t, r);
+    }
+}
+
 // T[l][s][kb][h][lane][i] = W[l][64kb + 16(lane/16) + 8h + i][16s + lane%16]
 __global__ void pack_tiles_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ p,
                                   int64_t layers, int64_t K, int64_t H) {
@@ -117,6 +190,37 @@ __global__ void pack_acts_kernel(const uint16_t* __restrict__ x0, const uint16_t
         if (k0 < K)  // K is a multiple of 8: the 8 rows are all inside or all past
             out = *reinterpret_cast<const u32x4_t*>((second ? x1 : x0) + (l * B + tok) * K + k0);
         *reinterpret_cast<u32x4_t*>((second ? p1 : p0) + w * 8) = out;
+    }
+}
+
+// MX codes [L][K][H] (FP8) or [L][K/2][H] (FP4) and scales [L][K/32][H]
+// -> MX tiles [L][H/16][ceil(K/64)] (codes lane-major, then the 32 scale
+// bytes), zero past K. One thread per (tile, lane): its code bytes, and for
+// lanes < 32 the scale byte (block lane/16, column lane%16).
+template <int WF>
+__global__ void pack_mx_tiles_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                     uint8_t* __restrict__ p, int64_t layers, int64_t K, int64_t H) {
+    constexpr int TB = tile_bytes<WF>(), CB = WF == TP_WEIGHTS_MXFP8 ? 16 : 8;
+    const int64_t strips = H / 16, nkb = (K + kTileRows - 1) / kTileRows;
+    const int64_t crows = WF == TP_WEIGHTS_MXFP8 ? K : K / 2;  // code rows per layer
+    const int64_t total = layers * strips * nkb * 64;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+         v += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t tile = v / 64, lane = v % 64;
+        const int64_t kb = tile % nkb, s = (tile / nkb) % strips, l = tile / (nkb * strips);
+        const int64_t n = 16 * s + lane % 16, r0 = kTileRows * kb + 16 * (lane / 16);
+        uint8_t* out = p + tile * TB;
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            // FP8: byte i = row r0 + i; FP4: byte i = rows r0 + 2i (low nibble), r0 + 2i + 1
+            const int64_t r = WF == TP_WEIGHTS_MXFP8 ? r0 + i : r0 + 2 * i;
+            const int64_t cr = WF == TP_WEIGHTS_MXFP8 ? r : r / 2;
+            out[lane * CB + i] = r < K ? codes[(l * crows + cr) * H + n] : (uint8_t)0;
+        }
+        if (lane < 32) {
+            const int64_t blk = 2 * kb + lane / 16, c = 16 * s + lane % 16;
+            out[64 * CB + lane] = 32 * blk < K ? scales[(l * (K / 32) + blk) * H + c] : (uint8_t)0;
+        }
     }
 }
 
@@ -207,8 +311,9 @@ constexpr int kMaxDBufs = 8;  // D-tile buffers (arrival counts) at most
 constexpr int kFlagArrived = 0, kFlagConsumed = kMaxDBufs, kFlagStaged = kMaxDBufs + 1,
               kFlagOthFree = kFlagStaged + kMaxOth,
               kFlagReduced = kFlagOthFree + 1, kFlagDone = kFlagOthFree + 2, kFlagCount = kFlagOthFree + 3;
-template <int BT, int SL, int WPS, int NSTG, int NBUF, bool XRM, bool FLAT>
+template <int BT, int SL, int WPS, int NSTG, int NBUF, bool XRM, bool FLAT, int WF = TP_WEIGHTS_BF16>
 __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(MfmaArgs a) {
+    constexpr int TB = tile_bytes<WF>();
     static_assert(NBUF <= kMaxDBufs, "one arrival count per D-tile buffer");
     constexpr int kRed = WPS * BT * 256;                  // floats of one buffer
     __shared__ __align__(16) float red[NBUF * kRed];       // [NBUF][WPS][BT][64][4] D tiles
@@ -504,15 +609,15 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
         // the tile, 16 contiguous bytes of the packed activations (XRM: of
         // the token's row of x; the 4 lanes of a token and both halves then
         // read one 128-byte line)
-        auto issue = [&](u32x4_t (&wv)[SL][2], u32x4_t (&xv)[SL][2][BT], const Cursor& c) {
+        auto issue = [&](u32x4_t (&wv)[SL][2], uint32_t (&sv)[SL], u32x4_t (&xv)[SL][2][BT], const Cursor& c) {
             const int t = c.j & 1, l = c.j >> 1;
             const bool live = c.j < n_points;
             const int nkb = t ? a.nkb1 : a.nkb0;
             const int K = t ? a.K1 : a.K0;
-            const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
+            const char* wb = reinterpret_cast<const char*>(t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * TB;
             const uint16_t* xb = (t ? a.x1 : a.x0) + (XRM ? (int64_t)l * B * K : (int64_t)l * nkb * BT * 1024);
             const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
+                const_cast<char*>(live ? wb : reinterpret_cast<const char*>(a.w0)), (short)0, live ? nkb * TB : 0,
                 kBufferRsrcWord3);
             const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(live ? xb : a.x0), (short)0,
@@ -526,11 +631,7 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                 int kl = wi + (c.m0 + i) * WPS + c.rot;
                 kl = kl >= span ? kl - span : kl;
                 const int kb = (c.m0 + i < c.bpw && kl < c.len) ? c.kb0 + kl : nkb;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    wv[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               wr, kb * kTileBytes + h * 1024 + lane * 16, 0,
-                                                               kCachePolicyNT));
+                load_w_tile<WF>(wr, kb, lane, wv[i], sv[i]);
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt)
 #pragma unroll
@@ -549,16 +650,17 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
         floatx4_t acc[BT];
 #pragma unroll
         for (int tt = 0; tt < BT; ++tt) acc[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        auto consume = [&](const u32x4_t (&wv)[SL][2], const u32x4_t (&xv)[SL][2][BT]) {
+        auto consume = [&](const u32x4_t (&wv)[SL][2], const uint32_t (&sv)[SL], const u32x4_t (&xv)[SL][2][BT]) {
 #pragma unroll
             for (int i = 0; i < SL; ++i)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x8_t wb = b_operand<WF>(wv[i], sv[i], h);
 #pragma unroll
                     for (int tt = 0; tt < BT; ++tt)
                         acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xv[i][h][tt]), __builtin_bit_cast(bf16x8_t, wv[i][h]),
-                            acc[tt], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8_t, xv[i][h][tt]), wb, acc[tt], 0, 0, 0);
+                }
         };
         int e = 0;
         auto seg_end = [&]() {
@@ -602,16 +704,16 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                     fset(c);
                 }
             };
-            auto fissue = [&](u32x4_t (&wv)[2], u32x4_t (&xv)[2][BT], const SlotCursor& c) {
+            auto fissue = [&](u32x4_t (&wv)[2], uint32_t& sv, u32x4_t (&xv)[2][BT], const SlotCursor& c) {
                 const int t = c.j & 1, l = c.j >> 1;
                 const bool live = c.j < n_points;
                 const int nkb = t ? a.nkb1 : a.nkb0;
                 const int K = t ? a.K1 : a.K0;
-                const uint16_t* wb = (t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * (kTileBytes / 2);
+                const char* wb = reinterpret_cast<const char*>(t ? a.w1 : a.w0) + ((int64_t)l * a.S16 + c.s) * nkb * TB;
                 const uint16_t* xb = (t ? a.x1 : a.x0) + (XRM ? (int64_t)l * B * K : (int64_t)l * nkb * BT * 1024);
                 const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint16_t*>(live ? wb : a.w0), (short)0, live ? nkb * kTileBytes : 0,
-                    kBufferRsrcWord3);
+                    const_cast<char*>(live ? wb : reinterpret_cast<const char*>(a.w0)), (short)0,
+                    live ? nkb * TB : 0, kBufferRsrcWord3);
                 const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint16_t*>(live ? xb : a.x0), (short)0,
                     live ? (XRM ? B * K * 2 : nkb * BT * 2048) : 0, kBufferRsrcWord3);
@@ -621,11 +723,7 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                     mm = mm >= c.nr ? mm - c.nr : mm;
                     kb = c.kb0 + wi + mm * WPS;
                 }
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    wv[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                            wr, kb * kTileBytes + h * 1024 + lane * 16, 0,
-                                                            kCachePolicyNT));
+                load_w_tile<WF>(wr, kb, lane, wv, sv);
 #pragma unroll
                 for (int tt = 0; tt < BT; ++tt)
 #pragma unroll
@@ -639,12 +737,13 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                     }
             };
             u32x4_t wr_[2 * SL][2], xr_[2 * SL][2][BT];
+            uint32_t sr_[2 * SL];
             SlotCursor fi{0, 0, 0, 0, 0, 0, 0, 0}, fc;
             fset(fi);
             fc = fi;
 #pragma unroll
             for (int q = 0; q < 2 * SL; ++q) {
-                fissue(wr_[q], xr_[q], fi);
+                fissue(wr_[q], sr_[q], xr_[q], fi);
                 fadv(fi);
             }
             while (fc.j < n_points) {
@@ -653,35 +752,37 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                     bool last = false;
                     if (fc.j < n_points) {
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
+                        for (int h = 0; h < 2; ++h) {
+                            const bf16x8_t wb = b_operand<WF>(wr_[q], sr_[q], h);
 #pragma unroll
                             for (int tt = 0; tt < BT; ++tt)
                                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8_t, xr_[q][h][tt]),
-                                    __builtin_bit_cast(bf16x8_t, wr_[q][h]), acc[tt], 0, 0, 0);
+                                    __builtin_bit_cast(bf16x8_t, xr_[q][h][tt]), wb, acc[tt], 0, 0, 0);
+                        }
                         last = fc.m == fc.ns - 1;
                         fadv(fc);
                     }
-                    fissue(wr_[q], xr_[q], fi);
+                    fissue(wr_[q], sr_[q], xr_[q], fi);
                     fadv(fi);
                     if (last) seg_end();
                 }
             }
         } else {
         u32x4_t w0[SL][2], w1[SL][2], x0[SL][2][BT], x1[SL][2][BT];
+        uint32_t s0[SL], s1[SL];
         Cursor ci{0, 0, 0, 0, 0, 0, 0, 0}, cc;
         set_seg(ci);
         cc = ci;
-        issue(w0, x0, ci);
+        issue(w0, s0, x0, ci);
         advance(ci);
-        issue(w1, x1, ci);
+        issue(w1, s1, x1, ci);
         advance(ci);
         while (cc.j < n_points) {
             {
-                consume(w0, x0);
+                consume(w0, s0, x0);
                 const bool last = cc.m0 + SL >= cc.bpw;
                 advance(cc);
-                issue(w0, x0, ci);
+                issue(w0, s0, x0, ci);
                 advance(ci);
                 if (last) seg_end();
             }
@@ -689,11 +790,11 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                 const bool live = cc.j < n_points;
                 bool last = false;
                 if (live) {
-                    consume(w1, x1);
+                    consume(w1, s1, x1);
                     last = cc.m0 + SL >= cc.bpw;
                     advance(cc);
                 }
-                issue(w1, x1, ci);
+                issue(w1, s1, x1, ci);
                 advance(ci);
                 if (last) seg_end();
             }
@@ -740,7 +841,18 @@ mfma_stream_fn mfma_stream_kernel_v(int sl, int wps) {
     if (wps == 8 && sl == 3) return decode_stream_mfma<BT, 3, 8, kStagers[BT], kDBufs[BT], XRM, FLAT>;
     return nullptr;
 }
+// Microscaled weights: one token block, banks of 3 tiles on 8 waves.
+template <int WF>
+mfma_stream_fn mfma_stream_kernel_mx(const MfmaGeom& g) {
+    if (g.bt != 1 || g.sl != 3 || g.wps != 8) return nullptr;
+    if (g.flat) return g.acts_rm ? decode_stream_mfma<1, 3, 8, kStagers[1], kDBufs[1], true, true, WF>
+                                 : decode_stream_mfma<1, 3, 8, kStagers[1], kDBufs[1], false, true, WF>;
+    return g.acts_rm ? decode_stream_mfma<1, 3, 8, kStagers[1], kDBufs[1], true, false, WF>
+                     : decode_stream_mfma<1, 3, 8, kStagers[1], kDBufs[1], false, false, WF>;
+}
 mfma_stream_fn mfma_stream_kernel(const MfmaGeom& g) {
+    if (g.wf == TP_WEIGHTS_MXFP8) return mfma_stream_kernel_mx<TP_WEIGHTS_MXFP8>(g);
+    if (g.wf == TP_WEIGHTS_MXFP4) return mfma_stream_kernel_mx<TP_WEIGHTS_MXFP4>(g);
     switch (g.bt) {
         case 1:
             if (g.flat) return g.acts_rm ? mfma_stream_kernel_v<1, true, true>(g.sl, g.wps)
@@ -790,6 +902,12 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     const int wps = knobs && p->mfma_wps ? p->mfma_wps : kWps[bt], nstg = kStagers[bt];
     const int sl = knobs && p->mfma_sl ? p->mfma_sl : kSl[bt];
     if (knobs && !((wps == 12 && sl == 2) || (wps == 8 && sl == 3))) return false;
+    // microscaled weights: up to 16 tokens, banks of 3 on 8 waves, K_r in
+    // whole 32-row scale blocks
+    const int wf = p->weight_format;
+    if (wf != TP_WEIGHTS_BF16 && (bt != 1 || sl != 3 || wps != 8 || k0 % 32 || k1 % 32)) return false;
+    const int tbytes = wf == TP_WEIGHTS_MXFP8 ? tile_bytes<TP_WEIGHTS_MXFP8>()
+                       : wf == TP_WEIGHTS_MXFP4 ? tile_bytes<TP_WEIGHTS_MXFP4>() : kTileBytes;
     const int nbuf = kDBufs[bt];
     const bool flat = knobs && (p->mfma_flat == 1 || (p->mfma_flat < 0 && bt == 1 && b >= kFlatFromBatch));
     // activations: row-major up to 8 tokens (read directly, no layout
@@ -815,7 +933,9 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     if (g->lds_bytes + stat > 152 * 1024) return false;
     g->oth_lg = noth == 8 ? 3 : noth == 4 ? 2 : 1;
     // the largest buffer offsets must fit 32 bits
-    if ((nkb0 > nkb1 ? nkb0 : nkb1) * kTileBytes * bt >= ((int64_t)1 << 31)) return false;
+    if ((nkb0 > nkb1 ? nkb0 : nkb1) * (int64_t)(tbytes > kTileBytes * bt ? tbytes : kTileBytes * bt) >=
+        ((int64_t)1 << 31))
+        return false;
     if ((int64_t)b * p->hidden >= ((int64_t)1 << 31)) return false;
     if (acts_rm && (int64_t)b * (k0 > k1 ? k0 : k1) * 2 >= ((int64_t)1 << 31)) return false;
     g->grid = (int32_t)G;
@@ -824,6 +944,8 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     g->sl = sl;
     g->acts_rm = acts_rm ? 1 : 0;
     g->flat = flat ? 1 : 0;
+    g->wf = wf;
+    g->tile_bytes = tbytes;
     g->block = (2 + nstg + wps) * 64;
     g->nkb0 = (int32_t)nkb0;
     g->nkb1 = (int32_t)nkb1;
@@ -865,6 +987,26 @@ tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void*
                         void* stream) {
     const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
     return tp_pack_tile_stack(n_layers, K, p->hidden, w, w_packed, stream);
+}
+
+tp_status tp_mx_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* codes,
+                           const void* scales, void* w_packed, void* stream) {
+    const int64_t K = (point == TP_POINT_ATTN_OUT ? p->k_attn : p->inter) / p->n_ranks;
+    const int64_t total = (int64_t)n_layers * (p->hidden / 16) * ((K + kTileRows - 1) / kTileRows) * 64;
+    if (total == 0) return TP_OK;
+    const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+    auto k = p->weight_format == TP_WEIGHTS_MXFP8 ? pack_mx_tiles_kernel<TP_WEIGHTS_MXFP8>
+                                                  : pack_mx_tiles_kernel<TP_WEIGHTS_MXFP4>;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                       static_cast<uint8_t*>(w_packed), (int64_t)n_layers, K, p->hidden);
+    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+}
+
+int64_t tp_mfma_packed_bytes(const tp_plan_s* p, int point, int64_t n_layers) {
+    MfmaGeom g;
+    if (!tp_mfma_geometry(p, &g)) return 0;
+    return n_layers * (p->hidden / 16) * (point == TP_POINT_ATTN_OUT ? g.nkb0 : g.nkb1) * g.tile_bytes;
 }
 
 tp_status tp_decode_mfma_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank,

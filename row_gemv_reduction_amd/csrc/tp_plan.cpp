@@ -414,7 +414,9 @@ tp_status tp_plan_info(tp_plan_t p, struct tp_plan_info* o) {
     o->acts_layout = mfma && !mg.acts_rm ? 1 : 0;
     o->weight_format = p->weight_format;
     for (int pt = 0; pt < 2; ++pt)
-        o->packed_layer_bytes[pt] = o->packed_kind == 1 ? tp_stream_packed_bytes(p, pt, 1) : 0;
+        o->packed_layer_bytes[pt] = o->packed_kind == 1   ? tp_stream_packed_bytes(p, pt, 1)
+                                    : o->packed_kind == 2 ? tp_mfma_packed_bytes(p, pt, 1)
+                                                          : 0;
     return TP_OK;
 }
 

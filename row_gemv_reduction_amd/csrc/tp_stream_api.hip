@@ -74,8 +74,22 @@ int tp_packed_kind(const tp_plan_s* p) {
     StreamGeom sg;
     MfmaGeom mg;
     const bool valu = tp_stream_geometry(p, &sg);
-    if (p->weight_format != TP_WEIGHTS_BF16) return valu ? 1 : 0;  // MX: the vector-ALU stream
     const bool mfma = tp_mfma_geometry(p, &mg);
+    if (p->weight_format != TP_WEIGHTS_BF16) {
+        // MX weights, measured on MI355X: where strips stay whole the
+        // matrix-core stream is as fast or faster (H4096 MXFP8 b=1: N=4
+        // 0.188 against 0.197 ms) except for MXFP4 at one token (N=4 0.172
+        // against 0.156); where strips are cut the vector-ALU stream is
+        // faster; beyond 4 tokens the vector-ALU stream's widened vectors
+        // spill (N=8 b=8: 0.151 against 0.392 ms).
+        if (p->stream_kind == 1) return valu ? 1 : 0;
+        if (p->stream_kind == 2) return mfma ? 2 : 0;
+        const bool whole = mfma && p->hidden / 16 <= mg.grid;
+        const bool fp4_one = p->weight_format == TP_WEIGHTS_MXFP4 && p->batch == 1;
+        if (valu && p->batch <= 4 && (!whole || fp4_one)) return 1;
+        if (mfma) return 2;
+        return valu ? 1 : 0;
+    }
     if (p->stream_kind == 1) return valu ? 1 : 0;
     if (p->stream_kind == 2) return mfma ? 2 : 0;
     // Measured on MI355X: the matrix-core stream is the faster one from b = 5
@@ -117,7 +131,10 @@ tp_status tp_pack_weights_mx(tp_plan_t p, int32_t point, int32_t n_layers, const
     if (!p || !codes || !scales || !w_packed || n_layers < 0) return TP_ERR_INVALID_ARG;
     if (point != TP_POINT_ATTN_OUT && point != TP_POINT_FFN_DOWN) return TP_ERR_INVALID_ARG;
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(w_packed)) return TP_ERR_ALIGNMENT;
-    if (p->weight_format == TP_WEIGHTS_BF16 || tp_packed_kind(p) != 1) return TP_ERR_UNSUPPORTED;
+    if (p->weight_format == TP_WEIGHTS_BF16) return TP_ERR_UNSUPPORTED;
+    const int kind = tp_packed_kind(p);
+    if (kind == 2) return tp_mx_pack_tiles(p, point, n_layers, codes, scales, w_packed, stream);
+    if (kind != 1) return TP_ERR_UNSUPPORTED;
     return tp_mx_pack(p, point, n_layers, codes, scales, w_packed, stream);
 }
 

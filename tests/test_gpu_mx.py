@@ -6,10 +6,11 @@ statically, to MXFP8; MXFP4 weighed too).
   for bit (random weights over many binades, zero blocks, subnormal and
   non-finite weights, the full page-1 FFN slice).
 - tp_pack_weights_mx is a layout change: checked byte for byte.
-- The packed decode step on MX weights: each partial within 1e-5 * rms of
-  the oracle's exact MX projection; the ring stage bit for bit against the
-  oracle's ring chain on the GPU's partials; both point orders, the
-  partials-only and the no-alloc forms give the same bits.
+- The packed decode step on MX weights, on either stream (the vector-ALU
+  stream on pair strips, the matrix-core stream on MX tiles): each partial
+  within 1e-5 * rms of the oracle's exact MX projection; the ring stage bit
+  for bit against the oracle's ring chain on the GPU's partials; both point
+  orders, the partials-only and the no-alloc forms give the same bits.
 """
 import numpy as np
 import pytest
@@ -154,7 +155,7 @@ MX_CASES = [
 def test_mx_decode_matches_oracle(fmt, n, b, h, ka, ki, rank):
     L = 3
     say("MX decode fmt=%d n=%d b=%d h=%d ka=%d ki=%d rank=%d" % (fmt, n, b, h, ka, ki, rank))
-    plan = tp.Plan(h, ki, n, b, k_attn=ka, weight_format=fmt)
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, weight_format=fmt, tune={"stream_kind": 1})
     assert plan.info()["packed_kind"] == 1
     xa, wo, xf, wd, slots, h0 = mx_stack(plan, L, n, b, h, ka, ki, rank, 13)
     qo = quantize_dev(plan, 0, dev_u16(wo))
@@ -266,3 +267,94 @@ def test_mx_page1_full_size_sampled(fmt):
             assert_bits_equal(s_got_, s_or, "scales l=%d pt=%d" % (l, pt))
             ref64, _ = oracle.mx_partial(fmt, bf16_bits_host(x[l]), c_or, s_or)
             assert_partial_close(s_got[l, pt, rank][:, cols], ref64, "partial l=%d pt=%d" % (l, pt))
+
+
+# ------------------------------------------- the matrix-core stream (MX tiles)
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pack_layout_mfma_tiles(fmt):
+    """MX tiles of the matrix-core stream, byte for byte: per tile of 64 rows
+    x 16 columns the codes lane-major (lane l: rows 16(l/16) .. +15 of column
+    l%16; FP8 one byte a row, FP4 two rows a byte), then the 32 scale bytes
+    [block][column]; zero past K (K_r = 160: a half tile)."""
+    L, n, h, ka, ki = 2, 2, 528, 320, 1024
+    plan = tp.Plan(h, ki, n, 1, k_attn=ka, weight_format=fmt, tune={"stream_kind": 2})
+    assert plan.info()["packed_kind"] == 2
+    say("MX tile layout fmt=%d" % fmt)
+    for point, k in ((0, ka // n), (1, ki // n)):
+        w = synth.normal_bf16((L, k, h), synth.WEIGHT_STD, seed=14, tensor="w", layer=point)
+        codes, scales = quantize_dev(plan, point, dev_u16(w))
+        got = u8(pack_mx_dev(plan, point, codes, scales))
+        torch.cuda.synchronize()
+        c, sc = u8(codes), u8(scales)
+        nkb, S = (k + 63) // 64, h // 16
+        if fmt == tp.TP_WEIGHTS_MXFP8:
+            cz = np.zeros((L, 64 * nkb, h), np.uint8)
+            cz[:, :k] = c
+            # rows 64kb + 16g + i, columns 16s + col -> [l][s][kb][g][col][i]
+            cw = cz.reshape(L, nkb, 4, 16, S, 16).transpose(0, 4, 1, 2, 5, 3).reshape(L, S, nkb, 1024)
+        else:
+            cz = np.zeros((L, 32 * nkb, h), np.uint8)
+            cz[:, :k // 2] = c
+            cw = cz.reshape(L, nkb, 4, 8, S, 16).transpose(0, 4, 1, 2, 5, 3).reshape(L, S, nkb, 512)
+        sz = np.zeros((L, 2 * nkb, h), np.uint8)
+        sz[:, :k // 32] = sc
+        sw = sz.reshape(L, nkb, 2, S, 16).transpose(0, 3, 1, 2, 4).reshape(L, S, nkb, 32)
+        want = np.concatenate([cw, sw], axis=3)
+        assert_bits_equal(got, want.ravel(), "tiles point %d" % point)
+
+
+MX_MFMA_CASES = [
+    # (n, b, hidden, k_attn, inter, rank): the H4096 N=8 slices; K_r of 160
+    # and 512 (a half tile) with 65 strips and activations in A-operand
+    # order; 672 rows (ragged) at 3 tokens row-major; 16 tokens; one rank
+    (8, 1, 4096, 4096, 12288, 7), (4, 5, 1040, 640, 2048, 1), (2, 3, 528, 512, 1344, 0),
+    (4, 16, 256, 512, 1024, 2), (1, 2, 64, 64, 128, 0),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,b,h,ka,ki,rank", MX_MFMA_CASES)
+def test_mx_mfma_stream_matches_oracle(fmt, n, b, h, ka, ki, rank):
+    """The matrix-core stream on MX tiles: each partial within 1e-5 * rms of
+    the oracle's exact MX projection, the ring stage bit for bit against the
+    oracle's ring chain on the GPU's partials, in both ways of holding the
+    tiles in registers (a bank per segment, a ring of slots) and both
+    activation layouts; the no-alloc form gives the same bits."""
+    L = 3
+    say("MX matrix-core stream fmt=%d n=%d b=%d h=%d ka=%d ki=%d rank=%d" % (fmt, n, b, h, ka, ki, rank))
+    plan = tp.Plan(h, ki, n, b, k_attn=ka, weight_format=fmt, tune={"stream_kind": 2})
+    assert plan.info()["packed_kind"] == 2
+    xa, wo, xf, wd, slots, h0 = mx_stack(plan, L, n, b, h, ka, ki, rank, 15)
+    qo = quantize_dev(plan, 0, dev_u16(wo))
+    qd = quantize_dev(plan, 1, dev_u16(wd))
+    po, pd = pack_mx_dev(plan, 0, *qo), pack_mx_dev(plan, 1, *qd)
+    co, so = u8(qo[0]), u8(qo[1])
+    cd, sd = u8(qd[0]), u8(qd[1])
+    refs = [(oracle.mx_partial(fmt, xa[l], co[l], so[l])[0], oracle.mx_partial(fmt, xf[l], cd[l], sd[l])[0])
+            for l in range(L)]
+    others = [r for r in range(n) if r != rank]
+    for flat in (0, 1):
+        for acts in ((1, 2) if b <= 16 else (2,)):
+            plan.tune("mfma_flat", flat)
+            plan.tune("mfma_acts", acts)
+            XA, XF = dev_u16(xa), dev_u16(xf)
+            pa = torch.empty(tp.packed_act_shape(plan, 0, L), dtype=torch.bfloat16, device="cuda")
+            pf = torch.empty(tp.packed_act_shape(plan, 1, L), dtype=torch.bfloat16, device="cuda")
+            tp.tp_pack_activations(plan, XA, XF, pa, pf)
+            ws = plan.new_workspace()
+            S, Hd = torch.from_numpy(slots).cuda(), torch.from_numpy(h0).cuda()
+            tp.tp_decode_layers_packed(plan, L, rank, pa, po, pf, pd, S, Hd, ws)
+            S2, H2 = torch.from_numpy(slots).cuda(), torch.from_numpy(h0).cuda()
+            tp.tp_decode_layers_packed_noalloc(plan, L, rank, pa, po, pf, pd, S2, H2)
+            torch.cuda.synchronize()
+            assert tp.tp_workspace_status(plan, ws) == 0
+            s_gpu, h_gpu = host(S), host(Hd)
+            what = "flat=%d acts=%d" % (flat, acts)
+            assert_bits_equal(host(S2), s_gpu, "no-alloc slots " + what)
+            assert_bits_equal(host(H2), h_gpu, "no-alloc hidden " + what)
+            for l in range(L):
+                assert_partial_close(s_gpu[l, 0, rank], refs[l][0], "attn l=%d %s" % (l, what))
+                assert_partial_close(s_gpu[l, 1, rank], refs[l][1], "ffn l=%d %s" % (l, what))
+            assert_bits_equal(s_gpu[:, :, others], slots[:, :, others], "other ranks' slots untouched")
+            assert_bits_equal(h_gpu, ring_chain(s_gpu, h0), "hidden vs the oracle's ring chain " + what)
