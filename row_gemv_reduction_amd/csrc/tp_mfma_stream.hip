@@ -582,17 +582,34 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
         // --------------------------------------------------- compute waves
         const int wi = wave - 2 - NSTG;
         __syncthreads();  // start: the segment tables are in LDS
-        auto set_seg = [&](Cursor& c) {
-            if (c.j >= n_points) return;
-            const int* tb = segtab[c.j & 1][c.i];
+        // whole strips start their walk at different places (a rotation by
+        // whole rounds of WPS tiles), so that workgroups do not all read the
+        // same rows of x at the same moment
+        auto seg_fields = [&](const int* tb, Cursor& c) {
             c.s = tb[0];
             c.kb0 = tb[1];
             c.len = tb[2];
             c.bpw = (c.len + WPS - 1) / WPS;
-            // whole strips start their walk at different places (a rotation
-            // by whole rounds of WPS tiles), so that workgroups do not all
-            // read the same rows of x at the same moment
             c.rot = tb[3] == kFull ? (g % c.bpw) * WPS : 0;
+        };
+        // The first segment of each kind of point (every segment where
+        // strips stay whole) is read and its walk worked out once, so that
+        // a bank's issue needs no LDS read or division at small points.
+        Cursor first0{}, first1{};
+        seg_fields(segtab[0][0], first0);
+        seg_fields(segtab[1][0], first1);
+        auto set_seg = [&](Cursor& c) {
+            if (c.j >= n_points) return;
+            if (c.i == 0) {
+                const Cursor& f = (c.j & 1) ? first1 : first0;
+                c.s = f.s;
+                c.kb0 = f.kb0;
+                c.len = f.len;
+                c.bpw = f.bpw;
+                c.rot = f.rot;
+                return;
+            }
+            seg_fields(segtab[c.j & 1][c.i], c);
         };
         auto advance = [&](Cursor& c) {
             c.m0 += SL;
@@ -683,15 +700,30 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
             // point boundaries (small segments would leave most of a bank
             // empty). Every slot issues the same loads (empty ranges past a
             // segment's tiles or past the step), so the waits stay exact.
-            auto fset = [&](SlotCursor& c) {
-                if (c.j >= n_points) return;
-                const int* tb = segtab[c.j & 1][c.i];
+            auto slot_fields = [&](const int* tb, SlotCursor& c) {
                 c.s = tb[0];
                 c.kb0 = tb[1];
                 const int len = tb[2];
                 c.nr = len > wi ? (len - wi + WPS - 1) / WPS : 0;
                 c.ns = c.nr > 0 ? c.nr : 1;
                 c.r0 = tb[3] == kFull && c.nr > 0 ? g % c.nr : 0;
+            };
+            // the first segment of each kind worked out once (as for the banks)
+            SlotCursor sfirst0{}, sfirst1{};
+            slot_fields(segtab[0][0], sfirst0);
+            slot_fields(segtab[1][0], sfirst1);
+            auto fset = [&](SlotCursor& c) {
+                if (c.j >= n_points) return;
+                if (c.i == 0) {
+                    const SlotCursor& f = (c.j & 1) ? sfirst1 : sfirst0;
+                    c.s = f.s;
+                    c.kb0 = f.kb0;
+                    c.nr = f.nr;
+                    c.ns = f.ns;
+                    c.r0 = f.r0;
+                    return;
+                }
+                slot_fields(segtab[c.j & 1][c.i], c);
             };
             auto fadv = [&](SlotCursor& c) {
                 if (c.j >= n_points) return;
