@@ -598,6 +598,7 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
         Cursor first0{}, first1{};
         seg_fields(segtab[0][0], first0);
         seg_fields(segtab[1][0], first1);
+        const int nseg0 = nseg[0], nseg1 = nseg[1];  // segments per kind of point
         auto set_seg = [&](Cursor& c) {
             if (c.j >= n_points) return;
             if (c.i == 0) {
@@ -615,7 +616,7 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
             c.m0 += SL;
             if (c.m0 >= c.bpw) {
                 c.m0 = 0;
-                if (++c.i >= nseg[c.j & 1]) {
+                if (++c.i >= ((c.j & 1) ? nseg1 : nseg0)) {
                     c.i = 0;
                     ++c.j;
                 }
@@ -729,7 +730,7 @@ __global__ __launch_bounds__((2 + NSTG + WPS) * 64) void decode_stream_mfma(Mfma
                 if (c.j >= n_points) return;
                 if (++c.m >= c.ns) {
                     c.m = 0;
-                    if (++c.i >= nseg[c.j & 1]) {
+                    if (++c.i >= ((c.j & 1) ? nseg1 : nseg0)) {
                         c.i = 0;
                         ++c.j;
                     }
