@@ -516,7 +516,9 @@ tp_status tp_pack_activations(tp_plan_t plan, int32_t n_layers, const void* x_at
  * activation slices of a point within about 150 KiB of on-chip buffers and
  * 16 * batch * ceil(hidden / 1024) <= 192; packed_kind 2 needs batch <= 64,
  * n_ranks <= 8, hidden a multiple of 16, K_r a multiple of 8 and
- * hidden/16 <= 2 * stream_wgs), or with "serial_points" = 1 on packed_kind 2.
+ * hidden/16 <= 2 * stream_wgs), or with "serial_points" = 1 on packed_kind 2
+ * or on a packed_kind 1 stream of more than 256 workgroups (hidden above
+ * 15,360: one cooperative workgroup per compute unit).
  */
 tp_status tp_decode_layers_packed(tp_plan_t plan, int32_t n_layers, int32_t rank,
                                   const void* x_attn, const void* w_o_packed,

@@ -939,6 +939,9 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     if (geo.grid > 1024) return TP_ERR_UNSUPPORTED;  // completion words of the serial order
     if (n_layers == 0) return TP_OK;
     const bool serial = p->serial_points != 0 && !partials;
+    // the serial order's cooperative launch holds one workgroup per compute
+    // unit, and its wait reads 256 completion words
+    if (serial && geo.grid > kTargetCUs) return TP_ERR_UNSUPPORTED;
     // the dataflow order takes the stream block by block across points where
     // a layer's blocks fit one bank (small points: measured up to 33 %
     // faster; larger points, up to 5 % slower that way, keep a point per bank)

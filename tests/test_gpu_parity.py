@@ -666,10 +666,19 @@ def test_pack_activations_copies_where_read_row_major(kind, b):
     assert_bits_equal(bf16_bits_host(pf), xf, "x_ffn")
 
 
+def valu_stream_grid(hidden):
+    """Workgroups of the vector-ALU stream: 4-column strips dealt to 256
+    workgroups, at most 15 strips each."""
+    strips = hidden // 4
+    per = min(-(-strips // 256), 15)
+    return -(-strips // per)
+
+
 def run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps=1):
     """Both point orders on the same inputs; they must give the same bits.
-    (The serial order exists on the vector-ALU stream only.)"""
-    if plan.info()["packed_kind"] == 2:
+    (The serial order exists on the vector-ALU stream only, up to 256
+    workgroups: one per compute unit in its cooperative launch.)"""
+    if plan.info()["packed_kind"] == 2 or valu_stream_grid(plan.info()["hidden"]) > 256:
         plan.tune("serial_points", 1)
         with pytest.raises(tp.TPError):
             _run_decode_packed(plan, L, rank, xa, wo, xf, wd, slots, h0, steps)
@@ -707,6 +716,9 @@ PACKED_CASES = [
     (4, 17, 1024, 1024, 4096, 2, 2), (8, 33, 512, 512, 1024, 5, 2), (4, 64, 1024, 2048, 4096, 3, 2),
     (1, 20, 256, 256, 512, 0, 2), (3, 7, 48, 48, 96, 1, 2), (4, 1, 1024, 1024, 2048, 2, 2),
     (2, 48, 4112, 256, 512, 1, 2),
+    # 274 workgroups of 15 strips: the dataflow order only (the serial
+    # order is refused beyond one workgroup per compute unit)
+    (2, 1, 16400, 128, 256, 1, 1),
 ]
 
 
