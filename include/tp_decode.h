@@ -735,6 +735,18 @@ tp_status tp_moe_layer_decode(tp_plan_t plan, int32_t rank, const float* logits,
 tp_status tp_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups,
                                void* stream);
 
+/*
+ * Debug mode, process-wide: with on = 1 every entry point waits for its
+ * stream after each kernel launch and returns TP_ERR_DEVICE from the call
+ * whose kernel failed (a fault, an abort, a launch error), rather than
+ * leaving it to a later call; nothing waits while the stream is being
+ * captured into a graph. Off by default; on from the first launch if the
+ * environment variable TP_DEBUG_SYNC is set to a value other than "0".
+ * Slows every call down by a host round trip. TP_ERR_INVALID_ARG unless on
+ * is 0 or 1.
+ */
+tp_status tp_set_debug_sync(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

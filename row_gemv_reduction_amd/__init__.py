@@ -15,6 +15,6 @@ from .binding import (  # noqa: F401
     tp_moe_pack_experts, tp_moe_partial, tp_moe_route, tp_pack_weights,
     moe_attn_packed_shape, tp_moe_pack_attn, tp_moe_layer_decode,
     tp_plan, tp_ring_reduce, tp_rowparallel_partial, tp_rowparallel_partials,
-    tp_rowparallel_partials_packed, tp_stream_read_probe, tp_workspace_init,
+    tp_rowparallel_partials_packed, tp_set_debug_sync, tp_stream_read_probe, tp_workspace_init,
     tp_workspace_status,
 )

@@ -109,6 +109,7 @@ EXPORTS = {
                           + [ctypes.c_void_p] * 8),
     "tp_stream_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_int32, ctypes.c_void_p]),
+    "tp_set_debug_sync": (ctypes.c_int, [ctypes.c_int32]),
 }
 
 
@@ -595,6 +596,13 @@ def tp_moe_layer_decode(plan: Plan, rank, logits, x_attn, w_attn_packed, u, w_pa
         raise ValueError("workspace too small")
     _check(_lib().tp_moe_layer_decode(plan.handle, rank, lg, 1 if renorm else 0, *args, _stream()),
            "tp_moe_layer_decode")
+
+
+def tp_set_debug_sync(on) -> None:
+    """Debug mode, process-wide: each entry point waits for its stream after
+    every kernel launch and raises from the call whose kernel failed (not
+    while the stream is captured into a graph). `on` is 0/1 or a bool."""
+    _check(_lib().tp_set_debug_sync(int(on)), "tp_set_debug_sync")
 
 
 def tp_stream_read_probe(buf, sink):

@@ -229,3 +229,8 @@ tp_status tp_scratch_status(int32_t* flags);
 // Packed layout (and streamed kernel) the plan uses: 0 none, 1 pair strips, 2 MFMA tiles.
 int tp_packed_kind(const tp_plan_s* p);
 int64_t tp_moe_workspace_bytes(const tp_plan_s* p);  // pair table and expert projections
+
+// After a kernel launch: TP_ERR_DEVICE if the launch failed; with the debug
+// mode on (tp_set_debug_sync), also waits for the stream (unless it is being
+// captured) and reports an error the kernels raised.
+tp_status tp_launch_status(void* stream);

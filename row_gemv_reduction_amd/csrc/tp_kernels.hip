@@ -38,6 +38,10 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
 
 #include "tp_device.h"
 #include "tp_internal.h"
@@ -1169,7 +1173,7 @@ tp_status launch_projection(const tp_plan_s* p, const PointGeom& g, int batch, c
         if (!k) return TP_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(k, dim3(g.grid), dim3(kMfmaWaves * 64), 0, st, a, batch);
     }
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(st);
 }
 
 // The persistent step; with `partials` set, only the 2L partials (no ring,
@@ -1246,7 +1250,7 @@ tp_status decode_persistent(const tp_plan_s* p, int32_t n_layers, int32_t rank, 
     if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(block), args,
                                    0, st) != hipSuccess)
         return TP_ERR_DEVICE;
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(st);
 }
 
 }  // namespace
@@ -1255,10 +1259,40 @@ tp_status tp_fill_u32(uint32_t* p, int64_t n, uint32_t v, void* stream) {
     if (n <= 0) return TP_OK;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, p, n, v);
+    return tp_launch_status(stream);
+}
+
+// Debug mode: -1 until first read (then the environment decides), 0 or 1.
+static std::atomic<int> g_debug_sync{-1};
+
+static bool debug_sync_on() {
+    int v = g_debug_sync.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = getenv("TP_DEBUG_SYNC");
+        int want = e && e[0] && strcmp(e, "0") != 0 ? 1 : 0;
+        g_debug_sync.compare_exchange_strong(v, want);
+        v = g_debug_sync.load(std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
+tp_status tp_launch_status(void* stream) {
+    if (hipGetLastError() != hipSuccess) return TP_ERR_DEVICE;
+    if (!debug_sync_on()) return TP_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return TP_ERR_DEVICE;
+    if (cs != hipStreamCaptureStatusNone) return TP_OK;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TP_ERR_DEVICE;
     return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
 }
 
 extern "C" {
+
+tp_status tp_set_debug_sync(int32_t on) {
+    if (on != 0 && on != 1) return TP_ERR_INVALID_ARG;
+    g_debug_sync.store(on, std::memory_order_relaxed);
+    return TP_OK;
+}
 
 tp_status tp_workspace_init(tp_plan_t p, void* ws, void* stream) {
     if (!p || !ws) return TP_ERR_INVALID_ARG;
@@ -1266,7 +1300,7 @@ tp_status tp_workspace_init(tp_plan_t p, void* ws, void* stream) {
     int64_t n = kCounterBytes / 4;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, ws_counters(ws), n, 0u);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_workspace_status(tp_plan_t p, const void* ws, int32_t* flags) {
@@ -1370,7 +1404,7 @@ tp_status tp_qkv_proj(tp_plan_t p, int32_t n_layers, const void* x, const void* 
         const int64_t total = (int64_t)(lstep == 2 ? 2 * units : 1) * b * C;
         hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, sums,
                            ob + (int64_t)l0 * b * C, total);
-        return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+        return tp_launch_status(stream);
     };
     for (int32_t k = 0; k < launches; ++k) {
         // layer pairs spread evenly over the launches
@@ -1429,7 +1463,7 @@ tp_status tp_ring_reduce(tp_plan_t p, const float* partials, const float* residu
     hipLaunchKernelGGL(ring_reduce_kernel, dim3((unsigned)((len + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, partials, residual, out,
                        static_cast<uint16_t*>(out_bf16), len, chunk, (int)p->n_ranks);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_decode_point(tp_plan_t p, int32_t point, int32_t rank, const void* x, const void* w,

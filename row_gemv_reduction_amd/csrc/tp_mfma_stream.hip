@@ -1003,7 +1003,7 @@ tp_status tp_pack_acts(const tp_plan_s* p, int n_layers, const void* x_attn, con
                        static_cast<const uint16_t*>(x_attn), static_cast<const uint16_t*>(x_ffn),
                        static_cast<uint16_t*>(xa_packed), static_cast<uint16_t*>(xf_packed),
                        (int64_t)n_layers, (int64_t)p->batch, K0, K1, bt);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_pack_tile_stack(int64_t n_mats, int64_t K, int64_t H, const void* w, void* w_packed,
@@ -1013,7 +1013,7 @@ tp_status tp_pack_tile_stack(int64_t n_mats, int64_t K, int64_t H, const void* w
     const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
     hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint16_t*>(w), static_cast<uint16_t*>(w_packed), n_mats, K, H);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_pack_tiles(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
@@ -1033,7 +1033,7 @@ tp_status tp_mx_pack_tiles(const tp_plan_s* p, int point, int n_layers, const vo
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
                        static_cast<uint8_t*>(w_packed), (int64_t)n_layers, K, p->hidden);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 int64_t tp_mfma_packed_bytes(const tp_plan_s* p, int point, int64_t n_layers) {
@@ -1102,5 +1102,5 @@ tp_status tp_decode_mfma_stream_at(const tp_plan_s* p, int32_t n_layers, int32_t
     if (geo.grid > device_cus()) return TP_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(k, dim3((unsigned)geo.grid), dim3((unsigned)geo.block), (unsigned)geo.lds_bytes,
                        (hipStream_t)stream, a);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }

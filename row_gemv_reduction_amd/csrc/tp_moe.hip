@@ -674,7 +674,7 @@ tp_status tp_moe_route(tp_plan_t p, const float* logits, int32_t tokens, int32_t
     hipLaunchKernelGGL(k, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, (hipStream_t)stream, logits,
                        (int)tokens, (int)p->n_experts, (int)p->top_k, (int)(renorm != 0), sel_expert,
                        sel_weight);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_moe_pack_experts(tp_plan_t p, const void* w_local, void* w_packed, void* stream) {
@@ -715,7 +715,7 @@ tp_status moe_experts(const tp_plan_s* p, int32_t rank, const int32_t* sel_exper
     a.col_blocks = (int32_t)((S16 + v.sb - 1) / v.sb);
     const int64_t grid = el * a.col_blocks;
     hipLaunchKernelGGL(v.fn, dim3((unsigned)grid), dim3(v.nw * 64), 0, st, a);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(st);
 }
 
 }  // namespace
@@ -738,7 +738,7 @@ tp_status tp_moe_partial(tp_plan_t p, int32_t rank, const int32_t* sel_expert,
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n_out / 4 + 255) / 256)), dim3(256), 0, st,
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
                        (int)p->top_k, (int)H, part);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, const float* sel_weight,
@@ -761,7 +761,7 @@ tp_status tp_moe_decode(tp_plan_t p, int32_t rank, const int32_t* sel_expert, co
     hipLaunchKernelGGL(moe_combine_ring_kernel, dim3((unsigned)((len / 4 + 255) / 256)), dim3(256), 0, st,
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)tokens,
                        (int)p->top_k, (int)H, slots, hidden, (int)p->n_ranks, (int)rank, len / p->n_ranks);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_moe_pack_attn(tp_plan_t p, const void* w, void* w_packed, void* stream) {
@@ -842,7 +842,7 @@ tp_status tp_moe_layer_decode(tp_plan_t p, int32_t rank, const float* logits, in
                        sel_expert, sel_weight, moe_rows(p, ws), (int)(rank * el), (int)el, (int)T,
                        (int)p->top_k, (int)H, slots_attn, slots_moe, hidden, (int)p->n_ranks, (int)rank,
                        len / p->n_ranks, a.ctr);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 }  // extern "C"

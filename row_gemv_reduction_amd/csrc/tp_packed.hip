@@ -891,7 +891,7 @@ tp_status tp_mx_quantize(const tp_plan_s* p, int point, int n_layers, const void
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
                        static_cast<uint8_t*>(scales), (int64_t)n_layers, K, p->hidden);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_mx_pack(const tp_plan_s* p, int point, int n_layers, const void* codes, const void* scales,
@@ -908,7 +908,7 @@ tp_status tp_mx_pack(const tp_plan_s* p, int point, int n_layers, const void* co
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
                        static_cast<uint8_t*>(w_packed), (int64_t)n_layers, K, p->hidden);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void* w, void* w_packed,
@@ -920,7 +920,7 @@ tp_status tp_pack_pairs(const tp_plan_s* p, int point, int n_layers, const void*
     hipLaunchKernelGGL(pack_pairs_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint16_t*>(w), static_cast<uint16_t*>(w_packed),
                        (int64_t)n_layers, K, p->hidden);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, const void* x_attn,
@@ -1003,6 +1003,6 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
         hipLaunchKernelGGL(k, dim3((unsigned)geo.grid), dim3((unsigned)geo.block),
                            (unsigned)geo.lds_bytes, (hipStream_t)stream, a);
     }
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 

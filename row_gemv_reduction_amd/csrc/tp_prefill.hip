@@ -425,7 +425,7 @@ tp_status tp_prefill_layers(tp_plan_t p, int32_t n_layers, int32_t rank, int32_t
     if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(kPfThreads), args, 0,
                                    (hipStream_t)stream) != hipSuccess)
         return TP_ERR_DEVICE;
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }
 
 }  // extern "C"

@@ -62,5 +62,5 @@ extern "C" tp_status tp_stream_read_probe(const void* buf, int64_t bytes, uint32
     if (bytes == 0) return TP_OK;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)workgroups), dim3(kProbeBlock), 0,
                        (hipStream_t)stream, static_cast<const u32x4_t*>(buf), bytes / 16, sink);
-    return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_DEVICE;
+    return tp_launch_status(stream);
 }

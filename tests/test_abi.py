@@ -156,3 +156,12 @@ def test_weight_format_plans():
     assert L.tp_plan_set_weight_format(h, -1) == TP_ERR_INVALID_ARG
     assert L.tp_plan_set_weight_format(h, 1) == TP_OK
     L.tp_plan_destroy(h)
+
+
+def test_debug_sync_switch():
+    """The debug mode's switch takes 0 and 1 and refuses anything else (no
+    device call is made: the mode only acts at the next launch)."""
+    binding.tp_set_debug_sync(1)
+    binding.tp_set_debug_sync(0)
+    with pytest.raises(binding.TPError):
+        binding.tp_set_debug_sync(2)

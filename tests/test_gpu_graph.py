@@ -85,6 +85,17 @@ def test_partial_and_ring_sequence_replays_bitwise(b):
     plan.close()
 
 
+def test_debug_sync_mode_eager_and_graph():
+    """With the library's debug mode on (a stream wait and an error check
+    after every launch) the same sequence runs eagerly, and a graph captured
+    meanwhile (no waits while capturing) replays it bit for bit."""
+    tp.tp_set_debug_sync(1)
+    try:
+        test_partial_and_ring_sequence_replays_bitwise(4)
+    finally:
+        tp.tp_set_debug_sync(0)
+
+
 def test_moe_share_on_two_streams_replays_bitwise():
     T, E, k, I, H, ep, KA = 64, 32, 4, 512, 1024, 4, 2048
     rank = 2
