@@ -184,7 +184,9 @@ tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
  * "mfma_oth" (matrix-core stream: the other ranks' values are staged up
  *                to this many points ahead, 2, 4 or 8; 0 = automatic: 2),
  * "mfma_flat" (matrix-core stream, up to 32 tokens: -1 = automatic (1 from
- *                8 to 16 tokens), 0 = a register bank per segment of a point,
+ *                8 to 16 tokens, and with bf16 weights below 8 tokens where
+ *                a layer's tiles per compute wave fit the ring of slots,
+ *                e.g. H4096 N=8), 0 = a register bank per segment of a point,
  *                1 = a ring of 2 mfma_sl tile slots running across
  *                segments and points),
  * "moe_variant" (tp_moe_partial's expert kernel: 0 = default, 1..7),

@@ -942,12 +942,19 @@ bool tp_mfma_geometry(const tp_plan_s* p, MfmaGeom* g) {
     const int tbytes = wf == TP_WEIGHTS_MXFP8 ? tile_bytes<TP_WEIGHTS_MXFP8>()
                        : wf == TP_WEIGHTS_MXFP4 ? tile_bytes<TP_WEIGHTS_MXFP4>() : kTileBytes;
     const int nbuf = kDBufs[bt];
-    const bool flat = knobs && (p->mfma_flat == 1 || (p->mfma_flat < 0 && bt == 1 && b >= kFlatFromBatch));
     // activations: row-major up to 8 tokens (read directly, no layout
     // launch per step), else in A-operand order (1 KB per operand load)
     const bool acts_rm = p->mfma_acts == 1 || (p->mfma_acts == 0 && b <= kMfmaRowMajorActsMax);
     if (acts_rm && bt != 1) return false;
     const int64_t nkb0 = (k0 + kTileRows - 1) / kTileRows, nkb1 = (k1 + kTileRows - 1) / kTileRows;
+    // the ring of slots: from kFlatFromBatch tokens, and for bf16 weights
+    // where a layer's tiles per compute wave (whole strips) fit its 2 SL
+    // slots (small points: measured 1-6 % faster at H4096 N=8, 1-4 tokens;
+    // 1-2 % slower at N=4, whose points fill the banks)
+    const bool small_layer = (nkb0 + wps - 1) / wps + (nkb1 + wps - 1) / wps <= 2 * sl;
+    const bool flat = knobs && (p->mfma_flat == 1 ||
+                                (p->mfma_flat < 0 && bt == 1 &&
+                                 (b >= kFlatFromBatch || (small_layer && wf == TP_WEIGHTS_BF16))));
     // static LDS: D tiles of both parities, owned hidden state, a segment's
     // partial, tables; dynamic: the other ranks' values of the owned strips
     // (room for one rank's values even with N = 1, so that the clamped reads
