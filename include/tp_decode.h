@@ -170,6 +170,10 @@ tp_status tp_plan_set_weight_format(tp_plan_t plan, int32_t weight_format);
  *                banks of tp_decode_layers_packed: 4 or 8; 0 = automatic,
  *                8 for batch <= 4, else 4; 8 only takes effect for
  *                batch <= 4),
+ * "stream_flat" (vector-ALU stream, dataflow order: -1 = automatic: 1
+ *                where a layer's blocks fit one register bank, and with
+ *                bf16 weights from 4 tokens; 0 = a point per bank, 1 = the
+ *                banks run across points with no per-point barrier),
  * "stream_kind" (tp_decode_layers_packed: 0 = automatic, 1 = vector-ALU
  *                stream on pair strips, 2 = matrix-core stream on MFMA tiles),
  * "stream_wgs" (matrix-core stream: workgroups sharing the tiles, 0 = one

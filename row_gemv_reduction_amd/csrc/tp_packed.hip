@@ -944,10 +944,14 @@ tp_status tp_decode_stream(const tp_plan_s* p, int32_t n_layers, int32_t rank, c
     if (serial && geo.grid > kTargetCUs) return TP_ERR_UNSUPPORTED;
     // the dataflow order takes the stream block by block across points where
     // a layer's blocks fit one bank (small points: measured up to 33 %
-    // faster; larger points, up to 5 % slower that way, keep a point per bank)
-    // FLAT keeps two x buffers per kind
+    // faster; larger points, up to 5 % slower that way, keep a point per
+    // bank), and with bf16 weights from 4 tokens, where the compute waves'
+    // skew at the per-point barriers weighs (page-1 N=4 b=4 6 % faster, N=2
+    // b=4 the same; at 2 tokens 1 % slower). FLAT keeps two x buffers per kind
     const bool flat = !serial && !partials && 2 * (int64_t)geo.lds_bytes <= kStreamMaxLdsBytes &&
-                      (p->stream_flat >= 0 ? p->stream_flat == 1 : geo.bpw0 + geo.bpw1 <= geo.sl);
+                      (p->stream_flat >= 0 ? p->stream_flat == 1
+                                           : geo.bpw0 + geo.bpw1 <= geo.sl ||
+                                                 (p->batch >= 4 && p->weight_format == TP_WEIGHTS_BF16));
     const int32_t xpair = geo.xdwords;
     if (flat) {
         geo.xdwords *= 2;
