@@ -79,13 +79,15 @@ int tp_packed_kind(const tp_plan_s* p) {
         // MX weights, measured on MI355X: where strips stay whole the
         // matrix-core stream is as fast or faster (H4096 MXFP8 b=1: N=4
         // 0.188 against 0.197 ms) except for MXFP4 at one token (N=4 0.172
-        // against 0.156); where strips are cut the vector-ALU stream is
-        // faster; beyond 4 tokens the vector-ALU stream's widened vectors
-        // spill (N=8 b=8: 0.151 against 0.392 ms).
+        // against 0.156) unless a layer's tiles per compute wave fit the
+        // stream's 2 SL slots (N=8: 0.118 against 0.132 ms); where strips are
+        // cut the vector-ALU stream is faster; beyond 4 tokens the vector-ALU
+        // stream's widened vectors spill (N=8 b=8: 0.151 against 0.392 ms).
         if (p->stream_kind == 1) return valu ? 1 : 0;
         if (p->stream_kind == 2) return mfma ? 2 : 0;
         const bool whole = mfma && p->hidden / 16 <= mg.grid;
-        const bool fp4_one = p->weight_format == TP_WEIGHTS_MXFP4 && p->batch == 1;
+        const bool small = mfma && (mg.nkb0 + mg.wps - 1) / mg.wps + (mg.nkb1 + mg.wps - 1) / mg.wps <= 2 * mg.sl;
+        const bool fp4_one = p->weight_format == TP_WEIGHTS_MXFP4 && p->batch == 1 && !small;
         if (valu && p->batch <= 4 && (!whole || fp4_one)) return 1;
         if (mfma) return 2;
         return valu ? 1 : 0;
