@@ -916,6 +916,10 @@ FULL_SIZE = [
     (workloads.page1_n2(32), 2, 0),
     (workloads.h4096(8, 64), 2, 5),
     (workloads.h4096(4, 8), 2, 3),
+    # the matrix-core stream's ring of slots at small points (N=8, one
+    # token) and the vector-ALU stream's banks across points from 4 tokens
+    (workloads.h4096(8, 1), 3, 6),
+    (workloads.page1_n4(4), 2, 2),
 ]
 
 
